@@ -1,0 +1,152 @@
+"""Seeded synthetic inputs for the gated GQA attention core.
+
+This module only draws random numbers and lays them out; it holds none of the
+method's arithmetic (no norm, rotation, softmax or gate).  Both the HIP path's
+tests/benchmark and the CPU oracle's callers take their inputs from here.
+
+Shapes follow the pages' workloads: the Qwen3.5-4B attention geometry
+(16 query / 4 KV heads, head_dim 256, rotary_dim 64, theta 1e7, eps 1e-6 --
+Atlas ``qwen3_5/mod.rs``, ``Qwen35ForwardConfig::qwen3_5_4b_mlx_int8``) and the
+24-query / 2-KV-head, dim-256, four-row speculative-verify case (DS4Server
+issue #113, Reproduction).
+
+Recipe (one ``torch.Generator('cpu')`` per workload, seeded with its seed):
+
+1. ragged workloads only: prior lengths ``randint(lo, hi + 1, (B,))``;
+2. ``q_gate`` ``randn(B, L, Hq, 2D)``, then ``k_new``, ``v_new``
+   ``randn(B, L, Hkv, D)``;
+3. cached K rows, sequence by sequence ``randn(n_b, Hkv, D)``, then cached V
+   rows the same way;
+4. ``w_q = 1 + 0.1 randn(D)``, ``w_k = 1 + 0.1 randn(D)``;
+5. stress variant only: per (b, l, head) scale factors drawn from {0.05, 20}
+   (``randint(0, 2)``) for the query half of ``q_gate`` and for ``k_new``;
+6. every array is drawn in fp32 and then cast to the storage dtype
+   (bf16: round to nearest even, as ``Tensor.to`` does).
+
+Cache layout: token-major rows of ``[Hkv, D]``; sequence b owns rows
+``seq_offset[b] .. seq_offset[b] + capacity[b] - 1``; rows past ``n_b`` are
+zero.  Uniform batches give every sequence ``capacity = n + L`` rows; ragged
+batches pack sequences back to back with ``capacity_b = n_b + L``.  Positions
+of the new rows are ``n_b + l``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import torch
+
+DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    q_len: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    rotary_dim: int
+    rope_theta: float
+    dtype: str
+    prior: int                      # cached rows per sequence (uniform batches)
+    seed: int
+    rms_eps: float = 1e-6
+    ragged: tuple | None = None     # (lo, hi): prior lengths drawn uniformly in [lo, hi]
+    description: str = ""
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny_f32": Workload(
+        "tiny_f32", batch=1, q_len=1, num_q_heads=4, num_kv_heads=1, head_dim=64,
+        rotary_dim=16, rope_theta=1e4, dtype="f32", prior=32, seed=1,
+        description="tiny fp32 check: 4/1 heads, D 64, r 16, 32 cached tokens"),
+    "decode_4b": Workload(
+        "decode_4b", batch=1, q_len=1, num_q_heads=16, num_kv_heads=4, head_dim=256,
+        rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=4096, seed=2,
+        description="Qwen3.5-4B single-stream decode, 4096 cached tokens"),
+    "verify_24x2": Workload(
+        "verify_24x2", batch=8, q_len=4, num_q_heads=24, num_kv_heads=2, head_dim=256,
+        rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=2048, seed=3,
+        description="speculative verify: 8 sequences x 4 causal rows, 24/2 heads, 2048 cached"),
+    "ragged_4b": Workload(
+        "ragged_4b", batch=64, q_len=1, num_q_heads=16, num_kv_heads=4, head_dim=256,
+        rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=0, seed=4, ragged=(512, 32768),
+        description="ragged batched decode: 64 sequences, cached lengths U[512, 32768]"),
+    "prefill_4b": Workload(
+        "prefill_4b", batch=1, q_len=2048, num_q_heads=16, num_kv_heads=4, head_dim=256,
+        rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=30720, seed=5,
+        description="long prefill chunk: 2048 causal rows on 30720 cached tokens"),
+}
+
+
+def prior_lengths(w: Workload, gen: torch.Generator | None = None) -> torch.Tensor:
+    """Cached length per sequence (draw step 1 for ragged workloads)."""
+    if w.ragged is None:
+        return torch.full((w.batch,), w.prior, dtype=torch.int32)
+    lo, hi = w.ragged
+    if gen is None:
+        gen = torch.Generator("cpu").manual_seed(w.seed)
+    return torch.randint(lo, hi + 1, (w.batch,), generator=gen).to(torch.int32)
+
+
+def make_inputs(w: Workload, variant: str = "graded", seed: int | None = None) -> dict:
+    """Draw one call's inputs on the CPU.  See the module docstring for the recipe."""
+    if variant not in ("graded", "stress"):
+        raise ValueError(f"unknown variant {variant!r}")
+    gen = torch.Generator("cpu").manual_seed(w.seed if seed is None else seed)
+    B, L, Hq, Hkv, D = w.batch, w.q_len, w.num_q_heads, w.num_kv_heads, w.head_dim
+    dt = DTYPES[w.dtype]
+
+    n = prior_lengths(w, gen)
+    cap = (n + L).to(torch.int32)
+    offset = torch.zeros(B, dtype=torch.int64)
+    if B > 1:
+        offset[1:] = torch.cumsum(cap.to(torch.int64), 0)[:-1]
+    rows = int(cap.to(torch.int64).sum().item())
+
+    q_gate = torch.randn((B, L, Hq, 2 * D), generator=gen)
+    k_new = torch.randn((B, L, Hkv, D), generator=gen)
+    v_new = torch.randn((B, L, Hkv, D), generator=gen)
+    k_cache = torch.zeros((rows, Hkv, D), dtype=dt)
+    v_cache = torch.zeros((rows, Hkv, D), dtype=dt)
+    for cache in (k_cache, v_cache):
+        for b in range(B):
+            nb, o = int(n[b]), int(offset[b])
+            if nb:
+                cache[o:o + nb] = torch.randn((nb, Hkv, D), generator=gen).to(dt)
+    w_q = 1.0 + 0.1 * torch.randn(D, generator=gen)
+    w_k = 1.0 + 0.1 * torch.randn(D, generator=gen)
+    if variant == "stress":
+        levels = torch.tensor([0.05, 20.0])
+        sq = levels[torch.randint(0, 2, (B, L, Hq, 1), generator=gen)]
+        sk = levels[torch.randint(0, 2, (B, L, Hkv, 1), generator=gen)]
+        q_gate[..., :D] *= sq
+        k_new *= sk
+
+    positions = (n.view(B, 1) + torch.arange(L, dtype=torch.int32).view(1, L)).to(torch.int32)
+    return {
+        "q_gate": q_gate.to(dt).contiguous(),
+        "k_new": k_new.to(dt).contiguous(),
+        "v_new": v_new.to(dt).contiguous(),
+        "k_cache": k_cache,
+        "v_cache": v_cache,
+        "w_q": w_q.to(dt),
+        "w_k": w_k.to(dt),
+        "seq_lens": n.clone(),
+        "positions": positions.contiguous(),
+        "seq_offset": offset,
+        "capacity": cap,
+    }
+
+
+def to_device(inputs: dict, device) -> dict:
+    """Copy every tensor of an input dict to ``device``."""
+    return {k: v.to(device) if isinstance(v, torch.Tensor) else v for k, v in inputs.items()}

@@ -1,0 +1,233 @@
+"""CPU oracle for the gated grouped-query attention core.
+
+TEST INFRASTRUCTURE ONLY.  The test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` are the only callers.  The product library
+(``gated_gqa_attention_amd``) never imports this package, and this package
+never imports the product library.
+
+The arithmetic lives in ``qsa_oracle.c`` (plain C, IEEE double, one row at a
+time).  This module only builds it with gcc, loads it with ctypes and marshals
+arrays.  The steps it follows, with the pages they come from:
+
+* split of the doubled q_proj output per head into ``[query | gate]`` --
+  mlxd PR #99 "stage D6", Summary and the second review (``mlx_split`` index 0
+  = queries, index 1 = gate); Atlas ``qwen3_5/mod.rs``, ``q_total``;
+* per-head RMS QK-norm -- mlxd PR #99, config audit table (``has_qk_norm``);
+  Atlas ``FullAttentionLayer`` (``q_norm``, ``k_norm``);
+* partial RoPE on the first ``rotary_dim`` dims -- mlxd PR #99 Summary
+  (``partial_rotary_factor``); Atlas ``Qwen35ForwardConfig::rotary_dim``;
+* KV append at slot ``n_b + l`` then attention over ``n_b + l + 1`` keys --
+  Atlas ``qwen3_5/mod.rs`` module doc;
+* grouped-query attention with contiguous head groups -- DS4Server issue #113,
+  Reproduction; Atlas ``Qwen35ForwardConfig`` (16 query / 4 KV heads);
+* ``attn * sigmoid(gate)`` -- mlxd PR #99 Summary; Atlas ``sigmoid_gate``.
+
+Readings where the pages are silent are listed with each function below.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qsa_oracle.c")
+_LIB = os.path.join(_HERE, "libqsa_oracle.so")
+
+F64, F32, BF16 = 0, 1, 2
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, strict IEEE: no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
+             "-ffp-contract=off", "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("q_len", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("rotary_dim", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_double),
+        ("softmax_scale", ctypes.c_double), ("store_bits", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        p = ctypes.c_void_p
+        lib.qsa_oracle_round.restype = ctypes.c_double
+        lib.qsa_oracle_round.argtypes = [ctypes.c_double, ctypes.c_int]
+        lib.qsa_oracle_new_kv.restype = ctypes.c_int
+        lib.qsa_oracle_new_kv.argtypes = [ctypes.POINTER(_Cfg), p, p, p, p, p, p]
+        lib.qsa_oracle_attention.restype = ctypes.c_int
+        lib.qsa_oracle_attention.argtypes = [
+            ctypes.POINTER(_Cfg), p, p, p, p, ctypes.c_int32, p, p, p, p, p, p,
+            ctypes.c_int64, p, p]
+        lib.qsa_oracle_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+@dataclass
+class Geometry:
+    """Shape and numeric parameters of one call (plain values, no arrays)."""
+    batch: int
+    q_len: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    rotary_dim: int
+    rope_theta: float
+    rms_eps: float = 1e-6
+    softmax_scale: float = 0.0          # 0 selects 1/sqrt(head_dim)
+    dtype: str = "bf16"                  # storage dtype: "bf16" | "f32" | "f64"
+
+    def _c(self) -> _Cfg:
+        bits = {"bf16": 8, "f32": 24, "f64": 53}[self.dtype]
+        return _Cfg(self.batch, self.q_len, self.num_q_heads, self.num_kv_heads,
+                    self.head_dim, self.rotary_dim, float(self.rope_theta),
+                    float(self.rms_eps), float(self.softmax_scale), bits)
+
+
+def _f64(t) -> np.ndarray:
+    if isinstance(t, torch.Tensor):
+        t = t.detach().to("cpu", torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(t, dtype=np.float64))
+
+
+def _i32(t) -> np.ndarray:
+    if isinstance(t, torch.Tensor):
+        t = t.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(t, dtype=np.int32))
+
+
+def _i64(t) -> np.ndarray:
+    if isinstance(t, torch.Tensor):
+        t = t.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(t, dtype=np.int64))
+
+
+def _cache(t):
+    """Raw storage of a cache buffer and its dtype code (no copy of bf16 data)."""
+    if isinstance(t, torch.Tensor):
+        t = t.detach().cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16), BF16
+        if t.dtype == torch.float32:
+            return t.numpy(), F32
+        return t.to(torch.float64).numpy(), F64
+    a = np.ascontiguousarray(t)
+    if a.dtype == np.uint16:
+        return a, BF16
+    if a.dtype == np.float32:
+        return a, F32
+    return a.astype(np.float64), F64
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def round_to(x, dtype: str):
+    """Round doubles to a storage dtype (ties to even) with the oracle's rounding."""
+    lib = _load()
+    bits = {"bf16": 8, "f32": 24, "f64": 53}[dtype]
+    a = _f64(x)
+    return np.vectorize(lambda v: lib.qsa_oracle_round(float(v), bits))(a)
+
+
+def new_kv(geo: Geometry, k_new, v_new, w_k, positions):
+    """Roped, normalized K rows and V rows of the new tokens, rounded to storage.
+
+    Reading: the cache holds K after norm and rotation and V as given
+    (mlxd PR #99 first review, issue 2: KV-shared layers take K "pre-rotated"
+    from the source layer's cache); both rounded to nearest-even.
+    """
+    lib = _load()
+    kn, vn, wk, pos = _f64(k_new), _f64(v_new), _f64(w_k), _i32(positions)
+    kr = np.empty_like(kn)
+    vr = np.empty_like(vn)
+    rc = lib.qsa_oracle_new_kv(ctypes.byref(geo._c()), _ptr(kn), _ptr(vn), _ptr(wk),
+                               _ptr(pos), _ptr(kr), _ptr(vr))
+    if rc != 0:
+        raise ValueError("oracle rejected the configuration")
+    return kr, vr
+
+
+def attention(geo: Geometry, q_gate, w_q, k_cache, v_cache, seq_offset, seq_lens, positions,
+              k_rows=None, v_rows=None, rows=None, want_attn=False):
+    """Gated attention of the new rows (see qsa_oracle.h for layouts).
+
+    ``k_rows``/``v_rows`` (from :func:`new_kv`) supply keys n_b..n_b+L-1; pass
+    ``None`` for both when those rows are already in the cache.  ``rows`` is an
+    optional array of flat ``(b*L + l)*Hq + h`` indices.  Returns ``out`` (and
+    the ungated ``attn`` when ``want_attn``) as float64 arrays, shape
+    ``[B, L, Hq, D]`` or ``[n_rows, D]``.
+    """
+    lib = _load()
+    qg, wq = _f64(q_gate), _f64(w_q)
+    kc, kdt = _cache(k_cache)
+    vc, vdt = _cache(v_cache)
+    if kdt != vdt:
+        raise ValueError("K and V caches must share a storage dtype")
+    off, sl, pos = _i64(seq_offset), _i32(seq_lens), _i32(positions)
+    kr = None if k_rows is None else _f64(k_rows)
+    vr = None if v_rows is None else _f64(v_rows)
+    D = geo.head_dim
+    if rows is None:
+        shape = (geo.batch, geo.q_len, geo.num_q_heads, D)
+        r = None
+        n = 0
+    else:
+        r = _i64(rows)
+        n = r.size
+        shape = (n, D)
+    out = np.empty(shape, dtype=np.float64)
+    att = np.empty(shape, dtype=np.float64) if want_attn else None
+    rc = lib.qsa_oracle_attention(ctypes.byref(geo._c()), _ptr(qg), _ptr(wq), _ptr(kc),
+                                  _ptr(vc), kdt, _ptr(off), _ptr(sl), _ptr(pos), _ptr(kr),
+                                  _ptr(vr), _ptr(r), n, _ptr(out), _ptr(att))
+    if rc != 0:
+        raise ValueError("oracle rejected the configuration or a row index")
+    return (out, att) if want_attn else out
+
+
+def gated_attention(geo: Geometry, inputs: dict, rows=None, want_attn=False, fused=True):
+    """Whole call: append the new rows (when ``fused``), then gated attention.
+
+    ``inputs`` holds ``q_gate, k_new, v_new, k_cache, v_cache, w_q, w_k,
+    seq_offset, seq_lens, positions`` (CPU tensors or arrays).  Returns
+    ``(out, k_rows, v_rows)`` plus ``attn`` when requested.
+    """
+    kr = vr = None
+    if fused:
+        kr, vr = new_kv(geo, inputs["k_new"], inputs["v_new"], inputs["w_k"],
+                        inputs["positions"])
+    res = attention(geo, inputs["q_gate"], inputs["w_q"], inputs["k_cache"], inputs["v_cache"],
+                    inputs["seq_offset"], inputs["seq_lens"], inputs["positions"], kr, vr,
+                    rows=rows, want_attn=want_attn)
+    if want_attn:
+        out, att = res
+        return out, kr, vr, att
+    return res, kr, vr
+
+
+def threads() -> int:
+    return int(_load().qsa_oracle_threads())

@@ -1,0 +1,98 @@
+/*
+ * qsa_oracle.h -- plain CPU oracle for the gated grouped-query attention core.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or helper with the HIP library under gated_gqa_attention_amd/.
+ *
+ * What it computes (per new row l of sequence b and query head h):
+ *   split  : the q_proj output of one head is [query(D) | gate(D)]
+ *            (mlxd PR #99 "stage D6", Summary: doubled q_proj -> split into
+ *            queries and gate -> o_proj(attn * sigmoid(gate)); Atlas
+ *            qwen3_5/mod.rs, Qwen35ForwardConfig::q_total)
+ *   norm   : per-head RMS norm of q and k over D, times a [D] weight
+ *            (mlxd PR #99 config audit table, has_qk_norm; Atlas
+ *            FullAttentionLayer q_norm / k_norm)
+ *   rope   : rotation of only the first rotary_dim dims of q and k
+ *            (mlxd PR #99 Summary, partial_rotary_factor; Atlas
+ *            Qwen35ForwardConfig::rotary_dim doc comment)
+ *   append : roped K and raw V of the new rows stored at slot n_b + l
+ *            (Atlas qwen3_5/mod.rs module doc: KV append at cache_pos,
+ *            attention over cache_pos + 1 keys)
+ *   attend : softmax(scale * q.K^T) V over keys 0 .. n_b + l, with the
+ *            query heads of one KV head forming a contiguous group
+ *            (DS4Server issue #113, Reproduction: query heads divided
+ *            within their KV groups)
+ *   gate   : out = attn * sigmoid(gate), rounded to the storage dtype.
+ *
+ * All arithmetic is IEEE double.  Inputs are the stored (bf16 or fp32)
+ * values widened exactly.  Rounding to the storage dtype is round to
+ * nearest, ties to even, written from its definition.
+ */
+#ifndef QSA_ORACLE_H
+#define QSA_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage codes for cache buffers handed to the oracle. */
+enum { QSA_ORACLE_F64 = 0, QSA_ORACLE_F32 = 1, QSA_ORACLE_BF16 = 2 };
+
+typedef struct {
+  int32_t batch;          /* B */
+  int32_t q_len;          /* L, new rows per sequence */
+  int32_t num_q_heads;    /* Hq */
+  int32_t num_kv_heads;   /* Hkv, Hq % Hkv == 0 */
+  int32_t head_dim;       /* D */
+  int32_t rotary_dim;     /* r, even, 0 <= r <= D; 0 disables the rotation */
+  double rope_theta;      /* theta */
+  double rms_eps;         /* eps inside the square root */
+  double softmax_scale;   /* 0 selects 1/sqrt(D) */
+  int32_t store_bits;     /* significand bits of the storage dtype: 8 bf16, 24 fp32, 53 keeps double */
+} qsa_oracle_cfg;
+
+/* Round x to a binary floating-point value with `bits` significand bits,
+ * ties to even.  bits >= 53 returns x. */
+double qsa_oracle_round(double x, int bits);
+
+/* New cache rows.  k_new, v_new: [B][L][Hkv][D]; w_k: [D]; positions: [B][L].
+ * Writes k_rows = round(rope(rmsnorm(k_new) * w_k)) and v_rows = round(v_new),
+ * both [B][L][Hkv][D].  Returns 0, or -1 on an invalid configuration. */
+int qsa_oracle_new_kv(const qsa_oracle_cfg *cfg, const double *k_new, const double *v_new,
+                      const double *w_k, const int32_t *positions, double *k_rows,
+                      double *v_rows);
+
+/* Gated attention of the new rows.
+ *   q_gate     [B][L][Hq][2D]   per head [query | gate]
+ *   w_q        [D]
+ *   k_cache,
+ *   v_cache    token-major rows of [Hkv][D] in storage `cache_dtype`; sequence b
+ *              starts at row seq_offset[b]
+ *   seq_lens   [B] cached rows before this call (n_b)
+ *   positions  [B][L] rotary positions of the new rows
+ *   k_rows,
+ *   v_rows     [B][L][Hkv][D] new rows from qsa_oracle_new_kv, used for keys
+ *              n_b .. n_b+L-1; both NULL means those keys are read from the cache
+ *   rows       flat (b*L + l)*Hq + h indices to evaluate, or NULL for all
+ *   out        [n_rows][D] (or [B][L][Hq][D] when rows is NULL): gated output
+ *              rounded to the storage dtype
+ *   attn       optional, same shape: the attention output before the gate,
+ *              unrounded
+ * Row l of sequence b attends to keys 0 .. n_b + l.  Returns 0 or -1. */
+int qsa_oracle_attention(const qsa_oracle_cfg *cfg, const double *q_gate, const double *w_q,
+                         const void *k_cache, const void *v_cache, int32_t cache_dtype,
+                         const int64_t *seq_offset, const int32_t *seq_lens,
+                         const int32_t *positions, const double *k_rows,
+                         const double *v_rows, const int64_t *rows, int64_t n_rows,
+                         double *out, double *attn);
+
+/* Number of OpenMP threads the oracle runs with. */
+int qsa_oracle_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

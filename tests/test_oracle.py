@@ -1,0 +1,399 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle is only trusted once it agrees with things other than itself:
+library routines that compute the same quantity (transformers' Qwen3.5
+attention layer, torch's rms_norm and scaled_dot_product_attention, torch's
+round-to-nearest-even casts), closed forms, invariants of the method, the
+head-chunk plan from DS4Server issue #113, and an independently written NumPy
+twin.  The mutation tests then show that each plausible slip moves the result
+far past the parity tolerance.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_gqa_attention_amd.workloads import WORKLOADS, Workload, make_inputs
+from twin import MUTANTS, round_bits, twin
+
+BF16_TOL_REL_L2 = 5e-3
+F32_TOL_REL_L2 = 1e-5
+
+SMALL = [
+    Workload("s_gqa", batch=2, q_len=3, num_q_heads=4, num_kv_heads=2, head_dim=64,
+             rotary_dim=16, rope_theta=1e4, dtype="bf16", prior=5, seed=11),
+    Workload("s_mha_full_rope", batch=1, q_len=2, num_q_heads=2, num_kv_heads=2, head_dim=32,
+             rotary_dim=32, rope_theta=1e4, dtype="f32", prior=4, seed=12),
+    Workload("s_ragged_norope", batch=3, q_len=1, num_q_heads=4, num_kv_heads=1, head_dim=64,
+             rotary_dim=0, rope_theta=1e4, dtype="bf16", prior=0, seed=13, ragged=(1, 9)),
+    Workload("s_verify", batch=2, q_len=4, num_q_heads=12, num_kv_heads=1, head_dim=64,
+             rotary_dim=16, rope_theta=1e7, dtype="bf16", prior=7, seed=14),
+    WORKLOADS["tiny_f32"],
+]
+BITS = {"bf16": 8, "f32": 24, "f64": 53}
+
+
+def geo(w: Workload, dtype=None) -> oracle.Geometry:
+    return oracle.Geometry(w.batch, w.q_len, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                           w.rotary_dim, w.rope_theta, w.rms_eps, 0.0, dtype or w.dtype)
+
+
+def rel_l2(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def run(w, inp, dtype=None, **kw):
+    return oracle.gated_attention(geo(w, dtype), inp, **kw)
+
+
+# ---------------------------------------------------------------- rounding
+def test_round_ties_to_even_examples():
+    r = lambda x: float(oracle.round_to(np.array([x]), "bf16")[0])
+    assert r(1.0 + 2.0 ** -8) == 1.0                       # tie -> even (down)
+    assert r(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6       # tie -> even (up)
+    assert r(1.0 + 2.0 ** -8 + 2.0 ** -30) == 1.0 + 2.0 ** -7
+    assert r(-(1.0 + 3 * 2.0 ** -8)) == -(1.0 + 2.0 ** -6)
+    assert r(0.0) == 0.0
+
+
+def test_round_matches_library_casts():
+    g = torch.Generator().manual_seed(0)
+    x32 = torch.randn(20000, generator=g) * torch.exp(4 * torch.randn(20000, generator=g))
+    ours = oracle.round_to(x32.double().numpy(), "bf16")
+    lib = x32.to(torch.bfloat16).double().numpy()        # torch casts fp32 -> bf16 with RNE
+    assert np.array_equal(ours, lib)
+    x64 = np.random.default_rng(1).standard_normal(20000) * 1e3
+    assert np.array_equal(oracle.round_to(x64, "f32"), x64.astype(np.float32).astype(np.float64))
+
+
+# ---------------------------------------------------------------- twin
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+@pytest.mark.parametrize("fused", [True, False])
+def test_twin_agrees_with_oracle(w, fused):
+    inp = make_inputs(w)
+    out, _, _, att = run(w, inp, want_attn=True, fused=fused)
+    t_out, t_att = twin(w, inp, BITS[w.dtype], fused=fused)
+    assert np.max(np.abs(att - t_att)) <= 1e-12 * max(1.0, np.max(np.abs(t_att)))
+    ulp = np.abs(t_out) * 2.0 ** (1 - BITS[w.dtype]) + 1e-300
+    assert np.all(np.abs(out - t_out) <= ulp)
+
+
+# ---------------------------------------------------------------- transformers Qwen3.5 layer
+def _hf_attention(w: Workload, inp: dict):
+    """The same computation through transformers' Qwen3_5Attention (float64 module).
+
+    The projections are set to exact selections so the layer's input is the
+    concatenation [q_gate | k_new | v_new]; o_proj is removed.  transformers'
+    RMSNorm scales by (1 + weight), so it is given weight = w - 1.
+    """
+    from transformers import DynamicCache
+    from transformers.models.qwen3_5 import modeling_qwen3_5 as M
+    from transformers.models.qwen3_5.configuration_qwen3_5 import Qwen3_5TextConfig
+
+    B, L, Hq, Hkv, D, r = (w.batch, w.q_len, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                           w.rotary_dim)
+    nq, nk = Hq * 2 * D, Hkv * D
+    half = r // 2
+    sec = [half - 2 * (half // 3), half // 3, half // 3]
+    cfg = Qwen3_5TextConfig(
+        hidden_size=nq + 2 * nk, num_attention_heads=Hq, num_key_value_heads=Hkv, head_dim=D,
+        rope_parameters={"rope_type": "default", "rope_theta": w.rope_theta,
+                         "partial_rotary_factor": r / D, "mrope_section": sec},
+        rms_norm_eps=w.rms_eps, attention_bias=False, num_hidden_layers=1,
+        layer_types=["full_attention"])
+    cfg._attn_implementation = "eager"
+    att = M.Qwen3_5Attention(cfg, 0).double()
+    eye = torch.eye(nq + 2 * nk, dtype=torch.float64)
+    with torch.no_grad():
+        att.q_proj.weight.copy_(eye[:nq])
+        att.k_proj.weight.copy_(eye[nq:nq + nk])
+        att.v_proj.weight.copy_(eye[nq + nk:])
+        att.q_norm.weight.copy_(inp["w_q"].double() - 1)
+        att.k_norm.weight.copy_(inp["w_k"].double() - 1)
+    att.o_proj = torch.nn.Identity()
+    rot = M.Qwen3_5TextRotaryEmbedding(cfg)
+
+    outs = []
+    for b in range(B):
+        n, off = int(inp["seq_lens"][b]), int(inp["seq_offset"][b])
+        x = torch.cat([inp["q_gate"][b].reshape(L, -1), inp["k_new"][b].reshape(L, -1),
+                       inp["v_new"][b].reshape(L, -1)], dim=-1).double()[None]
+        pos = inp["positions"][b:b + 1].long()
+        cos, sin = rot(x, pos)
+        cache = DynamicCache()
+        if n:
+            kp = inp["k_cache"][off:off + n].double().permute(1, 0, 2)[None]
+            vp = inp["v_cache"][off:off + n].double().permute(1, 0, 2)[None]
+            cache.update(kp, vp, 0)
+        mask = torch.full((L, n + L), float("-inf"), dtype=torch.float64)
+        for l in range(L):
+            mask[l, :n + l + 1] = 0.0
+        with torch.no_grad():
+            o, _ = att(x, (cos, sin), mask[None, None], past_key_values=cache)
+        outs.append(o.reshape(L, Hq, D).numpy())
+    return np.stack(outs)
+
+
+HF_CASES = [
+    WORKLOADS["tiny_f32"],
+    Workload("hf_gqa_causal", batch=2, q_len=3, num_q_heads=6, num_kv_heads=2, head_dim=64,
+             rotary_dim=16, rope_theta=1e4, dtype="f32", prior=9, seed=21),
+    Workload("hf_full_rope", batch=1, q_len=2, num_q_heads=4, num_kv_heads=1, head_dim=32,
+             rotary_dim=32, rope_theta=1e6, dtype="f32", prior=6, seed=22),
+    Workload("hf_4b_heads", batch=1, q_len=2, num_q_heads=16, num_kv_heads=4, head_dim=256,
+             rotary_dim=64, rope_theta=1e7, dtype="f32", prior=11, seed=23),
+]
+
+
+@pytest.mark.parametrize("w", HF_CASES, ids=lambda w: w.name)
+def test_oracle_matches_transformers_qwen3_5_attention(w):
+    inp = make_inputs(w)
+    ours, _, _ = run(w, inp, dtype="f64")
+    ref = _hf_attention(w, inp)
+    # transformers runs its norm and rotary tables in fp32 internally
+    assert rel_l2(ours, ref) < 2e-6
+
+
+# ---------------------------------------------------------------- library routines
+def test_kv_rows_match_torch_rms_norm():
+    w = Workload("rms", batch=2, q_len=3, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                 rotary_dim=0, rope_theta=1e4, dtype="f32", prior=1, seed=31)
+    inp = make_inputs(w, variant="stress")
+    kr, vr = oracle.new_kv(geo(w, "f64"), inp["k_new"], inp["v_new"], inp["w_k"], inp["positions"])
+    ref = torch.nn.functional.rms_norm(inp["k_new"].double(), (64,), inp["w_k"].double(), w.rms_eps)
+    assert np.max(np.abs(kr - ref.numpy())) < 1e-12 * np.max(np.abs(kr))
+    assert np.array_equal(vr, inp["v_new"].double().numpy())
+
+
+def test_attention_core_matches_torch_sdpa():
+    """With every position 0 the rotation is the identity; q~ is then torch's rms_norm."""
+    w = Workload("sdpa", batch=2, q_len=3, num_q_heads=6, num_kv_heads=2, head_dim=64,
+                 rotary_dim=16, rope_theta=1e4, dtype="f32", prior=7, seed=32)
+    inp = make_inputs(w)
+    inp["positions"].zero_()
+    _, _, _, att = run(w, inp, dtype="f64", want_attn=True, fused=False)
+    D, G, L = w.head_dim, w.group, w.q_len
+    for b in range(w.batch):
+        n, off = int(inp["seq_lens"][b]), int(inp["seq_offset"][b])
+        q = torch.nn.functional.rms_norm(inp["q_gate"][b, :, :, :D].double(), (D,),
+                                         inp["w_q"].double(), w.rms_eps)      # [L, Hq, D]
+        k = inp["k_cache"][off:off + n + L].double().repeat_interleave(G, dim=1)
+        v = inp["v_cache"][off:off + n + L].double().repeat_interleave(G, dim=1)
+        mask = torch.zeros(L, n + L, dtype=torch.bool)
+        for l in range(L):
+            mask[l, :n + l + 1] = True
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q.transpose(0, 1), k.transpose(0, 1).contiguous(), v.transpose(0, 1).contiguous(),
+            attn_mask=mask)
+        assert np.max(np.abs(att[b] - ref.transpose(0, 1).numpy())) < 1e-12
+
+
+# ---------------------------------------------------------------- closed forms
+def test_identical_keys_give_mean_of_values():
+    w = SMALL[0]
+    inp = make_inputs(w)
+    inp["k_cache"][:] = inp["k_cache"][int(inp["seq_offset"][0])]
+    out, _, _, att = run(w, inp, want_attn=True, fused=False)
+    for b in range(w.batch):
+        n, off = int(inp["seq_lens"][b]), int(inp["seq_offset"][b])
+        v = inp["v_cache"].double().numpy()
+        for l in range(w.q_len):
+            mean = v[off:off + n + l + 1].mean(axis=0)                     # [Hkv, D]
+            expect = np.repeat(mean, w.group, axis=0)
+            assert np.max(np.abs(att[b, l] - expect)) < 1e-12
+
+
+def test_zero_query_weight_gives_uniform_mean():
+    w = SMALL[3]
+    inp = make_inputs(w)
+    inp["w_q"].zero_()
+    out, kr, vr, att = run(w, inp, want_attn=True)
+    for b in range(w.batch):
+        n, off = int(inp["seq_lens"][b]), int(inp["seq_offset"][b])
+        vals = inp["v_cache"][off:off + n].double().numpy()
+        for l in range(w.q_len):
+            allv = np.concatenate([vals, vr[b, :l + 1]], axis=0)
+            expect = np.repeat(allv.mean(axis=0), w.group, axis=0)
+            assert np.max(np.abs(att[b, l] - expect)) < 1e-12
+
+
+def test_single_key_returns_gated_value():
+    w = Workload("one", batch=2, q_len=1, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                 rotary_dim=16, rope_theta=1e7, dtype="bf16", prior=0, seed=33)
+    inp = make_inputs(w)
+    out, kr, vr = run(w, inp)
+    z = inp["q_gate"][..., 64:].double().numpy()
+    v = np.repeat(inp["v_new"].double().numpy(), 2, axis=2)
+    expect = round_bits(v / (1 + np.exp(-z)), 8)
+    ulp = np.abs(expect) * 2.0 ** -7 + 1e-300
+    assert np.all(np.abs(out - expect) <= ulp)
+
+
+def test_gate_zero_halves_and_large_gate_passes():
+    w = SMALL[0]
+    inp = make_inputs(w)
+    D = w.head_dim
+    inp["q_gate"][..., D:] = 0.0
+    out, _, _, att = run(w, inp, dtype="f64", want_attn=True)
+    assert np.max(np.abs(out - 0.5 * att)) < 1e-15
+    inp["q_gate"][..., D:] = 40.0
+    out, _, _, att = run(w, inp, dtype="f64", want_attn=True)
+    assert np.max(np.abs(out - att)) < 1e-15
+
+
+# ---------------------------------------------------------------- rotary invariants
+def test_rotary_dim_zero_equals_all_positions_zero():
+    w = SMALL[0]
+    inp = make_inputs(w)
+    a, _, _ = run(w.with_(rotary_dim=0), inp, dtype="f64")
+    inp0 = dict(inp, positions=torch.zeros_like(inp["positions"]))
+    b, _, _ = run(w, inp0, dtype="f64")
+    assert np.array_equal(a, b)
+    c, _, _ = run(w, inp, dtype="f64")
+    assert rel_l2(c, a) > 1e-3          # and the rotation does act at nonzero positions
+
+
+def test_rotation_preserves_norm_and_leaves_tail_dims():
+    w = SMALL[3]
+    inp = make_inputs(w, variant="stress")
+    g = geo(w, "f64")
+    kr, _ = oracle.new_kv(g, inp["k_new"], inp["v_new"], inp["w_k"], inp["positions"])
+    k0, _ = oracle.new_kv(g, inp["k_new"], inp["v_new"], inp["w_k"],
+                          torch.zeros_like(inp["positions"]))
+    r = w.rotary_dim
+    assert np.allclose(np.linalg.norm(kr[..., :r], axis=-1), np.linalg.norm(k0[..., :r], axis=-1),
+                       rtol=1e-13)
+    assert np.array_equal(kr[..., r:], k0[..., r:])
+    h = r // 2
+    # each rotated pair (i, i + r/2) keeps its length
+    assert np.allclose(kr[..., :h] ** 2 + kr[..., h:r] ** 2, k0[..., :h] ** 2 + k0[..., h:r] ** 2,
+                       rtol=1e-12, atol=1e-14)
+
+
+def test_relative_position_invariance():
+    """Keys appended at positions p_j and a query at p: shifting every position
+    by the same amount leaves the output unchanged (RoPE depends on p - p_j)."""
+    w = Workload("relpos", batch=1, q_len=9, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                 rotary_dim=32, rope_theta=1e4, dtype="f64", prior=0, seed=34)
+    inp = make_inputs(w.with_(dtype="f32"))
+    outs = []
+    for shift in (0, 1000, 12345):
+        x = dict(inp, positions=inp["positions"] + shift)
+        out, _, _ = oracle.gated_attention(geo(w, "f64"), x)
+        outs.append(out)
+    assert rel_l2(outs[1], outs[0]) < 1e-10
+    assert rel_l2(outs[2], outs[0]) < 1e-10
+
+
+# ---------------------------------------------------------------- method invariants
+def head_chunk_plan(q_len, num_q_heads, num_kv_heads, limit=32):
+    """Head-chunked evaluation plan of DS4Server issue #113: eligible when
+    q_len * (Hq / Hkv) > 32 and q_len <= 32; query heads are then split within
+    each KV group into chunks of max(1, min(G, 32 // q_len)), the last chunk of
+    a group keeping the remainder.  Returns a list of head-index lists."""
+    G = num_q_heads // num_kv_heads
+    if not (q_len * G > limit and q_len <= limit):
+        return [list(range(num_q_heads))]
+    per = max(1, min(G, limit // q_len))
+    chunks = []
+    for g in range(num_kv_heads):
+        heads = list(range(g * G, (g + 1) * G))
+        chunks += [heads[i:i + per] for i in range(0, G, per)]
+    return chunks
+
+
+def test_head_chunk_plan_shapes():
+    assert [len(c) for c in head_chunk_plan(4, 24, 2)] == [8, 4, 8, 4]
+    assert head_chunk_plan(1, 16, 4) == [list(range(16))]          # 1 * 4 <= 32
+    assert head_chunk_plan(33, 16, 4) == [list(range(16))]         # q_len > 32
+    assert [len(c) for c in head_chunk_plan(16, 16, 4)] == [2] * 8
+    assert [len(c) for c in head_chunk_plan(32, 8, 1)] == [1] * 8
+
+
+@pytest.mark.parametrize("w", [WORKLOADS["verify_24x2"].with_(prior=40, head_dim=64, rotary_dim=16),
+                               SMALL[3]], ids=["verify_24x2_short", "s_verify"])
+def test_head_chunked_equals_unchunked(w):
+    inp = make_inputs(w)
+    full, kr, vr = run(w, inp)
+    g = geo(w)
+    B, L, Hq = w.batch, w.q_len, w.num_q_heads
+    chunked = np.empty_like(full)
+    for heads in head_chunk_plan(L, Hq, w.num_kv_heads):
+        rows = np.array([(b * L + l) * Hq + h for b in range(B) for l in range(L) for h in heads])
+        part = oracle.attention(g, inp["q_gate"], inp["w_q"], inp["k_cache"], inp["v_cache"],
+                                inp["seq_offset"], inp["seq_lens"], inp["positions"], kr, vr,
+                                rows=rows)
+        for i, f in enumerate(rows):
+            chunked[f // (L * Hq), (f // Hq) % L, f % Hq] = part[i]
+    assert np.array_equal(chunked, full)
+
+
+def test_prefill_equals_row_by_row_decode():
+    """L causal rows in one call == L single-row calls, each appending its row."""
+    w = SMALL[3]
+    inp = make_inputs(w)
+    full, kr, vr = run(w, inp)
+    B, L = w.batch, w.q_len
+    kc, vc = inp["k_cache"].clone(), inp["v_cache"].clone()
+    one = w.with_(q_len=1)
+    for l in range(L):
+        step = {
+            "q_gate": inp["q_gate"][:, l:l + 1], "k_new": inp["k_new"][:, l:l + 1],
+            "v_new": inp["v_new"][:, l:l + 1], "k_cache": kc, "v_cache": vc,
+            "w_q": inp["w_q"], "w_k": inp["w_k"], "seq_offset": inp["seq_offset"],
+            "seq_lens": inp["seq_lens"] + l, "positions": inp["positions"][:, l:l + 1],
+        }
+        out, k1, v1 = run(one, step)
+        assert np.array_equal(out[:, 0], full[:, l])
+        for b in range(B):
+            slot = int(inp["seq_offset"][b]) + int(inp["seq_lens"][b]) + l
+            kc[slot] = torch.from_numpy(k1[b, 0]).to(kc.dtype)
+            vc[slot] = torch.from_numpy(v1[b, 0]).to(vc.dtype)
+
+
+def test_later_rows_do_not_reach_earlier_rows():
+    w = SMALL[3]
+    inp = make_inputs(w)
+    base, _, _ = run(w, inp)
+    pert = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    pert["k_new"][:, 2:] += 3.0
+    pert["v_new"][:, 2:] -= 5.0
+    out, _, _ = run(w, pert)
+    assert np.array_equal(out[:, :2], base[:, :2])
+    assert not np.array_equal(out[:, 2:], base[:, 2:])
+
+
+def test_norm_scale_invariance():
+    """With eps = 0 the per-head RMS norm makes the result independent of the
+    scale of the query half and of the new key."""
+    w = SMALL[0].with_(rms_eps=0.0)
+    inp = make_inputs(w)
+    D = w.head_dim
+    a, _, _ = run(w, inp, dtype="f64")
+    x = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    x["q_gate"] = x["q_gate"].double()
+    x["q_gate"][..., :D] *= 7.5
+    x["k_new"] = x["k_new"].double() * 0.125
+    b, _, _ = run(w, x, dtype="f64")
+    assert rel_l2(b, a) < 1e-12
+
+
+# ---------------------------------------------------------------- mutation sensitivity
+MUT_CASES = [SMALL[3], SMALL[0], WORKLOADS["tiny_f32"]]
+
+
+@pytest.mark.parametrize("mutant", MUTANTS)
+def test_each_mutant_breaks_parity_tolerance(mutant):
+    """Every plausible slip moves rel-L2 at least 10x past the bf16 tolerance
+    on at least one graded or stress input, so parity would catch it."""
+    worst = 0.0
+    for w in MUT_CASES:
+        for variant in ("graded", "stress"):
+            inp = make_inputs(w, variant=variant)
+            ref, _, _ = run(w, inp)
+            mut, _ = twin(w, inp, BITS[w.dtype], mutant=mutant)
+            worst = max(worst, rel_l2(mut, ref))
+    assert worst >= 10 * BF16_TOL_REL_L2, (mutant, worst)
