@@ -1,0 +1,268 @@
+"""Benchmark: one step = one gated GQA attention call (split, QK-norm, partial RoPE,
+KV append, causal GQA attention, sigmoid gate) on one batch of synthetic input.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_4b]
+
+Prints one JSON line.  The default workload is the Qwen3.5-4B single-stream
+decode (16 query / 4 KV heads, head_dim 256, rotary_dim 64, 4096 cached
+tokens, bf16).  Inputs are resident in HBM before timing starts; decode and
+verify rotate over enough distinct buffer sets (>= 1 GB) that every step reads
+its KV cache from HBM rather than from the 256 MB Infinity Cache.  The K timed
+steps are captured in one HIP graph and replayed once, bracketed by HIP events
+on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from gated_gqa_attention_amd import binding  # noqa: E402
+from gated_gqa_attention_amd.workloads import DTYPES, WORKLOADS, make_inputs  # noqa: E402
+
+METRIC = "gated-GQA attn tokens/s + effective HBM GB/s (% of peak), 4B geometry decode"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA
+ROTATE_BYTES = 1 << 30         # rotate over at least this many bytes of inputs
+
+DEFAULT_STEPS = {"decode_4b": (2000, 200), "verify_24x2": (1000, 100), "ragged_4b": (20, 3),
+                 "prefill_4b": (20, 3), "tiny_f32": (1000, 100)}
+
+
+def algorithmic_work(w, seq_lens):
+    """Bytes the method must move and FLOPs it must do per call (QK^T and PV only)."""
+    es = 2 if w.dtype == "bf16" else 4
+    B, L, Hq, Hkv, D = w.batch, w.q_len, w.num_q_heads, w.num_kv_heads, w.head_dim
+    n = [int(x) for x in seq_lens]
+    kv_read = sum(n) * Hkv * D * 2 * es                 # cached K and V rows
+    reads = B * L * Hq * 2 * D * es + 2 * B * L * Hkv * D * es + 2 * D * es + 4 * B + 4 * B * L
+    writes = B * L * Hq * D * es + 2 * B * L * Hkv * D * es
+    keys = sum(nb * L + L * (L + 1) // 2 for nb in n)    # sum over rows of the keys each row sees
+    flops = keys * Hq * 4 * D
+    return kv_read + reads + writes, flops
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "gated_gqa_attention_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload, per_launch_units=1):
+    """HBM bytes per launch from committed rocprofv3 PMC summaries, if they were
+    taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"]) * per_launch_units
+    except (KeyError, ValueError):
+        return None
+
+
+class Call:
+    """Device buffers and C-ABI arguments of one buffer set."""
+
+    def __init__(self, w, dev, workspace, max_seq_len, stream):
+        self.w, self.dev = w, dev
+        self.cfg = binding.make_cfg(
+            batch=w.batch, q_len=w.q_len, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+            head_dim=w.head_dim, rotary_dim=w.rotary_dim, rope_theta=w.rope_theta, rms_eps=w.rms_eps,
+            dtype=DTYPES[w.dtype], max_seq_len=max_seq_len, q_norm_w=dev["w_q"], k_norm_w=dev["w_k"],
+            workspace=workspace, stream=stream)
+        self.kv = binding.make_kv(dev["k_cache"], dev["v_cache"], dev["seq_offset"], dev["capacity"])
+        self.ws = workspace
+        self.out = torch.empty((w.batch, w.q_len, w.num_q_heads, w.head_dim), dtype=DTYPES[w.dtype],
+                               device=dev["q_gate"].device)
+
+    def __call__(self):
+        d = self.dev
+        binding.gated_attention(self.cfg, self.kv, d["q_gate"], d["k_new"], d["v_new"], d["seq_lens"],
+                                d["positions"], self.out)
+
+
+def cpu_baseline(w, inputs, tokens_per_call, budget_s=10.0):
+    """The oracle, as is, on this host's cores over a bounded sample of the workload."""
+    import numpy as np
+    import oracle
+
+    g = oracle.Geometry(w.batch, w.q_len, w.num_q_heads, w.num_kv_heads, w.head_dim, w.rotary_dim,
+                        w.rope_theta, w.rms_eps, 0.0, w.dtype)
+    total_rows = w.batch * w.q_len * w.num_q_heads
+    threads = max(1, oracle.threads())
+    # time a few rows (one per core at most, so they run side by side) to size the sample
+    rng = np.random.default_rng(0)
+    probe = np.sort(rng.choice(total_rows, size=min(total_rows, threads), replace=False)).astype(np.int64)
+    kr, vr = oracle.new_kv(g, inputs["k_new"], inputs["v_new"], inputs["w_k"], inputs["positions"])
+    t0 = time.perf_counter()
+    oracle.attention(g, inputs["q_gate"], inputs["w_q"], inputs["k_cache"], inputs["v_cache"],
+                     inputs["seq_offset"], inputs["seq_lens"], inputs["positions"], kr, vr, rows=probe)
+    t_row = max(time.perf_counter() - t0, 1e-6)         # wall time of one row per core
+    est_full = -(-total_rows // threads) * t_row
+    rows_budget = total_rows if est_full <= budget_s else int(budget_s / t_row) * threads
+    if rows_budget >= total_rows:
+        t0 = time.perf_counter()
+        done = 0
+        while done == 0 or time.perf_counter() - t0 < budget_s:
+            oracle.gated_attention(g, inputs)
+            done += 1
+        dt = time.perf_counter() - t0
+        sample = f"{done} full call(s) of {w.name} ({total_rows} query rows each, append included)"
+        tokens = done * tokens_per_call
+    else:
+        rows = np.sort(rng.choice(total_rows, size=max(1, rows_budget), replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        kr, vr = oracle.new_kv(g, inputs["k_new"], inputs["v_new"], inputs["w_k"], inputs["positions"])
+        oracle.attention(g, inputs["q_gate"], inputs["w_q"], inputs["k_cache"], inputs["v_cache"],
+                         inputs["seq_offset"], inputs["seq_lens"], inputs["positions"], kr, vr, rows=rows)
+        dt = time.perf_counter() - t0
+        sample = (f"{len(rows)} of {total_rows} query rows of {w.name} (random, seeded) plus the "
+                  f"full append; scaled by rows")
+        tokens = tokens_per_call * len(rows) / total_rows
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode_4b", choices=sorted(WORKLOADS))
+    ap.add_argument("--launch", default="graph", choices=["graph", "eager"])
+    ap.add_argument("--force-splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sets", type=int, default=None, help="buffer sets to rotate over")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the attention core shards by sequence or KV head without any exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+
+    w = WORKLOADS[args.workload]
+    steps, warm = DEFAULT_STEPS.get(w.name, (100, 10))
+    steps = args.steps if args.steps is not None else steps
+    warm = args.warmup if args.warmup is not None else warm
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    inputs = make_inputs(w)
+    max_seq_len = int((inputs["seq_lens"].max() + w.q_len).item())
+    base = {k: v.to(dev) for k, v in inputs.items()}
+    set_bytes = sum(v.numel() * v.element_size() for v in base.values())
+    sets = args.sets or max(1, min(256, -(-ROTATE_BYTES // set_bytes)))
+    if set_bytes * sets > 64 * (1 << 30):
+        sets = 1
+    stream = torch.cuda.Stream()   # default priority
+    probe = binding.make_cfg(
+        batch=w.batch, q_len=w.q_len, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+        head_dim=w.head_dim, rotary_dim=w.rotary_dim, rope_theta=w.rope_theta, rms_eps=w.rms_eps,
+        dtype=DTYPES[w.dtype], max_seq_len=max_seq_len, q_norm_w=base["w_q"], k_norm_w=base["w_k"],
+        force_splits=args.force_splits, stream=stream)
+    ws_bytes = binding.workspace_size(probe)
+    plan = binding.describe_plan(probe)
+
+    calls = []
+    for i in range(sets):
+        d = base if i == 0 else {k: v.clone() for k, v in base.items()}
+        ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+        c = Call(w, d, ws, max_seq_len, stream)
+        c.cfg.force_splits = args.force_splits
+        calls.append(c)
+    torch.cuda.synchronize()
+
+    with torch.cuda.stream(stream):
+        for i in range(warm):
+            calls[i % sets]()
+    torch.cuda.synchronize()
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if args.launch == "graph":
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(steps):
+                calls[(warm + i) % sets]()
+        torch.cuda.synchronize()
+        t_host = time.perf_counter()
+        with torch.cuda.stream(stream):     # replay() launches on the current stream
+            start.record(stream)
+            graph.replay()
+            end.record(stream)
+        torch.cuda.synchronize()
+        t_host = time.perf_counter() - t_host
+    else:
+        t_host = time.perf_counter()
+        with torch.cuda.stream(stream):
+            start.record(stream)
+            for i in range(steps):
+                calls[(warm + i) % sets]()
+            end.record(stream)
+        torch.cuda.synchronize()
+        t_host = time.perf_counter() - t_host
+    ms = start.elapsed_time(end)
+    errs = [int(c.ws[:4].view(torch.int32).item()) for c in calls]
+    if any(errs):
+        print(f"bench.py: device-side range error flagged: {errs}", file=sys.stderr)
+        sys.exit(1)
+
+    tokens_per_call = w.batch * w.q_len
+    bytes_call, flops_call = algorithmic_work(w, inputs["seq_lens"])
+    s_per_step = ms / 1e3 / steps
+    value = tokens_per_call / s_per_step
+    gbs = bytes_call / s_per_step / 1e9
+    tfs = flops_call / s_per_step / 1e12
+    hbm_bound = w.name != "prefill_4b"
+    traffic = traffic_from_profiles(w.name)
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic}
+    roof["kernel"] = "tiles_bf16_kernel" if w.dtype == "bf16" else "rows_f32_kernel"
+    roof["algorithmic_bytes_per_launch"] = bytes_call
+    roof["algorithmic_flops_per_launch"] = flops_call
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warm, "ms_per_step": round(ms / steps, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1) inputs, norm weights 1+N(0,0.1))",
+        "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len,
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "rotary_dim": w.rotary_dim, "rope_theta": w.rope_theta,
+                   "cached_tokens": int(inputs["seq_lens"].sum()), "buffer_sets": sets,
+                   "launch": "hipgraph" if args.launch == "graph" else "eager", "plan": plan},
+        "effective_gbs": round(gbs, 1), "effective_tflops": round(tfs, 3),
+        "host_wall_s": round(t_host, 4),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inputs, tokens_per_call)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

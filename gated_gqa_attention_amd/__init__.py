@@ -2,17 +2,11 @@
 
 The compute runs in hand-written HIP kernels behind a C ABI (``libqsa.so``,
 declared in ``include/qsa.h``).  This package holds the kernels' sources
-(``csrc/``), the thin ctypes binding (``binding``) and the seeded input
-generators (``workloads``).  Importing the package does not load the library;
-the first call through ``binding`` does, and raises if it has not been built.
+(``csrc/``), the thin ctypes binding (``binding``), device-buffer plumbing
+(``session``) and the seeded input generators (``workloads``).  Importing the
+package does not load the library; the first call through ``binding`` does,
+and raises if it has not been built.
 """
-from . import workloads  # noqa: F401
+from . import binding, workloads  # noqa: F401
 
-__all__ = ["workloads", "binding"]
-
-
-def __getattr__(name):
-    if name == "binding":
-        from . import binding
-        return binding
-    raise AttributeError(name)
+__all__ = ["binding", "workloads"]

@@ -1,0 +1,142 @@
+"""ctypes binding of libqsa.so (declared in include/qsa.h).
+
+Argument marshalling only: tensors become device pointers, the configuration
+becomes a ``qsa_cfg`` struct, negative status codes become ``QSAError``.  Every
+step of the computation runs in the library's HIP kernels; there is no other
+path.  Loading fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsa.so")
+
+QSA_OK, QSA_ERR_INVALID, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE, QSA_ERR_DEVICE = 0, -1, -2, -3, -4
+QSA_BF16, QSA_F32 = 0, 1
+_DT = {torch.bfloat16: QSA_BF16, torch.float32: QSA_F32}
+
+EXPORTS = ("qsa_workspace_size", "qsa_append_kv", "qsa_gated_attention", "qsa_describe_plan",
+           "qsa_last_error")
+
+
+class QSAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"qsa status {code}: {msg}")
+        self.code = code
+
+
+class Cfg(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("q_len", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("rotary_dim", ctypes.c_int32),
+        ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
+        ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32), ("force_splits", ctypes.c_int32),
+        ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+class KVCache(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("seq_offset", ctypes.c_void_p), ("capacity", ctypes.c_void_p),
+        ("num_rows", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libqsa.so once; raise if it is missing (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built: run `python -m gated_gqa_attention_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        p = ctypes.c_void_p
+        lib.qsa_workspace_size.restype = ctypes.c_size_t
+        lib.qsa_workspace_size.argtypes = [ctypes.POINTER(Cfg)]
+        lib.qsa_append_kv.restype = ctypes.c_int
+        lib.qsa_append_kv.argtypes = [p, p, ctypes.POINTER(KVCache), p, p, ctypes.POINTER(Cfg)]
+        lib.qsa_gated_attention.restype = ctypes.c_int
+        lib.qsa_gated_attention.argtypes = [p, p, p, ctypes.POINTER(KVCache), p, p,
+                                            ctypes.POINTER(Cfg), p]
+        lib.qsa_describe_plan.restype = ctypes.c_int
+        lib.qsa_describe_plan.argtypes = [ctypes.POINTER(Cfg), ctypes.c_char_p, ctypes.c_size_t]
+        lib.qsa_last_error.restype = ctypes.c_char_p
+        lib.qsa_last_error.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def last_error() -> str:
+    return load().qsa_last_error().decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _check(rc: int):
+    if rc != QSA_OK:
+        raise QSAError(rc, last_error())
+
+
+def make_cfg(*, batch, q_len, num_q_heads, num_kv_heads, head_dim, rotary_dim, rope_theta,
+             rms_eps, dtype, max_seq_len, q_norm_w=None, k_norm_w=None, workspace=None,
+             softmax_scale=0.0, force_splits=0, stream=None) -> Cfg:
+    """Build a qsa_cfg.  ``dtype`` is a torch dtype; tensors are passed as device pointers."""
+    if stream is None and torch.cuda.is_available():
+        stream = torch.cuda.current_stream()
+    stream_handle = None if stream is None else (stream if isinstance(stream, int) else stream.cuda_stream)
+    return Cfg(batch, q_len, num_q_heads, num_kv_heads, head_dim, rotary_dim, float(rope_theta),
+               float(rms_eps), float(softmax_scale), _DT[dtype] if not isinstance(dtype, int) else dtype,
+               max_seq_len, force_splits, _ptr(q_norm_w), _ptr(k_norm_w), _ptr(workspace),
+               0 if workspace is None else workspace.numel() * workspace.element_size(),
+               stream_handle)
+
+
+def make_kv(k_cache, v_cache, seq_offset, capacity=None) -> KVCache:
+    """Describe a token-major cache: k/v ``[rows, Hkv, D]``, seq_offset int64 ``[B]``."""
+    return KVCache(_ptr(k_cache), _ptr(v_cache), _ptr(seq_offset), _ptr(capacity),
+                   int(k_cache.shape[0]))
+
+
+def workspace_size(cfg: Cfg) -> int:
+    n = load().qsa_workspace_size(ctypes.byref(cfg))
+    if n == 0:
+        raise QSAError(QSA_ERR_INVALID, last_error())
+    return int(n)
+
+
+def describe_plan(cfg: Cfg) -> str:
+    buf = ctypes.create_string_buffer(512)
+    rc = load().qsa_describe_plan(ctypes.byref(cfg), buf, len(buf))
+    if rc < 0:
+        raise QSAError(rc, last_error())
+    return buf.value.decode()
+
+
+def append_kv(cfg: Cfg, kv: KVCache, k_new, v_new, seq_lens, positions) -> None:
+    _check(load().qsa_append_kv(_ptr(k_new), _ptr(v_new), ctypes.byref(kv), _ptr(seq_lens),
+                                _ptr(positions), ctypes.byref(cfg)))
+
+
+def gated_attention(cfg: Cfg, kv: KVCache, q_gate, k_new, v_new, seq_lens, positions, out) -> None:
+    _check(load().qsa_gated_attention(_ptr(q_gate), _ptr(k_new), _ptr(v_new), ctypes.byref(kv),
+                                      _ptr(seq_lens), _ptr(positions), ctypes.byref(cfg), _ptr(out)))

@@ -1,0 +1,304 @@
+// qsa_api.hip -- the C ABI (include/qsa.h): host-side validation, launch
+// planning, workspace sizing and kernel launches.  Nothing here allocates,
+// synchronises or falls back to another path: an unsupported request is an
+// error, as the pages' engines do at admission (mlxd PR #99, Decision R1 and
+// the first reply: reject at load rather than approximate; Atlas
+// Qwen35Kernels::resolve: fail loudly).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/qsa.h"
+#include "qsa_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+enum Route { kRouteF32 = 0, kRouteFused = 1, kRoutePrepared = 2 };
+const char *route_name(int r) {
+  return r == kRouteF32 ? "f32_rows" : r == kRouteFused ? "fused_splitk" : "prepared_tiles";
+}
+
+struct Plan {
+  int route = 0;
+  int rows = 0, tiles = 0, chunks = 1, chunk_keys = 0;
+  int64_t blocks = 0;
+  size_t off_counters = 0, off_ml = 0, off_o = 0, off_qt = 0, total = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int validate_cfg(const qsa_cfg *c) {
+  if (!c) return fail(QSA_ERR_INVALID, "cfg is NULL");
+  if (c->batch < 1 || c->q_len < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1)
+    return fail(QSA_ERR_INVALID, "batch, q_len, num_q_heads and num_kv_heads must be >= 1 (got %d, %d, %d, %d)",
+                c->batch, c->q_len, c->num_q_heads, c->num_kv_heads);
+  if (c->num_q_heads % c->num_kv_heads)
+    return fail(QSA_ERR_INVALID, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)", c->num_q_heads,
+                c->num_kv_heads);
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
+    return fail(QSA_ERR_UNSUPPORTED, "head_dim %d not supported (64 | 128 | 256)", c->head_dim);
+  if (c->rotary_dim < 0 || c->rotary_dim > c->head_dim || (c->rotary_dim & 1))
+    return fail(QSA_ERR_INVALID, "rotary_dim %d must be even and in [0, head_dim=%d]", c->rotary_dim,
+                c->head_dim);
+  if (!(std::isfinite(c->rope_theta) && c->rope_theta > 0.f))
+    return fail(QSA_ERR_INVALID, "rope_theta must be finite and > 0");
+  if (!(std::isfinite(c->rms_eps) && c->rms_eps >= 0.f))
+    return fail(QSA_ERR_INVALID, "rms_eps must be finite and >= 0");
+  if (!(std::isfinite(c->softmax_scale) && c->softmax_scale >= 0.f))
+    return fail(QSA_ERR_INVALID, "softmax_scale must be finite and >= 0 (0 selects 1/sqrt(head_dim))");
+  if (c->dtype != QSA_BF16 && c->dtype != QSA_F32)
+    return fail(QSA_ERR_UNSUPPORTED, "dtype %d not supported (QSA_BF16 | QSA_F32)", c->dtype);
+  if (c->max_seq_len < c->q_len || c->max_seq_len > (1 << 30))
+    return fail(QSA_ERR_INVALID, "max_seq_len %d must be in [q_len=%d, 2^30]", c->max_seq_len, c->q_len);
+  if (c->force_splits < 0) return fail(QSA_ERR_INVALID, "force_splits must be >= 0");
+  if (!c->q_norm_w || !c->k_norm_w) return fail(QSA_ERR_INVALID, "q_norm_w and k_norm_w must be device pointers");
+  return QSA_OK;
+}
+
+int make_plan(const qsa_cfg *c, Plan *pl) {
+  const int64_t B = c->batch, L = c->q_len, Hq = c->num_q_heads, Hkv = c->num_kv_heads, D = c->head_dim;
+  const int64_t G = Hq / Hkv;
+  const int64_t rows_total = L * G;
+  const size_t es = c->dtype == QSA_BF16 ? 2 : 4;
+  Plan p;
+  if (c->dtype == QSA_F32) {
+    p.route = kRouteF32;
+    p.rows = (int)std::min<int64_t>(rows_total, qsa::kTileRows);
+    p.tiles = 1;
+    p.chunks = 1;
+    p.chunk_keys = c->max_seq_len;
+    p.blocks = B * L * Hq;
+  } else {
+    const bool fused = rows_total <= qsa::kTileRows && L <= qsa::kMaxFusedNewRows;
+    p.route = fused ? kRouteFused : kRoutePrepared;
+    p.tiles = (int)cdiv(rows_total, qsa::kTileRows);
+    p.rows = (int)std::min<int64_t>(rows_total, qsa::kTileRows);
+    const int64_t base = B * Hkv * p.tiles;
+    const int64_t max_chunks = cdiv(c->max_seq_len, qsa::kTileKeys);
+    int64_t want = c->force_splits > 0 ? c->force_splits : std::max<int64_t>(1, cdiv(512, base));
+    want = std::min(want, max_chunks);
+    int64_t ck = cdiv(cdiv(c->max_seq_len, want), qsa::kTileKeys) * qsa::kTileKeys;
+    if (c->force_splits == 0) {
+      // keep partials small next to the keys they summarise
+      ck = std::max<int64_t>(ck, cdiv(2 * (int64_t)p.rows, qsa::kTileKeys) * qsa::kTileKeys);
+    }
+    int64_t chunks = cdiv(c->max_seq_len, ck);
+    // the merging workgroup stages chunks x rows softmax statistics in LDS
+    const int64_t lds_cap = 32 * (D + 8);
+    while (chunks > 1 && chunks * p.rows > lds_cap) {
+      ck += qsa::kTileKeys;
+      chunks = cdiv(c->max_seq_len, ck);
+    }
+    p.chunk_keys = (int)ck;
+    p.chunks = (int)chunks;
+    p.blocks = base * chunks;
+  }
+  if (p.blocks > 0x7fffffffLL) return fail(QSA_ERR_UNSUPPORTED, "launch grid too large (%lld workgroups)",
+                                           (long long)p.blocks);
+  const int64_t slots = B * Hkv * p.tiles;
+  size_t off = 256;
+  p.off_counters = off;
+  off = align256(off + (size_t)slots * 4);
+  if (p.chunks > 1) {
+    p.off_ml = off;
+    off = align256(off + (size_t)slots * p.chunks * p.rows * 2 * 4);
+    p.off_o = off;
+    off = align256(off + (size_t)slots * p.chunks * p.rows * D * 4);
+  }
+  if (p.route != kRouteFused) {
+    p.off_qt = off;
+    off = align256(off + (size_t)(B * L * Hq * D) * es);
+  }
+  p.total = off;
+  *pl = p;
+  return QSA_OK;
+}
+
+qsa::Params base_params(const qsa_cfg *c, const Plan &pl) {
+  qsa::Params p{};
+  p.B = c->batch;
+  p.L = c->q_len;
+  p.Hq = c->num_q_heads;
+  p.Hkv = c->num_kv_heads;
+  p.G = p.Hq / p.Hkv;
+  p.D = c->head_dim;
+  p.r = c->rotary_dim;
+  p.rows = pl.rows;
+  p.tiles = pl.tiles;
+  p.chunks = pl.chunks;
+  p.chunk_keys = pl.chunk_keys;
+  p.max_seq_len = c->max_seq_len;
+  p.eps = c->rms_eps;
+  p.scale = c->softmax_scale > 0.f ? c->softmax_scale : (float)(1.0 / std::sqrt((double)c->head_dim));
+  p.scale_log2 = p.scale * qsa::kLog2e;
+  p.theta = (double)c->rope_theta;
+  p.wq = c->q_norm_w;
+  p.wk = c->k_norm_w;
+  return p;
+}
+
+int check_device() {
+  static std::once_flag once;
+  static int status = QSA_OK;
+  static std::string msg;
+  std::call_once(once, [] {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      status = QSA_ERR_DEVICE;
+      msg = "no HIP device available";
+      return;
+    }
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+      status = QSA_ERR_DEVICE;
+      msg = std::string("device is ") + prop.gcnArchName + ", this library is built for gfx950 only";
+    }
+  });
+  if (status != QSA_OK) return fail(status, "%s", msg.c_str());
+  return QSA_OK;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b) return false;
+  const char *pa = (const char *)a, *pb = (const char *)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+int check_kv(const qsa_kv_cache *kv) {
+  if (!kv) return fail(QSA_ERR_INVALID, "kv cache descriptor is NULL");
+  if (!kv->k || !kv->v || !kv->seq_offset) return fail(QSA_ERR_INVALID, "kv->k, kv->v and kv->seq_offset are required");
+  if (kv->num_rows < 1) return fail(QSA_ERR_INVALID, "kv->num_rows must be >= 1");
+  if (kv->k == kv->v) return fail(QSA_ERR_INVALID, "kv->k and kv->v must be different buffers");
+  return QSA_OK;
+}
+
+void fill_kv(qsa::Params &p, const qsa_kv_cache *kv, const int32_t *seq_lens, const int32_t *positions) {
+  p.kc = kv->k;
+  p.vc = kv->v;
+  p.seq_offset = kv->seq_offset;
+  p.capacity = kv->capacity;
+  p.num_rows = kv->num_rows;
+  p.seq_lens = seq_lens;
+  p.positions = positions;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qsa_last_error(void) { return g_err.c_str(); }
+
+size_t qsa_workspace_size(const qsa_cfg *cfg) {
+  if (validate_cfg(cfg) != QSA_OK) return 0;
+  Plan pl;
+  if (make_plan(cfg, &pl) != QSA_OK) return 0;
+  return pl.total;
+}
+
+int qsa_describe_plan(const qsa_cfg *cfg, char *buf, size_t len) {
+  int rc = validate_cfg(cfg);
+  if (rc != QSA_OK) return rc;
+  Plan pl;
+  if ((rc = make_plan(cfg, &pl)) != QSA_OK) return rc;
+  return snprintf(buf, len,
+                  "route=%s rows=%d tiles=%d chunks=%d chunk_keys=%d workgroups=%lld threads=%d "
+                  "workspace=%zu",
+                  route_name(pl.route), pl.rows, pl.tiles, pl.chunks, pl.chunk_keys, (long long)pl.blocks,
+                  qsa::kThreads, pl.total);
+}
+
+int qsa_append_kv(const void *k_new, const void *v_new, const qsa_kv_cache *kv, const int32_t *seq_lens,
+                  const int32_t *positions, const qsa_cfg *cfg) {
+  int rc = validate_cfg(cfg);
+  if (rc != QSA_OK) return rc;
+  if ((rc = check_kv(kv)) != QSA_OK) return rc;
+  if (!k_new || !v_new || !seq_lens || !positions)
+    return fail(QSA_ERR_INVALID, "k_new, v_new, seq_lens and positions are required");
+  if ((rc = check_device()) != QSA_OK) return rc;
+  Plan pl;
+  if ((rc = make_plan(cfg, &pl)) != QSA_OK) return rc;
+  qsa::Params p = base_params(cfg, pl);
+  fill_kv(p, kv, seq_lens, positions);
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.err = cfg->workspace ? (int32_t *)cfg->workspace : nullptr;
+  hipError_t e = qsa::launch_prologue(p, cfg->dtype, false, true, (hipStream_t)cfg->stream);
+  if (e != hipSuccess) return fail(QSA_ERR_DEVICE, "append launch failed: %s", hipGetErrorString(e));
+  return QSA_OK;
+}
+
+int qsa_gated_attention(const void *q_gate, const void *k_new, const void *v_new, const qsa_kv_cache *kv,
+                        const int32_t *seq_lens, const int32_t *positions, const qsa_cfg *cfg, void *out) {
+  int rc = validate_cfg(cfg);
+  if (rc != QSA_OK) return rc;
+  if ((rc = check_kv(kv)) != QSA_OK) return rc;
+  if (!q_gate || !seq_lens || !positions || !out)
+    return fail(QSA_ERR_INVALID, "q_gate, seq_lens, positions and out are required");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(QSA_ERR_INVALID, "k_new and v_new must both be given or both be NULL");
+  const size_t es = cfg->dtype == QSA_BF16 ? 2 : 4;
+  const size_t nrow = (size_t)cfg->batch * cfg->q_len;
+  const size_t out_bytes = nrow * cfg->num_q_heads * cfg->head_dim * es;
+  const size_t kv_bytes = (size_t)kv->num_rows * cfg->num_kv_heads * cfg->head_dim * es;
+  const size_t new_bytes = nrow * cfg->num_kv_heads * cfg->head_dim * es;
+  if (overlaps(out, out_bytes, q_gate, 2 * out_bytes) || overlaps(out, out_bytes, k_new, new_bytes) ||
+      overlaps(out, out_bytes, v_new, new_bytes) || overlaps(out, out_bytes, kv->k, kv_bytes) ||
+      overlaps(out, out_bytes, kv->v, kv_bytes))
+    return fail(QSA_ERR_INVALID, "out must not alias q_gate, k_new, v_new or the cache");
+  Plan pl;
+  if ((rc = make_plan(cfg, &pl)) != QSA_OK) return rc;
+  if (!cfg->workspace || cfg->workspace_bytes < pl.total)
+    return fail(QSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.total,
+                cfg->workspace ? cfg->workspace_bytes : (size_t)0);
+  if ((rc = check_device()) != QSA_OK) return rc;
+
+  qsa::Params p = base_params(cfg, pl);
+  fill_kv(p, kv, seq_lens, positions);
+  p.q_gate = q_gate;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.out = out;
+  char *ws = (char *)cfg->workspace;
+  p.err = (int32_t *)ws;
+  p.counters = (int32_t *)(ws + pl.off_counters);
+  p.part_ml = pl.off_ml ? (float *)(ws + pl.off_ml) : nullptr;
+  p.part_o = pl.off_o ? (float *)(ws + pl.off_o) : nullptr;
+  p.qt = pl.off_qt ? (void *)(ws + pl.off_qt) : nullptr;
+  hipStream_t s = (hipStream_t)cfg->stream;
+  const bool has_new = k_new != nullptr;
+
+  hipError_t e = hipSuccess;
+  switch (pl.route) {
+    case kRouteF32:
+      e = qsa::launch_prologue(p, QSA_F32, true, has_new, s);
+      if (e == hipSuccess) e = qsa::launch_rows_f32(p, s);
+      break;
+    case kRouteFused:
+      e = qsa::launch_tiles_bf16(p, false, s);
+      break;
+    default:
+      e = qsa::launch_prologue(p, QSA_BF16, true, has_new, s);
+      if (e == hipSuccess) e = qsa::launch_tiles_bf16(p, true, s);
+      break;
+  }
+  if (e != hipSuccess) return fail(QSA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+  return QSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+// qsa_internal.h -- launch parameters and device helpers shared by the HIP kernels.
+//
+// Target: AMD CDNA4 (gfx950), 64-wide wavefronts, MFMA bf16 16x16x32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qsa {
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;   // four wavefronts per workgroup
+constexpr int kWave = 64;
+constexpr int kTileKeys = 64;   // keys staged in LDS per pipeline stage
+constexpr int kTileRows = 64;   // query rows (group heads x new rows) per workgroup
+constexpr int kMaxFusedNewRows = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Workspace layout (bytes, all offsets 256-aligned):
+//   [0, 256)                 header; int32 at 0 = sticky device error bits
+//   counters                 int32 [slots]          arrival tickets, left at zero
+//   part_ml                  float [slots][S][rows][2]
+//   part_o                   float [slots][S][rows][D]
+//   qt                       prepared queries [B][L][Hq][D] (bf16 or fp32)
+// where slots = B * Hkv * tiles, S = chunks, rows = rows per tile.
+constexpr int32_t kErrRange = 1;
+
+struct Params {
+  int B, L, Hq, Hkv, G, D, r;
+  int rows;           // query rows per tile (<= kTileRows)
+  int tiles;          // row tiles per (sequence, KV head)
+  int chunks;         // key chunks per (sequence, KV head, tile) planned for max_seq_len
+  int chunk_keys;     // keys per chunk, a multiple of kTileKeys
+  int max_seq_len;
+  float eps;
+  float scale_log2;   // softmax scale * log2(e)
+  float scale;        // softmax scale
+  double theta;
+  const void *q_gate;
+  const void *k_new;
+  const void *v_new;
+  void *kc;
+  void *vc;
+  const int64_t *seq_offset;
+  const int32_t *capacity;  // may be null
+  int64_t num_rows;
+  const int32_t *seq_lens;
+  const int32_t *positions;
+  const void *wq;
+  const void *wk;
+  void *out;
+  int32_t *err;       // may be null
+  int32_t *counters;
+  float *part_ml;
+  float *part_o;
+  void *qt;
+};
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16_t x) { return (float)x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f(float x);
+template <>
+__device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16_t from_f<bf16_t>(float x) { return (bf16_t)x; }  // v_cvt_pk_bf16_f32: nearest-even
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+// Rotation angle of pair i at position pos: pos * theta^(-2i/r), evaluated in
+// double (positions reach 3e4 rad at the first pair), then cos/sin rounded to fp32.
+__device__ __forceinline__ void rope_cs(int pos, int i, int r, double theta, float &c, float &s) {
+  const double a = (double)pos * pow(theta, -2.0 * (double)i / (double)r);
+  double sd, cd;
+  sincos(a, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}
+
+// Sequence bounds check shared by the kernels.  Returns false (and flags the
+// error) when rows [0, total) of sequence b would leave the cache.
+__device__ __forceinline__ bool seq_in_range(const Params &p, int b, int n, int64_t &off) {
+  off = p.seq_offset[b];
+  const int64_t total = (int64_t)n + p.L;
+  bool ok = n >= 0 && off >= 0 && total <= p.max_seq_len && off + total <= p.num_rows;
+  if (ok && p.capacity) ok = total <= (int64_t)p.capacity[b];
+  return ok;
+}
+
+__device__ __forceinline__ void flag_error(const Params &p) {
+  if (p.err) atomicOr(p.err, kErrRange);
+}
+
+// --------------------------------------------------------------- launchers
+// (defined in the kernel translation units, called by the C ABI layer)
+hipError_t launch_prologue(const Params &p, int dtype, bool do_q, bool do_kv, hipStream_t s);
+hipError_t launch_rows_f32(const Params &p, hipStream_t s);
+hipError_t launch_tiles_bf16(const Params &p, bool prepared_q, hipStream_t s);
+
+}  // namespace qsa

@@ -1,0 +1,225 @@
+// qsa_rows.hip -- row-wise kernels: the prologue (norm + partial rotation of new
+// keys and/or queries, KV append) and the fp32 attention path.
+//
+// Norm: x * w / sqrt(mean(x^2) + eps) per head (mlxd PR #99 config audit,
+// has_qk_norm; Atlas FullAttentionLayer q_norm / k_norm).  Rotation: first
+// rotary_dim dims, dim i paired with i + rotary_dim/2 (mlxd PR #99 Summary,
+// partial_rotary_factor; Atlas Qwen35ForwardConfig::rotary_dim).  Append at
+// slot seq_lens[b] + l (Atlas qwen3_5/mod.rs module doc).
+#include "qsa_internal.h"
+
+namespace qsa {
+
+// One wavefront per head-row; EPL = D/64 contiguous elements per lane.
+// Jobs [0, nk) are key rows (b, l, kvh): normalised, rotated, rounded and
+// written with the matching value row to the cache.  Jobs [nk, nk+nq) are
+// query rows (b, l, h): normalised and rotated into the prepared-query
+// buffer p.qt (element type TQ).
+template <typename T, typename TQ, int D>
+__global__ __launch_bounds__(kThreads) void prologue_kernel(Params p, int do_q, int do_kv) {
+  constexpr int EPL = D / kWave;
+  __shared__ float scratch[kThreads / kWave][D];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t nk = do_kv ? (int64_t)p.B * p.L * p.Hkv : 0;
+  const int64_t nq = do_q ? (int64_t)p.B * p.L * p.Hq : 0;
+  const int64_t job = (int64_t)blockIdx.x * (kThreads / kWave) + wave;
+  const bool active = job < nk + nq;
+  const bool is_k = job < nk;
+
+  int64_t bl = 0;
+  int head = 0;
+  const T *src = nullptr;
+  const T *w = nullptr;
+  if (active) {
+    if (is_k) {
+      head = (int)(job % p.Hkv);
+      bl = job / p.Hkv;
+      src = (const T *)p.k_new + (bl * p.Hkv + head) * D;
+      w = (const T *)p.wk;
+    } else {
+      const int64_t j = job - nk;
+      head = (int)(j % p.Hq);
+      bl = j / p.Hq;
+      src = (const T *)p.q_gate + (bl * p.Hq + head) * 2 * D;  // query half of [q | gate]
+      w = (const T *)p.wq;
+    }
+  }
+  float x[EPL];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    x[j] = active ? to_f(src[lane * EPL + j]) : 0.f;
+    ss += x[j] * x[j];
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)D + p.eps);
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const float wj = active ? to_f(w[lane * EPL + j]) : 0.f;
+    x[j] = x[j] * inv * wj;
+    scratch[wave][lane * EPL + j] = x[j];
+  }
+  __syncthreads();
+  if (active && p.r > 0) {
+    const int half = p.r / 2;
+    const int pos = p.positions[bl];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane * EPL + j;
+      if (e < p.r) {
+        const int i = e < half ? e : e - half;
+        float c, s;
+        rope_cs(pos, i, p.r, p.theta, c, s);
+        const float other = scratch[wave][e < half ? e + half : e - half];
+        x[j] = e < half ? x[j] * c - other * s : x[j] * c + other * s;
+      }
+    }
+  }
+  if (!active) return;
+
+  const int b = (int)(bl / p.L), l = (int)(bl % p.L);
+  if (is_k) {
+    const int n = p.seq_lens[b];
+    int64_t off;
+    if (!seq_in_range(p, b, n, off)) {
+      if (lane == 0) flag_error(p);
+      return;
+    }
+    const int64_t dst = ((off + n + l) * p.Hkv + head) * D;
+    const T *vsrc = (const T *)p.v_new + (bl * p.Hkv + head) * D;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane * EPL + j;
+      ((T *)p.kc)[dst + e] = from_f<T>(x[j]);
+      ((T *)p.vc)[dst + e] = vsrc[e];
+    }
+  } else {
+    TQ *dst = (TQ *)p.qt + (bl * p.Hq + head) * D;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) dst[lane * EPL + j] = from_f<TQ>(x[j]);
+  }
+}
+
+// fp32 attention: one workgroup per query row (b, l, h), plain two-pass softmax
+// over keys 0 .. n_b + l of KV head h / G, reading the prepared query from p.qt.
+template <int D>
+__global__ __launch_bounds__(kThreads) void rows_f32_kernel(Params p) {
+  __shared__ float q[D];
+  __shared__ float pbuf[kThreads];
+  __shared__ float red_m[kThreads / kWave], red_s[kThreads / kWave];
+  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
+  const int64_t f = blockIdx.x;
+  const int h = (int)(f % p.Hq);
+  const int64_t bl = f / p.Hq;
+  const int l = (int)(bl % p.L), b = (int)(bl / p.L);
+  const int g = h / p.G;
+  float *out = (float *)p.out + f * D;
+  const int n = p.seq_lens[b];
+  int64_t off;
+  if (!seq_in_range(p, b, n, off)) {
+    if (t < D) out[t] = __builtin_nanf("");
+    if (t == 0) flag_error(p);
+    return;
+  }
+  if (t < D) q[t] = ((const float *)p.qt)[f * D + t];
+  __syncthreads();
+  const float *K = (const float *)p.kc;
+  const float *V = (const float *)p.vc;
+  const int64_t total = (int64_t)n + l + 1;
+
+  auto score = [&](int64_t j) {
+    const float *kr = K + ((off + j) * p.Hkv + g) * D;
+    float acc = 0.f;
+    for (int d = 0; d < D; ++d) acc += q[d] * kr[d];
+    return acc * p.scale;
+  };
+
+  // pass 1: max and normaliser
+  float m = -INFINITY, s = 0.f;
+  for (int64_t j = t; j < total; j += kThreads) {
+    const float sc = score(j);
+    if (sc > m) {
+      s = s * expf(m - sc) + 1.f;
+      m = sc;
+    } else {
+      s += expf(sc - m);
+    }
+  }
+  const float mw = wave_max(m);
+  s = (s > 0.f) ? s * expf(m - mw) : 0.f;
+  s = wave_sum(s);
+  if (lane == 0) {
+    red_m[wave] = mw;
+    red_s[wave] = s;
+  }
+  __syncthreads();
+  float M = red_m[0];
+  for (int w = 1; w < kThreads / kWave; ++w) M = fmaxf(M, red_m[w]);
+  float S = 0.f;
+  for (int w = 0; w < kThreads / kWave; ++w)
+    if (red_s[w] > 0.f) S += red_s[w] * expf(red_m[w] - M);
+
+  // pass 2: weighted values
+  float acc = 0.f;
+  for (int64_t base = 0; base < total; base += kThreads) {
+    const int64_t j = base + t;
+    pbuf[t] = j < total ? expf(score(j) - M) / S : 0.f;
+    __syncthreads();
+    if (t < D) {
+      const int64_t cnt = min((int64_t)kThreads, total - base);
+      for (int64_t k = 0; k < cnt; ++k) acc += pbuf[k] * V[((off + base + k) * p.Hkv + g) * D + t];
+    }
+    __syncthreads();
+  }
+  if (t < D) {
+    const float z = ((const float *)p.q_gate)[f * 2 * D + D + t];
+    out[t] = acc / (1.f + expf(-z));
+  }
+}
+
+template <typename T, typename TQ>
+static hipError_t prologue_for(const Params &p, bool do_q, bool do_kv, hipStream_t s) {
+  const int64_t jobs = (do_kv ? (int64_t)p.B * p.L * p.Hkv : 0) + (do_q ? (int64_t)p.B * p.L * p.Hq : 0);
+  if (jobs == 0) return hipSuccess;
+  const int64_t blocks = (jobs + 3) / 4;
+  switch (p.D) {
+    case 64:
+      hipLaunchKernelGGL((prologue_kernel<T, TQ, 64>), dim3(blocks), dim3(kThreads), 0, s, p, (int)do_q, (int)do_kv);
+      break;
+    case 128:
+      hipLaunchKernelGGL((prologue_kernel<T, TQ, 128>), dim3(blocks), dim3(kThreads), 0, s, p, (int)do_q, (int)do_kv);
+      break;
+    case 256:
+      hipLaunchKernelGGL((prologue_kernel<T, TQ, 256>), dim3(blocks), dim3(kThreads), 0, s, p, (int)do_q, (int)do_kv);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prologue(const Params &p, int dtype, bool do_q, bool do_kv, hipStream_t s) {
+  // bf16 path prepares bf16 queries (MFMA operands); fp32 path keeps fp32
+  return dtype == 0 ? prologue_for<bf16_t, bf16_t>(p, do_q, do_kv, s)
+                    : prologue_for<float, float>(p, do_q, do_kv, s);
+}
+
+hipError_t launch_rows_f32(const Params &p, hipStream_t s) {
+  const int64_t blocks = (int64_t)p.B * p.L * p.Hq;
+  switch (p.D) {
+    case 64:
+      hipLaunchKernelGGL((rows_f32_kernel<64>), dim3(blocks), dim3(kThreads), 0, s, p);
+      break;
+    case 128:
+      hipLaunchKernelGGL((rows_f32_kernel<128>), dim3(blocks), dim3(kThreads), 0, s, p);
+      break;
+    case 256:
+      hipLaunchKernelGGL((rows_f32_kernel<256>), dim3(blocks), dim3(kThreads), 0, s, p);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qsa

@@ -1,0 +1,54 @@
+"""Device-side set-up for one layer call: inputs on the GPU, workspace, output,
+``qsa_cfg`` and ``qsa_kv_cache``.  Plumbing only; the call itself is one
+``qsa_gated_attention`` through the C ABI."""
+from __future__ import annotations
+
+import torch
+
+from . import binding
+from .workloads import DTYPES, Workload
+
+
+class Session:
+    def __init__(self, w: Workload, inputs: dict, device="cuda", force_splits: int = 0,
+                 max_seq_len: int | None = None, stream=None):
+        self.w = w
+        self.dev = {k: v.to(device) if isinstance(v, torch.Tensor) else v for k, v in inputs.items()}
+        d = self.dev
+        if max_seq_len is None:
+            max_seq_len = int((inputs["seq_lens"].max() + w.q_len).item())
+        self.dtype = DTYPES[w.dtype]
+        self.max_seq_len = max_seq_len
+        self.force_splits = force_splits
+        self.stream = stream
+        probe = self._cfg(None)
+        nbytes = binding.workspace_size(probe)
+        self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        self.out = torch.empty((w.batch, w.q_len, w.num_q_heads, w.head_dim), dtype=self.dtype,
+                               device=device)
+        self.cfg = self._cfg(self.workspace)
+        self.kv = binding.make_kv(d["k_cache"], d["v_cache"], d["seq_offset"], d["capacity"])
+
+    def _cfg(self, workspace):
+        w, d = self.w, self.dev
+        return binding.make_cfg(
+            batch=w.batch, q_len=w.q_len, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+            head_dim=w.head_dim, rotary_dim=w.rotary_dim, rope_theta=w.rope_theta, rms_eps=w.rms_eps,
+            dtype=self.dtype, max_seq_len=self.max_seq_len, q_norm_w=d["w_q"], k_norm_w=d["w_k"],
+            workspace=workspace, force_splits=self.force_splits, stream=self.stream)
+
+    def plan(self) -> str:
+        return binding.describe_plan(self.cfg)
+
+    def run(self, fused: bool = True):
+        d = self.dev
+        binding.gated_attention(self.cfg, self.kv, d["q_gate"], d["k_new"] if fused else None,
+                                d["v_new"] if fused else None, d["seq_lens"], d["positions"], self.out)
+        return self.out
+
+    def append(self):
+        d = self.dev
+        binding.append_kv(self.cfg, self.kv, d["k_new"], d["v_new"], d["seq_lens"], d["positions"])
+
+    def device_error(self) -> int:
+        return int(self.workspace[:4].view(torch.int32).item())

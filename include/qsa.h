@@ -1,0 +1,150 @@
+/*
+ * qsa.h -- C ABI of the gated grouped-query attention core for AMD MI355X (gfx950).
+ *
+ * The operation is the full-attention core of a Qwen3.5 decoder layer:
+ *
+ *   1. split the doubled q_proj output of every query head into a query half
+ *      and a gate half (mlxd PR #99 "stage D6", Summary: doubled q_proj, split
+ *      into queries and gate, o_proj(attn * sigmoid(gate)); Atlas
+ *      spark_model/forward/qwen3_5/mod.rs, Qwen35ForwardConfig::q_total);
+ *   2. RMS-normalise every query head and every new key head over head_dim and
+ *      scale by a [head_dim] weight (mlxd PR #99, config audit table,
+ *      has_qk_norm; Atlas FullAttentionLayer q_norm / k_norm);
+ *   3. rotate only the first rotary_dim dims of query and key (partial RoPE;
+ *      mlxd PR #99 Summary, partial_rotary_factor; Atlas
+ *      Qwen35ForwardConfig::rotary_dim);
+ *   4. append the rotated keys and the values of the new rows to the KV cache
+ *      at slot seq_lens[b] + l, then attend over keys 0 .. seq_lens[b] + l
+ *      (Atlas qwen3_5/mod.rs module doc: KV append at cache_pos, attention at
+ *      cache_pos + 1);
+ *   5. grouped-query softmax attention, the query heads of KV head g being the
+ *      contiguous group g*G .. g*G+G-1, G = num_q_heads / num_kv_heads
+ *      (DS4Server issue #113, Reproduction: query heads divided within their
+ *      KV groups; Atlas Qwen35ForwardConfig: 16 query / 4 KV heads);
+ *   6. multiply by sigmoid(gate) (mlxd PR #99 Summary; Atlas sigmoid_gate).
+ *
+ * Conventions fixed by this interface where the pages leave them open:
+ *   - per head the q_proj output is [query(D) | gate(D)] (head-blocked halves);
+ *   - RMS norm: x * w / sqrt(mean(x^2) + eps), with the weight w applied as
+ *     given (a checkpoint that stores zero-centred weights passes 1 + w);
+ *   - rotation pairs dim i with dim i + rotary_dim/2, angle
+ *     position * rope_theta^(-2i/rotary_dim); rotary_dim = 0 disables it;
+ *   - softmax scale 1/sqrt(head_dim) unless softmax_scale is set;
+ *   - the cache stores K after norm and rotation and V as given, rounded to the
+ *     storage dtype (round to nearest even);
+ *   - new row l of a call sees new rows 0 .. l (causal by row order).
+ *
+ * Memory and ownership.  Every buffer is device memory allocated and owned by
+ * the caller: inputs, the KV cache, the output and the workspace.  The
+ * library allocates nothing, never synchronises, and launches all work on
+ * cfg->stream; calls return as soon as the work is queued.  The library owns
+ * only its code objects.  seq_lens is never advanced by the library: the
+ * caller owns the cache position.
+ *
+ * Errors.  Every entry point validates its arguments on the host before any
+ * launch and returns a negative qsa_status on failure, with a message for the
+ * calling thread in qsa_last_error().  Nothing falls back to another path.
+ * Values that live on the device (seq_lens, seq_offset, capacity) are checked
+ * by the kernels: a sequence whose rows would leave the cache, exceed its
+ * capacity or exceed cfg->max_seq_len gets NaN outputs, its cache is not
+ * written, and bit 0 of the int32 at the start of the workspace is set
+ * (sticky until the caller clears it).
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QSA_OK = 0,
+  QSA_ERR_INVALID = -1,      /* malformed argument (NULL pointer, bad size, odd rotary_dim, ...) */
+  QSA_ERR_UNSUPPORTED = -2,  /* well-formed but not supported (head_dim, dtype, group size) */
+  QSA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than qsa_workspace_size() */
+  QSA_ERR_DEVICE = -4        /* a HIP launch failed, or the device is not gfx950 */
+} qsa_status;
+
+typedef enum {
+  QSA_BF16 = 0,              /* bfloat16 activations, cache, norm weights and output; fp32 accumulation */
+  QSA_F32 = 1                /* fp32 everywhere */
+} qsa_dtype;
+
+/* One call's shape, numerics and execution context. */
+typedef struct {
+  int32_t batch;             /* B >= 1 sequences */
+  int32_t q_len;             /* L >= 1 new rows per sequence */
+  int32_t num_q_heads;       /* Hq >= 1 */
+  int32_t num_kv_heads;      /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;          /* D: 64, 128 or 256 */
+  int32_t rotary_dim;        /* r: even, 0 <= r <= D; 0 = no rotation */
+  float rope_theta;          /* theta > 0 */
+  float rms_eps;             /* eps >= 0, added to mean(x^2) inside the square root */
+  float softmax_scale;       /* > 0, or 0 for 1/sqrt(D) */
+  int32_t dtype;             /* qsa_dtype */
+  int32_t max_seq_len;       /* host bound: seq_lens[b] + q_len <= max_seq_len for every b */
+  int32_t force_splits;      /* 0 = automatic; k > 0 plans k key chunks for max_seq_len (tests) */
+  const void *q_norm_w;      /* device [D] query norm weight, in dtype */
+  const void *k_norm_w;      /* device [D] key norm weight, in dtype */
+  void *workspace;           /* device scratch, zero-filled before its first use */
+  size_t workspace_bytes;    /* >= qsa_workspace_size(cfg) */
+  void *stream;              /* hipStream_t to launch on; NULL = the null stream */
+} qsa_cfg;
+
+/* KV cache of one attention layer.  Token-major: row t of sequence b is
+ * [num_kv_heads][head_dim] elements of cfg->dtype at element offset
+ * (seq_offset[b] + t) * num_kv_heads * head_dim of k (and of v).  Sequences may
+ * be packed back to back (ragged batches) or strided uniformly. */
+typedef struct {
+  void *k;                   /* device base of the K rows */
+  void *v;                   /* device base of the V rows */
+  const int64_t *seq_offset; /* device [B]: first row of sequence b (64-bit: caches may exceed 2^31 elements) */
+  const int32_t *capacity;   /* device [B]: rows owned by sequence b, or NULL for "up to num_rows" */
+  int64_t num_rows;          /* host: rows allocated in k and in v */
+} qsa_kv_cache;
+
+/* Bytes of workspace a call with this cfg needs (split-K partials, arrival
+ * counters, the prepared queries of long calls and a 256-byte header).  The
+ * workspace must be zero-filled once before its first use; every call leaves
+ * its counters at zero again.  Calls that share a workspace must be ordered
+ * on one stream.  Returns 0 if cfg is invalid (see qsa_last_error()). */
+size_t qsa_workspace_size(const qsa_cfg *cfg);
+
+/* Steps 2-4 for the keys only: normalise and rotate k_new, round, and write it
+ * with v_new to rows seq_lens[b] + l of the cache.
+ *   k_new, v_new : device [B][L][Hkv][D] in cfg->dtype (raw k_proj / v_proj outputs)
+ *   seq_lens     : device [B] int32, cached rows before this call
+ *   positions    : device [B][L] int32, rotary positions of the new rows
+ * cfg->workspace may be NULL here (then device-side range errors only skip
+ * the write).  Returns a qsa_status. */
+int qsa_append_kv(const void *k_new, const void *v_new, const qsa_kv_cache *kv,
+                  const int32_t *seq_lens, const int32_t *positions, const qsa_cfg *cfg);
+
+/* Steps 1-6.  Equivalent to qsa_append_kv followed by gated attention over the
+ * cache.
+ *   q_gate       : device [B][L][Hq][2D], per head [query | gate]
+ *   k_new, v_new : device [B][L][Hkv][D]; both NULL when the new rows are
+ *                  already in the cache (then the cache is only read)
+ *   seq_lens     : device [B] int32, cached rows before this call
+ *   positions    : device [B][L] int32, rotary positions of the new rows
+ *   out          : device [B][L][Hq][D] in cfg->dtype; must not alias any input
+ * Returns a qsa_status. */
+int qsa_gated_attention(const void *q_gate, const void *k_new, const void *v_new,
+                        const qsa_kv_cache *kv, const int32_t *seq_lens,
+                        const int32_t *positions, const qsa_cfg *cfg, void *out);
+
+/* Human-readable launch plan for cfg (route, chunking, grid), written to buf.
+ * Returns the number of characters the full text needs, or a negative
+ * qsa_status if cfg is invalid. */
+int qsa_describe_plan(const qsa_cfg *cfg, char *buf, size_t buf_len);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char *qsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

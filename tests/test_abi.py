@@ -1,0 +1,119 @@
+"""The C ABI on the host (no GPU): the library loads, exports every entry point
+that include/qsa.h declares, rejects malformed calls before any launch, sizes
+workspaces and picks the documented route for each workload."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from gated_gqa_attention_amd import binding
+from gated_gqa_attention_amd.workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7f0000000000   # never dereferenced: every case below fails validation first
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "qsa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(qsa_\w+)\s*\(", text, re.M)))
+
+
+def cfg_for(w, **kw):
+    args = dict(batch=w.batch, q_len=w.q_len, num_q_heads=w.num_q_heads,
+                num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, rotary_dim=w.rotary_dim,
+                rope_theta=w.rope_theta, rms_eps=w.rms_eps,
+                dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32,
+                max_seq_len=(w.ragged[1] if w.ragged else w.prior) + w.q_len,
+                q_norm_w=FAKE, k_norm_w=FAKE)
+    args.update(kw)
+    return binding.make_cfg(**args)
+
+
+def test_library_exports_every_declared_entry_point():
+    lib = binding.load()
+    declared = header_functions()
+    assert set(binding.EXPORTS) <= set(declared)
+    assert len(declared) >= 5
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_library_is_gfx950_code_object():
+    data = open(binding.library_path(), "rb").read()
+    assert b"gfx950" in data
+
+
+@pytest.mark.parametrize("name,route", [("tiny_f32", "f32_rows"), ("decode_4b", "fused_splitk"),
+                                        ("verify_24x2", "fused_splitk"), ("ragged_4b", "fused_splitk"),
+                                        ("prefill_4b", "prepared_tiles")])
+def test_route_per_workload(name, route):
+    plan = binding.describe_plan(cfg_for(WORKLOADS[name]))
+    assert f"route={route}" in plan
+    fields = dict(kv.split("=") for kv in plan.split())
+    assert int(fields["workspace"]) == binding.workspace_size(cfg_for(WORKLOADS[name]))
+
+
+def test_plan_covers_max_seq_len_and_forced_splits():
+    w = WORKLOADS["decode_4b"]
+    for k in (1, 2, 7, 65):
+        f = dict(kv.split("=") for kv in binding.describe_plan(cfg_for(w, force_splits=k)).split())
+        assert int(f["chunks"]) * int(f["chunk_keys"]) >= 4097
+        assert int(f["chunk_keys"]) % 64 == 0
+        assert int(f["chunks"]) <= k or int(f["chunk_keys"]) == 64
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(num_q_heads=6, num_kv_heads=4), binding.QSA_ERR_INVALID),
+    (dict(rotary_dim=63), binding.QSA_ERR_INVALID),
+    (dict(rotary_dim=258), binding.QSA_ERR_INVALID),
+    (dict(head_dim=96, rotary_dim=32), binding.QSA_ERR_UNSUPPORTED),
+    (dict(dtype=7), binding.QSA_ERR_UNSUPPORTED),
+    (dict(max_seq_len=0), binding.QSA_ERR_INVALID),
+    (dict(q_len=0), binding.QSA_ERR_INVALID),
+    (dict(rope_theta=-1.0), binding.QSA_ERR_INVALID),
+    (dict(rms_eps=float("nan")), binding.QSA_ERR_INVALID),
+    (dict(q_norm_w=None), binding.QSA_ERR_INVALID),
+    (dict(force_splits=-2), binding.QSA_ERR_INVALID),
+])
+def test_invalid_configurations_are_rejected(bad, code):
+    cfg = cfg_for(WORKLOADS["decode_4b"], **bad)
+    lib = binding.load()
+    assert lib.qsa_workspace_size(ctypes.byref(cfg)) == 0
+    assert binding.last_error() != ""
+    kv = binding.KVCache(FAKE, FAKE + (1 << 30), FAKE, None, 8192)
+    rc = lib.qsa_gated_attention(FAKE, None, None, ctypes.byref(kv), FAKE, FAKE, ctypes.byref(cfg),
+                                 FAKE + (2 << 30))
+    assert rc == code, binding.last_error()
+
+
+def test_argument_errors_before_launch():
+    w = WORKLOADS["decode_4b"]
+    lib = binding.load()
+    kv = binding.KVCache(FAKE, FAKE + (1 << 30), FAKE, None, 8192)
+    need = binding.workspace_size(cfg_for(w))
+    small = cfg_for(w)
+    small.workspace, small.workspace_bytes = FAKE + (3 << 30), need - 1
+    out = FAKE + (2 << 30)
+    call = lambda q, k, v, kvd, sl, pos, c, o: lib.qsa_gated_attention(
+        q, k, v, ctypes.byref(kvd) if kvd is not None else None, sl, pos, ctypes.byref(c), o)
+    assert call(FAKE, FAKE, FAKE, kv, FAKE, FAKE, small, out) == binding.QSA_ERR_WORKSPACE
+    assert "workspace" in binding.last_error()
+    assert call(FAKE, FAKE, None, kv, FAKE, FAKE, small, out) == binding.QSA_ERR_INVALID
+    assert call(None, FAKE, FAKE, kv, FAKE, FAKE, small, out) == binding.QSA_ERR_INVALID
+    assert call(FAKE, FAKE, FAKE, None, FAKE, FAKE, small, out) == binding.QSA_ERR_INVALID
+    same = binding.KVCache(FAKE, FAKE, FAKE, None, 8192)
+    assert call(FAKE, FAKE, FAKE, same, FAKE, FAKE, small, out) == binding.QSA_ERR_INVALID
+    # output aliasing the query input
+    assert call(FAKE, FAKE, FAKE, kv, FAKE, FAKE, small, FAKE + 64) == binding.QSA_ERR_INVALID
+    assert "alias" in binding.last_error()
+    assert lib.qsa_append_kv(None, FAKE, ctypes.byref(kv), FAKE, FAKE, ctypes.byref(small)) == \
+        binding.QSA_ERR_INVALID
+
+
+def test_workspace_scales_with_chunks():
+    w = WORKLOADS["decode_4b"]
+    one = binding.workspace_size(cfg_for(w, force_splits=1))
+    many = binding.workspace_size(cfg_for(w, force_splits=32))
+    assert many > one >= 256

@@ -1,0 +1,208 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Tolerances: bf16 storage with fp32 accumulation -- max-abs <= 2e-2 and
+relative L2 <= 5e-3 over the compared outputs; fp32 -- relative L2 <= 1e-5.
+Appended cache rows must match the oracle's rounded rows to one unit in the
+last place of the storage dtype.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_gqa_attention_amd.session import Session
+from gated_gqa_attention_amd.workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+TOL = {"bf16": dict(max_abs=2e-2, rel_l2=5e-3), "f32": dict(max_abs=1e-3, rel_l2=1e-5)}
+ULP_BITS = {"bf16": 8, "f32": 24}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def geo(w):
+    return oracle.Geometry(w.batch, w.q_len, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                           w.rotary_dim, w.rope_theta, w.rms_eps, 0.0, w.dtype)
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def check(got, ref, dtype, what=""):
+    got = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
+    err, rl2 = float(np.max(np.abs(got - ref))), rel_l2(got, ref)
+    say(f"  {what}: max_abs={err:.3g} rel_l2={rl2:.3g}")
+    assert err <= TOL[dtype]["max_abs"], (what, err)
+    assert rl2 <= TOL[dtype]["rel_l2"], (what, rl2)
+
+
+def check_rows(sess, inp, kr, vr, w):
+    """Cache rows n_b .. n_b+L-1 written by the GPU vs the oracle's rounded rows."""
+    kc = sess.dev["k_cache"].float().cpu().double().numpy()
+    vc = sess.dev["v_cache"].float().cpu().double().numpy()
+    ulp = 2.0 ** (1 - ULP_BITS[w.dtype])
+    for b in range(w.batch):
+        s = int(inp["seq_offset"][b]) + int(inp["seq_lens"][b])
+        gk, gv = kc[s:s + w.q_len], vc[s:s + w.q_len]
+        # the GPU normalises and rotates in fp32: its value before rounding is within a few
+        # fp32 ulps of the row's scale, so the stored element is within one storage ulp of
+        # the oracle's, or within that fp32 error for elements far below the row's scale
+        row_scale = np.max(np.abs(kr[b]), axis=-1, keepdims=True)
+        bound = np.maximum(np.abs(kr[b]) * ulp, 8 * 2.0 ** -24 * row_scale)
+        assert np.all(np.abs(gk - kr[b]) <= bound), f"K rows of sequence {b}"
+        assert np.array_equal(gv, vr[b]), f"V rows of sequence {b}"
+
+
+def to_np(t):
+    return t.float().cpu().double().numpy()
+
+
+SMALL = [
+    WORKLOADS["tiny_f32"],
+    Workload("f32_gqa_causal", batch=2, q_len=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
+             rotary_dim=32, rope_theta=1e6, dtype="f32", prior=70, seed=101),
+    Workload("f32_ragged", batch=3, q_len=1, num_q_heads=4, num_kv_heads=4, head_dim=64,
+             rotary_dim=64, rope_theta=1e4, dtype="f32", prior=0, seed=102, ragged=(0, 200)),
+    Workload("bf16_decode_ragged", batch=3, q_len=1, num_q_heads=8, num_kv_heads=2, head_dim=256,
+             rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=0, seed=103, ragged=(1, 300)),
+    Workload("bf16_d64_mha", batch=2, q_len=2, num_q_heads=4, num_kv_heads=4, head_dim=64,
+             rotary_dim=0, rope_theta=1e4, dtype="bf16", prior=129, seed=104),
+    Workload("bf16_d128_full_rope", batch=2, q_len=1, num_q_heads=6, num_kv_heads=1, head_dim=128,
+             rotary_dim=128, rope_theta=1e6, dtype="bf16", prior=191, seed=105),
+    Workload("bf16_verify_small", batch=2, q_len=4, num_q_heads=24, num_kv_heads=2, head_dim=256,
+             rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=130, seed=106),
+    Workload("bf16_fused_l16", batch=1, q_len=16, num_q_heads=4, num_kv_heads=1, head_dim=256,
+             rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=77, seed=107),
+    Workload("bf16_no_prior", batch=2, q_len=5, num_q_heads=16, num_kv_heads=4, head_dim=256,
+             rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=0, seed=108),
+    Workload("bf16_prefill_tiles", batch=2, q_len=40, num_q_heads=16, num_kv_heads=4, head_dim=256,
+             rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=100, seed=109),
+    Workload("bf16_prefill_l17", batch=1, q_len=17, num_q_heads=4, num_kv_heads=2, head_dim=128,
+             rotary_dim=32, rope_theta=1e7, dtype="bf16", prior=33, seed=110),
+]
+
+
+@pytest.mark.parametrize("splits", [0, 1, 2, 7])
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_parity_small(w, splits):
+    for variant in ("graded", "stress"):
+        say(f"case {w.name} splits={splits} variant={variant}")
+        inp = make_inputs(w, variant=variant)
+        sess = Session(w, inp, force_splits=splits)
+        say(f"  plan {sess.plan()}")
+        out = to_np(sess.run())
+        torch.cuda.synchronize()
+        ref, kr, vr = oracle.gated_attention(geo(w), inp)
+        check(out, ref, w.dtype, f"{w.name}/{variant}")
+        check_rows(sess, inp, kr, vr, w)
+        assert sess.device_error() == 0
+
+
+@pytest.mark.parametrize("name", ["decode_4b", "verify_24x2"])
+def test_parity_full_workload(name):
+    w = WORKLOADS[name]
+    say(f"case {name} full")
+    inp = make_inputs(w)
+    sess = Session(w, inp)
+    say(f"  plan {sess.plan()}")
+    out = to_np(sess.run())
+    ref, kr, vr = oracle.gated_attention(geo(w), inp)
+    check(out, ref, w.dtype, name)
+    check_rows(sess, inp, kr, vr, w)
+    # worst (sequence, head) slice as a diagnostic
+    worst = max(rel_l2(out[b, :, h], ref[b, :, h]) for b in range(w.batch) for h in range(w.num_q_heads))
+    say(f"  worst per-(b,h) rel_l2={worst:.3g}")
+
+
+def sampled_rows(w, count, seed):
+    rng = np.random.default_rng(seed)
+    B, L, Hq = w.batch, w.q_len, w.num_q_heads
+    fixed = [0, Hq - 1, (L - 1) * Hq, ((B - 1) * L + L - 1) * Hq + Hq - 1]
+    rand = rng.choice(B * L * Hq, size=count, replace=False)
+    return np.unique(np.concatenate([fixed, rand]).astype(np.int64))
+
+
+@pytest.mark.parametrize("name,count", [("ragged_4b", 96), ("prefill_4b", 96)])
+def test_parity_full_size_sampled(name, count):
+    w = WORKLOADS[name]
+    say(f"case {name} full size, {count} sampled rows")
+    inp = make_inputs(w)
+    say(f"  sum of cached lengths {int(inp['seq_lens'].sum())}")
+    sess = Session(w, inp)
+    say(f"  plan {sess.plan()}")
+    out = to_np(sess.run()).reshape(-1, w.head_dim)
+    rows = sampled_rows(w, count, seed=w.seed)
+    g = geo(w)
+    kr, vr = oracle.new_kv(g, inp["k_new"], inp["v_new"], inp["w_k"], inp["positions"])
+    ref = oracle.attention(g, inp["q_gate"], inp["w_q"], inp["k_cache"], inp["v_cache"],
+                           inp["seq_offset"], inp["seq_lens"], inp["positions"], kr, vr, rows=rows)
+    check(out[rows], ref, w.dtype, f"{name} sampled")
+    check_rows(sess, inp, kr, vr, w)
+    assert np.all(np.isfinite(out))
+    assert sess.device_error() == 0
+
+
+def test_append_then_attend_equals_fused():
+    w = WORKLOADS["verify_24x2"].with_(prior=300)
+    inp = make_inputs(w)
+    say("case append+attend vs fused")
+    fused = Session(w, inp)
+    a = to_np(fused.run())
+    split = Session(w, inp)
+    split.append()
+    b = to_np(split.run(fused=False))
+    assert np.array_equal(a, b)
+    assert torch.equal(fused.dev["k_cache"], split.dev["k_cache"])
+    assert torch.equal(fused.dev["v_cache"], split.dev["v_cache"])
+
+
+def test_split_count_invariance():
+    w = WORKLOADS["decode_4b"]
+    inp = make_inputs(w)
+    outs = {}
+    for k in (0, 1, 2, 7, 65):
+        say(f"case decode_4b force_splits={k}")
+        outs[k] = to_np(Session(w, inp, force_splits=k).run())
+    for k, o in outs.items():
+        assert rel_l2(o, outs[1]) < 5e-3, k
+
+
+def test_repeat_calls_are_idempotent():
+    w = WORKLOADS["decode_4b"]
+    inp = make_inputs(w)
+    sess = Session(w, inp)
+    first = sess.run().clone()
+    kc = sess.dev["k_cache"].clone()
+    for _ in range(3):
+        again = sess.run()
+    torch.cuda.synchronize()
+    assert torch.equal(first, again)
+    assert torch.equal(kc, sess.dev["k_cache"])
+    assert sess.device_error() == 0
+
+
+def test_device_side_range_error_is_reported_not_faulted():
+    """A sequence whose rows would pass its capacity gets NaN outputs and a
+    workspace flag; its cache rows are not written; other sequences are fine."""
+    w = Workload("range", batch=2, q_len=1, num_q_heads=8, num_kv_heads=2, head_dim=256,
+                 rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=50, seed=111)
+    inp = make_inputs(w)
+    sess = Session(w, inp, max_seq_len=64)
+    sess.dev["capacity"][1] = 40           # sequence 1 claims fewer rows than n + L
+    kc = sess.dev["k_cache"].clone()
+    out = to_np(sess.run())
+    torch.cuda.synchronize()
+    assert np.all(np.isnan(out[1]))
+    assert np.all(np.isfinite(out[0]))
+    assert sess.device_error() & 1
+    s1 = int(inp["seq_offset"][1]) + 50
+    assert torch.equal(kc[s1], sess.dev["k_cache"][s1])
