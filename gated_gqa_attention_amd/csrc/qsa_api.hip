@@ -37,7 +37,7 @@ struct Plan {
   int route = 0;
   int rows = 0, tiles = 0, chunks = 1, chunk_keys = 0;
   int64_t blocks = 0;
-  size_t off_counters = 0, off_ml = 0, off_o = 0, off_qt = 0, total = 0;
+  size_t off_ml = 0, off_o = 0, off_qt = 0, total = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -76,13 +76,14 @@ int make_plan(const qsa_cfg *c, Plan *pl) {
   const int64_t G = Hq / Hkv;
   const int64_t rows_total = L * G;
   const size_t es = c->dtype == QSA_BF16 ? 2 : 4;
+  const int64_t S = c->max_seq_len;
   Plan p;
   if (c->dtype == QSA_F32) {
     p.route = kRouteF32;
     p.rows = (int)std::min<int64_t>(rows_total, qsa::kTileRows);
     p.tiles = 1;
     p.chunks = 1;
-    p.chunk_keys = c->max_seq_len;
+    p.chunk_keys = (int)S;
     p.blocks = B * L * Hq;
   } else {
     const bool fused = rows_total <= qsa::kTileRows && L <= qsa::kMaxFusedNewRows;
@@ -90,31 +91,27 @@ int make_plan(const qsa_cfg *c, Plan *pl) {
     p.tiles = (int)cdiv(rows_total, qsa::kTileRows);
     p.rows = (int)std::min<int64_t>(rows_total, qsa::kTileRows);
     const int64_t base = B * Hkv * p.tiles;
-    const int64_t max_chunks = cdiv(c->max_seq_len, qsa::kTileKeys);
-    int64_t want = c->force_splits > 0 ? c->force_splits : std::max<int64_t>(1, cdiv(512, base));
-    want = std::min(want, max_chunks);
-    int64_t ck = cdiv(cdiv(c->max_seq_len, want), qsa::kTileKeys) * qsa::kTileKeys;
-    if (c->force_splits == 0) {
-      // keep partials small next to the keys they summarise
-      ck = std::max<int64_t>(ck, cdiv(2 * (int64_t)p.rows, qsa::kTileKeys) * qsa::kTileKeys);
+    int64_t ck;
+    if (c->force_splits > 0) {
+      ck = std::max<int64_t>(1, S / c->force_splits);
+    } else if (!fused && base >= 256) {
+      ck = S;                                   // long prefill: one chunk per row tile
+    } else {
+      // one round of workgroups (one per CU) for short work; for long work
+      // ~2048 chunks so ragged lengths balance across the CUs
+      const int64_t total = base * S;
+      ck = std::max<int64_t>(qsa::kTileKeys, total / 256);
+      if (ck > 2048) ck = std::max<int64_t>(2048, total / 2048);
     }
-    int64_t chunks = cdiv(c->max_seq_len, ck);
-    // the merging workgroup stages chunks x rows softmax statistics in LDS
-    const int64_t lds_cap = 32 * (D + 8);
-    while (chunks > 1 && chunks * p.rows > lds_cap) {
-      ck += qsa::kTileKeys;
-      chunks = cdiv(c->max_seq_len, ck);
-    }
-    p.chunk_keys = (int)ck;
-    p.chunks = (int)chunks;
-    p.blocks = base * chunks;
+    ck = std::max<int64_t>(ck, cdiv(S, qsa::kMaxChunks));
+    p.chunk_keys = (int)std::min<int64_t>(ck, S);
+    p.chunks = (int)std::max<int64_t>(1, S / p.chunk_keys);
+    p.blocks = base * p.chunks;
   }
   if (p.blocks > 0x7fffffffLL) return fail(QSA_ERR_UNSUPPORTED, "launch grid too large (%lld workgroups)",
                                            (long long)p.blocks);
   const int64_t slots = B * Hkv * p.tiles;
   size_t off = 256;
-  p.off_counters = off;
-  off = align256(off + (size_t)slots * 4);
   if (p.chunks > 1) {
     p.off_ml = off;
     off = align256(off + (size_t)slots * p.chunks * p.rows * 2 * 4);
@@ -147,7 +144,8 @@ qsa::Params base_params(const qsa_cfg *c, const Plan &pl) {
   p.eps = c->rms_eps;
   p.scale = c->softmax_scale > 0.f ? c->softmax_scale : (float)(1.0 / std::sqrt((double)c->head_dim));
   p.scale_log2 = p.scale * qsa::kLog2e;
-  p.theta = (double)c->rope_theta;
+  for (int i = 0; i < c->rotary_dim / 2; ++i)
+    p.inv_freq[i] = std::pow((double)c->rope_theta, -2.0 * i / (double)c->rotary_dim);
   p.wq = c->q_norm_w;
   p.wk = c->k_norm_w;
   return p;
@@ -276,7 +274,6 @@ int qsa_gated_attention(const void *q_gate, const void *k_new, const void *v_new
   p.out = out;
   char *ws = (char *)cfg->workspace;
   p.err = (int32_t *)ws;
-  p.counters = (int32_t *)(ws + pl.off_counters);
   p.part_ml = pl.off_ml ? (float *)(ws + pl.off_ml) : nullptr;
   p.part_o = pl.off_o ? (float *)(ws + pl.off_o) : nullptr;
   p.qt = pl.off_qt ? (void *)(ws + pl.off_qt) : nullptr;
@@ -290,11 +287,13 @@ int qsa_gated_attention(const void *q_gate, const void *k_new, const void *v_new
       if (e == hipSuccess) e = qsa::launch_rows_f32(p, s);
       break;
     case kRouteFused:
-      e = qsa::launch_tiles_bf16(p, false, s);
+      e = qsa::launch_split_bf16(p, false, s);
+      if (e == hipSuccess && pl.chunks > 1) e = qsa::launch_combine_bf16(p, s);
       break;
     default:
       e = qsa::launch_prologue(p, QSA_BF16, true, has_new, s);
-      if (e == hipSuccess) e = qsa::launch_tiles_bf16(p, true, s);
+      if (e == hipSuccess) e = qsa::launch_split_bf16(p, true, s);
+      if (e == hipSuccess && pl.chunks > 1) e = qsa::launch_combine_bf16(p, s);
       break;
   }
   if (e != hipSuccess) return fail(QSA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));

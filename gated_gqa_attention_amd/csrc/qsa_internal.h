@@ -14,33 +14,33 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;   // four wavefronts per workgroup
+constexpr int kThreads = 256;         // four wavefronts per workgroup
 constexpr int kWave = 64;
-constexpr int kTileKeys = 64;   // keys staged in LDS per pipeline stage
-constexpr int kTileRows = 64;   // query rows (group heads x new rows) per workgroup
-constexpr int kMaxFusedNewRows = 16;
+constexpr int kTileKeys = 64;         // keys staged in LDS per pipeline stage
+constexpr int kTileRows = 64;         // query rows (group heads x new rows) per workgroup
+constexpr int kMaxFusedNewRows = 16;  // new rows a fused call may append per sequence
+constexpr int kMaxPairs = 128;        // rotary pairs (rotary_dim / 2) supported
+constexpr int kMaxChunks = 4096;      // key chunks per (sequence, KV head, tile)
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Workspace layout (bytes, all offsets 256-aligned):
-//   [0, 256)                 header; int32 at 0 = sticky device error bits
-//   counters                 int32 [slots]          arrival tickets, left at zero
-//   part_ml                  float [slots][S][rows][2]
-//   part_o                   float [slots][S][rows][D]
-//   qt                       prepared queries [B][L][Hq][D] (bf16 or fp32)
-// where slots = B * Hkv * tiles, S = chunks, rows = rows per tile.
+// Workspace layout (bytes, 256-aligned sections):
+//   [0, 256)   header; int32 at 0 = sticky device error bits
+//   part_ml    float [slots][chunks][rows][2]   per-chunk running max (log2 units) and sum
+//   part_o     float [slots][chunks][rows][D]   per-chunk unnormalised outputs
+//   qt         prepared queries [B][L][Hq][D] (bf16 or fp32)
+// where slots = B * Hkv * tiles.
 constexpr int32_t kErrRange = 1;
 
 struct Params {
   int B, L, Hq, Hkv, G, D, r;
   int rows;           // query rows per tile (<= kTileRows)
   int tiles;          // row tiles per (sequence, KV head)
-  int chunks;         // key chunks per (sequence, KV head, tile) planned for max_seq_len
-  int chunk_keys;     // keys per chunk, a multiple of kTileKeys
+  int chunks;         // grid extent in key chunks = chunk_count(max_seq_len)
+  int chunk_keys;     // keys per chunk (the last chunk of a tile also takes the remainder)
   int max_seq_len;
   float eps;
   float scale_log2;   // softmax scale * log2(e)
   float scale;        // softmax scale
-  double theta;
   const void *q_gate;
   const void *k_new;
   const void *v_new;
@@ -55,10 +55,10 @@ struct Params {
   const void *wk;
   void *out;
   int32_t *err;       // may be null
-  int32_t *counters;
   float *part_ml;
   float *part_o;
   void *qt;
+  double inv_freq[kMaxPairs];  // theta^(-2i/r), computed on the host in double
 };
 
 // ------------------------------------------------------------------ helpers
@@ -85,18 +85,26 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Rotation angle of pair i at position pos: pos * theta^(-2i/r), evaluated in
-// double (positions reach 3e4 rad at the first pair), then cos/sin rounded to fp32.
-__device__ __forceinline__ void rope_cs(int pos, int i, int r, double theta, float &c, float &s) {
-  const double a = (double)pos * pow(theta, -2.0 * (double)i / (double)r);
-  double sd, cd;
-  sincos(a, &sd, &cd);
-  c = (float)cd;
-  s = (float)sd;
+// cos/sin of pair i at position pos.  The angle pos * theta^(-2i/r) reaches
+// 3e4 rad, so it is formed and reduced modulo 2*pi in double (two-part
+// Cody-Waite constant), and only the reduced angle goes through fp32 sincos.
+__device__ __forceinline__ void rope_cs(const Params &p, int pos, int i, float &c, float &s) {
+  const double a = (double)pos * p.inv_freq[i];
+  const double k = rint(a * 0.15915494309189535);  // 1 / (2 pi)
+  double red = fma(-k, 6.283185307179586, a);
+  red = fma(-k, 2.4492935982947064e-16, red);
+  sincosf((float)red, &s, &c);
 }
 
-// Sequence bounds check shared by the kernels.  Returns false (and flags the
-// error) when rows [0, total) of sequence b would leave the cache.
+// Keys [0, kend) of one (sequence, row tile) are cut into max(1, kend / chunk_keys)
+// chunks of chunk_keys keys; the last chunk also takes the remainder.
+__device__ __forceinline__ int chunk_count(int64_t kend, int chunk_keys) {
+  const int64_t c = kend / chunk_keys;
+  return c < 1 ? 1 : (int)c;
+}
+
+// Sequence bounds check shared by the kernels.  Returns false when rows
+// [0, n + L) of sequence b would leave the cache or pass its capacity.
 __device__ __forceinline__ bool seq_in_range(const Params &p, int b, int n, int64_t &off) {
   off = p.seq_offset[b];
   const int64_t total = (int64_t)n + p.L;
@@ -113,6 +121,7 @@ __device__ __forceinline__ void flag_error(const Params &p) {
 // (defined in the kernel translation units, called by the C ABI layer)
 hipError_t launch_prologue(const Params &p, int dtype, bool do_q, bool do_kv, hipStream_t s);
 hipError_t launch_rows_f32(const Params &p, hipStream_t s);
-hipError_t launch_tiles_bf16(const Params &p, bool prepared_q, hipStream_t s);
+hipError_t launch_split_bf16(const Params &p, bool prepared_q, hipStream_t s);
+hipError_t launch_combine_bf16(const Params &p, hipStream_t s);
 
 }  // namespace qsa

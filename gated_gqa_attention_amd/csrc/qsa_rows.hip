@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(Params p, int do_q, 
       if (e < p.r) {
         const int i = e < half ? e : e - half;
         float c, s;
-        rope_cs(pos, i, p.r, p.theta, c, s);
+        rope_cs(p, pos, i, c, s);
         const float other = scratch[wave][e < half ? e + half : e - half];
         x[j] = e < half ? x[j] * c - other * s : x[j] * c + other * s;
       }

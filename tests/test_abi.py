@@ -59,9 +59,17 @@ def test_plan_covers_max_seq_len_and_forced_splits():
     w = WORKLOADS["decode_4b"]
     for k in (1, 2, 7, 65):
         f = dict(kv.split("=") for kv in binding.describe_plan(cfg_for(w, force_splits=k)).split())
-        assert int(f["chunks"]) * int(f["chunk_keys"]) >= 4097
-        assert int(f["chunk_keys"]) % 64 == 0
-        assert int(f["chunks"]) <= k or int(f["chunk_keys"]) == 64
+        chunks, ck = int(f["chunks"]), int(f["chunk_keys"])
+        # chunks of chunk_keys keys, the last one also taking the remainder
+        assert chunks * ck <= 4097 < (chunks + 1) * ck
+        assert k <= chunks <= k + 1
+
+
+def test_default_plans_fill_one_round_for_short_work():
+    f = dict(kv.split("=") for kv in binding.describe_plan(cfg_for(WORKLOADS["decode_4b"])).split())
+    assert int(f["workgroups"]) == 256
+    f = dict(kv.split("=") for kv in binding.describe_plan(cfg_for(WORKLOADS["verify_24x2"])).split())
+    assert int(f["workgroups"]) == 256
 
 
 @pytest.mark.parametrize("bad,code", [
