@@ -121,12 +121,16 @@ __device__ __forceinline__ void norm_rope_rows16(float (&x)[D / 16], const float
   for (int j = 0; j < E; ++j) row[c16 * E + j] = x[j];
   wave_lds_sync();
   const int h = r / 2;
+  if (c16 * E < r) {                              // this lane holds rotated elements
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    const int e = c16 * E + j;
-    if (e < r) {
-      const float2 t = cs[e < h ? e : e - h];   // (cos, sin)
-      x[j] = e < h ? x[j] * t.x - row[e + h] * t.y : x[j] * t.x + row[e - h] * t.y;
+    for (int j = 0; j < E; ++j) {
+      const int e = c16 * E + j;
+      const bool lo = e < h;
+      const int pe = lo ? e + h : e - h;          // pair partner
+      const float2 t = cs[lo ? e : e - h];        // (cos, sin)
+      const float other = row[min(pe, D - 1)];
+      const float y = lo ? x[j] * t.x - other * t.y : x[j] * t.x + other * t.y;
+      x[j] = e < r ? y : x[j];
     }
   }
 }
@@ -148,8 +152,10 @@ __global__ __launch_bounds__(kThreads) void split_kernel(Params p) {
   constexpr int QU = (RMAX * OCT + kThreads - 1) / kThreads;  // 16-byte query units per thread
   static_assert(KU >= 1 && E >= 4 && RMAX <= kTileRows, "head_dim too small for the tile");
 
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[kTileKeys * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[kTileKeys * KSTR];   // V rows, same layout as K
+  // fused mode keeps 32 spare rows so a chunk's new rows can join its last stage
+  constexpr int TROWS = PREP ? kTileKeys : kTileKeys + 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[TROWS * KSTR];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[TROWS * KSTR];   // V rows, same layout as K
   __shared__ __attribute__((aligned(16))) bf16_t newK[NEWR * D];
   __shared__ __attribute__((aligned(16))) bf16_t newV[NEWR * D];
 
@@ -293,16 +299,18 @@ __global__ __launch_bounds__(kThreads) void split_kernel(Params p) {
     float2 *cs = reinterpret_cast<float2 *>(Vt);
     float *scr = reinterpret_cast<float *>(Vt) + 16 * D + wave * 4 * D;
     float *red = reinterpret_cast<float *>(Vt) + 32 * D + wave * 64;
-    for (int e = t; e < tent; e += kThreads) {
-      const int pos = e == t ? tpos : gload<int>(p.positions + b * p.L + e / half);
-      const double a = (double)pos * (e == t ? tinv : p.inv_freq[e % half]);
+    auto put_cs = [&](int e, int pos, double inv) {
+      const double a = (double)pos * inv;
       const double k = rint(a * 0.15915494309189535);  // 1 / (2 pi), reduction in double
       double rd = fma(-k, 6.283185307179586, a);
       rd = fma(-k, 2.4492935982947064e-16, rd);
       float c, sn;
       sincosf((float)rd, &sn, &c);
       cs[e] = make_float2(c, sn);
-    }
+    };
+    if (t < tent) put_cs(t, tpos, tinv);
+    for (int e = t + kThreads; e < tent; e += kThreads)   // only when L * r/2 > 256
+      put_cs(e, gload<int>(p.positions + b * p.L + e / half), p.inv_freq[e % half]);
     float wq[E], wk[E];
 #pragma unroll
     for (int u = 0; u < EU; ++u) {
@@ -361,9 +369,15 @@ __global__ __launch_bounds__(kThreads) void split_kernel(Params p) {
   const int rowg = row0 + rt * 16 + m16;
   const int64_t lim = (int64_t)n + rowg / p.G;          // causal: row sees keys <= n + l
 
-  const int nst = (int)((k1 - k0 + kTileKeys - 1) / kTileKeys);
+  int nst = (int)((k1 - k0 + kTileKeys - 1) / kTileKeys);
+  if (TROWS > kTileKeys && nst >= 2) {
+    // a final stage holding nothing but new rows (at most 32) joins the one before
+    const int64_t last = k0 + (int64_t)(nst - 1) * kTileKeys;
+    if (last >= patch_from && k1 - last <= TROWS - kTileKeys) --nst;
+  }
   for (int st = 0; st < nst; ++st) {
     const int64_t sb = k0 + (int64_t)st * kTileKeys;
+    const int64_t se = st == nst - 1 ? k1 : sb + kTileKeys;   // stage end (at most TROWS keys)
 #pragma unroll
     for (int i = 0; i < KU; ++i) {
       const int u = t + kThreads * i, key = u / OCT, o = u % OCT;
@@ -377,16 +391,30 @@ __global__ __launch_bounds__(kThreads) void split_kernel(Params p) {
       *(uint4 *)&Ks[key * KSTR + 8 * o] = kv;
       *(uint4 *)&Vt[key * KSTR + 8 * o] = vv;
     }
+    if (TROWS > kTileKeys && se - sb > kTileKeys) {
+      // spare rows: new rows from LDS, zeros past the chunk end
+      for (int e = t; e < (TROWS - kTileKeys) * OCT; e += kThreads) {
+        const int key = kTileKeys + e / OCT, o = e % OCT;
+        const int64_t ka = sb + key;
+        uint4 kv = uint4{0, 0, 0, 0}, vv = uint4{0, 0, 0, 0};
+        if (ka >= patch_from && ka < k1) {
+          kv = *(const uint4 *)&newK[(ka - n - nlo) * D + 8 * o];
+          vv = *(const uint4 *)&newV[(ka - n - nlo) * D + 8 * o];
+        }
+        *(uint4 *)&Ks[key * KSTR + 8 * o] = kv;
+        *(uint4 *)&Vt[key * KSTR + 8 * o] = vv;
+      }
+    }
     __syncthreads();
     if (st + 1 < nst) load_stage(sb + kTileKeys);
     __builtin_amdgcn_sched_barrier(0);
 
     if (computes) {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
+      for (int blk = 0; blk < TROWS / 32; ++blk) {
         if ((blk % KS) != ksub) continue;
         const int kb = 32 * blk;
-        if (sb + kb >= k1) continue;           // block entirely past the chunk end
+        if (sb + kb >= se) continue;           // block entirely past the stage end
         f32x4 sacc[2];
 #pragma unroll
         for (int beta = 0; beta < 2; ++beta) {
@@ -498,9 +526,11 @@ __global__ __launch_bounds__(kThreads) void split_kernel(Params p) {
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(Params p) {
   constexpr int EPL = D / kWave;
+  constexpr int kBatch = 16;                            // chunks in flight per wave
   __shared__ float wts[kMaxChunks];
   __shared__ float acc_x[kThreads / kWave][D];
-  __shared__ float s_ml[2];
+  __shared__ float red[kThreads / kWave];
+  __shared__ float s_inv;
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
   const int rr = blockIdx.x % p.rows;
   const int slot = blockIdx.x / p.rows;
@@ -511,30 +541,48 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Params p) {
   const int row0 = tile * kTileRows;
   const int R = min(p.rows, rows_total - row0);
   if (rr >= R) return;
-  const int n = p.seq_lens[b];
+  const int n = gload<int>(p.seq_lens + b);
   int64_t off;
   if (!seq_in_range(p, b, n, off)) return;              // the split kernel wrote NaN
   const int lmax = (row0 + R - 1) / p.G;
   const int nch = chunk_count((int64_t)n + lmax + 1, p.chunk_keys);
   if (nch == 1) return;                                 // finished by the split kernel
 
+  // every load first: chunk statistics, the gate, the first batch of partial outputs
   const int64_t base = (int64_t)slot * p.chunks * p.rows + rr;   // + c * rows
-  float mx = -INFINITY;
-  for (int c = t; c < nch; c += kThreads) {
-    const float m = p.part_ml[(base + (int64_t)c * p.rows) * 2];
-    wts[c] = m;
-    mx = fmaxf(mx, m);
+  const int rg = row0 + rr, l = rg / p.G, h = kvh * p.G + rg % p.G;
+  const bf16_t *zp = (const bf16_t *)p.q_gate + (((int64_t)b * p.L + l) * p.Hq + h) * 2 * D + D + lane * EPL;
+  float z[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) z[j] = to_f(gload<bf16_t>(zp + j));
+  const int cm = min(t, nch - 1);
+  const float m_c = gload<float>(p.part_ml + (base + (int64_t)cm * p.rows) * 2);
+  const float l_c = gload<float>(p.part_ml + (base + (int64_t)cm * p.rows) * 2 + 1);
+  float v[kBatch][EPL];
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int c = min(wave + k * (kThreads / kWave), nch - 1);
+    const float *po = p.part_o + (base + (int64_t)c * p.rows) * D + lane * EPL;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) v[k][j] = gload<float>(po + j);
   }
-  __shared__ float red[kThreads / kWave];
+  __builtin_amdgcn_sched_barrier(0);
+
+  // weights w_c = 2^(m_c - M) / sum_c l_c 2^(m_c - M)   (chunks beyond 256 are rare)
+  float mx = t < nch ? m_c : -INFINITY;
+  for (int c = t + kThreads; c < nch; c += kThreads) mx = fmaxf(mx, p.part_ml[(base + (int64_t)c * p.rows) * 2]);
   mx = wave_max(mx);
   if (lane == 0) red[wave] = mx;
   __syncthreads();
-  float M = red[0];
-#pragma unroll
-  for (int w = 1; w < kThreads / kWave; ++w) M = fmaxf(M, red[w]);
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float ls = 0.f;
-  for (int c = t; c < nch; c += kThreads) {
-    const float e = exp2f(wts[c] - M);
+  if (t < nch) {
+    const float e = exp2f(m_c - M);
+    wts[t] = e;
+    ls = e * l_c;
+  }
+  for (int c = t + kThreads; c < nch; c += kThreads) {
+    const float e = exp2f(p.part_ml[(base + (int64_t)c * p.rows) * 2] - M);
     wts[c] = e;
     ls += e * p.part_ml[(base + (int64_t)c * p.rows) * 2 + 1];
   }
@@ -542,44 +590,36 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Params p) {
   __syncthreads();
   if (lane == 0) red[wave] = ls;
   __syncthreads();
-  if (t == 0) s_ml[0] = 1.f / (red[0] + red[1] + red[2] + red[3]);
+  if (t == 0) s_inv = 1.f / ((red[0] + red[1]) + (red[2] + red[3]));
   __syncthreads();
-  const float invL = s_ml[0];
 
-  // chunks c = wave + 4i, eight in flight per thread
-  constexpr int kBatch = 8;
   float acc[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
-  for (int c0 = wave; c0 < nch; c0 += kBatch * (kThreads / kWave)) {
-    float v[kBatch][EPL];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int c = c0 + k * (kThreads / kWave);
-      const float *po = p.part_o + (base + (int64_t)min(c, nch - 1) * p.rows) * D + lane * EPL;
+  for (int k = 0; k < kBatch; ++k) {
+    const int c = wave + k * (kThreads / kWave);
+    const float wc = c < nch ? wts[c] : 0.f;
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) v[k][j] = po[j];
-    }
+    for (int j = 0; j < EPL; ++j) acc[j] += wc * v[k][j];
+  }
+  for (int c0 = wave + kBatch * (kThreads / kWave); c0 < nch; c0 += kThreads / kWave) {
+    const float wc = wts[c0];
+    const float *po = p.part_o + (base + (int64_t)c0 * p.rows) * D + lane * EPL;
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int c = c0 + k * (kThreads / kWave);
-      const float wc = c < nch ? wts[c] : 0.f;
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) acc[j] += wc * v[k][j];
-    }
+    for (int j = 0; j < EPL; ++j) acc[j] += wc * po[j];
   }
 #pragma unroll
   for (int j = 0; j < EPL; ++j) acc_x[wave][lane * EPL + j] = acc[j];
   __syncthreads();
   if (wave != 0) return;
-  const int rg = row0 + rr, l = rg / p.G, h = kvh * p.G + rg % p.G;
-  const bf16_t *z = (const bf16_t *)p.q_gate + (((int64_t)b * p.L + l) * p.Hq + h) * 2 * D + D;
+  const float inv = s_inv;
   bf16_t *out = (bf16_t *)p.out + (((int64_t)b * p.L + l) * p.Hq + h) * D;
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int d = lane * EPL + j;
-    const float o = (acc_x[0][d] + acc_x[1][d] + acc_x[2][d] + acc_x[3][d]) * invL;
-    out[d] = (bf16_t)(o * sigmoid(to_f(z[d])));
+    const float o = ((acc_x[0][d] + acc_x[1][d]) + (acc_x[2][d] + acc_x[3][d])) * inv;
+    out[d] = (bf16_t)(o * sigmoid(z[j]));
   }
 }
 

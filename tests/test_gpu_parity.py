@@ -88,6 +88,9 @@ SMALL = [
              rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=100, seed=109),
     Workload("bf16_prefill_l17", batch=1, q_len=17, num_q_heads=4, num_kv_heads=2, head_dim=128,
              rotary_dim=32, rope_theta=1e7, dtype="bf16", prior=33, seed=110),
+    # 64 cached + 16 new keys in one chunk: the new rows join the first stage's spare rows
+    Workload("bf16_new_rows_fold", batch=2, q_len=16, num_q_heads=4, num_kv_heads=1, head_dim=256,
+             rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=64, seed=112),
 ]
 
 
