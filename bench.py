@@ -14,7 +14,6 @@ on the launch stream.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -39,22 +38,29 @@ DEFAULT_STEPS = {"decode_4b": (2000, 200), "verify_24x2": (1000, 100), "ragged_4
 
 
 def algorithmic_work(w, seq_lens):
-    """Bytes the method must move and FLOPs it must do per call (QK^T and PV only)."""
+    """Bytes the method must move and FLOPs it must do per call (QK^T and PV only).
+
+    Returns (total bytes, output bytes, flops).  The output bytes are listed apart
+    because a call that splits its keys writes the output from a second, small
+    kernel; every other byte is moved by the kernel that streams the KV cache."""
     es = 2 if w.dtype == "bf16" else 4
     B, L, Hq, Hkv, D = w.batch, w.q_len, w.num_q_heads, w.num_kv_heads, w.head_dim
     n = [int(x) for x in seq_lens]
     kv_read = sum(n) * Hkv * D * 2 * es                 # cached K and V rows
     reads = B * L * Hq * 2 * D * es + 2 * B * L * Hkv * D * es + 2 * D * es + 4 * B + 4 * B * L
-    writes = B * L * Hq * D * es + 2 * B * L * Hkv * D * es
+    out = B * L * Hq * D * es
+    writes = out + 2 * B * L * Hkv * D * es
     keys = sum(nb * L + L * (L + 1) // 2 for nb in n)    # sum over rows of the keys each row sees
     flops = keys * Hq * 4 * D
-    return kv_read + reads + writes, flops
+    return kv_read + reads + writes, out, flops
 
 
 def kernel_source_hash():
+    """Hash of the sources that define the attention kernels (their device code and
+    the parameter block they read); a traffic figure taken on other sources is stale."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "gated_gqa_attention_amd", "csrc", "*"))):
-        h.update(open(f, "rb").read())
+    for name in ("qsa_tiles.hip", "qsa_internal.h"):
+        h.update(open(os.path.join(ROOT, "gated_gqa_attention_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -96,6 +102,48 @@ class Call:
         d = self.dev
         binding.gated_attention(self.cfg, self.kv, d["q_gate"], d["k_new"], d["v_new"], d["seq_lens"],
                                 d["positions"], self.out)
+
+
+def kernel_times(calls, stream, n):
+    """Average duration (ms) of the attention kernel over n eager calls, from HIP
+    events the library records on the launch stream right around that kernel."""
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n)]
+    with torch.cuda.stream(stream):
+        for a, b in pairs:              # torch creates an event on its first record
+            a.record(stream)
+            b.record(stream)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i, (a, b) in enumerate(pairs):
+            c = calls[i % len(calls)]
+            c.cfg.timing_begin, c.cfg.timing_end = a.cuda_event, b.cuda_event
+            c()
+    torch.cuda.synchronize()
+    for c in calls:
+        c.cfg.timing_begin = c.cfg.timing_end = None
+    return sum(a.elapsed_time(b) for a, b in pairs) / n
+
+
+def copy_calibration(steps=20, nbytes=256 << 20):
+    """Plain device-to-device copy of known size (torch's copy kernel): the
+    reference point that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters."""
+    dev = torch.device("cuda:0")
+    src = torch.randn(nbytes // 4, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "steps": steps,
+                      "ms_per_copy": round(ms, 4), "gbs_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}),
+          flush=True)
 
 
 def cpu_baseline(w, inputs, tokens_per_call, budget_s=10.0):
@@ -150,6 +198,8 @@ def main():
     ap.add_argument("--force-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=None, help="buffer sets to rotate over")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain 256 MiB device copy instead (reference for the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -161,6 +211,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration()
+        return
     w = WORKLOADS[args.workload]
     steps, warm = DEFAULT_STEPS.get(w.name, (100, 10))
     steps = args.steps if args.steps is not None else steps
@@ -227,23 +280,33 @@ def main():
         print(f"bench.py: device-side range error flagged: {errs}", file=sys.stderr)
         sys.exit(1)
 
+    # the kernel that streams the KV cache, timed on its own in a separate eager pass
+    kernel_ms = kernel_times(calls, stream, min(steps, 500))
+
     tokens_per_call = w.batch * w.q_len
-    bytes_call, flops_call = algorithmic_work(w, inputs["seq_lens"])
+    bytes_call, out_bytes, flops_call = algorithmic_work(w, inputs["seq_lens"])
+    chunks = int(plan.split("chunks=")[1].split()[0])
+    bytes_kernel = bytes_call - (out_bytes if chunks > 1 else 0)
     s_per_step = ms / 1e3 / steps
     value = tokens_per_call / s_per_step
     gbs = bytes_call / s_per_step / 1e9
     tfs = flops_call / s_per_step / 1e12
+    k_s = kernel_ms / 1e3
     hbm_bound = w.name != "prefill_4b"
     traffic = traffic_from_profiles(w.name)
+    kname = "split_kernel" if w.dtype == "bf16" else "rows_f32_kernel"
     if hbm_bound:
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+        ach = bytes_kernel / k_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
     else:
-        roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS,
-                "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic}
-    roof["kernel"] = "tiles_bf16_kernel" if w.dtype == "bf16" else "rows_f32_kernel"
-    roof["algorithmic_bytes_per_launch"] = bytes_call
-    roof["algorithmic_flops_per_launch"] = flops_call
+        ach = flops_call / k_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic}
+    roof.update({"kernel": kname, "kernel_us": round(kernel_ms * 1e3, 3),
+                 "algorithmic_bytes_per_launch": bytes_kernel,
+                 "algorithmic_flops_per_launch": flops_call,
+                 "kernel_share_of_step": round(kernel_ms / (ms / steps), 3)})
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,

@@ -39,6 +39,7 @@ class Cfg(ctypes.Structure):
         ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
+        ("timing_begin", ctypes.c_void_p), ("timing_end", ctypes.c_void_p),
     ]
 
 

@@ -280,19 +280,24 @@ int qsa_gated_attention(const void *q_gate, const void *k_new, const void *v_new
   hipStream_t s = (hipStream_t)cfg->stream;
   const bool has_new = k_new != nullptr;
 
+  // optional timing events: the dispatch times of the kernel that streams the KV cache
+  qsa::Timing tm;
+  tm.begin = (hipEvent_t)cfg->timing_begin;
+  tm.end = (hipEvent_t)cfg->timing_end;
+
   hipError_t e = hipSuccess;
   switch (pl.route) {
     case kRouteF32:
       e = qsa::launch_prologue(p, QSA_F32, true, has_new, s);
-      if (e == hipSuccess) e = qsa::launch_rows_f32(p, s);
+      if (e == hipSuccess) e = qsa::launch_rows_f32(p, s, tm);
       break;
     case kRouteFused:
-      e = qsa::launch_split_bf16(p, false, s);
+      e = qsa::launch_split_bf16(p, false, s, tm);
       if (e == hipSuccess && pl.chunks > 1) e = qsa::launch_combine_bf16(p, s);
       break;
     default:
       e = qsa::launch_prologue(p, QSA_BF16, true, has_new, s);
-      if (e == hipSuccess) e = qsa::launch_split_bf16(p, true, s);
+      if (e == hipSuccess) e = qsa::launch_split_bf16(p, true, s, tm);
       if (e == hipSuccess && pl.chunks > 1) e = qsa::launch_combine_bf16(p, s);
       break;
   }

@@ -3,6 +3,7 @@
 // Target: AMD CDNA4 (gfx950), 64-wide wavefronts, MFMA bf16 16x16x32.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -118,10 +119,25 @@ __device__ __forceinline__ void flag_error(const Params &p) {
 }
 
 // --------------------------------------------------------------- launchers
+// Optional events that time one kernel.  When either is set the kernel goes
+// through hipExtLaunchKernel, which stamps the events with the dispatch's own
+// begin and end times (the interval a kernel-trace profiler reports).
+struct Timing {
+  hipEvent_t begin = nullptr, end = nullptr;
+};
+
+template <typename Kernel, typename... Args>
+inline void launch_kernel(Kernel kernel, int64_t blocks, hipStream_t s, const Timing &tm, Args... args) {
+  if (tm.begin || tm.end)
+    hipExtLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, tm.begin, tm.end, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, args...);
+}
+
 // (defined in the kernel translation units, called by the C ABI layer)
 hipError_t launch_prologue(const Params &p, int dtype, bool do_q, bool do_kv, hipStream_t s);
-hipError_t launch_rows_f32(const Params &p, hipStream_t s);
-hipError_t launch_split_bf16(const Params &p, bool prepared_q, hipStream_t s);
+hipError_t launch_rows_f32(const Params &p, hipStream_t s, const Timing &tm);
+hipError_t launch_split_bf16(const Params &p, bool prepared_q, hipStream_t s, const Timing &tm);
 hipError_t launch_combine_bf16(const Params &p, hipStream_t s);
 
 }  // namespace qsa

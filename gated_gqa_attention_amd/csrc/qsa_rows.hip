@@ -204,20 +204,13 @@ hipError_t launch_prologue(const Params &p, int dtype, bool do_q, bool do_kv, hi
                     : prologue_for<float, float>(p, do_q, do_kv, s);
 }
 
-hipError_t launch_rows_f32(const Params &p, hipStream_t s) {
+hipError_t launch_rows_f32(const Params &p, hipStream_t s, const Timing &tm) {
   const int64_t blocks = (int64_t)p.B * p.L * p.Hq;
   switch (p.D) {
-    case 64:
-      hipLaunchKernelGGL((rows_f32_kernel<64>), dim3(blocks), dim3(kThreads), 0, s, p);
-      break;
-    case 128:
-      hipLaunchKernelGGL((rows_f32_kernel<128>), dim3(blocks), dim3(kThreads), 0, s, p);
-      break;
-    case 256:
-      hipLaunchKernelGGL((rows_f32_kernel<256>), dim3(blocks), dim3(kThreads), 0, s, p);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 64: launch_kernel(rows_f32_kernel<64>, blocks, s, tm, p); break;
+    case 128: launch_kernel(rows_f32_kernel<128>, blocks, s, tm, p); break;
+    case 256: launch_kernel(rows_f32_kernel<256>, blocks, s, tm, p); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -624,22 +624,22 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Params p) {
 }
 
 template <int D>
-static hipError_t launch_split_d(const Params &p, bool prep, hipStream_t s) {
+static hipError_t launch_split_d(const Params &p, bool prep, hipStream_t s, const Timing &tm) {
   const int64_t blocks = (int64_t)p.B * p.Hkv * p.tiles * p.chunks;
   if (prep)
-    hipLaunchKernelGGL((split_kernel<D, true, kTileRows>), dim3(blocks), dim3(kThreads), 0, s, p);
+    launch_kernel(split_kernel<D, true, kTileRows>, blocks, s, tm, p);
   else if (p.rows <= 16)
-    hipLaunchKernelGGL((split_kernel<D, false, 16>), dim3(blocks), dim3(kThreads), 0, s, p);
+    launch_kernel(split_kernel<D, false, 16>, blocks, s, tm, p);
   else
-    hipLaunchKernelGGL((split_kernel<D, false, kTileRows>), dim3(blocks), dim3(kThreads), 0, s, p);
+    launch_kernel(split_kernel<D, false, kTileRows>, blocks, s, tm, p);
   return hipGetLastError();
 }
 
-hipError_t launch_split_bf16(const Params &p, bool prepared_q, hipStream_t s) {
+hipError_t launch_split_bf16(const Params &p, bool prepared_q, hipStream_t s, const Timing &tm) {
   switch (p.D) {
-    case 64: return launch_split_d<64>(p, prepared_q, s);
-    case 128: return launch_split_d<128>(p, prepared_q, s);
-    case 256: return launch_split_d<256>(p, prepared_q, s);
+    case 64: return launch_split_d<64>(p, prepared_q, s, tm);
+    case 128: return launch_split_d<128>(p, prepared_q, s, tm);
+    case 256: return launch_split_d<256>(p, prepared_q, s, tm);
     default: return hipErrorInvalidValue;
   }
 }

@@ -92,6 +92,11 @@ typedef struct {
   void *workspace;           /* device scratch, zero-filled before its first use */
   size_t workspace_bytes;    /* >= qsa_workspace_size(cfg) */
   void *stream;              /* hipStream_t to launch on; NULL = the null stream */
+  void *timing_begin;        /* optional hipEvent_t, recorded on stream right before the call's
+                                attention kernel (the one that reads the KV cache) is launched;
+                                NULL for none.  For profilers and benchmarks; leave both NULL
+                                while the stream is being captured into a graph. */
+  void *timing_end;          /* optional hipEvent_t, recorded right after that launch */
 } qsa_cfg;
 
 /* KV cache of one attention layer.  Token-major: row t of sequence b is
@@ -106,11 +111,11 @@ typedef struct {
   int64_t num_rows;          /* host: rows allocated in k and in v */
 } qsa_kv_cache;
 
-/* Bytes of workspace a call with this cfg needs (split-K partials, arrival
- * counters, the prepared queries of long calls and a 256-byte header).  The
- * workspace must be zero-filled once before its first use; every call leaves
- * its counters at zero again.  Calls that share a workspace must be ordered
- * on one stream.  Returns 0 if cfg is invalid (see qsa_last_error()). */
+/* Bytes of workspace a call with this cfg needs (split-K partials, the
+ * prepared queries of long calls and a 256-byte header holding the device
+ * error bits).  The workspace must be zero-filled once before its first use.
+ * Calls that share a workspace must be ordered on one stream.  Returns 0 if
+ * cfg is invalid (see qsa_last_error()). */
 size_t qsa_workspace_size(const qsa_cfg *cfg);
 
 /* Steps 2-4 for the keys only: normalise and rotate k_new, round, and write it

@@ -125,3 +125,27 @@ def test_workspace_scales_with_chunks():
     one = binding.workspace_size(cfg_for(w, force_splits=1))
     many = binding.workspace_size(cfg_for(w, force_splits=32))
     assert many > one >= 256
+
+
+def test_ctypes_structs_match_the_header_layout(tmp_path):
+    """Every field of the ctypes mirrors sits at the offset a C compiler gives it."""
+    structs = {"qsa_cfg": binding.Cfg, "qsa_kv_cache": binding.KVCache}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "qsa.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = {}
+    for line in subprocess.check_output([str(exe)], text=True).splitlines():
+        s, f, v = line.split()
+        got[(s, f)] = int(v)
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
