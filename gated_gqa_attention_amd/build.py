@@ -18,7 +18,13 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqsa.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["qsa_api.hip", "qsa_rows.hip", "qsa_tiles.hip"]
+SOURCES = ["qsa_api.hip", "qsa_rows.hip", "qsa_tiles.hip", "qsa_stream.hip"]
+# per-source extra flags: the streaming kernel takes its first thirteen argument
+# dwords (metadata, query, weight and position pointers, grid shape) preloaded
+# into SGPRs
+# (its LDS copies set M0 from inline assembly, hence -Wno-inline-asm: nothing
+# else in that file uses M0)
+EXTRA = {"qsa_stream.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=13", "-Wno-inline-asm"]}
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,7 +37,7 @@ FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr}")

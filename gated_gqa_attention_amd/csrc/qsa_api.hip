@@ -86,7 +86,10 @@ int make_plan(const qsa_cfg *c, Plan *pl) {
     p.chunk_keys = (int)S;
     p.blocks = B * L * Hq;
   } else {
-    const bool fused = rows_total <= qsa::kTileRows && L <= qsa::kMaxFusedNewRows;
+    // The short-query kernel packs L, G and Hq into one 32-bit argument and
+    // tabulates (cos, sin) for its L positions x r/2 pairs in LDS.
+    const bool fused = rows_total <= qsa::kTileRows && L <= qsa::kMaxFusedNewRows && c->num_q_heads <= 32767 &&
+                       L * (c->rotary_dim / 2) <= qsa::kMaxTableEntries;
     p.route = fused ? kRouteFused : kRoutePrepared;
     p.tiles = (int)cdiv(rows_total, qsa::kTileRows);
     p.rows = (int)std::min<int64_t>(rows_total, qsa::kTileRows);
@@ -146,6 +149,7 @@ qsa::Params base_params(const qsa_cfg *c, const Plan &pl) {
   p.scale_log2 = p.scale * qsa::kLog2e;
   for (int i = 0; i < c->rotary_dim / 2; ++i)
     p.inv_freq[i] = std::pow((double)c->rope_theta, -2.0 * i / (double)c->rotary_dim);
+  p.log2_theta = std::log2((double)c->rope_theta);
   p.wq = c->q_norm_w;
   p.wk = c->k_norm_w;
   return p;
@@ -292,7 +296,7 @@ int qsa_gated_attention(const void *q_gate, const void *k_new, const void *v_new
       if (e == hipSuccess) e = qsa::launch_rows_f32(p, s, tm);
       break;
     case kRouteFused:
-      e = qsa::launch_split_bf16(p, false, s, tm);
+      e = qsa::launch_stream_bf16(p, s, tm);
       if (e == hipSuccess && pl.chunks > 1) e = qsa::launch_combine_bf16(p, s);
       break;
     default:

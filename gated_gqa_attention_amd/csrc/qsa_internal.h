@@ -22,6 +22,7 @@ constexpr int kTileRows = 64;         // query rows (group heads x new rows) per
 constexpr int kMaxFusedNewRows = 16;  // new rows a fused call may append per sequence
 constexpr int kMaxPairs = 128;        // rotary pairs (rotary_dim / 2) supported
 constexpr int kMaxChunks = 4096;      // key chunks per (sequence, KV head, tile)
+constexpr int kMaxTableEntries = 1024;  // (cos, sin) pairs a short-query call tabulates: L * r/2
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Workspace layout (bytes, 256-aligned sections):
@@ -59,6 +60,7 @@ struct Params {
   float *part_ml;
   float *part_o;
   void *qt;
+  double log2_theta;           // log2(theta), computed on the host in double
   double inv_freq[kMaxPairs];  // theta^(-2i/r), computed on the host in double
 };
 
@@ -86,15 +88,20 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// cos/sin of pair i at position pos.  The angle pos * theta^(-2i/r) reaches
-// 3e4 rad, so it is formed and reduced modulo 2*pi in double (two-part
-// Cody-Waite constant), and only the reduced angle goes through fp32 sincos.
-__device__ __forceinline__ void rope_cs(const Params &p, int pos, int i, float &c, float &s) {
-  const double a = (double)pos * p.inv_freq[i];
+// cos/sin of the angle pos * inv, inv = theta^(-2i/r).  The angle reaches 3e4
+// rad, so it is formed and reduced modulo 2*pi in double (two-part Cody-Waite
+// constant), and only the reduced angle goes through fp32 sincos.
+__device__ __forceinline__ void rope_angle_cs(int pos, double inv, float &c, float &s) {
+  const double a = (double)pos * inv;
   const double k = rint(a * 0.15915494309189535);  // 1 / (2 pi)
   double red = fma(-k, 6.283185307179586, a);
   red = fma(-k, 2.4492935982947064e-16, red);
   sincosf((float)red, &s, &c);
+}
+
+// cos/sin of rotary pair i at position pos.
+__device__ __forceinline__ void rope_cs(const Params &p, int pos, int i, float &c, float &s) {
+  rope_angle_cs(pos, p.inv_freq[i], c, s);
 }
 
 // Keys [0, kend) of one (sequence, row tile) are cut into max(1, kend / chunk_keys)
@@ -138,6 +145,7 @@ inline void launch_kernel(Kernel kernel, int64_t blocks, hipStream_t s, const Ti
 hipError_t launch_prologue(const Params &p, int dtype, bool do_q, bool do_kv, hipStream_t s);
 hipError_t launch_rows_f32(const Params &p, hipStream_t s, const Timing &tm);
 hipError_t launch_split_bf16(const Params &p, bool prepared_q, hipStream_t s, const Timing &tm);
+hipError_t launch_stream_bf16(const Params &p, hipStream_t s, const Timing &tm);
 hipError_t launch_combine_bf16(const Params &p, hipStream_t s);
 
 }  // namespace qsa

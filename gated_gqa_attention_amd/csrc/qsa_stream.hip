@@ -1,0 +1,678 @@
+// qsa_stream.hip -- bf16 gated grouped-query attention for short query blocks
+// (decode, speculative verify, ragged batched decode) on gfx950.
+//
+// stream_kernel: one workgroup = (sequence b, KV head g, key chunk).  Its rows
+// are the G query heads of KV head g times the L new rows (DS4Server issue
+// #113, Reproduction: query heads grouped within their KV group; Atlas
+// Qwen35ForwardConfig: 16 query / 4 KV heads), at most 64, in order
+// r = l * G + (h - g * G).
+//
+// Memory pipeline.  The chunk's cached keys stream through a ring of 64-key
+// stages in LDS (64 KB for K and 64 KB for V at head_dim 256).  Stages are
+// copied straight from HBM into LDS by global_load_lds_dwordx4 (no register
+// staging); a stage's rows are XOR-swizzled in 16-byte units so that both the
+// K operand reads (16 keys, one column) and the transposing V reads are free
+// of bank conflicts.  While the first stages are in flight the workgroup
+// splits q_gate, RMS-normalises and rotates its query rows (mlxd PR #99
+// Summary and config audit table; Atlas FullAttentionLayer q_norm / k_norm,
+// Qwen35ForwardConfig::rotary_dim), and the workgroup whose chunk ends the
+// sequence does the same for the new keys, which it keeps in LDS and appends
+// to the cache at the end (Atlas qwen3_5/mod.rs module doc: append at
+// cache_pos, attend over cache_pos + 1 keys).
+//
+// Compute.  Each wavefront owns one 16-key block of every stage and keeps its
+// own online softmax (log2 domain) over all row tiles:
+//   S^T[key][row] = K[key][:] . Q[row][:]      v_mfma_f32_16x16x32_bf16
+//   O^T[dim][row] += V^T[dim][key] . P^T[key][row]   v_mfma_f32_16x16x16_bf16
+// With lane l, g = l / 16, m = l % 16, the score tile leaves keys 4g .. 4g+3 of
+// row m in lane l, which is exactly the lane's share of the P^T operand.  The
+// four wavefronts merge their (max, sum, output) through LDS at the end.  A
+// chunk that covers the whole sequence applies the gate attn * sigmoid(gate)
+// (mlxd PR #99 Summary) and stores bf16; otherwise it writes the chunk's
+// (max, sum, unnormalised output) for the merge kernel.
+//
+// Counters.  The copies are issued from inline assembly and waited for
+// explicitly (s_waitcnt vmcnt with the number of younger copies): the compiler
+// cannot count them, and any load it had to wait for after them would drain
+// the whole ring.  So every small load the prologue needs lands before the
+// first copy is issued, and later loads are consumed only after the stages.
+#include <type_traits>
+
+#include "qsa_internal.h"
+
+namespace qsa {
+
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D>
+struct Geo {
+  static constexpr int RB = 2 * D;                      // bytes of one key row of one KV head
+  static constexpr int OCT = D / 8;                     // 16-byte units per row
+  static constexpr int SW = (OCT < 16 ? OCT : 16) - 1;  // XOR swizzle mask over units
+  static constexpr int SK = 64;                         // keys per stage
+  static constexpr int STAGE = SK * RB;                 // bytes per stage and tensor
+  static constexpr int RING = 65536;                    // bytes per tensor ring
+  static constexpr int NS = RING / STAGE;               // stages in flight
+  static constexpr int LPS = SK * OCT / kThreads;       // 16-byte copies per thread, stage and tensor
+  static constexpr int KST = D / 32;                    // k-steps of the score product
+  static constexpr int NDB = D / 16;                    // 16-dim blocks of the value product
+  static constexpr int E = D / 16;                      // elements per lane in row work (16 lanes per row)
+  static constexpr int SCR = 16 * D * 4;                // 16 fp32 rows; later new K | new V tiles
+  static constexpr int TAB_N = kMaxTableEntries;        // (cos, sin) entries
+  static constexpr int OB_STRIDE = D + 4;               // floats per row of the merge buffer
+};
+
+__device__ __forceinline__ f32x4 mfma_qk(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_pv(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + __expf(-z)); }
+
+// Waits for this wave's LDS operations, then for every wave of the workgroup.
+// Vector-memory copies still in flight are not waited for.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// One 16-byte HBM -> LDS copy per lane: lane i writes LDS bytes lds + 16 i.
+// The LDS address must be uniform over the wave (it goes through M0).
+__device__ __forceinline__ void dma16_asm(const void *src, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most `younger` stages (2 * LPS copies each) are outstanding.
+template <int LPS2, int NS>
+__device__ __forceinline__ void wait_stages(int younger) {
+  static_assert((NS - 1) * LPS2 <= 63, "vmcnt field");
+  switch (younger) {
+    case 0: wait_vm<0>(); break;
+    case 1: if constexpr (NS > 1) wait_vm<1 * LPS2>(); break;
+    case 2: if constexpr (NS > 2) wait_vm<2 * LPS2>(); break;
+    case 3: if constexpr (NS > 3) wait_vm<3 * LPS2>(); break;
+    case 4: if constexpr (NS > 4) wait_vm<4 * LPS2>(); break;
+    case 5: if constexpr (NS > 5) wait_vm<5 * LPS2>(); break;
+    case 6: if constexpr (NS > 6) wait_vm<6 * LPS2>(); break;
+    default: if constexpr (NS > 7) wait_vm<7 * LPS2>(); break;
+  }
+}
+
+// Global loads through the global address space (never flat).
+template <typename T> struct nat { using type = T; };
+template <> struct nat<uint4> { using type = unsigned __attribute__((ext_vector_type(4))); };
+template <> struct nat<uint2> { using type = unsigned __attribute__((ext_vector_type(2))); };
+template <typename T>
+__device__ __forceinline__ T gld(const void *ptr) {
+  using N = typename nat<T>::type;
+  return __builtin_bit_cast(T, *(const __attribute__((address_space(1))) N *)ptr);
+}
+
+// E consecutive bf16 values as raw 16- or 8-byte pieces.
+template <int E>
+struct RawE {
+  static constexpr int NV = E >= 8 ? E / 8 : 1;
+  using V = typename std::conditional<E >= 8, uint4, uint2>::type;
+  V v[NV];
+  __device__ __forceinline__ void load(const bf16_t *src) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = gld<V>(src + i * (E >= 8 ? 8 : 4));
+  }
+  // Make the compiler wait for the load here (an empty use of the registers).
+  __device__ __forceinline__ void land() const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const typename nat<V>::type r = __builtin_bit_cast(typename nat<V>::type, v[i]);
+      asm volatile("" ::"v"(r));
+    }
+  }
+  __device__ __forceinline__ void to_float(float *x) const {
+    constexpr int PER = E >= 8 ? 8 : 4;
+    typedef __bf16 bfP __attribute__((ext_vector_type(PER)));
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const bfP b = __builtin_bit_cast(bfP, v[i]);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) x[i * PER + j] = (float)b[j];
+    }
+  }
+};
+
+// Byte offset of (row, 16-byte unit) in a swizzled tile of `rb`-byte rows.
+template <int SW>
+__device__ __forceinline__ int swz(int row, int unit, int rb) {
+  return row * rb + 16 * (unit ^ (row & SW));
+}
+
+// Store E floats (rounded to bf16) of one row at elements [e0, e0 + E) of a swizzled tile.
+template <int D>
+__device__ __forceinline__ void put_row_bf16(unsigned char *tile, int rb, int row, int e0, const float *x) {
+  using G = Geo<D>;
+  constexpr int E = G::E;
+  if constexpr (E >= 8) {
+#pragma unroll
+    for (int u = 0; u < E / 8; ++u) {
+      bf16x8 v;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = (bf16_t)x[8 * u + j];
+      *(bf16x8 *)(tile + swz<G::SW>(row, e0 / 8 + u, rb)) = v;
+    }
+  } else {
+    bf16x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = (bf16_t)x[j];
+    *(bf16x4 *)(tile + swz<G::SW>(row, e0 / 8, rb) + 8 * ((e0 / 4) & 1)) = v;
+  }
+}
+
+// RMS norm and partial rotation of one head row held by 16 lanes (E elements
+// each, lane c16 holds elements E*c16 .. E*c16+E-1).  scr_row: this row's fp32
+// scratch (D floats); cs: (cos, sin) of this row's position for pairs
+// 0 .. r/2-1.  Every LDS read of a lane is issued before any is used.
+template <int D>
+__device__ __forceinline__ void norm_rope(float (&x)[D / 16], const float (&w)[D / 16], bool valid, float eps,
+                                          int r, const float2 *cs, float *scr_row) {
+  constexpr int E = D / 16;
+  const int c16 = threadIdx.x & 15;
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < E; ++j) ss += x[j] * x[j];
+  ss += __shfl_xor(ss, 1, kWave);
+  ss += __shfl_xor(ss, 2, kWave);
+  ss += __shfl_xor(ss, 4, kWave);
+  ss += __shfl_xor(ss, 8, kWave);
+  const float inv = valid ? 1.0f / sqrtf(ss / (float)D + eps) : 0.f;
+#pragma unroll
+  for (int j = 0; j < E; ++j) x[j] = x[j] * inv * w[j];
+  if (r == 0) return;
+  const int half = r / 2;
+#pragma unroll
+  for (int j = 0; j < E; j += 4) *(float4 *)(scr_row + c16 * E + j) = make_float4(x[j], x[j + 1], x[j + 2], x[j + 3]);
+  wave_lds_sync();
+  if (c16 * E >= r) return;                             // no rotated element in this lane
+  float xp[E], c[E], sn[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int e = c16 * E + j;
+    const bool lo = e < half;
+    xp[j] = scr_row[lo ? e + half : e - half];          // in range for every e < D
+  }
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int e = c16 * E + j;
+    const int i = min(e < half ? e : e - half, half - 1);
+    const float2 v = cs[i];
+    c[j] = v.x;
+    sn[j] = v.y;
+  }
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int e = c16 * E + j;
+    const float lo_v = x[j] * c[j] - xp[j] * sn[j], hi_v = x[j] * c[j] + xp[j] * sn[j];
+    x[j] = e < half ? lo_v : (e < r ? hi_v : x[j]);
+  }
+}
+
+// Scores, online softmax and value product of one 16-key block against all
+// row tiles.  kt / vt: the block's first K / V row in a swizzled LDS tile of
+// rb-byte rows whose swizzle phase starts at this block (blocks are 16-aligned).
+// Key j of the block (global index key0 + j) is visible to row r when
+// j < nvalid and key0 + j <= lim[r] (causal limit n_b + l_r).
+template <int D, int RTM>
+__device__ __forceinline__ void attend_block(const unsigned char *kt, const unsigned char *vt, int rb, int nvalid,
+                                             int64_t key0, const bf16x8 (&qf)[RTM][D / 32],
+                                             f32x4 (&O)[RTM][D / 16], float (&m)[RTM], float (&lsum)[RTM],
+                                             const int64_t (&lim)[RTM], int RT, float scale_log2) {
+  using G = Geo<D>;
+  const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
+  f32x4 S[RTM];
+#pragma unroll
+  for (int rt = 0; rt < RTM; ++rt) S[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < G::KST; ++ks) {
+    const bf16x8 a = *(const bf16x8 *)(kt + swz<G::SW>(m16, 4 * ks + g4, rb));
+#pragma unroll
+    for (int rt = 0; rt < RTM; ++rt)
+      if (rt < RT) S[rt] = mfma_qk(a, qf[rt][ks], S[rt]);
+  }
+  s16x4 pb[RTM];
+#pragma unroll
+  for (int rt = 0; rt < RTM; ++rt) {
+    if (rt >= RT) continue;
+    float s[4], bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * g4 + i;
+      const bool ok = j < nvalid && key0 + j <= lim[rt];
+      s[i] = ok ? S[rt][i] * scale_log2 : -INFINITY;
+      bm = fmaxf(bm, s[i]);
+    }
+    bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+    const float mn = fmaxf(m[rt], bm);
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    const float alpha = exp2f(m[rt] - mu);
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16_t pv = (bf16_t)exp2f(s[i] - mu);
+      ps += (float)pv;
+      pb[rt][i] = __builtin_bit_cast(short, pv);
+    }
+    ps += __shfl_xor(ps, 16, kWave);
+    ps += __shfl_xor(ps, 32, kWave);
+    lsum[rt] = lsum[rt] * alpha + ps;
+    // rescale only rows whose running max rose (a row still at -inf holds zeros);
+    // skipping a factor of exactly 1 changes nothing
+    const bool rescale = alpha != 1.f && m[rt] != -INFINITY;
+    m[rt] = mn;
+    if (__any(rescale)) {
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db) O[rt][db] *= alpha;
+    }
+  }
+  // V^T operand of dims 16 db .. 16 db + 15 and the block's 16 keys: lane (g4, i)
+  // addresses the 8-byte piece (key 4 g4 + i/4, dims 16 db + 4 (i%4) ..) and
+  // receives dim 16 db + i of keys 4 g4 .. 4 g4 + 3.
+  const int vk = 4 * g4 + (m16 >> 2), q4 = m16 & 3;
+#pragma unroll
+  for (int db = 0; db < G::NDB; ++db) {
+    const int unit = 2 * db + (q4 >> 1);
+    const unsigned char *src = vt + swz<G::SW>(vk, unit, rb) + 8 * (q4 & 1);
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src);
+#pragma unroll
+    for (int rt = 0; rt < RTM; ++rt)
+      if (rt < RT) O[rt][db] = mfma_pv(a, pb[rt], O[rt][db]);
+  }
+}
+
+}  // namespace
+
+// RTW: row tiles (16 rows each) per wavefront; BPW: 16-key blocks per
+// wavefront and stage.  Up to 32 rows every wave covers all rows and one block
+// of each stage; above 32 rows waves 0, 1 cover row tiles 0, 1 and waves 2, 3
+// row tiles 2, 3, each pair splitting a stage's four blocks.
+//
+// The leading arguments are preloaded into SGPRs at wave launch, so the loads
+// that need only them (sequence metadata, query rows, query norm weight,
+// positions) are issued at once.  All of them are waited for before the first
+// copy is issued: the vector-memory counter retires in order, and a load
+// consumed after the copies would make its consumer wait for every copy.
+// lgh packs L (bits 0-7), G (bits 8-15) and Hq (bits 16-31).
+template <int D, int RTW, int BPW>
+__global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restrict__ seq_lens,
+                                                          const int64_t *__restrict__ seq_offset,
+                                                          const bf16_t *__restrict__ q_gate,
+                                                          const bf16_t *__restrict__ wq_ptr,
+                                                          const int32_t *__restrict__ positions, int nslot, int hkv,
+                                                          int lgh, Params p) {
+  using G = Geo<D>;
+  constexpr int E = G::E, KST = G::KST, NDB = G::NDB, RB = G::RB, NS = G::NS, LPS = G::LPS;
+  constexpr int RTALL = BPW == 2 ? 4 : RTW;             // row tiles of the workgroup (at most)
+  __shared__ __attribute__((aligned(16))) unsigned char ring[2 * G::RING];   // K ring | V ring
+  unsigned char *const kring = ring, *const vring = ring + G::RING;
+  __shared__ __attribute__((aligned(16))) float scr[G::SCR / 4];
+  __shared__ __attribute__((aligned(16))) float2 tab[G::TAB_N];
+  __shared__ float wml[4][16][2];
+  __shared__ int spos[kMaxFusedNewRows];
+  unsigned char *const scrb = (unsigned char *)scr;
+
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+  const int lane = t % kWave, g4 = lane >> 4, m16 = lane & 15;
+  const int chunk = blockIdx.x / nslot, slot = blockIdx.x % nslot;
+  const int b = slot / hkv, kvh = slot % hkv;
+  const int L = lgh & 0xff, Gq = (lgh >> 8) & 0xff, Hq = lgh >> 16;
+  const int R = L * Gq, RT = (R + 15) / 16;
+
+  // ------------------------------------------------------------ round trip 1: everything small
+  const int n = seq_lens[b];
+  const int64_t off = seq_offset[b];
+  RawE<E> qraw[RTALL];                                  // query half, row 16 rt + 4 wave + g4
+#pragma unroll
+  for (int rt = 0; rt < RTALL; ++rt) {
+    const int r = min(16 * rt + 4 * wave + g4, R - 1);
+    const int l = r / Gq, h = kvh * Gq + r % Gq;
+    qraw[rt].load(q_gate + (((int64_t)b * L + l) * Hq + h) * 2 * D + E * m16);
+  }
+  RawE<E> wqraw;
+  wqraw.load(wq_ptr + E * m16);
+  const int tpos = positions[(int64_t)b * L + min(t, L - 1)];
+  // arguments that live in memory, fetched in the same round trip
+  const int ck = p.chunk_keys, msl = p.max_seq_len, rdim = p.r, pchunks = p.chunks;
+  const int64_t nrows = p.num_rows;
+  const bf16_t *const kc = (const bf16_t *)p.kc;
+  const bf16_t *const vc = (const bf16_t *)p.vc;
+  const bf16_t *const knew = (const bf16_t *)p.k_new;
+  const double l2t = p.log2_theta;
+  const float eps = p.eps, sl2 = p.scale_log2;
+  __builtin_amdgcn_sched_barrier(0);                   // every load above is issued before any wait
+  asm volatile("" ::"s"(n), "s"(off), "s"(ck), "s"(msl), "s"(rdim), "s"(pchunks), "s"(nrows), "s"(kc), "s"(vc),
+               "s"(knew), "s"(l2t), "s"(eps), "s"(sl2));
+#pragma unroll
+  for (int rt = 0; rt < RTALL; ++rt) qraw[rt].land();
+  wqraw.land();
+  asm volatile("" ::"v"(tpos));
+
+  const int64_t total = (int64_t)n + L;
+  const bool in_range = n >= 0 && off >= 0 && total <= msl && off + total <= nrows;
+  // capacity only guards the writes at the end; its load is issued now so that
+  // its round trip overlaps the stages
+  const int32_t *const capp = p.capacity;
+  const int cap = capp ? capp[b] : 0x7fffffff;
+  const int64_t kend = total;
+  const int nch = chunk_count(kend, ck);
+  if (chunk >= nch) return;
+  if (!in_range) {
+    if (chunk == 0) {
+      for (int e = t; e < R * D; e += kThreads) {
+        const int r = e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
+        ((bf16_t *)p.out)[(((int64_t)b * L + l) * Hq + h) * D + d] = (bf16_t)__builtin_nanf("");
+      }
+      if (t == 0) flag_error(p);
+    }
+    return;
+  }
+  const int64_t k0 = (int64_t)chunk * ck;
+  const int64_t k1 = chunk == nch - 1 ? kend : k0 + ck;
+  const bool fuse_new = knew != nullptr;
+  const bool tail = fuse_new && chunk == nch - 1;       // this workgroup holds the new keys
+  const int64_t cend = fuse_new ? min(k1, (int64_t)n) : k1;   // cached keys [k0, cend)
+  const int nst = cend > k0 ? (int)((cend - k0 + G::SK - 1) / G::SK) : 0;
+
+  // ------------------------------------------------------------ ring fill
+  const unsigned kring_lds = (unsigned)(uintptr_t)(lds_void *)kring;
+  const unsigned vring_lds = (unsigned)(uintptr_t)(lds_void *)vring;
+  auto issue_stage = [&](int st) {   // keys k0 + 64 st .. into ring slot st % NS
+#pragma unroll
+    for (int i = 0; i < LPS; ++i) {
+      const int u = t + kThreads * i;
+      const int key = u / G::OCT, pos = u % G::OCT, oct = pos ^ (key & G::SW);
+      const int64_t kk = min(k0 + (int64_t)G::SK * st + key, cend - 1);
+      const int64_t e = ((off + kk) * hkv + kvh) * D + 8 * oct;
+      const unsigned dst = (st % NS) * G::STAGE + kThreads * 16 * i + wave * 1024;
+      dma16_asm(kc + e, kring_lds + dst);
+      dma16_asm(vc + e, vring_lds + dst);
+    }
+  };
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+    if (st < nst) issue_stage(st);
+
+  // new keys and values (tail workgroup): consumed only after the key stages
+  RawE<E> knraw, vnraw, wkraw;
+  if (tail) {
+    const int l = min(4 * wave + g4, L - 1);
+    const int64_t src = (((int64_t)b * L + l) * hkv + kvh) * D + E * m16;
+    knraw.load(knew + src);
+    vnraw.load((const bf16_t *)p.v_new + src);
+    wkraw.load((const bf16_t *)p.wk + E * m16);
+  }
+
+  // ------------------------------------------------------------ rotation table
+  const int half = rdim / 2;
+  if (t < L) spos[t] = tpos;
+  lds_barrier();
+  {   // L * r/2 <= TAB_N (a condition of this route)
+    for (int e = t; e < L * half; e += kThreads) {
+      // theta^(-2i/r) = exp2(-(2i/r) log2 theta)
+      const double inv = exp2(-2.0 * (double)(e % half) / (double)rdim * l2t);
+      float c, s;
+      rope_angle_cs(spos[e / half], inv, c, s);
+      tab[e] = make_float2(c, s);
+    }
+  }
+  lds_barrier();
+
+  // ------------------------------------------------------------ query rows -> MFMA operands
+  float wq[E];
+  wqraw.to_float(wq);
+  const int rtb = BPW == 2 ? 2 * (wave >> 1) : 0;     // first row tile of this wave
+  const int rtw = max(0, min(RTW, RT - rtb));          // row tiles this wave works on
+  bf16x8 qf[RTW][KST];
+  int64_t lim[RTW];
+#pragma unroll
+  for (int q = 0; q < RTW; ++q) lim[q] = (int64_t)n + (16 * (rtb + q) + m16) / Gq;
+  const int srow = 4 * wave + g4;                       // scratch row of this lane group
+  float *const my_scr = scr + srow * D;
+  auto cs_of = [&](int l, float2 *&cs) { cs = tab + l * half; };
+  auto prep_pass = [&](const int rt, const RawE<E> &raw) {
+    const int r = 16 * rt + srow;
+    const bool valid = r < R;
+    const int l = min(r, R - 1) / Gq;
+    float x[E];
+    raw.to_float(x);
+    float2 *cs;
+    cs_of(l, cs);
+    norm_rope<D>(x, wq, valid, eps, rdim, cs, my_scr);
+    wave_lds_sync();
+    // bf16 copy of the row into its own scratch row (stride 4D bytes, swizzled units)
+    put_row_bf16<D>(scrb, 4 * D, srow, E * m16, x);
+    lds_barrier();
+#pragma unroll
+    for (int q = 0; q < RTW; ++q)
+      if (rt == rtb + q) {
+#pragma unroll
+        for (int ks = 0; ks < KST; ++ks) qf[q][ks] = *(const bf16x8 *)(scrb + swz<G::SW>(m16, 4 * ks + g4, 4 * D));
+      }
+    lds_barrier();
+  };
+  prep_pass(0, qraw[0]);
+  if constexpr (RTALL > 1) {
+    if (1 < RT) prep_pass(1, qraw[1]);
+  }
+  if constexpr (RTALL > 2) {
+    if (2 < RT) prep_pass(2, qraw[2]);
+    if (3 < RT) prep_pass(3, qraw[3]);
+  }
+
+  // ------------------------------------------------------------ key stages
+  f32x4 O[RTW][NDB];
+  float mrun[RTW], lrun[RTW];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) {
+    mrun[rt] = -INFINITY;
+    lrun[rt] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) O[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int st = 0; st < nst; ++st) {
+    wait_stages<2 * LPS, NS>(min(NS - 1, nst - 1 - st));
+    lds_barrier();
+#pragma nounroll
+    for (int k = 0; k < BPW; ++k) {
+      const int blk = BPW == 2 ? (wave & 1) + 2 * k : wave;
+      const int64_t bk0 = k0 + (int64_t)G::SK * st + 16 * blk;
+      const int nvalid = (int)min<int64_t>(16, cend - bk0);
+      if (nvalid > 0) {
+        const int so = (st % NS) * G::STAGE + 16 * blk * RB;
+        attend_block<D, RTW>(kring + so, vring + so, RB, nvalid, bk0, qf, O, mrun, lrun, lim, rtw, sl2);
+      }
+    }
+    lds_barrier();
+    if (st + NS < nst) issue_stage(st + NS);
+  }
+
+  // ------------------------------------------------------------ new keys (tail workgroup)
+  // scr becomes the new K tile (rows 0..15, RB bytes each, swizzled) followed by
+  // the new V tile; rows >= L are zero.
+  if (tail) {
+    float wk[E], x[E], v[E];
+    wkraw.to_float(wk);
+    knraw.to_float(x);
+    vnraw.to_float(v);
+    const int l = srow;
+    const bool valid = l < L;
+    float2 *cs;
+    cs_of(min(l, L - 1), cs);
+    norm_rope<D>(x, wk, valid, eps, rdim, cs, my_scr);
+    if (!valid) {
+#pragma unroll
+      for (int j = 0; j < E; ++j) v[j] = 0.f;
+    }
+    lds_barrier();                                      // every wave is done with the fp32 scratch
+    put_row_bf16<D>(scrb, RB, l, E * m16, x);
+    put_row_bf16<D>(scrb + 16 * RB, RB, l, E * m16, v);  // v_new is bf16 already: exact
+    lds_barrier();
+    const int nb = (int)((cend - k0 + 15) / 16);        // cached 16-key blocks, dealt round robin
+    if (BPW == 2 ? (wave & 1) == nb % 2 : wave == nb % 4)
+      attend_block<D, RTW>(scrb, scrb + 16 * RB, RB, L, (int64_t)n, qf, O, mrun, lrun, lim, rtw, sl2);
+  }
+
+  // ------------------------------------------------------------ capacity (guards the writes)
+  const bool cap_ok = total <= (int64_t)cap;
+
+  // ------------------------------------------------------------ merge the four wavefronts
+  lds_barrier();
+  float *const obuf = (float *)ring;                    // [4 waves][16 rows][OB_STRIDE]
+  static_assert(4 * 16 * G::OB_STRIDE * 4 <= 2 * G::RING, "merge buffer");
+  const bool single = nch == 1;
+  const int64_t slot_rows = ((int64_t)slot * pchunks + chunk) * p.rows;
+  for (int rt = 0; rt < RT; ++rt) {
+    // this wave's statistics and unnormalised output for rows 16 rt .. 16 rt + 15
+    // (a wave that does not cover this tile contributes max -inf, sum 0, output 0)
+    float mm = -INFINITY, ll = 0.f;
+    f32x4 *const orow = (f32x4 *)(obuf + (wave * 16 + m16) * G::OB_STRIDE + 4 * g4);
+    bool mine = false;
+#pragma unroll
+    for (int q = 0; q < RTW; ++q)
+      if (rt == rtb + q) {
+        mine = true;
+        mm = mrun[q];
+        ll = lrun[q];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) orow[4 * db] = O[q][db];
+      }
+    if (!mine) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) orow[4 * db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (g4 == 0) {
+      wml[wave][m16][0] = mm;
+      wml[wave][m16][1] = ll;
+    }
+    lds_barrier();
+    // thread t: row t / 16 of the tile, elements E * (t % 16) .. + E
+    const int row = t / 16, e0 = E * (t % 16), r = 16 * rt + row;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wml[w][row][0]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float fw[4], Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      fw[w] = exp2f(wml[w][row][0] - Mu);
+      Ls += wml[w][row][1] * fw[w];
+    }
+    float acc[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float *src = obuf + (w * 16 + row) * G::OB_STRIDE + e0;
+#pragma unroll
+      for (int j = 0; j < E; j += 4) {
+        const float4 v = *(const float4 *)(src + j);
+        acc[j] += v.x * fw[w];
+        acc[j + 1] += v.y * fw[w];
+        acc[j + 2] += v.z * fw[w];
+        acc[j + 3] += v.w * fw[w];
+      }
+    }
+    if (r < R) {
+      const int l = r / Gq, h = kvh * Gq + r % Gq;
+      const int64_t orow_i = ((int64_t)b * L + l) * Hq + h;
+      if (single) {
+        float z[E];
+        RawE<E> zr;
+        zr.load(q_gate + orow_i * 2 * D + D + e0);
+        zr.to_float(z);
+        const float inv = 1.f / Ls;
+#pragma unroll
+        for (int j = 0; j < E; ++j) z[j] = cap_ok ? acc[j] * inv * sigmoid_f(z[j]) : __builtin_nanf("");
+        bf16_t *dst = (bf16_t *)p.out + orow_i * D + e0;
+#pragma unroll
+        for (int j = 0; j < E; j += 4) {
+          bf16x4 o4 = {(bf16_t)z[j], (bf16_t)z[j + 1], (bf16_t)z[j + 2], (bf16_t)z[j + 3]};
+          *(bf16x4 *)(dst + j) = o4;
+        }
+      } else if (cap_ok) {
+        float *po = p.part_o + (slot_rows + r) * D + e0;
+#pragma unroll
+        for (int j = 0; j < E; j += 4) *(float4 *)(po + j) = make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
+        if (t % 16 == 0) *(float2 *)(p.part_ml + (slot_rows + r) * 2) = make_float2(M, Ls);
+      }
+    }
+    lds_barrier();
+  }
+  if (!cap_ok) {
+    // the sequence's rows would pass its capacity: NaN outputs (written above when
+    // the chunk is the whole sequence), no partials, no append, error bit set
+    if (chunk == 0) {
+      if (!single) {
+        for (int e = t; e < R * D; e += kThreads) {
+          const int r = e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
+          ((bf16_t *)p.out)[(((int64_t)b * L + l) * Hq + h) * D + d] = (bf16_t)__builtin_nanf("");
+        }
+      }
+      if (t == 0) flag_error(p);
+    }
+    return;
+  }
+
+  // ------------------------------------------------------------ append the new rows to the cache
+  if (tail) {
+    for (int u = t; u < 16 * G::OCT; u += kThreads) {
+      const int l = u / G::OCT, oct = u % G::OCT;
+      if (l < L) {
+        const int64_t dst = ((off + n + l) * hkv + kvh) * D + 8 * oct;
+        const uint4 kv = *(const uint4 *)(scrb + swz<G::SW>(l, oct, RB));
+        const uint4 vv = *(const uint4 *)(scrb + 16 * RB + swz<G::SW>(l, oct, RB));
+        *(uint4 *)((bf16_t *)p.kc + dst) = kv;
+        *(uint4 *)((bf16_t *)p.vc + dst) = vv;
+      }
+    }
+  }
+}
+
+template <int D, int RTW, int BPW>
+static void launch_stream_rt(const Params &p, hipStream_t s, const Timing &tm) {
+  const int nslot = p.B * p.Hkv;
+  const int64_t blocks = (int64_t)nslot * p.chunks;
+  const int lgh = p.L | (p.G << 8) | (p.Hq << 16);
+  launch_kernel(stream_kernel<D, RTW, BPW>, blocks, s, tm, p.seq_lens, p.seq_offset, (const bf16_t *)p.q_gate,
+                (const bf16_t *)p.wq, p.positions, nslot, p.Hkv, lgh, p);
+}
+
+template <int D>
+static hipError_t launch_stream_d(const Params &p, hipStream_t s, const Timing &tm) {
+  if (p.rows <= 16)
+    launch_stream_rt<D, 1, 1>(p, s, tm);
+  else if (p.rows <= 32)
+    launch_stream_rt<D, 2, 1>(p, s, tm);
+  else if (p.rows <= 64)
+    launch_stream_rt<D, 2, 2>(p, s, tm);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_bf16(const Params &p, hipStream_t s, const Timing &tm) {
+  switch (p.D) {
+    case 64: return launch_stream_d<64>(p, s, tm);
+    case 128: return launch_stream_d<128>(p, s, tm);
+    case 256: return launch_stream_d<256>(p, s, tm);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace qsa

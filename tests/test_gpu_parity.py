@@ -88,7 +88,7 @@ SMALL = [
              rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=100, seed=109),
     Workload("bf16_prefill_l17", batch=1, q_len=17, num_q_heads=4, num_kv_heads=2, head_dim=128,
              rotary_dim=32, rope_theta=1e7, dtype="bf16", prior=33, seed=110),
-    # 64 cached + 16 new keys in one chunk: the new rows join the first stage's spare rows
+    # 64 cached + 16 new keys in one chunk: one full stage plus the new-key block
     Workload("bf16_new_rows_fold", batch=2, q_len=16, num_q_heads=4, num_kv_heads=1, head_dim=256,
              rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=64, seed=112),
 ]
@@ -163,9 +163,22 @@ def test_append_then_attend_equals_fused():
     split = Session(w, inp)
     split.append()
     b = to_np(split.run(fused=False))
-    assert np.array_equal(a, b)
-    assert torch.equal(fused.dev["k_cache"], split.dev["k_cache"])
+    # both equal the oracle; between themselves they differ only by the order in
+    # which fp32 sums meet the new keys (the fused call attends them from its own
+    # LDS copy), so by at most a couple of bf16 ulps of an output element
+    out, _, _ = oracle.gated_attention(geo(w), inp)
+    check(a, out, w.dtype, "fused")
+    check(b, out, w.dtype, "append then attend")
+    ulp = 2.0 ** -7
+    diff = float(np.max(np.abs(a - b)))
+    say(f"  fused vs append+attend: max_abs={diff:.3g} rel_l2={rel_l2(a, b):.3g}")
+    assert diff <= 1e-3
+    assert rel_l2(a, b) <= 1e-3
+    # appended rows: V is copied exactly; K is an fp32 norm and rotation rounded
+    # once, so the two kernels' roundings agree to one bf16 ulp
     assert torch.equal(fused.dev["v_cache"], split.dev["v_cache"])
+    ka, kb = to_np(fused.dev["k_cache"]), to_np(split.dev["k_cache"])
+    assert np.all(np.abs(ka - kb) <= ulp * np.maximum(np.abs(ka), np.abs(kb)))
 
 
 def test_split_count_invariance():
@@ -193,15 +206,21 @@ def test_repeat_calls_are_idempotent():
     assert sess.device_error() == 0
 
 
-def test_device_side_range_error_is_reported_not_faulted():
-    """A sequence whose rows would pass its capacity gets NaN outputs and a
-    workspace flag; its cache rows are not written; other sequences are fine."""
+@pytest.mark.parametrize("case", ["capacity_one_chunk", "capacity_split", "length_past_bound"])
+def test_device_side_range_error_is_reported_not_faulted(case):
+    """A sequence whose rows would pass its capacity (or the call's max_seq_len)
+    gets NaN outputs and a workspace flag; its cache rows are not written; the
+    other sequence is unaffected.  Every case stays inside the buffers."""
     w = Workload("range", batch=2, q_len=1, num_q_heads=8, num_kv_heads=2, head_dim=256,
                  rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=50, seed=111)
     inp = make_inputs(w)
-    sess = Session(w, inp, max_seq_len=64)
-    sess.dev["capacity"][1] = 40           # sequence 1 claims fewer rows than n + L
+    sess = Session(w, inp, max_seq_len=64, force_splits=3 if case == "capacity_split" else 0)
+    if case == "length_past_bound":
+        sess.dev["seq_lens"][1] = 70       # n + L exceeds max_seq_len (and the sequence's rows)
+    else:
+        sess.dev["capacity"][1] = 40       # sequence 1 claims fewer rows than n + L
     kc = sess.dev["k_cache"].clone()
+    print(f"range case {case}", flush=True)
     out = to_np(sess.run())
     torch.cuda.synchronize()
     assert np.all(np.isnan(out[1]))
