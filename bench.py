@@ -59,7 +59,7 @@ def kernel_source_hash():
     """Hash of the sources that define the attention kernels (their device code and
     the parameter block they read); a traffic figure taken on other sources is stale."""
     h = hashlib.sha256()
-    for name in ("qsa_tiles.hip", "qsa_internal.h"):
+    for name in ("qsa_stream.hip", "qsa_tiles.hip", "qsa_internal.h"):
         h.update(open(os.path.join(ROOT, "gated_gqa_attention_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
@@ -294,7 +294,8 @@ def main():
     k_s = kernel_ms / 1e3
     hbm_bound = w.name != "prefill_4b"
     traffic = traffic_from_profiles(w.name)
-    kname = "split_kernel" if w.dtype == "bf16" else "rows_f32_kernel"
+    route = plan.split("route=")[1].split()[0]
+    kname = {"fused_splitk": "stream_kernel", "prepared_tiles": "split_kernel"}.get(route, "rows_f32_kernel")
     if hbm_bound:
         ach = bytes_kernel / k_s / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

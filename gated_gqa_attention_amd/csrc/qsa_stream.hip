@@ -69,11 +69,37 @@ struct Geo {
 __device__ __forceinline__ f32x4 mfma_qk(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma_pv(s16x4 a, s16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + __expf(-z)); }
+
+// Cross-lane reductions without LDS traffic.  Each step combines a lane with
+// one partner symmetrically (a + b == b + a), so every lane of a group ends
+// with the bitwise same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {   // DPP move (row_ror / quad_perm), all lanes valid
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+// sum over the 16 lanes of a row
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0x128>(v);   // row_ror:8
+  v += dpp<0x124>(v);   // row_ror:4
+  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  return v;
+}
+// combine lanes i, i^16, i^32, i^48 (the four rows) with gfx950's lane swaps
+__device__ __forceinline__ float rows4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+__device__ __forceinline__ float rows4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
 
 // Waits for this wave's LDS operations, then for every wave of the workgroup.
 // Vector-memory copies still in flight are not waited for.
@@ -186,10 +212,7 @@ __device__ __forceinline__ void norm_rope(float (&x)[D / 16], const float (&w)[D
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < E; ++j) ss += x[j] * x[j];
-  ss += __shfl_xor(ss, 1, kWave);
-  ss += __shfl_xor(ss, 2, kWave);
-  ss += __shfl_xor(ss, 4, kWave);
-  ss += __shfl_xor(ss, 8, kWave);
+  ss = row16_sum(ss);
   const float inv = valid ? 1.0f / sqrtf(ss / (float)D + eps) : 0.f;
 #pragma unroll
   for (int j = 0; j < E; ++j) x[j] = x[j] * inv * w[j];
@@ -222,85 +245,131 @@ __device__ __forceinline__ void norm_rope(float (&x)[D / 16], const float (&w)[D
   }
 }
 
-// Scores, online softmax and value product of one 16-key block against all
-// row tiles.  kt / vt: the block's first K / V row in a swizzled LDS tile of
-// rb-byte rows whose swizzle phase starts at this block (blocks are 16-aligned).
-// Key j of the block (global index key0 + j) is visible to row r when
-// j < nvalid and key0 + j <= lim[r] (causal limit n_b + l_r).
+// Exchange area of one stage: the probability tile P[row tile][row][key] in
+// bf16 (row stride padded to 144 bytes, conflict-free for the 16-byte reads
+// of the value product) and each wavefront's block maxima and sums per row.
+struct Xch {
+  static constexpr int PSTRIDE = 64 * 2 + 16;
+  static constexpr int PBYTES = 4 * 16 * PSTRIDE;
+  static constexpr int BYTES = PBYTES + 2 * 4 * 64 * 4;
+};
+
+// One stage of up to 64 keys (global indices key0 ..) held in swizzled LDS
+// tiles kt / vt of RB-byte rows.  Wavefront w scores keys 16w .. 16w+15 against
+// every row tile; the four wavefronts agree on each row's new running max
+// through LDS and publish their probabilities as one bf16 tile; then each
+// wavefront accumulates its own D/4 output dims over all keys of the stage.
+// Key k is visible to row r when k < nkeys and key0 + k <= lim[r] (causal
+// limit n_b + l_r).  Contains two workgroup barriers.
 template <int D, int RTM>
-__device__ __forceinline__ void attend_block(const unsigned char *kt, const unsigned char *vt, int rb, int nvalid,
-                                             int64_t key0, const bf16x8 (&qf)[RTM][D / 32],
-                                             f32x4 (&O)[RTM][D / 16], float (&m)[RTM], float (&lsum)[RTM],
-                                             const int64_t (&lim)[RTM], int RT, float scale_log2) {
+__device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsigned char *vt, int nkeys, int64_t key0,
+                                             const bf16x8 (&qf)[RTM][D / 32], f32x4 (&O)[RTM][D / 64],
+                                             float (&m)[RTM], float (&lsum)[RTM], const int64_t (&lim)[RTM],
+                                             float scale_log2, unsigned char *xch) {
   using G = Geo<D>;
+  constexpr int KST = D / 32, DBW = D / 64, RB = G::RB;
   const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  float *const wmax = (float *)(xch + Xch::PBYTES);     // [4 waves][64 rows]
+  float *const wsum = wmax + 4 * 64;
+  const int nvalid = max(0, min(16, nkeys - 16 * wave));
+
+  // scores of this wavefront's 16 keys
   f32x4 S[RTM];
 #pragma unroll
   for (int rt = 0; rt < RTM; ++rt) S[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (nvalid > 0) {
+    const unsigned char *kb = kt + 16 * wave * RB;
 #pragma unroll
-  for (int ks = 0; ks < G::KST; ++ks) {
-    const bf16x8 a = *(const bf16x8 *)(kt + swz<G::SW>(m16, 4 * ks + g4, rb));
+    for (int ks = 0; ks < KST; ++ks) {
+      const bf16x8 a = *(const bf16x8 *)(kb + swz<G::SW>(m16, 4 * ks + g4, RB));
 #pragma unroll
-    for (int rt = 0; rt < RTM; ++rt)
-      if (rt < RT) S[rt] = mfma_qk(a, qf[rt][ks], S[rt]);
+      for (int rt = 0; rt < RTM; ++rt) S[rt] = mfma_qk(a, qf[rt][ks], S[rt]);
+    }
   }
-  s16x4 pb[RTM];
+  float sc[RTM][4];
 #pragma unroll
   for (int rt = 0; rt < RTM; ++rt) {
-    if (rt >= RT) continue;
-    float s[4], bm = -INFINITY;
+    float bm = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = 4 * g4 + i;
-      const bool ok = j < nvalid && key0 + j <= lim[rt];
-      s[i] = ok ? S[rt][i] * scale_log2 : -INFINITY;
-      bm = fmaxf(bm, s[i]);
+      const bool ok = j < nvalid && key0 + 16 * wave + j <= lim[rt];
+      sc[rt][i] = ok ? S[rt][i] * scale_log2 : -INFINITY;
+      bm = fmaxf(bm, sc[rt][i]);
     }
-    bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
-    const float mn = fmaxf(m[rt], bm);
+    bm = rows4_max(bm);
+    if (g4 == 0) wmax[wave * 64 + 16 * rt + m16] = bm;
+  }
+  lds_barrier();
+
+  // new running max of each row, probabilities, block sums
+  float alpha[RTM];
+  bool rescale = false;
+#pragma unroll
+  for (int rt = 0; rt < RTM; ++rt) {
+    const int row = 16 * rt + m16;
+    const float M = fmaxf(fmaxf(wmax[row], wmax[64 + row]), fmaxf(wmax[128 + row], wmax[192 + row]));
+    const float mn = fmaxf(m[rt], M);
     const float mu = mn == -INFINITY ? 0.f : mn;
-    const float alpha = exp2f(m[rt] - mu);
+    alpha[rt] = exp2f(m[rt] - mu);
+    rescale |= alpha[rt] != 1.f && m[rt] != -INFINITY;
+    m[rt] = mn;
     float ps = 0.f;
+    bf16x4 pv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bf16_t pv = (bf16_t)exp2f(s[i] - mu);
-      ps += (float)pv;
-      pb[rt][i] = __builtin_bit_cast(short, pv);
+      pv[i] = (bf16_t)exp2f(sc[rt][i] - mu);
+      ps += (float)pv[i];
     }
-    ps += __shfl_xor(ps, 16, kWave);
-    ps += __shfl_xor(ps, 32, kWave);
-    lsum[rt] = lsum[rt] * alpha + ps;
-    // rescale only rows whose running max rose (a row still at -inf holds zeros);
-    // skipping a factor of exactly 1 changes nothing
-    const bool rescale = alpha != 1.f && m[rt] != -INFINITY;
-    m[rt] = mn;
-    if (__any(rescale)) {
-#pragma unroll
-      for (int db = 0; db < G::NDB; ++db) O[rt][db] *= alpha;
-    }
+    *(bf16x4 *)(xch + (16 * rt + m16) * Xch::PSTRIDE + 2 * (16 * wave + 4 * g4)) = pv;
+    ps = rows4_sum(ps);
+    if (g4 == 0) wsum[wave * 64 + row] = ps;
   }
-  // V^T operand of dims 16 db .. 16 db + 15 and the block's 16 keys: lane (g4, i)
-  // addresses the 8-byte piece (key 4 g4 + i/4, dims 16 db + 4 (i%4) ..) and
-  // receives dim 16 db + i of keys 4 g4 .. 4 g4 + 3.
-  const int vk = 4 * g4 + (m16 >> 2), q4 = m16 & 3;
+  lds_barrier();
 #pragma unroll
-  for (int db = 0; db < G::NDB; ++db) {
-    const int unit = 2 * db + (q4 >> 1);
-    const unsigned char *src = vt + swz<G::SW>(vk, unit, rb) + 8 * (q4 & 1);
-    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src);
+  for (int rt = 0; rt < RTM; ++rt) {
+    const int row = 16 * rt + m16;
+    lsum[rt] = lsum[rt] * alpha[rt] + ((wsum[row] + wsum[64 + row]) + (wsum[128 + row] + wsum[192 + row]));
+  }
+  if (__any(rescale)) {
 #pragma unroll
     for (int rt = 0; rt < RTM; ++rt)
-      if (rt < RT) O[rt][db] = mfma_pv(a, pb[rt], O[rt][db]);
+#pragma unroll
+      for (int db = 0; db < DBW; ++db) O[rt][db] *= alpha[rt];
+  }
+
+  // value product over this wavefront's dims: O^T[dim][row] += V^T[dim][key] P^T[key][row].
+  // V^T operand (dims dim0 + m16, keys kb + 8 g4 .. + 7) from two transposing
+  // reads; lane (g4, i) addresses the 8-byte piece (key kb + 8 g4 + i/4 (+4),
+  // dims dim0 + 4 (i%4) ..) of the swizzled V tile.
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    if (32 * ks >= nkeys) break;
+    bf16x8 bp[RTM];
+#pragma unroll
+    for (int rt = 0; rt < RTM; ++rt)
+      bp[rt] = *(const bf16x8 *)(xch + (16 * rt + m16) * Xch::PSTRIDE + 2 * (32 * ks + 8 * g4));
+    const int vk = 32 * ks + 8 * g4 + (m16 >> 2), q4 = m16 & 3;
+#pragma unroll
+    for (int db = 0; db < DBW; ++db) {
+      const int unit = 2 * (DBW * wave + db) + (q4 >> 1);
+      const unsigned char *p0 = vt + swz<G::SW>(vk, unit, RB) + 8 * (q4 & 1);
+      const unsigned char *p1 = vt + swz<G::SW>(vk + 4, unit, RB) + 8 * (q4 & 1);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const bf16x8 a = __builtin_bit_cast(bf16x8, v8);
+#pragma unroll
+      for (int rt = 0; rt < RTM; ++rt) O[rt][db] = mfma_qk(a, bp[rt], O[rt][db]);
+    }
   }
 }
 
 }  // namespace
 
-// RTW: row tiles (16 rows each) per wavefront; BPW: 16-key blocks per
-// wavefront and stage.  Up to 32 rows every wave covers all rows and one block
-// of each stage; above 32 rows waves 0, 1 cover row tiles 0, 1 and waves 2, 3
-// row tiles 2, 3, each pair splitting a stage's four blocks.
+// RTM: row tiles (16 rows each) of the workgroup, ceil(L * G / 16).
 //
 // The leading arguments are preloaded into SGPRs at wave launch, so the loads
 // that need only them (sequence metadata, query rows, query norm weight,
@@ -308,7 +377,7 @@ __device__ __forceinline__ void attend_block(const unsigned char *kt, const unsi
 // copy is issued: the vector-memory counter retires in order, and a load
 // consumed after the copies would make its consumer wait for every copy.
 // lgh packs L (bits 0-7), G (bits 8-15) and Hq (bits 16-31).
-template <int D, int RTW, int BPW>
+template <int D, int RTM>
 __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restrict__ seq_lens,
                                                           const int64_t *__restrict__ seq_offset,
                                                           const bf16_t *__restrict__ q_gate,
@@ -316,13 +385,12 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
                                                           const int32_t *__restrict__ positions, int nslot, int hkv,
                                                           int lgh, Params p) {
   using G = Geo<D>;
-  constexpr int E = G::E, KST = G::KST, NDB = G::NDB, RB = G::RB, NS = G::NS, LPS = G::LPS;
-  constexpr int RTALL = BPW == 2 ? 4 : RTW;             // row tiles of the workgroup (at most)
+  constexpr int E = G::E, KST = G::KST, RB = G::RB, NS = G::NS, LPS = G::LPS, DBW = D / 64;
+  constexpr int SCR = G::SCR > Xch::BYTES ? G::SCR : Xch::BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char ring[2 * G::RING];   // K ring | V ring
   unsigned char *const kring = ring, *const vring = ring + G::RING;
-  __shared__ __attribute__((aligned(16))) float scr[G::SCR / 4];
+  __shared__ __attribute__((aligned(16))) float scr[SCR / 4];   // row scratch, then the stage exchange
   __shared__ __attribute__((aligned(16))) float2 tab[G::TAB_N];
-  __shared__ float wml[4][16][2];
   __shared__ int spos[kMaxFusedNewRows];
   unsigned char *const scrb = (unsigned char *)scr;
 
@@ -332,14 +400,14 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   const int chunk = blockIdx.x / nslot, slot = blockIdx.x % nslot;
   const int b = slot / hkv, kvh = slot % hkv;
   const int L = lgh & 0xff, Gq = (lgh >> 8) & 0xff, Hq = lgh >> 16;
-  const int R = L * Gq, RT = (R + 15) / 16;
+  const int R = L * Gq;
 
   // ------------------------------------------------------------ round trip 1: everything small
   const int n = seq_lens[b];
   const int64_t off = seq_offset[b];
-  RawE<E> qraw[RTALL];                                  // query half, row 16 rt + 4 wave + g4
+  RawE<E> qraw[RTM];                                    // query half, row 16 rt + 4 wave + g4
 #pragma unroll
-  for (int rt = 0; rt < RTALL; ++rt) {
+  for (int rt = 0; rt < RTM; ++rt) {
     const int r = min(16 * rt + 4 * wave + g4, R - 1);
     const int l = r / Gq, h = kvh * Gq + r % Gq;
     qraw[rt].load(q_gate + (((int64_t)b * L + l) * Hq + h) * 2 * D + E * m16);
@@ -359,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   asm volatile("" ::"s"(n), "s"(off), "s"(ck), "s"(msl), "s"(rdim), "s"(pchunks), "s"(nrows), "s"(kc), "s"(vc),
                "s"(knew), "s"(l2t), "s"(eps), "s"(sl2));
 #pragma unroll
-  for (int rt = 0; rt < RTALL; ++rt) qraw[rt].land();
+  for (int rt = 0; rt < RTM; ++rt) qraw[rt].land();
   wqraw.land();
   asm volatile("" ::"v"(tpos));
 
@@ -419,92 +487,72 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   }
 
   // ------------------------------------------------------------ rotation table
+  // L * r/2 <= TAB_N is a condition of this route
   const int half = rdim / 2;
   if (t < L) spos[t] = tpos;
   lds_barrier();
-  {   // L * r/2 <= TAB_N (a condition of this route)
-    for (int e = t; e < L * half; e += kThreads) {
-      // theta^(-2i/r) = exp2(-(2i/r) log2 theta)
-      const double inv = exp2(-2.0 * (double)(e % half) / (double)rdim * l2t);
-      float c, s;
-      rope_angle_cs(spos[e / half], inv, c, s);
-      tab[e] = make_float2(c, s);
-    }
+  for (int e = t; e < L * half; e += kThreads) {
+    // theta^(-2i/r) = exp2(-(2i/r) log2 theta)
+    const double inv = exp2(-2.0 * (double)(e % half) / (double)rdim * l2t);
+    float c, s;
+    rope_angle_cs(spos[e / half], inv, c, s);
+    tab[e] = make_float2(c, s);
   }
   lds_barrier();
 
   // ------------------------------------------------------------ query rows -> MFMA operands
   float wq[E];
   wqraw.to_float(wq);
-  const int rtb = BPW == 2 ? 2 * (wave >> 1) : 0;     // first row tile of this wave
-  const int rtw = max(0, min(RTW, RT - rtb));          // row tiles this wave works on
-  bf16x8 qf[RTW][KST];
-  int64_t lim[RTW];
+  bf16x8 qf[RTM][KST];
+  int64_t lim[RTM];
 #pragma unroll
-  for (int q = 0; q < RTW; ++q) lim[q] = (int64_t)n + (16 * (rtb + q) + m16) / Gq;
+  for (int rt = 0; rt < RTM; ++rt) lim[rt] = (int64_t)n + (16 * rt + m16) / Gq;
   const int srow = 4 * wave + g4;                       // scratch row of this lane group
-  float *const my_scr = scr + srow * D;
-  auto cs_of = [&](int l, float2 *&cs) { cs = tab + l * half; };
   auto prep_pass = [&](const int rt, const RawE<E> &raw) {
     const int r = 16 * rt + srow;
     const bool valid = r < R;
     const int l = min(r, R - 1) / Gq;
     float x[E];
     raw.to_float(x);
-    float2 *cs;
-    cs_of(l, cs);
-    norm_rope<D>(x, wq, valid, eps, rdim, cs, my_scr);
+    norm_rope<D>(x, wq, valid, eps, rdim, tab + l * half, scr + srow * D);
     wave_lds_sync();
     // bf16 copy of the row into its own scratch row (stride 4D bytes, swizzled units)
     put_row_bf16<D>(scrb, 4 * D, srow, E * m16, x);
     lds_barrier();
 #pragma unroll
-    for (int q = 0; q < RTW; ++q)
-      if (rt == rtb + q) {
-#pragma unroll
-        for (int ks = 0; ks < KST; ++ks) qf[q][ks] = *(const bf16x8 *)(scrb + swz<G::SW>(m16, 4 * ks + g4, 4 * D));
-      }
+    for (int ks = 0; ks < KST; ++ks) qf[rt][ks] = *(const bf16x8 *)(scrb + swz<G::SW>(m16, 4 * ks + g4, 4 * D));
     lds_barrier();
   };
   prep_pass(0, qraw[0]);
-  if constexpr (RTALL > 1) {
-    if (1 < RT) prep_pass(1, qraw[1]);
-  }
-  if constexpr (RTALL > 2) {
-    if (2 < RT) prep_pass(2, qraw[2]);
-    if (3 < RT) prep_pass(3, qraw[3]);
-  }
+  if constexpr (RTM > 1) prep_pass(1, qraw[1]);
+  if constexpr (RTM > 2) prep_pass(2, qraw[2]);
+  if constexpr (RTM > 3) prep_pass(3, qraw[3]);
 
   // ------------------------------------------------------------ key stages
-  f32x4 O[RTW][NDB];
-  float mrun[RTW], lrun[RTW];
+  f32x4 O[RTM][DBW];
+  float mrun[RTM], lrun[RTM];
 #pragma unroll
-  for (int rt = 0; rt < RTW; ++rt) {
+  for (int rt = 0; rt < RTM; ++rt) {
     mrun[rt] = -INFINITY;
     lrun[rt] = 0.f;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) O[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < DBW; ++db) O[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   for (int st = 0; st < nst; ++st) {
     wait_stages<2 * LPS, NS>(min(NS - 1, nst - 1 - st));
     lds_barrier();
-#pragma nounroll
-    for (int k = 0; k < BPW; ++k) {
-      const int blk = BPW == 2 ? (wave & 1) + 2 * k : wave;
-      const int64_t bk0 = k0 + (int64_t)G::SK * st + 16 * blk;
-      const int nvalid = (int)min<int64_t>(16, cend - bk0);
-      if (nvalid > 0) {
-        const int so = (st % NS) * G::STAGE + 16 * blk * RB;
-        attend_block<D, RTW>(kring + so, vring + so, RB, nvalid, bk0, qf, O, mrun, lrun, lim, rtw, sl2);
-      }
-    }
-    lds_barrier();
+    const int so = (st % NS) * G::STAGE;
+    const int64_t sk0 = k0 + (int64_t)G::SK * st;
+    const int nk = (int)min<int64_t>(G::SK, cend - sk0);
+    attend_stage<D, RTM>(kring + so, vring + so, nk, sk0, qf, O, mrun, lrun, lim, sl2, scrb);
+    lds_barrier();                                      // every wave is done with ring slot st % NS
     if (st + NS < nst) issue_stage(st + NS);
   }
 
   // ------------------------------------------------------------ new keys (tail workgroup)
-  // scr becomes the new K tile (rows 0..15, RB bytes each, swizzled) followed by
-  // the new V tile; rows >= L are zero.
+  // The new rows become one more stage in ring slot 0: K and V rows 0 .. 15
+  // (rows >= L zero) and V rows 16 .. 31 zero (read by the value product).
+  // The fp32 scratch of their norm sits in the K ring past slot 0.
   if (tail) {
     float wk[E], x[E], v[E];
     wkraw.to_float(wk);
@@ -512,107 +560,57 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     vnraw.to_float(v);
     const int l = srow;
     const bool valid = l < L;
-    float2 *cs;
-    cs_of(min(l, L - 1), cs);
-    norm_rope<D>(x, wk, valid, eps, rdim, cs, my_scr);
+    norm_rope<D>(x, wk, valid, eps, rdim, tab + min(l, L - 1) * half, (float *)(kring + G::STAGE) + srow * D);
     if (!valid) {
 #pragma unroll
       for (int j = 0; j < E; ++j) v[j] = 0.f;
     }
-    lds_barrier();                                      // every wave is done with the fp32 scratch
-    put_row_bf16<D>(scrb, RB, l, E * m16, x);
-    put_row_bf16<D>(scrb + 16 * RB, RB, l, E * m16, v);  // v_new is bf16 already: exact
+    float zero[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) zero[j] = 0.f;
+    put_row_bf16<D>(kring, RB, l, E * m16, x);
+    put_row_bf16<D>(vring, RB, l, E * m16, v);          // v_new is bf16 already: exact
+    put_row_bf16<D>(vring, RB, 16 + l, E * m16, zero);
     lds_barrier();
-    const int nb = (int)((cend - k0 + 15) / 16);        // cached 16-key blocks, dealt round robin
-    if (BPW == 2 ? (wave & 1) == nb % 2 : wave == nb % 4)
-      attend_block<D, RTW>(scrb, scrb + 16 * RB, RB, L, (int64_t)n, qf, O, mrun, lrun, lim, rtw, sl2);
+    attend_stage<D, RTM>(kring, vring, L, (int64_t)n, qf, O, mrun, lrun, lim, sl2, scrb);
   }
 
-  // ------------------------------------------------------------ capacity (guards the writes)
+  // ------------------------------------------------------------ outputs
+  // Every wavefront writes its own dims 16 (DBW wave + db) + 4 g4 .. + 3 of row
+  // 16 rt + m16: the gated output when the chunk is the whole sequence, else
+  // the chunk's unnormalised output and (max, sum) for the merge kernel.
   const bool cap_ok = total <= (int64_t)cap;
-
-  // ------------------------------------------------------------ merge the four wavefronts
-  lds_barrier();
-  float *const obuf = (float *)ring;                    // [4 waves][16 rows][OB_STRIDE]
-  static_assert(4 * 16 * G::OB_STRIDE * 4 <= 2 * G::RING, "merge buffer");
   const bool single = nch == 1;
   const int64_t slot_rows = ((int64_t)slot * pchunks + chunk) * p.rows;
-  for (int rt = 0; rt < RT; ++rt) {
-    // this wave's statistics and unnormalised output for rows 16 rt .. 16 rt + 15
-    // (a wave that does not cover this tile contributes max -inf, sum 0, output 0)
-    float mm = -INFINITY, ll = 0.f;
-    f32x4 *const orow = (f32x4 *)(obuf + (wave * 16 + m16) * G::OB_STRIDE + 4 * g4);
-    bool mine = false;
 #pragma unroll
-    for (int q = 0; q < RTW; ++q)
-      if (rt == rtb + q) {
-        mine = true;
-        mm = mrun[q];
-        ll = lrun[q];
+  for (int rt = 0; rt < RTM; ++rt) {
+    const int r = 16 * rt + m16;
+    if (r >= R) continue;
+    const int l = r / Gq, h = kvh * Gq + r % Gq;
+    const int64_t orow = ((int64_t)b * L + l) * Hq + h;
+    if (single) {
+      const float inv = 1.f / lrun[rt];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) orow[4 * db] = O[q][db];
-      }
-    if (!mine) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) orow[4 * db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    if (g4 == 0) {
-      wml[wave][m16][0] = mm;
-      wml[wave][m16][1] = ll;
-    }
-    lds_barrier();
-    // thread t: row t / 16 of the tile, elements E * (t % 16) .. + E
-    const int row = t / 16, e0 = E * (t % 16), r = 16 * rt + row;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, wml[w][row][0]);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    float fw[4], Ls = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      fw[w] = exp2f(wml[w][row][0] - Mu);
-      Ls += wml[w][row][1] * fw[w];
-    }
-    float acc[E];
-#pragma unroll
-    for (int j = 0; j < E; ++j) acc[j] = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float *src = obuf + (w * 16 + row) * G::OB_STRIDE + e0;
-#pragma unroll
-      for (int j = 0; j < E; j += 4) {
-        const float4 v = *(const float4 *)(src + j);
-        acc[j] += v.x * fw[w];
-        acc[j + 1] += v.y * fw[w];
-        acc[j + 2] += v.z * fw[w];
-        acc[j + 3] += v.w * fw[w];
-      }
-    }
-    if (r < R) {
-      const int l = r / Gq, h = kvh * Gq + r % Gq;
-      const int64_t orow_i = ((int64_t)b * L + l) * Hq + h;
-      if (single) {
-        float z[E];
-        RawE<E> zr;
-        zr.load(q_gate + orow_i * 2 * D + D + e0);
+      for (int db = 0; db < DBW; ++db) {
+        const int d = 16 * (DBW * wave + db) + 4 * g4;
+        RawE<4> zr;
+        zr.load(q_gate + orow * 2 * D + D + d);
+        float z[4];
         zr.to_float(z);
-        const float inv = 1.f / Ls;
+        bf16x4 o4;
 #pragma unroll
-        for (int j = 0; j < E; ++j) z[j] = cap_ok ? acc[j] * inv * sigmoid_f(z[j]) : __builtin_nanf("");
-        bf16_t *dst = (bf16_t *)p.out + orow_i * D + e0;
-#pragma unroll
-        for (int j = 0; j < E; j += 4) {
-          bf16x4 o4 = {(bf16_t)z[j], (bf16_t)z[j + 1], (bf16_t)z[j + 2], (bf16_t)z[j + 3]};
-          *(bf16x4 *)(dst + j) = o4;
-        }
-      } else if (cap_ok) {
-        float *po = p.part_o + (slot_rows + r) * D + e0;
-#pragma unroll
-        for (int j = 0; j < E; j += 4) *(float4 *)(po + j) = make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
-        if (t % 16 == 0) *(float2 *)(p.part_ml + (slot_rows + r) * 2) = make_float2(M, Ls);
+        for (int i = 0; i < 4; ++i)
+          o4[i] = (bf16_t)(cap_ok ? O[rt][db][i] * inv * sigmoid_f(z[i]) : __builtin_nanf(""));
+        *(bf16x4 *)((bf16_t *)p.out + orow * D + d) = o4;
       }
+    } else if (cap_ok) {
+#pragma unroll
+      for (int db = 0; db < DBW; ++db) {
+        const int d = 16 * (DBW * wave + db) + 4 * g4;
+        *(float4 *)(p.part_o + (slot_rows + r) * D + d) = make_float4(O[rt][db][0], O[rt][db][1], O[rt][db][2], O[rt][db][3]);
+      }
+      if (wave == 0 && g4 == 0) *(float2 *)(p.part_ml + (slot_rows + r) * 2) = make_float2(mrun[rt], lrun[rt]);
     }
-    lds_barrier();
   }
   if (!cap_ok) {
     // the sequence's rows would pass its capacity: NaN outputs (written above when
@@ -635,34 +633,31 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
       const int l = u / G::OCT, oct = u % G::OCT;
       if (l < L) {
         const int64_t dst = ((off + n + l) * hkv + kvh) * D + 8 * oct;
-        const uint4 kv = *(const uint4 *)(scrb + swz<G::SW>(l, oct, RB));
-        const uint4 vv = *(const uint4 *)(scrb + 16 * RB + swz<G::SW>(l, oct, RB));
-        *(uint4 *)((bf16_t *)p.kc + dst) = kv;
-        *(uint4 *)((bf16_t *)p.vc + dst) = vv;
+        *(uint4 *)((bf16_t *)p.kc + dst) = *(const uint4 *)(kring + swz<G::SW>(l, oct, RB));
+        *(uint4 *)((bf16_t *)p.vc + dst) = *(const uint4 *)(vring + swz<G::SW>(l, oct, RB));
       }
     }
   }
 }
 
-template <int D, int RTW, int BPW>
+template <int D, int RTM>
 static void launch_stream_rt(const Params &p, hipStream_t s, const Timing &tm) {
   const int nslot = p.B * p.Hkv;
   const int64_t blocks = (int64_t)nslot * p.chunks;
   const int lgh = p.L | (p.G << 8) | (p.Hq << 16);
-  launch_kernel(stream_kernel<D, RTW, BPW>, blocks, s, tm, p.seq_lens, p.seq_offset, (const bf16_t *)p.q_gate,
+  launch_kernel(stream_kernel<D, RTM>, blocks, s, tm, p.seq_lens, p.seq_offset, (const bf16_t *)p.q_gate,
                 (const bf16_t *)p.wq, p.positions, nslot, p.Hkv, lgh, p);
 }
 
 template <int D>
 static hipError_t launch_stream_d(const Params &p, hipStream_t s, const Timing &tm) {
-  if (p.rows <= 16)
-    launch_stream_rt<D, 1, 1>(p, s, tm);
-  else if (p.rows <= 32)
-    launch_stream_rt<D, 2, 1>(p, s, tm);
-  else if (p.rows <= 64)
-    launch_stream_rt<D, 2, 2>(p, s, tm);
-  else
-    return hipErrorInvalidValue;
+  switch ((p.rows + 15) / 16) {
+    case 1: launch_stream_rt<D, 1>(p, s, tm); break;
+    case 2: launch_stream_rt<D, 2>(p, s, tm); break;
+    case 3: launch_stream_rt<D, 3>(p, s, tm); break;
+    case 4: launch_stream_rt<D, 4>(p, s, tm); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
