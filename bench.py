@@ -56,11 +56,13 @@ def algorithmic_work(w, seq_lens):
 
 
 def kernel_source_hash():
-    """Hash of the sources that define the attention kernels (their device code and
-    the parameter block they read); a traffic figure taken on other sources is stale."""
+    """Hash of the device sources and the launch planner (every file under csrc/);
+    a traffic figure taken on other sources is stale."""
     h = hashlib.sha256()
-    for name in ("qsa_stream.hip", "qsa_tiles.hip", "qsa_internal.h"):
-        h.update(open(os.path.join(ROOT, "gated_gqa_attention_amd", "csrc", name), "rb").read())
+    csrc = os.path.join(ROOT, "gated_gqa_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -295,7 +297,7 @@ def main():
     hbm_bound = w.name != "prefill_4b"
     traffic = traffic_from_profiles(w.name)
     route = plan.split("route=")[1].split()[0]
-    kname = {"fused_splitk": "stream_kernel", "prepared_tiles": "split_kernel"}.get(route, "rows_f32_kernel")
+    kname = {"fused_splitk": "stream_kernel", "prepared_tiles": "tile_kernel"}.get(route, "rows_f32_kernel")
     if hbm_bound:
         ach = bytes_kernel / k_s / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -18,13 +18,13 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqsa.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["qsa_api.hip", "qsa_rows.hip", "qsa_tiles.hip", "qsa_stream.hip"]
-# per-source extra flags: the streaming kernel takes its first thirteen argument
-# dwords (metadata, query, weight and position pointers, grid shape) preloaded
-# into SGPRs
-# (its LDS copies set M0 from inline assembly, hence -Wno-inline-asm: nothing
-# else in that file uses M0)
-EXTRA = {"qsa_stream.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=13", "-Wno-inline-asm"]}
+SOURCES = ["qsa_api.hip", "qsa_rows.hip", "qsa_stream.hip", "qsa_prefill.hip", "qsa_merge.hip"]
+# per-source extra flags: the streaming and tile kernels take their leading
+# argument dwords (metadata and query pointers, grid shape) preloaded into
+# SGPRs; their LDS copies set M0 from inline assembly, hence -Wno-inline-asm
+# (nothing else in those files uses M0)
+EXTRA = {"qsa_stream.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=13", "-Wno-inline-asm"],
+         "qsa_prefill.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=11", "-Wno-inline-asm"]}
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

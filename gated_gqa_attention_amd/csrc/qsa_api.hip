@@ -91,8 +91,9 @@ int make_plan(const qsa_cfg *c, Plan *pl) {
     const bool fused = rows_total <= qsa::kTileRows && L <= qsa::kMaxFusedNewRows && c->num_q_heads <= 32767 &&
                        L * (c->rotary_dim / 2) <= qsa::kMaxTableEntries;
     p.route = fused ? kRouteFused : kRoutePrepared;
-    p.tiles = (int)cdiv(rows_total, qsa::kTileRows);
-    p.rows = (int)std::min<int64_t>(rows_total, qsa::kTileRows);
+    const int64_t tile_rows = fused ? qsa::kTileRows : qsa::kPrefillTileRows;
+    p.tiles = (int)cdiv(rows_total, tile_rows);
+    p.rows = (int)std::min<int64_t>(rows_total, tile_rows);
     const int64_t base = B * Hkv * p.tiles;
     int64_t ck;
     if (c->force_splits > 0) {
@@ -301,7 +302,7 @@ int qsa_gated_attention(const void *q_gate, const void *k_new, const void *v_new
       break;
     default:
       e = qsa::launch_prologue(p, QSA_BF16, true, has_new, s);
-      if (e == hipSuccess) e = qsa::launch_split_bf16(p, true, s, tm);
+      if (e == hipSuccess) e = qsa::launch_tile_bf16(p, s, tm);
       if (e == hipSuccess && pl.chunks > 1) e = qsa::launch_combine_bf16(p, s);
       break;
   }

@@ -1,0 +1,293 @@
+// qsa_device.h -- device helpers shared by the streaming and tile kernels
+// (gfx950): stage geometry of the HBM -> LDS key ring, the copies and their
+// explicit counter waits, the XOR row swizzle, cross-lane reductions without
+// LDS traffic, and global loads that stay in the global address space.
+#pragma once
+
+#include <type_traits>
+
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D>
+struct Geo {
+  static constexpr int RB = 2 * D;                      // bytes of one key row of one KV head
+  static constexpr int OCT = D / 8;                     // 16-byte units per row
+  static constexpr int SW = (OCT < 16 ? OCT : 16) - 1;  // XOR swizzle mask over units
+  static constexpr int SK = 64;                         // keys per stage
+  static constexpr int STAGE = SK * RB;                 // bytes per stage and tensor
+  static constexpr int RING = 65536;                    // bytes per tensor ring
+  static constexpr int NS = RING / STAGE;               // stages in flight
+  static constexpr int LPS = SK * OCT / kThreads;       // 16-byte copies per thread, stage and tensor
+  static constexpr int KST = D / 32;                    // k-steps of the score product
+  static constexpr int NDB = D / 16;                    // 16-dim blocks of the value product
+  static constexpr int E = D / 16;                      // elements per lane in row work (16 lanes per row)
+  static constexpr int SCR = 16 * D * 4;                // 16 fp32 rows of row scratch
+  static constexpr int TAB_N = kMaxTableEntries;        // (cos, sin) entries
+};
+
+__device__ __forceinline__ f32x4 mfma_qk(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + __expf(-z)); }
+
+// Cross-lane reductions without LDS traffic.  Each step combines a lane with
+// one partner symmetrically (a + b == b + a), so every lane of a group ends
+// with the bitwise same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {   // DPP move (row_ror / quad_perm), all lanes valid
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+// sum over the 16 lanes of a row
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0x128>(v);   // row_ror:8
+  v += dpp<0x124>(v);   // row_ror:4
+  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  return v;
+}
+// combine lanes i, i^16, i^32, i^48 (the four rows) with gfx950's lane swaps
+__device__ __forceinline__ float rows4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+__device__ __forceinline__ float rows4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+// Waits for this wave's LDS operations, then for every wave of the workgroup.
+// Vector-memory copies still in flight are not waited for.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// One 16-byte HBM -> LDS copy per lane: lane i writes LDS bytes lds + 16 i.
+// The LDS address must be uniform over the wave (it goes through M0).
+__device__ __forceinline__ void dma16_asm(const void *src, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most `younger` stages (2 * LPS copies each) are outstanding.
+template <int LPS2, int NS>
+__device__ __forceinline__ void wait_stages(int younger) {
+  static_assert((NS - 1) * LPS2 <= 63, "vmcnt field");
+  switch (younger) {
+    case 0: wait_vm<0>(); break;
+    case 1: if constexpr (NS > 1) wait_vm<1 * LPS2>(); break;
+    case 2: if constexpr (NS > 2) wait_vm<2 * LPS2>(); break;
+    case 3: if constexpr (NS > 3) wait_vm<3 * LPS2>(); break;
+    case 4: if constexpr (NS > 4) wait_vm<4 * LPS2>(); break;
+    case 5: if constexpr (NS > 5) wait_vm<5 * LPS2>(); break;
+    case 6: if constexpr (NS > 6) wait_vm<6 * LPS2>(); break;
+    default: if constexpr (NS > 7) wait_vm<7 * LPS2>(); break;
+  }
+}
+
+// Global loads through the global address space (never flat).
+template <typename T> struct nat { using type = T; };
+template <> struct nat<uint4> { using type = unsigned __attribute__((ext_vector_type(4))); };
+template <> struct nat<uint2> { using type = unsigned __attribute__((ext_vector_type(2))); };
+template <typename T>
+__device__ __forceinline__ T gld(const void *ptr) {
+  using N = typename nat<T>::type;
+  return __builtin_bit_cast(T, *(const __attribute__((address_space(1))) N *)ptr);
+}
+
+// E consecutive bf16 values as raw 16- or 8-byte pieces.
+template <int E>
+struct RawE {
+  static constexpr int NV = E >= 8 ? E / 8 : 1;
+  using V = typename std::conditional<E >= 8, uint4, uint2>::type;
+  V v[NV];
+  __device__ __forceinline__ void load(const bf16_t *src) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = gld<V>(src + i * (E >= 8 ? 8 : 4));
+  }
+  // Make the compiler wait for the load here (an empty use of the registers).
+  __device__ __forceinline__ void land() const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const typename nat<V>::type r = __builtin_bit_cast(typename nat<V>::type, v[i]);
+      asm volatile("" ::"v"(r));
+    }
+  }
+  __device__ __forceinline__ void to_float(float *x) const {
+    constexpr int PER = E >= 8 ? 8 : 4;
+    typedef __bf16 bfP __attribute__((ext_vector_type(PER)));
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const bfP b = __builtin_bit_cast(bfP, v[i]);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) x[i * PER + j] = (float)b[j];
+    }
+  }
+};
+
+// Byte offset of (row, 16-byte unit) in a swizzled tile of `rb`-byte rows.
+template <int SW>
+__device__ __forceinline__ int swz(int row, int unit, int rb) {
+  return row * rb + 16 * (unit ^ (row & SW));
+}
+
+// Store E floats (rounded to bf16) of one row at elements [e0, e0 + E) of a swizzled tile.
+template <int D>
+__device__ __forceinline__ void put_row_bf16(unsigned char *tile, int rb, int row, int e0, const float *x) {
+  using G = Geo<D>;
+  constexpr int E = G::E;
+  if constexpr (E >= 8) {
+#pragma unroll
+    for (int u = 0; u < E / 8; ++u) {
+      bf16x8 v;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = (bf16_t)x[8 * u + j];
+      *(bf16x8 *)(tile + swz<G::SW>(row, e0 / 8 + u, rb)) = v;
+    }
+  } else {
+    bf16x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = (bf16_t)x[j];
+    *(bf16x4 *)(tile + swz<G::SW>(row, e0 / 8, rb) + 8 * ((e0 / 4) & 1)) = v;
+  }
+}
+
+
+// Exchange area of one stage: the probability tile P[row tile][row][key] in
+// bf16 (row stride padded to 144 bytes, conflict-free for the 16-byte reads
+// of the value product) and each wavefront's block maxima and sums per row.
+struct Xch {
+  static constexpr int PSTRIDE = 64 * 2 + 16;
+  static constexpr int PBYTES = 4 * 16 * PSTRIDE;
+  static constexpr int BYTES = PBYTES + 2 * 4 * 64 * 4;
+};
+
+// One stage of up to 64 keys (global indices key0 ..) held in swizzled LDS
+// tiles kt / vt of RB-byte rows.  Wavefront w scores keys 16w .. 16w+15 against
+// every row tile; the four wavefronts agree on each row's new running max
+// through LDS and publish their probabilities as one bf16 tile; then each
+// wavefront accumulates its own D/4 output dims over all keys of the stage.
+// Key k is visible to row r when k < nkeys and key0 + k <= lim[r] (causal
+// limit n_b + l_r).  Contains two workgroup barriers.
+template <int D, int RTM>
+__device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsigned char *vt, int nkeys, int64_t key0,
+                                             const bf16x8 (&qf)[RTM][D / 32], f32x4 (&O)[RTM][D / 64],
+                                             float (&m)[RTM], float (&lsum)[RTM], const int64_t (&lim)[RTM],
+                                             float scale_log2, unsigned char *xch) {
+  using G = Geo<D>;
+  constexpr int KST = D / 32, DBW = D / 64, RB = G::RB;
+  const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  float *const wmax = (float *)(xch + Xch::PBYTES);     // [4 waves][64 rows]
+  float *const wsum = wmax + 4 * 64;
+  const int nvalid = max(0, min(16, nkeys - 16 * wave));
+
+  // scores of this wavefront's 16 keys
+  f32x4 S[RTM];
+#pragma unroll
+  for (int rt = 0; rt < RTM; ++rt) S[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (nvalid > 0) {
+    const unsigned char *kb = kt + 16 * wave * RB;
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks) {
+      const bf16x8 a = *(const bf16x8 *)(kb + swz<G::SW>(m16, 4 * ks + g4, RB));
+#pragma unroll
+      for (int rt = 0; rt < RTM; ++rt) S[rt] = mfma_qk(a, qf[rt][ks], S[rt]);
+    }
+  }
+  float sc[RTM][4];
+#pragma unroll
+  for (int rt = 0; rt < RTM; ++rt) {
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * g4 + i;
+      const bool ok = j < nvalid && key0 + 16 * wave + j <= lim[rt];
+      sc[rt][i] = ok ? S[rt][i] * scale_log2 : -INFINITY;
+      bm = fmaxf(bm, sc[rt][i]);
+    }
+    bm = rows4_max(bm);
+    if (g4 == 0) wmax[wave * 64 + 16 * rt + m16] = bm;
+  }
+  lds_barrier();
+
+  // new running max of each row, probabilities, block sums
+  float alpha[RTM];
+  bool rescale = false;
+#pragma unroll
+  for (int rt = 0; rt < RTM; ++rt) {
+    const int row = 16 * rt + m16;
+    const float M = fmaxf(fmaxf(wmax[row], wmax[64 + row]), fmaxf(wmax[128 + row], wmax[192 + row]));
+    const float mn = fmaxf(m[rt], M);
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    alpha[rt] = exp2f(m[rt] - mu);
+    rescale |= alpha[rt] != 1.f && m[rt] != -INFINITY;
+    m[rt] = mn;
+    float ps = 0.f;
+    bf16x4 pv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = (bf16_t)exp2f(sc[rt][i] - mu);
+      ps += (float)pv[i];
+    }
+    *(bf16x4 *)(xch + (16 * rt + m16) * Xch::PSTRIDE + 2 * (16 * wave + 4 * g4)) = pv;
+    ps = rows4_sum(ps);
+    if (g4 == 0) wsum[wave * 64 + row] = ps;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int rt = 0; rt < RTM; ++rt) {
+    const int row = 16 * rt + m16;
+    lsum[rt] = lsum[rt] * alpha[rt] + ((wsum[row] + wsum[64 + row]) + (wsum[128 + row] + wsum[192 + row]));
+  }
+  if (__any(rescale)) {
+#pragma unroll
+    for (int rt = 0; rt < RTM; ++rt)
+#pragma unroll
+      for (int db = 0; db < DBW; ++db) O[rt][db] *= alpha[rt];
+  }
+
+  // value product over this wavefront's dims: O^T[dim][row] += V^T[dim][key] P^T[key][row].
+  // V^T operand (dims dim0 + m16, keys kb + 8 g4 .. + 7) from two transposing
+  // reads; lane (g4, i) addresses the 8-byte piece (key kb + 8 g4 + i/4 (+4),
+  // dims dim0 + 4 (i%4) ..) of the swizzled V tile.
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    if (32 * ks >= nkeys) break;
+    bf16x8 bp[RTM];
+#pragma unroll
+    for (int rt = 0; rt < RTM; ++rt)
+      bp[rt] = *(const bf16x8 *)(xch + (16 * rt + m16) * Xch::PSTRIDE + 2 * (32 * ks + 8 * g4));
+    const int vk = 32 * ks + 8 * g4 + (m16 >> 2), q4 = m16 & 3;
+#pragma unroll
+    for (int db = 0; db < DBW; ++db) {
+      const int unit = 2 * (DBW * wave + db) + (q4 >> 1);
+      const unsigned char *p0 = vt + swz<G::SW>(vk, unit, RB) + 8 * (q4 & 1);
+      const unsigned char *p1 = vt + swz<G::SW>(vk + 4, unit, RB) + 8 * (q4 & 1);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const bf16x8 a = __builtin_bit_cast(bf16x8, v8);
+#pragma unroll
+      for (int rt = 0; rt < RTM; ++rt) O[rt][db] = mfma_qk(a, bp[rt], O[rt][db]);
+    }
+  }
+}
+
+}  // namespace
+}  // namespace qsa

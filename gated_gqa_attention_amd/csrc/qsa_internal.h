@@ -18,7 +18,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;         // four wavefronts per workgroup
 constexpr int kWave = 64;
 constexpr int kTileKeys = 64;         // keys staged in LDS per pipeline stage
-constexpr int kTileRows = 64;         // query rows (group heads x new rows) per workgroup
+constexpr int kTileRows = 64;         // query rows (group heads x new rows) of a short-query call
+constexpr int kPrefillTileRows = 64;  // query rows per workgroup of the tile (prefill) kernel
 constexpr int kMaxFusedNewRows = 16;  // new rows a fused call may append per sequence
 constexpr int kMaxPairs = 128;        // rotary pairs (rotary_dim / 2) supported
 constexpr int kMaxChunks = 4096;      // key chunks per (sequence, KV head, tile)
@@ -35,7 +36,7 @@ constexpr int32_t kErrRange = 1;
 
 struct Params {
   int B, L, Hq, Hkv, G, D, r;
-  int rows;           // query rows per tile (<= kTileRows)
+  int rows;           // query rows per tile
   int tiles;          // row tiles per (sequence, KV head)
   int chunks;         // grid extent in key chunks = chunk_count(max_seq_len)
   int chunk_keys;     // keys per chunk (the last chunk of a tile also takes the remainder)
@@ -144,7 +145,7 @@ inline void launch_kernel(Kernel kernel, int64_t blocks, hipStream_t s, const Ti
 // (defined in the kernel translation units, called by the C ABI layer)
 hipError_t launch_prologue(const Params &p, int dtype, bool do_q, bool do_kv, hipStream_t s);
 hipError_t launch_rows_f32(const Params &p, hipStream_t s, const Timing &tm);
-hipError_t launch_split_bf16(const Params &p, bool prepared_q, hipStream_t s, const Timing &tm);
+hipError_t launch_tile_bf16(const Params &p, hipStream_t s, const Timing &tm);
 hipError_t launch_stream_bf16(const Params &p, hipStream_t s, const Timing &tm);
 hipError_t launch_combine_bf16(const Params &p, hipStream_t s);
 

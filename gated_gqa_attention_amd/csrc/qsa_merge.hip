@@ -1,0 +1,128 @@
+// qsa_merge.hip -- merge of split-K partials (gfx950).
+//
+// The attention kernels cut the keys of a (sequence, KV head, row tile) into
+// chunks when one workgroup per tile would leave the chip idle (flash-decoding
+// split-K).  Each chunk leaves its running max (log2 domain), sum and
+// unnormalised output; this kernel combines them with log-sum-exp weights and
+// applies the output gate attn * sigmoid(gate) (mlxd PR #99 Summary; Atlas
+// sigmoid_gate).  It runs after the attention kernel on the same stream, so
+// the kernel boundary orders the partials' stores before these loads.
+#include "qsa_device.h"
+
+namespace qsa {
+
+// Merge the key chunks of one (slot, row): weights 2^(m_c - M) / sum_c l_c 2^(m_c - M),
+// weighted sum of the unnormalised chunk outputs, then the sigmoid gate.  Waves
+// take interleaved chunks; lanes take EPL = D/64 dims.
+template <int D>
+__global__ __launch_bounds__(kThreads) void combine_kernel(Params p) {
+  constexpr int EPL = D / kWave;
+  constexpr int kBatch = 16;                            // chunks in flight per wave
+  __shared__ float wts[kMaxChunks];
+  __shared__ float acc_x[kThreads / kWave][D];
+  __shared__ float red[kThreads / kWave];
+  __shared__ float s_inv;
+  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
+  const int rr = blockIdx.x % p.rows;
+  const int slot = blockIdx.x / p.rows;
+  const int tile = slot % p.tiles;
+  const int kvh = (slot / p.tiles) % p.Hkv;
+  const int b = slot / (p.tiles * p.Hkv);
+  const int rows_total = p.L * p.G;
+  const int row0 = tile * p.rows;                      // rows per tile
+  const int R = min(p.rows, rows_total - row0);
+  if (rr >= R) return;
+  const int n = gld<int>(p.seq_lens + b);
+  int64_t off;
+  if (!seq_in_range(p, b, n, off)) return;              // the attention kernel wrote NaN
+  const int lmax = (row0 + R - 1) / p.G;
+  const int nch = chunk_count((int64_t)n + lmax + 1, p.chunk_keys);
+  if (nch == 1) return;                                 // finished by the attention kernel
+
+  // every load first: chunk statistics, the gate, the first batch of partial outputs
+  const int64_t base = (int64_t)slot * p.chunks * p.rows + rr;   // + c * rows
+  const int rg = row0 + rr, l = rg / p.G, h = kvh * p.G + rg % p.G;
+  const bf16_t *zp = (const bf16_t *)p.q_gate + (((int64_t)b * p.L + l) * p.Hq + h) * 2 * D + D + lane * EPL;
+  float z[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) z[j] = (float)gld<bf16_t>(zp + j);
+  const int cm = min(t, nch - 1);
+  const float m_c = gld<float>(p.part_ml + (base + (int64_t)cm * p.rows) * 2);
+  const float l_c = gld<float>(p.part_ml + (base + (int64_t)cm * p.rows) * 2 + 1);
+  float v[kBatch][EPL];
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int c = min(wave + k * (kThreads / kWave), nch - 1);
+    const float *po = p.part_o + (base + (int64_t)c * p.rows) * D + lane * EPL;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) v[k][j] = gld<float>(po + j);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // weights w_c = 2^(m_c - M) / sum_c l_c 2^(m_c - M)   (chunks beyond 256 are rare)
+  float mx = t < nch ? m_c : -INFINITY;
+  for (int c = t + kThreads; c < nch; c += kThreads) mx = fmaxf(mx, p.part_ml[(base + (int64_t)c * p.rows) * 2]);
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float ls = 0.f;
+  if (t < nch) {
+    const float e = exp2f(m_c - M);
+    wts[t] = e;
+    ls = e * l_c;
+  }
+  for (int c = t + kThreads; c < nch; c += kThreads) {
+    const float e = exp2f(p.part_ml[(base + (int64_t)c * p.rows) * 2] - M);
+    wts[c] = e;
+    ls += e * p.part_ml[(base + (int64_t)c * p.rows) * 2 + 1];
+  }
+  ls = wave_sum(ls);
+  __syncthreads();
+  if (lane == 0) red[wave] = ls;
+  __syncthreads();
+  if (t == 0) s_inv = 1.f / ((red[0] + red[1]) + (red[2] + red[3]));
+  __syncthreads();
+
+  float acc[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int c = wave + k * (kThreads / kWave);
+    const float wc = c < nch ? wts[c] : 0.f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) acc[j] += wc * v[k][j];
+  }
+  for (int c0 = wave + kBatch * (kThreads / kWave); c0 < nch; c0 += kThreads / kWave) {
+    const float wc = wts[c0];
+    const float *po = p.part_o + (base + (int64_t)c0 * p.rows) * D + lane * EPL;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) acc[j] += wc * po[j];
+  }
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) acc_x[wave][lane * EPL + j] = acc[j];
+  __syncthreads();
+  if (wave != 0) return;
+  const float inv = s_inv;
+  bf16_t *out = (bf16_t *)p.out + (((int64_t)b * p.L + l) * p.Hq + h) * D;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int d = lane * EPL + j;
+    const float o = ((acc_x[0][d] + acc_x[1][d]) + (acc_x[2][d] + acc_x[3][d])) * inv;
+    out[d] = (bf16_t)(o * sigmoid_f(z[j]));
+  }
+}
+
+hipError_t launch_combine_bf16(const Params &p, hipStream_t s) {
+  const int64_t blocks = (int64_t)p.B * p.Hkv * p.tiles * p.rows;
+  switch (p.D) {
+    case 64: hipLaunchKernelGGL((combine_kernel<64>), dim3(blocks), dim3(kThreads), 0, s, p); break;
+    case 128: hipLaunchKernelGGL((combine_kernel<128>), dim3(blocks), dim3(kThreads), 0, s, p); break;
+    case 256: hipLaunchKernelGGL((combine_kernel<256>), dim3(blocks), dim3(kThreads), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qsa
