@@ -55,18 +55,27 @@ def algorithmic_work(w, seq_lens):
     return kv_read + reads + writes, out, flops
 
 
-def kernel_source_hash():
-    """Hash of the device sources and the launch planner (every file under csrc/);
-    a traffic figure taken on other sources is stale."""
+# Sources that define the kernels of each route (the kernels, their shared
+# device code and the launch planner); a traffic figure taken on other
+# versions of these files is stale.
+ROUTE_SOURCES = {
+    "fused_splitk": ("qsa_stream.hip", "qsa_merge.hip", "qsa_device.h", "qsa_internal.h", "qsa_api.hip"),
+    "prepared_tiles": ("qsa_prefill.hip", "qsa_rows.hip", "qsa_merge.hip", "qsa_device.h", "qsa_internal.h",
+                       "qsa_api.hip"),
+}
+
+
+def kernel_source_hash(route="fused_splitk"):
+    """Hash of the sources the kernels of `route` are built from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_gqa_attention_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in ROUTE_SOURCES[route]:
         h.update(name.encode())
         h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload, per_launch_units=1):
+def traffic_from_profiles(workload, route, per_launch_units=1):
     """HBM bytes per launch from committed rocprofv3 PMC summaries, if they were
     taken on the current kernel sources; otherwise None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
@@ -77,7 +86,7 @@ def traffic_from_profiles(workload, per_launch_units=1):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha") != kernel_source_hash():
+    if vals.get("kernel_source_sha") != kernel_source_hash(route):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"]) * per_launch_units
@@ -295,8 +304,8 @@ def main():
     tfs = flops_call / s_per_step / 1e12
     k_s = kernel_ms / 1e3
     hbm_bound = w.name != "prefill_4b"
-    traffic = traffic_from_profiles(w.name)
     route = plan.split("route=")[1].split()[0]
+    traffic = traffic_from_profiles(w.name, route) if route in ROUTE_SOURCES else None
     kname = {"fused_splitk": "stream_kernel", "prepared_tiles": "tile_kernel"}.get(route, "rows_f32_kernel")
     if hbm_bound:
         ach = bytes_kernel / k_s / 1e9
