@@ -3,27 +3,146 @@
 // rotated the queries into the prepared buffer and appended the new keys and
 // values to the cache (Atlas qwen3_5/mod.rs module doc: append, then attend).
 //
-// tile_kernel: one workgroup = (sequence b, KV head g, tile of 64 query rows,
+// tile_kernel: one workgroup = (sequence b, KV head g, tile of 128 query rows,
 // key chunk).  The rows are (new row l, head of group g) pairs in order
 // r = l * G + (h - g * G) (DS4Server issue #113, Reproduction: query heads
-// grouped within their KV group).  The chunk's keys stream through the same
-// HBM -> LDS ring of 64-key stages as the short-query kernel, and each stage
-// goes through the same step: every wavefront scores its 16 keys against all
-// 64 rows, the four agree on each row's running max and publish a bf16
-// probability tile, and each accumulates its own D/4 output dims over the 64
-// keys.  Per stage a wavefront reads 16 K rows and a quarter of the V tile from
-// LDS for 64 x 64 x D x 4 flops of the workgroup, so the LDS stays well below
-// its bandwidth while the MFMAs work.  A tile covered by one chunk applies the
-// gate attn * sigmoid(gate) (mlxd PR #99 Summary) and stores bf16; otherwise
-// it writes the chunk's (max, sum, unnormalised output) for the merge kernel.
+// grouped within their KV group), so one K/V stream serves the whole group.
+// The chunk's keys stream through an HBM -> LDS ring of 32-key stages; each
+// wavefront owns 32 rows and runs its own online softmax over every stage:
+// scores S^T = K Q^T on MFMA with the queries in registers, the running max and
+// the probabilities in registers, then O^T += V^T P^T on MFMA.  The value
+// product takes its keys in a permuted order that matches the layout the score
+// product leaves the probabilities in, so P never goes through LDS; the
+// transposing LDS reads fetch V^T in that same order.  One workgroup barrier
+// per stage guards the ring slot.  A tile covered by one chunk applies the gate
+// attn * sigmoid(gate) (mlxd PR #99 Summary) and stores bf16; otherwise it
+// writes the chunk's (max, sum, unnormalised output) for the merge kernel.
 #include "qsa_device.h"
 
 namespace qsa {
 
 namespace {
 
-constexpr int kPrefillRows = kPrefillTileRows;   // query rows per workgroup: four 16-row MFMA tiles
-static_assert(kPrefillRows == 64, "the stage step handles four row tiles");
+constexpr int kRowsPerWave = 32;                     // two 16-row MFMA tiles
+constexpr float kLazyMax = 8.f;                      // headroom of the running max, log2 units
+constexpr int kPrefillRows = kPrefillTileRows;       // query rows per workgroup
+static_assert(kPrefillRows == (kThreads / kWave) * kRowsPerWave, "four wavefronts of 32 rows");
+
+template <int D>
+struct PGeo {
+  static constexpr int RB = 2 * D;                      // bytes of one key row of one KV head
+  static constexpr int OCT = D / 8;                     // 16-byte units per row
+  static constexpr int SW = (OCT < 16 ? OCT : 16) - 1;  // XOR swizzle mask over units
+  static constexpr int SK = 32;                         // keys per stage
+  static constexpr int STAGE = SK * RB;                 // bytes per stage and tensor
+  static constexpr int NS = 4;                          // ring slots per tensor
+  static constexpr int LPS = SK * OCT / kThreads;       // 16-byte copies per thread, stage and tensor
+  static_assert(LPS >= 1 && LPS * kThreads == SK * OCT, "stage copies");
+};
+
+// Scores and online softmax of one 32-key stage for this wavefront's two row
+// tiles.  kt: swizzled K stage tile; keys key0 .. key0 + nkeys - 1; row tile
+// rt sees key k when key0 + k <= lim[rt] (causal limit n_b + l).  MASK = false
+// when every key of the stage is visible to every row of the workgroup.  ls
+// holds per-lane partial row sums (the four lanes of a row add up at the end).
+// Leaves the bf16 probabilities in bp in the score layout: lane (g4, m16)
+// holds keys 4 g4 + i and 16 + 4 g4 + i of row m16.
+template <int D, bool MASK>
+__device__ __forceinline__ bool stage_scores(const unsigned char *kt, int nkeys, int64_t key0,
+                                             const bf16x8 (&qf)[2][D / 32], float (&m)[2], float (&ls)[2],
+                                             const int64_t (&lim)[2], float scale_log2, bf16x8 (&bp)[2],
+                                             float (&alpha)[2]) {
+  using G = PGeo<D>;
+  constexpr int KST = D / 32, RB = G::RB;
+  const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
+
+  // S^T[key 16 kb + 4 g4 + i][row m16] of row tile rt, in S[kb][rt][i]
+  f32x4 S[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) S[kb][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Unit 4 ks + g4 of key row 16 kb + m16 sits at unit (4 ks + g4) ^ (m16 & SW)
+  // = 4 ((ks & 3) ^ c) + 16 (ks >> 2) + (g4 ^ (m16 & 3)) with c = (m16 & SW) >> 2,
+  // so four lane offsets cover every k-step (the rest are immediates).
+  const int c = (m16 & G::SW) >> 2;
+  const unsigned char *kl = kt + m16 * RB + 16 * (g4 ^ (m16 & 3));
+#pragma unroll
+  for (int ks = 0; ks < KST; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 a = *(const bf16x8 *)(kl + 64 * ((ks & 3) ^ c) + 256 * (ks >> 2) + 16 * RB * kb);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) S[kb][rt] = mfma_qk(a, qf[rt][ks], S[kb][rt]);
+    }
+
+  bool rescale = false;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    float sc[8], bm = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = S[kb][rt][i] * scale_log2;
+        if constexpr (MASK) {
+          const int k = 16 * kb + 4 * g4 + i;
+          v = (k < nkeys && key0 + k <= lim[rt]) ? v : -INFINITY;
+        }
+        sc[4 * kb + i] = v;
+        bm = fmaxf(bm, v);
+      }
+    bm = rows4_max(bm);
+    // The reference max moves only when the block max passes it by more than
+    // kLazyMax (log2 units), so the probabilities stay <= 2^kLazyMax and the
+    // output rarely needs rescaling; sums, outputs and the chunk's (max, sum)
+    // all refer to the same reference, which keeps the result exact.
+    const bool up = bm > m[rt] + kLazyMax;
+    const float mn = up ? bm : m[rt];
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    alpha[rt] = exp2f(m[rt] - mu);
+    rescale |= up && m[rt] != -INFINITY;
+    m[rt] = mn;
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bp[rt][j] = (bf16_t)exp2f(sc[j] - mu);
+      ps += (float)bp[rt][j];
+    }
+    ls[rt] = ls[rt] * alpha[rt] + ps;
+  }
+  return rescale;
+}
+
+// O^T[dim][row] += V^T[dim][key] P^T[key][row] over one 32-key stage, with the
+// MFMA's k index j of lane group g4 standing for key 4 g4 + j (j < 4) or
+// 16 + 4 g4 + j - 4, the order the probabilities were left in; the transposing
+// reads fetch those two 4-key runs of the swizzled V tile for dims 16 db + m16.
+template <int D>
+__device__ __forceinline__ void stage_values(const unsigned char *vt, const bf16x8 (&bp)[2], f32x4 (&O)[2][D / 16]) {
+  using G = PGeo<D>;
+  constexpr int NDB = D / 16, RB = G::RB;
+  const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
+  // Unit 2 db + h (h = bit 1 of m16) of key row klo sits at unit (2 db + h) ^ s,
+  // s = klo & SW, = 2 ((db % E) ^ (s >> 1)) + 2 E (db / E) + (h ^ (s & 1)) with
+  // E = (SW + 1) / 2; row klo + 16 has the same s.  E lane offsets cover every
+  // dim block.
+  constexpr int E = (G::SW + 1) / 2;
+  const int klo = 4 * g4 + (m16 >> 2), s = klo & G::SW;
+  const unsigned char *vl = vt + klo * RB + 16 * (((m16 >> 1) & 1) ^ (s & 1)) + 8 * (m16 & 1);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const unsigned char *p0 = vl + 32 * ((db % E) ^ (s >> 1)) + 32 * E * (db / E);
+    const unsigned char *p1 = p0 + 16 * RB;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const bf16x8 a = __builtin_bit_cast(bf16x8, v8);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) O[rt][db] = mfma_qk(a, bp[rt], O[rt][db]);
+  }
+}
 
 }  // namespace
 
@@ -36,11 +155,10 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
                                                         const int64_t *__restrict__ seq_offset,
                                                         const bf16_t *__restrict__ qt, int L, int Gq, int Hq,
                                                         int tiles, int nitems, Params p) {
-  using G = Geo<D>;
-  constexpr int KST = D / 32, DBW = D / 64, NS = G::NS, LPS = G::LPS;
-  __shared__ __attribute__((aligned(16))) unsigned char ring[2 * G::RING];   // K ring | V ring
-  __shared__ __attribute__((aligned(16))) unsigned char xch[Xch::BYTES];    // stage exchange
-  unsigned char *const kring = ring, *const vring = ring + G::RING;
+  using G = PGeo<D>;
+  constexpr int KST = D / 32, NDB = D / 16, NS = G::NS, LPS = G::LPS, SK = G::SK;
+  __shared__ __attribute__((aligned(16))) unsigned char ring[2 * NS * G::STAGE];   // K ring | V ring
+  unsigned char *const kring = ring, *const vring = ring + NS * G::STAGE;
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
@@ -54,15 +172,15 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
   const int b = bk / hkv, kvh = bk % hkv;
   const int R = L * Gq;                                 // rows of this KV head
   const int row0 = tile * kPrefillRows;
+  const int wrow0 = row0 + kRowsPerWave * wave;         // this wavefront's first row
 
   // ------------------------------------------------------------ round trip 1: metadata and queries
   const int n = seq_lens[b];
   const int64_t off = seq_offset[b];
-  bf16x8 qf[4][KST];
-  int64_t lim[4];
+  bf16x8 qf[2][KST];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int r = min(row0 + 16 * rt + m16, R - 1);
+  for (int rt = 0; rt < 2; ++rt) {
+    const int r = min(wrow0 + 16 * rt + m16, R - 1);
     const int l = r / Gq, h = kvh * Gq + r % Gq;
     const bf16_t *src = qt + (((int64_t)b * L + l) * Hq + h) * D + 8 * g4;
 #pragma unroll
@@ -77,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::"s"(n), "s"(off), "s"(ck), "s"(msl), "s"(nrows), "s"(kc), "s"(vc), "s"(capp), "s"(sl2));
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int ks = 0; ks < KST; ++ks) {
       typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -103,19 +221,21 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
   }
   const int64_t k0 = (int64_t)chunk * ck;
   const int64_t k1 = chunk == nch - 1 ? kend : k0 + ck;
-  const int nst = (int)((k1 - k0 + G::SK - 1) / G::SK);
+  const int nst = (int)((k1 - k0 + SK - 1) / SK);
+  const int64_t kfull = min(k1, (int64_t)n + row0 / Gq + 1);   // keys below this are visible to every row
+  int64_t lim[2];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) lim[rt] = (int64_t)n + (row0 + 16 * rt + m16) / Gq;
+  for (int rt = 0; rt < 2; ++rt) lim[rt] = (int64_t)n + min(wrow0 + 16 * rt + m16, R - 1) / Gq;
 
   // ------------------------------------------------------------ key stages
   const unsigned kring_lds = (unsigned)(uintptr_t)(lds_void *)kring;
   const unsigned vring_lds = (unsigned)(uintptr_t)(lds_void *)vring;
-  auto issue_stage = [&](int st) {   // keys k0 + 64 st .. into ring slot st % NS
+  auto issue_stage = [&](int st) {   // keys k0 + SK st .. into ring slot st % NS
 #pragma unroll
     for (int i = 0; i < LPS; ++i) {
       const int u = t + kThreads * i;
       const int key = u / G::OCT, pos = u % G::OCT, oct = pos ^ (key & G::SW);
-      const int64_t kk = min(k0 + (int64_t)G::SK * st + key, k1 - 1);
+      const int64_t kk = min(k0 + (int64_t)SK * st + key, k1 - 1);
       const int64_t e = ((off + kk) * hkv + kvh) * D + 8 * oct;
       const unsigned dst = (st % NS) * G::STAGE + kThreads * 16 * i + wave * 1024;
       dma16_asm(kc + e, kring_lds + dst);
@@ -123,45 +243,56 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
     }
   };
 #pragma unroll
-  for (int st = 0; st < NS; ++st)
+  for (int st = 0; st < NS - 1; ++st)
     if (st < nst) issue_stage(st);
 
-  f32x4 O[4][DBW];
-  float mrun[4], lrun[4];
+  f32x4 O[2][NDB];
+  float mrun[2], lrun[2];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+  for (int rt = 0; rt < 2; ++rt) {
     mrun[rt] = -INFINITY;
     lrun[rt] = 0.f;
 #pragma unroll
-    for (int db = 0; db < DBW; ++db) O[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < NDB; ++db) O[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   for (int st = 0; st < nst; ++st) {
-    wait_stages<2 * LPS, NS>(min(NS - 1, nst - 1 - st));
-    lds_barrier();
+    wait_stages<2 * LPS, NS>(min(NS - 2, nst - 1 - st));
+    lds_barrier();                                      // stage st is in LDS; every wave is done with stage st - 1
+    if (st + NS - 1 < nst) issue_stage(st + NS - 1);    // refill the slot of stage st - 1
     const int so = (st % NS) * G::STAGE;
-    const int64_t sk0 = k0 + (int64_t)G::SK * st;
-    const int nk = (int)min<int64_t>(G::SK, k1 - sk0);
-    attend_stage<D, 4>(kring + so, vring + so, nk, sk0, qf, O, mrun, lrun, lim, sl2, xch);
-    lds_barrier();                                      // every wave is done with ring slot st % NS
-    if (st + NS < nst) issue_stage(st + NS);
+    const int64_t sk0 = k0 + (int64_t)SK * st;
+    const int nk = (int)min<int64_t>(SK, k1 - sk0);
+    bf16x8 bp[2];
+    float alpha[2];
+    const bool rescale = sk0 + SK <= kfull
+                             ? stage_scores<D, false>(kring + so, nk, sk0, qf, mrun, lrun, lim, sl2, bp, alpha)
+                             : stage_scores<D, true>(kring + so, nk, sk0, qf, mrun, lrun, lim, sl2, bp, alpha);
+    if (__any(rescale)) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) O[rt][db] *= alpha[rt];
+    }
+    stage_values<D>(vring + so, bp, O);
   }
 
   // ------------------------------------------------------------ outputs
-  // every wavefront writes its own dims 16 (DBW wave + db) + 4 g4 .. + 3
+  // lane (g4, m16) holds dims 16 db + 4 g4 .. + 3 of row m16 of each row tile
   const bool cap_ok = total <= (int64_t)cap;
   const bool single = nch == 1;
   const int64_t slot_rows = ((int64_t)slot * pchunks + chunk) * p.rows;
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int r = row0 + 16 * rt + m16;
+  for (int rt = 0; rt < 2; ++rt) {
+    const float lsum = rows4_sum(lrun[rt]);
+    const int r = wrow0 + 16 * rt + m16;
     if (r >= R) continue;
     const int l = r / Gq, h = kvh * Gq + r % Gq;
     const int64_t orow = ((int64_t)b * L + l) * Hq + h;
     if (single) {
-      const float inv = 1.f / lrun[rt];
+      const float inv = 1.f / lsum;
 #pragma unroll
-      for (int db = 0; db < DBW; ++db) {
-        const int d = 16 * (DBW * wave + db) + 4 * g4;
+      for (int db = 0; db < NDB; ++db) {
+        const int d = 16 * db + 4 * g4;
         RawE<4> zr;
         zr.load((const bf16_t *)p.q_gate + orow * 2 * D + D + d);
         float z[4];
@@ -175,11 +306,11 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
     } else if (cap_ok) {
       const int rr = r - row0;
 #pragma unroll
-      for (int db = 0; db < DBW; ++db) {
-        const int d = 16 * (DBW * wave + db) + 4 * g4;
+      for (int db = 0; db < NDB; ++db) {
+        const int d = 16 * db + 4 * g4;
         *(float4 *)(p.part_o + (slot_rows + rr) * D + d) = make_float4(O[rt][db][0], O[rt][db][1], O[rt][db][2], O[rt][db][3]);
       }
-      if (wave == 0 && g4 == 0) *(float2 *)(p.part_ml + (slot_rows + rr) * 2) = make_float2(mrun[rt], lrun[rt]);
+      if (g4 == 0) *(float2 *)(p.part_ml + (slot_rows + rr) * 2) = make_float2(mrun[rt], lsum);
     }
   }
   if (!cap_ok && chunk == 0) {
