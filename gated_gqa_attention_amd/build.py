@@ -24,8 +24,7 @@ SOURCES = ["qsa_api.hip", "qsa_rows.hip", "qsa_stream.hip", "qsa_prefill.hip", "
 # SGPRs; their LDS copies set M0 from inline assembly, hence -Wno-inline-asm
 # (nothing else in those files uses M0)
 EXTRA = {"qsa_stream.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=13", "-Wno-inline-asm"],
-         "qsa_prefill.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=11", "-mllvm", "-amdgpu-mfma-vgpr-form",
-                             "-Wno-inline-asm"]}
+         "qsa_prefill.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=11", "-Wno-inline-asm"]}
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

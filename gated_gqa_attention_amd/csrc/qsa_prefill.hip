@@ -230,16 +230,29 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
   // ------------------------------------------------------------ key stages
   const unsigned kring_lds = (unsigned)(uintptr_t)(lds_void *)kring;
   const unsigned vring_lds = (unsigned)(uintptr_t)(lds_void *)vring;
+  // This thread's copies of a stage: key row keyi[i] of the stage, 16-byte unit
+  // at byte ub[i] of the swizzled row; the source is that key's row of KV head
+  // kvh, addressed from the stage's first key (wave-uniform) plus a lane offset.
+  const unsigned rowb = (unsigned)(hkv * D * 2);       // bytes between consecutive keys of one KV head
+  int keyi[LPS];
+  unsigned ub[LPS];
+#pragma unroll
+  for (int i = 0; i < LPS; ++i) {
+    const int u = t + kThreads * i;
+    keyi[i] = u / G::OCT;
+    ub[i] = 16u * (unsigned)((u % G::OCT) ^ (keyi[i] & G::SW));
+  }
   auto issue_stage = [&](int st) {   // keys k0 + SK st .. into ring slot st % NS
+    const int64_t sk0 = k0 + (int64_t)SK * st;
+    const int last = (int)min<int64_t>(SK - 1, k1 - 1 - sk0);   // keys past the chunk repeat its last key
+    const int64_t row = ((off + sk0) * hkv + kvh) * D;
+    const bf16_t *kb = kc + row, *vb = vc + row;
 #pragma unroll
     for (int i = 0; i < LPS; ++i) {
-      const int u = t + kThreads * i;
-      const int key = u / G::OCT, pos = u % G::OCT, oct = pos ^ (key & G::SW);
-      const int64_t kk = min(k0 + (int64_t)SK * st + key, k1 - 1);
-      const int64_t e = ((off + kk) * hkv + kvh) * D + 8 * oct;
+      const unsigned voff = (unsigned)min(keyi[i], last) * rowb + ub[i];
       const unsigned dst = (st % NS) * G::STAGE + kThreads * 16 * i + wave * 1024;
-      dma16_asm(kc + e, kring_lds + dst);
-      dma16_asm(vc + e, vring_lds + dst);
+      dma16_sbase(kb, voff, kring_lds + dst);
+      dma16_sbase(vb, voff, vring_lds + dst);
     }
   };
 #pragma unroll
@@ -255,25 +268,36 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
 #pragma unroll
     for (int db = 0; db < NDB; ++db) O[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  for (int st = 0; st < nst; ++st) {
-    wait_stages<2 * LPS, NS>(min(NS - 2, nst - 1 - st));
-    lds_barrier();                                      // stage st is in LDS; every wave is done with stage st - 1
-    if (st + NS - 1 < nst) issue_stage(st + NS - 1);    // refill the slot of stage st - 1
-    const int so = (st % NS) * G::STAGE;
-    const int64_t sk0 = k0 + (int64_t)SK * st;
-    const int nk = (int)min<int64_t>(SK, k1 - sk0);
+  // The inner loop holds no rescaling code, so the accumulators stay where the
+  // MFMAs leave them; a stage whose running max moved (rare with the lazy max)
+  // leaves it, rescales, finishes its value product and re-enters.
+  int st = 0;
+  while (st < nst) {
     bf16x8 bp[2];
     float alpha[2];
-    const bool rescale = sk0 + SK <= kfull
-                             ? stage_scores<D, false>(kring + so, nk, sk0, qf, mrun, lrun, lim, sl2, bp, alpha)
-                             : stage_scores<D, true>(kring + so, nk, sk0, qf, mrun, lrun, lim, sl2, bp, alpha);
-    if (__any(rescale)) {
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) O[rt][db] *= alpha[rt];
+    bool moved = false;
+    int so = 0;
+    for (; st < nst; ++st) {
+      wait_stages<2 * LPS, NS>(min(NS - 2, nst - 1 - st));
+      lds_barrier();                                    // stage st is in LDS; every wave is done with stage st - 1
+      if (st + NS - 1 < nst) issue_stage(st + NS - 1);  // refill the slot of stage st - 1
+      so = (st % NS) * G::STAGE;
+      const int64_t sk0 = k0 + (int64_t)SK * st;
+      const int nk = (int)min<int64_t>(SK, k1 - sk0);
+      const bool r = sk0 + SK <= kfull
+                         ? stage_scores<D, false>(kring + so, nk, sk0, qf, mrun, lrun, lim, sl2, bp, alpha)
+                         : stage_scores<D, true>(kring + so, nk, sk0, qf, mrun, lrun, lim, sl2, bp, alpha);
+      moved = __any(r);
+      if (moved) break;
+      stage_values<D>(vring + so, bp, O);
     }
+    if (!moved) break;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) O[rt][db] *= alpha[rt];
     stage_values<D>(vring + so, bp, O);
+    ++st;
   }
 
   // ------------------------------------------------------------ outputs
