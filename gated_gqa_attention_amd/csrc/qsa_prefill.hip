@@ -40,24 +40,14 @@ struct PGeo {
   static_assert(LPS >= 1 && LPS * kThreads == SK * OCT, "stage copies");
 };
 
-// Scores and online softmax of one 32-key stage for this wavefront's two row
-// tiles.  kt: swizzled K stage tile; keys key0 .. key0 + nkeys - 1; row tile
-// rt sees key k when key0 + k <= lim[rt] (causal limit n_b + l).  MASK = false
-// when every key of the stage is visible to every row of the workgroup.  ls
-// holds per-lane partial row sums (the four lanes of a row add up at the end).
-// Leaves the bf16 probabilities in bp in the score layout: lane (g4, m16)
-// holds keys 4 g4 + i and 16 + 4 g4 + i of row m16.
-template <int D, bool MASK>
-__device__ __forceinline__ bool stage_scores(const unsigned char *kt, int nkeys, int64_t key0,
-                                             const bf16x8 (&qf)[2][D / 32], float (&m)[2], float (&ls)[2],
-                                             const int64_t (&lim)[2], float scale_log2, bf16x8 (&bp)[2],
-                                             float (&alpha)[2]) {
+// Scores of one 32-key stage for this wavefront's two row tiles:
+// S[kb][rt][i] = S^T[key 16 kb + 4 g4 + i][row m16 of tile rt], from the
+// swizzled K stage tile kt and the query fragments in registers.
+template <int D>
+__device__ __forceinline__ void stage_qk(const unsigned char *kt, const bf16x8 (&qf)[2][D / 32], f32x4 (&S)[2][2]) {
   using G = PGeo<D>;
   constexpr int KST = D / 32, RB = G::RB;
   const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
-
-  // S^T[key 16 kb + 4 g4 + i][row m16] of row tile rt, in S[kb][rt][i]
-  f32x4 S[2][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -75,7 +65,20 @@ __device__ __forceinline__ bool stage_scores(const unsigned char *kt, int nkeys,
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) S[kb][rt] = mfma_qk(a, qf[rt][ks], S[kb][rt]);
     }
+}
 
+// Online softmax of one stage's scores.  Keys key0 .. key0 + nkeys - 1; row
+// tile rt sees key k when key0 + k <= lim[rt] (causal limit n_b + l).
+// MASK = false when every key of the stage is visible to every row of the
+// workgroup.  ls holds per-lane partial row sums (the four lanes of a row add
+// up at the end).  Leaves the bf16 probabilities in bp in the score layout:
+// lane (g4, m16) holds keys 4 g4 + i and 16 + 4 g4 + i of row m16.  Returns
+// whether this lane's rows need their outputs rescaled by alpha.
+template <bool MASK>
+__device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2][2], int nkeys, int64_t key0, float (&m)[2],
+                                              float (&ls)[2], const int64_t (&lim)[2], float scale_log2,
+                                              bf16x8 (&bp)[2], float (&alpha)[2]) {
+  const int g4 = (threadIdx.x % kWave) >> 4;
   bool rescale = false;
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
@@ -100,13 +103,15 @@ __device__ __forceinline__ bool stage_scores(const unsigned char *kt, int nkeys,
     const bool up = bm > m[rt] + kLazyMax;
     const float mn = up ? bm : m[rt];
     const float mu = mn == -INFINITY ? 0.f : mn;
-    alpha[rt] = exp2f(m[rt] - mu);
+    // v_exp_f32 directly: results below 2^-126 flush to zero, which is
+    // negligible next to the reference's probability of at least 2^-kLazyMax
+    alpha[rt] = __builtin_amdgcn_exp2f(m[rt] - mu);
     rescale |= up && m[rt] != -INFINITY;
     m[rt] = mn;
     float ps = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      bp[rt][j] = (bf16_t)exp2f(sc[j] - mu);
+      bp[rt][j] = (bf16_t)__builtin_amdgcn_exp2f(sc[j] - mu);
       ps += (float)bp[rt][j];
     }
     ls[rt] = ls[rt] * alpha[rt] + ps;
@@ -255,6 +260,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
       dma16_sbase(vb, voff, vring_lds + dst);
     }
   };
+  static_assert(NS >= 3, "the pipeline reads one stage ahead");
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
     if (st < nst) issue_stage(st);
@@ -268,9 +274,16 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
 #pragma unroll
     for (int db = 0; db < NDB; ++db) O[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // The inner loop holds no rescaling code, so the accumulators stay where the
-  // MFMAs leave them; a stage whose running max moved (rare with the lazy max)
-  // leaves it, rescales, finishes its value product and re-enters.
+  // Software pipeline: the scores of stage st + 1 are computed in the same
+  // block as the softmax of stage st, so the MFMAs of one overlap the vector
+  // work of the other; the value product of stage st follows.  The inner loop
+  // holds no rescaling code, so the accumulators stay where the MFMAs leave
+  // them; a stage whose running max moved (rare with the lazy max) leaves it,
+  // rescales, finishes its value product and re-enters.
+  f32x4 S[2][2];
+  wait_stages<2 * LPS, NS>(min(NS - 2, nst - 1));
+  lds_barrier();
+  stage_qk<D>(kring, qf, S);
   int st = 0;
   while (st < nst) {
     bf16x8 bp[2];
@@ -278,15 +291,29 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
     bool moved = false;
     int so = 0;
     for (; st < nst; ++st) {
-      wait_stages<2 * LPS, NS>(min(NS - 2, nst - 1 - st));
-      lds_barrier();                                    // stage st is in LDS; every wave is done with stage st - 1
-      if (st + NS - 1 < nst) issue_stage(st + NS - 1);  // refill the slot of stage st - 1
       so = (st % NS) * G::STAGE;
+      if (st + 1 < nst) {
+        wait_stages<2 * LPS, NS>(min(NS - 3, nst - 2 - st));
+        lds_barrier();                                  // stage st + 1 is in LDS; every wave is done with stage st - 1
+        if (st + NS - 1 < nst) issue_stage(st + NS - 1);  // refill the slot of stage st - 1
+      }
+      // (after the last stage the next slot holds stale keys; those scores are unused)
+      const unsigned char *kn = kring + ((st + 1) % NS) * G::STAGE;
       const int64_t sk0 = k0 + (int64_t)SK * st;
       const int nk = (int)min<int64_t>(SK, k1 - sk0);
-      const bool r = sk0 + SK <= kfull
-                         ? stage_scores<D, false>(kring + so, nk, sk0, qf, mrun, lrun, lim, sl2, bp, alpha)
-                         : stage_scores<D, true>(kring + so, nk, sk0, qf, mrun, lrun, lim, sl2, bp, alpha);
+      f32x4 Sn[2][2];
+      bool r;
+      if (sk0 + SK <= kfull) {
+        stage_qk<D>(kn, qf, Sn);
+        r = stage_softmax<false>(S, nk, sk0, mrun, lrun, lim, sl2, bp, alpha);
+      } else {
+        stage_qk<D>(kn, qf, Sn);
+        r = stage_softmax<true>(S, nk, sk0, mrun, lrun, lim, sl2, bp, alpha);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) S[kb][rt] = Sn[kb][rt];
       moved = __any(r);
       if (moved) break;
       stage_values<D>(vring + so, bp, O);
