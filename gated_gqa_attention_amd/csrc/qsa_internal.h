@@ -134,12 +134,12 @@ struct Timing {
   hipEvent_t begin = nullptr, end = nullptr;
 };
 
-template <typename Kernel, typename... Args>
+template <int THREADS = kThreads, typename Kernel, typename... Args>
 inline void launch_kernel(Kernel kernel, int64_t blocks, hipStream_t s, const Timing &tm, Args... args) {
   if (tm.begin || tm.end)
-    hipExtLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, tm.begin, tm.end, 0, args...);
+    hipExtLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(THREADS), 0, s, tm.begin, tm.end, 0, args...);
   else
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, args...);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(THREADS), 0, s, args...);
 }
 
 // (defined in the kernel translation units, called by the C ABI layer)

@@ -7,8 +7,9 @@
 // key chunk).  The rows are (new row l, head of group g) pairs in order
 // r = l * G + (h - g * G) (DS4Server issue #113, Reproduction: query heads
 // grouped within their KV group), so one K/V stream serves the whole group.
-// The chunk's keys stream through an HBM -> LDS ring of 32-key stages; each
-// wavefront owns 32 rows and runs its own online softmax over every stage:
+// The chunk's keys stream through an HBM -> LDS ring of 32-key stages; eight
+// wavefronts (two per SIMD, so one can issue while the other waits) each own
+// 16 rows and run their own online softmax over every stage:
 // scores S^T = K Q^T on MFMA with the queries in registers, the running max and
 // the probabilities in registers, then O^T += V^T P^T on MFMA.  The value
 // product takes its keys in a permuted order that matches the layout the score
@@ -23,35 +24,35 @@ namespace qsa {
 
 namespace {
 
-constexpr int kRowsPerWave = 32;                     // two 16-row MFMA tiles
+constexpr int kTileThreads = 512;                    // eight wavefronts
+constexpr int kTileWaves = kTileThreads / kWave;
 constexpr float kLazyMax = 8.f;                      // headroom of the running max, log2 units
 constexpr int kPrefillRows = kPrefillTileRows;       // query rows per workgroup
-static_assert(kPrefillRows == (kThreads / kWave) * kRowsPerWave, "four wavefronts of 32 rows");
+static_assert(kPrefillRows == kTileWaves * 16, "one 16-row MFMA tile per wavefront");
 
 template <int D>
 struct PGeo {
   static constexpr int RB = 2 * D;                      // bytes of one key row of one KV head
   static constexpr int OCT = D / 8;                     // 16-byte units per row
-  static constexpr int SW = (OCT < 16 ? OCT : 16) - 1;  // XOR swizzle mask over units
+  static constexpr int SW = (OCT < 16 ? OCT : 16) - 1;  // K tile: unit u of row r sits at u ^ (r & SW)
+  static constexpr int SWV = (OCT < 16 ? OCT : 16) / 2 - 1;   // V tile: at u ^ 2 (r & SWV)
   static constexpr int SK = 32;                         // keys per stage
   static constexpr int STAGE = SK * RB;                 // bytes per stage and tensor
   static constexpr int NS = 4;                          // ring slots per tensor
-  static constexpr int LPS = SK * OCT / kThreads;       // 16-byte copies per thread, stage and tensor
-  static_assert(LPS >= 1 && LPS * kThreads == SK * OCT, "stage copies");
+  static constexpr int NCP = SK * OCT;                  // 16-byte copies per stage and tensor
+  static constexpr int LPS = (NCP + kTileThreads - 1) / kTileThreads;   // per thread (some idle when D = 64)
 };
 
-// Scores of one 32-key stage for this wavefront's two row tiles:
-// S[kb][rt][i] = S^T[key 16 kb + 4 g4 + i][row m16 of tile rt], from the
-// swizzled K stage tile kt and the query fragments in registers.
+// Scores of one 32-key stage for this wavefront's 16 rows:
+// S[kb][i] = S^T[key 16 kb + 4 g4 + i][row m16], from the swizzled K stage
+// tile kt and the query fragments in registers.
 template <int D>
-__device__ __forceinline__ void stage_qk(const unsigned char *kt, const bf16x8 (&qf)[2][D / 32], f32x4 (&S)[2][2]) {
+__device__ __forceinline__ void stage_qk(const unsigned char *kt, const bf16x8 (&qf)[D / 32], f32x4 (&S)[2]) {
   using G = PGeo<D>;
   constexpr int KST = D / 32, RB = G::RB;
   const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) S[kb][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kb = 0; kb < 2; ++kb) S[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Unit 4 ks + g4 of key row 16 kb + m16 sits at unit (4 ks + g4) ^ (m16 & SW)
   // = 4 ((ks & 3) ^ c) + 16 (ks >> 2) + (g4 ^ (m16 & 3)) with c = (m16 & SW) >> 2,
   // so four lane offsets cover every k-step (the rest are immediates).
@@ -62,60 +63,54 @@ __device__ __forceinline__ void stage_qk(const unsigned char *kt, const bf16x8 (
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const bf16x8 a = *(const bf16x8 *)(kl + 64 * ((ks & 3) ^ c) + 256 * (ks >> 2) + 16 * RB * kb);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) S[kb][rt] = mfma_qk(a, qf[rt][ks], S[kb][rt]);
+      S[kb] = mfma_qk(a, qf[ks], S[kb]);
     }
 }
 
-// Online softmax of one stage's scores.  Keys key0 .. key0 + nkeys - 1; row
-// tile rt sees key k when key0 + k <= lim[rt] (causal limit n_b + l).
+// Online softmax of one stage's scores.  Keys key0 .. key0 + nkeys - 1; this
+// lane's row sees key k when key0 + k <= lim (causal limit n_b + l).
 // MASK = false when every key of the stage is visible to every row of the
-// workgroup.  ls holds per-lane partial row sums (the four lanes of a row add
+// workgroup.  ls holds the lane's partial row sum (the four lanes of a row add
 // up at the end).  Leaves the bf16 probabilities in bp in the score layout:
 // lane (g4, m16) holds keys 4 g4 + i and 16 + 4 g4 + i of row m16.  Returns
-// whether this lane's rows need their outputs rescaled by alpha.
+// whether the row's outputs need rescaling by alpha.
 template <bool MASK>
-__device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2][2], int nkeys, int64_t key0, float (&m)[2],
-                                              float (&ls)[2], const int64_t (&lim)[2], float scale_log2,
-                                              bf16x8 (&bp)[2], float (&alpha)[2]) {
+__device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2], int nkeys, int64_t key0, float &m, float &ls,
+                                              int64_t lim, float scale_log2, bf16x8 &bp, float &alpha) {
   const int g4 = (threadIdx.x % kWave) >> 4;
-  bool rescale = false;
+  float sc[8], bm = -INFINITY;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    float sc[8], bm = -INFINITY;
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = S[kb][rt][i] * scale_log2;
-        if constexpr (MASK) {
-          const int k = 16 * kb + 4 * g4 + i;
-          v = (k < nkeys && key0 + k <= lim[rt]) ? v : -INFINITY;
-        }
-        sc[4 * kb + i] = v;
-        bm = fmaxf(bm, v);
+    for (int i = 0; i < 4; ++i) {
+      float v = S[kb][i] * scale_log2;
+      if constexpr (MASK) {
+        const int k = 16 * kb + 4 * g4 + i;
+        v = (k < nkeys && key0 + k <= lim) ? v : -INFINITY;
       }
-    bm = rows4_max(bm);
-    // The reference max moves only when the block max passes it by more than
-    // kLazyMax (log2 units), so the probabilities stay <= 2^kLazyMax and the
-    // output rarely needs rescaling; sums, outputs and the chunk's (max, sum)
-    // all refer to the same reference, which keeps the result exact.
-    const bool up = bm > m[rt] + kLazyMax;
-    const float mn = up ? bm : m[rt];
-    const float mu = mn == -INFINITY ? 0.f : mn;
-    // v_exp_f32 directly: results below 2^-126 flush to zero, which is
-    // negligible next to the reference's probability of at least 2^-kLazyMax
-    alpha[rt] = __builtin_amdgcn_exp2f(m[rt] - mu);
-    rescale |= up && m[rt] != -INFINITY;
-    m[rt] = mn;
-    float ps = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      bp[rt][j] = (bf16_t)__builtin_amdgcn_exp2f(sc[j] - mu);
-      ps += (float)bp[rt][j];
+      sc[4 * kb + i] = v;
+      bm = fmaxf(bm, v);
     }
-    ls[rt] = ls[rt] * alpha[rt] + ps;
+  bm = rows4_max(bm);
+  // The reference max moves only when the block max passes it by more than
+  // kLazyMax (log2 units), so the probabilities stay <= 2^kLazyMax and the
+  // output rarely needs rescaling; sums, outputs and the chunk's (max, sum)
+  // all refer to the same reference, which keeps the result exact.
+  const bool up = bm > m + kLazyMax;
+  const float mn = up ? bm : m;
+  const float mu = mn == -INFINITY ? 0.f : mn;
+  // v_exp_f32 directly: results below 2^-126 flush to zero, which is
+  // negligible next to the reference's probability of at least 2^-kLazyMax
+  alpha = __builtin_amdgcn_exp2f(m - mu);
+  const bool rescale = up && m != -INFINITY;
+  m = mn;
+  float ps = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    bp[j] = (bf16_t)__builtin_amdgcn_exp2f(sc[j] - mu);
+    ps += (float)bp[j];
   }
+  ls = ls * alpha + ps;
   return rescale;
 }
 
@@ -124,28 +119,27 @@ __device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2][2], int nkeys,
 // 16 + 4 g4 + j - 4, the order the probabilities were left in; the transposing
 // reads fetch those two 4-key runs of the swizzled V tile for dims 16 db + m16.
 template <int D>
-__device__ __forceinline__ void stage_values(const unsigned char *vt, const bf16x8 (&bp)[2], f32x4 (&O)[2][D / 16]) {
+__device__ __forceinline__ void stage_values(const unsigned char *vt, const bf16x8 &bp, f32x4 (&O)[D / 16]) {
   using G = PGeo<D>;
   constexpr int NDB = D / 16, RB = G::RB;
   const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
-  // Unit 2 db + h (h = bit 1 of m16) of key row klo sits at unit (2 db + h) ^ s,
-  // s = klo & SW, = 2 ((db % E) ^ (s >> 1)) + 2 E (db / E) + (h ^ (s & 1)) with
-  // E = (SW + 1) / 2; row klo + 16 has the same s.  E lane offsets cover every
-  // dim block.
-  constexpr int E = (G::SW + 1) / 2;
-  const int klo = 4 * g4 + (m16 >> 2), s = klo & G::SW;
-  const unsigned char *vl = vt + klo * RB + 16 * (((m16 >> 1) & 1) ^ (s & 1)) + 8 * (m16 & 1);
+  // Unit 2 db + h (h = bit 1 of m16) of key row klo sits at unit
+  // 2 (db ^ s) + h, s = klo & SWV, = 2 ((db % E) ^ s) + 2 E (db / E) + h with
+  // E = SWV + 1; row klo + 16 has the same s.  E lane offsets cover every dim
+  // block.  The swizzle leaves h alone, so the 32 lanes of rows klo = 0..7
+  // (or 8..15) read 16 distinct units: no bank conflicts.
+  constexpr int E = G::SWV + 1;
+  const int klo = 4 * g4 + (m16 >> 2), s = klo & G::SWV;
+  const unsigned char *vl = vt + klo * RB + 16 * ((m16 >> 1) & 1) + 8 * (m16 & 1);
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
-    const unsigned char *p0 = vl + 32 * ((db % E) ^ (s >> 1)) + 32 * E * (db / E);
+    const unsigned char *p0 = vl + 32 * ((db % E) ^ s) + 32 * E * (db / E);
     const unsigned char *p1 = p0 + 16 * RB;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    const bf16x8 a = __builtin_bit_cast(bf16x8, v8);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) O[rt][db] = mfma_qk(a, bp[rt], O[rt][db]);
+    O[db] = mfma_qk(__builtin_bit_cast(bf16x8, v8), bp, O[db]);
   }
 }
 
@@ -156,7 +150,7 @@ __device__ __forceinline__ void stage_values(const unsigned char *vt, const bf16
 // of items so that the tiles sharing a KV head share that XCD's L2.
 // Preloaded arguments: sequence metadata, the prepared queries and the grid shape.
 template <int D>
-__global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restrict__ seq_lens,
+__global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__restrict__ seq_lens,
                                                         const int64_t *__restrict__ seq_offset,
                                                         const bf16_t *__restrict__ qt, int L, int Gq, int Hq,
                                                         int tiles, int nitems, Params p) {
@@ -177,19 +171,18 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
   const int b = bk / hkv, kvh = bk % hkv;
   const int R = L * Gq;                                 // rows of this KV head
   const int row0 = tile * kPrefillRows;
-  const int wrow0 = row0 + kRowsPerWave * wave;         // this wavefront's first row
+  const int wrow = row0 + 16 * wave + m16;              // this lane's row
+  const int wr = min(wrow, R - 1);
 
   // ------------------------------------------------------------ round trip 1: metadata and queries
   const int n = seq_lens[b];
   const int64_t off = seq_offset[b];
-  bf16x8 qf[2][KST];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int r = min(wrow0 + 16 * rt + m16, R - 1);
-    const int l = r / Gq, h = kvh * Gq + r % Gq;
+  bf16x8 qf[KST];
+  {
+    const int l = wr / Gq, h = kvh * Gq + wr % Gq;
     const bf16_t *src = qt + (((int64_t)b * L + l) * Hq + h) * D + 8 * g4;
 #pragma unroll
-    for (int ks = 0; ks < KST; ++ks) qf[rt][ks] = __builtin_bit_cast(bf16x8, gld<uint4>(src + 32 * ks));
+    for (int ks = 0; ks < KST; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, gld<uint4>(src + 32 * ks));
   }
   const int ck = p.chunk_keys, msl = p.max_seq_len;
   const int64_t nrows = p.num_rows;
@@ -200,12 +193,10 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::"s"(n), "s"(off), "s"(ck), "s"(msl), "s"(nrows), "s"(kc), "s"(vc), "s"(capp), "s"(sl2));
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int ks = 0; ks < KST; ++ks) {
-      typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-      asm volatile("" ::"v"(__builtin_bit_cast(u32x4, qf[rt][ks])));
-    }
+  for (int ks = 0; ks < KST; ++ks) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    asm volatile("" ::"v"(__builtin_bit_cast(u32x4, qf[ks])));
+  }
 
   const int64_t total = (int64_t)n + L;
   const bool in_range = n >= 0 && off >= 0 && total <= msl && off + total <= nrows;
@@ -216,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
   if (chunk >= nch) return;
   if (!in_range) {
     if (chunk == 0) {
-      for (int e = t; e < (rlast - row0 + 1) * D; e += kThreads) {
+      for (int e = t; e < (rlast - row0 + 1) * D; e += kTileThreads) {
         const int r = row0 + e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
         ((bf16_t *)p.out)[(((int64_t)b * L + l) * Hq + h) * D + d] = (bf16_t)__builtin_nanf("");
       }
@@ -228,24 +219,25 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
   const int64_t k1 = chunk == nch - 1 ? kend : k0 + ck;
   const int nst = (int)((k1 - k0 + SK - 1) / SK);
   const int64_t kfull = min(k1, (int64_t)n + row0 / Gq + 1);   // keys below this are visible to every row
-  int64_t lim[2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) lim[rt] = (int64_t)n + min(wrow0 + 16 * rt + m16, R - 1) / Gq;
+  const int64_t lim = (int64_t)n + wr / Gq;
 
   // ------------------------------------------------------------ key stages
   const unsigned kring_lds = (unsigned)(uintptr_t)(lds_void *)kring;
   const unsigned vring_lds = (unsigned)(uintptr_t)(lds_void *)vring;
-  // This thread's copies of a stage: key row keyi[i] of the stage, 16-byte unit
-  // at byte ub[i] of the swizzled row; the source is that key's row of KV head
-  // kvh, addressed from the stage's first key (wave-uniform) plus a lane offset.
+  // This thread's copies of a stage: key row keyi[i] of the stage, the 16-byte
+  // unit that the K (V) tile's swizzle puts at this thread's LDS position sits at
+  // byte ubk[i] (ubv[i]) of the source row; the source is that key's row of KV
+  // head kvh, addressed from the stage's first key (wave-uniform) plus a lane
+  // offset.
   const unsigned rowb = (unsigned)(hkv * D * 2);       // bytes between consecutive keys of one KV head
   int keyi[LPS];
-  unsigned ub[LPS];
+  unsigned ubk[LPS], ubv[LPS];
 #pragma unroll
   for (int i = 0; i < LPS; ++i) {
-    const int u = t + kThreads * i;
+    const int u = t + kTileThreads * i;
     keyi[i] = u / G::OCT;
-    ub[i] = 16u * (unsigned)((u % G::OCT) ^ (keyi[i] & G::SW));
+    ubk[i] = 16u * (unsigned)((u % G::OCT) ^ (keyi[i] & G::SW));
+    ubv[i] = 16u * (unsigned)((u % G::OCT) ^ (2 * (keyi[i] & G::SWV)));
   }
   auto issue_stage = [&](int st) {   // keys k0 + SK st .. into ring slot st % NS
     const int64_t sk0 = k0 + (int64_t)SK * st;
@@ -254,90 +246,71 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
     const bf16_t *kb = kc + row, *vb = vc + row;
 #pragma unroll
     for (int i = 0; i < LPS; ++i) {
-      const unsigned voff = (unsigned)min(keyi[i], last) * rowb + ub[i];
-      const unsigned dst = (st % NS) * G::STAGE + kThreads * 16 * i + wave * 1024;
-      dma16_sbase(kb, voff, kring_lds + dst);
-      dma16_sbase(vb, voff, vring_lds + dst);
+      const unsigned kr = (unsigned)min(keyi[i], last) * rowb;
+      const unsigned dst = (st % NS) * G::STAGE + kTileThreads * 16 * i + wave * 1024;
+      if (G::NCP % kTileThreads == 0 || kTileThreads * i + 64 * wave < G::NCP) {   // wave-uniform
+        dma16_sbase(kb, kr + ubk[i], kring_lds + dst);
+        dma16_sbase(vb, kr + ubv[i], vring_lds + dst);
+      }
     }
   };
-  static_assert(NS >= 3, "the pipeline reads one stage ahead");
+  static_assert(NS >= 3, "the stages read one stage ahead");
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
     if (st < nst) issue_stage(st);
 
-  f32x4 O[2][NDB];
-  float mrun[2], lrun[2];
+  f32x4 O[NDB];
+  float mrun = -INFINITY, lrun = 0.f;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    mrun[rt] = -INFINITY;
-    lrun[rt] = 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) O[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int db = 0; db < NDB; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Software pipeline: the scores of stage st + 1 are computed in the same
   // block as the softmax of stage st, so the MFMAs of one overlap the vector
-  // work of the other; the value product of stage st follows.  The inner loop
-  // holds no rescaling code, so the accumulators stay where the MFMAs leave
-  // them; a stage whose running max moved (rare with the lazy max) leaves it,
-  // rescales, finishes its value product and re-enters.
-  f32x4 S[2][2];
+  // work of the other; the value product of stage st follows.  (Running the two
+  // wavefronts of a SIMD in ping-pong instead measured slower: with half the
+  // wavefronts reading at a time the LDS reads become the critical path.)
+  f32x4 S[2];
   wait_stages<2 * LPS, NS>(min(NS - 2, nst - 1));
   lds_barrier();
   stage_qk<D>(kring, qf, S);
-  int st = 0;
-  while (st < nst) {
-    bf16x8 bp[2];
-    float alpha[2];
-    bool moved = false;
-    int so = 0;
-    for (; st < nst; ++st) {
-      so = (st % NS) * G::STAGE;
-      if (st + 1 < nst) {
-        wait_stages<2 * LPS, NS>(min(NS - 3, nst - 2 - st));
-        lds_barrier();                                  // stage st + 1 is in LDS; every wave is done with stage st - 1
-        if (st + NS - 1 < nst) issue_stage(st + NS - 1);  // refill the slot of stage st - 1
-      }
-      // (after the last stage the next slot holds stale keys; those scores are unused)
-      const unsigned char *kn = kring + ((st + 1) % NS) * G::STAGE;
-      const int64_t sk0 = k0 + (int64_t)SK * st;
-      const int nk = (int)min<int64_t>(SK, k1 - sk0);
-      f32x4 Sn[2][2];
-      bool r;
-      if (sk0 + SK <= kfull) {
-        stage_qk<D>(kn, qf, Sn);
-        r = stage_softmax<false>(S, nk, sk0, mrun, lrun, lim, sl2, bp, alpha);
-      } else {
-        stage_qk<D>(kn, qf, Sn);
-        r = stage_softmax<true>(S, nk, sk0, mrun, lrun, lim, sl2, bp, alpha);
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) S[kb][rt] = Sn[kb][rt];
-      moved = __any(r);
-      if (moved) break;
-      stage_values<D>(vring + so, bp, O);
+  for (int st = 0; st < nst; ++st) {
+    const int so = (st % NS) * G::STAGE;
+    if (st + 1 < nst) {
+      wait_stages<2 * LPS, NS>(min(NS - 3, nst - 2 - st));
+      lds_barrier();                                    // stage st + 1 is in LDS; every wave is done with stage st - 1
+      if (st + NS - 1 < nst) issue_stage(st + NS - 1);  // refill the slot of stage st - 1
     }
-    if (!moved) break;
+    // (after the last stage the next slot holds stale keys; those scores are unused)
+    const unsigned char *kn = kring + ((st + 1) % NS) * G::STAGE;
+    const int64_t sk0 = k0 + (int64_t)SK * st;
+    const int nk = (int)min<int64_t>(SK, k1 - sk0);
+    f32x4 Sn[2];
+    bf16x8 bp;
+    float alpha;
+    bool r;
+    if (sk0 + SK <= kfull) {
+      stage_qk<D>(kn, qf, Sn);
+      r = stage_softmax<false>(S, nk, sk0, mrun, lrun, lim, sl2, bp, alpha);
+    } else {
+      stage_qk<D>(kn, qf, Sn);
+      r = stage_softmax<true>(S, nk, sk0, mrun, lrun, lim, sl2, bp, alpha);
+    }
+    S[0] = Sn[0];
+    S[1] = Sn[1];
+    if (__any(r)) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) O[rt][db] *= alpha[rt];
+      for (int db = 0; db < NDB; ++db) O[db] *= alpha;
+    }
     stage_values<D>(vring + so, bp, O);
-    ++st;
   }
 
   // ------------------------------------------------------------ outputs
-  // lane (g4, m16) holds dims 16 db + 4 g4 .. + 3 of row m16 of each row tile
+  // lane (g4, m16) holds dims 16 db + 4 g4 .. + 3 of row m16
   const bool cap_ok = total <= (int64_t)cap;
   const bool single = nch == 1;
   const int64_t slot_rows = ((int64_t)slot * pchunks + chunk) * p.rows;
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const float lsum = rows4_sum(lrun[rt]);
-    const int r = wrow0 + 16 * rt + m16;
-    if (r >= R) continue;
-    const int l = r / Gq, h = kvh * Gq + r % Gq;
+  const float lsum = rows4_sum(lrun);
+  if (wrow < R) {
+    const int l = wrow / Gq, h = kvh * Gq + wrow % Gq;
     const int64_t orow = ((int64_t)b * L + l) * Hq + h;
     if (single) {
       const float inv = 1.f / lsum;
@@ -350,23 +323,22 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
         zr.to_float(z);
         bf16x4 o4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          o4[i] = (bf16_t)(cap_ok ? O[rt][db][i] * inv * sigmoid_f(z[i]) : __builtin_nanf(""));
+        for (int i = 0; i < 4; ++i) o4[i] = (bf16_t)(cap_ok ? O[db][i] * inv * sigmoid_f(z[i]) : __builtin_nanf(""));
         *(bf16x4 *)((bf16_t *)p.out + orow * D + d) = o4;
       }
     } else if (cap_ok) {
-      const int rr = r - row0;
+      const int rr = wrow - row0;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int d = 16 * db + 4 * g4;
-        *(float4 *)(p.part_o + (slot_rows + rr) * D + d) = make_float4(O[rt][db][0], O[rt][db][1], O[rt][db][2], O[rt][db][3]);
+        *(float4 *)(p.part_o + (slot_rows + rr) * D + d) = make_float4(O[db][0], O[db][1], O[db][2], O[db][3]);
       }
-      if (g4 == 0) *(float2 *)(p.part_ml + (slot_rows + rr) * 2) = make_float2(mrun[rt], lsum);
+      if (g4 == 0) *(float2 *)(p.part_ml + (slot_rows + rr) * 2) = make_float2(mrun, lsum);
     }
   }
   if (!cap_ok && chunk == 0) {
     if (!single) {
-      for (int e = t; e < (rlast - row0 + 1) * D; e += kThreads) {
+      for (int e = t; e < (rlast - row0 + 1) * D; e += kTileThreads) {
         const int r = row0 + e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
         ((bf16_t *)p.out)[(((int64_t)b * L + l) * Hq + h) * D + d] = (bf16_t)__builtin_nanf("");
       }
@@ -378,7 +350,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const int32_t *__restric
 template <int D>
 static hipError_t launch_tile_d(const Params &p, hipStream_t s, const Timing &tm) {
   const int64_t nitems = (int64_t)p.B * p.Hkv * p.tiles * p.chunks;
-  launch_kernel(tile_kernel<D>, nitems, s, tm, p.seq_lens, p.seq_offset, (const bf16_t *)p.qt, p.L, p.G, p.Hq,
+  launch_kernel<kTileThreads>(tile_kernel<D>, nitems, s, tm, p.seq_lens, p.seq_offset, (const bf16_t *)p.qt, p.L, p.G, p.Hq,
                 p.tiles, (int)nitems, p);
   return hipGetLastError();
 }
