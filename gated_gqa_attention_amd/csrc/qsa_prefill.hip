@@ -70,28 +70,28 @@ __device__ __forceinline__ void stage_qk(const unsigned char *kt, const bf16x8 (
 // Online softmax of one stage's scores.  Keys key0 .. key0 + nkeys - 1; this
 // lane's row sees key k when key0 + k <= lim (causal limit n_b + l).
 // MASK = false when every key of the stage is visible to every row of the
-// workgroup.  ls holds the lane's partial row sum (the four lanes of a row add
-// up at the end).  Leaves the bf16 probabilities in bp in the score layout:
-// lane (g4, m16) holds keys 4 g4 + i and 16 + 4 g4 + i of row m16.  Returns
-// whether the row's outputs need rescaling by alpha.
+// workgroup.  Leaves the bf16 probabilities in bp in the score layout: lane
+// (g4, m16) holds keys 4 g4 + i and 16 + 4 g4 + i of row m16.  Returns whether
+// the row's outputs (and its sum, kept as an output column) need rescaling by
+// alpha.  scale_log2 > 0, so the max is taken on the raw scores.
 template <bool MASK>
-__device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2], int nkeys, int64_t key0, float &m, float &ls,
-                                              int64_t lim, float scale_log2, bf16x8 &bp, float &alpha) {
+__device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2], int nkeys, int64_t key0, float &m, int64_t lim,
+                                              float scale_log2, bf16x8 &bp, float &alpha) {
   const int g4 = (threadIdx.x % kWave) >> 4;
-  float sc[8], bm = -INFINITY;
+  float sc[8];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float v = S[kb][i] * scale_log2;
+      float v = S[kb][i];
       if constexpr (MASK) {
         const int k = 16 * kb + 4 * g4 + i;
         v = (k < nkeys && key0 + k <= lim) ? v : -INFINITY;
       }
       sc[4 * kb + i] = v;
-      bm = fmaxf(bm, v);
     }
-  bm = rows4_max(bm);
+  float bm = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+  bm = rows4_max(bm) * scale_log2;
   // The reference max moves only when the block max passes it by more than
   // kLazyMax (log2 units), so the probabilities stay <= 2^kLazyMax and the
   // output rarely needs rescaling; sums, outputs and the chunk's (max, sum)
@@ -104,13 +104,16 @@ __device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2], int nkeys, in
   alpha = __builtin_amdgcn_exp2f(m - mu);
   const bool rescale = up && m != -INFINITY;
   m = mn;
-  float ps = 0.f;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    bp[j] = (bf16_t)__builtin_amdgcn_exp2f(sc[j] - mu);
-    ps += (float)bp[j];
+  for (int j = 0; j < 8; j += 2) {
+    const f32x2 e = {__builtin_amdgcn_exp2f(__builtin_fmaf(sc[j], scale_log2, -mu)),
+                     __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j + 1], scale_log2, -mu))};
+    const bf16x2_t h = __builtin_convertvector(e, bf16x2_t);
+    bp[j] = h[0];
+    bp[j + 1] = h[1];
   }
-  ls = ls * alpha + ps;
   return rescale;
 }
 
@@ -118,8 +121,10 @@ __device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2], int nkeys, in
 // MFMA's k index j of lane group g4 standing for key 4 g4 + j (j < 4) or
 // 16 + 4 g4 + j - 4, the order the probabilities were left in; the transposing
 // reads fetch those two 4-key runs of the swizzled V tile for dims 16 db + m16.
+// O[NDB] accumulates P against a block of ones: every lane's entries hold its
+// row's running sum of the same bf16 probabilities the value product uses.
 template <int D>
-__device__ __forceinline__ void stage_values(const unsigned char *vt, const bf16x8 &bp, f32x4 (&O)[D / 16]) {
+__device__ __forceinline__ void stage_values(const unsigned char *vt, const bf16x8 &bp, f32x4 (&O)[D / 16 + 1]) {
   using G = PGeo<D>;
   constexpr int NDB = D / 16, RB = G::RB;
   const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
@@ -141,6 +146,9 @@ __device__ __forceinline__ void stage_values(const unsigned char *vt, const bf16
     const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     O[db] = mfma_qk(__builtin_bit_cast(bf16x8, v8), bp, O[db]);
   }
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80};   // bf16 1.0
+  O[NDB] = mfma_qk(__builtin_bit_cast(bf16x8, ones), bp, O[NDB]);
 }
 
 }  // namespace
@@ -259,10 +267,10 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
   for (int st = 0; st < NS - 1; ++st)
     if (st < nst) issue_stage(st);
 
-  f32x4 O[NDB];
-  float mrun = -INFINITY, lrun = 0.f;
+  f32x4 O[NDB + 1];                                    // output dims, then the row sum
+  float mrun = -INFINITY;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db <= NDB; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Software pipeline: the scores of stage st + 1 are computed in the same
   // block as the softmax of stage st, so the MFMAs of one overlap the vector
   // work of the other; the value product of stage st follows.  (Running the two
@@ -289,16 +297,16 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
     bool r;
     if (sk0 + SK <= kfull) {
       stage_qk<D>(kn, qf, Sn);
-      r = stage_softmax<false>(S, nk, sk0, mrun, lrun, lim, sl2, bp, alpha);
+      r = stage_softmax<false>(S, nk, sk0, mrun, lim, sl2, bp, alpha);
     } else {
       stage_qk<D>(kn, qf, Sn);
-      r = stage_softmax<true>(S, nk, sk0, mrun, lrun, lim, sl2, bp, alpha);
+      r = stage_softmax<true>(S, nk, sk0, mrun, lim, sl2, bp, alpha);
     }
     S[0] = Sn[0];
     S[1] = Sn[1];
     if (__any(r)) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) O[db] *= alpha;
+      for (int db = 0; db <= NDB; ++db) O[db] *= alpha;
     }
     stage_values<D>(vring + so, bp, O);
   }
@@ -308,7 +316,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
   const bool cap_ok = total <= (int64_t)cap;
   const bool single = nch == 1;
   const int64_t slot_rows = ((int64_t)slot * pchunks + chunk) * p.rows;
-  const float lsum = rows4_sum(lrun);
+  const float lsum = O[NDB][0];
   if (wrow < R) {
     const int l = wrow / Gq, h = kvh * Gq + wrow % Gq;
     const int64_t orow = ((int64_t)b * L + l) * Hq + h;
