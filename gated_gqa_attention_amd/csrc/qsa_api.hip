@@ -223,7 +223,7 @@ int qsa_describe_plan(const qsa_cfg *cfg, char *buf, size_t len) {
                   "route=%s rows=%d tiles=%d chunks=%d chunk_keys=%d workgroups=%lld threads=%d "
                   "workspace=%zu",
                   route_name(pl.route), pl.rows, pl.tiles, pl.chunks, pl.chunk_keys, (long long)pl.blocks,
-                  qsa::kThreads, pl.total);
+                  pl.route == kRoutePrepared ? qsa::kPrefillThreads : qsa::kThreads, pl.total);
 }
 
 int qsa_append_kv(const void *k_new, const void *v_new, const qsa_kv_cache *kv, const int32_t *seq_lens,

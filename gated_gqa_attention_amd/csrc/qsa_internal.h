@@ -20,6 +20,7 @@ constexpr int kWave = 64;
 constexpr int kTileKeys = 64;         // keys staged in LDS per pipeline stage
 constexpr int kTileRows = 64;         // query rows (group heads x new rows) of a short-query call
 constexpr int kPrefillTileRows = 128; // query rows per workgroup of the tile (prefill) kernel
+constexpr int kPrefillThreads = 512;  // eight wavefronts per workgroup of the tile kernel
 constexpr int kMaxFusedNewRows = 16;  // new rows a fused call may append per sequence
 constexpr int kMaxPairs = 128;        // rotary pairs (rotary_dim / 2) supported
 constexpr int kMaxChunks = 4096;      // key chunks per (sequence, KV head, tile)

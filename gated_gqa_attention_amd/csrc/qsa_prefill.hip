@@ -24,7 +24,7 @@ namespace qsa {
 
 namespace {
 
-constexpr int kTileThreads = 512;                    // eight wavefronts
+constexpr int kTileThreads = kPrefillThreads;        // eight wavefronts
 constexpr int kTileWaves = kTileThreads / kWave;
 constexpr float kLazyMax = 8.f;                      // headroom of the running max, log2 units
 constexpr int kPrefillRows = kPrefillTileRows;       // query rows per workgroup
