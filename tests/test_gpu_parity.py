@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import oracle
+import twin
 from gated_gqa_attention_amd.session import Session
 from gated_gqa_attention_amd.workloads import WORKLOADS, Workload, make_inputs
 
@@ -91,6 +92,13 @@ SMALL = [
     # 64 cached + 16 new keys in one chunk: one full stage plus the new-key block
     Workload("bf16_new_rows_fold", batch=2, q_len=16, num_q_heads=4, num_kv_heads=1, head_dim=256,
              rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=64, seed=112),
+    # tile route at head_dim 64 (half of the workgroup issues no stage copies):
+    # 132 rows = one full and one ragged 128-row tile, 183 keys = 5 full 32-key stages + a ragged one
+    Workload("bf16_prefill_d64", batch=2, q_len=33, num_q_heads=8, num_kv_heads=2, head_dim=64,
+             rotary_dim=32, rope_theta=1e4, dtype="bf16", prior=150, seed=113),
+    # tile route at head_dim 128: 280 rows = three tiles
+    Workload("bf16_prefill_d128_tiles", batch=1, q_len=70, num_q_heads=8, num_kv_heads=2, head_dim=128,
+             rotary_dim=64, rope_theta=1e6, dtype="bf16", prior=200, seed=114),
 ]
 
 
@@ -108,6 +116,49 @@ def test_parity_small(w, splits):
         check(out, ref, w.dtype, f"{w.name}/{variant}")
         check_rows(sess, inp, kr, vr, w)
         assert sess.device_error() == 0
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+@pytest.mark.parametrize("w", [
+    # short-query route (one new row per sequence)
+    Workload("bf16_dominant_decode", batch=2, q_len=1, num_q_heads=8, num_kv_heads=2, head_dim=256,
+             rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=400, seed=116),
+    # tile route (160 rows)
+    Workload("bf16_dominant_prefill", batch=1, q_len=40, num_q_heads=8, num_kv_heads=2, head_dim=256,
+             rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=300, seed=115),
+], ids=lambda w: w.name)
+def test_late_dominant_keys_move_the_running_max(w, splits):
+    """Three cached keys late in each sequence point along the prepared query of
+    one row per KV head (last new row, first head of the group) with scores 6,
+    14 and 24, so that row's maximum jumps by more than 8 log2 units (the tile
+    kernel's lazy-max headroom) at each of them and the output rescaling runs;
+    the earlier keys' weights must shrink exactly as in the oracle's softmax.
+    (Keys along the query keep one key dominant per row: random huge keys would
+    instead make two keys compete, where the bf16 rounding of q, about 1.1e-3 of
+    the score, is amplified past the bf16 tolerance.)"""
+    inp = make_inputs(w)
+    B, L, Hq, Hkv, D = w.batch, w.q_len, w.num_q_heads, w.num_kv_heads, w.head_dim
+    G = Hq // Hkv
+    qg = twin._f64(inp["q_gate"])
+    wq = twin._f64(inp["w_q"])
+    pos = np.asarray(inp["positions"]).astype(np.float64)
+    kc = inp["k_cache"]
+    for b in range(B):
+        o, nb = int(inp["seq_offset"][b]), int(inp["seq_lens"][b])
+        rot = twin.rotation_matrix(pos[b, L - 1], w.rotary_dim, w.rope_theta, D)
+        for g in range(Hkv):
+            qh = twin._norm(qg[b, L - 1, g * G, :D], wq, w.rms_eps) @ rot.T
+            for frac, score in ((0.15, 6.0), (0.45, 14.0), (0.9, 24.0)):
+                kc[o + int(frac * nb), g] = torch.from_numpy(score * np.sqrt(D) / (qh @ qh) * qh).to(kc.dtype)
+    say(f"case {w.name} splits={splits}")
+    sess = Session(w, inp, force_splits=splits)
+    say(f"  plan {sess.plan()}")
+    out = to_np(sess.run())
+    torch.cuda.synchronize()
+    ref, kr, vr = oracle.gated_attention(geo(w), inp)
+    check(out, ref, w.dtype, w.name)
+    check_rows(sess, inp, kr, vr, w)
+    assert sess.device_error() == 0
 
 
 @pytest.mark.parametrize("name", ["decode_4b", "verify_24x2"])
