@@ -180,16 +180,24 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   // ------------------------------------------------------------ ring fill
   const unsigned kring_lds = (unsigned)(uintptr_t)(lds_void *)kring;
   const unsigned vring_lds = (unsigned)(uintptr_t)(lds_void *)vring;
+  // This thread's copies of a stage: key row u / OCT of the stage, and the
+  // 16-byte unit that the swizzle puts at LDS position u % OCT of that row; the
+  // source is addressed from the stage's first key (wave-uniform, in SGPRs)
+  // plus a 32-bit lane offset shared by K and V.
+  const unsigned rowb = (unsigned)(hkv * D * 2);       // bytes between consecutive keys of one KV head
   auto issue_stage = [&](int st) {   // keys k0 + 64 st .. into ring slot st % NS
+    const int64_t sk0 = k0 + (int64_t)G::SK * st;
+    const int last = (int)min<int64_t>(G::SK - 1, cend - 1 - sk0);   // keys past the chunk repeat its last key
+    const int64_t row = ((off + sk0) * hkv + kvh) * D;
+    const bf16_t *kb = kc + row, *vb = vc + row;
 #pragma unroll
     for (int i = 0; i < LPS; ++i) {
       const int u = t + kThreads * i;
       const int key = u / G::OCT, pos = u % G::OCT, oct = pos ^ (key & G::SW);
-      const int64_t kk = min(k0 + (int64_t)G::SK * st + key, cend - 1);
-      const int64_t e = ((off + kk) * hkv + kvh) * D + 8 * oct;
+      const unsigned voff = (unsigned)min(key, last) * rowb + 16u * (unsigned)oct;
       const unsigned dst = (st % NS) * G::STAGE + kThreads * 16 * i + wave * 1024;
-      dma16_asm(kc + e, kring_lds + dst);
-      dma16_asm(vc + e, vring_lds + dst);
+      dma16_sbase(kb, voff, kring_lds + dst);
+      dma16_sbase(vb, voff, vring_lds + dst);
     }
   };
 #pragma unroll
