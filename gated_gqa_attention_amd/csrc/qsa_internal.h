@@ -17,7 +17,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;         // four wavefronts per workgroup
 constexpr int kWave = 64;
-constexpr int kTileKeys = 64;         // keys staged in LDS per pipeline stage
+constexpr int kTileKeys = 64;         // shortest key chunk the planner makes (one short-query stage)
 constexpr int kTileRows = 64;         // query rows (group heads x new rows) of a short-query call
 constexpr int kPrefillTileRows = 128; // query rows per workgroup of the tile (prefill) kernel
 constexpr int kPrefillThreads = 512;  // eight wavefronts per workgroup of the tile kernel

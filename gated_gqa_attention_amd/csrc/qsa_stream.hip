@@ -16,20 +16,22 @@
 // splits q_gate, RMS-normalises and rotates its query rows (mlxd PR #99
 // Summary and config audit table; Atlas FullAttentionLayer q_norm / k_norm,
 // Qwen35ForwardConfig::rotary_dim), and the workgroup whose chunk ends the
-// sequence does the same for the new keys, which it keeps in LDS and appends
-// to the cache at the end (Atlas qwen3_5/mod.rs module doc: append at
-// cache_pos, attend over cache_pos + 1 keys).
+// sequence normalises and rotates the new keys after the cached stages, keeps
+// them in LDS as the last stage and appends them to the cache at the end (Atlas
+// qwen3_5/mod.rs module doc: append at cache_pos, attend over cache_pos + 1 keys).
 //
-// Compute.  Each wavefront owns one 16-key block of every stage and keeps its
-// own online softmax (log2 domain) over all row tiles:
-//   S^T[key][row] = K[key][:] . Q[row][:]      v_mfma_f32_16x16x32_bf16
-//   O^T[dim][row] += V^T[dim][key] . P^T[key][row]   v_mfma_f32_16x16x16_bf16
-// With lane l, g = l / 16, m = l % 16, the score tile leaves keys 4g .. 4g+3 of
-// row m in lane l, which is exactly the lane's share of the P^T operand.  The
-// four wavefronts merge their (max, sum, output) through LDS at the end.  A
-// chunk that covers the whole sequence applies the gate attn * sigmoid(gate)
-// (mlxd PR #99 Summary) and stores bf16; otherwise it writes the chunk's
-// (max, sum, unnormalised output) for the merge kernel.
+// Compute (the stage step in qsa_device.h).  Wavefront w scores keys
+// 16 w .. 16 w + 15 of the stage against every row tile,
+//   S^T[key][row] = K[key][:] . Q[row][:]            v_mfma_f32_16x16x32_bf16,
+// the four wavefronts agree on each row's running max (log2 domain) through
+// LDS and publish the stage's probabilities as one bf16 tile, and each
+// wavefront then accumulates its own D/4 output dims over all keys of the stage,
+//   O^T[dim][row] += V^T[dim][key] . P^T[key][row]   v_mfma_f32_16x16x32_bf16,
+// with V^T read by gfx950's transposing LDS loads.  A chunk that covers the
+// whole sequence applies the gate attn * sigmoid(gate) (mlxd PR #99 Summary)
+// and stores bf16; otherwise it writes the chunk's (max, sum, unnormalised
+// output) for the merge kernel.  The new keys become one more stage after the
+// cached ones.
 //
 // Counters.  The copies are issued from inline assembly and waited for
 // explicitly (s_waitcnt vmcnt with the number of younger copies): the compiler
