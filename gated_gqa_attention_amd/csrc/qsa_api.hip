@@ -35,7 +35,7 @@ const char *route_name(int r) {
 
 struct Plan {
   int route = 0;
-  int rows = 0, tiles = 0, chunks = 1, chunk_keys = 0;
+  int rows = 0, tiles = 0, chunks = 1, chunk_keys = 0, even_split = 0;
   int64_t blocks = 0;
   size_t off_ml = 0, off_o = 0, off_qt = 0, total = 0;
 };
@@ -95,21 +95,32 @@ int make_plan(const qsa_cfg *c, Plan *pl) {
     p.tiles = (int)cdiv(rows_total, tile_rows);
     p.rows = (int)std::min<int64_t>(rows_total, tile_rows);
     const int64_t base = B * Hkv * p.tiles;
-    int64_t ck;
-    if (c->force_splits > 0) {
-      ck = std::max<int64_t>(1, S / c->force_splits);
-    } else if (!fused && base >= 256) {
-      ck = S;                                   // long prefill: one chunk per row tile
+    if (!fused) {
+      // Tile route: a tile's keys are cut into chunks of equal length, just
+      // enough of them to give every CU a workgroup (none shorter than 1024
+      // keys; 32 when a test fixes the count).
+      const int64_t min_keys = c->force_splits > 0 ? 32 : 1024;
+      int64_t ch = c->force_splits > 0 ? c->force_splits : (base >= 256 ? 1 : cdiv(256, base));
+      ch = std::min<int64_t>(std::min<int64_t>(ch, std::max<int64_t>(1, S / min_keys)), qsa::kMaxChunks);
+      p.even_split = 1;
+      p.chunk_keys = (int)std::min<int64_t>(min_keys, S);
+      p.chunks = (int)ch;
     } else {
-      // one round of workgroups (one per CU) for short work; for long work
-      // ~2048 chunks so ragged lengths balance across the CUs
-      const int64_t total = base * S;
-      ck = std::max<int64_t>(qsa::kTileKeys, total / 256);
-      if (ck > 2048) ck = std::max<int64_t>(2048, total / 2048);
+      // Short-query route: chunks of fixed length, the last one taking the
+      // remainder.  One round of workgroups (one per CU) for short work; for
+      // long work ~2048 chunks so ragged lengths balance across the CUs.
+      int64_t ck;
+      if (c->force_splits > 0) {
+        ck = std::max<int64_t>(1, S / c->force_splits);
+      } else {
+        const int64_t total = base * S;
+        ck = std::max<int64_t>(qsa::kTileKeys, total / 256);
+        if (ck > 2048) ck = std::max<int64_t>(2048, total / 2048);
+      }
+      ck = std::max<int64_t>(ck, cdiv(S, qsa::kMaxChunks));
+      p.chunk_keys = (int)std::min<int64_t>(ck, S);
+      p.chunks = (int)std::max<int64_t>(1, S / p.chunk_keys);
     }
-    ck = std::max<int64_t>(ck, cdiv(S, qsa::kMaxChunks));
-    p.chunk_keys = (int)std::min<int64_t>(ck, S);
-    p.chunks = (int)std::max<int64_t>(1, S / p.chunk_keys);
     p.blocks = base * p.chunks;
   }
   if (p.blocks > 0x7fffffffLL) return fail(QSA_ERR_UNSUPPORTED, "launch grid too large (%lld workgroups)",
@@ -144,6 +155,7 @@ qsa::Params base_params(const qsa_cfg *c, const Plan &pl) {
   p.tiles = pl.tiles;
   p.chunks = pl.chunks;
   p.chunk_keys = pl.chunk_keys;
+  p.even_split = pl.even_split;
   p.max_seq_len = c->max_seq_len;
   p.eps = c->rms_eps;
   p.scale = c->softmax_scale > 0.f ? c->softmax_scale : (float)(1.0 / std::sqrt((double)c->head_dim));

@@ -19,8 +19,9 @@ constexpr int kThreads = 256;         // four wavefronts per workgroup
 constexpr int kWave = 64;
 constexpr int kTileKeys = 64;         // shortest key chunk the planner makes (one short-query stage)
 constexpr int kTileRows = 64;         // query rows (group heads x new rows) of a short-query call
-constexpr int kPrefillTileRows = 128; // query rows per workgroup of the tile (prefill) kernel
+constexpr int kPrefillRowTiles = 2;  // 16-row MFMA tiles per wavefront of the tile (prefill) kernel
 constexpr int kPrefillThreads = 512;  // eight wavefronts per workgroup of the tile kernel
+constexpr int kPrefillTileRows = 16 * kPrefillRowTiles * kPrefillThreads / kWave;   // query rows per workgroup
 constexpr int kMaxFusedNewRows = 16;  // new rows a fused call may append per sequence
 constexpr int kMaxPairs = 128;        // rotary pairs (rotary_dim / 2) supported
 constexpr int kMaxChunks = 4096;      // key chunks per (sequence, KV head, tile)
@@ -39,8 +40,10 @@ struct Params {
   int B, L, Hq, Hkv, G, D, r;
   int rows;           // query rows per tile
   int tiles;          // row tiles per (sequence, KV head)
-  int chunks;         // grid extent in key chunks = chunk_count(max_seq_len)
-  int chunk_keys;     // keys per chunk (the last chunk of a tile also takes the remainder)
+  int chunks;         // grid extent in key chunks
+  int chunk_keys;     // fixed chunks: keys per chunk (the last one also takes the remainder);
+                      // even chunks: the shortest chunk
+  int even_split;     // 1: a tile's keys are cut into up to `chunks` chunks of equal length
   int max_seq_len;
   float eps;
   float scale_log2;   // softmax scale * log2(e)
@@ -111,6 +114,17 @@ __device__ __forceinline__ void rope_cs(const Params &p, int pos, int i, float &
 __device__ __forceinline__ int chunk_count(int64_t kend, int chunk_keys) {
   const int64_t c = kend / chunk_keys;
   return c < 1 ? 1 : (int)c;
+}
+// With even_split (the tile route) they are cut instead into
+// min(chunks, max(1, kend / chunk_keys)) chunks of equal length: chunk c covers
+// [c kend / nch, (c + 1) kend / nch).
+__device__ __forceinline__ int tile_chunk_count(int64_t kend, int even_split, int chunks, int chunk_keys) {
+  if (!even_split) return chunk_count(kend, chunk_keys);
+  const int64_t c = kend / chunk_keys;
+  return c < 1 ? 1 : (c > chunks ? chunks : (int)c);
+}
+__device__ __forceinline__ int64_t chunk_begin(int64_t kend, int even_split, int nch, int chunk_keys, int c) {
+  return even_split ? (int64_t)c * kend / nch : (int64_t)c * chunk_keys;
 }
 
 // Sequence bounds check shared by the kernels.  Returns false when rows

@@ -12,8 +12,10 @@
 namespace qsa {
 
 // Merge the key chunks of one (slot, row): weights 2^(m_c - M) / sum_c l_c 2^(m_c - M),
-// weighted sum of the unnormalised chunk outputs, then the sigmoid gate.  Waves
-// take interleaved chunks; lanes take EPL = D/64 dims.
+// weighted sum of the unnormalised chunk outputs, then the sigmoid gate.  For
+// the short-query route, whose rows can have thousands of chunks: one
+// workgroup per (slot, row), waves take interleaved chunks, lanes take
+// EPL = D/64 dims.
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(Params p) {
   constexpr int EPL = D / kWave;
@@ -36,7 +38,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Params p) {
   int64_t off;
   if (!seq_in_range(p, b, n, off)) return;              // the attention kernel wrote NaN
   const int lmax = (row0 + R - 1) / p.G;
-  const int nch = chunk_count((int64_t)n + lmax + 1, p.chunk_keys);
+  const int nch = tile_chunk_count((int64_t)n + lmax + 1, p.even_split, p.chunks, p.chunk_keys);
   if (nch == 1) return;                                 // finished by the attention kernel
 
   // every load first: chunk statistics, the gate, the first batch of partial outputs
@@ -114,7 +116,81 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Params p) {
   }
 }
 
+// Merge for the tile route, whose rows have few key chunks each: one wavefront
+// per (slot, row), lanes take EPL = D/64 dims, and the chunks are walked in
+// order: the chunk statistics are wave-uniform (scalar loads), the unnormalised
+// outputs one vector load per lane and chunk.
+template <int D>
+__global__ __launch_bounds__(kThreads) void combine_rows_kernel(Params p) {
+  constexpr int EPL = D / kWave;
+  const int prows = p.rows, ptiles = p.tiles, hkv = p.Hkv, L = p.L, Gq = p.G, Hq = p.Hq, pch = p.chunks;
+  const int ck = p.chunk_keys, msl = p.max_seq_len, even = p.even_split;
+  const int64_t nrows = p.num_rows;
+  const int32_t *const seq_lens = p.seq_lens, *const capp = p.capacity;
+  const int64_t *const seq_offset = p.seq_offset;
+  const bf16_t *const q_gate = (const bf16_t *)p.q_gate;
+  const float *const part_ml = p.part_ml, *const part_o = p.part_o;
+  bf16_t *const outp = (bf16_t *)p.out;
+  asm volatile("" ::"s"(prows), "s"(ptiles), "s"(hkv), "s"(L), "s"(Gq), "s"(Hq), "s"(pch), "s"(ck), "s"(msl),
+               "s"(even), "s"(nrows), "s"(seq_lens), "s"(capp), "s"(seq_offset), "s"(q_gate), "s"(part_ml),
+               "s"(part_o), "s"(outp));
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  const int64_t id = (int64_t)blockIdx.x * (kThreads / kWave) + wave;   // (slot, row) pair
+  const int64_t nslots = (int64_t)p.B * hkv * ptiles;
+  if (id >= nslots * prows) return;
+  const int rr = (int)(id % prows);
+  const int64_t slot = id / prows;
+  const int tile = (int)(slot % ptiles);
+  const int kvh = (int)((slot / ptiles) % hkv);
+  const int b = (int)(slot / ((int64_t)ptiles * hkv));
+  const int row0 = tile * prows;
+  const int R = min(prows, L * Gq - row0);
+  if (rr >= R) return;
+  const int n = seq_lens[b];
+  const int64_t off = seq_offset[b];
+  const int cap = capp ? capp[b] : 0x7fffffff;
+  const int64_t total = (int64_t)n + L;
+  if (!(n >= 0 && off >= 0 && total <= msl && off + total <= nrows && total <= (int64_t)cap))
+    return;                                             // the attention kernel wrote NaN
+  const int nch = tile_chunk_count((int64_t)n + (row0 + R - 1) / Gq + 1, even, pch, ck);
+  if (nch == 1) return;                                 // finished by the attention kernel
+  const int64_t base = slot * pch * prows + rr;         // + c * rows
+  const int rg = row0 + rr, l = rg / Gq, h = kvh * Gq + rg % Gq;
+  const bf16_t *zp = q_gate + (((int64_t)b * L + l) * Hq + h) * 2 * D + D + lane * EPL;
+  float z[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) z[j] = (float)zp[j];
+  float M = -INFINITY;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, part_ml[(base + (int64_t)c * prows) * 2]);
+  float lsum = 0.f, acc[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
+  for (int c = 0; c < nch; ++c) {
+    const float *ml = part_ml + (base + (int64_t)c * prows) * 2;
+    const float wc = exp2f(ml[0] - M);                  // a chunk whose rows saw no key has m = -inf: weight 0
+    lsum += wc * ml[1];
+    const float *po = part_o + (base + (int64_t)c * prows) * D + lane * EPL;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) acc[j] += wc * po[j];
+  }
+  const float inv = 1.f / lsum;
+  bf16_t *out = outp + (((int64_t)b * L + l) * Hq + h) * D + lane * EPL;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) out[j] = (bf16_t)(acc[j] * inv * sigmoid_f(z[j]));
+}
+
 hipError_t launch_combine_bf16(const Params &p, hipStream_t s) {
+  if (p.even_split) {
+    const int64_t pairs = (int64_t)p.B * p.Hkv * p.tiles * p.rows;
+    const int64_t blocks = (pairs + kThreads / kWave - 1) / (kThreads / kWave);
+    switch (p.D) {
+      case 64: hipLaunchKernelGGL((combine_rows_kernel<64>), dim3(blocks), dim3(kThreads), 0, s, p); break;
+      case 128: hipLaunchKernelGGL((combine_rows_kernel<128>), dim3(blocks), dim3(kThreads), 0, s, p); break;
+      case 256: hipLaunchKernelGGL((combine_rows_kernel<256>), dim3(blocks), dim3(kThreads), 0, s, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const int64_t blocks = (int64_t)p.B * p.Hkv * p.tiles * p.rows;
   switch (p.D) {
     case 64: hipLaunchKernelGGL((combine_kernel<64>), dim3(blocks), dim3(kThreads), 0, s, p); break;

@@ -26,9 +26,10 @@ namespace {
 
 constexpr int kTileThreads = kPrefillThreads;        // eight wavefronts
 constexpr int kTileWaves = kTileThreads / kWave;
+constexpr int kRowTiles = kPrefillRowTiles;          // 16-row MFMA tiles per wavefront
 constexpr float kLazyMax = 8.f;                      // headroom of the running max, log2 units
 constexpr int kPrefillRows = kPrefillTileRows;       // query rows per workgroup
-static_assert(kPrefillRows == kTileWaves * 16, "one 16-row MFMA tile per wavefront");
+static_assert(kPrefillRows == kTileWaves * 16 * kRowTiles, "row tiles of the wavefronts");
 
 template <int D>
 struct PGeo {
@@ -43,16 +44,18 @@ struct PGeo {
   static constexpr int LPS = (NCP + kTileThreads - 1) / kTileThreads;   // per thread (some idle when D = 64)
 };
 
-// Scores of one 32-key stage for this wavefront's 16 rows:
-// S[kb][i] = S^T[key 16 kb + 4 g4 + i][row m16], from the swizzled K stage
-// tile kt and the query fragments in registers.
-template <int D>
-__device__ __forceinline__ void stage_qk(const unsigned char *kt, const bf16x8 (&qf)[D / 32], f32x4 (&S)[2]) {
+// Scores of one 32-key stage for this wavefront's RT row tiles:
+// S[kb][rt][i] = S^T[key 16 kb + 4 g4 + i][row m16 of tile rt], from the
+// swizzled K stage tile kt and the query fragments in registers.
+template <int D, int RT>
+__device__ __forceinline__ void stage_qk(const unsigned char *kt, const bf16x8 (&qf)[RT][D / 32], f32x4 (&S)[2][RT]) {
   using G = PGeo<D>;
   constexpr int KST = D / 32, RB = G::RB;
   const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) S[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) S[kb][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Unit 4 ks + g4 of key row 16 kb + m16 sits at unit (4 ks + g4) ^ (m16 & SW)
   // = 4 ((ks & 3) ^ c) + 16 (ks >> 2) + (g4 ^ (m16 & 3)) with c = (m16 & SW) >> 2,
   // so four lane offsets cover every k-step (the rest are immediates).
@@ -63,7 +66,8 @@ __device__ __forceinline__ void stage_qk(const unsigned char *kt, const bf16x8 (
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const bf16x8 a = *(const bf16x8 *)(kl + 64 * ((ks & 3) ^ c) + 256 * (ks >> 2) + 16 * RB * kb);
-      S[kb] = mfma_qk(a, qf[ks], S[kb]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) S[kb][rt] = mfma_qk(a, qf[rt][ks], S[kb][rt]);
     }
 }
 
@@ -75,7 +79,7 @@ __device__ __forceinline__ void stage_qk(const unsigned char *kt, const bf16x8 (
 // the row's outputs (and its sum, kept as an output column) need rescaling by
 // alpha.  scale_log2 > 0, so the max is taken on the raw scores.
 template <bool MASK>
-__device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2], int nkeys, int64_t key0, float &m, int64_t lim,
+__device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2], int nkeys, int rel0, float &m, float &ls, int lim,
                                               float scale_log2, bf16x8 &bp, float &alpha) {
   const int g4 = (threadIdx.x % kWave) >> 4;
   float sc[8];
@@ -86,7 +90,7 @@ __device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2], int nkeys, in
       float v = S[kb][i];
       if constexpr (MASK) {
         const int k = 16 * kb + 4 * g4 + i;
-        v = (k < nkeys && key0 + k <= lim) ? v : -INFINITY;
+        v = (k < nkeys && rel0 + k <= lim) ? v : -INFINITY;
       }
       sc[4 * kb + i] = v;
     }
@@ -106,6 +110,7 @@ __device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2], int nkeys, in
   m = mn;
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  float ps = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; j += 2) {
     const f32x2 e = {__builtin_amdgcn_exp2f(__builtin_fmaf(sc[j], scale_log2, -mu)),
@@ -113,18 +118,19 @@ __device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2], int nkeys, in
     const bf16x2_t h = __builtin_convertvector(e, bf16x2_t);
     bp[j] = h[0];
     bp[j + 1] = h[1];
+    ps += (float)h[0] + (float)h[1];
   }
+  ls = ls * alpha + ps;
   return rescale;
 }
 
-// O^T[dim][row] += V^T[dim][key] P^T[key][row] over one 32-key stage, with the
-// MFMA's k index j of lane group g4 standing for key 4 g4 + j (j < 4) or
-// 16 + 4 g4 + j - 4, the order the probabilities were left in; the transposing
-// reads fetch those two 4-key runs of the swizzled V tile for dims 16 db + m16.
-// O[NDB] accumulates P against a block of ones: every lane's entries hold its
-// row's running sum of the same bf16 probabilities the value product uses.
-template <int D>
-__device__ __forceinline__ void stage_values(const unsigned char *vt, const bf16x8 &bp, f32x4 (&O)[D / 16 + 1]) {
+// O^T[dim][row] += V^T[dim][key] P^T[key][row] over one 32-key stage for each
+// row tile, with the MFMA's k index j of lane group g4 standing for key
+// 4 g4 + j (j < 4) or 16 + 4 g4 + j - 4, the order the probabilities were left
+// in; the transposing reads fetch those two 4-key runs of the swizzled V tile
+// for dims 16 db + m16.
+template <int D, int RT>
+__device__ __forceinline__ void stage_values(const unsigned char *vt, const bf16x8 (&bp)[RT], f32x4 (&O)[RT][D / 16]) {
   using G = PGeo<D>;
   constexpr int NDB = D / 16, RB = G::RB;
   const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
@@ -136,19 +142,17 @@ __device__ __forceinline__ void stage_values(const unsigned char *vt, const bf16
   constexpr int E = G::SWV + 1;
   const int klo = 4 * g4 + (m16 >> 2), s = klo & G::SWV;
   const unsigned char *vl = vt + klo * RB + 16 * ((m16 >> 1) & 1) + 8 * (m16 & 1);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     const unsigned char *p0 = vl + 32 * ((db % E) ^ s) + 32 * E * (db / E);
     const unsigned char *p1 = p0 + 16 * RB;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
     const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    O[db] = mfma_qk(__builtin_bit_cast(bf16x8, v8), bp, O[db]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) O[rt][db] = mfma_qk(__builtin_bit_cast(bf16x8, v8), bp[rt], O[rt][db]);
   }
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  const s16x8 ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80};   // bf16 1.0
-  O[NDB] = mfma_qk(__builtin_bit_cast(bf16x8, ones), bp, O[NDB]);
 }
 
 }  // namespace
@@ -163,7 +167,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
                                                         const bf16_t *__restrict__ qt, int L, int Gq, int Hq,
                                                         int tiles, int nitems, Params p) {
   using G = PGeo<D>;
-  constexpr int KST = D / 32, NDB = D / 16, NS = G::NS, LPS = G::LPS, SK = G::SK;
+  constexpr int KST = D / 32, NDB = D / 16, NS = G::NS, LPS = G::LPS, SK = G::SK, RT = kRowTiles;
   __shared__ __attribute__((aligned(16))) unsigned char ring[2 * NS * G::STAGE];   // K ring | V ring
   unsigned char *const kring = ring, *const vring = ring + NS * G::STAGE;
 
@@ -179,39 +183,47 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
   const int b = bk / hkv, kvh = bk % hkv;
   const int R = L * Gq;                                 // rows of this KV head
   const int row0 = tile * kPrefillRows;
-  const int wrow = row0 + 16 * wave + m16;              // this lane's row
-  const int wr = min(wrow, R - 1);
+  int wrow[RT], wr[RT];                                 // this lane's row in each of its row tiles
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    wrow[rt] = row0 + 16 * (RT * wave + rt) + m16;
+    wr[rt] = min(wrow[rt], R - 1);
+  }
 
   // ------------------------------------------------------------ round trip 1: metadata and queries
   const int n = seq_lens[b];
   const int64_t off = seq_offset[b];
-  bf16x8 qf[KST];
-  {
-    const int l = wr / Gq, h = kvh * Gq + wr % Gq;
+  bf16x8 qf[RT][KST];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int l = wr[rt] / Gq, h = kvh * Gq + wr[rt] % Gq;
     const bf16_t *src = qt + (((int64_t)b * L + l) * Hq + h) * D + 8 * g4;
 #pragma unroll
-    for (int ks = 0; ks < KST; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, gld<uint4>(src + 32 * ks));
+    for (int ks = 0; ks < KST; ++ks) qf[rt][ks] = __builtin_bit_cast(bf16x8, gld<uint4>(src + 32 * ks));
   }
-  const int ck = p.chunk_keys, msl = p.max_seq_len;
+  const int ck = p.chunk_keys, msl = p.max_seq_len, even = p.even_split;
   const int64_t nrows = p.num_rows;
   const bf16_t *const kc = (const bf16_t *)p.kc;
   const bf16_t *const vc = (const bf16_t *)p.vc;
   const int32_t *const capp = p.capacity;
   const float sl2 = p.scale_log2;
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::"s"(n), "s"(off), "s"(ck), "s"(msl), "s"(nrows), "s"(kc), "s"(vc), "s"(capp), "s"(sl2));
+  asm volatile("" ::"s"(n), "s"(off), "s"(ck), "s"(msl), "s"(even), "s"(nrows), "s"(kc), "s"(vc), "s"(capp),
+               "s"(sl2));
 #pragma unroll
-  for (int ks = 0; ks < KST; ++ks) {
-    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-    asm volatile("" ::"v"(__builtin_bit_cast(u32x4, qf[ks])));
-  }
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks) {
+      typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+      asm volatile("" ::"v"(__builtin_bit_cast(u32x4, qf[rt][ks])));
+    }
 
   const int64_t total = (int64_t)n + L;
   const bool in_range = n >= 0 && off >= 0 && total <= msl && off + total <= nrows;
   const int cap = capp ? capp[b] : 0x7fffffff;
   const int rlast = min(row0 + kPrefillRows, R) - 1;    // last row of the tile
   const int64_t kend = (int64_t)n + rlast / Gq + 1;     // keys the tile's rows can see
-  const int nch = chunk_count(kend, ck);
+  const int nch = tile_chunk_count(kend, even, pchunks, ck);
   if (chunk >= nch) return;
   if (!in_range) {
     if (chunk == 0) {
@@ -223,30 +235,22 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
     }
     return;
   }
-  const int64_t k0 = (int64_t)chunk * ck;
-  const int64_t k1 = chunk == nch - 1 ? kend : k0 + ck;
+  const int64_t k0 = chunk_begin(kend, even, nch, ck, chunk);
+  const int64_t k1 = chunk == nch - 1 ? kend : chunk_begin(kend, even, nch, ck, chunk + 1);
   const int nst = (int)((k1 - k0 + SK - 1) / SK);
   const int64_t kfull = min(k1, (int64_t)n + row0 / Gq + 1);   // keys below this are visible to every row
-  const int64_t lim = (int64_t)n + wr / Gq;
+  int lim[RT];                                          // causal limit of the lane's rows, relative to n_b
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) lim[rt] = wr[rt] / Gq;
 
   // ------------------------------------------------------------ key stages
   const unsigned kring_lds = (unsigned)(uintptr_t)(lds_void *)kring;
   const unsigned vring_lds = (unsigned)(uintptr_t)(lds_void *)vring;
-  // This thread's copies of a stage: key row keyi[i] of the stage, the 16-byte
-  // unit that the K (V) tile's swizzle puts at this thread's LDS position sits at
-  // byte ubk[i] (ubv[i]) of the source row; the source is that key's row of KV
-  // head kvh, addressed from the stage's first key (wave-uniform) plus a lane
-  // offset.
+  // This thread's copies of a stage: key row u / OCT of the stage, and the
+  // 16-byte unit that the K (V) tile's swizzle puts at LDS position u % OCT of
+  // that row; the source is that key's row of KV head kvh, addressed from the
+  // stage's first key (wave-uniform) plus a lane offset.
   const unsigned rowb = (unsigned)(hkv * D * 2);       // bytes between consecutive keys of one KV head
-  int keyi[LPS];
-  unsigned ubk[LPS], ubv[LPS];
-#pragma unroll
-  for (int i = 0; i < LPS; ++i) {
-    const int u = t + kTileThreads * i;
-    keyi[i] = u / G::OCT;
-    ubk[i] = 16u * (unsigned)((u % G::OCT) ^ (keyi[i] & G::SW));
-    ubv[i] = 16u * (unsigned)((u % G::OCT) ^ (2 * (keyi[i] & G::SWV)));
-  }
   auto issue_stage = [&](int st) {   // keys k0 + SK st .. into ring slot st % NS
     const int64_t sk0 = k0 + (int64_t)SK * st;
     const int last = (int)min<int64_t>(SK - 1, k1 - 1 - sk0);   // keys past the chunk repeat its last key
@@ -254,61 +258,65 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
     const bf16_t *kb = kc + row, *vb = vc + row;
 #pragma unroll
     for (int i = 0; i < LPS; ++i) {
-      const unsigned kr = (unsigned)min(keyi[i], last) * rowb;
+      const int u = t + kTileThreads * i, key = u / G::OCT, pos = u % G::OCT;
+      const unsigned kr = (unsigned)min(key, last) * rowb;
       const unsigned dst = (st % NS) * G::STAGE + kTileThreads * 16 * i + wave * 1024;
       if (G::NCP % kTileThreads == 0 || kTileThreads * i + 64 * wave < G::NCP) {   // wave-uniform
-        dma16_sbase(kb, kr + ubk[i], kring_lds + dst);
-        dma16_sbase(vb, kr + ubv[i], vring_lds + dst);
+        dma16_sbase(kb, kr + 16u * (unsigned)(pos ^ (key & G::SW)), kring_lds + dst);
+        dma16_sbase(vb, kr + 16u * (unsigned)(pos ^ (2 * (key & G::SWV))), vring_lds + dst);
       }
     }
   };
-  static_assert(NS >= 3, "the stages read one stage ahead");
+  static_assert(NS >= 2, "stage copies overlap the stage before");
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
     if (st < nst) issue_stage(st);
 
-  f32x4 O[NDB + 1];                                    // output dims, then the row sum
-  float mrun = -INFINITY;
+  f32x4 O[RT][NDB];
+  float mrun[RT], lrun[RT];                             // lrun: this lane's share of the row sum
 #pragma unroll
-  for (int db = 0; db <= NDB; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Software pipeline: the scores of stage st + 1 are computed in the same
-  // block as the softmax of stage st, so the MFMAs of one overlap the vector
-  // work of the other; the value product of stage st follows.  (Running the two
-  // wavefronts of a SIMD in ping-pong instead measured slower: with half the
-  // wavefronts reading at a time the LDS reads become the critical path.)
-  f32x4 S[2];
-  wait_stages<2 * LPS, NS>(min(NS - 2, nst - 1));
-  lds_barrier();
-  stage_qk<D>(kring, qf, S);
+  for (int rt = 0; rt < RT; ++rt) {
+    mrun[rt] = -INFINITY;
+    lrun[rt] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) O[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // One barrier per stage: stage st is in LDS, and every wavefront is done with
+  // stage st - 1, whose slot is refilled.  Each wavefront then scores, runs its
+  // softmax and accumulates the values of stage st; the two wavefronts of a SIMD
+  // overlap each other's waits.
   for (int st = 0; st < nst; ++st) {
     const int so = (st % NS) * G::STAGE;
-    if (st + 1 < nst) {
-      wait_stages<2 * LPS, NS>(min(NS - 3, nst - 2 - st));
-      lds_barrier();                                    // stage st + 1 is in LDS; every wave is done with stage st - 1
-      if (st + NS - 1 < nst) issue_stage(st + NS - 1);  // refill the slot of stage st - 1
-    }
-    // (after the last stage the next slot holds stale keys; those scores are unused)
-    const unsigned char *kn = kring + ((st + 1) % NS) * G::STAGE;
+    wait_stages<2 * LPS, NS>(min(NS - 2, nst - 1 - st));
+    lds_barrier();
+    if (st + NS - 1 < nst) issue_stage(st + NS - 1);    // refill the slot of stage st - 1
     const int64_t sk0 = k0 + (int64_t)SK * st;
     const int nk = (int)min<int64_t>(SK, k1 - sk0);
-    f32x4 Sn[2];
-    bf16x8 bp;
-    float alpha;
-    bool r;
+    f32x4 S[2][RT];
+    bf16x8 bp[RT];
+    float alpha[RT];
+    bool r = false;
+    stage_qk<D, RT>(kring + so, qf, S);
     if (sk0 + SK <= kfull) {
-      stage_qk<D>(kn, qf, Sn);
-      r = stage_softmax<false>(S, nk, sk0, mrun, lim, sl2, bp, alpha);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const f32x4 st2[2] = {S[0][rt], S[1][rt]};
+        r |= stage_softmax<false>(st2, nk, (int)(sk0 - n), mrun[rt], lrun[rt], lim[rt], sl2, bp[rt], alpha[rt]);
+      }
     } else {
-      stage_qk<D>(kn, qf, Sn);
-      r = stage_softmax<true>(S, nk, sk0, mrun, lim, sl2, bp, alpha);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const f32x4 st2[2] = {S[0][rt], S[1][rt]};
+        r |= stage_softmax<true>(st2, nk, (int)(sk0 - n), mrun[rt], lrun[rt], lim[rt], sl2, bp[rt], alpha[rt]);
+      }
     }
-    S[0] = Sn[0];
-    S[1] = Sn[1];
     if (__any(r)) {
 #pragma unroll
-      for (int db = 0; db <= NDB; ++db) O[db] *= alpha;
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) O[rt][db] *= alpha[rt];
     }
-    stage_values<D>(vring + so, bp, O);
+    stage_values<D, RT>(vring + so, bp, O);
   }
 
   // ------------------------------------------------------------ outputs
@@ -316,9 +324,11 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
   const bool cap_ok = total <= (int64_t)cap;
   const bool single = nch == 1;
   const int64_t slot_rows = ((int64_t)slot * pchunks + chunk) * p.rows;
-  const float lsum = O[NDB][0];
-  if (wrow < R) {
-    const int l = wrow / Gq, h = kvh * Gq + wrow % Gq;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const float lsum = rows4_sum(lrun[rt]);
+    if (wrow[rt] >= R) continue;
+    const int l = wrow[rt] / Gq, h = kvh * Gq + wrow[rt] % Gq;
     const int64_t orow = ((int64_t)b * L + l) * Hq + h;
     if (single) {
       const float inv = 1.f / lsum;
@@ -331,17 +341,19 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
         zr.to_float(z);
         bf16x4 o4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o4[i] = (bf16_t)(cap_ok ? O[db][i] * inv * sigmoid_f(z[i]) : __builtin_nanf(""));
+        for (int i = 0; i < 4; ++i)
+          o4[i] = (bf16_t)(cap_ok ? O[rt][db][i] * inv * sigmoid_f(z[i]) : __builtin_nanf(""));
         *(bf16x4 *)((bf16_t *)p.out + orow * D + d) = o4;
       }
     } else if (cap_ok) {
-      const int rr = wrow - row0;
+      const int rr = wrow[rt] - row0;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int d = 16 * db + 4 * g4;
-        *(float4 *)(p.part_o + (slot_rows + rr) * D + d) = make_float4(O[db][0], O[db][1], O[db][2], O[db][3]);
+        *(float4 *)(p.part_o + (slot_rows + rr) * D + d) =
+            make_float4(O[rt][db][0], O[rt][db][1], O[rt][db][2], O[rt][db][3]);
       }
-      if (g4 == 0) *(float2 *)(p.part_ml + (slot_rows + rr) * 2) = make_float2(mrun, lsum);
+      if (g4 == 0) *(float2 *)(p.part_ml + (slot_rows + rr) * 2) = make_float2(mrun[rt], lsum);
     }
   }
   if (!cap_ok && chunk == 0) {
