@@ -6,97 +6,89 @@
 // rotary_dim dims, dim i paired with i + rotary_dim/2 (mlxd PR #99 Summary,
 // partial_rotary_factor; Atlas Qwen35ForwardConfig::rotary_dim).  Append at
 // slot seq_lens[b] + l (Atlas qwen3_5/mod.rs module doc).
-#include "qsa_internal.h"
+#include "qsa_device.h"
 
 namespace qsa {
 
-// One wavefront per head-row; EPL = D/64 contiguous elements per lane.
-// Jobs [0, nk) are key rows (b, l, kvh): normalised, rotated, rounded and
-// written with the matching value row to the cache.  Jobs [nk, nk+nq) are
-// query rows (b, l, h): normalised and rotated into the prepared-query
-// buffer p.qt (element type TQ).
+// One workgroup per new row (b, l): it tabulates the (cos, sin) of the row's
+// position once, then its four wavefronts walk the row's heads, one head-row
+// per wavefront at a time, EPL = D/64 contiguous elements per lane.  Heads
+// [0, nk) are key heads: normalised, rotated, rounded and written with the
+// matching value row to the cache.  Heads [nk, nk+nq) are query heads:
+// normalised and rotated into the prepared-query buffer p.qt (element type TQ).
 template <typename T, typename TQ, int D>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(Params p, int do_q, int do_kv) {
   constexpr int EPL = D / kWave;
   __shared__ float scratch[kThreads / kWave][D];
+  __shared__ float2 cs[kMaxPairs];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int64_t nk = do_kv ? (int64_t)p.B * p.L * p.Hkv : 0;
-  const int64_t nq = do_q ? (int64_t)p.B * p.L * p.Hq : 0;
-  const int64_t job = (int64_t)blockIdx.x * (kThreads / kWave) + wave;
-  const bool active = job < nk + nq;
-  const bool is_k = job < nk;
-
-  int64_t bl = 0;
-  int head = 0;
-  const T *src = nullptr;
-  const T *w = nullptr;
-  if (active) {
-    if (is_k) {
-      head = (int)(job % p.Hkv);
-      bl = job / p.Hkv;
-      src = (const T *)p.k_new + (bl * p.Hkv + head) * D;
-      w = (const T *)p.wk;
-    } else {
-      const int64_t j = job - nk;
-      head = (int)(j % p.Hq);
-      bl = j / p.Hq;
-      src = (const T *)p.q_gate + (bl * p.Hq + head) * 2 * D;  // query half of [q | gate]
-      w = (const T *)p.wq;
+  const int64_t bl = blockIdx.x;                        // new row (b, l)
+  const int b = (int)(bl / p.L), l = (int)(bl % p.L);
+  const int nk = do_kv ? p.Hkv : 0, nq = do_q ? p.Hq : 0;
+  const int r = p.r, half = r / 2;
+  if (r > 0) {
+    const int pos = p.positions[bl];
+    for (int i = threadIdx.x; i < half; i += kThreads) {
+      float c, sn;
+      rope_cs(p, pos, i, c, sn);
+      cs[i] = make_float2(c, sn);
     }
-  }
-  float x[EPL];
-  float ss = 0.f;
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    x[j] = active ? to_f(src[lane * EPL + j]) : 0.f;
-    ss += x[j] * x[j];
-  }
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)D + p.eps);
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const float wj = active ? to_f(w[lane * EPL + j]) : 0.f;
-    x[j] = x[j] * inv * wj;
-    scratch[wave][lane * EPL + j] = x[j];
   }
   __syncthreads();
-  if (active && p.r > 0) {
-    const int half = p.r / 2;
-    const int pos = p.positions[bl];
+
+  for (int job = wave; job < nk + nq; job += kThreads / kWave) {
+    const bool is_k = job < nk;
+    const int head = is_k ? job : job - nk;
+    const T *src = is_k ? (const T *)p.k_new + (bl * p.Hkv + head) * D
+                        : (const T *)p.q_gate + (bl * p.Hq + head) * 2 * D;   // query half of [q | gate]
+    const T *w = is_k ? (const T *)p.wk : (const T *)p.wq;
+    float x[EPL];
+    float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
-      const int e = lane * EPL + j;
-      if (e < p.r) {
-        const int i = e < half ? e : e - half;
-        float c, s;
-        rope_cs(p, pos, i, c, s);
-        const float other = scratch[wave][e < half ? e + half : e - half];
-        x[j] = e < half ? x[j] * c - other * s : x[j] * c + other * s;
+      x[j] = to_f(src[lane * EPL + j]);
+      ss += x[j] * x[j];
+    }
+    ss = rows4_sum(row16_sum(ss));
+    const float inv = 1.0f / sqrtf(ss / (float)D + p.eps);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) x[j] = x[j] * inv * to_f(w[lane * EPL + j]);
+    if (r > 0) {
+      // partner i +- r/2 of each rotated element, through this wavefront's scratch row
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) scratch[wave][lane * EPL + j] = x[j];
+      wave_lds_sync();
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = lane * EPL + j;
+        if (e < r) {
+          const bool lo = e < half;
+          const float2 v = cs[lo ? e : e - half];
+          const float other = scratch[wave][lo ? e + half : e - half];
+          x[j] = lo ? x[j] * v.x - other * v.y : x[j] * v.x + other * v.y;
+        }
       }
     }
-  }
-  if (!active) return;
-
-  const int b = (int)(bl / p.L), l = (int)(bl % p.L);
-  if (is_k) {
-    const int n = p.seq_lens[b];
-    int64_t off;
-    if (!seq_in_range(p, b, n, off)) {
-      if (lane == 0) flag_error(p);
-      return;
-    }
-    const int64_t dst = ((off + n + l) * p.Hkv + head) * D;
-    const T *vsrc = (const T *)p.v_new + (bl * p.Hkv + head) * D;
+    if (is_k) {
+      const int n = p.seq_lens[b];
+      int64_t off;
+      if (!seq_in_range(p, b, n, off)) {
+        if (lane == 0) flag_error(p);
+        continue;
+      }
+      const int64_t dst = ((off + n + l) * p.Hkv + head) * D;
+      const T *vsrc = (const T *)p.v_new + (bl * p.Hkv + head) * D;
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      const int e = lane * EPL + j;
-      ((T *)p.kc)[dst + e] = from_f<T>(x[j]);
-      ((T *)p.vc)[dst + e] = vsrc[e];
-    }
-  } else {
-    TQ *dst = (TQ *)p.qt + (bl * p.Hq + head) * D;
+      for (int j = 0; j < EPL; ++j) {
+        const int e = lane * EPL + j;
+        ((T *)p.kc)[dst + e] = from_f<T>(x[j]);
+        ((T *)p.vc)[dst + e] = vsrc[e];
+      }
+    } else {
+      TQ *dst = (TQ *)p.qt + (bl * p.Hq + head) * D;
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) dst[lane * EPL + j] = from_f<TQ>(x[j]);
+      for (int j = 0; j < EPL; ++j) dst[lane * EPL + j] = from_f<TQ>(x[j]);
+    }
   }
 }
 
@@ -179,9 +171,8 @@ __global__ __launch_bounds__(kThreads) void rows_f32_kernel(Params p) {
 
 template <typename T, typename TQ>
 static hipError_t prologue_for(const Params &p, bool do_q, bool do_kv, hipStream_t s) {
-  const int64_t jobs = (do_kv ? (int64_t)p.B * p.L * p.Hkv : 0) + (do_q ? (int64_t)p.B * p.L * p.Hq : 0);
-  if (jobs == 0) return hipSuccess;
-  const int64_t blocks = (jobs + 3) / 4;
+  if (!do_q && !do_kv) return hipSuccess;
+  const int64_t blocks = (int64_t)p.B * p.L;            // one workgroup per new row
   switch (p.D) {
     case 64:
       hipLaunchKernelGGL((prologue_kernel<T, TQ, 64>), dim3(blocks), dim3(kThreads), 0, s, p, (int)do_q, (int)do_kv);
