@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from gated_gqa_attention_amd import binding
-from gated_gqa_attention_amd.workloads import WORKLOADS
+from gated_gqa_attention_amd.workloads import WORKLOADS, Workload
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FAKE = 0x7f0000000000   # never dereferenced: every case below fails validation first
@@ -70,6 +70,28 @@ def test_default_plans_fill_one_round_for_short_work():
     assert int(f["workgroups"]) == 256
     f = dict(kv.split("=") for kv in binding.describe_plan(cfg_for(WORKLOADS["verify_24x2"])).split())
     assert int(f["workgroups"]) == 256
+
+
+def test_tile_route_plan_fills_the_chip_with_equal_chunks():
+    """Prefill: 256-row tiles of 512 threads, and just enough equal key chunks
+    per tile (none shorter than 1024 keys) that the grid gives every CU one
+    workgroup; a forced count is capped by the 32-key minimum."""
+    w = WORKLOADS["prefill_4b"]
+    f = dict(kv.split("=") for kv in binding.describe_plan(cfg_for(w)).split())
+    rows = w.q_len * w.num_q_heads // w.num_kv_heads
+    assert int(f["rows"]) == 256 and int(f["threads"]) == 512
+    assert int(f["tiles"]) == -(-rows // 256)
+    slots = w.batch * w.num_kv_heads * int(f["tiles"])
+    assert int(f["chunks"]) == -(-256 // slots) and int(f["chunk_keys"]) == 1024
+    assert int(f["workgroups"]) == slots * int(f["chunks"]) == 256
+    for k in (1, 3, 5000):
+        g = dict(kv.split("=") for kv in binding.describe_plan(cfg_for(w, force_splits=k)).split())
+        assert int(g["chunks"]) == min(k, 32768 // 32) and int(g["chunk_keys"]) == 32
+    # two sequences' tiles already fill the chip: one chunk each
+    w2 = Workload("prefill_b2", batch=2, q_len=2048, num_q_heads=16, num_kv_heads=4, head_dim=256, rotary_dim=64,
+                  rope_theta=1e7, dtype="bf16", prior=30720, seed=1)
+    g = dict(kv.split("=") for kv in binding.describe_plan(cfg_for(w2)).split())
+    assert int(g["chunks"]) == 1 and int(g["workgroups"]) == 256
 
 
 @pytest.mark.parametrize("bad,code", [
