@@ -188,12 +188,17 @@ struct Xch {
 // through LDS and publish their probabilities as one bf16 tile; then each
 // wavefront accumulates its own D/4 output dims over all keys of the stage.
 // Key k is visible to row r when k < nkeys and key0 + k <= lim[r] (causal
-// limit n_b + l_r).  Contains two workgroup barriers.
-template <int D, int RTM>
+// limit n_b + l_r).  Contains two workgroup barriers; on_k_free runs right
+// after the first, when no wave reads the K tile any more.
+struct NoOp {
+  __device__ void operator()() const {}
+};
+
+template <int D, int RTM, typename KFree = NoOp>
 __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsigned char *vt, int nkeys, int64_t key0,
                                              const bf16x8 (&qf)[RTM][D / 32], f32x4 (&O)[RTM][D / 64],
                                              float (&m)[RTM], float (&lsum)[RTM], const int64_t (&lim)[RTM],
-                                             float scale_log2, unsigned char *xch) {
+                                             float scale_log2, unsigned char *xch, KFree on_k_free = KFree()) {
   using G = Geo<D>;
   constexpr int KST = D / 32, DBW = D / 64, RB = G::RB;
   const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
@@ -230,6 +235,7 @@ __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsi
     if (g4 == 0) wmax[wave * 64 + 16 * rt + m16] = bm;
   }
   lds_barrier();
+  on_k_free();                                          // every wave is done with the K tile
 
   // new running max of each row, probabilities, block sums
   float alpha[RTM];

@@ -187,9 +187,22 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   // source is addressed from the stage's first key (wave-uniform, in SGPRs)
   // plus a 32-bit lane offset shared by K and V.
   const unsigned rowb = (unsigned)(hkv * D * 2);       // bytes between consecutive keys of one KV head
-  auto issue_stage = [&](int st) {   // keys k0 + 64 st .. into ring slot st % NS
+  auto issue_half = [&](int st, bool is_k) {   // K or V of keys k0 + 64 st .. into ring slot st % NS
     const int64_t sk0 = k0 + (int64_t)G::SK * st;
     const int last = (int)min<int64_t>(G::SK - 1, cend - 1 - sk0);   // keys past the chunk repeat its last key
+    const bf16_t *base = (is_k ? kc : vc) + ((off + sk0) * hkv + kvh) * D;
+    const unsigned ring_lds = is_k ? kring_lds : vring_lds;
+#pragma unroll
+    for (int i = 0; i < LPS; ++i) {
+      const int u = t + kThreads * i;
+      const int key = u / G::OCT, pos = u % G::OCT, oct = pos ^ (key & G::SW);
+      const unsigned voff = (unsigned)min(key, last) * rowb + 16u * (unsigned)oct;
+      dma16_sbase(base, voff, ring_lds + (st % NS) * G::STAGE + kThreads * 16 * i + wave * 1024);
+    }
+  };
+  auto issue_stage = [&](int st) {   // K and V of keys k0 + 64 st .. into ring slot st % NS, interleaved
+    const int64_t sk0 = k0 + (int64_t)G::SK * st;
+    const int last = (int)min<int64_t>(G::SK - 1, cend - 1 - sk0);
     const int64_t row = ((off + sk0) * hkv + kvh) * D;
     const bf16_t *kb = kc + row, *vb = vc + row;
 #pragma unroll
@@ -202,6 +215,8 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
       dma16_sbase(vb, voff, vring_lds + dst);
     }
   };
+  // Whichever way a stage is issued, its 2 LPS copies stay contiguous in issue
+  // order, so a stage is complete once at most 2 LPS copies per younger stage remain.
 #pragma unroll
   for (int st = 0; st < NS; ++st)
     if (st < nst) issue_stage(st);
@@ -274,9 +289,12 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     const int so = (st % NS) * G::STAGE;
     const int64_t sk0 = k0 + (int64_t)G::SK * st;
     const int nk = (int)min<int64_t>(G::SK, cend - sk0);
-    attend_stage<D, RTM>(kring + so, vring + so, nk, sk0, qf, O, mrun, lrun, lim, sl2, scrb);
+    // the K half of the slot is refilled as soon as the scores are done, the V half after the stage
+    attend_stage<D, RTM>(kring + so, vring + so, nk, sk0, qf, O, mrun, lrun, lim, sl2, scrb, [&]() {
+      if (st + NS < nst) issue_half(st + NS, true);
+    });
     lds_barrier();                                      // every wave is done with ring slot st % NS
-    if (st + NS < nst) issue_stage(st + NS);
+    if (st + NS < nst) issue_half(st + NS, false);
   }
 
   // ------------------------------------------------------------ new keys (tail workgroup)
