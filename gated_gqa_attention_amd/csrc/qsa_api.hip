@@ -108,18 +108,23 @@ int make_plan(const qsa_cfg *c, Plan *pl) {
     } else {
       // Short-query route: chunks of fixed length, the last one taking the
       // remainder.  One round of workgroups (one per CU) for short work; for
-      // long work ~2048 chunks so ragged lengths balance across the CUs.
+      // long work chunks of ~2048 keys (up to ~4096 of them), so ragged lengths
+      // balance across the CUs (measured best between 1024 and 8192 keys).
       int64_t ck;
       if (c->force_splits > 0) {
         ck = std::max<int64_t>(1, S / c->force_splits);
       } else {
         const int64_t total = base * S;
         ck = std::max<int64_t>(qsa::kTileKeys, total / 256);
-        if (ck > 2048) ck = std::max<int64_t>(2048, total / 2048);
+        if (ck > 2048) ck = std::max<int64_t>(2048, total / 4096);
       }
       ck = std::max<int64_t>(ck, cdiv(S, qsa::kMaxChunks));
       p.chunk_keys = (int)std::min<int64_t>(ck, S);
-      p.chunks = (int)std::max<int64_t>(1, S / p.chunk_keys);
+      // long chunks are cut to equal lengths (round(keys / chunk_keys) of them),
+      // so no sequence's last chunk carries a remainder of almost a chunk; short
+      // ones keep the fixed 64-key stage grid
+      p.even_split = c->force_splits == 0 && p.chunk_keys >= 1024;
+      p.chunks = (int)std::max<int64_t>(1, (S + (p.even_split ? p.chunk_keys / 2 : 0)) / p.chunk_keys);
     }
     p.blocks = base * p.chunks;
   }
@@ -310,12 +315,12 @@ int qsa_gated_attention(const void *q_gate, const void *k_new, const void *v_new
       break;
     case kRouteFused:
       e = qsa::launch_stream_bf16(p, s, tm);
-      if (e == hipSuccess && pl.chunks > 1) e = qsa::launch_combine_bf16(p, s);
+      if (e == hipSuccess && pl.chunks > 1) e = qsa::launch_combine_bf16(p, s, false);
       break;
     default:
       e = qsa::launch_prologue(p, QSA_BF16, true, has_new, s);
       if (e == hipSuccess) e = qsa::launch_tile_bf16(p, s, tm);
-      if (e == hipSuccess && pl.chunks > 1) e = qsa::launch_combine_bf16(p, s);
+      if (e == hipSuccess && pl.chunks > 1) e = qsa::launch_combine_bf16(p, s, true);
       break;
   }
   if (e != hipSuccess) return fail(QSA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));

@@ -115,12 +115,12 @@ __device__ __forceinline__ int chunk_count(int64_t kend, int chunk_keys) {
   const int64_t c = kend / chunk_keys;
   return c < 1 ? 1 : (int)c;
 }
-// With even_split (the tile route) they are cut instead into
-// min(chunks, max(1, kend / chunk_keys)) chunks of equal length: chunk c covers
-// [c kend / nch, (c + 1) kend / nch).
+// With even_split they are cut instead into min(chunks, max(1, round(kend /
+// chunk_keys))) chunks of equal length: chunk c covers [c kend / nch,
+// (c + 1) kend / nch).
 __device__ __forceinline__ int tile_chunk_count(int64_t kend, int even_split, int chunks, int chunk_keys) {
   if (!even_split) return chunk_count(kend, chunk_keys);
-  const int64_t c = kend / chunk_keys;
+  const int64_t c = (kend + chunk_keys / 2) / chunk_keys;
   return c < 1 ? 1 : (c > chunks ? chunks : (int)c);
 }
 __device__ __forceinline__ int64_t chunk_begin(int64_t kend, int even_split, int nch, int chunk_keys, int c) {
@@ -162,6 +162,6 @@ hipError_t launch_prologue(const Params &p, int dtype, bool do_q, bool do_kv, hi
 hipError_t launch_rows_f32(const Params &p, hipStream_t s, const Timing &tm);
 hipError_t launch_tile_bf16(const Params &p, hipStream_t s, const Timing &tm);
 hipError_t launch_stream_bf16(const Params &p, hipStream_t s, const Timing &tm);
-hipError_t launch_combine_bf16(const Params &p, hipStream_t s);
+hipError_t launch_combine_bf16(const Params &p, hipStream_t s, bool per_row);   // per_row: the tile route's merge
 
 }  // namespace qsa

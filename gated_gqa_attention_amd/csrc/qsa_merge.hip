@@ -179,8 +179,8 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(Params p) {
   for (int j = 0; j < EPL; ++j) out[j] = (bf16_t)(acc[j] * inv * sigmoid_f(z[j]));
 }
 
-hipError_t launch_combine_bf16(const Params &p, hipStream_t s) {
-  if (p.even_split) {
+hipError_t launch_combine_bf16(const Params &p, hipStream_t s, bool per_row) {
+  if (per_row) {
     const int64_t pairs = (int64_t)p.B * p.Hkv * p.tiles * p.rows;
     const int64_t blocks = (pairs + kThreads / kWave - 1) / (kThreads / kWave);
     switch (p.D) {

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   wqraw.load(wq_ptr + E * m16);
   const int tpos = positions[(int64_t)b * L + min(t, L - 1)];
   // arguments that live in memory, fetched in the same round trip
-  const int ck = p.chunk_keys, msl = p.max_seq_len, rdim = p.r, pchunks = p.chunks;
+  const int ck = p.chunk_keys, msl = p.max_seq_len, rdim = p.r, pchunks = p.chunks, even = p.even_split;
   const int64_t nrows = p.num_rows;
   const bf16_t *const kc = (const bf16_t *)p.kc;
   const bf16_t *const vc = (const bf16_t *)p.vc;
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   const double l2t = p.log2_theta;
   const float eps = p.eps, sl2 = p.scale_log2;
   __builtin_amdgcn_sched_barrier(0);                   // every load above is issued before any wait
-  asm volatile("" ::"s"(n), "s"(off), "s"(ck), "s"(msl), "s"(rdim), "s"(pchunks), "s"(nrows), "s"(kc), "s"(vc),
+  asm volatile("" ::"s"(n), "s"(off), "s"(ck), "s"(msl), "s"(rdim), "s"(pchunks), "s"(even), "s"(nrows), "s"(kc), "s"(vc),
                "s"(knew), "s"(l2t), "s"(eps), "s"(sl2));
 #pragma unroll
   for (int rt = 0; rt < RTM; ++rt) qraw[rt].land();
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   const int32_t *const capp = p.capacity;
   const int cap = capp ? capp[b] : 0x7fffffff;
   const int64_t kend = total;
-  const int nch = chunk_count(kend, ck);
+  const int nch = tile_chunk_count(kend, even, pchunks, ck);
   if (chunk >= nch) return;
   if (!in_range) {
     if (chunk == 0) {
@@ -172,8 +172,8 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     }
     return;
   }
-  const int64_t k0 = (int64_t)chunk * ck;
-  const int64_t k1 = chunk == nch - 1 ? kend : k0 + ck;
+  const int64_t k0 = chunk_begin(kend, even, nch, ck, chunk);
+  const int64_t k1 = chunk == nch - 1 ? kend : chunk_begin(kend, even, nch, ck, chunk + 1);
   const bool fuse_new = knew != nullptr;
   const bool tail = fuse_new && chunk == nch - 1;       // this workgroup holds the new keys
   const int64_t cend = fuse_new ? min(k1, (int64_t)n) : k1;   // cached keys [k0, cend)

@@ -161,6 +161,25 @@ def test_late_dominant_keys_move_the_running_max(w, splits):
     assert sess.device_error() == 0
 
 
+def test_long_decode_equal_chunks():
+    """Enough keys that the short-query route cuts each sequence into
+    equal-length chunks of ~2048 keys (rounded count) instead of fixed ones."""
+    w = Workload("bf16_long_even", batch=8, q_len=1, num_q_heads=8, num_kv_heads=4, head_dim=128,
+                 rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=0, seed=117, ragged=(17000, 23000))
+    inp = make_inputs(w)
+    sess = Session(w, inp)
+    plan = sess.plan()
+    say(f"case {w.name} plan {plan}")
+    fields = dict(kv.split("=") for kv in plan.split())
+    assert fields["route"] == "fused_splitk" and int(fields["chunk_keys"]) >= 1024
+    out = to_np(sess.run())
+    torch.cuda.synchronize()
+    ref, kr, vr = oracle.gated_attention(geo(w), inp)
+    check(out, ref, w.dtype, w.name)
+    check_rows(sess, inp, kr, vr, w)
+    assert sess.device_error() == 0
+
+
 @pytest.mark.parametrize("name", ["decode_4b", "verify_24x2"])
 def test_parity_full_workload(name):
     w = WORKLOADS[name]
