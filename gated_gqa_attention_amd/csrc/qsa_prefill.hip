@@ -3,13 +3,14 @@
 // rotated the queries into the prepared buffer and appended the new keys and
 // values to the cache (Atlas qwen3_5/mod.rs module doc: append, then attend).
 //
-// tile_kernel: one workgroup = (sequence b, KV head g, tile of 128 query rows,
+// tile_kernel: one workgroup = (sequence b, KV head g, tile of 256 query rows,
 // key chunk).  The rows are (new row l, head of group g) pairs in order
 // r = l * G + (h - g * G) (DS4Server issue #113, Reproduction: query heads
 // grouped within their KV group), so one K/V stream serves the whole group.
 // The chunk's keys stream through an HBM -> LDS ring of 32-key stages; eight
 // wavefronts (two per SIMD, so one can issue while the other waits) each own
-// 16 rows and run their own online softmax over every stage:
+// two 16-row MFMA tiles (32 rows) and run their own online softmax over every
+// stage:
 // scores S^T = K Q^T on MFMA with the queries in registers, the running max and
 // the probabilities in registers, then O^T += V^T P^T on MFMA.  The value
 // product takes its keys in a permuted order that matches the layout the score
