@@ -22,8 +22,12 @@ SOURCES = ["qsa_api.hip", "qsa_rows.hip", "qsa_stream.hip", "qsa_prefill.hip", "
 # per-source extra flags: the streaming and tile kernels take their leading
 # argument dwords (metadata and query pointers, grid shape) preloaded into
 # SGPRs; their LDS copies set M0 from inline assembly, hence -Wno-inline-asm
-# (nothing else in those files uses M0)
-EXTRA = {"qsa_stream.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=13", "-Wno-inline-asm"],
+# (nothing else in those files uses M0).  The short-query kernel keeps its MFMA
+# accumulators in VGPRs (-amdgpu-mfma-vgpr-form): it fits in the 512 registers
+# of one wavefront per SIMD, and AGPR accumulators cost a copy of every output
+# register per key stage.
+EXTRA = {"qsa_stream.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=13", "-mllvm", "-amdgpu-mfma-vgpr-form",
+                           "-Wno-inline-asm"],
          "qsa_prefill.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=11", "-Wno-inline-asm"]}
 ARCH = "gfx950"
 

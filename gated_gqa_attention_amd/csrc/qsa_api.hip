@@ -86,12 +86,15 @@ int make_plan(const qsa_cfg *c, Plan *pl) {
     p.chunk_keys = (int)S;
     p.blocks = B * L * Hq;
   } else {
-    // The short-query kernel packs L, G and Hq into one 32-bit argument and
-    // tabulates (cos, sin) for its L positions x r/2 pairs in LDS.
-    const bool fused = rows_total <= qsa::kTileRows && L <= qsa::kMaxFusedNewRows && c->num_q_heads <= 32767 &&
-                       L * (c->rotary_dim / 2) <= qsa::kMaxTableEntries;
+    // The short-query kernel packs L, G and Hq into one 32-bit argument,
+    // keeps up to 48 prepared query rows and two (cos, sin) tables of L
+    // positions x r/2 pairs in LDS beside its key ring, and rotates by whole
+    // lanes, so r/2 must be a multiple of the head_dim/16 elements a lane holds.
+    const bool fused = rows_total <= qsa::kMaxFusedRows && L <= qsa::kMaxFusedNewRows &&
+                       c->num_q_heads <= 32767 && L * (c->rotary_dim / 2) <= qsa::kMaxFusedTable &&
+                       (c->rotary_dim / 2) % (D / 16) == 0;
     p.route = fused ? kRouteFused : kRoutePrepared;
-    const int64_t tile_rows = fused ? qsa::kTileRows : qsa::kPrefillTileRows;
+    const int64_t tile_rows = fused ? qsa::kMaxFusedRows : qsa::kPrefillTileRows;
     p.tiles = (int)cdiv(rows_total, tile_rows);
     p.rows = (int)std::min<int64_t>(rows_total, tile_rows);
     const int64_t base = B * Hkv * p.tiles;
@@ -168,6 +171,7 @@ qsa::Params base_params(const qsa_cfg *c, const Plan &pl) {
   for (int i = 0; i < c->rotary_dim / 2; ++i)
     p.inv_freq[i] = std::pow((double)c->rope_theta, -2.0 * i / (double)c->rotary_dim);
   p.log2_theta = std::log2((double)c->rope_theta);
+  p.rope_step = c->rotary_dim > 0 ? std::pow((double)c->rope_theta, -2.0 / (double)c->rotary_dim) : 1.0;
   p.wq = c->q_norm_w;
   p.wk = c->k_norm_w;
   return p;

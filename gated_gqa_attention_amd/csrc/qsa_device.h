@@ -28,8 +28,6 @@ struct Geo {
   static constexpr int KST = D / 32;                    // k-steps of the score product
   static constexpr int NDB = D / 16;                    // 16-dim blocks of the value product
   static constexpr int E = D / 16;                      // elements per lane in row work (16 lanes per row)
-  static constexpr int SCR = 16 * D * 4;                // 16 fp32 rows of row scratch
-  static constexpr int TAB_N = kMaxTableEntries;        // (cos, sin) entries
 };
 
 __device__ __forceinline__ f32x4 mfma_qk(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -51,6 +49,14 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp<0x124>(v);   // row_ror:4
   v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
   v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  return v;
+}
+// max over the 16 lanes of a row
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<0x128>(v));   // row_ror:8
+  v = fmaxf(v, dpp<0x124>(v));   // row_ror:4
+  v = fmaxf(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp<0xB1>(v));    // quad_perm [1,0,3,2]
   return v;
 }
 // combine lanes i, i^16, i^32, i^48 (the four rows) with gfx950's lane swaps
@@ -109,6 +115,7 @@ __device__ __forceinline__ void wait_stages(int younger) {
 template <typename T> struct nat { using type = T; };
 template <> struct nat<uint4> { using type = unsigned __attribute__((ext_vector_type(4))); };
 template <> struct nat<uint2> { using type = unsigned __attribute__((ext_vector_type(2))); };
+template <> struct nat<float2> { using type = float __attribute__((ext_vector_type(2))); };
 template <typename T>
 __device__ __forceinline__ T gld(const void *ptr) {
   using N = typename nat<T>::type;
@@ -190,14 +197,16 @@ struct Xch {
 // Key k is visible to row r when k < nkeys and key0 + k <= lim[r] (causal
 // limit n_b + l_r).  Contains two workgroup barriers; on_k_free runs right
 // after the first, when no wave reads the K tile any more.
+constexpr float kMaxLead = 8.f;
+
 struct NoOp {
   __device__ void operator()() const {}
 };
 
 template <int D, int RTM, typename KFree = NoOp>
-__device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsigned char *vt, int nkeys, int64_t key0,
+__device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsigned char *vt, int nkeys, int key0,
                                              const bf16x8 (&qf)[RTM][D / 32], f32x4 (&O)[RTM][D / 64],
-                                             float (&m)[RTM], float (&lsum)[RTM], const int64_t (&lim)[RTM],
+                                             float (&m)[RTM], float (&lsum)[RTM], const int (&lim)[RTM],
                                              float scale_log2, unsigned char *xch, KFree on_k_free = KFree()) {
   using G = Geo<D>;
   constexpr int KST = D / 32, DBW = D / 64, RB = G::RB;
@@ -223,12 +232,13 @@ __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsi
   float sc[RTM][4];
 #pragma unroll
   for (int rt = 0; rt < RTM; ++rt) {
+    // keys j of this wavefront with j < vis are visible to the lane's row
+    const int vis = min(lim[rt] - key0 - 16 * wave + 1, nvalid);
     float bm = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = 4 * g4 + i;
-      const bool ok = j < nvalid && key0 + 16 * wave + j <= lim[rt];
-      sc[rt][i] = ok ? S[rt][i] * scale_log2 : -INFINITY;
+      sc[rt][i] = j < vis ? S[rt][i] * scale_log2 : -INFINITY;
       bm = fmaxf(bm, sc[rt][i]);
     }
     bm = rows4_max(bm);
@@ -237,23 +247,28 @@ __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsi
   lds_barrier();
   on_k_free();                                          // every wave is done with the K tile
 
-  // new running max of each row, probabilities, block sums
+  // reference max of each row, probabilities, block sums.  The reference max
+  // moves only when the stage max passes it by more than kMaxLead (log2
+  // units), so probabilities stay <= 2^kMaxLead and the output rescale is rare;
+  // sums and outputs always refer to the current reference, which is what the
+  // merge receives.  exp2 is v_exp_f32 (results below 2^-126 flush to zero).
   float alpha[RTM];
   bool rescale = false;
 #pragma unroll
   for (int rt = 0; rt < RTM; ++rt) {
     const int row = 16 * rt + m16;
     const float M = fmaxf(fmaxf(wmax[row], wmax[64 + row]), fmaxf(wmax[128 + row], wmax[192 + row]));
-    const float mn = fmaxf(m[rt], M);
+    const bool grow = M > m[rt] + kMaxLead;             // also when m is -inf and M is finite
+    const float mn = grow ? M : m[rt];
     const float mu = mn == -INFINITY ? 0.f : mn;
-    alpha[rt] = exp2f(m[rt] - mu);
-    rescale |= alpha[rt] != 1.f && m[rt] != -INFINITY;
+    alpha[rt] = __builtin_amdgcn_exp2f(m[rt] - mu);
+    rescale |= grow && m[rt] != -INFINITY;
     m[rt] = mn;
     float ps = 0.f;
     bf16x4 pv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pv[i] = (bf16_t)exp2f(sc[rt][i] - mu);
+      pv[i] = (bf16_t)__builtin_amdgcn_exp2f(sc[rt][i] - mu);
       ps += (float)pv[i];
     }
     *(bf16x4 *)(xch + (16 * rt + m16) * Xch::PSTRIDE + 2 * (16 * wave + 4 * g4)) = pv;

@@ -25,7 +25,8 @@ constexpr int kPrefillTileRows = 16 * kPrefillRowTiles * kPrefillThreads / kWave
 constexpr int kMaxFusedNewRows = 16;  // new rows a fused call may append per sequence
 constexpr int kMaxPairs = 128;        // rotary pairs (rotary_dim / 2) supported
 constexpr int kMaxChunks = 4096;      // key chunks per (sequence, KV head, tile)
-constexpr int kMaxTableEntries = 1024;  // (cos, sin) pairs a short-query call tabulates: L * r/2
+constexpr int kMaxFusedTable = 512;   // (cos, sin) pairs a short-query call tabulates: L * r/2
+constexpr int kMaxFusedRows = 48;     // query rows (group heads x new rows) of a short-query call
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Workspace layout (bytes, 256-aligned sections):
@@ -66,6 +67,7 @@ struct Params {
   float *part_o;
   void *qt;
   double log2_theta;           // log2(theta), computed on the host in double
+  double rope_step;            // theta^(-2/r) (r > 0), computed on the host in double
   double inv_freq[kMaxPairs];  // theta^(-2i/r), computed on the host in double
 };
 

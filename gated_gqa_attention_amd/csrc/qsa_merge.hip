@@ -14,17 +14,14 @@ namespace qsa {
 // Merge the key chunks of one (slot, row): weights 2^(m_c - M) / sum_c l_c 2^(m_c - M),
 // weighted sum of the unnormalised chunk outputs, then the sigmoid gate.  For
 // the short-query route, whose rows can have thousands of chunks: one
-// workgroup per (slot, row), waves take interleaved chunks, lanes take
-// EPL = D/64 dims.
+// workgroup of D threads per (slot, row), one output dim per lane, so each
+// wavefront merges its 64 dims over every chunk on its own, with no LDS and no
+// barrier.  Chunks go in batches of 64: lane c holds chunk c's statistics, the
+// batch max and sums are wavefront reductions, and each chunk's weight is
+// broadcast from its lane to the whole wavefront.
 template <int D>
-__global__ __launch_bounds__(kThreads) void combine_kernel(Params p) {
-  constexpr int EPL = D / kWave;
-  constexpr int kBatch = 16;                            // chunks in flight per wave
-  __shared__ float wts[kMaxChunks];
-  __shared__ float acc_x[kThreads / kWave][D];
-  __shared__ float red[kThreads / kWave];
-  __shared__ float s_inv;
-  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
+__global__ __launch_bounds__(D) void combine_kernel(Params p) {
+  const int d = threadIdx.x, lane = d % kWave;
   const int rr = blockIdx.x % p.rows;
   const int slot = blockIdx.x / p.rows;
   const int tile = slot % p.tiles;
@@ -41,79 +38,30 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Params p) {
   const int nch = tile_chunk_count((int64_t)n + lmax + 1, p.even_split, p.chunks, p.chunk_keys);
   if (nch == 1) return;                                 // finished by the attention kernel
 
-  // every load first: chunk statistics, the gate, the first batch of partial outputs
   const int64_t base = (int64_t)slot * p.chunks * p.rows + rr;   // + c * rows
   const int rg = row0 + rr, l = rg / p.G, h = kvh * p.G + rg % p.G;
-  const bf16_t *zp = (const bf16_t *)p.q_gate + (((int64_t)b * p.L + l) * p.Hq + h) * 2 * D + D + lane * EPL;
-  float z[EPL];
+  const float z = (float)gld<bf16_t>((const bf16_t *)p.q_gate + (((int64_t)b * p.L + l) * p.Hq + h) * 2 * D + D + d);
+  float M = -INFINITY, lsum = 0.f, acc = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += kWave) {
+    // every load of the batch first: this lane's chunk statistics, then the 64 chunk outputs of dim d
+    const int cl = min(c0 + lane, nch - 1);
+    const float2 ml = gld<float2>(p.part_ml + (base + (int64_t)cl * p.rows) * 2);
+    float v[kWave];
 #pragma unroll
-  for (int j = 0; j < EPL; ++j) z[j] = (float)gld<bf16_t>(zp + j);
-  const int cm = min(t, nch - 1);
-  const float m_c = gld<float>(p.part_ml + (base + (int64_t)cm * p.rows) * 2);
-  const float l_c = gld<float>(p.part_ml + (base + (int64_t)cm * p.rows) * 2 + 1);
-  float v[kBatch][EPL];
+    for (int k = 0; k < kWave; ++k) v[k] = gld<float>(p.part_o + (base + (int64_t)min(c0 + k, nch - 1) * p.rows) * D + d);
+    const bool own = c0 + lane < nch;
+    const float mc = own ? ml.x : -INFINITY;
+    const float Mn = fmaxf(M, rows4_max(row16_max(mc)));
+    const float mu = Mn == -INFINITY ? 0.f : Mn;        // a chunk whose rows saw no key has m = -inf: weight 0
+    const float alpha = __builtin_amdgcn_exp2f(M - mu);
+    const float wc = own ? __builtin_amdgcn_exp2f(mc - mu) : 0.f;
+    lsum = lsum * alpha + rows4_sum(row16_sum(wc * (own ? ml.y : 0.f)));
+    acc *= alpha;
 #pragma unroll
-  for (int k = 0; k < kBatch; ++k) {
-    const int c = min(wave + k * (kThreads / kWave), nch - 1);
-    const float *po = p.part_o + (base + (int64_t)c * p.rows) * D + lane * EPL;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) v[k][j] = gld<float>(po + j);
+    for (int k = 0; k < kWave; ++k) acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wc), k)) * v[k];
+    M = Mn;
   }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // weights w_c = 2^(m_c - M) / sum_c l_c 2^(m_c - M)   (chunks beyond 256 are rare)
-  float mx = t < nch ? m_c : -INFINITY;
-  for (int c = t + kThreads; c < nch; c += kThreads) mx = fmaxf(mx, p.part_ml[(base + (int64_t)c * p.rows) * 2]);
-  mx = wave_max(mx);
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float ls = 0.f;
-  if (t < nch) {
-    const float e = exp2f(m_c - M);
-    wts[t] = e;
-    ls = e * l_c;
-  }
-  for (int c = t + kThreads; c < nch; c += kThreads) {
-    const float e = exp2f(p.part_ml[(base + (int64_t)c * p.rows) * 2] - M);
-    wts[c] = e;
-    ls += e * p.part_ml[(base + (int64_t)c * p.rows) * 2 + 1];
-  }
-  ls = wave_sum(ls);
-  __syncthreads();
-  if (lane == 0) red[wave] = ls;
-  __syncthreads();
-  if (t == 0) s_inv = 1.f / ((red[0] + red[1]) + (red[2] + red[3]));
-  __syncthreads();
-
-  float acc[EPL];
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
-#pragma unroll
-  for (int k = 0; k < kBatch; ++k) {
-    const int c = wave + k * (kThreads / kWave);
-    const float wc = c < nch ? wts[c] : 0.f;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) acc[j] += wc * v[k][j];
-  }
-  for (int c0 = wave + kBatch * (kThreads / kWave); c0 < nch; c0 += kThreads / kWave) {
-    const float wc = wts[c0];
-    const float *po = p.part_o + (base + (int64_t)c0 * p.rows) * D + lane * EPL;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) acc[j] += wc * po[j];
-  }
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) acc_x[wave][lane * EPL + j] = acc[j];
-  __syncthreads();
-  if (wave != 0) return;
-  const float inv = s_inv;
-  bf16_t *out = (bf16_t *)p.out + (((int64_t)b * p.L + l) * p.Hq + h) * D;
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const int d = lane * EPL + j;
-    const float o = ((acc_x[0][d] + acc_x[1][d]) + (acc_x[2][d] + acc_x[3][d])) * inv;
-    out[d] = (bf16_t)(o * sigmoid_f(z[j]));
-  }
+  ((bf16_t *)p.out)[(((int64_t)b * p.L + l) * p.Hq + h) * D + d] = (bf16_t)(acc / lsum * sigmoid_f(z));
 }
 
 // Merge for the tile route, whose rows have few key chunks each: one wavefront
@@ -193,9 +141,9 @@ hipError_t launch_combine_bf16(const Params &p, hipStream_t s, bool per_row) {
   }
   const int64_t blocks = (int64_t)p.B * p.Hkv * p.tiles * p.rows;
   switch (p.D) {
-    case 64: hipLaunchKernelGGL((combine_kernel<64>), dim3(blocks), dim3(kThreads), 0, s, p); break;
-    case 128: hipLaunchKernelGGL((combine_kernel<128>), dim3(blocks), dim3(kThreads), 0, s, p); break;
-    case 256: hipLaunchKernelGGL((combine_kernel<256>), dim3(blocks), dim3(kThreads), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((combine_kernel<64>), dim3(blocks), dim3(64), 0, s, p); break;
+    case 128: hipLaunchKernelGGL((combine_kernel<128>), dim3(blocks), dim3(128), 0, s, p); break;
+    case 256: hipLaunchKernelGGL((combine_kernel<256>), dim3(blocks), dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

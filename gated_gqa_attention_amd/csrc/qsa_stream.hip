@@ -12,13 +12,13 @@
 // copied straight from HBM into LDS by global_load_lds_dwordx4 (no register
 // staging); a stage's rows are XOR-swizzled in 16-byte units so that both the
 // K operand reads (16 keys, one column) and the transposing V reads are free
-// of bank conflicts.  While the first stages are in flight the workgroup
-// splits q_gate, RMS-normalises and rotates its query rows (mlxd PR #99
+// of bank conflicts.  Two wavefronts issue the first stages while the other
+// two split q_gate, RMS-normalise and rotate the query rows (mlxd PR #99
 // Summary and config audit table; Atlas FullAttentionLayer q_norm / k_norm,
-// Qwen35ForwardConfig::rotary_dim), and the workgroup whose chunk ends the
-// sequence normalises and rotates the new keys after the cached stages, keeps
-// them in LDS as the last stage and appends them to the cache at the end (Atlas
-// qwen3_5/mod.rs module doc: append at cache_pos, attend over cache_pos + 1 keys).
+// Qwen35ForwardConfig::rotary_dim) and, in the workgroup whose chunk ends the
+// sequence, the new keys; those are kept in registers, become the last stage
+// and are appended to the cache at the end (Atlas qwen3_5/mod.rs module doc:
+// append at cache_pos, attend over cache_pos + 1 keys).
 //
 // Compute (the stage step in qsa_device.h).  Wavefront w scores keys
 // 16 w .. 16 w + 15 of the stage against every row tile,
@@ -30,14 +30,14 @@
 // with V^T read by gfx950's transposing LDS loads.  A chunk that covers the
 // whole sequence applies the gate attn * sigmoid(gate) (mlxd PR #99 Summary)
 // and stores bf16; otherwise it writes the chunk's (max, sum, unnormalised
-// output) for the merge kernel.  The new keys become one more stage after the
-// cached ones.
+// output) for the merge kernel.
 //
 // Counters.  The copies are issued from inline assembly and waited for
 // explicitly (s_waitcnt vmcnt with the number of younger copies): the compiler
 // cannot count them, and any load it had to wait for after them would drain
-// the whole ring.  So every small load the prologue needs lands before the
-// first copy is issued, and later loads are consumed only after the stages.
+// the whole ring.  So the wavefronts that issue the first stages load nothing
+// but the sequence metadata before them, and later loads are consumed only
+// after the stages.
 #include "qsa_device.h"
 
 namespace qsa {
@@ -45,14 +45,17 @@ namespace qsa {
 namespace {
 
 // RMS norm and partial rotation of one head row held by 16 lanes (E elements
-// each, lane c16 holds elements E*c16 .. E*c16+E-1).  scr_row: this row's fp32
-// scratch (D floats); cs: (cos, sin) of this row's position for pairs
-// 0 .. r/2-1.  Every LDS read of a lane is issued before any is used.
+// each, lane c16 holds elements E*c16 .. E*c16+E-1).  cs: (cos, sin) of this
+// row's position for pairs 0 .. r/2-1, 16-byte aligned.  The route admits only
+// rotary dims with r/2 a multiple of E, so every rotated lane holds E elements
+// of one half, its partner lane is r/(2E) lanes away in the same row, and its
+// pairs are the E consecutive pairs from i0: the partner values come over by
+// lane permutes and the pair table is read as whole vectors.
 template <int D>
 __device__ __forceinline__ void norm_rope(float (&x)[D / 16], const float (&w)[D / 16], bool valid, float eps,
-                                          int r, const float2 *cs, float *scr_row) {
+                                          int r, const float2 *cs) {
   constexpr int E = D / 16;
-  const int c16 = threadIdx.x & 15;
+  const int lane = threadIdx.x % kWave, c16 = lane & 15;
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < E; ++j) ss += x[j] * x[j];
@@ -61,44 +64,59 @@ __device__ __forceinline__ void norm_rope(float (&x)[D / 16], const float (&w)[D
 #pragma unroll
   for (int j = 0; j < E; ++j) x[j] = x[j] * inv * w[j];
   if (r == 0) return;
-  const int half = r / 2;
+  const int half = r / 2, e0 = c16 * E, nl = half / E;
+  const bool lo = e0 < half, rot = e0 < r;
+  const int src = rot ? (lo ? lane + nl : lane - nl) : lane;
+  float xp[E];
 #pragma unroll
-  for (int j = 0; j < E; j += 4) *(float4 *)(scr_row + c16 * E + j) = make_float4(x[j], x[j + 1], x[j + 2], x[j + 3]);
-  wave_lds_sync();
-  if (c16 * E >= r) return;                             // no rotated element in this lane
-  float xp[E], c[E], sn[E];
+  for (int j = 0; j < E; ++j) xp[j] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(x[j])));
+  if (!rot) return;
+  const int i0 = lo ? e0 : e0 - half;
+  float4 cs4[E / 2];
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    const int e = c16 * E + j;
-    const bool lo = e < half;
-    xp[j] = scr_row[lo ? e + half : e - half];          // in range for every e < D
-  }
-#pragma unroll
-  for (int j = 0; j < E; ++j) {
-    const int e = c16 * E + j;
-    const int i = min(e < half ? e : e - half, half - 1);
-    const float2 v = cs[i];
-    c[j] = v.x;
-    sn[j] = v.y;
-  }
+  for (int j = 0; j < E / 2; ++j) cs4[j] = *(const float4 *)(cs + i0 + 2 * j);
+  const float sg = lo ? -1.f : 1.f;                     // lo: x c - x' s; hi: x c + x' s
 #pragma unroll
   for (int j = 0; j < E; ++j) {
-    const int e = c16 * E + j;
-    const float lo_v = x[j] * c[j] - xp[j] * sn[j], hi_v = x[j] * c[j] + xp[j] * sn[j];
-    x[j] = e < half ? lo_v : (e < r ? hi_v : x[j]);
+    const float cj = j % 2 == 0 ? cs4[j / 2].x : cs4[j / 2].z;
+    const float sj = j % 2 == 0 ? cs4[j / 2].y : cs4[j / 2].w;
+    x[j] = fmaf(sg * xp[j], sj, x[j] * cj);
   }
 }
 
+// Waits until at most u * LPS vector-memory operations of this wave are
+// outstanding (u wave-uniform, 0 <= u <= U).
+template <int LPS, int U>
+struct WaitUnits {
+  __device__ static __forceinline__ void run(int u) {
+    if (u == U) {
+      wait_vm<U * LPS>();
+      return;
+    }
+    WaitUnits<LPS, U - 1>::run(u);
+  }
+};
+template <int LPS>
+struct WaitUnits<LPS, 0> {
+  __device__ static __forceinline__ void run(int) { wait_vm<0>(); }
+};
+
 }  // namespace
 
-// RTM: row tiles (16 rows each) of the workgroup, ceil(L * G / 16).
+// RTM: row tiles (16 rows each) of the workgroup, ceil(L * G / 16) <= 3.
 //
-// The leading arguments are preloaded into SGPRs at wave launch, so the loads
-// that need only them (sequence metadata, query rows, query norm weight,
-// positions) are issued at once.  All of them are waited for before the first
-// copy is issued: the vector-memory counter retires in order, and a load
-// consumed after the copies would make its consumer wait for every copy.
-// lgh packs L (bits 0-7), G (bits 8-15) and Hq (bits 16-31).
+// Two roles until the first stage.  Wavefronts 0-1 (the copy waves) load the
+// sequence metadata and issue every copy of the first stages; the memory
+// system accepts them at the rate it delivers, so those waves are held at the
+// issue for most of the transfer.  Their vector-memory counter must see no
+// other load after the copies, since it retires in order and a later load
+// would make its consumer wait for every copy.  Wavefronts 2-3 (the prep
+// waves) issue no copies, so they load freely: each builds its own (cos, sin)
+// table, the two normalise and rotate all query rows into bf16 MFMA operands
+// in LDS, and, in the workgroup that holds the new keys, normalise and rotate
+// those too.  Then all four wavefronts meet, take their query operands and run
+// the stages together; refills of the ring are shared by all four.
+// lgh packs L (bits 0-7), G (bits 8-15) and r/2 (bits 16-31).
 template <int D, int RTM>
 __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restrict__ seq_lens,
                                                           const int64_t *__restrict__ seq_offset,
@@ -108,57 +126,64 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
                                                           int lgh, Params p) {
   using G = Geo<D>;
   constexpr int E = G::E, KST = G::KST, RB = G::RB, NS = G::NS, LPS = G::LPS, DBW = D / 64;
-  constexpr int SCR = G::SCR > Xch::BYTES ? G::SCR : Xch::BYTES;
+  constexpr int QBYTES = 16 * RTM * RB;                 // prepared query rows, bf16, swizzled
+  constexpr int TABN = kMaxFusedTable;                  // (cos, sin) entries per table copy
+  constexpr int PREP = QBYTES + 2 * TABN * 8;
+  constexpr int ARENA = PREP > Xch::BYTES ? PREP : Xch::BYTES;
+  constexpr int NPASS = 2 * RTM;                        // query row passes per prep wave (8 rows each)
+  static_assert(RTM <= 3, "query rows of the short-query route");
   __shared__ __attribute__((aligned(16))) unsigned char ring[2 * G::RING];   // K ring | V ring
   unsigned char *const kring = ring, *const vring = ring + G::RING;
-  __shared__ __attribute__((aligned(16))) float scr[SCR / 4];   // row scratch, then the stage exchange
-  __shared__ __attribute__((aligned(16))) float2 tab[G::TAB_N];
-  __shared__ int spos[kMaxFusedNewRows];
-  unsigned char *const scrb = (unsigned char *)scr;
+  // query operands and the two (cos, sin) tables, then the stage exchange
+  __shared__ __attribute__((aligned(16))) unsigned char arena[ARENA];
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
   const int lane = t % kWave, g4 = lane >> 4, m16 = lane & 15;
+  const bool copier = wave < 2;
+  const int pw = wave - 2;                              // prep wave index (prep waves)
   const int chunk = blockIdx.x / nslot, slot = blockIdx.x % nslot;
   const int b = slot / hkv, kvh = slot % hkv;
-  const int L = lgh & 0xff, Gq = (lgh >> 8) & 0xff, Hq = lgh >> 16;
+  const int L = lgh & 0xff, Gq = (lgh >> 8) & 0xff, half = lgh >> 16, Hq = Gq * hkv;
   const int R = L * Gq;
 
-  // ------------------------------------------------------------ round trip 1: everything small
+  // ------------------------------------------------------------ round trip 1
   const int n = seq_lens[b];
   const int64_t off = seq_offset[b];
-  RawE<E> qraw[RTM];                                    // query half, row 16 rt + 4 wave + g4
-#pragma unroll
-  for (int rt = 0; rt < RTM; ++rt) {
-    const int r = min(16 * rt + 4 * wave + g4, R - 1);
-    const int l = r / Gq, h = kvh * Gq + r % Gq;
-    qraw[rt].load(q_gate + (((int64_t)b * L + l) * Hq + h) * 2 * D + E * m16);
-  }
-  RawE<E> wqraw;
-  wqraw.load(wq_ptr + E * m16);
-  const int tpos = positions[(int64_t)b * L + min(t, L - 1)];
-  // arguments that live in memory, fetched in the same round trip
-  const int ck = p.chunk_keys, msl = p.max_seq_len, rdim = p.r, pchunks = p.chunks, even = p.even_split;
+  const int ck = p.chunk_keys, msl = p.max_seq_len, pchunks = p.chunks, even = p.even_split;
   const int64_t nrows = p.num_rows;
   const bf16_t *const kc = (const bf16_t *)p.kc;
   const bf16_t *const vc = (const bf16_t *)p.vc;
   const bf16_t *const knew = (const bf16_t *)p.k_new;
-  const double l2t = p.log2_theta;
   const float eps = p.eps, sl2 = p.scale_log2;
-  __builtin_amdgcn_sched_barrier(0);                   // every load above is issued before any wait
-  asm volatile("" ::"s"(n), "s"(off), "s"(ck), "s"(msl), "s"(rdim), "s"(pchunks), "s"(even), "s"(nrows), "s"(kc), "s"(vc),
-               "s"(knew), "s"(l2t), "s"(eps), "s"(sl2));
+  // prep waves: query rows 8 k + 4 pw + g4 of pass k, the norm weight, and the
+  // position of table entries lane + 64 j; none of these addresses waits on an
+  // argument loaded from memory
+  RawE<E> qraw[NPASS], wqraw, knraw[2], vnraw[2], wkraw;
+  constexpr int TJ = TABN / kWave;
+  int tpos[TJ], tpair[TJ];
+  if (!copier) {
 #pragma unroll
-  for (int rt = 0; rt < RTM; ++rt) qraw[rt].land();
-  wqraw.land();
-  asm volatile("" ::"v"(tpos));
+    for (int k = 0; k < NPASS; ++k) {
+      const int r = min(8 * k + 4 * pw + g4, R - 1);
+      const int l = r / Gq, h = kvh * Gq + r % Gq;
+      qraw[k].load(q_gate + (((int64_t)b * L + l) * Hq + h) * 2 * D + E * m16);
+    }
+    wqraw.load(wq_ptr + E * m16);
+    // unconditional, with clamped (in-range) indices, so that every load is in
+    // flight at once; entries past L * r/2 are not used
+    const int hh = max(half, 1);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int e = lane + kWave * j, q = e / hh;
+      tpos[j] = positions[(int64_t)b * L + min(q, L - 1)];
+      tpair[j] = e - q * hh;
+    }
+    __builtin_amdgcn_sched_barrier(0);                 // every load above is issued before any wait
+  }
 
   const int64_t total = (int64_t)n + L;
   const bool in_range = n >= 0 && off >= 0 && total <= msl && off + total <= nrows;
-  // capacity only guards the writes at the end; its load is issued now so that
-  // its round trip overlaps the stages
-  const int32_t *const capp = p.capacity;
-  const int cap = capp ? capp[b] : 0x7fffffff;
   const int64_t kend = total;
   const int nch = tile_chunk_count(kend, even, pchunks, ck);
   if (chunk >= nch) return;
@@ -182,96 +207,145 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   // ------------------------------------------------------------ ring fill
   const unsigned kring_lds = (unsigned)(uintptr_t)(lds_void *)kring;
   const unsigned vring_lds = (unsigned)(uintptr_t)(lds_void *)vring;
-  // This thread's copies of a stage: key row u / OCT of the stage, and the
-  // 16-byte unit that the swizzle puts at LDS position u % OCT of that row; the
-  // source is addressed from the stage's first key (wave-uniform, in SGPRs)
-  // plus a 32-bit lane offset shared by K and V.
+  // A copy of unit u of a stage: key row u / OCT of the stage, and the 16-byte
+  // unit that the swizzle puts at LDS position u % OCT of that row; the source
+  // is addressed from the stage's first key (wave-uniform, in SGPRs) plus a
+  // 32-bit lane offset shared by K and V.
   const unsigned rowb = (unsigned)(hkv * D * 2);       // bytes between consecutive keys of one KV head
-  auto issue_half = [&](int st, bool is_k) {   // K or V of keys k0 + 64 st .. into ring slot st % NS
-    const int64_t sk0 = k0 + (int64_t)G::SK * st;
-    const int last = (int)min<int64_t>(G::SK - 1, cend - 1 - sk0);   // keys past the chunk repeat its last key
-    const bf16_t *base = (is_k ? kc : vc) + ((off + sk0) * hkv + kvh) * D;
-    const unsigned ring_lds = is_k ? kring_lds : vring_lds;
-#pragma unroll
-    for (int i = 0; i < LPS; ++i) {
-      const int u = t + kThreads * i;
-      const int key = u / G::OCT, pos = u % G::OCT, oct = pos ^ (key & G::SW);
-      const unsigned voff = (unsigned)min(key, last) * rowb + 16u * (unsigned)oct;
-      dma16_sbase(base, voff, ring_lds + (st % NS) * G::STAGE + kThreads * 16 * i + wave * 1024);
-    }
+  // ub: the wave's first unit (wave-uniform); the lane copies unit ub + lane
+  auto copy_unit = [&](const bf16_t *base, unsigned ring_lds, int st, int ub, int last) {
+    const int u = ub + lane;
+    const int key = u / G::OCT, pos = u % G::OCT, oct = pos ^ (key & G::SW);
+    const unsigned voff = (unsigned)min(key, last) * rowb + 16u * (unsigned)oct;
+    dma16_sbase(base, voff, ring_lds + (st % NS) * G::STAGE + 16 * ub);
   };
-  auto issue_stage = [&](int st) {   // K and V of keys k0 + 64 st .. into ring slot st % NS, interleaved
-    const int64_t sk0 = k0 + (int64_t)G::SK * st;
-    const int last = (int)min<int64_t>(G::SK - 1, cend - 1 - sk0);
-    const int64_t row = ((off + sk0) * hkv + kvh) * D;
-    const bf16_t *kb = kc + row, *vb = vc + row;
-#pragma unroll
-    for (int i = 0; i < LPS; ++i) {
-      const int u = t + kThreads * i;
-      const int key = u / G::OCT, pos = u % G::OCT, oct = pos ^ (key & G::SW);
-      const unsigned voff = (unsigned)min(key, last) * rowb + 16u * (unsigned)oct;
-      const unsigned dst = (st % NS) * G::STAGE + kThreads * 16 * i + wave * 1024;
-      dma16_sbase(kb, voff, kring_lds + dst);
-      dma16_sbase(vb, voff, vring_lds + dst);
-    }
+  auto stage_src = [&](int st, bool is_k) {
+    return (is_k ? kc : vc) + ((off + k0 + (int64_t)G::SK * st) * hkv + kvh) * D;
   };
-  // Whichever way a stage is issued, its 2 LPS copies stay contiguous in issue
-  // order, so a stage is complete once at most 2 LPS copies per younger stage remain.
+  auto stage_last = [&](int st) {   // keys past the chunk repeat its last key
+    return (int)min<int64_t>(G::SK - 1, cend - 1 - (k0 + (int64_t)G::SK * st));
+  };
+  // refills: K or V of stage st, 2 LPS units per thread over all four waves
+  auto issue_half = [&](int st, bool is_k) {
+    const int last = stage_last(st);
+    const bf16_t *base = stage_src(st, is_k);
 #pragma unroll
-  for (int st = 0; st < NS; ++st)
-    if (st < nst) issue_stage(st);
-
-  // new keys and values (tail workgroup): consumed only after the key stages
-  RawE<E> knraw, vnraw, wkraw;
-  if (tail) {
-    const int l = min(4 * wave + g4, L - 1);
-    const int64_t src = (((int64_t)b * L + l) * hkv + kvh) * D + E * m16;
-    knraw.load(knew + src);
-    vnraw.load((const bf16_t *)p.v_new + src);
-    wkraw.load((const bf16_t *)p.wk + E * m16);
+    for (int i = 0; i < LPS; ++i) copy_unit(base, is_k ? kring_lds : vring_lds, st, kWave * wave + kThreads * i, last);
+  };
+  // The first stages.  The copy waves issue every K half, and the V half of
+  // stage 0 when more stages follow; the prep waves issue the other V halves
+  // (the only stage's, or those of stages 1 ..).  Each wave issues in stage
+  // order, 2 LPS copies per thread for every stage after the first, so the
+  // copies younger than a stage are 2 LPS per thread per later stage in both roles.
+  auto issue_first_half = [&](int st, bool is_k, int w2) {
+    const int last = stage_last(st);
+    const bf16_t *base = stage_src(st, is_k);
+#pragma unroll
+    for (int i = 0; i < 2 * LPS; ++i)
+      copy_unit(base, is_k ? kring_lds : vring_lds, st, kWave * w2 + (kThreads / 2) * i, last);
+  };
+  const bool v0_by_copiers = nst > 1;
+  if (copier) {
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      if (st < nst) {
+        issue_first_half(st, true, wave);
+        if (st == 0 && v0_by_copiers) issue_first_half(0, false, wave);
+      }
+    }
   }
 
-  // ------------------------------------------------------------ rotation table
-  // L * r/2 <= TAB_N is a condition of this route
-  const int half = rdim / 2;
-  if (t < L) spos[t] = tpos;
-  lds_barrier();
-  for (int e = t; e < L * half; e += kThreads) {
-    // theta^(-2i/r) = exp2(-(2i/r) log2 theta)
-    const double inv = exp2(-2.0 * (double)(e % half) / (double)rdim * l2t);
-    float c, s;
-    rope_angle_cs(spos[e / half], inv, c, s);
-    tab[e] = make_float2(c, s);
+  // capacity only guards the writes at the end; its pointer comes from the
+  // argument segment, so it is loaded behind the copies
+  const int32_t *const capp = p.capacity;
+  const int cap = capp ? capp[b] : 0x7fffffff;
+
+  // ------------------------------------------------------------ prep waves
+  float2 *const tabw = (float2 *)(arena + QBYTES) + (copier ? 0 : pw) * TABN;
+  float kx[2][E];                                       // new key rows 8 k + 4 pw + g4 (prep waves)
+  if (!copier) {
+    // every load of this wave lands before its copies are issued
+#pragma unroll
+    for (int k = 0; k < NPASS; ++k) qraw[k].land();
+    wqraw.land();
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) asm volatile("" ::"v"(tpos[j]));
+    // the only stage's V is needed soon: issue it before the preparation; V
+    // halves of later stages are issued after it
+    if (!v0_by_copiers && nst > 0) issue_first_half(0, false, pw);
+    // this wave's (cos, sin) table: entry l * r/2 + i for new row l, pair i,
+    // with the frequency theta^(-2i/r) = step^i by binary powers of the host's
+    // step theta^(-2/r) in double (a handful of roundings, ~1e-15 relative)
+    const double step = p.rope_step;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int e = lane + kWave * j;
+      if (kWave * j < L * half) {
+        double f = 1.0, sq = step;
+#pragma unroll
+        for (int bit = 0; bit < 7; ++bit) {             // pairs < kMaxPairs = 2^7
+          f = (tpair[j] >> bit) & 1 ? f * sq : f;
+          sq *= sq;
+        }
+        float c, sn;
+        rope_angle_cs(tpos[j], f, c, sn);
+        if (e < L * half) tabw[e] = make_float2(c, sn);
+      }
+    }
+    wave_lds_sync();
+    // new key and value rows 8 k + 4 pw + g4 of the tail workgroup.  Their
+    // pointers come from the argument segment; they queue behind this wave's
+    // copies and are waited for only by the key preparation below.
+    if (tail) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int l = min(8 * k + 4 * pw + g4, L - 1);
+        const int64_t src = (((int64_t)b * L + l) * hkv + kvh) * D + E * m16;
+        knraw[k].load(knew + src);
+        vnraw[k].load((const bf16_t *)p.v_new + src);
+      }
+      wkraw.load((const bf16_t *)p.wk + E * m16);
+    }
+    float wq[E];
+    wqraw.to_float(wq);
+#pragma unroll
+    for (int k = 0; k < NPASS; ++k) {
+      const int r = 8 * k + 4 * pw + g4;
+      float x[E];
+#pragma unroll
+      for (int j = 0; j < E; ++j) x[j] = 0.f;           // rows >= R are zero
+      if (8 * k + 4 * pw < R) {
+        qraw[k].to_float(x);
+        norm_rope<D>(x, wq, r < R, eps, 2 * half, tabw + (min(r, R - 1) / Gq) * half);
+      }
+      put_row_bf16<D>(arena, RB, r, E * m16, x);
+    }
+    if (tail) {
+      float wk[E];
+      wkraw.to_float(wk);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int l = 8 * k + 4 * pw + g4;
+        knraw[k].to_float(kx[k]);
+        norm_rope<D>(kx[k], wk, l < L, eps, 2 * half, tabw + min(l, L - 1) * half);   // rows >= L become zero
+      }
+    }
+#pragma unroll
+    for (int st = 1; st < NS; ++st)
+      if (st < nst) issue_first_half(st, false, pw);
   }
-  lds_barrier();
+  lds_barrier();                                        // query operands ready; first stages issued
 
   // ------------------------------------------------------------ query rows -> MFMA operands
-  float wq[E];
-  wqraw.to_float(wq);
   bf16x8 qf[RTM][KST];
-  int64_t lim[RTM];
 #pragma unroll
-  for (int rt = 0; rt < RTM; ++rt) lim[rt] = (int64_t)n + (16 * rt + m16) / Gq;
-  const int srow = 4 * wave + g4;                       // scratch row of this lane group
-  auto prep_pass = [&](const int rt, const RawE<E> &raw) {
-    const int r = 16 * rt + srow;
-    const bool valid = r < R;
-    const int l = min(r, R - 1) / Gq;
-    float x[E];
-    raw.to_float(x);
-    norm_rope<D>(x, wq, valid, eps, rdim, tab + l * half, scr + srow * D);
-    wave_lds_sync();
-    // bf16 copy of the row into its own scratch row (stride 4D bytes, swizzled units)
-    put_row_bf16<D>(scrb, 4 * D, srow, E * m16, x);
-    lds_barrier();
+  for (int rt = 0; rt < RTM; ++rt)
 #pragma unroll
-    for (int ks = 0; ks < KST; ++ks) qf[rt][ks] = *(const bf16x8 *)(scrb + swz<G::SW>(m16, 4 * ks + g4, 4 * D));
-    lds_barrier();
-  };
-  prep_pass(0, qraw[0]);
-  if constexpr (RTM > 1) prep_pass(1, qraw[1]);
-  if constexpr (RTM > 2) prep_pass(2, qraw[2]);
-  if constexpr (RTM > 3) prep_pass(3, qraw[3]);
+    for (int ks = 0; ks < KST; ++ks) qf[rt][ks] = *(const bf16x8 *)(arena + swz<G::SW>(16 * rt + m16, 4 * ks + g4, RB));
+  // key positions and causal limits fit in 32 bits: n + L <= max_seq_len <= 2^30
+  int lim[RTM];
+#pragma unroll
+  for (int rt = 0; rt < RTM; ++rt) lim[rt] = n + (16 * rt + m16) / Gq;
 
   // ------------------------------------------------------------ key stages
   f32x4 O[RTM][DBW];
@@ -284,13 +358,16 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     for (int db = 0; db < DBW; ++db) O[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   for (int st = 0; st < nst; ++st) {
-    wait_stages<2 * LPS, NS>(min(NS - 1, nst - 1 - st));
+    // copies younger than stage st that this wave issued: 2 LPS per thread for
+    // each later stage of the first fill (its K or V half) and each refill
+    const int ys = min(NS - 1, nst - 1 - st);
+    WaitUnits<LPS, 2 * (NS - 1)>::run(2 * ys);
     lds_barrier();
     const int so = (st % NS) * G::STAGE;
-    const int64_t sk0 = k0 + (int64_t)G::SK * st;
-    const int nk = (int)min<int64_t>(G::SK, cend - sk0);
+    const int sk0 = (int)k0 + G::SK * st;
+    const int nk = min(G::SK, (int)cend - sk0);
     // the K half of the slot is refilled as soon as the scores are done, the V half after the stage
-    attend_stage<D, RTM>(kring + so, vring + so, nk, sk0, qf, O, mrun, lrun, lim, sl2, scrb, [&]() {
+    attend_stage<D, RTM>(kring + so, vring + so, nk, sk0, qf, O, mrun, lrun, lim, sl2, arena, [&]() {
       if (st + NS < nst) issue_half(st + NS, true);
     });
     lds_barrier();                                      // every wave is done with ring slot st % NS
@@ -299,28 +376,31 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
 
   // ------------------------------------------------------------ new keys (tail workgroup)
   // The new rows become one more stage in ring slot 0: K and V rows 0 .. 15
-  // (rows >= L zero) and V rows 16 .. 31 zero (read by the value product).
-  // The fp32 scratch of their norm sits in the K ring past slot 0.
+  // (rows >= L zero) from the prep waves, V rows 16 .. 31 zero (read by the
+  // value product) from the copy waves.
   if (tail) {
-    float wk[E], x[E], v[E];
-    wkraw.to_float(wk);
-    knraw.to_float(x);
-    vnraw.to_float(v);
-    const int l = srow;
-    const bool valid = l < L;
-    norm_rope<D>(x, wk, valid, eps, rdim, tab + min(l, L - 1) * half, (float *)(kring + G::STAGE) + srow * D);
-    if (!valid) {
 #pragma unroll
-      for (int j = 0; j < E; ++j) v[j] = 0.f;
+    for (int k = 0; k < 2; ++k) {
+      float v[E];
+      if (!copier) {
+        const int l = 8 * k + 4 * pw + g4;
+#pragma unroll
+        for (int j = 0; j < E; ++j) v[j] = 0.f;
+        vnraw[k].to_float(v);
+        if (l >= L) {
+#pragma unroll
+          for (int j = 0; j < E; ++j) v[j] = 0.f;
+        }
+        put_row_bf16<D>(kring, RB, l, E * m16, kx[k]);
+        put_row_bf16<D>(vring, RB, l, E * m16, v);      // v_new is bf16 already: exact
+      } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j) v[j] = 0.f;
+        put_row_bf16<D>(vring, RB, 16 + 8 * k + 4 * wave + g4, E * m16, v);
+      }
     }
-    float zero[E];
-#pragma unroll
-    for (int j = 0; j < E; ++j) zero[j] = 0.f;
-    put_row_bf16<D>(kring, RB, l, E * m16, x);
-    put_row_bf16<D>(vring, RB, l, E * m16, v);          // v_new is bf16 already: exact
-    put_row_bf16<D>(vring, RB, 16 + l, E * m16, zero);
     lds_barrier();
-    attend_stage<D, RTM>(kring, vring, L, (int64_t)n, qf, O, mrun, lrun, lim, sl2, scrb);
+    attend_stage<D, RTM>(kring, vring, L, n, qf, O, mrun, lrun, lim, sl2, arena);
   }
 
   // ------------------------------------------------------------ outputs
@@ -392,7 +472,7 @@ template <int D, int RTM>
 static void launch_stream_rt(const Params &p, hipStream_t s, const Timing &tm) {
   const int nslot = p.B * p.Hkv;
   const int64_t blocks = (int64_t)nslot * p.chunks;
-  const int lgh = p.L | (p.G << 8) | (p.Hq << 16);
+  const int lgh = p.L | (p.G << 8) | ((p.r / 2) << 16);
   launch_kernel(stream_kernel<D, RTM>, blocks, s, tm, p.seq_lens, p.seq_offset, (const bf16_t *)p.q_gate,
                 (const bf16_t *)p.wq, p.positions, nslot, p.Hkv, lgh, p);
 }
@@ -403,7 +483,6 @@ static hipError_t launch_stream_d(const Params &p, hipStream_t s, const Timing &
     case 1: launch_stream_rt<D, 1>(p, s, tm); break;
     case 2: launch_stream_rt<D, 2>(p, s, tm); break;
     case 3: launch_stream_rt<D, 3>(p, s, tm); break;
-    case 4: launch_stream_rt<D, 4>(p, s, tm); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
