@@ -244,7 +244,28 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     for (int i = 0; i < 2 * LPS; ++i)
       copy_unit(base, is_k ? kring_lds : vring_lds, st, kWave * w2 + (kThreads / 2) * i, last);
   };
-  const bool v0_by_copiers = nst > 1;
+  // The new keys become one more stage.  When the cached stages leave a ring
+  // slot unused, the new keys take it and are attended first, while the cached
+  // stages are still in flight; otherwise they follow the cached stages in slot 0.
+  const bool early_new = tail && nst < NS;
+  const int new_slot = (early_new ? nst : 0) * G::STAGE;
+  const bool v0_by_copiers = nst > 1 || early_new;
+  // New key and value rows 8 k + 4 pw + g4 of the tail workgroup (prep waves).
+  // Their pointers come from the argument segment, so they are a second round
+  // trip; they are issued before any copy of the workgroup (the barrier below),
+  // since a load behind the copies in the CU's memory pipeline lands only after
+  // them.  No copy of the prep waves precedes their consumer, the key preparation.
+  if (!copier && tail) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int l = min(8 * k + 4 * pw + g4, L - 1);
+      const int64_t src = (((int64_t)b * L + l) * hkv + kvh) * D + E * m16;
+      knraw[k].load(knew + src);
+      vnraw[k].load((const bf16_t *)p.v_new + src);
+    }
+    wkraw.load((const bf16_t *)p.wk + E * m16);
+  }
+  lds_barrier();
   if (copier) {
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
@@ -263,6 +284,25 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   // ------------------------------------------------------------ prep waves
   float2 *const tabw = (float2 *)(arena + QBYTES) + (copier ? 0 : pw) * TABN;
   float kx[2][E];                                       // new key rows 8 k + 4 pw + g4 (prep waves)
+  // The new-key stage, written by the prep waves into ring slot new_slot: K and
+  // V rows 0 .. 15 (rows >= L zero) and V rows 16 .. 31 zero (read by the value
+  // product).
+  auto put_new_rows = [&]() {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int l = 8 * k + 4 * pw + g4;
+      float v[E], zero[E];
+      vnraw[k].to_float(v);
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        zero[j] = 0.f;
+        if (l >= L) v[j] = 0.f;
+      }
+      put_row_bf16<D>(kring + new_slot, RB, l, E * m16, kx[k]);
+      put_row_bf16<D>(vring + new_slot, RB, l, E * m16, v);   // v_new is bf16 already: exact
+      put_row_bf16<D>(vring + new_slot, RB, 16 + l, E * m16, zero);
+    }
+  };
   if (!copier) {
     // every load of this wave lands before its copies are issued
 #pragma unroll
@@ -293,19 +333,6 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
       }
     }
     wave_lds_sync();
-    // new key and value rows 8 k + 4 pw + g4 of the tail workgroup.  Their
-    // pointers come from the argument segment; they queue behind this wave's
-    // copies and are waited for only by the key preparation below.
-    if (tail) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int l = min(8 * k + 4 * pw + g4, L - 1);
-        const int64_t src = (((int64_t)b * L + l) * hkv + kvh) * D + E * m16;
-        knraw[k].load(knew + src);
-        vnraw[k].load((const bf16_t *)p.v_new + src);
-      }
-      wkraw.load((const bf16_t *)p.wk + E * m16);
-    }
     float wq[E];
     wqraw.to_float(wq);
 #pragma unroll
@@ -330,6 +357,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
         norm_rope<D>(kx[k], wk, l < L, eps, 2 * half, tabw + min(l, L - 1) * half);   // rows >= L become zero
       }
     }
+    if (early_new) put_new_rows();
 #pragma unroll
     for (int st = 1; st < NS; ++st)
       if (st < nst) issue_first_half(st, false, pw);
@@ -357,6 +385,10 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
 #pragma unroll
     for (int db = 0; db < DBW; ++db) O[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  if (early_new) {
+    lds_barrier();                                      // every wave has its query operands (the exchange reuses them)
+    attend_stage<D, RTM>(kring + new_slot, vring + new_slot, L, n, qf, O, mrun, lrun, lim, sl2, arena);
+  }
   for (int st = 0; st < nst; ++st) {
     // copies younger than stage st that this wave issued: 2 LPS per thread for
     // each later stage of the first fill (its K or V half) and each refill
@@ -378,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   // The new rows become one more stage in ring slot 0: K and V rows 0 .. 15
   // (rows >= L zero) from the prep waves, V rows 16 .. 31 zero (read by the
   // value product) from the copy waves.
-  if (tail) {
+  if (tail && !early_new) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       float v[E];
@@ -461,8 +493,8 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
       const int l = u / G::OCT, oct = u % G::OCT;
       if (l < L) {
         const int64_t dst = ((off + n + l) * hkv + kvh) * D + 8 * oct;
-        *(uint4 *)((bf16_t *)p.kc + dst) = *(const uint4 *)(kring + swz<G::SW>(l, oct, RB));
-        *(uint4 *)((bf16_t *)p.vc + dst) = *(const uint4 *)(vring + swz<G::SW>(l, oct, RB));
+        *(uint4 *)((bf16_t *)p.kc + dst) = *(const uint4 *)(kring + new_slot + swz<G::SW>(l, oct, RB));
+        *(uint4 *)((bf16_t *)p.vc + dst) = *(const uint4 *)(vring + new_slot + swz<G::SW>(l, oct, RB));
       }
     }
   }
