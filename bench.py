@@ -117,7 +117,9 @@ class Call:
 
 def kernel_times(calls, stream, n):
     """Average duration (ms) of the attention kernel over n eager calls, from HIP
-    events the library records on the launch stream right around that kernel."""
+    events the library records on the launch stream right around that kernel.
+    The stream drains before each call, so a dispatch's begin stamp is not
+    taken while it waits for the previous call's kernels."""
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(n)]
     with torch.cuda.stream(stream):
@@ -129,6 +131,7 @@ def kernel_times(calls, stream, n):
         for i, (a, b) in enumerate(pairs):
             c = calls[i % len(calls)]
             c.cfg.timing_begin, c.cfg.timing_end = a.cuda_event, b.cuda_event
+            stream.synchronize()
             c()
     torch.cuda.synchronize()
     for c in calls:

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqsa.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["qsa_api.hip", "qsa_rows.hip", "qsa_stream.hip", "qsa_prefill.hip", "qsa_merge.hip"]
-# per-source extra flags: the streaming and tile kernels take their leading
+# per-source extra flags: the streaming, tile and merge kernels take their leading
 # argument dwords (metadata and query pointers, grid shape) preloaded into
 # SGPRs; their LDS copies set M0 from inline assembly, hence -Wno-inline-asm
 # (nothing else in those files uses M0).  The short-query kernel keeps its MFMA
@@ -28,7 +28,8 @@ SOURCES = ["qsa_api.hip", "qsa_rows.hip", "qsa_stream.hip", "qsa_prefill.hip", "
 # register per key stage.
 EXTRA = {"qsa_stream.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=13", "-mllvm", "-amdgpu-mfma-vgpr-form",
                            "-Wno-inline-asm"],
-         "qsa_prefill.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=11", "-Wno-inline-asm"]}
+         "qsa_prefill.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=11", "-Wno-inline-asm"],
+         "qsa_merge.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=12"]}
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -13,42 +13,54 @@ namespace qsa {
 
 // Merge the key chunks of one (slot, row): weights 2^(m_c - M) / sum_c l_c 2^(m_c - M),
 // weighted sum of the unnormalised chunk outputs, then the sigmoid gate.  For
-// the short-query route, whose rows can have thousands of chunks: one
-// workgroup of D threads per (slot, row), one output dim per lane, so each
-// wavefront merges its 64 dims over every chunk on its own, with no LDS and no
-// barrier.  Chunks go in batches of 64: lane c holds chunk c's statistics, the
-// batch max and sums are wavefront reductions, and each chunk's weight is
-// broadcast from its lane to the whole wavefront.
+// the short-query route (one row tile per sequence and KV head), whose rows can
+// have thousands of chunks: one wavefront per (slot, row, 64-dim slice), one
+// output dim per lane, with no LDS and no barrier; the slices spread the
+// partials' bytes over D/64 times more CUs.  Chunks go in batches of 64: lane c
+// holds chunk c's statistics, the batch max and sums are wavefront reductions,
+// and each chunk's weight is broadcast from its lane to the whole wavefront.
+//
+// The leading arguments are preloaded into SGPRs, so the first batch's loads
+// (taken for the grid's chunk count, before the sequence length is known) and
+// the length itself form one round trip.  A sequence out of range has NaN
+// statistics in chunk 0 (written by the attention kernel), so its merged rows
+// are NaN.  lg packs L (bits 0-15) and G (bits 16-31).
 template <int D>
-__global__ __launch_bounds__(D) void combine_kernel(Params p) {
-  const int d = threadIdx.x, lane = d % kWave;
-  const int rr = blockIdx.x % p.rows;
-  const int slot = blockIdx.x / p.rows;
-  const int tile = slot % p.tiles;
-  const int kvh = (slot / p.tiles) % p.Hkv;
-  const int b = slot / (p.tiles * p.Hkv);
-  const int rows_total = p.L * p.G;
-  const int row0 = tile * p.rows;                      // rows per tile
-  const int R = min(p.rows, rows_total - row0);
-  if (rr >= R) return;
-  const int n = gld<int>(p.seq_lens + b);
-  int64_t off;
-  if (!seq_in_range(p, b, n, off)) return;              // the attention kernel wrote NaN
-  const int lmax = (row0 + R - 1) / p.G;
-  const int nch = tile_chunk_count((int64_t)n + lmax + 1, p.even_split, p.chunks, p.chunk_keys);
-  if (nch == 1) return;                                 // finished by the attention kernel
+__global__ __launch_bounds__(kWave) void combine_kernel(const int32_t *__restrict__ seq_lens,
+                                                    const float *__restrict__ part_ml,
+                                                    const float *__restrict__ part_o,
+                                                    const bf16_t *__restrict__ q_gate, int rows, int chunks,
+                                                    int hkv, int lg, Params p) {
+  constexpr int NSL = D / kWave;                        // 64-dim slices per row
+  const int lane = threadIdx.x, d = kWave * (blockIdx.x % NSL) + lane;
+  const int L = lg & 0xffff, G = lg >> 16, Hq = G * hkv;
+  const int rr = (blockIdx.x / NSL) % rows;
+  const int slot = blockIdx.x / NSL / rows;
+  const int kvh = slot % hkv, b = slot / hkv;
+  const int l = rr / G, h = kvh * G + rr % G;
+  if (rr >= L * G) return;
+  const int64_t base = (int64_t)slot * chunks * rows + rr;   // + c * rows
+  const int n = seq_lens[b];
+  const float z = (float)gld<bf16_t>(q_gate + (((int64_t)b * L + l) * Hq + h) * 2 * D + D + d);
+  float2 ml = gld<float2>(part_ml + (base + (int64_t)min(lane, chunks - 1) * rows) * 2);
+  float v[kWave];
+#pragma unroll
+  for (int k = 0; k < kWave; ++k) {
+    v[k] = 0.f;
+    if (k < chunks) v[k] = gld<float>(part_o + (base + (int64_t)k * rows) * D + d);
+  }
+  __builtin_amdgcn_sched_barrier(0);                   // every load above is issued before any wait
 
-  const int64_t base = (int64_t)slot * p.chunks * p.rows + rr;   // + c * rows
-  const int rg = row0 + rr, l = rg / p.G, h = kvh * p.G + rg % p.G;
-  const float z = (float)gld<bf16_t>((const bf16_t *)p.q_gate + (((int64_t)b * p.L + l) * p.Hq + h) * 2 * D + D + d);
+  // chunks of this sequence (the grid's count at most, whatever the length says)
+  const int nch = min(chunks, tile_chunk_count((int64_t)n + (L * G - 1) / G + 1, p.even_split, chunks, p.chunk_keys));
+  if (nch == 1) return;                                 // finished by the attention kernel
   float M = -INFINITY, lsum = 0.f, acc = 0.f;
   for (int c0 = 0; c0 < nch; c0 += kWave) {
-    // every load of the batch first: this lane's chunk statistics, then the 64 chunk outputs of dim d
-    const int cl = min(c0 + lane, nch - 1);
-    const float2 ml = gld<float2>(p.part_ml + (base + (int64_t)cl * p.rows) * 2);
-    float v[kWave];
+    if (c0 > 0) {
+      ml = gld<float2>(part_ml + (base + (int64_t)min(c0 + lane, nch - 1) * rows) * 2);
 #pragma unroll
-    for (int k = 0; k < kWave; ++k) v[k] = gld<float>(p.part_o + (base + (int64_t)min(c0 + k, nch - 1) * p.rows) * D + d);
+      for (int k = 0; k < kWave; ++k) v[k] = gld<float>(part_o + (base + (int64_t)min(c0 + k, nch - 1) * rows) * D + d);
+    }
     const bool own = c0 + lane < nch;
     const float mc = own ? ml.x : -INFINITY;
     const float Mn = fmaxf(M, rows4_max(row16_max(mc)));
@@ -61,7 +73,7 @@ __global__ __launch_bounds__(D) void combine_kernel(Params p) {
     for (int k = 0; k < kWave; ++k) acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wc), k)) * v[k];
     M = Mn;
   }
-  ((bf16_t *)p.out)[(((int64_t)b * p.L + l) * p.Hq + h) * D + d] = (bf16_t)(acc / lsum * sigmoid_f(z));
+  ((bf16_t *)p.out)[(((int64_t)b * L + l) * Hq + h) * D + d] = (bf16_t)(acc / lsum * sigmoid_f(z));
 }
 
 // Merge for the tile route, whose rows have few key chunks each: one wavefront
@@ -139,11 +151,22 @@ hipError_t launch_combine_bf16(const Params &p, hipStream_t s, bool per_row) {
     }
     return hipGetLastError();
   }
-  const int64_t blocks = (int64_t)p.B * p.Hkv * p.tiles * p.rows;
+  const int64_t blocks = (int64_t)p.B * p.Hkv * p.tiles * p.rows * (p.D / kWave);   // tiles == 1 on this route
+  const int lg = p.L | (p.G << 16);
+  const bf16_t *qg = (const bf16_t *)p.q_gate;
   switch (p.D) {
-    case 64: hipLaunchKernelGGL((combine_kernel<64>), dim3(blocks), dim3(64), 0, s, p); break;
-    case 128: hipLaunchKernelGGL((combine_kernel<128>), dim3(blocks), dim3(128), 0, s, p); break;
-    case 256: hipLaunchKernelGGL((combine_kernel<256>), dim3(blocks), dim3(256), 0, s, p); break;
+    case 64:
+      hipLaunchKernelGGL((combine_kernel<64>), dim3(blocks), dim3(kWave), 0, s, p.seq_lens, p.part_ml, p.part_o, qg,
+                         p.rows, p.chunks, p.Hkv, lg, p);
+      break;
+    case 128:
+      hipLaunchKernelGGL((combine_kernel<128>), dim3(blocks), dim3(kWave), 0, s, p.seq_lens, p.part_ml, p.part_o, qg,
+                         p.rows, p.chunks, p.Hkv, lg, p);
+      break;
+    case 256:
+      hipLaunchKernelGGL((combine_kernel<256>), dim3(blocks), dim3(kWave), 0, s, p.seq_lens, p.part_ml, p.part_o, qg,
+                         p.rows, p.chunks, p.Hkv, lg, p);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

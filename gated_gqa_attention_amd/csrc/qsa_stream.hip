@@ -188,11 +188,16 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   const int nch = tile_chunk_count(kend, even, pchunks, ck);
   if (chunk >= nch) return;
   if (!in_range) {
+    // NaN outputs, and NaN chunk statistics for the merge kernel, which then
+    // writes NaN too; no append; error bit set
     if (chunk == 0) {
       for (int e = t; e < R * D; e += kThreads) {
         const int r = e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
         ((bf16_t *)p.out)[(((int64_t)b * L + l) * Hq + h) * D + d] = (bf16_t)__builtin_nanf("");
       }
+      if (p.part_ml && t < R)
+        *(float2 *)(p.part_ml + ((int64_t)slot * pchunks * p.rows + t) * 2) =
+            make_float2(__builtin_nanf(""), __builtin_nanf(""));
       if (t == 0) flag_error(p);
     }
     return;
@@ -474,13 +479,15 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   }
   if (!cap_ok) {
     // the sequence's rows would pass its capacity: NaN outputs (written above when
-    // the chunk is the whole sequence), no partials, no append, error bit set
+    // the chunk is the whole sequence), NaN chunk statistics in place of the
+    // partials (so the merge kernel writes NaN too), no append, error bit set
     if (chunk == 0) {
       if (!single) {
         for (int e = t; e < R * D; e += kThreads) {
           const int r = e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
           ((bf16_t *)p.out)[(((int64_t)b * L + l) * Hq + h) * D + d] = (bf16_t)__builtin_nanf("");
         }
+        if (t < R) *(float2 *)(p.part_ml + (slot_rows + t) * 2) = make_float2(__builtin_nanf(""), __builtin_nanf(""));
       }
       if (t == 0) flag_error(p);
     }
