@@ -55,6 +55,25 @@ def test_route_per_workload(name, route):
     assert int(fields["workspace"]) == binding.workspace_size(cfg_for(WORKLOADS[name]))
 
 
+@pytest.mark.parametrize("geo,route", [
+    (dict(head_dim=256, rotary_dim=64, q_len=1, num_q_heads=16, num_kv_heads=4), "fused_splitk"),
+    (dict(head_dim=256, rotary_dim=32, q_len=4, num_q_heads=24, num_kv_heads=2), "fused_splitk"),   # 48 rows
+    (dict(head_dim=64, rotary_dim=8, q_len=3, num_q_heads=8, num_kv_heads=2), "fused_splitk"),
+    (dict(head_dim=128, rotary_dim=0, q_len=16, num_q_heads=3, num_kv_heads=1), "fused_splitk"),
+    (dict(head_dim=256, rotary_dim=16, q_len=1, num_q_heads=16, num_kv_heads=4), "prepared_tiles"),  # r/2 % 16
+    (dict(head_dim=128, rotary_dim=24, q_len=1, num_q_heads=4, num_kv_heads=1), "prepared_tiles"),   # r/2 % 8
+    (dict(head_dim=256, rotary_dim=64, q_len=7, num_q_heads=7, num_kv_heads=1), "prepared_tiles"),   # 49 rows
+    (dict(head_dim=256, rotary_dim=128, q_len=16, num_q_heads=2, num_kv_heads=1), "prepared_tiles"),  # L r/2 = 1024
+    (dict(head_dim=256, rotary_dim=64, q_len=17, num_q_heads=1, num_kv_heads=1), "prepared_tiles"),   # L > 16
+])
+def test_short_query_route_limits(geo, route):
+    """The short-query kernel takes at most 48 query rows and 16 new rows per
+    sequence, tabulates at most 512 (cos, sin) pairs, and rotates by whole
+    lanes (r/2 a multiple of head_dim/16); anything else takes the tile route."""
+    w = Workload("limits", batch=2, rope_theta=1e7, dtype="bf16", prior=100, seed=1, **geo)
+    assert f"route={route}" in binding.describe_plan(cfg_for(w))
+
+
 def test_plan_covers_max_seq_len_and_forced_splits():
     w = WORKLOADS["decode_4b"]
     for k in (1, 2, 7, 65):

@@ -99,6 +99,16 @@ SMALL = [
     # tile route at head_dim 128: 280 rows = three tiles
     Workload("bf16_prefill_d128_tiles", batch=1, q_len=70, num_q_heads=8, num_kv_heads=2, head_dim=128,
              rotary_dim=64, rope_theta=1e6, dtype="bf16", prior=200, seed=114),
+    # short-query route, smallest rotation by whole lanes: r/2 = D/16 at head_dim 64 and 128
+    Workload("bf16_d64_r8", batch=2, q_len=3, num_q_heads=8, num_kv_heads=2, head_dim=64,
+             rotary_dim=8, rope_theta=1e4, dtype="bf16", prior=90, seed=118),
+    Workload("bf16_d128_r16_rows48", batch=2, q_len=4, num_q_heads=12, num_kv_heads=1, head_dim=128,
+             rotary_dim=16, rope_theta=1e6, dtype="bf16", prior=150, seed=119),
+    # decode shapes outside the short-query route: r/2 not a multiple of D/16, and 49 rows
+    Workload("bf16_decode_r16_prepared", batch=2, q_len=1, num_q_heads=16, num_kv_heads=4, head_dim=256,
+             rotary_dim=16, rope_theta=1e7, dtype="bf16", prior=200, seed=120),
+    Workload("bf16_rows49_prepared", batch=1, q_len=7, num_q_heads=7, num_kv_heads=1, head_dim=256,
+             rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=60, seed=121),
 ]
 
 
