@@ -140,6 +140,23 @@ struct RawE {
       asm volatile("" ::"v"(r));
     }
   }
+  // Byte offset of piece i (elements [e0 + 8 i, ..) for E >= 8, or the half
+  // unit holding [e0, e0 + 4) for E == 4) in a tile of rb-byte rows whose
+  // 16-byte units are XOR-swizzled by the row (the layout of put_row_bf16).
+  template <int SW>
+  __device__ __forceinline__ static int lds_off(int rb, int row, int e0, int i) {
+    return E >= 8 ? row * rb + 16 * ((e0 / 8 + i) ^ (row & SW)) : row * rb + 16 * ((e0 / 8) ^ (row & SW)) + 8 * ((e0 / 4) & 1);
+  }
+  template <int SW>
+  __device__ __forceinline__ void store_lds(unsigned char *tile, int rb, int row, int e0) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) *(V *)(tile + lds_off<SW>(rb, row, e0, i)) = v[i];
+  }
+  template <int SW>
+  __device__ __forceinline__ void load_lds(const unsigned char *tile, int rb, int row, int e0) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = *(const V *)(tile + lds_off<SW>(rb, row, e0, i));
+  }
   __device__ __forceinline__ void to_float(float *x) const {
     constexpr int PER = E >= 8 ? 8 : 4;
     typedef __bf16 bfP __attribute__((ext_vector_type(PER)));

@@ -340,14 +340,21 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     wave_lds_sync();
     float wq[E];
     wqraw.to_float(wq);
+    // The raw rows wait in their LDS slots and one loop (not unrolled: its code
+    // stays in the instruction cache from the first pass on) prepares them in place.
 #pragma unroll
+    for (int k = 0; k < NPASS; ++k) qraw[k].template store_lds<G::SW>(arena, RB, 8 * k + 4 * pw + g4, E * m16);
+    const int npass = min(NPASS, (R - 4 * pw + 7) / 8);   // passes with rows < R; later rows are zero
+#pragma unroll 1
     for (int k = 0; k < NPASS; ++k) {
       const int r = 8 * k + 4 * pw + g4;
       float x[E];
 #pragma unroll
       for (int j = 0; j < E; ++j) x[j] = 0.f;           // rows >= R are zero
-      if (8 * k + 4 * pw < R) {
-        qraw[k].to_float(x);
+      if (k < npass) {
+        RawE<E> raw;
+        raw.template load_lds<G::SW>(arena, RB, r, E * m16);
+        raw.to_float(x);
         norm_rope<D>(x, wq, r < R, eps, 2 * half, tabw + (min(r, R - 1) / Gq) * half);
       }
       put_row_bf16<D>(arena, RB, r, E * m16, x);
