@@ -78,13 +78,9 @@ __device__ __forceinline__ float rows4_max(float v) {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// One 16-byte HBM -> LDS copy per lane: lane i writes LDS bytes lds + 16 i.
+// 16-byte HBM -> LDS copies, one per lane: lane i writes LDS bytes lds + 16 i.
 // The LDS address must be uniform over the wave (it goes through M0).
-__device__ __forceinline__ void dma16_asm(const void *src, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
-}
-
-// The same copy from a wave-uniform base address (SGPRs) plus a 32-bit byte
+// The source is a wave-uniform base address (SGPRs) plus a 32-bit byte
 // offset per lane.
 __device__ __forceinline__ void dma16_sbase(const void *base, unsigned voff, unsigned lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");

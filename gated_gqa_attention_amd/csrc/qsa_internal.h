@@ -18,7 +18,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;         // four wavefronts per workgroup
 constexpr int kWave = 64;
 constexpr int kTileKeys = 64;         // shortest key chunk the planner makes (one short-query stage)
-constexpr int kTileRows = 64;         // query rows (group heads x new rows) of a short-query call
+constexpr int kTileRows = 64;         // query rows per tile of the fp32 route
 constexpr int kPrefillRowTiles = 2;  // 16-row MFMA tiles per wavefront of the tile (prefill) kernel
 constexpr int kPrefillThreads = 512;  // eight wavefronts per workgroup of the tile kernel
 constexpr int kPrefillTileRows = 16 * kPrefillRowTiles * kPrefillThreads / kWave;   // query rows per workgroup
@@ -66,7 +66,6 @@ struct Params {
   float *part_ml;
   float *part_o;
   void *qt;
-  double log2_theta;           // log2(theta), computed on the host in double
   double rope_step;            // theta^(-2/r) (r > 0), computed on the host in double
   double inv_freq[kMaxPairs];  // theta^(-2i/r), computed on the host in double
 };
