@@ -112,6 +112,7 @@ template <typename T> struct nat { using type = T; };
 template <> struct nat<uint4> { using type = unsigned __attribute__((ext_vector_type(4))); };
 template <> struct nat<uint2> { using type = unsigned __attribute__((ext_vector_type(2))); };
 template <> struct nat<float2> { using type = float __attribute__((ext_vector_type(2))); };
+template <> struct nat<float4> { using type = float __attribute__((ext_vector_type(4))); };
 template <typename T>
 __device__ __forceinline__ T gld(const void *ptr) {
   using N = typename nat<T>::type;

@@ -14,11 +14,13 @@ namespace qsa {
 // Merge the key chunks of one (slot, row): weights 2^(m_c - M) / sum_c l_c 2^(m_c - M),
 // weighted sum of the unnormalised chunk outputs, then the sigmoid gate.  For
 // the short-query route (one row tile per sequence and KV head), whose rows can
-// have thousands of chunks: one wavefront per (slot, row, 64-dim slice), one
-// output dim per lane, with no LDS and no barrier; the slices spread the
-// partials' bytes over D/64 times more CUs.  Chunks go in batches of 64: lane c
-// holds chunk c's statistics, the batch max and sums are wavefront reductions,
-// and each chunk's weight is broadcast from its lane to the whole wavefront.
+// have thousands of chunks: one wavefront per (slot, row, 64-dim slice), with
+// no LDS and no barrier; the slices spread the partials' bytes over D/64 times
+// more CUs.  Chunks go in batches of 64: lane c holds chunk c's statistics and
+// the batch max and sums are wavefront reductions.  Lane (q, c16) reads 16-byte
+// pieces (dims 4 c16 .. + 3 of the slice) of chunks q, q + 4, ..., so a batch is
+// 16 wide loads per lane; it fetches each of those chunks' weight from the lane
+// holding its statistics, and the four lane groups are summed at the end.
 //
 // The leading arguments are preloaded into SGPRs, so the first batch's loads
 // (taken for the grid's chunk count, before the sequence length is known) and
@@ -32,7 +34,10 @@ __global__ __launch_bounds__(kWave) void combine_kernel(const int32_t *__restric
                                                     const bf16_t *__restrict__ q_gate, int rows, int chunks,
                                                     int hkv, int lg, Params p) {
   constexpr int NSL = D / kWave;                        // 64-dim slices per row
-  const int lane = threadIdx.x, d = kWave * (blockIdx.x % NSL) + lane;
+  constexpr int CPL = kWave / 4;                        // chunks per lane and batch
+  // lane (q, c16) holds dims 4 c16 .. 4 c16 + 3 of the slice for chunks q, q + 4, ...
+  const int lane = threadIdx.x, q = lane >> 4, c16 = lane & 15;
+  const int d = kWave * (blockIdx.x % NSL) + 4 * c16;
   const int L = lg & 0xffff, G = lg >> 16, Hq = G * hkv;
   const int rr = (blockIdx.x / NSL) % rows;
   const int slot = blockIdx.x / NSL / rows;
@@ -41,45 +46,68 @@ __global__ __launch_bounds__(kWave) void combine_kernel(const int32_t *__restric
   if (rr >= L * G) return;
   const int64_t base = (int64_t)slot * chunks * rows + rr;   // + c * rows
   const int n = seq_lens[b];
-  const float z = (float)gld<bf16_t>(q_gate + (((int64_t)b * L + l) * Hq + h) * 2 * D + D + d);
+  RawE<4> zr;
+  zr.load(q_gate + (((int64_t)b * L + l) * Hq + h) * 2 * D + D + d);
   float2 ml = gld<float2>(part_ml + (base + (int64_t)min(lane, chunks - 1) * rows) * 2);
-  float v[kWave];
+  float4 v[CPL];
 #pragma unroll
-  for (int k = 0; k < kWave; ++k) {
-    v[k] = 0.f;
-    if (k < chunks) v[k] = gld<float>(part_o + (base + (int64_t)k * rows) * D + d);
+  for (int j = 0; j < CPL; ++j) {
+    v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (4 * j < chunks) v[j] = gld<float4>(part_o + (base + (int64_t)min(q + 4 * j, chunks - 1) * rows) * D + d);
   }
   __builtin_amdgcn_sched_barrier(0);                   // every load above is issued before any wait
 
   // chunks of this sequence (the grid's count at most, whatever the length says)
   const int nch = min(chunks, tile_chunk_count((int64_t)n + (L * G - 1) / G + 1, p.even_split, chunks, p.chunk_keys));
   if (nch == 1) return;                                 // finished by the attention kernel
-  float M = -INFINITY, lsum = 0.f, acc = 0.f;
+  float M = -INFINITY, lsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c0 = 0; c0 < nch; c0 += kWave) {
     if (c0 > 0) {
       ml = gld<float2>(part_ml + (base + (int64_t)min(c0 + lane, nch - 1) * rows) * 2);
 #pragma unroll
-      for (int k = 0; k < kWave; ++k) v[k] = gld<float>(part_o + (base + (int64_t)min(c0 + k, nch - 1) * rows) * D + d);
+      for (int j = 0; j < CPL; ++j) v[j] = gld<float4>(part_o + (base + (int64_t)min(c0 + q + 4 * j, nch - 1) * rows) * D + d);
     }
-    const bool own = c0 + lane < nch;
+    const bool own = c0 + lane < nch;                   // lane c holds chunk c0 + c's statistics
     const float mc = own ? ml.x : -INFINITY;
     const float Mn = fmaxf(M, rows4_max(row16_max(mc)));
     const float mu = Mn == -INFINITY ? 0.f : Mn;        // a chunk whose rows saw no key has m = -inf: weight 0
     const float alpha = __builtin_amdgcn_exp2f(M - mu);
     const float wc = own ? __builtin_amdgcn_exp2f(mc - mu) : 0.f;
     lsum = lsum * alpha + rows4_sum(row16_sum(wc * (own ? ml.y : 0.f)));
-    acc *= alpha;
+    acc.x *= alpha;
+    acc.y *= alpha;
+    acc.z *= alpha;
+    acc.w *= alpha;
 #pragma unroll
-    for (int k = 0; k < kWave; ++k) acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wc), k)) * v[k];
+    for (int j = 0; j < CPL; ++j) {
+      // the weight of chunk c0 + q + 4 j, from the lane that holds its statistics
+      const float w = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (q + 4 * j), __float_as_int(wc)));
+      acc.x += w * v[j].x;
+      acc.y += w * v[j].y;
+      acc.z += w * v[j].z;
+      acc.w += w * v[j].w;
+    }
     M = Mn;
   }
-  ((bf16_t *)p.out)[(((int64_t)b * L + l) * Hq + h) * D + d] = (bf16_t)(acc / lsum * sigmoid_f(z));
+  // the four lane groups hold disjoint chunk sets of the same dims
+  acc.x = rows4_sum(acc.x);
+  acc.y = rows4_sum(acc.y);
+  acc.z = rows4_sum(acc.z);
+  acc.w = rows4_sum(acc.w);
+  if (q == 0) {
+    float z[4];
+    zr.to_float(z);
+    const float inv = 1.f / lsum;
+    bf16x4 o4;
+    o4[0] = (bf16_t)(acc.x * inv * sigmoid_f(z[0]));
+    o4[1] = (bf16_t)(acc.y * inv * sigmoid_f(z[1]));
+    o4[2] = (bf16_t)(acc.z * inv * sigmoid_f(z[2]));
+    o4[3] = (bf16_t)(acc.w * inv * sigmoid_f(z[3]));
+    *(bf16x4 *)((bf16_t *)p.out + (((int64_t)b * L + l) * Hq + h) * D + d) = o4;
+  }
 }
 
-// Merge for the tile route, whose rows have few key chunks each: one wavefront
-// per (slot, row), lanes take EPL = D/64 dims, and the chunks are walked in
-// order: the chunk statistics are wave-uniform (scalar loads), the unnormalised
-// outputs one vector load per lane and chunk.
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_rows_kernel(Params p) {
   constexpr int EPL = D / kWave;
