@@ -168,8 +168,6 @@ qsa::Params base_params(const qsa_cfg *c, const Plan &pl) {
   p.eps = c->rms_eps;
   p.scale = c->softmax_scale > 0.f ? c->softmax_scale : (float)(1.0 / std::sqrt((double)c->head_dim));
   p.scale_log2 = p.scale * qsa::kLog2e;
-  for (int i = 0; i < c->rotary_dim / 2; ++i)
-    p.inv_freq[i] = std::pow((double)c->rope_theta, -2.0 * i / (double)c->rotary_dim);
   p.rope_step = c->rotary_dim > 0 ? std::pow((double)c->rope_theta, -2.0 / (double)c->rotary_dim) : 1.0;
   p.wq = c->q_norm_w;
   p.wk = c->k_norm_w;

@@ -67,7 +67,6 @@ struct Params {
   float *part_o;
   void *qt;
   double rope_step;            // theta^(-2/r) (r > 0), computed on the host in double
-  double inv_freq[kMaxPairs];  // theta^(-2i/r), computed on the host in double
 };
 
 // ------------------------------------------------------------------ helpers
@@ -105,9 +104,18 @@ __device__ __forceinline__ void rope_angle_cs(int pos, double inv, float &c, flo
   sincosf((float)red, &s, &c);
 }
 
-// cos/sin of rotary pair i at position pos.
-__device__ __forceinline__ void rope_cs(const Params &p, int pos, int i, float &c, float &s) {
-  rope_angle_cs(pos, p.inv_freq[i], c, s);
+// theta^(-2i/r) = step^i for 0 <= i < kMaxPairs, by binary powers in double
+// (at most 14 roundings, ~1e-15 relative) of the host's step = theta^(-2/r): a
+// scalar argument, where reading a per-lane entry of a table in the argument
+// segment would be a slow vector load.
+__device__ __forceinline__ double rope_freq(double step, int i) {
+  double f = 1.0, sq = step;
+#pragma unroll
+  for (int bit = 0; bit < 7; ++bit) {                   // kMaxPairs = 2^7
+    f = (i >> bit) & 1 ? f * sq : f;
+    sq *= sq;
+  }
+  return f;
 }
 
 // Keys [0, kend) of one (sequence, row tile) are cut into max(1, kend / chunk_keys)

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(Params p, int do_q, 
     const int pos = p.positions[bl];
     for (int i = threadIdx.x; i < half; i += kThreads) {
       float c, sn;
-      rope_cs(p, pos, i, c, sn);
+      rope_angle_cs(pos, rope_freq(p.rope_step, i), c, sn);
       cs[i] = make_float2(c, sn);
     }
   }

@@ -318,22 +318,14 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     // the only stage's V is needed soon: issue it before the preparation; V
     // halves of later stages are issued after it
     if (!v0_by_copiers && nst > 0) issue_first_half(0, false, pw);
-    // this wave's (cos, sin) table: entry l * r/2 + i for new row l, pair i,
-    // with the frequency theta^(-2i/r) = step^i by binary powers of the host's
-    // step theta^(-2/r) in double (a handful of roundings, ~1e-15 relative)
+    // this wave's (cos, sin) table: entry l * r/2 + i for new row l, pair i
     const double step = p.rope_step;
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int e = lane + kWave * j;
       if (kWave * j < L * half) {
-        double f = 1.0, sq = step;
-#pragma unroll
-        for (int bit = 0; bit < 7; ++bit) {             // pairs < kMaxPairs = 2^7
-          f = (tpair[j] >> bit) & 1 ? f * sq : f;
-          sq *= sq;
-        }
         float c, sn;
-        rope_angle_cs(tpos[j], f, c, sn);
+        rope_angle_cs(tpos[j], rope_freq(step, tpair[j]), c, sn);
         if (e < L * half) tabw[e] = make_float2(c, sn);
       }
     }
