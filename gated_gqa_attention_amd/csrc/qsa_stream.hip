@@ -105,17 +105,20 @@ struct WaitUnits<LPS, 0> {
 
 // RTM: row tiles (16 rows each) of the workgroup, ceil(L * G / 16) <= 3.
 //
-// Two roles until the first stage.  Wavefronts 0-1 (the copy waves) load the
-// sequence metadata and issue every copy of the first stages; the memory
-// system accepts them at the rate it delivers, so those waves are held at the
-// issue for most of the transfer.  Their vector-memory counter must see no
-// other load after the copies, since it retires in order and a later load
-// would make its consumer wait for every copy.  Wavefronts 2-3 (the prep
-// waves) issue no copies, so they load freely: each builds its own (cos, sin)
-// table, the two normalise and rotate all query rows into bf16 MFMA operands
-// in LDS, and, in the workgroup that holds the new keys, normalise and rotate
-// those too.  Then all four wavefronts meet, take their query operands and run
-// the stages together; refills of the ring are shared by all four.
+// Two roles until the first stage.  Wavefronts 0-1 (the copy waves) load only
+// the sequence metadata, then issue the K copies of the first stages (and the
+// V copies of stage 0 when more stages follow, or when they hold the new
+// keys); the memory system accepts copies at the rate it delivers, so those
+// waves are held at the issue for most of the transfer.  A wave's
+// vector-memory counter retires in order, so no wave consumes a load issued
+// after its own copies: its consumer would wait for every copy.  Wavefronts
+// 2-3 (the prep waves) first land all their own loads, then issue the other V
+// copies (the only stage's before their preparation, later stages' after it);
+// each builds its own (cos, sin) table, the two normalise and rotate all query
+// rows into bf16 MFMA operands in LDS, and, in the workgroup that holds the new
+// keys, normalise and rotate those too.  Then all four wavefronts meet, take
+// their query operands and run the stages together; refills of the ring are
+// shared by all four.
 // lgh packs L (bits 0-7), G (bits 8-15) and r/2 (bits 16-31).
 template <int D, int RTM>
 __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restrict__ seq_lens,
