@@ -351,8 +351,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int d = 16 * db + 4 * g4;
-        *(float4 *)(p.part_o + (slot_rows + rr) * D + d) =
-            make_float4(O[rt][db][0], O[rt][db][1], O[rt][db][2], O[rt][db][3]);
+        __builtin_nontemporal_store(O[rt][db], (f32x4 *)(p.part_o + (slot_rows + rr) * D + d));
       }
       if (g4 == 0) *(float2 *)(p.part_ml + (slot_rows + rr) * 2) = make_float2(mrun[rt], lsum);
     }

@@ -258,7 +258,10 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   const bool early_new = tail && nst < NS;
   const int new_slot = (early_new ? nst : 0) * G::STAGE;
   const bool v0_by_copiers = nst > 1 || early_new;
-  // New key and value rows 8 k + 4 pw + g4 of the tail workgroup (prep waves).
+  const int nr = 4 * (pw ^ 1) + g4;
+  // New key and value rows 8 k + nr of the tail workgroup (prep waves).  They
+  // go to the other prep wave than query rows 8 k + 4 pw + g4, so that with
+  // few rows (decode: one query group, one new row) each prep wave has one pass.
   // Their pointers come from the argument segment, so they are a second round
   // trip; they are issued before any copy of the workgroup (the barrier below),
   // since a load behind the copies in the CU's memory pipeline lands only after
@@ -266,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   if (!copier && tail) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int l = min(8 * k + 4 * pw + g4, L - 1);
+      const int l = min(8 * k + nr, L - 1);
       const int64_t src = (((int64_t)b * L + l) * hkv + kvh) * D + E * m16;
       knraw[k].load(knew + src);
       vnraw[k].load((const bf16_t *)p.v_new + src);
@@ -291,14 +294,14 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
 
   // ------------------------------------------------------------ prep waves
   float2 *const tabw = (float2 *)(arena + QBYTES) + (copier ? 0 : pw) * TABN;
-  float kx[2][E];                                       // new key rows 8 k + 4 pw + g4 (prep waves)
+  float kx[2][E];                                       // new key rows 8 k + nr (prep waves)
   // The new-key stage, written by the prep waves into ring slot new_slot: K and
   // V rows 0 .. 15 (rows >= L zero) and V rows 16 .. 31 zero (read by the value
   // product).
   auto put_new_rows = [&]() {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int l = 8 * k + 4 * pw + g4;
+      const int l = 8 * k + nr;
       float v[E], zero[E];
       vnraw[k].to_float(v);
 #pragma unroll
@@ -359,9 +362,14 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
       wkraw.to_float(wk);
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        const int l = 8 * k + 4 * pw + g4;
-        knraw[k].to_float(kx[k]);
-        norm_rope<D>(kx[k], wk, l < L, eps, 2 * half, tabw + min(l, L - 1) * half);   // rows >= L become zero
+        const int l = 8 * k + nr;
+        if (8 * k + 4 * (pw ^ 1) < L) {                 // the pass holds a new row (wave-uniform)
+          knraw[k].to_float(kx[k]);
+          norm_rope<D>(kx[k], wk, l < L, eps, 2 * half, tabw + min(l, L - 1) * half);   // rows >= L become zero
+        } else {
+#pragma unroll
+          for (int j = 0; j < E; ++j) kx[k][j] = 0.f;
+        }
       }
     }
     if (early_new) put_new_rows();
@@ -422,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     for (int k = 0; k < 2; ++k) {
       float v[E];
       if (!copier) {
-        const int l = 8 * k + 4 * pw + g4;
+        const int l = 8 * k + nr;
 #pragma unroll
         for (int j = 0; j < E; ++j) v[j] = 0.f;
         vnraw[k].to_float(v);
@@ -474,7 +482,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
 #pragma unroll
       for (int db = 0; db < DBW; ++db) {
         const int d = 16 * (DBW * wave + db) + 4 * g4;
-        *(float4 *)(p.part_o + (slot_rows + r) * D + d) = make_float4(O[rt][db][0], O[rt][db][1], O[rt][db][2], O[rt][db][3]);
+        __builtin_nontemporal_store(O[rt][db], (f32x4 *)(p.part_o + (slot_rows + r) * D + d));
       }
       if (wave == 0 && g4 == 0) *(float2 *)(p.part_ml + (slot_rows + r) * 2) = make_float2(mrun[rt], lrun[rt]);
     }
