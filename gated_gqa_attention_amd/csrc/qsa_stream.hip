@@ -106,14 +106,14 @@ struct WaitUnits<LPS, 0> {
 // RTM: row tiles (16 rows each) of the workgroup, ceil(L * G / 16) <= 3.
 //
 // Two roles until the first stage.  Wavefronts 0-1 (the copy waves) load only
-// the sequence metadata, then issue the K copies of the first stages (and the
-// V copies of stage 0 when more stages follow, or when they hold the new
-// keys); the memory system accepts copies at the rate it delivers, so those
-// waves are held at the issue for most of the transfer.  A wave's
-// vector-memory counter retires in order, so no wave consumes a load issued
-// after its own copies: its consumer would wait for every copy.  Wavefronts
-// 2-3 (the prep waves) first land all their own loads, then issue the other V
-// copies (the only stage's before their preparation, later stages' after it);
+// the sequence metadata, then issue the K copies of the first stages (and
+// their V copies when more stages follow, or when they hold the new keys); the
+// memory system accepts copies at the rate it delivers, so those waves are
+// held at the issue for most of the transfer.  A wave's vector-memory counter
+// retires in order, so no wave consumes a load issued after its own copies:
+// its consumer would wait for every copy.  Wavefronts 2-3 (the prep waves)
+// first land all their own loads, then issue the V copies of a single cached
+// stage before their preparation (when the copy waves do not);
 // each builds its own (cos, sin) table, the two normalise and rotate all query
 // rows into bf16 MFMA operands in LDS, and, in the workgroup that holds the new
 // keys, normalise and rotate those too.  Then all four wavefronts meet, take
@@ -240,11 +240,11 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
 #pragma unroll
     for (int i = 0; i < LPS; ++i) copy_unit(base, is_k ? kring_lds : vring_lds, st, kWave * wave + kThreads * i, last);
   };
-  // The first stages.  The copy waves issue every K half, and the V half of
-  // stage 0 when more stages follow; the prep waves issue the other V halves
-  // (the only stage's, or those of stages 1 ..).  Each wave issues in stage
-  // order, 2 LPS copies per thread for every stage after the first, so the
-  // copies younger than a stage are 2 LPS per thread per later stage in both roles.
+  // The first stages.  The copy waves issue every K half, and the V halves too
+  // when more stages follow (or when the new keys take a free slot); otherwise
+  // the prep waves issue the only stage's V half.  Each wave issues in stage
+  // order, so the copies younger than a stage of the first fill are 4 LPS per
+  // thread per later stage in a copy wave (K and V) and none in a prep wave.
   auto issue_first_half = [&](int st, bool is_k, int w2) {
     const int last = stage_last(st);
     const bf16_t *base = stage_src(st, is_k);
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     for (int st = 0; st < NS; ++st) {
       if (st < nst) {
         issue_first_half(st, true, wave);
-        if (st == 0 && v0_by_copiers) issue_first_half(0, false, wave);
+        if (v0_by_copiers) issue_first_half(st, false, wave);
       }
     }
   }
@@ -321,8 +321,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     wqraw.land();
 #pragma unroll
     for (int j = 0; j < TJ; ++j) asm volatile("" ::"v"(tpos[j]));
-    // the only stage's V is needed soon: issue it before the preparation; V
-    // halves of later stages are issued after it
+    // the only stage's V is needed soon: issue it before the preparation
     if (!v0_by_copiers && nst > 0) issue_first_half(0, false, pw);
     // this wave's (cos, sin) table: entry l * r/2 + i for new row l, pair i
     const double step = p.rope_step;
@@ -373,9 +372,6 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
       }
     }
     if (early_new) put_new_rows();
-#pragma unroll
-    for (int st = 1; st < NS; ++st)
-      if (st < nst) issue_first_half(st, false, pw);
   }
   lds_barrier();                                        // query operands ready; first stages issued
 
@@ -405,10 +401,13 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     attend_stage<D, RTM>(kring + new_slot, vring + new_slot, L, n, qf, O, mrun, lrun, lim, sl2, arena);
   }
   for (int st = 0; st < nst; ++st) {
-    // copies younger than stage st that this wave issued: 2 LPS per thread for
-    // each later stage of the first fill (its K or V half) and each refill
+    // copies younger than stage st that this wave issued: of the ys later
+    // stages in flight, f are of the first fill (4 LPS per thread in a copy
+    // wave, K and V halves; none in a prep wave) and ys - f are refills (2 LPS
+    // per thread in every wave)
     const int ys = min(NS - 1, nst - 1 - st);
-    WaitUnits<LPS, 2 * (NS - 1)>::run(2 * ys);
+    const int f = max(0, min(NS, nst) - 1 - st);
+    WaitUnits<LPS, 4 * (NS - 1)>::run(copier ? 2 * (ys + f) : 2 * (ys - f));
     lds_barrier();
     const int so = (st % NS) * G::STAGE;
     const int sk0 = (int)k0 + G::SK * st;
