@@ -104,6 +104,12 @@ SMALL = [
              rotary_dim=8, rope_theta=1e4, dtype="bf16", prior=90, seed=118),
     Workload("bf16_d128_r16_rows48", batch=2, q_len=4, num_q_heads=12, num_kv_heads=1, head_dim=128,
              rotary_dim=16, rope_theta=1e6, dtype="bf16", prior=150, seed=119),
+    # short-query route with more stages than ring slots when unsplit (refills):
+    # head_dim 64 (8 slots), 700 + 2 keys = 11 stages; head_dim 128 (4 slots), 380 + 3 keys = 6 stages
+    Workload("bf16_d64_refills", batch=1, q_len=2, num_q_heads=4, num_kv_heads=2, head_dim=64,
+             rotary_dim=16, rope_theta=1e4, dtype="bf16", prior=700, seed=122),
+    Workload("bf16_d128_refills", batch=1, q_len=3, num_q_heads=6, num_kv_heads=2, head_dim=128,
+             rotary_dim=32, rope_theta=1e6, dtype="bf16", prior=380, seed=123),
     # decode shapes outside the short-query route: r/2 not a multiple of D/16, and 49 rows
     Workload("bf16_decode_r16_prepared", batch=2, q_len=1, num_q_heads=16, num_kv_heads=4, head_dim=256,
              rotary_dim=16, rope_theta=1e7, dtype="bf16", prior=200, seed=120),
