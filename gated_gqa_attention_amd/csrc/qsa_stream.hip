@@ -158,6 +158,8 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   const bf16_t *const kc = (const bf16_t *)p.kc;
   const bf16_t *const vc = (const bf16_t *)p.vc;
   const bf16_t *const knew = (const bf16_t *)p.k_new;
+  const bf16_t *const vnew = (const bf16_t *)p.v_new;
+  const bf16_t *const wkp = (const bf16_t *)p.wk;
   const float eps = p.eps, sl2 = p.scale_log2;
   // prep waves: query rows 8 k + 4 pw + g4 of pass k, the norm weight, and the
   // position of table entries lane + 64 j; none of these addresses waits on an
@@ -185,6 +187,10 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     __builtin_amdgcn_sched_barrier(0);                 // every load above is issued before any wait
   }
 
+  // The new-key pointers, which the workgroup holding the new keys loads from
+  // before its copies, are used here so that their loads from the argument
+  // segment are issued with the sequence length, not one round trip after it.
+  asm volatile("" ::"s"(knew), "s"(vnew), "s"(wkp));
   const int64_t total = (int64_t)n + L;
   const bool in_range = n >= 0 && off >= 0 && total <= msl && off + total <= nrows;
   const int64_t kend = total;
@@ -272,9 +278,9 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
       const int l = min(8 * k + nr, L - 1);
       const int64_t src = (((int64_t)b * L + l) * hkv + kvh) * D + E * m16;
       knraw[k].load(knew + src);
-      vnraw[k].load((const bf16_t *)p.v_new + src);
+      vnraw[k].load(vnew + src);
     }
-    wkraw.load((const bf16_t *)p.wk + E * m16);
+    wkraw.load(wkp + E * m16);
   }
   lds_barrier();
   if (copier) {
