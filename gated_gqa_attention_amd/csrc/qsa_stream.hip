@@ -132,7 +132,15 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   constexpr int QBYTES = 16 * RTM * RB;                 // prepared query rows, bf16, swizzled
   constexpr int TABN = kMaxFusedTable;                  // (cos, sin) entries per table copy
   constexpr int PREP = QBYTES + 2 * TABN * 8;
-  constexpr int ARENA = PREP > Xch::BYTES ? PREP : Xch::BYTES;
+  // With several row tiles and no free ring slot, the new rows sit in the
+  // arena after the stage exchange: V rows 0 .. 15 at NEWOFF, K rows 0 .. 15
+  // right after them, so V rows 16 .. 31 (read by the value product with P = 0)
+  // are the finite K rows.  With one row tile they follow the cached stages in
+  // ring slot 0 (a larger arena measured slower for decode).
+  constexpr bool ARENA_NEW = RTM > 1;
+  constexpr int NEWOFF = Xch::BYTES, NEWB = NEWOFF + 32 * RB;
+  constexpr int ARENA = ARENA_NEW ? (PREP > NEWB ? PREP : NEWB) : (PREP > Xch::BYTES ? PREP : Xch::BYTES);
+  static_assert(Xch::BYTES % 16 == 0, "arena layout");
   constexpr int NPASS = 2 * RTM;                        // query row passes per prep wave (8 rows each)
   static_assert(RTM <= 3, "query rows of the short-query route");
   __shared__ __attribute__((aligned(16))) unsigned char ring[2 * G::RING];   // K ring | V ring
@@ -260,7 +268,9 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   };
   // The new keys become one more stage.  When the cached stages leave a ring
   // slot unused, the new keys take it and are attended first, while the cached
-  // stages are still in flight; otherwise they follow the cached stages in slot 0.
+  // stages are still in flight; otherwise, with several row tiles, they are put
+  // in the arena once every wave has its query operands and attended first all
+  // the same, and with one row tile they follow the cached stages in slot 0.
   const bool early_new = tail && nst < NS;
   const int new_slot = (early_new ? nst : 0) * G::STAGE;
   const bool v0_by_copiers = nst > 1 || early_new;
@@ -301,9 +311,11 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   // ------------------------------------------------------------ prep waves
   float2 *const tabw = (float2 *)(arena + QBYTES) + (copier ? 0 : pw) * TABN;
   float kx[2][E];                                       // new key rows 8 k + nr (prep waves)
-  // The new-key stage, written by the prep waves into ring slot new_slot: K and
-  // V rows 0 .. 15 (rows >= L zero) and V rows 16 .. 31 zero (read by the value
-  // product).
+  // The new-key stage, written by the prep waves: K and V rows 0 .. 15 (rows >=
+  // L zero), into ring slot new_slot (with V rows 16 .. 31 zero, read by the
+  // value product) or into the arena.
+  unsigned char *const nkb = early_new || !ARENA_NEW ? kring + new_slot : arena + NEWOFF + 16 * RB;
+  unsigned char *const nvb = early_new || !ARENA_NEW ? vring + new_slot : arena + NEWOFF;
   auto put_new_rows = [&]() {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -315,9 +327,9 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
         zero[j] = 0.f;
         if (l >= L) v[j] = 0.f;
       }
-      put_row_bf16<D>(kring + new_slot, RB, l, E * m16, kx[k]);
-      put_row_bf16<D>(vring + new_slot, RB, l, E * m16, v);   // v_new is bf16 already: exact
-      put_row_bf16<D>(vring + new_slot, RB, 16 + l, E * m16, zero);
+      put_row_bf16<D>(nkb, RB, l, E * m16, kx[k]);
+      put_row_bf16<D>(nvb, RB, l, E * m16, v);        // v_new is bf16 already: exact
+      if (early_new) put_row_bf16<D>(nvb, RB, 16 + l, E * m16, zero);
     }
   };
   if (!copier) {
@@ -402,9 +414,16 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
 #pragma unroll
     for (int db = 0; db < DBW; ++db) O[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  if (early_new) {
+  // The new keys are attended first, while the cached stages are in flight:
+  // from the free ring slot, where the prep waves put them before the barrier
+  // above, or from the arena, once every wave has its query operands.
+  if (tail && (early_new || ARENA_NEW)) {
     lds_barrier();                                      // every wave has its query operands (the exchange reuses them)
-    attend_stage<D, RTM>(kring + new_slot, vring + new_slot, L, n, qf, O, mrun, lrun, lim, sl2, arena);
+    if (!early_new) {
+      if (!copier) put_new_rows();
+      lds_barrier();
+    }
+    attend_stage<D, RTM>(nkb, nvb, L, n, qf, O, mrun, lrun, lim, sl2, arena);
   }
   for (int st = 0; st < nst; ++st) {
     // copies younger than stage st that this wave issued: of the ys later
@@ -426,11 +445,11 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     if (st + NS < nst) issue_half(st + NS, false);
   }
 
-  // ------------------------------------------------------------ new keys (tail workgroup)
+  // ------------------------------------------------------------ new keys, one row tile, no free slot
   // The new rows become one more stage in ring slot 0: K and V rows 0 .. 15
   // (rows >= L zero) from the prep waves, V rows 16 .. 31 zero (read by the
   // value product) from the copy waves.
-  if (tail && !early_new) {
+  if (!ARENA_NEW && tail && !early_new) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       float v[E];
@@ -515,8 +534,8 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
       const int l = u / G::OCT, oct = u % G::OCT;
       if (l < L) {
         const int64_t dst = ((off + n + l) * hkv + kvh) * D + 8 * oct;
-        *(uint4 *)((bf16_t *)p.kc + dst) = *(const uint4 *)(kring + new_slot + swz<G::SW>(l, oct, RB));
-        *(uint4 *)((bf16_t *)p.vc + dst) = *(const uint4 *)(vring + new_slot + swz<G::SW>(l, oct, RB));
+        *(uint4 *)((bf16_t *)p.kc + dst) = *(const uint4 *)(nkb + swz<G::SW>(l, oct, RB));
+        *(uint4 *)((bf16_t *)p.vc + dst) = *(const uint4 *)(nvb + swz<G::SW>(l, oct, RB));
       }
     }
   }
