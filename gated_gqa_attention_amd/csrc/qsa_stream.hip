@@ -417,7 +417,28 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   // The new keys are attended first, while the cached stages are in flight:
   // from the free ring slot, where the prep waves put them before the barrier
   // above, or from the arena, once every wave has its query operands.
-  if (tail && (early_new || ARENA_NEW)) {
+  if (early_new && L == 1) {
+    // One new key, visible to every row: attending it leaves each row's
+    // reference max at its score, its sum at 1 (P = 2^0) and its output at the
+    // value row.  Each wavefront sets that state itself from the rows in the
+    // free slot (written before the barrier above): the same MFMA score as a
+    // stage, with no exchange.
+#pragma unroll
+    for (int rt = 0; rt < RTM; ++rt) {
+      f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KST; ++ks)
+        S = mfma_qk(*(const bf16x8 *)(nkb + swz<G::SW>(m16, 4 * ks + g4, RB)), qf[rt][ks], S);
+      mrun[rt] = rows4_max(g4 == 0 ? S[0] * sl2 : -INFINITY);   // key 0 sits in lane group 0
+      lrun[rt] = 1.f;
+#pragma unroll
+      for (int db = 0; db < DBW; ++db) {
+        const int d = 16 * (DBW * wave + db) + 4 * g4;
+        const bf16x4 v4 = *(const bf16x4 *)(nvb + swz<G::SW>(0, d / 8, RB) + 2 * (d % 8));
+        O[rt][db] = f32x4{(float)v4[0], (float)v4[1], (float)v4[2], (float)v4[3]};
+      }
+    }
+  } else if (tail && (early_new || ARENA_NEW)) {
     lds_barrier();                                      // every wave has its query operands (the exchange reuses them)
     if (!early_new) {
       if (!copier) put_new_rows();
