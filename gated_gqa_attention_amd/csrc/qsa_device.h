@@ -330,5 +330,56 @@ __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsi
   }
 }
 
+// The new rows attended by each wavefront on its own, as the first keys of the
+// chunk (m = -inf, sums and outputs zero): at most 16 keys, K and V rows 0 ..
+// 15 at kt and vt (rows >= nkeys finite).  All of them lie in one 16-key block,
+// so every wavefront scores that block against every row tile (the same MFMA
+// as a stage), takes the causal mask, reference max and sums within itself,
+// and runs the value product over its own dims from 16x16x16 MFMAs, whose B
+// operand is the score tile's own layout (lane group g4: keys 4 g4 .. 4 g4 + 3).
+template <int D, int RTM>
+__device__ __forceinline__ void attend_new_rows(const unsigned char *kt, const unsigned char *vt, int nkeys, int key0,
+                                                const bf16x8 (&qf)[RTM][D / 32], f32x4 (&O)[RTM][D / 64],
+                                                float (&m)[RTM], float (&lsum)[RTM], const int (&lim)[RTM],
+                                                float scale_log2) {
+  using G = Geo<D>;
+  constexpr int KST = D / 32, DBW = D / 64, RB = G::RB;
+  const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int vk = 4 * g4 + (m16 >> 2), q4 = m16 & 3;
+#pragma unroll
+  for (int rt = 0; rt < RTM; ++rt) {
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks) S = mfma_qk(*(const bf16x8 *)(kt + swz<G::SW>(m16, 4 * ks + g4, RB)), qf[rt][ks], S);
+    const int vis = min(lim[rt] - key0 + 1, nkeys);
+    float sc[4], bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = 4 * g4 + i < vis ? S[i] * scale_log2 : -INFINITY;
+      bm = fmaxf(bm, sc[i]);
+    }
+    const float M = rows4_max(bm);                      // the reference: m was -inf
+    const float mu = M == -INFINITY ? 0.f : M;
+    m[rt] = M;
+    bf16x4 pv;
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = (bf16_t)__builtin_amdgcn_exp2f(sc[i] - mu);
+      ps += (float)pv[i];
+    }
+    lsum[rt] = rows4_sum(ps);
+    const s16x4 pb = __builtin_bit_cast(s16x4, pv);
+#pragma unroll
+    for (int db = 0; db < DBW; ++db) {
+      // lane (g4, i) addresses the 8-byte piece (key 4 g4 + i/4, dims 16 (DBW w + db) + 4 (i%4) ..)
+      const unsigned char *pa = vt + swz<G::SW>(vk, 2 * (DBW * wave + db) + (q4 >> 1), RB) + 8 * (q4 & 1);
+      const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)pa);
+      O[rt][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, O[rt][db], 0, 0, 0);
+    }
+  }
+}
+
 }  // namespace
 }  // namespace qsa

@@ -439,12 +439,12 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
       }
     }
   } else if (tail && (early_new || ARENA_NEW)) {
-    lds_barrier();                                      // every wave has its query operands (the exchange reuses them)
     if (!early_new) {
+      lds_barrier();                                    // every wave has its query operands (the new rows reuse the arena)
       if (!copier) put_new_rows();
       lds_barrier();
     }
-    attend_stage<D, RTM>(nkb, nvb, L, n, qf, O, mrun, lrun, lim, sl2, arena);
+    attend_new_rows<D, RTM>(nkb, nvb, L, n, qf, O, mrun, lrun, lim, sl2);
   }
   for (int st = 0; st < nst; ++st) {
     // copies younger than stage st that this wave issued: of the ys later
