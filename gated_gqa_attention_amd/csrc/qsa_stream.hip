@@ -134,9 +134,8 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   constexpr int PREP = QBYTES + 2 * TABN * 8;
   // With several row tiles and no free ring slot, the new rows sit in the
   // arena after the stage exchange: V rows 0 .. 15 at NEWOFF, K rows 0 .. 15
-  // right after them, so V rows 16 .. 31 (read by the value product with P = 0)
-  // are the finite K rows.  With one row tile they follow the cached stages in
-  // ring slot 0 (a larger arena measured slower for decode).
+  // right after them.  With one row tile they follow the cached stages in ring
+  // slot 0 (a larger arena measured slower for decode).
   constexpr bool ARENA_NEW = RTM > 1;
   constexpr int NEWOFF = Xch::BYTES, NEWB = NEWOFF + 32 * RB;
   constexpr int ARENA = ARENA_NEW ? (PREP > NEWB ? PREP : NEWB) : (PREP > Xch::BYTES ? PREP : Xch::BYTES);
@@ -311,25 +310,21 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   // ------------------------------------------------------------ prep waves
   float2 *const tabw = (float2 *)(arena + QBYTES) + (copier ? 0 : pw) * TABN;
   float kx[2][E];                                       // new key rows 8 k + nr (prep waves)
-  // The new-key stage, written by the prep waves: K and V rows 0 .. 15 (rows >=
-  // L zero), into ring slot new_slot (with V rows 16 .. 31 zero, read by the
-  // value product) or into the arena.
+  // The new rows, written by the prep waves: K and V rows 0 .. 15 (rows >= L
+  // zero), into ring slot new_slot or into the arena.
   unsigned char *const nkb = early_new || !ARENA_NEW ? kring + new_slot : arena + NEWOFF + 16 * RB;
   unsigned char *const nvb = early_new || !ARENA_NEW ? vring + new_slot : arena + NEWOFF;
   auto put_new_rows = [&]() {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int l = 8 * k + nr;
-      float v[E], zero[E];
+      float v[E];
       vnraw[k].to_float(v);
 #pragma unroll
-      for (int j = 0; j < E; ++j) {
-        zero[j] = 0.f;
+      for (int j = 0; j < E; ++j)
         if (l >= L) v[j] = 0.f;
-      }
       put_row_bf16<D>(nkb, RB, l, E * m16, kx[k]);
       put_row_bf16<D>(nvb, RB, l, E * m16, v);        // v_new is bf16 already: exact
-      if (early_new) put_row_bf16<D>(nvb, RB, 16 + l, E * m16, zero);
     }
   };
   if (!copier) {
