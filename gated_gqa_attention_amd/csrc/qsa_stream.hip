@@ -303,9 +303,17 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   }
 
   // capacity only guards the writes at the end; its pointer comes from the
-  // argument segment, so it is loaded behind the copies
+  // argument segment, so it is loaded behind the copies, and as a vector load
+  // (its index is a lane value, an opaque zero), which lands after them and is
+  // awaited only at the outputs: a scalar load would hold up the next barrier,
+  // which waits for every outstanding scalar and LDS operation
   const int32_t *const capp = p.capacity;
-  const int cap = capp ? capp[b] : 0x7fffffff;
+  int cap = 0x7fffffff;
+  if (capp) {
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    cap = gld<int>(capp + b + z);
+  }
 
   // ------------------------------------------------------------ prep waves
   float2 *const tabw = (float2 *)(arena + QBYTES) + (copier ? 0 : pw) * TABN;
@@ -494,6 +502,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   // Every wavefront writes its own dims 16 (DBW wave + db) + 4 g4 .. + 3 of row
   // 16 rt + m16: the gated output when the chunk is the whole sequence, else
   // the chunk's unnormalised output and (max, sum) for the merge kernel.
+  asm volatile("" : "+v"(cap));                       // consumed only here, after every stage
   const bool cap_ok = total <= (int64_t)cap;
   const bool single = nch == 1;
   const int64_t slot_rows = ((int64_t)slot * pchunks + chunk) * p.rows;
