@@ -110,6 +110,12 @@ SMALL = [
              rotary_dim=16, rope_theta=1e4, dtype="bf16", prior=700, seed=122),
     Workload("bf16_d128_refills", batch=1, q_len=3, num_q_heads=6, num_kv_heads=2, head_dim=128,
              rotary_dim=32, rope_theta=1e6, dtype="bf16", prior=380, seed=123),
+    # short-query route with many new rows (keys 4 .. 15 of the first-attended new block,
+    # causal among themselves): 16 x 3 rows at head_dim 128, 12 x 4 rows at head_dim 256
+    Workload("bf16_fused_new16_d128", batch=2, q_len=16, num_q_heads=6, num_kv_heads=2, head_dim=128,
+             rotary_dim=32, rope_theta=1e6, dtype="bf16", prior=200, seed=124),
+    Workload("bf16_fused_new12_d256", batch=1, q_len=12, num_q_heads=4, num_kv_heads=1, head_dim=256,
+             rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=100, seed=125),
     # decode shapes outside the short-query route: r/2 not a multiple of D/16, and 49 rows
     Workload("bf16_decode_r16_prepared", batch=2, q_len=1, num_q_heads=16, num_kv_heads=4, head_dim=256,
              rotary_dim=16, rope_theta=1e7, dtype="bf16", prior=200, seed=120),
