@@ -106,14 +106,12 @@ struct WaitUnits<LPS, 0> {
 // RTM: row tiles (16 rows each) of the workgroup, ceil(L * G / 16) <= 3.
 //
 // Two roles until the first stage.  Wavefronts 0-1 (the copy waves) load only
-// the sequence metadata, then issue the K copies of the first stages (and
-// their V copies when more stages follow, or when they hold the new keys); the
-// memory system accepts copies at the rate it delivers, so those waves are
+// the sequence metadata, then issue the K and V copies of the first stages;
+// the memory system accepts copies at the rate it delivers, so those waves are
 // held at the issue for most of the transfer.  A wave's vector-memory counter
 // retires in order, so no wave consumes a load issued after its own copies:
 // its consumer would wait for every copy.  Wavefronts 2-3 (the prep waves)
-// first land all their own loads, then issue the V copies of a single cached
-// stage before their preparation (when the copy waves do not);
+// issue no copy before the stages: they land all their own loads,
 // each builds its own (cos, sin) table, the two normalise and rotate all query
 // rows into bf16 MFMA operands in LDS, and, in the workgroup that holds the new
 // keys, normalise and rotate those too.  Then all four wavefronts meet, take
@@ -253,9 +251,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
 #pragma unroll
     for (int i = 0; i < LPS; ++i) copy_unit(base, is_k ? kring_lds : vring_lds, st, kWave * wave + kThreads * i, last);
   };
-  // The first stages.  The copy waves issue every K half, and the V halves too
-  // when more stages follow (or when the new keys take a free slot); otherwise
-  // the prep waves issue the only stage's V half.  Each wave issues in stage
+  // The first stages: the copy waves issue both halves of each, in stage
   // order, so the copies younger than a stage of the first fill are 4 LPS per
   // thread per later stage in a copy wave (K and V) and none in a prep wave.
   auto issue_first_half = [&](int st, bool is_k, int w2) {
@@ -272,7 +268,6 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   // the same, and with one row tile they follow the cached stages in slot 0.
   const bool early_new = tail && nst < NS;
   const int new_slot = (early_new ? nst : 0) * G::STAGE;
-  const bool v0_by_copiers = nst > 1 || early_new;
   const int nr = 4 * (pw ^ 1) + g4;
   // New key and value rows 8 k + nr of the tail workgroup (prep waves).  They
   // go to the other prep wave than query rows 8 k + 4 pw + g4, so that with
@@ -297,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     for (int st = 0; st < NS; ++st) {
       if (st < nst) {
         issue_first_half(st, true, wave);
-        if (v0_by_copiers) issue_first_half(st, false, wave);
+        issue_first_half(st, false, wave);
       }
     }
   }
@@ -342,8 +337,6 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     wqraw.land();
 #pragma unroll
     for (int j = 0; j < TJ; ++j) asm volatile("" ::"v"(tpos[j]));
-    // the only stage's V is needed soon: issue it before the preparation
-    if (!v0_by_copiers && nst > 0) issue_first_half(0, false, pw);
     // this wave's (cos, sin) table: entry l * r/2 + i for new row l, pair i
     const double step = p.rope_step;
 #pragma unroll
