@@ -16,8 +16,11 @@
 // two split q_gate, RMS-normalise and rotate the query rows (mlxd PR #99
 // Summary and config audit table; Atlas FullAttentionLayer q_norm / k_norm,
 // Qwen35ForwardConfig::rotary_dim) and, in the workgroup whose chunk ends the
-// sequence, the new keys; those are kept in registers, become the last stage
-// and are appended to the cache at the end (Atlas qwen3_5/mod.rs module doc:
+// sequence, the new keys.  Those are attended before the cached stages, from
+// a free ring slot or (several row tiles) from the arena, by each wavefront on
+// its own; a single new key only sets the running state.  With one row tile
+// and no free slot they follow the cached stages instead.  Either way they
+// are appended to the cache at the end (Atlas qwen3_5/mod.rs module doc:
 // append at cache_pos, attend over cache_pos + 1 keys).
 //
 // Compute (the stage step in qsa_device.h).  Wavefront w scores keys
@@ -30,7 +33,7 @@
 // with V^T read by gfx950's transposing LDS loads.  A chunk that covers the
 // whole sequence applies the gate attn * sigmoid(gate) (mlxd PR #99 Summary)
 // and stores bf16; otherwise it writes the chunk's (max, sum, unnormalised
-// output) for the merge kernel.
+// output) for the merge kernel, with non-temporal stores.
 //
 // Counters.  The copies are issued from inline assembly and waited for
 // explicitly (s_waitcnt vmcnt with the number of younger copies): the compiler
