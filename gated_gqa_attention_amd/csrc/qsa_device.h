@@ -200,7 +200,8 @@ __device__ __forceinline__ void put_row_bf16(unsigned char *tile, int rb, int ro
 struct Xch {
   static constexpr int PSTRIDE = 64 * 2 + 16;
   static constexpr int PBYTES = 4 * 16 * PSTRIDE;
-  static constexpr int BYTES = PBYTES + 2 * 4 * 64 * 4;
+  static constexpr int FLAGS = PBYTES + 2 * 4 * 64 * 4;    // after the block maxima and sums
+  static constexpr int BYTES = FLAGS + 16;
 };
 
 // One stage of up to 64 keys (global indices key0 ..) held in swizzled LDS
@@ -209,7 +210,11 @@ struct Xch {
 // through LDS and publish their probabilities as one bf16 tile; then each
 // wavefront accumulates its own D/4 output dims over all keys of the stage.
 // Key k is visible to row r when k < nkeys and key0 + k <= lim[r] (causal
-// limit n_b + l_r).  Contains two workgroup barriers; on_k_free runs right
+// limit n_b + l_r).  When every row already has a reference max, each wave
+// publishes its probabilities against it at once, with a flag if one of its
+// block maxima passes it by more than kMaxLead; only then is the stage
+// published again from the agreed maxima.  So a stage holds one workgroup
+// barrier, two on its first keys or when the reference moves; on_k_free runs
 // after the first, when no wave reads the K tile any more.
 constexpr float kMaxLead = 8.f;
 
@@ -244,6 +249,7 @@ __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsi
     }
   }
   float sc[RTM][4];
+  bool fresh = false, lifts = false;
 #pragma unroll
   for (int rt = 0; rt < RTM; ++rt) {
     // keys j of this wavefront with j < vis are visible to the lane's row
@@ -257,9 +263,12 @@ __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsi
     }
     bm = rows4_max(bm);
     if (g4 == 0) wmax[wave * 64 + 16 * rt + m16] = bm;
+    fresh |= m[rt] == -INFINITY;
+    lifts |= bm > m[rt] + kMaxLead;
   }
-  lds_barrier();
-  on_k_free();                                          // every wave is done with the K tile
+  // every wave holds the same reference max per row, so fresh is the same in all
+  fresh = __any(fresh);
+  int *const wflag = (int *)(xch + Xch::FLAGS);
 
   // reference max of each row, probabilities, block sums.  The reference max
   // moves only when the stage max passes it by more than kMaxLead (log2
@@ -268,28 +277,50 @@ __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsi
   // merge receives.  exp2 is v_exp_f32 (results below 2^-126 flush to zero).
   float alpha[RTM];
   bool rescale = false;
+  auto publish = [&](bool agreed) {                     // agreed: from the four block maxima
 #pragma unroll
-  for (int rt = 0; rt < RTM; ++rt) {
-    const int row = 16 * rt + m16;
-    const float M = fmaxf(fmaxf(wmax[row], wmax[64 + row]), fmaxf(wmax[128 + row], wmax[192 + row]));
-    const bool grow = M > m[rt] + kMaxLead;             // also when m is -inf and M is finite
-    const float mn = grow ? M : m[rt];
-    const float mu = mn == -INFINITY ? 0.f : mn;
-    alpha[rt] = __builtin_amdgcn_exp2f(m[rt] - mu);
-    rescale |= grow && m[rt] != -INFINITY;
-    m[rt] = mn;
-    float ps = 0.f;
-    bf16x4 pv;
+    for (int rt = 0; rt < RTM; ++rt) {
+      const int row = 16 * rt + m16;
+      float mu = m[rt];
+      alpha[rt] = 1.f;
+      if (agreed) {
+        const float M = fmaxf(fmaxf(wmax[row], wmax[64 + row]), fmaxf(wmax[128 + row], wmax[192 + row]));
+        const bool grow = M > m[rt] + kMaxLead;         // also when m is -inf and M is finite
+        const float mn = grow ? M : m[rt];
+        mu = mn == -INFINITY ? 0.f : mn;
+        alpha[rt] = __builtin_amdgcn_exp2f(m[rt] - mu);
+        rescale |= grow && m[rt] != -INFINITY;
+        m[rt] = mn;
+      }
+      float ps = 0.f;
+      bf16x4 pv;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pv[i] = (bf16_t)__builtin_amdgcn_exp2f(sc[rt][i] - mu);
-      ps += (float)pv[i];
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = (bf16_t)__builtin_amdgcn_exp2f(sc[rt][i] - mu);
+        ps += (float)pv[i];
+      }
+      *(bf16x4 *)(xch + (16 * rt + m16) * Xch::PSTRIDE + 2 * (16 * wave + 4 * g4)) = pv;
+      ps = rows4_sum(ps);
+      if (g4 == 0) wsum[wave * 64 + row] = ps;
     }
-    *(bf16x4 *)(xch + (16 * rt + m16) * Xch::PSTRIDE + 2 * (16 * wave + 4 * g4)) = pv;
-    ps = rows4_sum(ps);
-    if (g4 == 0) wsum[wave * 64 + row] = ps;
+  };
+  if (fresh) {
+    lds_barrier();
+    on_k_free();                                        // every wave is done with the K tile
+    publish(true);
+    lds_barrier();
+  } else {
+    // against the current reference (alpha = 1, the same values as publish(true)
+    // gives when no row's reference moves)
+    if (lane == 0) wflag[wave] = __any(lifts) ? 1 : 0;
+    publish(false);
+    lds_barrier();
+    on_k_free();
+    if (wflag[0] | wflag[1] | wflag[2] | wflag[3]) {    // the same in every wave
+      publish(true);                                    // each wave rewrites only its own columns and sums
+      lds_barrier();
+    }
   }
-  lds_barrier();
 #pragma unroll
   for (int rt = 0; rt < RTM; ++rt) {
     const int row = 16 * rt + m16;
