@@ -145,6 +145,10 @@ def test_parity_small(w, splits):
     # short-query route (one new row per sequence)
     Workload("bf16_dominant_decode", batch=2, q_len=1, num_q_heads=8, num_kv_heads=2, head_dim=256,
              rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=400, seed=116),
+    # short-query route at three row tiles (verify shape): with 3 splits a chunk holds
+    # several stages, so a later stage moves a reference max that is already set
+    Workload("bf16_dominant_verify", batch=2, q_len=4, num_q_heads=24, num_kv_heads=2, head_dim=256,
+             rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=400, seed=126),
     # tile route (160 rows)
     Workload("bf16_dominant_prefill", batch=1, q_len=40, num_q_heads=8, num_kv_heads=2, head_dim=256,
              rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=300, seed=115),
