@@ -134,6 +134,31 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(Params p) {
   const int row0 = tile * prows;
   const int R = min(prows, L * Gq - row0);
   if (rr >= R) return;
+  // Every load whose address does not wait on the sequence length goes out
+  // first, in the round trip of the length itself: the gate and the
+  // statistics and outputs of the first PF chunks of the grid (those past the
+  // sequence's own chunk count are read but not used).
+  constexpr int PF = 4;
+  const int64_t base = slot * pch * prows + rr;         // + c * rows
+  const int rg = row0 + rr, l = rg / Gq, h = kvh * Gq + rg % Gq;
+  const bf16_t *zp = q_gate + (((int64_t)b * L + l) * Hq + h) * 2 * D + D + lane * EPL;
+  float z[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) z[j] = (float)zp[j];
+  // unconditional, at clamped (in-range) chunks, and held in place by an empty
+  // asm with a memory clobber, so that the compiler issues them all here
+  float pm[PF], pl[PF], pv[PF][EPL];
+#pragma unroll
+  for (int c = 0; c < PF; ++c) {
+    const int cc = min(c, pch - 1);
+    const float *ml = part_ml + (base + (int64_t)cc * prows) * 2;
+    const float *po = part_o + (base + (int64_t)cc * prows) * D + lane * EPL;
+    pm[c] = ml[0];
+    pl[c] = ml[1];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) pv[c][j] = po[j];
+  }
+  asm volatile("" ::: "memory");
   const int n = seq_lens[b];
   const int64_t off = seq_offset[b];
   const int cap = capp ? capp[b] : 0x7fffffff;
@@ -142,20 +167,26 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(Params p) {
     return;                                             // the attention kernel wrote NaN
   const int nch = tile_chunk_count((int64_t)n + (row0 + R - 1) / Gq + 1, even, pch, ck);
   if (nch == 1) return;                                 // finished by the attention kernel
-  const int64_t base = slot * pch * prows + rr;         // + c * rows
-  const int rg = row0 + rr, l = rg / Gq, h = kvh * Gq + rg % Gq;
-  const bf16_t *zp = q_gate + (((int64_t)b * L + l) * Hq + h) * 2 * D + D + lane * EPL;
-  float z[EPL];
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) z[j] = (float)zp[j];
   float M = -INFINITY;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, part_ml[(base + (int64_t)c * prows) * 2]);
+#pragma unroll
+  for (int c = 0; c < PF; ++c)
+    if (c < nch) M = fmaxf(M, pm[c]);
+  for (int c = PF; c < nch; ++c) M = fmaxf(M, part_ml[(base + (int64_t)c * prows) * 2]);
   float lsum = 0.f, acc[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
-  for (int c = 0; c < nch; ++c) {
+#pragma unroll
+  for (int c = 0; c < PF; ++c) {
+    if (c < nch) {
+      const float wc = exp2f(pm[c] - M);                // a chunk whose rows saw no key has m = -inf: weight 0
+      lsum += wc * pl[c];
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) acc[j] += wc * pv[c][j];
+    }
+  }
+  for (int c = PF; c < nch; ++c) {
     const float *ml = part_ml + (base + (int64_t)c * prows) * 2;
-    const float wc = exp2f(ml[0] - M);                  // a chunk whose rows saw no key has m = -inf: weight 0
+    const float wc = exp2f(ml[0] - M);
     lsum += wc * ml[1];
     const float *po = part_o + (base + (int64_t)c * prows) * D + lane * EPL;
 #pragma unroll
