@@ -194,6 +194,59 @@ __device__ __forceinline__ void put_row_bf16(unsigned char *tile, int rb, int ro
 }
 
 
+// RMS norm of one head row held by 16 lanes (E = D/16 elements each, lane
+// c16 holding elements E c16 .. E c16 + E - 1): x * w / sqrt(mean(x^2) + eps)
+// (mlxd PR #99, config audit table, has_qk_norm; Atlas FullAttentionLayer
+// q_norm / k_norm).  A row that is not valid becomes zero.
+template <int D>
+__device__ __forceinline__ void row_norm(float (&x)[D / 16], const float (&w)[D / 16], bool valid, float eps) {
+  constexpr int E = D / 16;
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < E; ++j) ss += x[j] * x[j];
+  ss = row16_sum(ss);
+  const float inv = valid ? 1.0f / sqrtf(ss / (float)D + eps) : 0.f;
+#pragma unroll
+  for (int j = 0; j < E; ++j) x[j] = x[j] * inv * w[j];
+}
+
+// row_norm, then the partial rotation of the first r dims, dim i paired with
+// dim i + r/2 (mlxd PR #99 Summary, partial_rotary_factor; Atlas
+// Qwen35ForwardConfig::rotary_dim).  cs: (cos, sin) of this row's position for
+// pairs 0 .. r/2-1, 16-byte aligned.  Only rotary dims with r/2 a multiple of
+// E are taken here, so every rotated lane holds E elements of one half, its
+// partner lane is r/(2E) lanes away in the same row, and its pairs are the E
+// consecutive pairs from i0: the partner values come over by lane permutes and
+// the pair table is read as whole vectors.  Every lane of the wavefront must
+// take part.  This is the one routine that normalises and rotates new keys
+// before they are stored, whichever entry point stores them.
+template <int D>
+__device__ __forceinline__ void norm_rope(float (&x)[D / 16], const float (&w)[D / 16], bool valid, float eps,
+                                          int r, const float2 *cs) {
+  constexpr int E = D / 16;
+  const int lane = threadIdx.x % kWave, c16 = lane & 15;
+  row_norm<D>(x, w, valid, eps);
+  if (r == 0) return;
+  const int half = r / 2, e0 = c16 * E, nl = half / E;
+  const bool lo = e0 < half, rot = e0 < r;
+  const int src = rot ? (lo ? lane + nl : lane - nl) : lane;
+  float xp[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) xp[j] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(x[j])));
+  if (!rot) return;
+  const int i0 = lo ? e0 : e0 - half;
+  float4 cs4[E / 2];
+#pragma unroll
+  for (int j = 0; j < E / 2; ++j) cs4[j] = *(const float4 *)(cs + i0 + 2 * j);
+  const float sg = lo ? -1.f : 1.f;                     // lo: x c - x' s; hi: x c + x' s
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const float cj = j % 2 == 0 ? cs4[j / 2].x : cs4[j / 2].z;
+    const float sj = j % 2 == 0 ? cs4[j / 2].y : cs4[j / 2].w;
+    x[j] = fmaf(sg * xp[j], sj, x[j] * cj);
+  }
+}
+
 // Exchange area of one stage: the probability tile P[row tile][row][key] in
 // bf16 (row stride padded to 144 bytes, conflict-free for the 16-byte reads
 // of the value product) and each wavefront's block maxima and sums per row.

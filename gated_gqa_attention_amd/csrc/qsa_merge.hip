@@ -81,12 +81,18 @@ __global__ __launch_bounds__(kWave) void combine_kernel(const int32_t *__restric
     acc.w *= alpha;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-      // the weight of chunk c0 + q + 4 j, from the lane that holds its statistics
+      // the weight of chunk c0 + q + 4 j, from the lane that holds its statistics;
+      // chunks past the sequence's count were loaded at a clamped index (or, in the
+      // first batch, before the count was known) and are left out by a select, not
+      // by a zero weight, so that whatever an earlier call left there cannot reach
+      // the sum (0 * inf is NaN)
       const float w = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (q + 4 * j), __float_as_int(wc)));
-      acc.x += w * v[j].x;
-      acc.y += w * v[j].y;
-      acc.z += w * v[j].z;
-      acc.w += w * v[j].w;
+      if (c0 + q + 4 * j < nch) {
+        acc.x += w * v[j].x;
+        acc.y += w * v[j].y;
+        acc.z += w * v[j].z;
+        acc.w += w * v[j].w;
+      }
     }
     M = Mn;
   }

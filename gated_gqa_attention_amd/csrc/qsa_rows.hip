@@ -10,22 +10,29 @@
 
 namespace qsa {
 
-// One workgroup per new row (b, l): it tabulates the (cos, sin) of the row's
-// position once, then its four wavefronts walk the row's heads, one head-row
-// per wavefront at a time, EPL = D/64 contiguous elements per lane.  Heads
-// [0, nk) are key heads: normalised, rotated, rounded and written with the
-// matching value row to the cache.  Heads [nk, nk+nq) are query heads:
-// normalised and rotated into the prepared-query buffer p.qt (element type TQ).
+// One workgroup per new row (b, l).  It tabulates the (cos, sin) of the row's
+// position once; then every 16 lanes take one head row, lane c16 holding the
+// E = D/16 contiguous elements E c16 .., so that a wavefront works on four head
+// rows at a time.  Heads [0, nk) are key heads: normalised, rotated, rounded
+// and written with the matching value row to the cache.  Heads [nk, nk+nq) are
+// query heads: normalised and rotated into the prepared-query buffer p.qt
+// (element type TQ).  The norm and the rotation are norm_rope, the routine the
+// short-query kernel runs on the new keys of a fused call, with the same table
+// and the same reduction order, so the cache rows written here are bitwise the
+// rows that a fused call writes.  A rotation whose halves do not start on a
+// lane boundary (r/2 not a multiple of E, which the short-query route never
+// takes) goes through an LDS copy of the row instead.
 template <typename T, typename TQ, int D>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(Params p, int do_q, int do_kv) {
-  constexpr int EPL = D / kWave;
-  __shared__ float scratch[kThreads / kWave][D];
-  __shared__ float2 cs[kMaxPairs];
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  constexpr int E = D / 16, ROWS = kThreads / 16;
+  __shared__ float scratch[ROWS][D];
+  __shared__ __attribute__((aligned(16))) float2 cs[kMaxPairs];
+  const int m16 = threadIdx.x & 15, hr = threadIdx.x / 16;   // head-row slot of these 16 lanes
   const int64_t bl = blockIdx.x;                        // new row (b, l)
   const int b = (int)(bl / p.L), l = (int)(bl % p.L);
-  const int nk = do_kv ? p.Hkv : 0, nq = do_q ? p.Hq : 0;
+  const int nk = do_kv ? p.Hkv : 0, nq = do_q ? p.Hq : 0, njobs = nk + nq;
   const int r = p.r, half = r / 2;
+  const bool whole = half % E == 0;
   if (r > 0) {
     const int pos = p.positions[bl];
     for (int i = threadIdx.x; i < half; i += kThreads) {
@@ -35,59 +42,63 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(Params p, int do_q, 
     }
   }
   __syncthreads();
+  int n = 0;
+  int64_t off = 0;
+  bool kv_ok = true;
+  if (nk) kv_ok = seq_in_range(p, b, n = p.seq_lens[b], off);
+  if (!kv_ok && threadIdx.x == 0) flag_error(p);
 
-  for (int job = wave; job < nk + nq; job += kThreads / kWave) {
-    const bool is_k = job < nk;
-    const int head = is_k ? job : job - nk;
+  // every lane runs every pass (the rotation permutes across lanes); rows past
+  // the last job take a clamped row and are not stored
+  for (int j0 = 0; j0 < njobs; j0 += ROWS) {
+    const int job = j0 + hr;
+    const bool valid = job < njobs;
+    const int jb = valid ? job : njobs - 1;
+    const bool is_k = jb < nk;
+    const int head = is_k ? jb : jb - nk;
     const T *src = is_k ? (const T *)p.k_new + (bl * p.Hkv + head) * D
                         : (const T *)p.q_gate + (bl * p.Hq + head) * 2 * D;   // query half of [q | gate]
-    const T *w = is_k ? (const T *)p.wk : (const T *)p.wq;
-    float x[EPL];
-    float ss = 0.f;
+    const T *wp = is_k ? (const T *)p.wk : (const T *)p.wq;
+    float x[E], w[E];
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      x[j] = to_f(src[lane * EPL + j]);
-      ss += x[j] * x[j];
+    for (int j = 0; j < E; ++j) {
+      x[j] = to_f(src[E * m16 + j]);
+      w[j] = to_f(wp[E * m16 + j]);
     }
-    ss = rows4_sum(row16_sum(ss));
-    const float inv = 1.0f / sqrtf(ss / (float)D + p.eps);
+    if (whole) {
+      norm_rope<D>(x, w, valid, p.eps, r, cs);
+    } else {
+      row_norm<D>(x, w, valid, p.eps);
+      // partner i +- r/2 of each rotated element, through this row's scratch copy
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) x[j] = x[j] * inv * to_f(w[lane * EPL + j]);
-    if (r > 0) {
-      // partner i +- r/2 of each rotated element, through this wavefront's scratch row
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) scratch[wave][lane * EPL + j] = x[j];
+      for (int j = 0; j < E; ++j) scratch[hr][E * m16 + j] = x[j];
       wave_lds_sync();
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) {
-        const int e = lane * EPL + j;
+      for (int j = 0; j < E; ++j) {
+        const int e = E * m16 + j;
         if (e < r) {
           const bool lo = e < half;
           const float2 v = cs[lo ? e : e - half];
-          const float other = scratch[wave][lo ? e + half : e - half];
+          const float other = scratch[hr][lo ? e + half : e - half];
           x[j] = lo ? x[j] * v.x - other * v.y : x[j] * v.x + other * v.y;
         }
       }
+      wave_lds_sync();                                  // the next pass rewrites the scratch row
     }
+    if (!valid) continue;
     if (is_k) {
-      const int n = p.seq_lens[b];
-      int64_t off;
-      if (!seq_in_range(p, b, n, off)) {
-        if (lane == 0) flag_error(p);
-        continue;
-      }
-      const int64_t dst = ((off + n + l) * p.Hkv + head) * D;
-      const T *vsrc = (const T *)p.v_new + (bl * p.Hkv + head) * D;
+      if (!kv_ok) continue;
+      const int64_t dst = ((off + n + l) * p.Hkv + head) * D + E * m16;
+      const T *vsrc = (const T *)p.v_new + (bl * p.Hkv + head) * D + E * m16;
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) {
-        const int e = lane * EPL + j;
-        ((T *)p.kc)[dst + e] = from_f<T>(x[j]);
-        ((T *)p.vc)[dst + e] = vsrc[e];
+      for (int j = 0; j < E; ++j) {
+        ((T *)p.kc)[dst + j] = from_f<T>(x[j]);
+        ((T *)p.vc)[dst + j] = vsrc[j];
       }
     } else {
-      TQ *dst = (TQ *)p.qt + (bl * p.Hq + head) * D;
+      TQ *dst = (TQ *)p.qt + (bl * p.Hq + head) * D + E * m16;
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) dst[lane * EPL + j] = from_f<TQ>(x[j]);
+      for (int j = 0; j < E; ++j) dst[j] = from_f<TQ>(x[j]);
     }
   }
 }

@@ -19,9 +19,11 @@
 // sequence, the new keys.  Those are attended before the cached stages, from
 // a free ring slot or (several row tiles) from the arena, by each wavefront on
 // its own; a single new key only sets the running state.  With one row tile
-// and no free slot they follow the cached stages instead.  Either way they
-// are appended to the cache at the end (Atlas qwen3_5/mod.rs module doc:
-// append at cache_pos, attend over cache_pos + 1 keys).
+// and no free slot they follow the cached stages instead.  A call that is
+// given k_new appends them to the cache at the end (Atlas qwen3_5/mod.rs
+// module doc: append at cache_pos, attend over cache_pos + 1 keys); a call on
+// rows already appended loads them from the cache into the same place and
+// attends them the same way, so the two compute bitwise the same outputs.
 //
 // Compute (the stage step in qsa_device.h).  Wavefront w scores keys
 // 16 w .. 16 w + 15 of the stage against every row tile,
@@ -46,46 +48,6 @@
 namespace qsa {
 
 namespace {
-
-// RMS norm and partial rotation of one head row held by 16 lanes (E elements
-// each, lane c16 holds elements E*c16 .. E*c16+E-1).  cs: (cos, sin) of this
-// row's position for pairs 0 .. r/2-1, 16-byte aligned.  The route admits only
-// rotary dims with r/2 a multiple of E, so every rotated lane holds E elements
-// of one half, its partner lane is r/(2E) lanes away in the same row, and its
-// pairs are the E consecutive pairs from i0: the partner values come over by
-// lane permutes and the pair table is read as whole vectors.
-template <int D>
-__device__ __forceinline__ void norm_rope(float (&x)[D / 16], const float (&w)[D / 16], bool valid, float eps,
-                                          int r, const float2 *cs) {
-  constexpr int E = D / 16;
-  const int lane = threadIdx.x % kWave, c16 = lane & 15;
-  float ss = 0.f;
-#pragma unroll
-  for (int j = 0; j < E; ++j) ss += x[j] * x[j];
-  ss = row16_sum(ss);
-  const float inv = valid ? 1.0f / sqrtf(ss / (float)D + eps) : 0.f;
-#pragma unroll
-  for (int j = 0; j < E; ++j) x[j] = x[j] * inv * w[j];
-  if (r == 0) return;
-  const int half = r / 2, e0 = c16 * E, nl = half / E;
-  const bool lo = e0 < half, rot = e0 < r;
-  const int src = rot ? (lo ? lane + nl : lane - nl) : lane;
-  float xp[E];
-#pragma unroll
-  for (int j = 0; j < E; ++j) xp[j] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(x[j])));
-  if (!rot) return;
-  const int i0 = lo ? e0 : e0 - half;
-  float4 cs4[E / 2];
-#pragma unroll
-  for (int j = 0; j < E / 2; ++j) cs4[j] = *(const float4 *)(cs + i0 + 2 * j);
-  const float sg = lo ? -1.f : 1.f;                     // lo: x c - x' s; hi: x c + x' s
-#pragma unroll
-  for (int j = 0; j < E; ++j) {
-    const float cj = j % 2 == 0 ? cs4[j / 2].x : cs4[j / 2].z;
-    const float sj = j % 2 == 0 ? cs4[j / 2].y : cs4[j / 2].w;
-    x[j] = fmaf(sg * xp[j], sj, x[j] * cj);
-  }
-}
 
 // Waits until at most u * LPS vector-memory operations of this wave are
 // outstanding (u wave-uniform, 0 <= u <= U).
@@ -221,9 +183,14 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   }
   const int64_t k0 = chunk_begin(kend, even, nch, ck, chunk);
   const int64_t k1 = chunk == nch - 1 ? kend : chunk_begin(kend, even, nch, ck, chunk + 1);
+  // The new keys n .. n + L - 1 are attended by the last chunk's workgroup,
+  // the same way whether this call appends them (k_new given) or they are
+  // already in the cache: then its prep waves load the stored rows instead of
+  // normalising and rotating k_new, and the call computes bitwise what it
+  // computes when it appends them itself.
   const bool fuse_new = knew != nullptr;
-  const bool tail = fuse_new && chunk == nch - 1;       // this workgroup holds the new keys
-  const int64_t cend = fuse_new ? min(k1, (int64_t)n) : k1;   // cached keys [k0, cend)
+  const bool tail = chunk == nch - 1;                   // this workgroup holds the new keys
+  const int64_t cend = min(k1, (int64_t)n);             // cached keys [k0, cend)
   const int nst = cend > k0 ? (int)((cend - k0 + G::SK - 1) / G::SK) : 0;
 
   // ------------------------------------------------------------ ring fill
@@ -283,11 +250,17 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int l = min(8 * k + nr, L - 1);
-      const int64_t src = (((int64_t)b * L + l) * hkv + kvh) * D + E * m16;
-      knraw[k].load(knew + src);
-      vnraw[k].load(vnew + src);
+      if (fuse_new) {
+        const int64_t src = (((int64_t)b * L + l) * hkv + kvh) * D + E * m16;
+        knraw[k].load(knew + src);
+        vnraw[k].load(vnew + src);
+      } else {                                          // rows n + l of the cache (in range: checked above)
+        const int64_t src = ((off + n + l) * hkv + kvh) * D + E * m16;
+        knraw[k].load(kc + src);
+        vnraw[k].load(vc + src);
+      }
     }
-    wkraw.load(wkp + E * m16);
+    if (fuse_new) wkraw.load(wkp + E * m16);
   }
   lds_barrier();
   if (copier) {
@@ -375,13 +348,18 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     }
     if (tail) {
       float wk[E];
-      wkraw.to_float(wk);
+      if (fuse_new) wkraw.to_float(wk);
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int l = 8 * k + nr;
         if (8 * k + 4 * (pw ^ 1) < L) {                 // the pass holds a new row (wave-uniform)
           knraw[k].to_float(kx[k]);
-          norm_rope<D>(kx[k], wk, l < L, eps, 2 * half, tabw + min(l, L - 1) * half);   // rows >= L become zero
+          if (fuse_new) {
+            norm_rope<D>(kx[k], wk, l < L, eps, 2 * half, tabw + min(l, L - 1) * half);   // rows >= L become zero
+          } else if (l >= L) {
+#pragma unroll
+            for (int j = 0; j < E; ++j) kx[k][j] = 0.f;
+          }
         } else {
 #pragma unroll
           for (int j = 0; j < E; ++j) kx[k][j] = 0.f;
@@ -550,7 +528,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   }
 
   // ------------------------------------------------------------ append the new rows to the cache
-  if (tail) {
+  if (tail && fuse_new) {
     for (int u = t; u < 16 * G::OCT; u += kThreads) {
       const int l = u / G::OCT, oct = u % G::OCT;
       if (l < L) {

@@ -11,8 +11,9 @@ from .workloads import DTYPES, Workload
 
 class Session:
     def __init__(self, w: Workload, inputs: dict, device="cuda", force_splits: int = 0,
-                 max_seq_len: int | None = None, stream=None):
+                 max_seq_len: int | None = None, stream=None, softmax_scale: float = 0.0):
         self.w = w
+        self.softmax_scale = softmax_scale
         self.dev = {k: v.to(device) if isinstance(v, torch.Tensor) else v for k, v in inputs.items()}
         d = self.dev
         if max_seq_len is None:
@@ -35,13 +36,21 @@ class Session:
             batch=w.batch, q_len=w.q_len, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
             head_dim=w.head_dim, rotary_dim=w.rotary_dim, rope_theta=w.rope_theta, rms_eps=w.rms_eps,
             dtype=self.dtype, max_seq_len=self.max_seq_len, q_norm_w=d["w_q"], k_norm_w=d["w_k"],
-            workspace=workspace, force_splits=self.force_splits, stream=self.stream)
+            workspace=workspace, force_splits=self.force_splits, stream=self.stream,
+            softmax_scale=self.softmax_scale)
 
     def plan(self) -> str:
         return binding.describe_plan(self.cfg)
 
     def run(self, fused: bool = True):
+        """One call.  The output buffer is filled with NaN first, so an output
+        element that the call fails to write cannot pass for a result."""
         d = self.dev
+        if self.stream is None:
+            self.out.fill_(float("nan"))
+        else:
+            with torch.cuda.stream(self.stream):
+                self.out.fill_(float("nan"))
         binding.gated_attention(self.cfg, self.kv, d["q_gate"], d["k_new"] if fused else None,
                                 d["v_new"] if fused else None, d["seq_lens"], d["positions"], self.out)
         return self.out

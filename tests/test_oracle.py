@@ -168,13 +168,18 @@ def test_kv_rows_match_torch_rms_norm():
     assert np.array_equal(vr, inp["v_new"].double().numpy())
 
 
-def test_attention_core_matches_torch_sdpa():
-    """With every position 0 the rotation is the identity; q~ is then torch's rms_norm."""
+@pytest.mark.parametrize("scale", [0.0, 0.37, 0.021])
+def test_attention_core_matches_torch_sdpa(scale):
+    """With every position 0 the rotation is the identity; q~ is then torch's
+    rms_norm.  softmax_scale = 0 selects 1/sqrt(head_dim) (torch's default);
+    any other value is passed to torch as its scale."""
     w = Workload("sdpa", batch=2, q_len=3, num_q_heads=6, num_kv_heads=2, head_dim=64,
                  rotary_dim=16, rope_theta=1e4, dtype="f32", prior=7, seed=32)
     inp = make_inputs(w)
     inp["positions"].zero_()
-    _, _, _, att = run(w, inp, dtype="f64", want_attn=True, fused=False)
+    g = geo(w, "f64")
+    g.softmax_scale = scale
+    _, _, _, att = oracle.gated_attention(g, inp, want_attn=True, fused=False)
     D, G, L = w.head_dim, w.group, w.q_len
     for b in range(w.batch):
         n, off = int(inp["seq_lens"][b]), int(inp["seq_offset"][b])
@@ -187,8 +192,12 @@ def test_attention_core_matches_torch_sdpa():
             mask[l, :n + l + 1] = True
         ref = torch.nn.functional.scaled_dot_product_attention(
             q.transpose(0, 1), k.transpose(0, 1).contiguous(), v.transpose(0, 1).contiguous(),
-            attn_mask=mask)
+            attn_mask=mask, scale=scale if scale > 0 else None)
         assert np.max(np.abs(att[b] - ref.transpose(0, 1).numpy())) < 1e-12
+    if scale > 0:                       # the scale is not ignored
+        g.softmax_scale = 0.0
+        _, _, _, att0 = oracle.gated_attention(g, inp, want_attn=True, fused=False)
+        assert rel_l2(att0, att) > 1e-2
 
 
 # ---------------------------------------------------------------- closed forms
