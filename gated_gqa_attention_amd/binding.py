@@ -18,8 +18,9 @@ QSA_OK, QSA_ERR_INVALID, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE, QSA_ERR_DEVICE 
 QSA_BF16, QSA_F32 = 0, 1
 _DT = {torch.bfloat16: QSA_BF16, torch.float32: QSA_F32}
 
-EXPORTS = ("qsa_workspace_size", "qsa_append_kv", "qsa_gated_attention", "qsa_describe_plan",
-           "qsa_last_error")
+EXPORTS = ("qsa_workspace_size", "qsa_append_kv", "qsa_gated_attention", "qsa_gated_attention_noalloc",
+           "qsa_describe_plan", "qsa_last_error")
+NOALLOC_SCRATCH_BYTES = 64 << 20     # QSA_NOALLOC_SCRATCH_BYTES
 
 
 class QSAError(RuntimeError):
@@ -73,6 +74,9 @@ def load():
         lib.qsa_gated_attention.restype = ctypes.c_int
         lib.qsa_gated_attention.argtypes = [p, p, p, ctypes.POINTER(KVCache), p, p,
                                             ctypes.POINTER(Cfg), p]
+        lib.qsa_gated_attention_noalloc.restype = ctypes.c_int
+        lib.qsa_gated_attention_noalloc.argtypes = [p, p, p, ctypes.POINTER(KVCache), p, p,
+                                                    ctypes.POINTER(Cfg), p]
         lib.qsa_describe_plan.restype = ctypes.c_int
         lib.qsa_describe_plan.argtypes = [ctypes.POINTER(Cfg), ctypes.c_char_p, ctypes.c_size_t]
         lib.qsa_last_error.restype = ctypes.c_char_p
@@ -141,3 +145,11 @@ def append_kv(cfg: Cfg, kv: KVCache, k_new, v_new, seq_lens, positions) -> None:
 def gated_attention(cfg: Cfg, kv: KVCache, q_gate, k_new, v_new, seq_lens, positions, out) -> None:
     _check(load().qsa_gated_attention(_ptr(q_gate), _ptr(k_new), _ptr(v_new), ctypes.byref(kv),
                                       _ptr(seq_lens), _ptr(positions), ctypes.byref(cfg), _ptr(out)))
+
+
+def gated_attention_noalloc(cfg: Cfg, kv: KVCache, q_gate, k_new, v_new, seq_lens, positions, out) -> None:
+    """qsa_gated_attention_noalloc: the library's own per-GPU scratch instead of
+    ``cfg.workspace`` (which is ignored)."""
+    _check(load().qsa_gated_attention_noalloc(_ptr(q_gate), _ptr(k_new), _ptr(v_new), ctypes.byref(kv),
+                                              _ptr(seq_lens), _ptr(positions), ctypes.byref(cfg),
+                                              _ptr(out)))

@@ -264,8 +264,16 @@ int qsa_append_kv(const void *k_new, const void *v_new, const qsa_kv_cache *kv, 
   return QSA_OK;
 }
 
-int qsa_gated_attention(const void *q_gate, const void *k_new, const void *v_new, const qsa_kv_cache *kv,
-                        const int32_t *seq_lens, const int32_t *positions, const qsa_cfg *cfg, void *out) {
+}  // extern "C"
+
+namespace {
+
+// Everything of qsa_gated_attention after the workspace has been chosen: ws
+// holds ws_bytes of device memory (the caller's workspace, or this device's
+// scratch array for the allocation-free entry point).
+int gated_attention_in(const void *q_gate, const void *k_new, const void *v_new, const qsa_kv_cache *kv,
+                       const int32_t *seq_lens, const int32_t *positions, const qsa_cfg *cfg, void *out,
+                       void *ws_ptr, size_t ws_bytes, const char *ws_name) {
   int rc = validate_cfg(cfg);
   if (rc != QSA_OK) return rc;
   if ((rc = check_kv(kv)) != QSA_OK) return rc;
@@ -284,9 +292,9 @@ int qsa_gated_attention(const void *q_gate, const void *k_new, const void *v_new
     return fail(QSA_ERR_INVALID, "out must not alias q_gate, k_new, v_new or the cache");
   Plan pl;
   if ((rc = make_plan(cfg, &pl)) != QSA_OK) return rc;
-  if (!cfg->workspace || cfg->workspace_bytes < pl.total)
-    return fail(QSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.total,
-                cfg->workspace ? cfg->workspace_bytes : (size_t)0);
+  if (!ws_ptr || ws_bytes < pl.total)
+    return fail(QSA_ERR_WORKSPACE, "%s of %zu bytes needed, %zu %s", ws_name, pl.total,
+                ws_ptr ? ws_bytes : (size_t)0, ws_ptr ? "available" : "given");
   if ((rc = check_device()) != QSA_OK) return rc;
 
   qsa::Params p = base_params(cfg, pl);
@@ -295,7 +303,7 @@ int qsa_gated_attention(const void *q_gate, const void *k_new, const void *v_new
   p.k_new = k_new;
   p.v_new = v_new;
   p.out = out;
-  char *ws = (char *)cfg->workspace;
+  char *ws = (char *)ws_ptr;
   p.err = (int32_t *)ws;
   p.part_ml = pl.off_ml ? (float *)(ws + pl.off_ml) : nullptr;
   p.part_o = pl.off_o ? (float *)(ws + pl.off_o) : nullptr;
@@ -326,6 +334,71 @@ int qsa_gated_attention(const void *q_gate, const void *k_new, const void *v_new
   }
   if (e != hipSuccess) return fail(QSA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
   return QSA_OK;
+}
+
+// Scratch of the allocation-free entry point: one array per device, part of
+// the library's code object, held until the process ends.  In host code its
+// name is only a handle: the device address comes from hipGetSymbolAddress.
+constexpr size_t kScratchBytes = (size_t)QSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+__global__ void zero_words(uint4 *p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// This device's scratch address, set up once per device: the symbol's address
+// on the current device, and the array cleared once by a fill kernel on the
+// caller's stream (the calls keep it in the state they found it in: the merge
+// counters return to zero at the end of every call).
+int scratch_for_current_device(hipStream_t s, void **ptr) {
+  static std::mutex mu;
+  static void *addr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(QSA_ERR_DEVICE, "no current HIP device (or device index past 63)");
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *a = nullptr;
+    hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !a)
+      return fail(QSA_ERR_DEVICE, "scratch array not available on device %d: %s", dev, hipGetErrorString(e));
+    hipLaunchKernelGGL(zero_words, dim3(1024), dim3(256), 0, s, (uint4 *)a, kScratchBytes / 16);
+    if ((e = hipGetLastError()) != hipSuccess)
+      return fail(QSA_ERR_DEVICE, "scratch clear failed on device %d: %s", dev, hipGetErrorString(e));
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return QSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qsa_gated_attention(const void *q_gate, const void *k_new, const void *v_new, const qsa_kv_cache *kv,
+                        const int32_t *seq_lens, const int32_t *positions, const qsa_cfg *cfg, void *out) {
+  if (!cfg) return fail(QSA_ERR_INVALID, "cfg is NULL");
+  return gated_attention_in(q_gate, k_new, v_new, kv, seq_lens, positions, cfg, out, cfg->workspace,
+                            cfg->workspace_bytes, "workspace");
+}
+
+int qsa_gated_attention_noalloc(const void *q_gate, const void *k_new, const void *v_new, const qsa_kv_cache *kv,
+                                const int32_t *seq_lens, const int32_t *positions, const qsa_cfg *cfg,
+                                void *out) {
+  int rc = validate_cfg(cfg);
+  if (rc != QSA_OK) return rc;
+  Plan pl;
+  if ((rc = make_plan(cfg, &pl)) != QSA_OK) return rc;
+  if (pl.total > kScratchBytes)
+    return fail(QSA_ERR_WORKSPACE,
+                "this call needs %zu bytes of scratch; the allocation-free entry point holds %zu "
+                "(use qsa_gated_attention with a workspace)", pl.total, kScratchBytes);
+  if ((rc = check_device()) != QSA_OK) return rc;
+  void *ws = nullptr;
+  if ((rc = scratch_for_current_device((hipStream_t)cfg->stream, &ws)) != QSA_OK) return rc;
+  return gated_attention_in(q_gate, k_new, v_new, kv, seq_lens, positions, cfg, out, ws, kScratchBytes,
+                            "scratch");
 }
 
 }  // extern "C"

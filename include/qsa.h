@@ -141,6 +141,27 @@ int qsa_gated_attention(const void *q_gate, const void *k_new, const void *v_new
                         const qsa_kv_cache *kv, const int32_t *seq_lens,
                         const int32_t *positions, const qsa_cfg *cfg, void *out);
 
+/* Bytes of device scratch that qsa_gated_attention_noalloc holds per GPU. */
+#define QSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* qsa_gated_attention without a caller workspace, for callers that cannot
+ * allocate device memory around the call: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, result
+ * and errors as qsa_gated_attention, except that cfg->workspace and
+ * cfg->workspace_bytes are ignored: the call uses a scratch array of
+ * QSA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends (set up, and cleared once, on the first call on that
+ * GPU, which must be current).  It calls no hipMalloc, hipFree or allocating
+ * routine.  A call whose plan needs more scratch than that returns
+ * QSA_ERR_WORKSPACE (qsa_workspace_size() tells the need).  Every call on one
+ * GPU shares that GPU's array: calls that may overlap on one GPU (different
+ * streams, no ordering between them) race and give wrong results.  Device-side
+ * range errors show as NaN outputs only (the error bits stay in the scratch
+ * array, which the caller cannot read). */
+int qsa_gated_attention_noalloc(const void *q_gate, const void *k_new, const void *v_new,
+                                const qsa_kv_cache *kv, const int32_t *seq_lens,
+                                const int32_t *positions, const qsa_cfg *cfg, void *out);
+
 /* Human-readable launch plan for cfg (route, chunking, grid), written to buf.
  * Returns the number of characters the full text needs, or a negative
  * qsa_status if cfg is invalid. */

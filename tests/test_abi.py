@@ -161,6 +161,31 @@ def test_argument_errors_before_launch():
         binding.QSA_ERR_INVALID
 
 
+def test_noalloc_entry_point_checks_before_any_launch():
+    """The allocation-free entry point validates like qsa_gated_attention and
+    rejects a plan that needs more than its fixed scratch (prefill_4b needs
+    about 80 MiB) with QSA_ERR_WORKSPACE, before touching a device."""
+    lib = binding.load()
+    kv = binding.KVCache(FAKE, FAKE + (1 << 30), FAKE, None, 1 << 20)
+    out = FAKE + (2 << 30)
+    big = cfg_for(WORKLOADS["prefill_4b"])
+    assert binding.workspace_size(big) > binding.NOALLOC_SCRATCH_BYTES
+    rc = lib.qsa_gated_attention_noalloc(FAKE, FAKE, FAKE, ctypes.byref(kv), FAKE, FAKE, ctypes.byref(big), out)
+    assert rc == binding.QSA_ERR_WORKSPACE
+    assert "scratch" in binding.last_error()
+    bad = cfg_for(WORKLOADS["decode_4b"], rotary_dim=63)
+    rc = lib.qsa_gated_attention_noalloc(FAKE, FAKE, FAKE, ctypes.byref(kv), FAKE, FAKE, ctypes.byref(bad), out)
+    assert rc == binding.QSA_ERR_INVALID
+    for name in ("decode_4b", "verify_24x2", "ragged_4b"):
+        assert binding.workspace_size(cfg_for(WORKLOADS[name])) <= binding.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(os.path.join(ROOT, "include", "qsa.h")).read()
+    m = re.search(r"#define QSA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.NOALLOC_SCRATCH_BYTES
+
+
 def test_workspace_scales_with_chunks():
     w = WORKLOADS["decode_4b"]
     one = binding.workspace_size(cfg_for(w, force_splits=1))
