@@ -199,47 +199,30 @@ def cpu_baseline(w, inputs, tokens_per_call, budget_s=10.0):
                   f"full append; scaled by rows")
         tokens = tokens_per_call * len(rows) / total_rows
     return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 3)}
+            "sample": sample, "seconds": round(dt, 3), "cpu_model": cpu_model()}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None)
-    ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode_4b", choices=sorted(WORKLOADS))
-    ap.add_argument("--launch", default="graph", choices=["graph", "eager"])
-    ap.add_argument("--force-splits", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sets", type=int, default=None, help="buffer sets to rotate over")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="time a plain 256 MiB device copy instead (reference for the HBM byte counters)")
-    args = ap.parse_args()
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the attention core shards by sequence or KV head without any exchange; see DESIGN.md)",
-              file=sys.stderr)
-        sys.exit(2)
-    if not torch.cuda.is_available():
-        print("bench.py: no GPU visible", file=sys.stderr)
-        sys.exit(2)
 
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    w = WORKLOADS[args.workload]
-    steps, warm = DEFAULT_STEPS.get(w.name, (100, 10))
-    steps = args.steps if args.steps is not None else steps
-    warm = args.warmup if args.warmup is not None else warm
+def measure(w, steps, warm, launch="graph", force_splits=0, sets=None):
+    """Time one workload: `warm` untimed eager calls, then `steps` calls captured in
+    one HIP graph, replayed once untimed and once timed (HIP events on the launch
+    stream), then the attention kernel on its own in an eager pass.  Returns the
+    inputs and a dict of figures."""
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
     inputs = make_inputs(w)
     max_seq_len = int((inputs["seq_lens"].max() + w.q_len).item())
     base = {k: v.to(dev) for k, v in inputs.items()}
     set_bytes = sum(v.numel() * v.element_size() for v in base.values())
-    sets = args.sets or max(1, min(256, -(-ROTATE_BYTES // set_bytes)))
+    sets = sets or max(1, min(256, -(-ROTATE_BYTES // set_bytes)))
     if set_bytes * sets > 64 * (1 << 30):
         sets = 1
     stream = torch.cuda.Stream()   # default priority
@@ -247,7 +230,7 @@ def main():
         batch=w.batch, q_len=w.q_len, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
         head_dim=w.head_dim, rotary_dim=w.rotary_dim, rope_theta=w.rope_theta, rms_eps=w.rms_eps,
         dtype=DTYPES[w.dtype], max_seq_len=max_seq_len, q_norm_w=base["w_q"], k_norm_w=base["w_k"],
-        force_splits=args.force_splits, stream=stream)
+        force_splits=force_splits, stream=stream)
     ws_bytes = binding.workspace_size(probe)
     plan = binding.describe_plan(probe)
 
@@ -256,7 +239,7 @@ def main():
         d = base if i == 0 else {k: v.clone() for k, v in base.items()}
         ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
         c = Call(w, d, ws, max_seq_len, stream)
-        c.cfg.force_splits = args.force_splits
+        c.cfg.force_splits = force_splits
         calls.append(c)
     torch.cuda.synchronize()
 
@@ -266,11 +249,14 @@ def main():
     torch.cuda.synchronize()
 
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if args.launch == "graph":
+    if launch == "graph":
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             for i in range(steps):
                 calls[(warm + i) % sets]()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):     # one untimed replay: the graph's first launch sets it up
+            graph.replay()
         torch.cuda.synchronize()
         t_host = time.perf_counter()
         with torch.cuda.stream(stream):     # replay() launches on the current stream
@@ -291,7 +277,7 @@ def main():
     ms = start.elapsed_time(end)
     errs = [int(c.ws[:4].view(torch.int32).item()) for c in calls]
     if any(errs):
-        print(f"bench.py: device-side range error flagged: {errs}", file=sys.stderr)
+        print(f"bench.py: device-side range error flagged on {w.name}: {errs}", file=sys.stderr)
         sys.exit(1)
 
     # the kernel that streams the KV cache, timed on its own in a separate eager pass
@@ -299,46 +285,115 @@ def main():
 
     tokens_per_call = w.batch * w.q_len
     bytes_call, out_bytes, flops_call = algorithmic_work(w, inputs["seq_lens"])
-    chunks = int(plan.split("chunks=")[1].split()[0])
-    bytes_kernel = bytes_call - (out_bytes if chunks > 1 else 0)
-    s_per_step = ms / 1e3 / steps
-    value = tokens_per_call / s_per_step
-    gbs = bytes_call / s_per_step / 1e9
-    tfs = flops_call / s_per_step / 1e12
-    k_s = kernel_ms / 1e3
-    hbm_bound = w.name != "prefill_4b"
-    route = plan.split("route=")[1].split()[0]
-    traffic = traffic_from_profiles(w.name, route) if route in ROUTE_SOURCES else None
-    kname = {"fused_splitk": "stream_kernel", "prepared_tiles": "tile_kernel"}.get(route, "rows_f32_kernel")
+    fields = dict(kv.split("=") for kv in plan.split())
+    route = fields["route"]
+    # bytes the streaming kernel moves: all of the call's, except the output when a
+    # separate merge kernel writes it
+    merged_apart = int(fields["chunks"]) > 1 and fields.get("merge") == "kernel"
+    bytes_kernel = bytes_call - (out_bytes if merged_apart else 0)
+    step_s = ms / 1e3 / steps
+    hbm_bound = route != "prepared_tiles"
     if hbm_bound:
-        ach = bytes_kernel / k_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
+        call_ach, kern_ach = bytes_call / step_s / 1e9, bytes_kernel / (kernel_ms / 1e3) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
     else:
-        ach = flops_call / k_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFS,
-                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic}
-    roof.update({"kernel": kname, "kernel_us": round(kernel_ms * 1e3, 3),
-                 "algorithmic_bytes_per_launch": bytes_kernel,
-                 "algorithmic_flops_per_launch": flops_call,
-                 "kernel_share_of_step": round(kernel_ms / (ms / steps), 3)})
+        call_ach, kern_ach = flops_call / step_s / 1e12, flops_call / (kernel_ms / 1e3) / 1e12
+        peak, unit = MFMA_BF16_PEAK_TFS, "TFLOP/s"
+    kname = {"fused_splitk": "stream_kernel", "prepared_tiles": "tile_kernel"}.get(route, "rows_f32_kernel")
+    res = {
+        "steps": steps, "warmup": warm, "ms_per_step": ms / steps, "tokens_per_s": tokens_per_call / step_s,
+        "effective_gbs": bytes_call / step_s / 1e9, "effective_tflops": flops_call / step_s / 1e12,
+        "host_wall_s": t_host, "plan": plan, "route": route, "buffer_sets": sets,
+        "bound": "hbm" if hbm_bound else "mfma", "unit": unit, "peak": peak,
+        "call_achieved": call_ach, "call_frac": call_ach / peak,
+        "kernel": kname, "kernel_us": kernel_ms * 1e3, "kernel_achieved": kern_ach,
+        "kernel_frac": kern_ach / peak, "bytes_call": bytes_call, "bytes_kernel": bytes_kernel,
+        "flops_call": flops_call, "tokens_per_call": tokens_per_call,
+        "cached_tokens": int(inputs["seq_lens"].sum()),
+    }
+    del calls, base
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return inputs, res
 
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode_4b", choices=sorted(WORKLOADS))
+    ap.add_argument("--launch", default="graph", choices=["graph", "eager"])
+    ap.add_argument("--force-splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only --workload (by default the other bf16 workloads follow as extra keys)")
+    ap.add_argument("--sets", type=int, default=None, help="buffer sets to rotate over")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain 256 MiB device copy instead (reference for the HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the attention core shards by sequence or KV head without any exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    torch.cuda.set_device(torch.device("cuda:0"))
+    w = WORKLOADS[args.workload]
+    steps, warm = DEFAULT_STEPS.get(w.name, (100, 10))
+    steps = args.steps if args.steps is not None else steps
+    warm = args.warmup if args.warmup is not None else warm
+    inputs, r = measure(w, steps, warm, args.launch, args.force_splits, args.sets)
+
+    traffic = traffic_from_profiles(w.name, r["route"]) if r["route"] in ROUTE_SOURCES else None
+    roof = {"bound": r["bound"], "achieved": round(r["kernel_achieved"], 1), "peak": r["peak"],
+            "unit": r["unit"], "frac": round(r["kernel_frac"], 4), "traffic": traffic,
+            "kernel": r["kernel"], "kernel_us": round(r["kernel_us"], 3),
+            "algorithmic_bytes_per_launch": r["bytes_kernel"],
+            "algorithmic_flops_per_launch": r["flops_call"],
+            "kernel_share_of_step": round(r["kernel_us"] / 1e3 / r["ms_per_step"], 3),
+            # the whole call (every kernel of it, launch gaps included) against the same peak
+            "call_achieved": round(r["call_achieved"], 1), "call_frac": round(r["call_frac"], 4)}
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": steps, "warmup": warm, "ms_per_step": round(ms / steps, 6),
+        "metric": METRIC, "value": round(r["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warm, "ms_per_step": round(r["ms_per_step"], 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded N(0,1) inputs, norm weights 1+N(0,0.1))",
         "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len,
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "rotary_dim": w.rotary_dim, "rope_theta": w.rope_theta,
-                   "cached_tokens": int(inputs["seq_lens"].sum()), "buffer_sets": sets,
-                   "launch": "hipgraph" if args.launch == "graph" else "eager", "plan": plan},
-        "effective_gbs": round(gbs, 1), "effective_tflops": round(tfs, 3),
-        "host_wall_s": round(t_host, 4),
+                   "cached_tokens": r["cached_tokens"], "buffer_sets": r["buffer_sets"],
+                   "launch": "hipgraph" if args.launch == "graph" else "eager", "plan": r["plan"]},
+        "effective_gbs": round(r["effective_gbs"], 1), "effective_tflops": round(r["effective_tflops"], 3),
+        "host_wall_s": round(r["host_wall_s"], 4),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, inputs, tokens_per_call)
+        line["cpu_baseline"] = cpu_baseline(w, inputs, r["tokens_per_call"])
+    del inputs
+    if not args.no_extras:
+        extras = {}
+        for name in ("verify_24x2", "ragged_4b", "prefill_4b"):
+            if name == w.name:
+                continue
+            ew = WORKLOADS[name]
+            es, ewarm = DEFAULT_STEPS[name]
+            _, x = measure(ew, es, ewarm)
+            extras[name] = {
+                "tokens_per_s": round(x["tokens_per_s"], 1), "us_per_call": round(x["ms_per_step"] * 1e3, 3),
+                "steps": es, "warmup": ewarm, "plan": x["plan"], "bound": x["bound"], "unit": x["unit"],
+                "call_achieved": round(x["call_achieved"], 1), "call_frac": round(x["call_frac"], 4),
+                "kernel": x["kernel"], "kernel_us": round(x["kernel_us"], 3),
+                "kernel_achieved": round(x["kernel_achieved"], 1), "kernel_frac": round(x["kernel_frac"], 4),
+                "cached_tokens": x["cached_tokens"]}
+        line["workloads"] = extras
     print(json.dumps(line), flush=True)
 
 

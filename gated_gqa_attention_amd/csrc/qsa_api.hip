@@ -237,11 +237,14 @@ int qsa_describe_plan(const qsa_cfg *cfg, char *buf, size_t len) {
   if (rc != QSA_OK) return rc;
   Plan pl;
   if ((rc = make_plan(cfg, &pl)) != QSA_OK) return rc;
+  // merge: how split-K partials are combined -- "kernel" (a second kernel, launched
+  // only when the grid splits keys) or "none"
   return snprintf(buf, len,
                   "route=%s rows=%d tiles=%d chunks=%d chunk_keys=%d workgroups=%lld threads=%d "
-                  "workspace=%zu",
+                  "workspace=%zu merge=%s",
                   route_name(pl.route), pl.rows, pl.tiles, pl.chunks, pl.chunk_keys, (long long)pl.blocks,
-                  pl.route == kRoutePrepared ? qsa::kPrefillThreads : qsa::kThreads, pl.total);
+                  pl.route == kRoutePrepared ? qsa::kPrefillThreads : qsa::kThreads, pl.total,
+                  pl.chunks > 1 ? "kernel" : "none");
 }
 
 int qsa_append_kv(const void *k_new, const void *v_new, const qsa_kv_cache *kv, const int32_t *seq_lens,

@@ -91,6 +91,18 @@ def test_default_plans_fill_one_round_for_short_work():
     assert int(f["workgroups"]) == 256
 
 
+def test_split_merge_placement_per_route():
+    """Calls whose grid splits keys merge the partials in a second kernel
+    (plan field merge=kernel); unsplit calls launch no merge."""
+    for name in ("decode_4b", "verify_24x2", "ragged_4b", "prefill_4b"):
+        f = dict(kv.split("=") for kv in binding.describe_plan(cfg_for(WORKLOADS[name])).split())
+        assert f["merge"] == "kernel" and int(f["chunks"]) > 1, name
+    f = dict(kv.split("=") for kv in binding.describe_plan(cfg_for(WORKLOADS["tiny_f32"])).split())
+    assert f["merge"] == "none"
+    one = dict(kv.split("=") for kv in binding.describe_plan(cfg_for(WORKLOADS["decode_4b"], force_splits=1)).split())
+    assert one["merge"] == "none"
+
+
 def test_tile_route_plan_fills_the_chip_with_equal_chunks():
     """Prefill: 256-row tiles of 512 threads, and just enough equal key chunks
     per tile (none shorter than 1024 keys) that the grid gives every CU one
