@@ -317,6 +317,68 @@ def measure(w, steps, warm, launch="graph", force_splits=0, sets=None):
     return inputs, res
 
 
+def measure_proj(w, which, steps, warm, hidden=None):
+    """Time one projection (which: "qkv" or "o") on the rows of workload w, rotating
+    over >= 1 GB of weight sets so that every step streams its weights from HBM.
+    Returns figures against the HBM roofline (the weights dominate the bytes)."""
+    from gated_gqa_attention_amd.workloads import HIDDEN_4B, make_proj_inputs
+    hidden = hidden or HIDDEN_4B
+    dev = torch.device("cuda:0")
+    p = make_proj_inputs(w, hidden=hidden)
+    B, L, Hq, Hkv, D = w.batch, w.q_len, w.num_q_heads, w.num_kv_heads, w.head_dim
+    M = B * L
+    wkey = "w_qkv" if which == "qkv" else "w_o"
+    wbytes = p[wkey].numel() * 2
+    sets = max(1, min(256, -(-ROTATE_BYTES // wbytes)))
+    weights = [p[wkey].to(dev)] + [p[wkey].to(dev).clone() for _ in range(sets - 1)]
+    x = p["x"].to(dev)
+    attn = torch.randn((M, Hq * D), generator=torch.Generator().manual_seed(7)).to(torch.bfloat16).to(dev)
+    q_gate = torch.empty((B, L, Hq, 2 * D), dtype=torch.bfloat16, device=dev)
+    k_new = torch.empty((B, L, Hkv, D), dtype=torch.bfloat16, device=dev)
+    v_new = torch.empty_like(k_new)
+    y = torch.empty((M, hidden), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.Stream()
+    cfg = binding.make_cfg(batch=B, q_len=L, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, rotary_dim=w.rotary_dim,
+                           rope_theta=w.rope_theta, rms_eps=w.rms_eps, dtype=torch.bfloat16, max_seq_len=L,
+                           q_norm_w=1, k_norm_w=1, stream=stream)
+
+    def call(i):
+        if which == "qkv":
+            binding.qkv_proj(cfg, x, weights[i % sets], hidden, q_gate, k_new, v_new)
+        else:
+            binding.o_proj(cfg, attn, weights[i % sets], hidden, y)
+
+    with torch.cuda.stream(stream):
+        for i in range(warm):
+            call(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(steps):
+            call(warm + i)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    if which == "qkv":
+        nbytes = wbytes + M * hidden * 2 + (q_gate.numel() + k_new.numel() + v_new.numel()) * 2
+    else:
+        nbytes = wbytes + M * Hq * D * 2 + M * hidden * 2
+    gbs = nbytes / (ms / 1e3) / 1e9
+    del weights
+    torch.cuda.empty_cache()
+    return {"us_per_call": round(ms * 1e3, 3), "steps": steps, "warmup": warm, "rows": M, "hidden": hidden,
+            "weight_sets": sets, "algorithmic_bytes": nbytes, "bound": "hbm", "unit": "GB/s",
+            "call_achieved": round(gbs, 1), "call_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -329,6 +391,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="time only --workload (by default the other bf16 workloads follow as extra keys)")
     ap.add_argument("--sets", type=int, default=None, help="buffer sets to rotate over")
+    ap.add_argument("--proj", choices=["qkv", "o"], default=None,
+                    help="time only the q/k/v (or o) projection at the decode shape and print its figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 256 MiB device copy instead (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -346,6 +410,10 @@ def main():
         copy_calibration()
         return
     torch.cuda.set_device(torch.device("cuda:0"))
+    if args.proj:
+        print(json.dumps({"proj": args.proj, **measure_proj(WORKLOADS["decode_4b"], args.proj, args.steps or 1000,
+                                                            args.warmup or 50)}), flush=True)
+        return
     w = WORKLOADS[args.workload]
     steps, warm = DEFAULT_STEPS.get(w.name, (100, 10))
     steps = args.steps if args.steps is not None else steps
@@ -393,6 +461,9 @@ def main():
                 "kernel": x["kernel"], "kernel_us": round(x["kernel_us"], 3),
                 "kernel_achieved": round(x["kernel_achieved"], 1), "kernel_frac": round(x["kernel_frac"], 4),
                 "cached_tokens": x["cached_tokens"]}
+        # the projections either side of the core, at the decode shape (one row)
+        extras["qkv_proj_4b"] = measure_proj(WORKLOADS["decode_4b"], "qkv", 1000, 50)
+        extras["o_proj_4b"] = measure_proj(WORKLOADS["decode_4b"], "o", 1000, 50)
         line["workloads"] = extras
     print(json.dumps(line), flush=True)
 

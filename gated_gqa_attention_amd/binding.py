@@ -19,7 +19,7 @@ QSA_BF16, QSA_F32 = 0, 1
 _DT = {torch.bfloat16: QSA_BF16, torch.float32: QSA_F32}
 
 EXPORTS = ("qsa_workspace_size", "qsa_append_kv", "qsa_gated_attention", "qsa_gated_attention_noalloc",
-           "qsa_describe_plan", "qsa_last_error")
+           "qsa_qkv_proj", "qsa_o_proj", "qsa_describe_plan", "qsa_last_error")
 NOALLOC_SCRATCH_BYTES = 64 << 20     # QSA_NOALLOC_SCRATCH_BYTES
 
 
@@ -77,6 +77,10 @@ def load():
         lib.qsa_gated_attention_noalloc.restype = ctypes.c_int
         lib.qsa_gated_attention_noalloc.argtypes = [p, p, p, ctypes.POINTER(KVCache), p, p,
                                                     ctypes.POINTER(Cfg), p]
+        lib.qsa_qkv_proj.restype = ctypes.c_int
+        lib.qsa_qkv_proj.argtypes = [p, p, ctypes.c_int32, ctypes.POINTER(Cfg), p, p, p]
+        lib.qsa_o_proj.restype = ctypes.c_int
+        lib.qsa_o_proj.argtypes = [p, p, ctypes.c_int32, ctypes.POINTER(Cfg), p]
         lib.qsa_describe_plan.restype = ctypes.c_int
         lib.qsa_describe_plan.argtypes = [ctypes.POINTER(Cfg), ctypes.c_char_p, ctypes.c_size_t]
         lib.qsa_last_error.restype = ctypes.c_char_p
@@ -153,3 +157,14 @@ def gated_attention_noalloc(cfg: Cfg, kv: KVCache, q_gate, k_new, v_new, seq_len
     _check(load().qsa_gated_attention_noalloc(_ptr(q_gate), _ptr(k_new), _ptr(v_new), ctypes.byref(kv),
                                               _ptr(seq_lens), _ptr(positions), ctypes.byref(cfg),
                                               _ptr(out)))
+
+
+def qkv_proj(cfg: Cfg, x, w_qkv, hidden: int, q_gate, k_new, v_new) -> None:
+    """qsa_qkv_proj: x [rows, hidden] times the fused q/k/v weight, split into q_gate, k_new, v_new."""
+    _check(load().qsa_qkv_proj(_ptr(x), _ptr(w_qkv), int(hidden), ctypes.byref(cfg), _ptr(q_gate), _ptr(k_new),
+                               _ptr(v_new)))
+
+
+def o_proj(cfg: Cfg, attn, w_o, hidden: int, y) -> None:
+    """qsa_o_proj: y [rows, hidden] = attn [rows, Hq*D] times w_o^T."""
+    _check(load().qsa_o_proj(_ptr(attn), _ptr(w_o), int(hidden), ctypes.byref(cfg), _ptr(y)))

@@ -375,6 +375,26 @@ int scratch_for_current_device(hipStream_t s, void **ptr) {
   return QSA_OK;
 }
 
+// Shape checks of the projections: the rows, heads and head_dim of cfg, bf16,
+// hidden a multiple of 256 (the K split of the projection kernel).
+int validate_proj(const qsa_cfg *c, int32_t hidden) {
+  if (!c) return fail(QSA_ERR_INVALID, "cfg is NULL");
+  if (c->batch < 1 || c->q_len < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1 ||
+      c->num_q_heads % c->num_kv_heads)
+    return fail(QSA_ERR_INVALID, "batch, q_len >= 1 and num_q_heads a multiple of num_kv_heads >= 1 required");
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
+    return fail(QSA_ERR_UNSUPPORTED, "head_dim %d not supported (64 | 128 | 256)", c->head_dim);
+  if (c->dtype != QSA_BF16) return fail(QSA_ERR_UNSUPPORTED, "the projections take bf16 only");
+  if ((int64_t)c->batch * c->q_len > qsa::kMaxLinearRows)
+    return fail(QSA_ERR_UNSUPPORTED, "the projections take at most %d rows (batch * q_len = %lld)",
+                qsa::kMaxLinearRows, (long long)c->batch * c->q_len);
+  if (hidden < 256 || hidden % 256)
+    return fail(QSA_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 256", hidden);
+  if ((c->num_q_heads * c->head_dim) % 256)
+    return fail(QSA_ERR_UNSUPPORTED, "num_q_heads * head_dim must be a multiple of 256");
+  return QSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -384,6 +404,46 @@ int qsa_gated_attention(const void *q_gate, const void *k_new, const void *v_new
   if (!cfg) return fail(QSA_ERR_INVALID, "cfg is NULL");
   return gated_attention_in(q_gate, k_new, v_new, kv, seq_lens, positions, cfg, out, cfg->workspace,
                             cfg->workspace_bytes, "workspace");
+}
+
+int qsa_qkv_proj(const void *x, const void *w_qkv, int32_t hidden, const qsa_cfg *cfg, void *q_gate, void *k_new,
+                 void *v_new) {
+  int rc = validate_proj(cfg, hidden);
+  if (rc != QSA_OK) return rc;
+  if (!x || !w_qkv || !q_gate || !k_new || !v_new)
+    return fail(QSA_ERR_INVALID, "x, w_qkv, q_gate, k_new and v_new are required");
+  const int M = cfg->batch * cfg->q_len, D = cfg->head_dim;
+  const int nq = cfg->num_q_heads * 2 * D, nk = cfg->num_kv_heads * D;
+  const size_t xb = (size_t)M * hidden * 2, wb = (size_t)(nq + 2 * nk) * hidden * 2;
+  const size_t qb = (size_t)M * nq * 2, kb = (size_t)M * nk * 2;
+  const void *outs[3] = {q_gate, k_new, v_new};
+  const size_t ob[3] = {qb, kb, kb};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(outs[i], ob[i], x, xb) || overlaps(outs[i], ob[i], w_qkv, wb))
+      return fail(QSA_ERR_INVALID, "the outputs must not alias x or w_qkv");
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], ob[i], outs[j], ob[j])) return fail(QSA_ERR_INVALID, "q_gate, k_new and v_new overlap");
+  }
+  if ((rc = check_device()) != QSA_OK) return rc;
+  hipError_t e = qsa::launch_linear_bf16(x, w_qkv, M, nq + 2 * nk, hidden, q_gate, nq, nq, k_new, nq + nk, nk, v_new,
+                                         nk, (hipStream_t)cfg->stream);
+  if (e != hipSuccess) return fail(QSA_ERR_DEVICE, "projection launch failed: %s", hipGetErrorString(e));
+  return QSA_OK;
+}
+
+int qsa_o_proj(const void *attn, const void *w_o, int32_t hidden, const qsa_cfg *cfg, void *y) {
+  int rc = validate_proj(cfg, hidden);
+  if (rc != QSA_OK) return rc;
+  if (!attn || !w_o || !y) return fail(QSA_ERR_INVALID, "attn, w_o and y are required");
+  const int M = cfg->batch * cfg->q_len, K = cfg->num_q_heads * cfg->head_dim;
+  if (overlaps(y, (size_t)M * hidden * 2, attn, (size_t)M * K * 2) ||
+      overlaps(y, (size_t)M * hidden * 2, w_o, (size_t)hidden * K * 2))
+    return fail(QSA_ERR_INVALID, "y must not alias attn or w_o");
+  if ((rc = check_device()) != QSA_OK) return rc;
+  hipError_t e = qsa::launch_linear_bf16(attn, w_o, M, hidden, K, y, hidden, hidden, y, hidden, hidden, y, hidden,
+                                         (hipStream_t)cfg->stream);
+  if (e != hipSuccess) return fail(QSA_ERR_DEVICE, "projection launch failed: %s", hipGetErrorString(e));
+  return QSA_OK;
 }
 
 int qsa_gated_attention_noalloc(const void *q_gate, const void *k_new, const void *v_new, const qsa_kv_cache *kv,

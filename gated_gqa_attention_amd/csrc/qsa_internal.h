@@ -172,5 +172,8 @@ hipError_t launch_rows_f32(const Params &p, hipStream_t s, const Timing &tm);
 hipError_t launch_tile_bf16(const Params &p, hipStream_t s, const Timing &tm);
 hipError_t launch_stream_bf16(const Params &p, hipStream_t s, const Timing &tm);
 hipError_t launch_combine_bf16(const Params &p, hipStream_t s, bool per_row);   // per_row: the tile route's merge
+hipError_t launch_linear_bf16(const void *x, const void *w, int M, int N, int K, void *y0, int n0_end, int ld0,
+                              void *y1, int n1_end, int ld1, void *y2, int ld2, hipStream_t s);
+constexpr int kMaxLinearRows = 64;    // rows (tokens) a projection call takes
 
 }  // namespace qsa

@@ -150,3 +150,22 @@ def make_inputs(w: Workload, variant: str = "graded", seed: int | None = None) -
 def to_device(inputs: dict, device) -> dict:
     """Copy every tensor of an input dict to ``device``."""
     return {k: v.to(device) if isinstance(v, torch.Tensor) else v for k, v in inputs.items()}
+
+
+HIDDEN_4B = 2560   # Atlas qwen3_5_4b_mlx_int8: hidden
+
+
+def make_proj_inputs(w: Workload, hidden: int = HIDDEN_4B, seed: int | None = None) -> dict:
+    """Seeded inputs of the projections around the core: the rows x
+    [B*L, hidden] ~ N(0, 1), the fused q/k/v weight [2 Hq D + 2 Hkv D, hidden]
+    and the o_proj weight [hidden, Hq D], both N(0, 1) / sqrt(in_features) so
+    that outputs are O(1); drawn in fp32 (in that order) and cast to the
+    storage dtype."""
+    gen = torch.Generator("cpu").manual_seed((w.seed if seed is None else seed) + 1000)
+    dt = DTYPES[w.dtype]
+    M, D = w.batch * w.q_len, w.head_dim
+    nqkv = 2 * w.num_q_heads * D + 2 * w.num_kv_heads * D
+    x = torch.randn((M, hidden), generator=gen)
+    w_qkv = torch.randn((nqkv, hidden), generator=gen) / hidden ** 0.5
+    w_o = torch.randn((hidden, w.num_q_heads * D), generator=gen) / (w.num_q_heads * D) ** 0.5
+    return {"x": x.to(dt).contiguous(), "w_qkv": w_qkv.to(dt).contiguous(), "w_o": w_o.to(dt).contiguous()}

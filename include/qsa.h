@@ -141,6 +141,31 @@ int qsa_gated_attention(const void *q_gate, const void *k_new, const void *v_new
                         const qsa_kv_cache *kv, const int32_t *seq_lens,
                         const int32_t *positions, const qsa_cfg *cfg, void *out);
 
+/* The projections on either side of the core, for the few rows of decode and
+ * speculative verify (mlxd PR #99 Summary: doubled q_proj -> split into queries
+ * and gate -> o_proj(attn * sigmoid(gate)); Atlas FullAttentionLayer q_proj /
+ * k_proj / v_proj / o_proj and Qwen35Kernels qkv_split).  Only the shape
+ * fields of cfg (batch, q_len, num_q_heads, num_kv_heads, head_dim, dtype) and
+ * cfg->stream are read; rows = batch * q_len <= 64; bf16 only; hidden a
+ * multiple of 256; num_q_heads * head_dim a multiple of 256.  Accumulation is
+ * fp32 and each output is rounded once (nearest even).  Weights are row-major
+ * [out_features][in_features] (a linear layer's weight), device memory owned
+ * by the caller; outputs must not alias inputs.  Asynchronous on cfg->stream;
+ * returns a qsa_status.
+ *
+ * qsa_qkv_proj: x [rows][hidden]; w_qkv [2 Hq D + 2 Hkv D][hidden] holding the
+ * q_proj rows (per head h: its D query rows, then its D gate rows), then the
+ * k_proj rows, then the v_proj rows.  Writes q_gate [rows][Hq][2D] (per head
+ * [query | gate], the layout qsa_gated_attention reads), k_new [rows][Hkv][D]
+ * and v_new [rows][Hkv][D]: the split of the doubled q_proj output is where the
+ * products are stored. */
+int qsa_qkv_proj(const void *x, const void *w_qkv, int32_t hidden, const qsa_cfg *cfg, void *q_gate,
+                 void *k_new, void *v_new);
+
+/* qsa_o_proj: y [rows][hidden] = attn W_o^T with attn [rows][Hq D] (the gated
+ * output of qsa_gated_attention) and w_o [hidden][Hq D]. */
+int qsa_o_proj(const void *attn, const void *w_o, int32_t hidden, const qsa_cfg *cfg, void *y);
+
 /* Bytes of device scratch that qsa_gated_attention_noalloc holds per GPU. */
 #define QSA_NOALLOC_SCRATCH_BYTES (64u << 20)
 

@@ -20,7 +20,10 @@ arrays.  The steps it follows, with the pages they come from:
   Atlas ``qwen3_5/mod.rs`` module doc;
 * grouped-query attention with contiguous head groups -- DS4Server issue #113,
   Reproduction; Atlas ``Qwen35ForwardConfig`` (16 query / 4 KV heads);
-* ``attn * sigmoid(gate)`` -- mlxd PR #99 Summary; Atlas ``sigmoid_gate``.
+* ``attn * sigmoid(gate)`` -- mlxd PR #99 Summary; Atlas ``sigmoid_gate``;
+* the projections either side (fused q/k/v with the query/gate split in its
+  output layout, and o_proj) -- mlxd PR #99 Summary; Atlas
+  ``FullAttentionLayer`` q/k/v/o_proj and ``Qwen35Kernels`` ``qkv_split``.
 
 Readings where the pages are silent are listed with each function below.
 """
@@ -80,6 +83,10 @@ def _load():
         lib.qsa_oracle_attention.argtypes = [
             ctypes.POINTER(_Cfg), p, p, p, p, ctypes.c_int32, p, p, p, p, p, p,
             ctypes.c_int64, p, p]
+        lib.qsa_oracle_linear.restype = ctypes.c_int
+        lib.qsa_oracle_linear.argtypes = [p, p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, p]
+        lib.qsa_oracle_qkv_proj.restype = ctypes.c_int
+        lib.qsa_oracle_qkv_proj.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int32, p, p, p, p, p]
         lib.qsa_oracle_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -227,6 +234,47 @@ def gated_attention(geo: Geometry, inputs: dict, rows=None, want_attn=False, fus
         out, att = res
         return out, kr, vr, att
     return res, kr, vr
+
+
+def linear(x, w, dtype: str = "f64"):
+    """y = x w^T for x [M, K] and w [N, K] in double, rounded to `dtype`."""
+    lib = _load()
+    xa, wa = _f64(x), _f64(w)
+    M, K = xa.shape
+    N = wa.shape[0]
+    if wa.shape[1] != K:
+        raise ValueError("x and w disagree on the inner size")
+    y = np.empty((M, N), dtype=np.float64)
+    bits = {"bf16": 8, "f32": 24, "f64": 53}[dtype]
+    if lib.qsa_oracle_linear(_ptr(xa), _ptr(wa), M, N, K, bits, _ptr(y)) != 0:
+        raise ValueError("oracle rejected the sizes")
+    return y
+
+
+def qkv_proj(geo: Geometry, hidden: int, x, w_qkv):
+    """Fused q/k/v projection of x [B*L, hidden] and its split (see qsa_oracle.h).
+    Returns q_gate [B, L, Hq, 2D], k_new and v_new [B, L, Hkv, D], rounded to
+    the geometry's storage dtype."""
+    lib = _load()
+    xa, wa = _f64(x), _f64(w_qkv)
+    B, L, Hq, Hkv, D = geo.batch, geo.q_len, geo.num_q_heads, geo.num_kv_heads, geo.head_dim
+    if xa.shape != (B * L, hidden) or wa.shape != (2 * Hq * D + 2 * Hkv * D, hidden):
+        raise ValueError("x or w_qkv has the wrong shape")
+    qg = np.empty((B, L, Hq, 2 * D))
+    kn = np.empty((B, L, Hkv, D))
+    vn = np.empty((B, L, Hkv, D))
+    if lib.qsa_oracle_qkv_proj(ctypes.byref(geo._c()), hidden, _ptr(xa), _ptr(wa), _ptr(qg), _ptr(kn),
+                               _ptr(vn)) != 0:
+        raise ValueError("oracle rejected the configuration")
+    return qg, kn, vn
+
+
+def o_proj(geo: Geometry, hidden: int, attn, w_o):
+    """y [B*L, hidden] = attn [B*L, Hq*D] w_o^T, rounded to the storage dtype."""
+    a = _f64(attn).reshape(geo.batch * geo.q_len, geo.num_q_heads * geo.head_dim)
+    if _f64(w_o).shape != (hidden, geo.num_q_heads * geo.head_dim):
+        raise ValueError("w_o has the wrong shape")
+    return linear(a, w_o, geo.dtype)
 
 
 def threads() -> int:

@@ -188,6 +188,37 @@ int qsa_oracle_attention(const qsa_oracle_cfg *c, const double *q_gate, const do
   return err ? -1 : 0;
 }
 
+int qsa_oracle_linear(const double *x, const double *w, int64_t M, int64_t N, int64_t K, int32_t store_bits,
+                      double *y) {
+  if (M < 0 || N < 0 || K < 0) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < M * N; ++i) {
+    const int64_t m = i / N, n = i % N;
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k) acc += x[m * K + k] * w[n * K + k];
+    y[i] = qsa_oracle_round(acc, store_bits);
+  }
+  return 0;
+}
+
+int qsa_oracle_qkv_proj(const qsa_oracle_cfg *c, int32_t hidden, const double *x, const double *w_qkv,
+                        double *q_gate, double *k_new, double *v_new) {
+  if (!cfg_ok(c) || hidden < 1) return -1;
+  const int64_t M = (int64_t)c->batch * c->q_len, D = c->head_dim;
+  const int64_t nq = (int64_t)c->num_q_heads * 2 * D, nk = (int64_t)c->num_kv_heads * D, n = nq + 2 * nk;
+  double *y = (double *)malloc(sizeof(double) * (size_t)(M * n));
+  if (!y) return -1;
+  qsa_oracle_linear(x, w_qkv, M, n, hidden, c->store_bits, y);
+  /* the split: the first 2 Hq D features of each row are q_gate, then k, then v */
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t f = 0; f < nq; ++f) q_gate[m * nq + f] = y[m * n + f];
+    for (int64_t f = 0; f < nk; ++f) k_new[m * nk + f] = y[m * n + nq + f];
+    for (int64_t f = 0; f < nk; ++f) v_new[m * nk + f] = y[m * n + nq + nk + f];
+  }
+  free(y);
+  return 0;
+}
+
 int qsa_oracle_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

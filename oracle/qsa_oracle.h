@@ -89,6 +89,22 @@ int qsa_oracle_attention(const qsa_oracle_cfg *cfg, const double *q_gate, const 
                          const double *v_rows, const int64_t *rows, int64_t n_rows,
                          double *out, double *attn);
 
+/* A linear layer: y[m][n] = sum_k x[m][k] w[n][k] in double, rounded to
+ * store_bits significand bits.  x [M][K], w [N][K] (row-major, a linear
+ * layer's weight), y [M][N].  Returns 0, or -1 on a negative size. */
+int qsa_oracle_linear(const double *x, const double *w, int64_t M, int64_t N, int64_t K, int32_t store_bits,
+                      double *y);
+
+/* The fused q/k/v projection of the rows x [B*L][hidden] (mlxd PR #99 Summary:
+ * doubled q_proj -> split into queries and gate; Atlas FullAttentionLayer
+ * q_proj / k_proj / v_proj, Qwen35Kernels qkv_split).  w_qkv holds the q_proj
+ * rows ([Hq][2D]: per head its query rows, then its gate rows), then the k_proj
+ * rows [Hkv][D], then the v_proj rows [Hkv][D], each over hidden inputs.  Writes
+ * q_gate [B*L][Hq][2D], k_new and v_new [B*L][Hkv][D], rounded to storage.
+ * Returns 0 or -1. */
+int qsa_oracle_qkv_proj(const qsa_oracle_cfg *cfg, int32_t hidden, const double *x, const double *w_qkv,
+                        double *q_gate, double *k_new, double *v_new);
+
 /* Number of OpenMP threads the oracle runs with. */
 int qsa_oracle_threads(void);
 

@@ -198,6 +198,21 @@ def test_noalloc_scratch_size_matches_the_header():
     assert m and int(m.group(1)) << int(m.group(2)) == binding.NOALLOC_SCRATCH_BYTES
 
 
+def test_projection_arguments_checked_before_launch():
+    lib = binding.load()
+    ok = cfg_for(WORKLOADS["decode_4b"])
+    call = lambda c, hidden, *ptrs: lib.qsa_qkv_proj(*ptrs[:2], hidden, ctypes.byref(c), *ptrs[2:])
+    q, k, v, x, w = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30)
+    assert call(ok, 2560, x, w, q, k, None) == binding.QSA_ERR_INVALID
+    assert call(ok, 2500, x, w, q, k, v) == binding.QSA_ERR_UNSUPPORTED          # hidden % 256
+    assert call(cfg_for(WORKLOADS["decode_4b"], batch=65), 2560, x, w, q, k, v) == binding.QSA_ERR_UNSUPPORTED
+    assert call(cfg_for(WORKLOADS["tiny_f32"]), 2560, x, w, q, k, v) == binding.QSA_ERR_UNSUPPORTED   # fp32
+    assert call(ok, 2560, x, w, q, q + 64, v) == binding.QSA_ERR_INVALID          # outputs overlap
+    assert call(ok, 2560, x, w, x, k, v) == binding.QSA_ERR_INVALID               # output aliases x
+    assert lib.qsa_o_proj(x, w, 2560, ctypes.byref(ok), x + 8) == binding.QSA_ERR_INVALID
+    assert lib.qsa_o_proj(x, None, 2560, ctypes.byref(ok), q) == binding.QSA_ERR_INVALID
+
+
 def test_workspace_scales_with_chunks():
     w = WORKLOADS["decode_4b"]
     one = binding.workspace_size(cfg_for(w, force_splits=1))
