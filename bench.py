@@ -26,7 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from gated_gqa_attention_amd import binding  # noqa: E402
-from gated_gqa_attention_amd.workloads import DTYPES, WORKLOADS, make_inputs  # noqa: E402
+from gated_gqa_attention_amd.workloads import DTYPES, WORKLOADS, make_inputs, to_paged  # noqa: E402
 
 METRIC = "gated-GQA attn tokens/s + effective HBM GB/s (% of peak), 4B geometry decode"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
@@ -97,14 +97,18 @@ def traffic_from_profiles(workload, route, per_launch_units=1):
 class Call:
     """Device buffers and C-ABI arguments of one buffer set."""
 
-    def __init__(self, w, dev, workspace, max_seq_len, stream):
+    def __init__(self, w, dev, workspace, max_seq_len, stream, block_size=0):
         self.w, self.dev = w, dev
         self.cfg = binding.make_cfg(
             batch=w.batch, q_len=w.q_len, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
             head_dim=w.head_dim, rotary_dim=w.rotary_dim, rope_theta=w.rope_theta, rms_eps=w.rms_eps,
             dtype=DTYPES[w.dtype], max_seq_len=max_seq_len, q_norm_w=dev["w_q"], k_norm_w=dev["w_k"],
             workspace=workspace, stream=stream)
-        self.kv = binding.make_kv(dev["k_cache"], dev["v_cache"], dev["seq_offset"], dev["capacity"])
+        if "block_table" in dev:
+            self.kv = binding.make_kv(dev["k_cache"], dev["v_cache"], None, dev["capacity"], dev["block_table"],
+                                      block_size)
+        else:
+            self.kv = binding.make_kv(dev["k_cache"], dev["v_cache"], dev["seq_offset"], dev["capacity"])
         self.ws = workspace
         self.out = torch.empty((w.batch, w.q_len, w.num_q_heads, w.head_dim), dtype=DTYPES[w.dtype],
                                device=dev["q_gate"].device)
@@ -212,15 +216,18 @@ def cpu_model():
     return "unknown"
 
 
-def measure(w, steps, warm, launch="graph", force_splits=0, sets=None):
+def measure(w, steps, warm, launch="graph", force_splits=0, sets=None, block_size=0):
     """Time one workload: `warm` untimed eager calls, then `steps` calls captured in
     one HIP graph, replayed once untimed and once timed (HIP events on the launch
-    stream), then the attention kernel on its own in an eager pass.  Returns the
-    inputs and a dict of figures."""
+    stream), then the attention kernel on its own in an eager pass.  block_size >
+    0: the cache is laid out in shuffled blocks of that many rows (paged).
+    Returns the inputs and a dict of figures."""
     dev = torch.device("cuda:0")
     inputs = make_inputs(w)
     max_seq_len = int((inputs["seq_lens"].max() + w.q_len).item())
     base = {k: v.to(dev) for k, v in inputs.items()}
+    if block_size:
+        base = to_paged(base, block_size, seed=w.seed)
     set_bytes = sum(v.numel() * v.element_size() for v in base.values())
     sets = sets or max(1, min(256, -(-ROTATE_BYTES // set_bytes)))
     if set_bytes * sets > 64 * (1 << 30):
@@ -238,7 +245,7 @@ def measure(w, steps, warm, launch="graph", force_splits=0, sets=None):
     for i in range(sets):
         d = base if i == 0 else {k: v.clone() for k, v in base.items()}
         ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
-        c = Call(w, d, ws, max_seq_len, stream)
+        c = Call(w, d, ws, max_seq_len, stream, block_size)
         c.cfg.force_splits = force_splits
         calls.append(c)
     torch.cuda.synchronize()
@@ -285,6 +292,8 @@ def measure(w, steps, warm, launch="graph", force_splits=0, sets=None):
 
     tokens_per_call = w.batch * w.q_len
     bytes_call, out_bytes, flops_call = algorithmic_work(w, inputs["seq_lens"])
+    if block_size:                                      # the block table entries the call reads
+        bytes_call += 4 * int(((inputs["seq_lens"] + w.q_len + block_size - 1) // block_size).sum())
     fields = dict(kv.split("=") for kv in plan.split())
     route = fields["route"]
     # bytes the streaming kernel moves: all of the call's, except the output when a
@@ -309,7 +318,7 @@ def measure(w, steps, warm, launch="graph", force_splits=0, sets=None):
         "kernel": kname, "kernel_us": kernel_ms * 1e3, "kernel_achieved": kern_ach,
         "kernel_frac": kern_ach / peak, "bytes_call": bytes_call, "bytes_kernel": bytes_kernel,
         "flops_call": flops_call, "tokens_per_call": tokens_per_call,
-        "cached_tokens": int(inputs["seq_lens"].sum()),
+        "cached_tokens": int(inputs["seq_lens"].sum()), "block_size": block_size,
     }
     del calls, base
     torch.cuda.synchronize()
@@ -391,6 +400,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="time only --workload (by default the other bf16 workloads follow as extra keys)")
     ap.add_argument("--sets", type=int, default=None, help="buffer sets to rotate over")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="lay the cache out in shuffled blocks of this many rows (paged; 0: contiguous)")
     ap.add_argument("--proj", choices=["qkv", "o"], default=None,
                     help="time only the q/k/v (or o) projection at the decode shape and print its figures")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -418,7 +429,7 @@ def main():
     steps, warm = DEFAULT_STEPS.get(w.name, (100, 10))
     steps = args.steps if args.steps is not None else steps
     warm = args.warmup if args.warmup is not None else warm
-    inputs, r = measure(w, steps, warm, args.launch, args.force_splits, args.sets)
+    inputs, r = measure(w, steps, warm, args.launch, args.force_splits, args.sets, args.block_size)
 
     traffic = traffic_from_profiles(w.name, r["route"]) if r["route"] in ROUTE_SOURCES else None
     roof = {"bound": r["bound"], "achieved": round(r["kernel_achieved"], 1), "peak": r["peak"],
@@ -461,6 +472,14 @@ def main():
                 "kernel": x["kernel"], "kernel_us": round(x["kernel_us"], 3),
                 "kernel_achieved": round(x["kernel_achieved"], 1), "kernel_frac": round(x["kernel_frac"], 4),
                 "cached_tokens": x["cached_tokens"]}
+        # the ragged batch again, its cache in shuffled blocks of 64 rows (paged)
+        _, x = measure(WORKLOADS["ragged_4b"], *DEFAULT_STEPS["ragged_4b"], block_size=64)
+        extras["ragged_4b_paged64"] = {
+            "tokens_per_s": round(x["tokens_per_s"], 1), "us_per_call": round(x["ms_per_step"] * 1e3, 3),
+            "steps": x["steps"], "warmup": x["warmup"], "plan": x["plan"], "block_size": 64, "bound": "hbm",
+            "unit": "GB/s", "call_achieved": round(x["call_achieved"], 1), "call_frac": round(x["call_frac"], 4),
+            "kernel": x["kernel"], "kernel_us": round(x["kernel_us"], 3),
+            "kernel_achieved": round(x["kernel_achieved"], 1), "kernel_frac": round(x["kernel_frac"], 4)}
         # the projections either side of the core, at the decode shape (one row)
         extras["qkv_proj_4b"] = measure_proj(WORKLOADS["decode_4b"], "qkv", 1000, 50)
         extras["o_proj_4b"] = measure_proj(WORKLOADS["decode_4b"], "o", 1000, 50)

@@ -49,6 +49,7 @@ class KVCache(ctypes.Structure):
         ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("seq_offset", ctypes.c_void_p), ("capacity", ctypes.c_void_p),
         ("num_rows", ctypes.c_int64),
+        ("block_table", ctypes.c_void_p), ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
     ]
 
 
@@ -120,10 +121,12 @@ def make_cfg(*, batch, q_len, num_q_heads, num_kv_heads, head_dim, rotary_dim, r
                stream_handle)
 
 
-def make_kv(k_cache, v_cache, seq_offset, capacity=None) -> KVCache:
-    """Describe a token-major cache: k/v ``[rows, Hkv, D]``, seq_offset int64 ``[B]``."""
+def make_kv(k_cache, v_cache, seq_offset, capacity=None, block_table=None, block_size=0) -> KVCache:
+    """Describe a token-major cache: k/v ``[rows, Hkv, D]``; contiguous with
+    seq_offset int64 ``[B]``, or paged with block_table int32 ``[B, max_blocks]``."""
+    max_blocks = 0 if block_table is None else int(block_table.shape[1])
     return KVCache(_ptr(k_cache), _ptr(v_cache), _ptr(seq_offset), _ptr(capacity),
-                   int(k_cache.shape[0]))
+                   int(k_cache.shape[0]), _ptr(block_table), int(block_size), max_blocks)
 
 
 def workspace_size(cfg: Cfg) -> int:

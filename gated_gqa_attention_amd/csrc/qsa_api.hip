@@ -203,10 +203,25 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 
 int check_kv(const qsa_kv_cache *kv) {
   if (!kv) return fail(QSA_ERR_INVALID, "kv cache descriptor is NULL");
-  if (!kv->k || !kv->v || !kv->seq_offset) return fail(QSA_ERR_INVALID, "kv->k, kv->v and kv->seq_offset are required");
+  if (!kv->k || !kv->v) return fail(QSA_ERR_INVALID, "kv->k and kv->v are required");
   if (kv->num_rows < 1) return fail(QSA_ERR_INVALID, "kv->num_rows must be >= 1");
   if (kv->k == kv->v) return fail(QSA_ERR_INVALID, "kv->k and kv->v must be different buffers");
+  if (!kv->block_table) {
+    if (!kv->seq_offset) return fail(QSA_ERR_INVALID, "kv->seq_offset is required for a contiguous cache");
+    return QSA_OK;
+  }
+  const int32_t bs = kv->block_size;
+  if (bs < 64 || bs > (1 << 16) || (bs & (bs - 1)))
+    return fail(QSA_ERR_INVALID, "kv->block_size %d must be a power of two in [64, 65536]", bs);
+  if (kv->max_blocks < 1) return fail(QSA_ERR_INVALID, "kv->max_blocks must be >= 1");
+  if (kv->num_rows % bs) return fail(QSA_ERR_INVALID, "kv->num_rows must be a multiple of block_size for a paged cache");
   return QSA_OK;
+}
+
+int log2_of(int32_t x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
 }
 
 void fill_kv(qsa::Params &p, const qsa_kv_cache *kv, const int32_t *seq_lens, const int32_t *positions) {
@@ -215,6 +230,9 @@ void fill_kv(qsa::Params &p, const qsa_kv_cache *kv, const int32_t *seq_lens, co
   p.seq_offset = kv->seq_offset;
   p.capacity = kv->capacity;
   p.num_rows = kv->num_rows;
+  p.btab = kv->block_table;
+  p.bs_log2 = kv->block_table ? log2_of(kv->block_size) : 0;
+  p.max_blocks = kv->block_table ? kv->max_blocks : 0;
   p.seq_lens = seq_lens;
   p.positions = positions;
 }
@@ -295,6 +313,19 @@ int gated_attention_in(const void *q_gate, const void *k_new, const void *v_new,
     return fail(QSA_ERR_INVALID, "out must not alias q_gate, k_new, v_new or the cache");
   Plan pl;
   if ((rc = make_plan(cfg, &pl)) != QSA_OK) return rc;
+  if (kv->block_table) {
+    // Paged caches on the short-query route only.  A workgroup holds the block
+    // ids of its key chunk (at most 128): with fixed chunks the last one has
+    // fewer than 2 chunk_keys keys, with equal chunks about 1.5 chunk_keys.
+    if (pl.route != kRouteFused)
+      return fail(QSA_ERR_UNSUPPORTED,
+                  "paged caches are taken on the short-query route only (bf16, q_len <= 16, q_len * G <= 48); "
+                  "this call plans route %s", route_name(pl.route));
+    const int64_t span = 2 * (int64_t)pl.chunk_keys + cfg->q_len;
+    if ((span >> log2_of(kv->block_size)) + 2 > 128)
+      return fail(QSA_ERR_UNSUPPORTED, "key chunks of %d keys span more than 128 blocks of %d rows",
+                  pl.chunk_keys, kv->block_size);
+  }
   if (!ws_ptr || ws_bytes < pl.total)
     return fail(QSA_ERR_WORKSPACE, "%s of %zu bytes needed, %zu %s", ws_name, pl.total,
                 ws_ptr ? ws_bytes : (size_t)0, ws_ptr ? "available" : "given");

@@ -86,6 +86,12 @@ __device__ __forceinline__ void dma16_sbase(const void *base, unsigned voff, uns
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
 }
 
+// The same copy from a 64-bit address per lane (paged caches, whose rows of
+// one stage need not be contiguous).
+__device__ __forceinline__ void dma16_vaddr(const void *src, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");

@@ -57,6 +57,9 @@ struct Params {
   const int64_t *seq_offset;
   const int32_t *capacity;  // may be null
   int64_t num_rows;
+  const int32_t *btab;      // paged caches: block table [B][max_blocks]; null when contiguous
+  int bs_log2;              // paged: log2 of the rows per block
+  int max_blocks;           // paged: block table row stride
   const int32_t *seq_lens;
   const int32_t *positions;
   const void *wq;
@@ -136,14 +139,31 @@ __device__ __forceinline__ int64_t chunk_begin(int64_t kend, int even_split, int
   return even_split ? (int64_t)c * kend / nch : (int64_t)c * chunk_keys;
 }
 
-// Sequence bounds check shared by the kernels.  Returns false when rows
-// [0, n + L) of sequence b would leave the cache or pass its capacity.
+// Sequence bounds check shared by the prologue and the fp32 kernel.  Returns
+// false when rows [0, n + L) of sequence b would leave the cache or pass its
+// capacity (paged: the blocks its table row can name).  off: the first row
+// (contiguous caches).
 __device__ __forceinline__ bool seq_in_range(const Params &p, int b, int n, int64_t &off) {
-  off = p.seq_offset[b];
   const int64_t total = (int64_t)n + p.L;
-  bool ok = n >= 0 && off >= 0 && total <= p.max_seq_len && off + total <= p.num_rows;
+  bool ok;
+  if (p.btab) {
+    off = 0;
+    ok = n >= 0 && total <= p.max_seq_len && total <= ((int64_t)p.max_blocks << p.bs_log2);
+  } else {
+    off = p.seq_offset[b];
+    ok = n >= 0 && off >= 0 && total <= p.max_seq_len && off + total <= p.num_rows;
+  }
   if (ok && p.capacity) ok = total <= (int64_t)p.capacity[b];
   return ok;
+}
+
+// Cache row of token t of sequence b (off from seq_in_range); -1 when a paged
+// cache's table names a block outside the allocated rows.
+__device__ __forceinline__ int64_t cache_row(const Params &p, int b, int64_t off, int64_t t) {
+  if (!p.btab) return off + t;
+  const int64_t blk = p.btab[(int64_t)b * p.max_blocks + (t >> p.bs_log2)];
+  if (blk < 0 || blk >= (p.num_rows >> p.bs_log2)) return -1;
+  return (blk << p.bs_log2) + (t & ((1 << p.bs_log2) - 1));
 }
 
 __device__ __forceinline__ void flag_error(const Params &p) {

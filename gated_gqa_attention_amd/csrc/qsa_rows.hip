@@ -43,9 +43,12 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(Params p, int do_q, 
   }
   __syncthreads();
   int n = 0;
-  int64_t off = 0;
+  int64_t off = 0, row = 0;
   bool kv_ok = true;
-  if (nk) kv_ok = seq_in_range(p, b, n = p.seq_lens[b], off);
+  if (nk) {
+    kv_ok = seq_in_range(p, b, n = p.seq_lens[b], off);
+    if (kv_ok) kv_ok = (row = cache_row(p, b, off, (int64_t)n + l)) >= 0;   // the row this new token goes to
+  }
   if (!kv_ok && threadIdx.x == 0) flag_error(p);
 
   // every lane runs every pass (the rotation permutes across lanes); rows past
@@ -88,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(Params p, int do_q, 
     if (!valid) continue;
     if (is_k) {
       if (!kv_ok) continue;
-      const int64_t dst = ((off + n + l) * p.Hkv + head) * D + E * m16;
+      const int64_t dst = (row * p.Hkv + head) * D + E * m16;
       const T *vsrc = (const T *)p.v_new + (bl * p.Hkv + head) * D + E * m16;
 #pragma unroll
       for (int j = 0; j < E; ++j) {

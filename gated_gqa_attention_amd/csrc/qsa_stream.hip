@@ -82,8 +82,9 @@ struct WaitUnits<LPS, 0> {
 // keys, normalise and rotate those too.  Then all four wavefronts meet, take
 // their query operands and run the stages together; refills of the ring are
 // shared by all four.
-// lgh packs L (bits 0-7), G (bits 8-15) and r/2 (bits 16-31).
-template <int D, int RTM>
+// lgh packs L (bits 0-7), G (bits 8-15) and r/2 (bits 16-31).  PAGED: the
+// cache rows go through a block table.
+template <int D, int RTM, bool PAGED>
 __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restrict__ seq_lens,
                                                           const int64_t *__restrict__ seq_offset,
                                                           const bf16_t *__restrict__ q_gate,
@@ -118,11 +119,12 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   const int chunk = blockIdx.x / nslot, slot = blockIdx.x % nslot;
   const int b = slot / hkv, kvh = slot % hkv;
   const int L = lgh & 0xff, Gq = (lgh >> 8) & 0xff, half = lgh >> 16, Hq = Gq * hkv;
+  constexpr bool paged = PAGED;                         // rows through a block table (seq_offset not read)
   const int R = L * Gq;
 
   // ------------------------------------------------------------ round trip 1
   const int n = seq_lens[b];
-  const int64_t off = seq_offset[b];
+  const int64_t off = paged ? 0 : seq_offset[b];
   const int ck = p.chunk_keys, msl = p.max_seq_len, pchunks = p.chunks, even = p.even_split;
   const int64_t nrows = p.num_rows;
   const bf16_t *const kc = (const bf16_t *)p.kc;
@@ -162,7 +164,9 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   // segment are issued with the sequence length, not one round trip after it.
   asm volatile("" ::"s"(knew), "s"(vnew), "s"(wkp));
   const int64_t total = (int64_t)n + L;
-  const bool in_range = n >= 0 && off >= 0 && total <= msl && off + total <= nrows;
+  const int bsl = p.bs_log2, mblk = p.max_blocks;
+  const bool in_range = n >= 0 && total <= msl &&
+                        (paged ? total <= ((int64_t)mblk << bsl) : off >= 0 && off + total <= nrows);
   const int64_t kend = total;
   const int nch = tile_chunk_count(kend, even, pchunks, ck);
   if (chunk >= nch) return;
@@ -193,6 +197,43 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   const int64_t cend = min(k1, (int64_t)n);             // cached keys [k0, cend)
   const int nst = cend > k0 ? (int)((cend - k0 + G::SK - 1) / G::SK) : 0;
 
+  // Paged caches: the physical block of each logical block of this chunk's keys
+  // [k0, k1) (its new rows too), block blk0 + i in lane i of bid0 (i < 64) or
+  // of bid1 (i >= 64); the host keeps a chunk within 128 blocks.  A block id
+  // outside the allocated rows makes this chunk's result NaN (its output, or
+  // its statistics for the merge kernel) and nothing is read or written there.
+  int bid0 = 0, bid1 = 0, blk0 = 0;
+  if constexpr (PAGED) {
+    const int32_t *const trow = p.btab + (int64_t)b * mblk;
+    blk0 = (int)(k0 >> bsl);
+    const int nblk = (int)(((max(k1, k0 + 1) - 1) >> bsl) - blk0 + 1);
+    bid0 = trow[min(blk0 + lane, mblk - 1)];
+    bid1 = trow[min(blk0 + kWave + lane, mblk - 1)];
+    const int64_t nphys = nrows >> bsl;
+    const bool bad = (lane < nblk && (bid0 < 0 || bid0 >= nphys)) ||
+                     (lane + kWave < nblk && (bid1 < 0 || bid1 >= nphys));
+    if (__any(bad)) {
+      if (nch == 1) {
+        for (int e = t; e < R * D; e += kThreads) {
+          const int r = e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
+          ((bf16_t *)p.out)[(((int64_t)b * L + l) * Hq + h) * D + d] = (bf16_t)__builtin_nanf("");
+        }
+      } else if (t < R) {
+        *(float2 *)(p.part_ml + (((int64_t)slot * pchunks + chunk) * p.rows + t) * 2) =
+            make_float2(__builtin_nanf(""), __builtin_nanf(""));
+      }
+      if (t == 0) flag_error(p);
+      return;
+    }
+  }
+  // row of key tk (per lane) of this chunk in a paged cache
+  auto paged_row = [&](int64_t tk) {
+    const int i = (int)(tk >> bsl) - blk0;
+    const int a0 = __builtin_amdgcn_ds_bpermute(4 * (i & (kWave - 1)), bid0);
+    const int a1 = __builtin_amdgcn_ds_bpermute(4 * (i & (kWave - 1)), bid1);
+    return ((int64_t)(i < kWave ? a0 : a1) << bsl) + (tk & ((1 << bsl) - 1));
+  };
+
   // ------------------------------------------------------------ ring fill
   const unsigned kring_lds = (unsigned)(uintptr_t)(lds_void *)kring;
   const unsigned vring_lds = (unsigned)(uintptr_t)(lds_void *)vring;
@@ -201,14 +242,29 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   // is addressed from the stage's first key (wave-uniform, in SGPRs) plus a
   // 32-bit lane offset shared by K and V.
   const unsigned rowb = (unsigned)(hkv * D * 2);       // bytes between consecutive keys of one KV head
-  // ub: the wave's first unit (wave-uniform); the lane copies unit ub + lane
+  // ub: the wave's first unit (wave-uniform); the lane copies unit ub + lane.
+  // In a paged cache the rows of one stage need not be contiguous: each lane
+  // then addresses its own row (64-bit), and base is the tensor's.
   auto copy_unit = [&](const bf16_t *base, unsigned ring_lds, int st, int ub, int last) {
     const int u = ub + lane;
     const int key = u / G::OCT, pos = u % G::OCT, oct = pos ^ (key & G::SW);
-    const unsigned voff = (unsigned)min(key, last) * rowb + 16u * (unsigned)oct;
-    dma16_sbase(base, voff, ring_lds + (st % NS) * G::STAGE + 16 * ub);
+    const unsigned lds = ring_lds + (st % NS) * G::STAGE + 16 * ub;
+    if constexpr (PAGED) {
+      // blocks hold at least one stage, so the stage's keys lie in its first
+      // block or the next one: both ids by uniform lane reads, a select per lane
+      const int64_t ts = k0 + (int64_t)G::SK * st, tk = ts + min(key, last);
+      const int i0 = (int)(ts >> bsl) - blk0, i1 = i0 + 1;
+      const int blo = __builtin_amdgcn_readlane(i0 < kWave ? bid0 : bid1, i0 & (kWave - 1));
+      const int bhi = __builtin_amdgcn_readlane(i1 < kWave ? bid0 : bid1, i1 & (kWave - 1));
+      const int64_t blk = (tk >> bsl) == (ts >> bsl) ? blo : bhi;
+      const int64_t row = (blk << bsl) + (tk & ((1 << bsl) - 1));
+      dma16_vaddr(base + (row * hkv + kvh) * D + 8 * oct, lds);
+    } else {
+      dma16_sbase(base, (unsigned)min(key, last) * rowb + 16u * (unsigned)oct, lds);
+    }
   };
   auto stage_src = [&](int st, bool is_k) {
+    if constexpr (PAGED) return is_k ? kc : vc;
     return (is_k ? kc : vc) + ((off + k0 + (int64_t)G::SK * st) * hkv + kvh) * D;
   };
   auto stage_last = [&](int st) {   // keys past the chunk repeat its last key
@@ -255,7 +311,8 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
         knraw[k].load(knew + src);
         vnraw[k].load(vnew + src);
       } else {                                          // rows n + l of the cache (in range: checked above)
-        const int64_t src = ((off + n + l) * hkv + kvh) * D + E * m16;
+        const int64_t row = paged ? paged_row((int64_t)n + l) : off + n + l;
+        const int64_t src = (row * hkv + kvh) * D + E * m16;
         knraw[k].load(kc + src);
         vnraw[k].load(vc + src);
       }
@@ -531,8 +588,9 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   if (tail && fuse_new) {
     for (int u = t; u < 16 * G::OCT; u += kThreads) {
       const int l = u / G::OCT, oct = u % G::OCT;
+      const int64_t row = paged ? paged_row((int64_t)n + min(l, L - 1)) : off + n + l;
       if (l < L) {
-        const int64_t dst = ((off + n + l) * hkv + kvh) * D + 8 * oct;
+        const int64_t dst = (row * hkv + kvh) * D + 8 * oct;
         *(uint4 *)((bf16_t *)p.kc + dst) = *(const uint4 *)(nkb + swz<G::SW>(l, oct, RB));
         *(uint4 *)((bf16_t *)p.vc + dst) = *(const uint4 *)(nvb + swz<G::SW>(l, oct, RB));
       }
@@ -540,24 +598,29 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   }
 }
 
-template <int D, int RTM>
+template <int D, int RTM, bool PAGED>
 static void launch_stream_rt(const Params &p, hipStream_t s, const Timing &tm) {
   const int nslot = p.B * p.Hkv;
   const int64_t blocks = (int64_t)nslot * p.chunks;
   const int lgh = p.L | (p.G << 8) | ((p.r / 2) << 16);
-  launch_kernel(stream_kernel<D, RTM>, blocks, s, tm, p.seq_lens, p.seq_offset, (const bf16_t *)p.q_gate,
+  launch_kernel(stream_kernel<D, RTM, PAGED>, blocks, s, tm, p.seq_lens, p.seq_offset, (const bf16_t *)p.q_gate,
                 (const bf16_t *)p.wq, p.positions, nslot, p.Hkv, lgh, p);
+}
+
+template <int D, bool PAGED>
+static hipError_t launch_stream_dp(const Params &p, hipStream_t s, const Timing &tm) {
+  switch ((p.rows + 15) / 16) {
+    case 1: launch_stream_rt<D, 1, PAGED>(p, s, tm); break;
+    case 2: launch_stream_rt<D, 2, PAGED>(p, s, tm); break;
+    case 3: launch_stream_rt<D, 3, PAGED>(p, s, tm); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_stream_d(const Params &p, hipStream_t s, const Timing &tm) {
-  switch ((p.rows + 15) / 16) {
-    case 1: launch_stream_rt<D, 1>(p, s, tm); break;
-    case 2: launch_stream_rt<D, 2>(p, s, tm); break;
-    case 3: launch_stream_rt<D, 3>(p, s, tm); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return p.btab ? launch_stream_dp<D, true>(p, s, tm) : launch_stream_dp<D, false>(p, s, tm);
 }
 
 hipError_t launch_stream_bf16(const Params &p, hipStream_t s, const Timing &tm) {

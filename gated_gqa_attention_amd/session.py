@@ -11,9 +11,12 @@ from .workloads import DTYPES, Workload
 
 class Session:
     def __init__(self, w: Workload, inputs: dict, device="cuda", force_splits: int = 0,
-                 max_seq_len: int | None = None, stream=None, softmax_scale: float = 0.0):
+                 max_seq_len: int | None = None, stream=None, softmax_scale: float = 0.0,
+                 block_size: int = 0):
+        """block_size > 0: the cache is given in paged form (inputs hold block_table)."""
         self.w = w
         self.softmax_scale = softmax_scale
+        self.block_size = block_size
         self.dev = {k: v.to(device) if isinstance(v, torch.Tensor) else v for k, v in inputs.items()}
         d = self.dev
         if max_seq_len is None:
@@ -28,7 +31,10 @@ class Session:
         self.out = torch.empty((w.batch, w.q_len, w.num_q_heads, w.head_dim), dtype=self.dtype,
                                device=device)
         self.cfg = self._cfg(self.workspace)
-        self.kv = binding.make_kv(d["k_cache"], d["v_cache"], d["seq_offset"], d["capacity"])
+        if block_size:
+            self.kv = binding.make_kv(d["k_cache"], d["v_cache"], None, d["capacity"], d["block_table"], block_size)
+        else:
+            self.kv = binding.make_kv(d["k_cache"], d["v_cache"], d["seq_offset"], d["capacity"])
 
     def _cfg(self, workspace):
         w, d = self.w, self.dev

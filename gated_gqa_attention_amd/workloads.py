@@ -169,3 +169,50 @@ def make_proj_inputs(w: Workload, hidden: int = HIDDEN_4B, seed: int | None = No
     w_qkv = torch.randn((nqkv, hidden), generator=gen) / hidden ** 0.5
     w_o = torch.randn((hidden, w.num_q_heads * D), generator=gen) / (w.num_q_heads * D) ** 0.5
     return {"x": x.to(dt).contiguous(), "w_qkv": w_qkv.to(dt).contiguous(), "w_o": w_o.to(dt).contiguous()}
+
+
+def paged_layout(capacity: torch.Tensor, seq_offset: torch.Tensor, block_size: int, seed: int = 0,
+                 spare_blocks: int = 3):
+    """Placement of a contiguous cache's rows in blocks: sequence b's capacity
+    rows are cut into blocks of `block_size` rows placed at physical blocks
+    drawn by a seeded permutation (plus a few spare blocks that no sequence
+    owns).  Returns (block_table [B, max_blocks] int32 with -1 past each
+    sequence's blocks, src rows, dst rows, physical row count)."""
+    cap = capacity.to(torch.int64)
+    B = cap.numel()
+    nblk = (cap + block_size - 1) // block_size
+    nphys = int(nblk.sum()) + spare_blocks
+    max_blocks = int(nblk.max()) + 1
+    perm = torch.randperm(nphys, generator=torch.Generator("cpu").manual_seed(seed)).to(torch.int32)
+    table = torch.full((B, max_blocks), -1, dtype=torch.int32)
+    first = torch.cumsum(nblk, 0) - nblk
+    for b in range(B):
+        table[b, :int(nblk[b])] = perm[int(first[b]):int(first[b] + nblk[b])]
+    seq = torch.repeat_interleave(torch.arange(B), cap)
+    t = torch.arange(int(cap.sum())) - torch.repeat_interleave(torch.cumsum(cap, 0) - cap, cap)
+    src = seq_offset.to(torch.int64)[seq] + t
+    dst = table[seq, t // block_size].to(torch.int64) * block_size + t % block_size
+    return table, src, dst, nphys * block_size
+
+
+def to_paged(inputs: dict, block_size: int, seed: int = 0, spare_blocks: int = 3) -> dict:
+    """The same cache in paged form (see paged_layout); data movement only.
+    Returns a copy of `inputs` with k_cache, v_cache and block_table replaced
+    or added.  Works on CPU or device tensors."""
+    table, src, dst, rows = paged_layout(inputs["capacity"].cpu(), inputs["seq_offset"].cpu(), block_size, seed,
+                                         spare_blocks)
+    out = dict(inputs)
+    for name in ("k_cache", "v_cache"):
+        c = inputs[name]
+        pc = torch.zeros((rows,) + tuple(c.shape[1:]), dtype=c.dtype, device=c.device)
+        pc[dst.to(c.device)] = c[src.to(c.device)]
+        out[name] = pc
+    out["block_table"] = table.to(inputs["capacity"].device)
+    return out
+
+
+def paged_rows(cache: torch.Tensor, table: torch.Tensor, block_size: int, seq: int, count: int) -> torch.Tensor:
+    """Rows 0 .. count-1 of sequence `seq` gathered from a paged cache."""
+    t = torch.arange(count)
+    blk = table[seq].to(torch.int64)[t // block_size].to(cache.device)
+    return cache[blk * block_size + (t % block_size).to(cache.device)]

@@ -44,11 +44,17 @@
  * Errors.  Every entry point validates its arguments on the host before any
  * launch and returns a negative qsa_status on failure, with a message for the
  * calling thread in qsa_last_error().  Nothing falls back to another path.
- * Values that live on the device (seq_lens, seq_offset, capacity) are checked
- * by the kernels: a sequence whose rows would leave the cache, exceed its
- * capacity or exceed cfg->max_seq_len gets NaN outputs, its cache is not
- * written, and bit 0 of the int32 at the start of the workspace is set
- * (sticky until the caller clears it).
+ * Values that live on the device (seq_lens, seq_offset, capacity, block_table)
+ * are checked by the kernels: a sequence whose rows would leave the cache,
+ * exceed its capacity or exceed cfg->max_seq_len gets NaN outputs, its cache
+ * is not written, and bit 0 of the int32 at the start of the workspace is set
+ * (sticky until the caller clears it).  A paged sequence whose table names a
+ * block outside the cache gets NaN outputs and sets that bit too; nothing is
+ * read or written outside the cache (a new row whose own block is valid may
+ * still be stored there).  Paged caches: the attention call takes them on the short-query route
+ * (decode, verify, batched decode: q_len * G <= 48, q_len <= 16, bf16) with key
+ * chunks of at most 127 blocks, and returns QSA_ERR_UNSUPPORTED otherwise;
+ * qsa_append_kv takes them always.
  */
 #ifndef QSA_H
 #define QSA_H
@@ -99,16 +105,28 @@ typedef struct {
   void *timing_end;          /* optional hipEvent_t, recorded right after that launch */
 } qsa_cfg;
 
-/* KV cache of one attention layer.  Token-major: row t of sequence b is
- * [num_kv_heads][head_dim] elements of cfg->dtype at element offset
- * (seq_offset[b] + t) * num_kv_heads * head_dim of k (and of v).  Sequences may
- * be packed back to back (ragged batches) or strided uniformly. */
+/* KV cache of one attention layer.  Token-major: a row is [num_kv_heads][head_dim]
+ * elements of cfg->dtype, and row t of sequence b sits at element offset
+ * row(b, t) * num_kv_heads * head_dim of k (and of v), where
+ *   contiguous (block_table == NULL): row(b, t) = seq_offset[b] + t; sequences
+ *     may be packed back to back (ragged batches) or strided uniformly;
+ *   paged (block_table != NULL): row(b, t) = block_table[b][t / block_size] *
+ *     block_size + t % block_size; a sequence's rows live in blocks of
+ *     block_size rows that the caller hands out as the sequence grows
+ *     (TensorFold issue #503: grow-as-used K/V; Atlas qwen3_5/mod.rs module
+ *     doc: paged KV in the production decode path).  seq_offset is not read.
+ * The two layouts give bitwise the same results for the same rows. */
 typedef struct {
   void *k;                   /* device base of the K rows */
   void *v;                   /* device base of the V rows */
-  const int64_t *seq_offset; /* device [B]: first row of sequence b (64-bit: caches may exceed 2^31 elements) */
-  const int32_t *capacity;   /* device [B]: rows owned by sequence b, or NULL for "up to num_rows" */
-  int64_t num_rows;          /* host: rows allocated in k and in v */
+  const int64_t *seq_offset; /* device [B]: first row of sequence b (64-bit: caches may exceed 2^31
+                                elements); contiguous layout only */
+  const int32_t *capacity;   /* device [B]: rows owned by sequence b, or NULL for "up to num_rows"
+                                (contiguous) / "max_blocks * block_size" (paged) */
+  int64_t num_rows;          /* host: rows allocated in k and in v (paged: a multiple of block_size) */
+  const int32_t *block_table; /* device [B][max_blocks] physical block ids, or NULL (contiguous) */
+  int32_t block_size;        /* paged: rows per block, a power of two in [64, 65536] */
+  int32_t max_blocks;        /* paged: entries per sequence in block_table (row stride) */
 } qsa_kv_cache;
 
 /* Bytes of workspace a call with this cfg needs (split-K partials, the

@@ -213,6 +213,34 @@ def test_projection_arguments_checked_before_launch():
     assert lib.qsa_o_proj(x, None, 2560, ctypes.byref(ok), q) == binding.QSA_ERR_INVALID
 
 
+def test_paged_cache_descriptor_checked_before_launch():
+    lib = binding.load()
+    w = WORKLOADS["decode_4b"]
+    c = cfg_for(w)
+    c.workspace, c.workspace_bytes = FAKE + (3 << 30), binding.workspace_size(cfg_for(w))
+    out = FAKE + (2 << 30)
+
+    def call(kv, cfg=c):
+        return lib.qsa_gated_attention(FAKE, FAKE, FAKE, ctypes.byref(kv), FAKE, FAKE, ctypes.byref(cfg), out)
+
+    for bs, rows, mb in ((48, 4800, 8), (32, 4096, 8), (96, 4800, 8), (64, 4100, 8), (64, 4096, 0)):
+        kv = binding.KVCache(FAKE, FAKE + (1 << 30), None, None, rows, FAKE + (4 << 30), bs, mb)
+        assert call(kv) == binding.QSA_ERR_INVALID, (bs, rows, mb)
+    # a contiguous cache needs seq_offset
+    assert call(binding.KVCache(FAKE, FAKE + (1 << 30), None, None, 8192)) == binding.QSA_ERR_INVALID
+    # the tile route takes no paged cache
+    p = cfg_for(WORKLOADS["prefill_4b"])
+    p.workspace, p.workspace_bytes = FAKE + (3 << 30), binding.workspace_size(cfg_for(WORKLOADS["prefill_4b"]))
+    kv = binding.KVCache(FAKE, FAKE + (1 << 30), None, None, 1 << 16, FAKE + (4 << 30), 64, 600)
+    assert call(kv, p) == binding.QSA_ERR_UNSUPPORTED
+    # chunks longer than 128 blocks
+    f = cfg_for(w, force_splits=1)
+    f.workspace, f.workspace_bytes = FAKE + (3 << 30), binding.workspace_size(cfg_for(w, force_splits=1))
+    kv = binding.KVCache(FAKE, FAKE + (1 << 30), None, None, 1 << 16, FAKE + (4 << 30), 64, 80)
+    assert call(kv, f) == binding.QSA_ERR_UNSUPPORTED
+    assert "128 blocks" in binding.last_error()
+
+
 def test_workspace_scales_with_chunks():
     w = WORKLOADS["decode_4b"]
     one = binding.workspace_size(cfg_for(w, force_splits=1))
