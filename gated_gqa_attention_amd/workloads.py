@@ -216,3 +216,30 @@ def paged_rows(cache: torch.Tensor, table: torch.Tensor, block_size: int, seq: i
     t = torch.arange(count)
     blk = table[seq].to(torch.int64)[t // block_size].to(cache.device)
     return cache[blk * block_size + (t % block_size).to(cache.device)]
+
+
+def make_turbo8_inputs(w: Workload, variant: str = "graded", seed: int | None = None) -> dict:
+    """Inputs of a call on a Turbo8 cache: the bf16 inputs of make_inputs (their
+    cache replaced) plus cached rows in Turbo8 storage drawn directly: codes
+    [rows, Hkv, D] (uint8) as the E4M3 casts of 128 N(0, 1) clamped to +-448, and
+    scales [rows, Hkv, D/16] (bf16) as exp(0.25 N(0, 1)) / 128, so that the
+    stored rows are about N(0, 1); rows past n_b are zero.  Random draws and
+    library casts only (torch's float8_e4m3fn and bfloat16 conversions)."""
+    x = make_inputs(w, variant=variant, seed=seed)
+    gen = torch.Generator("cpu").manual_seed((w.seed if seed is None else seed) + 2000)
+    rows = x["k_cache"].shape[0]
+    D, Hkv = w.head_dim, w.num_kv_heads
+    n, off = x["seq_lens"], x["seq_offset"]
+    out = {k: v for k, v in x.items() if k not in ("k_cache", "v_cache")}
+    for t in ("k", "v"):
+        codes = torch.zeros((rows, Hkv, D), dtype=torch.uint8)
+        scales = torch.zeros((rows, Hkv, D // 16), dtype=torch.bfloat16)
+        for b in range(w.batch):
+            nb, o = int(n[b]), int(off[b])
+            if nb:
+                vals = (128.0 * torch.randn((nb, Hkv, D), generator=gen)).clamp(-448.0, 448.0)
+                codes[o:o + nb] = vals.to(torch.float8_e4m3fn).view(torch.uint8)
+                scales[o:o + nb] = (torch.exp(0.25 * torch.randn((nb, Hkv, D // 16), generator=gen)) / 128.0).to(
+                    torch.bfloat16)
+        out[f"{t}_codes"], out[f"{t}_scales"] = codes, scales
+    return out

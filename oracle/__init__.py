@@ -87,6 +87,19 @@ def _load():
         lib.qsa_oracle_linear.argtypes = [p, p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, p]
         lib.qsa_oracle_qkv_proj.restype = ctypes.c_int
         lib.qsa_oracle_qkv_proj.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int32, p, p, p, p, p]
+        lib.qsa_oracle_e4m3_value.restype = ctypes.c_double
+        lib.qsa_oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.qsa_oracle_e4m3_code.restype = ctypes.c_uint8
+        lib.qsa_oracle_e4m3_code.argtypes = [ctypes.c_double]
+        lib.qsa_oracle_wht.restype = ctypes.c_int
+        lib.qsa_oracle_wht.argtypes = [p, ctypes.c_int, p]
+        lib.qsa_oracle_turbo8_quantize.restype = ctypes.c_int
+        lib.qsa_oracle_turbo8_quantize.argtypes = [p, ctypes.c_int, p, p]
+        lib.qsa_oracle_turbo8_new_kv.restype = ctypes.c_int
+        lib.qsa_oracle_turbo8_new_kv.argtypes = [ctypes.POINTER(_Cfg), p, p, p, p, p, p, p, p]
+        lib.qsa_oracle_turbo8_attention.restype = ctypes.c_int
+        lib.qsa_oracle_turbo8_attention.argtypes = [ctypes.POINTER(_Cfg), p, p, p, p, p, p, p, p, p, p, p, p, p,
+                                                    p, ctypes.c_int64, p]
         lib.qsa_oracle_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -275,6 +288,133 @@ def o_proj(geo: Geometry, hidden: int, attn, w_o):
     if _f64(w_o).shape != (hidden, geo.num_q_heads * geo.head_dim):
         raise ValueError("w_o has the wrong shape")
     return linear(a, w_o, geo.dtype)
+
+
+# ------------------------------------------------------------------ Turbo8
+# Turbo8 KV cache (Atlas docs, spark_model/forward/qwen3_5/mod.rs, MetalKvDtype::
+# Turbo8 and LayerKvCache::alloc): FP8 E4M3 codes, one per element, and bf16
+# scales, one per group of 16 elements, in the Walsh-Hadamard rotated basis,
+# with WHT(Q) / iWHT(out) bookends around the attention.  The readings where the
+# page is silent (scale rule, rounding, WHT normalisation) are in qsa_oracle.h.
+
+def _u8(t):
+    if isinstance(t, torch.Tensor):
+        t = t.detach().cpu()
+        t = t.view(torch.uint8) if t.dtype != torch.uint8 else t
+        t = t.numpy()
+    return np.ascontiguousarray(np.asarray(t, dtype=np.uint8))
+
+
+def _u16(t):
+    if isinstance(t, torch.Tensor):
+        t = t.detach().cpu()
+        t = t.view(torch.int16) if t.dtype in (torch.bfloat16, torch.int16) else t
+        t = t.numpy()
+    return np.ascontiguousarray(np.asarray(t).view(np.uint16) if np.asarray(t).dtype == np.int16
+                                else np.asarray(t, dtype=np.uint16))
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """Values of E4M3 codes (uint8 array)."""
+    lib = _load()
+    c = _u8(codes)
+    return np.vectorize(lambda v: lib.qsa_oracle_e4m3_value(int(v)), otypes=[np.float64])(c)
+
+
+def e4m3_code(x) -> np.ndarray:
+    """E4M3 codes of x (nearest, ties to even, saturating)."""
+    lib = _load()
+    return np.vectorize(lambda v: lib.qsa_oracle_e4m3_code(float(v)), otypes=[np.uint8])(_f64(x))
+
+
+def wht(x) -> np.ndarray:
+    """Orthonormal Walsh-Hadamard transform along the last axis."""
+    lib = _load()
+    a = _f64(x)
+    flat = a.reshape(-1, a.shape[-1])
+    out = np.empty_like(flat)
+    for i in range(flat.shape[0]):
+        row = np.ascontiguousarray(flat[i])
+        res = np.empty_like(row)
+        if lib.qsa_oracle_wht(_ptr(row), row.size, _ptr(res)) != 0:
+            raise ValueError("the transform length must be a power of two")
+        out[i] = res
+    return out.reshape(a.shape)
+
+
+def turbo8_quantize(x):
+    """Turbo8 codes (uint8, same shape) and scale bits (uint16, last axis / 16) of x."""
+    lib = _load()
+    a = _f64(x)
+    flat = a.reshape(-1, a.shape[-1])
+    codes = np.empty(flat.shape, dtype=np.uint8)
+    scales = np.empty((flat.shape[0], flat.shape[1] // 16), dtype=np.uint16)
+    for i in range(flat.shape[0]):
+        row = np.ascontiguousarray(flat[i])
+        cr = np.empty(row.size, dtype=np.uint8)
+        sr = np.empty(row.size // 16, dtype=np.uint16)
+        if lib.qsa_oracle_turbo8_quantize(_ptr(row), row.size, _ptr(cr), _ptr(sr)) != 0:
+            raise ValueError("Turbo8 rows need a multiple of 16 elements")
+        codes[i], scales[i] = cr, sr
+    return codes.reshape(a.shape), scales.reshape(a.shape[:-1] + (a.shape[-1] // 16,))
+
+
+def turbo8_dequantize(codes, scale_bits) -> np.ndarray:
+    """codes x scales in double (the cache rows a Turbo8 attention reads)."""
+    c = e4m3_value(codes)
+    sb = _u16(scale_bits).astype(np.uint32) << 16
+    s = sb.view(np.float32).astype(np.float64)
+    return c * np.repeat(s, 16, axis=-1)
+
+
+def turbo8_new_kv(geo: Geometry, k_new, v_new, w_k, positions):
+    """Turbo8 rows of the new tokens: (k_codes, k_scales, v_codes, v_scales)."""
+    lib = _load()
+    kn, vn, wk, pos = _f64(k_new), _f64(v_new), _f64(w_k), _i32(positions)
+    D = geo.head_dim
+    kc = np.empty(kn.shape, dtype=np.uint8)
+    vc = np.empty(kn.shape, dtype=np.uint8)
+    ks = np.empty(kn.shape[:-1] + (D // 16,), dtype=np.uint16)
+    vs = np.empty_like(ks)
+    if lib.qsa_oracle_turbo8_new_kv(ctypes.byref(geo._c()), _ptr(kn), _ptr(vn), _ptr(wk), _ptr(pos), _ptr(kc),
+                                    _ptr(ks), _ptr(vc), _ptr(vs)) != 0:
+        raise ValueError("oracle rejected the configuration")
+    return kc, ks, vc, vs
+
+
+def turbo8_attention(geo: Geometry, q_gate, w_q, k_codes, k_scales, v_codes, v_scales, seq_offset, seq_lens,
+                     positions, new=None, rows=None):
+    """Gated attention over a Turbo8 cache; `new` = turbo8_new_kv(...) output for
+    keys n_b .. n_b+L-1, or None when those rows are in the cache."""
+    lib = _load()
+    qg, wq = _f64(q_gate), _f64(w_q)
+    kc, ks, vc, vs = _u8(k_codes), _u16(k_scales), _u8(v_codes), _u16(v_scales)
+    off, sl, pos = _i64(seq_offset), _i32(seq_lens), _i32(positions)
+    nk = [None] * 4 if new is None else [_u8(new[0]), _u16(new[1]), _u8(new[2]), _u16(new[3])]
+    D = geo.head_dim
+    if rows is None:
+        out = np.empty((geo.batch, geo.q_len, geo.num_q_heads, D))
+        r, n = None, 0
+    else:
+        r = _i64(rows)
+        n = r.size
+        out = np.empty((n, D))
+    rc = lib.qsa_oracle_turbo8_attention(ctypes.byref(geo._c()), _ptr(qg), _ptr(wq), _ptr(kc), _ptr(ks), _ptr(vc),
+                                         _ptr(vs), _ptr(off), _ptr(sl), _ptr(pos), _ptr(nk[0]), _ptr(nk[1]),
+                                         _ptr(nk[2]), _ptr(nk[3]), _ptr(r), n, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the configuration or a row index")
+    return out
+
+
+def turbo8_gated_attention(geo: Geometry, inputs: dict, rows=None, fused=True):
+    """Whole call on a Turbo8 cache (inputs from make_turbo8_inputs): quantize and
+    append the new rows (when fused), then attend.  Returns (out, new rows)."""
+    new = turbo8_new_kv(geo, inputs["k_new"], inputs["v_new"], inputs["w_k"], inputs["positions"]) if fused else None
+    out = turbo8_attention(geo, inputs["q_gate"], inputs["w_q"], inputs["k_codes"], inputs["k_scales"],
+                           inputs["v_codes"], inputs["v_scales"], inputs["seq_offset"], inputs["seq_lens"],
+                           inputs["positions"], new=new, rows=rows)
+    return out, new
 
 
 def threads() -> int:

@@ -219,6 +219,193 @@ int qsa_oracle_qkv_proj(const qsa_oracle_cfg *c, int32_t hidden, const double *x
   return 0;
 }
 
+/* ------------------------------------------------------------------ Turbo8 */
+
+double qsa_oracle_e4m3_value(uint8_t code) {
+  const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double mag = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+uint8_t qsa_oracle_e4m3_code(double x) {
+  const uint8_t sign = (x < 0 || (x == 0 && signbit(x))) ? 0x80 : 0;
+  double a = fabs(x);
+  if (a >= 448.0) return sign | 0x7E;              /* saturate: 1.75 * 2^8 */
+  if (a < ldexp(1.0, -6)) {                        /* subnormal grid m * 2^-9; m = 8 is 2^-6 */
+    const double m = nearbyint(ldexp(a, 9));       /* ties to even */
+    return sign | (uint8_t)m;
+  }
+  int e;
+  frexp(a, &e);                                    /* a = f * 2^e, 0.5 <= f < 1: exponent e - 1 */
+  const int ex = e - 1;                            /* -6 .. 8 */
+  const double q = nearbyint(ldexp(a, 3 - ex));    /* 8 .. 16, ties to even */
+  return sign | (uint8_t)(((ex + 7) << 3) + (int)q - 8);   /* q = 16 carries into the exponent */
+}
+
+int qsa_oracle_wht(const double *x, int n, double *y) {
+  if (n < 1 || (n & (n - 1))) return -1;
+  const double norm = 1.0 / sqrt((double)n);
+  for (int i = 0; i < n; ++i) {
+    double acc = 0.0;
+    for (int j = 0; j < n; ++j) acc += (__builtin_popcount((unsigned)(i & j)) & 1) ? -x[j] : x[j];
+    y[i] = acc * norm;
+  }
+  return 0;
+}
+
+static uint16_t bf16_bits(double x) {           /* RNE to bf16, as bits */
+  float f = (float)qsa_oracle_round(x, 8);
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
+static double bf16_value(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+int qsa_oracle_turbo8_quantize(const double *x, int n, uint8_t *codes, uint16_t *scale_bits) {
+  if (n < 16 || n % 16) return -1;
+  for (int g = 0; g < n / 16; ++g) {
+    float xf[16], amax = 0.f;
+    for (int i = 0; i < 16; ++i) {
+      xf[i] = (float)x[16 * g + i];                /* the row in fp32 */
+      amax = fabsf(xf[i]) > amax ? fabsf(xf[i]) : amax;
+    }
+    const float sq = amax / 448.0f;                /* fp32 division */
+    const uint16_t sb = bf16_bits((double)sq);
+    const float s = (float)bf16_value(sb);
+    scale_bits[g] = sb;
+    for (int i = 0; i < 16; ++i) {
+      if (s == 0.f) {
+        codes[16 * g + i] = 0;
+        continue;
+      }
+      float q = xf[i] / s;                         /* fp32 quotient */
+      q = q > 448.f ? 448.f : (q < -448.f ? -448.f : q);
+      codes[16 * g + i] = qsa_oracle_e4m3_code((double)q);
+    }
+  }
+  return 0;
+}
+
+int qsa_oracle_turbo8_new_kv(const qsa_oracle_cfg *c, const double *k_new, const double *v_new,
+                             const double *w_k, const int32_t *positions, uint8_t *k_codes,
+                             uint16_t *k_scales, uint8_t *v_codes, uint16_t *v_scales) {
+  if (!cfg_ok(c) || c->head_dim % 16 || (c->head_dim & (c->head_dim - 1))) return -1;
+  const int L = c->q_len, Hkv = c->num_kv_heads, D = c->head_dim;
+  const int64_t n = (int64_t)c->batch * L * Hkv;
+  int err = 0;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    double *t = (double *)malloc(sizeof(double) * (size_t)D);
+    double *r = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!t || !r) {
+#pragma omp atomic write
+      err = 1;
+      free(t); free(r);
+      continue;
+    }
+    rms_norm(k_new + i * D, w_k, D, c->rms_eps, t);
+    rope(t, c->rotary_dim, c->rope_theta, (double)positions[i / Hkv]);
+    qsa_oracle_wht(t, D, r);
+    qsa_oracle_turbo8_quantize(r, D, k_codes + i * D, k_scales + i * (D / 16));
+    qsa_oracle_wht(v_new + i * D, D, r);
+    qsa_oracle_turbo8_quantize(r, D, v_codes + i * D, v_scales + i * (D / 16));
+    free(t); free(r);
+  }
+  return err ? -1 : 0;
+}
+
+/* one decoded Turbo8 row: codes [D] times their group scales [D/16] */
+static void turbo8_row(const uint8_t *codes, const uint16_t *scales, int D, double *out) {
+  for (int d = 0; d < D; ++d) out[d] = qsa_oracle_e4m3_value(codes[d]) * bf16_value(scales[d / 16]);
+}
+
+int qsa_oracle_turbo8_attention(const qsa_oracle_cfg *c, const double *q_gate, const double *w_q,
+                                const uint8_t *k_codes, const uint16_t *k_scales, const uint8_t *v_codes,
+                                const uint16_t *v_scales, const int64_t *seq_offset, const int32_t *seq_lens,
+                                const int32_t *positions, const uint8_t *nk_codes, const uint16_t *nk_scales,
+                                const uint8_t *nv_codes, const uint16_t *nv_scales, const int64_t *rows,
+                                int64_t n_rows, double *out) {
+  if (!cfg_ok(c) || c->head_dim % 16 || (c->head_dim & (c->head_dim - 1))) return -1;
+  const int given = (nk_codes != NULL) + (nk_scales != NULL) + (nv_codes != NULL) + (nv_scales != NULL);
+  if (given != 0 && given != 4) return -1;
+  const int B = c->batch, L = c->q_len, Hq = c->num_q_heads, Hkv = c->num_kv_heads;
+  const int D = c->head_dim, G = Hq / Hkv;
+  const double scale = scale_of(c);
+  const int64_t total = (int64_t)B * L * Hq;
+  const int64_t count = rows ? n_rows : total;
+  for (int64_t i = 0; i < count; ++i) {
+    const int64_t f = rows ? rows[i] : i;
+    if (f < 0 || f >= total) return -1;
+  }
+  int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < count; ++i) {
+    const int64_t f = rows ? rows[i] : i;
+    const int h = (int)(f % Hq);
+    const int64_t bl = f / Hq;
+    const int l = (int)(bl % L), b = (int)(bl / L), g = h / G;
+    const int64_t n = seq_lens[b], nkeys = n + l + 1;
+    double *q0 = (double *)malloc(sizeof(double) * (size_t)D);
+    double *q = (double *)malloc(sizeof(double) * (size_t)D);
+    double *kv = (double *)malloc(sizeof(double) * (size_t)D);
+    double *o = (double *)calloc((size_t)D, sizeof(double));
+    double *ob = (double *)malloc(sizeof(double) * (size_t)D);
+    double *s = (double *)malloc(sizeof(double) * (size_t)nkeys);
+    if (!q0 || !q || !kv || !o || !ob || !s) {
+#pragma omp atomic write
+      err = 1;
+      free(q0); free(q); free(kv); free(o); free(ob); free(s);
+      continue;
+    }
+    const double *qh = q_gate + f * 2 * D, *zh = qh + D;
+    rms_norm(qh, w_q, D, c->rms_eps, q0);
+    rope(q0, c->rotary_dim, c->rope_theta, (double)positions[bl]);
+    qsa_oracle_wht(q0, D, q);                       /* WHT(Q) bookend */
+    for (int64_t j = 0; j < nkeys; ++j) {
+      if (j >= n && nk_codes) {
+        const int64_t r = ((int64_t)b * L + (j - n)) * Hkv + g;
+        turbo8_row(nk_codes + r * D, nk_scales + r * (D / 16), D, kv);
+      } else {
+        const int64_t r = (seq_offset[b] + j) * Hkv + g;
+        turbo8_row(k_codes + r * D, k_scales + r * (D / 16), D, kv);
+      }
+      double acc = 0.0;
+      for (int d = 0; d < D; ++d) acc += q[d] * kv[d];
+      s[j] = scale * acc;
+    }
+    double m = s[0];
+    for (int64_t j = 1; j < nkeys; ++j) m = s[j] > m ? s[j] : m;
+    double sum = 0.0;
+    for (int64_t j = 0; j < nkeys; ++j) {
+      s[j] = exp(s[j] - m);
+      sum += s[j];
+    }
+    for (int64_t j = 0; j < nkeys; ++j) {
+      if (j >= n && nv_codes) {
+        const int64_t r = ((int64_t)b * L + (j - n)) * Hkv + g;
+        turbo8_row(nv_codes + r * D, nv_scales + r * (D / 16), D, kv);
+      } else {
+        const int64_t r = (seq_offset[b] + j) * Hkv + g;
+        turbo8_row(v_codes + r * D, v_scales + r * (D / 16), D, kv);
+      }
+      const double p = s[j] / sum;
+      for (int d = 0; d < D; ++d) o[d] += p * kv[d];
+    }
+    qsa_oracle_wht(o, D, ob);                       /* iWHT(out) bookend: the transform is its own inverse */
+    double *dst = out + i * D;
+    for (int d = 0; d < D; ++d) dst[d] = qsa_oracle_round(ob[d] / (1.0 + exp(-zh[d])), c->store_bits);
+    free(q0); free(q); free(kv); free(o); free(ob); free(s);
+  }
+  return err ? -1 : 0;
+}
+
 int qsa_oracle_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -105,6 +105,51 @@ int qsa_oracle_linear(const double *x, const double *w, int64_t M, int64_t N, in
 int qsa_oracle_qkv_proj(const qsa_oracle_cfg *cfg, int32_t hidden, const double *x, const double *w_qkv,
                         double *q_gate, double *k_new, double *v_new);
 
+/* ---- Turbo8 KV cache (Atlas docs, spark_model/forward/qwen3_5/mod.rs:
+ * MetalKvDtype::Turbo8 -- FP8 E4M3 data plus bf16 scales for groups of 16
+ * elements, in the Walsh-Hadamard rotated basis; LayerKvCache::alloc -- one
+ * byte per element and two bytes per group of 16, for K and for V;
+ * Qwen35Kernels -- quantizing appends, dequantizing decode attention, and the
+ * WHT(Q) / iWHT(out) bookends).  Readings where the page is silent: the scale
+ * of a group is its largest magnitude over 448 (the largest E4M3 value),
+ * rounded to bf16; codes round x / scale to nearest E4M3, ties to even,
+ * saturating at +-448; the rotation is the orthonormal Walsh-Hadamard
+ * transform over head_dim (Sylvester order, divided by sqrt(head_dim)), which
+ * is its own inverse.  The quantizer takes its decisions in fp32, as the GPU
+ * does: row values rounded to fp32, scale = bf16(amax / 448) with an fp32
+ * division, code = E4M3(fp32 quotient). */
+
+/* Value of an FP8 E4M3 code (OCP: bias 7, 3 mantissa bits, no infinity,
+ * S.1111.111 is NaN). */
+double qsa_oracle_e4m3_value(uint8_t code);
+/* Code of x: round to nearest E4M3 value, ties to even, saturating at +-448
+ * (NaN is never produced). */
+uint8_t qsa_oracle_e4m3_code(double x);
+/* Orthonormal Walsh-Hadamard transform: y[i] = n^-1/2 sum_j (-1)^popcount(i & j) x[j];
+ * n a power of two.  y may not alias x.  Returns 0 or -1. */
+int qsa_oracle_wht(const double *x, int n, double *y);
+/* Quantize n values (n % 16 == 0) to Turbo8: codes[n] and scale_bits[n/16]
+ * (bf16 bit patterns).  Returns 0 or -1. */
+int qsa_oracle_turbo8_quantize(const double *x, int n, uint8_t *codes, uint16_t *scale_bits);
+/* New cache rows in Turbo8: K = quantize(WHT(rope(rmsnorm(k_new) * w_k))),
+ * V = quantize(WHT(v_new)), each [B][L][Hkv][D] codes and [B][L][Hkv][D/16]
+ * scale bits.  Returns 0 or -1. */
+int qsa_oracle_turbo8_new_kv(const qsa_oracle_cfg *cfg, const double *k_new, const double *v_new,
+                             const double *w_k, const int32_t *positions, uint8_t *k_codes,
+                             uint16_t *k_scales, uint8_t *v_codes, uint16_t *v_scales);
+/* Gated attention over a Turbo8 cache: like qsa_oracle_attention, with the
+ * query rotated by WHT after its norm and rotary embedding, keys and values
+ * decoded from codes x scales (cache rows token-major [rows][Hkv][D] codes,
+ * [rows][Hkv][D/16] scale bits; new rows from qsa_oracle_turbo8_new_kv, or
+ * all four NULL when they are already in the cache), and the attention output
+ * rotated back by WHT before the gate.  Returns 0 or -1. */
+int qsa_oracle_turbo8_attention(const qsa_oracle_cfg *cfg, const double *q_gate, const double *w_q,
+                                const uint8_t *k_codes, const uint16_t *k_scales, const uint8_t *v_codes,
+                                const uint16_t *v_scales, const int64_t *seq_offset, const int32_t *seq_lens,
+                                const int32_t *positions, const uint8_t *nk_codes, const uint16_t *nk_scales,
+                                const uint8_t *nv_codes, const uint16_t *nv_scales, const int64_t *rows,
+                                int64_t n_rows, double *out);
+
 /* Number of OpenMP threads the oracle runs with. */
 int qsa_oracle_threads(void);
 
