@@ -16,6 +16,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsa.so"
 
 QSA_OK, QSA_ERR_INVALID, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE, QSA_ERR_DEVICE = 0, -1, -2, -3, -4
 QSA_BF16, QSA_F32 = 0, 1
+QSA_KV_NATIVE, QSA_KV_TURBO8 = 0, 1
 _DT = {torch.bfloat16: QSA_BF16, torch.float32: QSA_F32}
 
 EXPORTS = ("qsa_workspace_size", "qsa_append_kv", "qsa_gated_attention", "qsa_gated_attention_noalloc",
@@ -50,6 +51,7 @@ class KVCache(ctypes.Structure):
         ("seq_offset", ctypes.c_void_p), ("capacity", ctypes.c_void_p),
         ("num_rows", ctypes.c_int64),
         ("block_table", ctypes.c_void_p), ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32), ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
     ]
 
 
@@ -121,12 +123,17 @@ def make_cfg(*, batch, q_len, num_q_heads, num_kv_heads, head_dim, rotary_dim, r
                stream_handle)
 
 
-def make_kv(k_cache, v_cache, seq_offset, capacity=None, block_table=None, block_size=0) -> KVCache:
+def make_kv(k_cache, v_cache, seq_offset, capacity=None, block_table=None, block_size=0,
+            k_scales=None, v_scales=None) -> KVCache:
     """Describe a token-major cache: k/v ``[rows, Hkv, D]``; contiguous with
-    seq_offset int64 ``[B]``, or paged with block_table int32 ``[B, max_blocks]``."""
+    seq_offset int64 ``[B]``, or paged with block_table int32 ``[B, max_blocks]``.
+    With k_scales / v_scales ``[rows, Hkv, D/16]`` (bf16) the cache is Turbo8:
+    k/v then hold E4M3 codes (uint8)."""
     max_blocks = 0 if block_table is None else int(block_table.shape[1])
+    turbo8 = k_scales is not None
     return KVCache(_ptr(k_cache), _ptr(v_cache), _ptr(seq_offset), _ptr(capacity),
-                   int(k_cache.shape[0]), _ptr(block_table), int(block_size), max_blocks)
+                   int(k_cache.shape[0]), _ptr(block_table), int(block_size), max_blocks,
+                   QSA_KV_TURBO8 if turbo8 else QSA_KV_NATIVE, _ptr(k_scales), _ptr(v_scales))
 
 
 def workspace_size(cfg: Cfg) -> int:

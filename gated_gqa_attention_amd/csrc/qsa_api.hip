@@ -206,6 +206,13 @@ int check_kv(const qsa_kv_cache *kv) {
   if (!kv->k || !kv->v) return fail(QSA_ERR_INVALID, "kv->k and kv->v are required");
   if (kv->num_rows < 1) return fail(QSA_ERR_INVALID, "kv->num_rows must be >= 1");
   if (kv->k == kv->v) return fail(QSA_ERR_INVALID, "kv->k and kv->v must be different buffers");
+  if (kv->kv_dtype != QSA_KV_NATIVE && kv->kv_dtype != QSA_KV_TURBO8)
+    return fail(QSA_ERR_UNSUPPORTED, "kv->kv_dtype %d not supported (QSA_KV_NATIVE | QSA_KV_TURBO8)", kv->kv_dtype);
+  if (kv->kv_dtype == QSA_KV_TURBO8) {
+    if (!kv->k_scales || !kv->v_scales)
+      return fail(QSA_ERR_INVALID, "a Turbo8 cache needs kv->k_scales and kv->v_scales");
+    if (kv->block_table) return fail(QSA_ERR_UNSUPPORTED, "Turbo8 caches are taken in the contiguous layout only");
+  }
   if (!kv->block_table) {
     if (!kv->seq_offset) return fail(QSA_ERR_INVALID, "kv->seq_offset is required for a contiguous cache");
     return QSA_OK;
@@ -216,6 +223,26 @@ int check_kv(const qsa_kv_cache *kv) {
   if (kv->max_blocks < 1) return fail(QSA_ERR_INVALID, "kv->max_blocks must be >= 1");
   if (kv->num_rows % bs) return fail(QSA_ERR_INVALID, "kv->num_rows must be a multiple of block_size for a paged cache");
   return QSA_OK;
+}
+
+// Turbo8 caches: bf16 activations, and the short-query route's whole-lane
+// rotation (the quantizing append shares its key preparation).
+int check_turbo8(const qsa_cfg *c, const Plan &pl) {
+  if (c->dtype != QSA_BF16) return fail(QSA_ERR_UNSUPPORTED, "Turbo8 caches take bf16 activations only");
+  if (pl.route != kRouteFused)
+    return fail(QSA_ERR_UNSUPPORTED,
+                "Turbo8 caches are taken on the short-query route only (q_len <= 16, q_len * G <= 48, "
+                "rotary_dim / 2 a multiple of head_dim / 16); this call plans route %s", route_name(pl.route));
+  return QSA_OK;
+}
+
+qsa::Turbo8Cache turbo8_of(const qsa_kv_cache *kv) {
+  qsa::Turbo8Cache c;
+  c.kq = (uint8_t *)kv->k;
+  c.vq = (uint8_t *)kv->v;
+  c.ks = (qsa::bf16_t *)kv->k_scales;
+  c.vs = (qsa::bf16_t *)kv->v_scales;
+  return c;
 }
 
 int log2_of(int32_t x) {
@@ -280,7 +307,14 @@ int qsa_append_kv(const void *k_new, const void *v_new, const qsa_kv_cache *kv, 
   p.k_new = k_new;
   p.v_new = v_new;
   p.err = cfg->workspace ? (int32_t *)cfg->workspace : nullptr;
-  hipError_t e = qsa::launch_prologue(p, cfg->dtype, false, true, (hipStream_t)cfg->stream);
+  hipError_t e;
+  if (kv->kv_dtype == QSA_KV_TURBO8) {
+    if ((rc = check_turbo8(cfg, pl)) != QSA_OK) return rc;
+    e = qsa::launch_turbo8_append(p, turbo8_of(kv), (hipStream_t)cfg->stream);
+    if (e != hipSuccess) return fail(QSA_ERR_DEVICE, "append launch failed: %s", hipGetErrorString(e));
+    return QSA_OK;
+  }
+  e = qsa::launch_prologue(p, cfg->dtype, false, true, (hipStream_t)cfg->stream);
   if (e != hipSuccess) return fail(QSA_ERR_DEVICE, "append launch failed: %s", hipGetErrorString(e));
   return QSA_OK;
 }
@@ -305,14 +339,18 @@ int gated_attention_in(const void *q_gate, const void *k_new, const void *v_new,
   const size_t es = cfg->dtype == QSA_BF16 ? 2 : 4;
   const size_t nrow = (size_t)cfg->batch * cfg->q_len;
   const size_t out_bytes = nrow * cfg->num_q_heads * cfg->head_dim * es;
-  const size_t kv_bytes = (size_t)kv->num_rows * cfg->num_kv_heads * cfg->head_dim * es;
+  const size_t kv_bytes = (size_t)kv->num_rows * cfg->num_kv_heads * cfg->head_dim *
+                          (kv->kv_dtype == QSA_KV_TURBO8 ? 1 : es);   // Turbo8: one byte per element
+  const size_t sc_bytes = kv->kv_dtype == QSA_KV_TURBO8 ? kv_bytes / 8 : 0;   // bf16 per 16 elements
   const size_t new_bytes = nrow * cfg->num_kv_heads * cfg->head_dim * es;
   if (overlaps(out, out_bytes, q_gate, 2 * out_bytes) || overlaps(out, out_bytes, k_new, new_bytes) ||
       overlaps(out, out_bytes, v_new, new_bytes) || overlaps(out, out_bytes, kv->k, kv_bytes) ||
-      overlaps(out, out_bytes, kv->v, kv_bytes))
+      overlaps(out, out_bytes, kv->v, kv_bytes) || overlaps(out, out_bytes, kv->k_scales, sc_bytes) ||
+      overlaps(out, out_bytes, kv->v_scales, sc_bytes))
     return fail(QSA_ERR_INVALID, "out must not alias q_gate, k_new, v_new or the cache");
   Plan pl;
   if ((rc = make_plan(cfg, &pl)) != QSA_OK) return rc;
+  if (kv->kv_dtype == QSA_KV_TURBO8 && (rc = check_turbo8(cfg, pl)) != QSA_OK) return rc;
   if (kv->block_table) {
     // Paged caches on the short-query route only.  A workgroup holds the block
     // ids of its key chunk (at most 128): with fixed chunks the last one has
@@ -357,7 +395,8 @@ int gated_attention_in(const void *q_gate, const void *k_new, const void *v_new,
       if (e == hipSuccess) e = qsa::launch_rows_f32(p, s, tm);
       break;
     case kRouteFused:
-      e = qsa::launch_stream_bf16(p, s, tm);
+      e = kv->kv_dtype == QSA_KV_TURBO8 ? qsa::launch_turbo8_bf16(p, turbo8_of(kv), s, tm)
+                                          : qsa::launch_stream_bf16(p, s, tm);
       if (e == hipSuccess && pl.chunks > 1) e = qsa::launch_combine_bf16(p, s, false);
       break;
     default:

@@ -33,6 +33,15 @@ struct Geo {
 __device__ __forceinline__ f32x4 mfma_qk(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma_qk(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 16-bit MFMA operand types: bf16 (the bf16 cache's own values) or fp16 (values
+// that need more than bf16's 8 significant bits, such as decoded Turbo8 codes).
+template <typename T> struct Op16;
+template <> struct Op16<bf16_t> { using x8 = bf16x8; using x4 = bf16x4; };
+template <> struct Op16<f16_t> { using x8 = f16x8; using x4 = f16x4; };
 
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + __expf(-z)); }
 
@@ -178,25 +187,32 @@ __device__ __forceinline__ int swz(int row, int unit, int rb) {
   return row * rb + 16 * (unit ^ (row & SW));
 }
 
-// Store E floats (rounded to bf16) of one row at elements [e0, e0 + E) of a swizzled tile.
-template <int D>
-__device__ __forceinline__ void put_row_bf16(unsigned char *tile, int rb, int row, int e0, const float *x) {
+// Store E floats (rounded to the 16-bit type T, nearest even) of one row at
+// elements [e0, e0 + E) of a swizzled tile.
+template <int D, typename T = bf16_t>
+__device__ __forceinline__ void put_row(unsigned char *tile, int rb, int row, int e0, const float *x) {
   using G = Geo<D>;
+  using V8 = typename Op16<T>::x8;
+  using V4 = typename Op16<T>::x4;
   constexpr int E = G::E;
   if constexpr (E >= 8) {
 #pragma unroll
     for (int u = 0; u < E / 8; ++u) {
-      bf16x8 v;
+      V8 v;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = (bf16_t)x[8 * u + j];
-      *(bf16x8 *)(tile + swz<G::SW>(row, e0 / 8 + u, rb)) = v;
+      for (int j = 0; j < 8; ++j) v[j] = (T)x[8 * u + j];
+      *(V8 *)(tile + swz<G::SW>(row, e0 / 8 + u, rb)) = v;
     }
   } else {
-    bf16x4 v;
+    V4 v;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = (bf16_t)x[j];
-    *(bf16x4 *)(tile + swz<G::SW>(row, e0 / 8, rb) + 8 * ((e0 / 4) & 1)) = v;
+    for (int j = 0; j < 4; ++j) v[j] = (T)x[j];
+    *(V4 *)(tile + swz<G::SW>(row, e0 / 8, rb) + 8 * ((e0 / 4) & 1)) = v;
   }
+}
+template <int D>
+__device__ __forceinline__ void put_row_bf16(unsigned char *tile, int rb, int row, int e0, const float *x) {
+  put_row<D, bf16_t>(tile, rb, row, e0, x);
 }
 
 
@@ -253,6 +269,96 @@ __device__ __forceinline__ void norm_rope(float (&x)[D / 16], const float (&w)[D
   }
 }
 
+// Orthonormal Walsh-Hadamard transform of one head row held by 16 lanes
+// (lane c16 holds elements E c16 .. E c16 + E - 1): butterflies (a, b) ->
+// (a + b, a - b) over every bit of the element index, the low log2(E) bits
+// inside the lane and the four lane bits across lanes, then a scale of
+// 1/sqrt(D).  Sylvester order, its own inverse (Atlas Qwen35Kernels
+// wht_bf16_inplace / wht_bf16_inplace_inv: the rotation bookends of the Turbo
+// KV formats).  Every lane of the wavefront must take part.
+template <int D>
+__device__ __forceinline__ void row_wht(float (&x)[D / 16]) {
+  constexpr int E = D / 16;
+  const int c16 = threadIdx.x & 15;
+#pragma unroll
+  for (int h = 1; h < E; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+      if (!(j & h)) {
+        const float a = x[j], b = x[j + h];
+        x[j] = a + b;
+        x[j + h] = a - b;
+      }
+#pragma unroll
+  for (int lh = 1; lh < 16; lh <<= 1) {
+    const bool up = c16 & lh;                           // this lane holds the b of each pair
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const float o = __shfl_xor(x[j], lh, kWave);
+      x[j] = up ? o - x[j] : x[j] + o;
+    }
+  }
+  const float norm = 1.0f / sqrtf((float)D);
+#pragma unroll
+  for (int j = 0; j < E; ++j) x[j] *= norm;
+}
+
+// Two floats to E4M3 codes in the low (hi = false) or high half of a dword, and
+// two codes from a dword's low or high half to floats (gfx950's conversions:
+// round to nearest even, the OCP E4M3 format; the halves must be constants).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_fp8(float a, float b, uint32_t old, bool hi) {
+  return hi ? (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, true)
+            : (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, false);
+}
+__device__ __forceinline__ f32x2_t unpk_fp8(uint32_t w, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+}
+
+// Turbo8 groups of 16 consecutive elements (Atlas MetalKvDtype::Turbo8: FP8
+// E4M3 codes with a bf16 scale per 16 elements).  A group spans 16 / E lanes
+// of a 16-lane row (one lane for D = 256).  The scale is the group's largest
+// magnitude over 448 (the largest E4M3 value), rounded to bf16; a code is
+// x / scale rounded to nearest E4M3, ties to even, after clamping to +-448
+// (the hardware conversion turns larger values into NaN rather than
+// saturating); a zero group has a zero scale and zero codes.  All in fp32.
+template <int D>
+struct Turbo8Row {
+  static constexpr int E = D / 16;
+  static constexpr int LPG = 16 / E < 1 ? 1 : 16 / E;   // lanes per group
+  static constexpr int CW = (E + 3) / 4;                // dwords of codes per lane
+  uint32_t codes[CW];                                   // E codes, byte j of element j
+  bf16_t scale;                                         // this lane's group scale
+  __device__ __forceinline__ void quantize(const float (&x)[E]) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < E; ++j) amax = fmaxf(amax, fabsf(x[j]));
+#pragma unroll
+    for (int lh = 1; lh < LPG; lh <<= 1) amax = fmaxf(amax, __shfl_xor(amax, lh, kWave));
+    scale = (bf16_t)(amax / 448.0f);
+    const float s = (float)scale;
+#pragma unroll
+    for (int w = 0; w < CW; ++w) codes[w] = 0;
+    if (s == 0.f) return;
+#pragma unroll
+    for (int j = 0; j < E; j += 2) {
+      const float a = fminf(fmaxf(x[j] / s, -448.f), 448.f);
+      const float b = fminf(fmaxf(x[j + 1] / s, -448.f), 448.f);
+      codes[j / 4] = pk_fp8(a, b, codes[j / 4], (j % 4) != 0);
+    }
+  }
+  // codes x scale in fp32 (exact: 4 x 8 significant bits)
+  __device__ __forceinline__ void dequantize(float (&x)[E]) const {
+    const float s = (float)scale;
+#pragma unroll
+    for (int j = 0; j < E; j += 2) {
+      const f32x2_t f = unpk_fp8(codes[j / 4], (j % 4) != 0);
+      x[j] = f[0] * s;
+      x[j + 1] = f[1] * s;
+    }
+  }
+};
+
 // Exchange area of one stage: the probability tile P[row tile][row][key] in
 // bf16 (row stride padded to 144 bytes, conflict-free for the 16-byte reads
 // of the value product) and each wavefront's block maxima and sums per row.
@@ -281,12 +387,14 @@ struct NoOp {
   __device__ void operator()() const {}
 };
 
-template <int D, int RTM, typename KFree = NoOp>
+template <int D, int RTM, typename KFree = NoOp, typename T = bf16_t>
 __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsigned char *vt, int nkeys, int key0,
-                                             const bf16x8 (&qf)[RTM][D / 32], f32x4 (&O)[RTM][D / 64],
+                                             const typename Op16<T>::x8 (&qf)[RTM][D / 32], f32x4 (&O)[RTM][D / 64],
                                              float (&m)[RTM], float (&lsum)[RTM], const int (&lim)[RTM],
                                              float scale_log2, unsigned char *xch, KFree on_k_free = KFree()) {
   using G = Geo<D>;
+  using V8 = typename Op16<T>::x8;
+  using V4 = typename Op16<T>::x4;
   constexpr int KST = D / 32, DBW = D / 64, RB = G::RB;
   const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -302,7 +410,7 @@ __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsi
     const unsigned char *kb = kt + 16 * wave * RB;
 #pragma unroll
     for (int ks = 0; ks < KST; ++ks) {
-      const bf16x8 a = *(const bf16x8 *)(kb + swz<G::SW>(m16, 4 * ks + g4, RB));
+      const V8 a = *(const V8 *)(kb + swz<G::SW>(m16, 4 * ks + g4, RB));
 #pragma unroll
       for (int rt = 0; rt < RTM; ++rt) S[rt] = mfma_qk(a, qf[rt][ks], S[rt]);
     }
@@ -352,13 +460,13 @@ __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsi
         m[rt] = mn;
       }
       float ps = 0.f;
-      bf16x4 pv;
+      V4 pv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pv[i] = (bf16_t)__builtin_amdgcn_exp2f(sc[rt][i] - mu);
+        pv[i] = (T)__builtin_amdgcn_exp2f(sc[rt][i] - mu);
         ps += (float)pv[i];
       }
-      *(bf16x4 *)(xch + (16 * rt + m16) * Xch::PSTRIDE + 2 * (16 * wave + 4 * g4)) = pv;
+      *(V4 *)(xch + (16 * rt + m16) * Xch::PSTRIDE + 2 * (16 * wave + 4 * g4)) = pv;
       ps = rows4_sum(ps);
       if (g4 == 0) wsum[wave * 64 + row] = ps;
     }
@@ -399,10 +507,10 @@ __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsi
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     if (32 * ks >= nkeys) break;
-    bf16x8 bp[RTM];
+    V8 bp[RTM];
 #pragma unroll
     for (int rt = 0; rt < RTM; ++rt)
-      bp[rt] = *(const bf16x8 *)(xch + (16 * rt + m16) * Xch::PSTRIDE + 2 * (32 * ks + 8 * g4));
+      bp[rt] = *(const V8 *)(xch + (16 * rt + m16) * Xch::PSTRIDE + 2 * (32 * ks + 8 * g4));
     const int vk = 32 * ks + 8 * g4 + (m16 >> 2), q4 = m16 & 3;
 #pragma unroll
     for (int db = 0; db < DBW; ++db) {
@@ -413,7 +521,7 @@ __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsi
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
       typedef short s16x8 __attribute__((ext_vector_type(8)));
       const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      const bf16x8 a = __builtin_bit_cast(bf16x8, v8);
+      const V8 a = __builtin_bit_cast(V8, v8);
 #pragma unroll
       for (int rt = 0; rt < RTM; ++rt) O[rt][db] = mfma_qk(a, bp[rt], O[rt][db]);
     }

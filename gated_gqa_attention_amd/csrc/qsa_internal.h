@@ -14,6 +14,9 @@ typedef __bf16 bf16_t;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16_t;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;         // four wavefronts per workgroup
 constexpr int kWave = 64;
@@ -192,6 +195,13 @@ hipError_t launch_rows_f32(const Params &p, hipStream_t s, const Timing &tm);
 hipError_t launch_tile_bf16(const Params &p, hipStream_t s, const Timing &tm);
 hipError_t launch_stream_bf16(const Params &p, hipStream_t s, const Timing &tm);
 hipError_t launch_combine_bf16(const Params &p, hipStream_t s, bool per_row);   // per_row: the tile route's merge
+// A Turbo8 cache: codes [rows][Hkv][D] bytes and bf16 scales [rows][Hkv][D/16], for K and V.
+struct Turbo8Cache {
+  uint8_t *kq, *vq;
+  bf16_t *ks, *vs;
+};
+hipError_t launch_turbo8_bf16(const Params &p, const Turbo8Cache &c, hipStream_t s, const Timing &tm);
+hipError_t launch_turbo8_append(const Params &p, const Turbo8Cache &c, hipStream_t s);
 hipError_t launch_linear_bf16(const void *x, const void *w, int M, int N, int K, void *y0, int n0_end, int ld0,
                               void *y1, int n1_end, int ld1, void *y2, int ld2, hipStream_t s);
 constexpr int kMaxLinearRows = 64;    // rows (tokens) a projection call takes

@@ -31,7 +31,10 @@ class Session:
         self.out = torch.empty((w.batch, w.q_len, w.num_q_heads, w.head_dim), dtype=self.dtype,
                                device=device)
         self.cfg = self._cfg(self.workspace)
-        if block_size:
+        if "k_codes" in d:                                 # Turbo8 cache
+            self.kv = binding.make_kv(d["k_codes"], d["v_codes"], d["seq_offset"], d["capacity"],
+                                      k_scales=d["k_scales"], v_scales=d["v_scales"])
+        elif block_size:
             self.kv = binding.make_kv(d["k_cache"], d["v_cache"], None, d["capacity"], d["block_table"], block_size)
         else:
             self.kv = binding.make_kv(d["k_cache"], d["v_cache"], d["seq_offset"], d["capacity"])

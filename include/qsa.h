@@ -79,6 +79,22 @@ typedef enum {
   QSA_F32 = 1                /* fp32 everywhere */
 } qsa_dtype;
 
+/* Storage of the KV cache. */
+typedef enum {
+  QSA_KV_NATIVE = 0,         /* rows in cfg->dtype */
+  QSA_KV_TURBO8 = 1          /* Turbo8 (Atlas qwen3_5/mod.rs, MetalKvDtype::Turbo8: FP8 E4M3 data and a
+                                bf16 scale per 16 elements, in the Walsh-Hadamard rotated basis): k / v
+                                hold one E4M3 code per element ([rows][Hkv][D] bytes) and k_scales /
+                                v_scales one bf16 scale per 16 consecutive elements of a row
+                                ([rows][Hkv][D/16]).  A group's scale is its largest magnitude over
+                                448 rounded to bf16, a code is value / scale rounded to nearest E4M3
+                                (ties to even, saturating at +-448), and rows are stored after the
+                                orthonormal Walsh-Hadamard transform over head_dim (keys after their
+                                norm and rotation), which the attention applies to the queries and
+                                undoes on its output.  bf16 activations only; contiguous caches on
+                                the short-query route. */
+} qsa_kv_dtype;
+
 /* One call's shape, numerics and execution context. */
 typedef struct {
   int32_t batch;             /* B >= 1 sequences */
@@ -127,6 +143,9 @@ typedef struct {
   const int32_t *block_table; /* device [B][max_blocks] physical block ids, or NULL (contiguous) */
   int32_t block_size;        /* paged: rows per block, a power of two in [64, 65536] */
   int32_t max_blocks;        /* paged: entries per sequence in block_table (row stride) */
+  int32_t kv_dtype;          /* qsa_kv_dtype; 0 = rows in cfg->dtype */
+  void *k_scales;            /* QSA_KV_TURBO8: device [rows][Hkv][D/16] bf16 group scales of k */
+  void *v_scales;            /* QSA_KV_TURBO8: the same for v */
 } qsa_kv_cache;
 
 /* Bytes of workspace a call with this cfg needs (split-K partials, the
