@@ -395,9 +395,13 @@ int gated_attention_in(const void *q_gate, const void *k_new, const void *v_new,
       if (e == hipSuccess) e = qsa::launch_rows_f32(p, s, tm);
       break;
     case kRouteFused:
-      e = kv->kv_dtype == QSA_KV_TURBO8 ? qsa::launch_turbo8_bf16(p, turbo8_of(kv), s, tm)
-                                          : qsa::launch_stream_bf16(p, s, tm);
-      if (e == hipSuccess && pl.chunks > 1) e = qsa::launch_combine_bf16(p, s, false);
+      if (kv->kv_dtype == QSA_KV_TURBO8) {
+        e = qsa::launch_turbo8_bf16(p, turbo8_of(kv), s, tm);
+        if (e == hipSuccess && pl.chunks > 1) e = qsa::launch_combine_wht_bf16(p, s);
+      } else {
+        e = qsa::launch_stream_bf16(p, s, tm);
+        if (e == hipSuccess && pl.chunks > 1) e = qsa::launch_combine_bf16(p, s, false);
+      }
       break;
     default:
       e = qsa::launch_prologue(p, QSA_BF16, true, has_new, s);

@@ -101,10 +101,43 @@ __device__ __forceinline__ void dma16_vaddr(const void *src, unsigned lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
 
+// The same copy of one dword per lane: lane i writes LDS bytes lds + 4 i.
+__device__ __forceinline__ void dma4_sbase(const void *base, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+
+// f(std::integral_constant<int, j>) for j = 0 .. N-1, in order (a loop whose
+// index is a compile-time constant in the body).
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>());
+  }
+}
+
+// Waits until at most u * PER vector-memory operations of this wave are
+// outstanding (u wave-uniform, 0 <= u <= MAXU).
+template <int PER, int MAXU>
+struct WaitUnits {
+  static_assert(PER * MAXU <= 63, "vmcnt field");
+  __device__ static __forceinline__ void run(int u) {
+    if (u == MAXU) {
+      wait_vm<MAXU * PER>();
+      return;
+    }
+    WaitUnits<PER, MAXU - 1>::run(u);
+  }
+};
+template <int PER>
+struct WaitUnits<PER, 0> {
+  __device__ static __forceinline__ void run(int) { wait_vm<0>(); }
+};
 
 // Wait until at most `younger` stages (2 * LPS copies each) are outstanding.
 template <int LPS2, int NS>
@@ -359,6 +392,34 @@ struct Turbo8Row {
   }
 };
 
+// Turbo8 codes to fp16 MFMA operands, code x scale rounded once to nearest
+// even (exact in fp32: 4 x 8 significant bits).  gfx950's scaled conversion
+// takes only the exponent of its fp32 scale, so it gives code x 2^e exactly
+// (the scale being 1.m x 2^e); one packed fp16 multiply by 1.m (exact in fp16)
+// then rounds the product.  Values that fall below fp16's normal range (2^-14)
+// keep fewer bits, and values past 65504 overflow.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+struct T8Scale {
+  float e;                                              // the scale itself: its exponent is used
+  f16x2_t m;                                            // (1.m, 1.m)
+  __device__ __forceinline__ explicit T8Scale(uint32_t bf16_bits) {
+    const uint32_t bits = bf16_bits << 16;
+    e = __uint_as_float(bits);
+    const _Float16 h = (_Float16)__uint_as_float((bits & 0x007F0000u) | 0x3F800000u);
+    m = f16x2_t{h, h};
+  }
+};
+// codes 0-3 of w (byte j = code j) decoded into fp16
+__device__ __forceinline__ f16x4 t8_decode4(uint32_t w, const T8Scale &s) {
+  const f16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, s.e, false) * s.m;
+  const f16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, s.e, true) * s.m;
+  return f16x4{lo[0], lo[1], hi[0], hi[1]};
+}
+__device__ __forceinline__ f16x8 t8_decode8(uint32_t w0, uint32_t w1, const T8Scale &s) {
+  const f16x4 a = t8_decode4(w0, s), b = t8_decode4(w1, s);
+  return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
 // Exchange area of one stage: the probability tile P[row tile][row][key] in
 // bf16 (row stride padded to 144 bytes, conflict-free for the 16-byte reads
 // of the value product) and each wavefront's block maxima and sums per row.
@@ -387,11 +448,23 @@ struct NoOp {
   __device__ void operator()() const {}
 };
 
-template <int D, int RTM, typename KFree = NoOp, typename T = bf16_t>
+// The score product's K operand of k-step ks for this lane (key m16 of the
+// wavefront's block kb, dims 8 (4 ks + g4) .. + 7) from a swizzled tile of
+// 16-bit values.
+template <int D, typename T>
+struct TileK {
+  __device__ __forceinline__ typename Op16<T>::x8 operator()(const unsigned char *kb, int ks) const {
+    const int lane = threadIdx.x % kWave;
+    return *(const typename Op16<T>::x8 *)(kb + swz<Geo<D>::SW>(lane & 15, 4 * ks + (lane >> 4), Geo<D>::RB));
+  }
+};
+
+template <int D, int RTM, typename KFree = NoOp, typename T = bf16_t, typename KOp = TileK<D, T>>
 __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsigned char *vt, int nkeys, int key0,
                                              const typename Op16<T>::x8 (&qf)[RTM][D / 32], f32x4 (&O)[RTM][D / 64],
                                              float (&m)[RTM], float (&lsum)[RTM], const int (&lim)[RTM],
-                                             float scale_log2, unsigned char *xch, KFree on_k_free = KFree()) {
+                                             float scale_log2, unsigned char *xch, KFree on_k_free = KFree(),
+                                             const KOp &kop = KOp()) {
   using G = Geo<D>;
   using V8 = typename Op16<T>::x8;
   using V4 = typename Op16<T>::x4;
@@ -410,7 +483,7 @@ __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsi
     const unsigned char *kb = kt + 16 * wave * RB;
 #pragma unroll
     for (int ks = 0; ks < KST; ++ks) {
-      const V8 a = *(const V8 *)(kb + swz<G::SW>(m16, 4 * ks + g4, RB));
+      const V8 a = kop(kb, ks);
 #pragma unroll
       for (int rt = 0; rt < RTM; ++rt) S[rt] = mfma_qk(a, qf[rt][ks], S[rt]);
     }

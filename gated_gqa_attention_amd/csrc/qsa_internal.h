@@ -195,6 +195,7 @@ hipError_t launch_rows_f32(const Params &p, hipStream_t s, const Timing &tm);
 hipError_t launch_tile_bf16(const Params &p, hipStream_t s, const Timing &tm);
 hipError_t launch_stream_bf16(const Params &p, hipStream_t s, const Timing &tm);
 hipError_t launch_combine_bf16(const Params &p, hipStream_t s, bool per_row);   // per_row: the tile route's merge
+hipError_t launch_combine_wht_bf16(const Params &p, hipStream_t s);              // partials in the WHT basis
 // A Turbo8 cache: codes [rows][Hkv][D] bytes and bf16 scales [rows][Hkv][D/16], for K and V.
 struct Turbo8Cache {
   uint8_t *kq, *vq;

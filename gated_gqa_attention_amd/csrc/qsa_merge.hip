@@ -27,20 +27,29 @@ namespace qsa {
 // the length itself form one round trip.  A sequence out of range has NaN
 // statistics in chunk 0 (written by the attention kernel), so its merged rows
 // are NaN.  lg packs L (bits 0-15) and G (bits 16-31).
-template <int D>
-__global__ __launch_bounds__(kWave) void combine_kernel(const int32_t *__restrict__ seq_lens,
-                                                    const float *__restrict__ part_ml,
-                                                    const float *__restrict__ part_o,
-                                                    const bf16_t *__restrict__ q_gate, int rows, int chunks,
-                                                    int hkv, int lg, Params p) {
+//
+// ROT: the partials are in the Walsh-Hadamard basis (the Turbo8 cache's), so
+// the merged row is rotated back (the iWHT(out) bookend) before the gate; the
+// merge is linear, so rotating the merged row is rotating every chunk's.  Then
+// one workgroup takes the D/64 slices of a row, one wavefront each, and the
+// merged row goes through LDS to wavefront 0, which holds it whole (D/64
+// dims per lane) for the rotation.
+template <int D, bool ROT>
+__global__ __launch_bounds__(ROT ? D : kWave) void combine_kernel(const int32_t *__restrict__ seq_lens,
+                                                                  const float *__restrict__ part_ml,
+                                                                  const float *__restrict__ part_o,
+                                                                  const bf16_t *__restrict__ q_gate, int rows,
+                                                                  int chunks, int hkv, int lg, Params p) {
   constexpr int NSL = D / kWave;                        // 64-dim slices per row
   constexpr int CPL = kWave / 4;                        // chunks per lane and batch
   // lane (q, c16) holds dims 4 c16 .. 4 c16 + 3 of the slice for chunks q, q + 4, ...
-  const int lane = threadIdx.x, q = lane >> 4, c16 = lane & 15;
-  const int d = kWave * (blockIdx.x % NSL) + 4 * c16;
+  const int lane = ROT ? threadIdx.x % kWave : threadIdx.x, q = lane >> 4, c16 = lane & 15;
+  const int slice = ROT ? __builtin_amdgcn_readfirstlane(threadIdx.x / kWave) : blockIdx.x % NSL;
+  const int rowid = ROT ? blockIdx.x : blockIdx.x / NSL;
+  const int d = kWave * slice + 4 * c16;
   const int L = lg & 0xffff, G = lg >> 16, Hq = G * hkv;
-  const int rr = (blockIdx.x / NSL) % rows;
-  const int slot = blockIdx.x / NSL / rows;
+  const int rr = rowid % rows;
+  const int slot = rowid / rows;
   const int kvh = slot % hkv, b = slot / hkv;
   const int l = rr / G, h = kvh * G + rr % G;
   if (rr >= L * G) return;
@@ -101,6 +110,40 @@ __global__ __launch_bounds__(kWave) void combine_kernel(const int32_t *__restric
   acc.y = rows4_sum(acc.y);
   acc.z = rows4_sum(acc.z);
   acc.w = rows4_sum(acc.w);
+  if constexpr (ROT) {
+    __shared__ __attribute__((aligned(16))) float mrow[D];
+    if (q == 0) *(float4 *)(mrow + d) = acc;
+    __syncthreads();
+    if (slice == 0) {
+      constexpr int EPL = D / kWave;                    // dims EPL lane .. + EPL - 1
+      float x[EPL];
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) x[j] = mrow[EPL * lane + j];
+#pragma unroll
+      for (int hb = 1; hb < EPL; hb <<= 1)
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+          if (!(j & hb)) {
+            const float a = x[j], c = x[j + hb];
+            x[j] = a + c;
+            x[j + hb] = a - c;
+          }
+#pragma unroll
+      for (int lh = 1; lh < kWave; lh <<= 1) {
+        const bool up = lane & lh;                      // this lane holds the second of each pair
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+          const float o = __shfl_xor(x[j], lh, kWave);
+          x[j] = up ? o - x[j] : x[j] + o;
+        }
+      }
+      const float norm = 1.0f / sqrtf((float)D);
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) mrow[EPL * lane + j] = x[j] * norm;
+    }
+    __syncthreads();
+    acc = *(const float4 *)(mrow + d);
+  }
   if (q == 0) {
     float z[4];
     zr.to_float(z);
@@ -221,16 +264,38 @@ hipError_t launch_combine_bf16(const Params &p, hipStream_t s, bool per_row) {
   const bf16_t *qg = (const bf16_t *)p.q_gate;
   switch (p.D) {
     case 64:
-      hipLaunchKernelGGL((combine_kernel<64>), dim3(blocks), dim3(kWave), 0, s, p.seq_lens, p.part_ml, p.part_o, qg,
+      hipLaunchKernelGGL((combine_kernel<64, false>), dim3(blocks), dim3(kWave), 0, s, p.seq_lens, p.part_ml, p.part_o,
+                         qg, p.rows, p.chunks, p.Hkv, lg, p);
+      break;
+    case 128:
+      hipLaunchKernelGGL((combine_kernel<128, false>), dim3(blocks), dim3(kWave), 0, s, p.seq_lens, p.part_ml,
+                         p.part_o, qg, p.rows, p.chunks, p.Hkv, lg, p);
+      break;
+    case 256:
+      hipLaunchKernelGGL((combine_kernel<256, false>), dim3(blocks), dim3(kWave), 0, s, p.seq_lens, p.part_ml,
+                         p.part_o, qg, p.rows, p.chunks, p.Hkv, lg, p);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_wht_bf16(const Params &p, hipStream_t s) {
+  const int64_t blocks = (int64_t)p.B * p.Hkv * p.rows;
+  const int lg = p.L | (p.G << 16);
+  const bf16_t *qg = (const bf16_t *)p.q_gate;
+  switch (p.D) {
+    case 64:
+      hipLaunchKernelGGL((combine_kernel<64, true>), dim3(blocks), dim3(64), 0, s, p.seq_lens, p.part_ml, p.part_o, qg,
                          p.rows, p.chunks, p.Hkv, lg, p);
       break;
     case 128:
-      hipLaunchKernelGGL((combine_kernel<128>), dim3(blocks), dim3(kWave), 0, s, p.seq_lens, p.part_ml, p.part_o, qg,
-                         p.rows, p.chunks, p.Hkv, lg, p);
+      hipLaunchKernelGGL((combine_kernel<128, true>), dim3(blocks), dim3(128), 0, s, p.seq_lens, p.part_ml, p.part_o,
+                         qg, p.rows, p.chunks, p.Hkv, lg, p);
       break;
     case 256:
-      hipLaunchKernelGGL((combine_kernel<256>), dim3(blocks), dim3(kWave), 0, s, p.seq_lens, p.part_ml, p.part_o, qg,
-                         p.rows, p.chunks, p.Hkv, lg, p);
+      hipLaunchKernelGGL((combine_kernel<256, true>), dim3(blocks), dim3(256), 0, s, p.seq_lens, p.part_ml, p.part_o,
+                         qg, p.rows, p.chunks, p.Hkv, lg, p);
       break;
     default: return hipErrorInvalidValue;
   }

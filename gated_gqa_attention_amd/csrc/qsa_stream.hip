@@ -47,27 +47,6 @@
 
 namespace qsa {
 
-namespace {
-
-// Waits until at most u * LPS vector-memory operations of this wave are
-// outstanding (u wave-uniform, 0 <= u <= U).
-template <int LPS, int U>
-struct WaitUnits {
-  __device__ static __forceinline__ void run(int u) {
-    if (u == U) {
-      wait_vm<U * LPS>();
-      return;
-    }
-    WaitUnits<LPS, U - 1>::run(u);
-  }
-};
-template <int LPS>
-struct WaitUnits<LPS, 0> {
-  __device__ static __forceinline__ void run(int) { wait_vm<0>(); }
-};
-
-}  // namespace
-
 // RTM: row tiles (16 rows each) of the workgroup, ceil(L * G / 16) <= 3.
 //
 // Two roles until the first stage.  Wavefronts 0-1 (the copy waves) load only

@@ -16,35 +16,25 @@
 // turbo8_kernel: one workgroup per (sequence, KV head, key chunk), the short-
 // query route's geometry (rows = the G query heads x L new rows, up to 48).
 // The query rows are normalised, rotated, taken to the WHT basis (the WHT(Q)
-// bookend: (H q).(H k) = q.k) and rounded to fp16 MFMA operands.  Each 64-key
-// stage's codes and scales are loaded into registers (the next stage's while
-// the current one is attended), decoded to codes x scales (12 significant bits,
-// which fp16's 11 keep better than bf16's 8), rounded to fp16 and written into
-// the same swizzled LDS tiles as the bf16 kernel's copies, so the stage step is
-// the bf16 kernel's (attend_stage), on fp16 MFMAs.  The workgroup holding the
-// sequence's end quantizes the new rows as the append does (when k_new is
-// given: and stores them), decodes them and attends them as a last stage.  At
-// the end the accumulated rows, still in the rotated basis, go through LDS and
-// are rotated back (the iWHT(out) bookend) before the gate (a whole sequence
-// in one chunk) or before they are stored as the chunk's partials for the
-// merge kernel (the merge is linear, so rotating each chunk is rotating the
-// sum).
+// bookend: (H q).(H k) = q.k) and rounded to fp16 MFMA operands.  The chunk's
+// keys stream through a ring of raw 64-key stages (codes and scales as
+// stored, 36 KB per stage at head_dim 256, three in flight), copied straight
+// from HBM into LDS.  Codes are decoded to code x scale (12 significant bits,
+// which fp16's 11 keep better than bf16's 8): the V codes of a stage into one
+// fp16 tile laid out like the bf16 kernel's V stages, the K codes per MFMA
+// operand straight from the ring, so the stage step is the bf16 kernel's
+// (attend_stage) on fp16 MFMAs.  The workgroup holding the sequence's end
+// quantizes the new rows as the append does (when k_new is given: and stores
+// them), decodes them and attends them first.  At the end a chunk that is
+// the whole sequence rotates its rows back (the iWHT(out) bookend) and applies
+// the gate; other chunks store their partials in the rotated basis and the
+// merge kernel rotates each merged row once (the merge is linear, so rotating
+// the merged row is rotating every chunk's).
 #include "qsa_device.h"
 
 namespace qsa {
 
 namespace {
-
-// (cos, sin) of the rotary angles of the L new rows of sequence b, entry
-// l * half + i, in LDS (half = rotary_dim / 2 pairs).
-__device__ __forceinline__ void rope_table(float2 *tab, const int32_t *positions, int b, int L, int half,
-                                           double step) {
-  for (int e = threadIdx.x; e < L * half; e += kThreads) {
-    float c, s;
-    rope_angle_cs(positions[(int64_t)b * L + e / half], rope_freq(step, e % half), c, s);
-    tab[e] = make_float2(c, s);
-  }
-}
 
 // One new row's K (norm, rotation, WHT, quantizer) or V (WHT, quantizer), for
 // the 16 lanes that hold it; x holds the raw row and is left as the value the
@@ -115,40 +105,154 @@ __global__ __launch_bounds__(kThreads) void turbo8_append_kernel(Params p, const
 }
 
 // ------------------------------------------------------------------ attention
+// Stage layout of the raw ring (one slot per 64-key stage): K codes [64][D]
+// with each row's 16-byte units XOR-swizzled by the key (conflict-free reads
+// of one column by 16 keys), K scales [64][D/16] bf16, V codes [64][D], V
+// scales [64][D/16], all copied straight from HBM by global_load_lds.
+template <int D>
+struct T8Geo {
+  static constexpr int SK = Geo<D>::SK;
+  static constexpr int UPR = D / 16;                    // 16-byte code units (= scale groups) per key row
+  static constexpr int SWC = (UPR < 16 ? UPR : 16) - 1;
+  static constexpr int CODES = SK * D, SCL = SK * D / 8;
+  static constexpr int KC = 0, KS = CODES, VC = CODES + SCL, VS = 2 * CODES + SCL;
+  static constexpr int SLOT = 2 * (CODES + SCL);
+  static constexpr int NC = 2 * UPR;                    // 16-byte code copy instructions per stage (K, V), 64 lanes each
+  // scale copies: 16-byte units when a key's scales fill whole units and the
+  // counts stay even (head_dim 256: two units per key), dwords otherwise
+  static constexpr bool SX4 = D == 256;
+  static constexpr int SPK = SX4 ? D / 128 : D / 32;    // scale copy units per key
+  static constexpr int NSC = SK * SPK / kWave;          // scale copy instructions per stage and tensor
+  static constexpr int NQ = NC + 2 * NSC;               // copy instructions per stage
+  static constexpr int U = NQ / 4;                      // per wavefront when all four issue
+  static constexpr int NS = D == 256 ? 3 : D == 128 ? 6 : 8;   // stages in flight: LDS and the vmcnt field
+  static constexpr int VT = SK * Geo<D>::RB;            // decoded fp16 V tile
+  static_assert(NQ % 4 == 0 && 2 * (NS - 1) * U <= 63, "copy counts");
+  static_assert(UPR % 2 == 0 && NSC % 2 == 0, "a copy wave's instructions q = w + 2 j have the kind of 2 j");
+  // instruction q copies: kind 0 K codes, 1 V codes, 2 K scales, 3 V scales
+  static constexpr int kind(int q) { return q < UPR ? 0 : q < 2 * UPR ? 1 : q < 2 * UPR + NSC ? 2 : 3; }
+  static constexpr int first(int k) { return k == 0 ? 0 : k == 1 ? UPR : k == 2 ? 2 * UPR : 2 * UPR + NSC; }
+  static constexpr int region(int k) { return k == 0 ? KC : k == 1 ? VC : k == 2 ? KS : VS; }
+  static constexpr int ibytes(int k) { return k < 2 || SX4 ? 16 * kWave : 4 * kWave; }   // LDS bytes per instruction
+  // This lane's source offset for instruction q, in bytes from the stage's
+  // first key row (head kvh) of the tensor it copies; keys past `last` repeat it.
+  // rowc / rows_: bytes between consecutive keys of one head (codes / scales).
+  __device__ static __forceinline__ unsigned lane_off(int q, int lane, int last, unsigned rowc, unsigned rows_) {
+    const int k = kind(q), i = q - first(k), s = kWave * i + lane;
+    if (k < 2) {
+      const int key = s / UPR, pos = s % UPR, gu = k == 0 ? pos ^ (key & SWC) : pos;
+      return (unsigned)min(key, last) * rowc + 16u * (unsigned)gu;
+    }
+    const int key = s / SPK, unit = s % SPK;
+    return (unsigned)min(key, last) * rows_ + (SX4 ? 16u : 4u) * (unsigned)unit;
+  }
+};
+
+// The score product's K operand straight from a raw stage: this lane's key
+// row (16 wave + m16) and k-step ks hold 8 codes of scale group 2 ks + g4/2.
+template <int D>
+struct T8K {
+  static constexpr int KST = D / 32;
+  uint2 cw[KST];                                        // the codes of k-step ks
+  uint32_t sb[KST];                                     // their scale (bf16 bits)
+  __device__ __forceinline__ explicit T8K(const unsigned char *slot) {
+    using T8 = T8Geo<D>;
+    const int lane = threadIdx.x % kWave, g4 = lane >> 4, key = 16 * (threadIdx.x / kWave) + (lane & 15);
+    const unsigned char *const row = slot + T8::KC + key * D;
+    const int sw = key & T8::SWC;
+    const uint16_t *const sr = (const uint16_t *)(slot + T8::KS) + key * T8::UPR + (g4 >> 1);
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks) {
+      const int u = 2 * ks + (g4 >> 1);
+      cw[ks] = *(const uint2 *)(row + 16 * (u ^ sw) + 8 * (g4 & 1));
+      sb[ks] = sr[2 * ks];
+    }
+  }
+  __device__ __forceinline__ f16x8 operator()(const unsigned char *, int ks) const {
+    return t8_decode8(cw[ks].x, cw[ks].y, T8Scale(sb[ks]));
+  }
+};
+
+// One workgroup per (sequence, KV head, key chunk), the short-query route's
+// geometry (rows r = l G + h - kvh G, at most 48).  Wavefronts 0-1 issue the
+// first NS stages' copies; wavefronts 2-3 meanwhile build their (cos, sin)
+// tables, normalise, rotate and WHT the query rows into fp16 operands and, in
+// the workgroup that ends the sequence, prepare the new rows: with k_new given
+// they are quantized as the append does and stored, otherwise read from the
+// cache; either way decoded from the same codes.  Those are attended first,
+// from fp16 tiles, while the cached stages land.  Each cached stage then
+// decodes its V codes into the fp16 V tile and takes its K codes into
+// registers, scores its keys from those codes (decoded per MFMA operand),
+// refills its slot, and accumulates.
+// At the end a chunk that is the whole sequence rotates its rows back
+// through LDS and gates them; other chunks store their partials as they are,
+// in the WHT basis, and the merge rotates the merged rows.
 template <int D, int RTM>
 __global__ __launch_bounds__(kThreads) void turbo8_kernel(Params p, const uint8_t *__restrict__ kq,
                                                           const bf16_t *__restrict__ ks,
                                                           const uint8_t *__restrict__ vq,
-                                                          const bf16_t *__restrict__ vs, uint8_t *__restrict__ kq_w,
-                                                          bf16_t *__restrict__ ks_w, uint8_t *__restrict__ vq_w,
-                                                          bf16_t *__restrict__ vs_w) {
+                                                          const bf16_t *__restrict__ vs, uint8_t *kq_w, bf16_t *ks_w,
+                                                          uint8_t *vq_w, bf16_t *vs_w) {
   using G = Geo<D>;
-  constexpr int E = G::E, KST = G::KST, RB = G::RB, DBW = D / 64, SK = G::SK;
-  constexpr int NG = D / 16;                            // groups per row
-  constexpr int GPT = SK * NG / kThreads;               // groups per thread and stage (per tensor)
+  using T8 = T8Geo<D>;
+  constexpr int E = G::E, KST = G::KST, RB = G::RB, DBW = D / 64, SK = G::SK, NS = T8::NS, U = T8::U;
+  constexpr int UPR = T8::UPR, NG = D / 16, SLOT = T8::SLOT;
   constexpr int QBYTES = 16 * RTM * RB;
   constexpr int TABN = kMaxFusedTable;
-  constexpr int PREP = QBYTES + TABN * 8;
-  constexpr int ARENA = PREP > Xch::BYTES ? PREP : Xch::BYTES;
-  constexpr int SLOT = SK * RB;                         // one stage of one tensor
-  static_assert(2 * 2 * SLOT >= 16 * RTM * D * 4 + 16 * RTM * 4, "the epilogue tile fits in the ring");
-  __shared__ __attribute__((aligned(16))) unsigned char ring[4 * SLOT];   // K slot 0 | K slot 1 | V slot 0 | V slot 1
+  constexpr int PREP = QBYTES + 2 * TABN * 8;           // query rows, then one (cos, sin) table per prep wave
+  constexpr int WORK = T8::VT + Xch::BYTES;             // V tile, then the stage exchange
+  constexpr int ARENA = PREP > WORK ? PREP : WORK;
+  constexpr int NPASS = 2 * RTM;
+  constexpr int TJ = TABN / kWave;
+  static_assert(16 * RTM * D * 4 + 16 * RTM * 4 <= NS * SLOT, "the epilogue tile fits in the ring");
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NS * SLOT];
   __shared__ __attribute__((aligned(16))) unsigned char arena[ARENA];
+  unsigned char *const vtile = arena, *const xch = arena + T8::VT;
 
   const int t = threadIdx.x, lane = t % kWave, g4 = lane >> 4, m16 = lane & 15, c16 = m16;
   const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
-  const int nslot = p.B * p.Hkv;
-  const int chunk = blockIdx.x / nslot, slot = blockIdx.x % nslot;
-  const int hkv = p.Hkv, b = slot / hkv, kvh = slot % hkv;
+  const bool copier = wave < 2;
+  const int pw = wave - 2;
+  // The KV heads of one (chunk, sequence) group run on one XCD (the workgroup
+  // of block i runs on XCD i % 8), so the scale lines they share (D/8 bytes
+  // per head of each key row) are fetched into one L2; groups go round the XCDs.
+  const int hkv = p.Hkv;
+  const int xj = blockIdx.x / 8, kvh = xj % hkv, grp = 8 * (xj / hkv) + blockIdx.x % 8;
+  if (grp >= p.chunks * p.B) return;                    // the grid is rounded up to 8 groups
+  const int chunk = grp / p.B, b = grp % p.B, slot = b * hkv + kvh;
   const int L = p.L, Gq = p.G, Hq = p.Hq, R = L * Gq, half = p.r / 2;
+  const bf16_t *const q_gate = (const bf16_t *)p.q_gate;
+  bf16_t *const outp = (bf16_t *)p.out;
   const int n = p.seq_lens[b];
   const int64_t off = p.seq_offset[b];
+  const int cap = p.capacity ? p.capacity[b] : 0x7fffffff;
+
+  // prep waves: query rows 8 k + 4 pw + g4 of pass k, the norm weights and the
+  // positions of their table entries (in-range indices whatever n is)
+  RawE<E> qraw[NPASS], wqraw, wkraw;
+  int tpos[TJ], tpair[TJ];
+  if (!copier) {
+#pragma unroll
+    for (int k = 0; k < NPASS; ++k) {
+      const int r = min(8 * k + 4 * pw + g4, R - 1);
+      const int l = r / Gq, h = kvh * Gq + r % Gq;
+      qraw[k].load(q_gate + (((int64_t)b * L + l) * Hq + h) * 2 * D + E * c16);
+    }
+    wqraw.load((const bf16_t *)p.wq + E * c16);
+    wkraw.load((const bf16_t *)p.wk + E * c16);
+    const int hh = max(half, 1);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int e = lane + kWave * j, q = e / hh;
+      tpos[j] = p.positions[(int64_t)b * L + min(q, L - 1)];
+      tpair[j] = e - q * hh;
+    }
+  }
+
   const int64_t total = (int64_t)n + L;
   const bool in_range = n >= 0 && off >= 0 && total <= p.max_seq_len && off + total <= p.num_rows;
   const int nch = tile_chunk_count(total, p.even_split, p.chunks, p.chunk_keys);
   if (chunk >= nch) return;
-  const bf16_t *const q_gate = (const bf16_t *)p.q_gate;
-  bf16_t *const outp = (bf16_t *)p.out;
   if (!in_range) {
     if (chunk == 0) {
       for (int e = t; e < R * D; e += kThreads) {
@@ -165,111 +269,136 @@ __global__ __launch_bounds__(kThreads) void turbo8_kernel(Params p, const uint8_
   const int64_t k0 = chunk_begin(total, p.even_split, nch, p.chunk_keys, chunk);
   const int64_t k1 = chunk == nch - 1 ? total : chunk_begin(total, p.even_split, nch, p.chunk_keys, chunk + 1);
   const bool tail = chunk == nch - 1, fuse_new = p.k_new != nullptr;
+  const bool cap_ok = total <= (int64_t)cap;
   const int64_t cend = min(k1, (int64_t)n);
   const int nst = cend > k0 ? (int)((cend - k0 + SK - 1) / SK) : 0;
 
-  // ---- one stage's codes and scales in registers: thread t holds groups
-  // t + 256 i of the stage (key = group / NG, 16-code group = group % NG)
-  uint4 kc[GPT], vc[GPT];
-  bf16_t ksc[GPT], vsc[GPT];
-  auto load_stage = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < GPT; ++i) {
-      const int gi = t + kThreads * i, key = gi / NG, grp = gi % NG;
-      const int64_t tk = min(k0 + (int64_t)SK * st + key, cend - 1);   // keys past the chunk repeat its last
-      const int64_t row = (off + tk) * hkv + kvh;
-      if constexpr (NG >= 1) {
-        kc[i] = gld<uint4>(kq + row * D + 16 * grp);
-        vc[i] = gld<uint4>(vq + row * D + 16 * grp);
-        ksc[i] = ks[row * NG + grp];
-        vsc[i] = vs[row * NG + grp];
-      }
+  // ---- copies.  Instruction q of a stage (0 <= q < NQ): K code rows (units
+  // 64 q + lane), V code rows, K scale dwords, V scale dwords.  Wavefront w
+  // has the list q = (w & 1) + 2 j (j < 2 U): a copy wave issues all of it in
+  // the first fill, a refill takes every other entry (j even in the copy
+  // waves, odd in the prep waves, so the four issue q = w + 4 j').  Its lane
+  // offsets are computed once; only a chunk's last, partial stage (keys past
+  // the chunk repeat its last) computes them again.
+  const unsigned ring_lds = (unsigned)(uintptr_t)(lds_void *)ring;
+  const unsigned rowc = (unsigned)(hkv * D), rows_ = (unsigned)(hkv * D / 8);
+  const int w1 = wave & 1;
+  unsigned offA[2 * U];
+  static_for<2 * U>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    offA[j] = T8::lane_off(w1 + 2 * j, lane, SK - 1, rowc, rows_);
+  });
+  auto issue = [&](int st, auto jc) {
+    constexpr int j = decltype(jc)::value, k = T8::kind(2 * j);
+    const int last = (int)min<int64_t>(SK - 1, cend - 1 - (k0 + (int64_t)SK * st));
+    const unsigned lo = last == SK - 1 ? offA[j] : T8::lane_off(w1 + 2 * j, lane, last, rowc, rows_);
+    const int64_t r0 = (off + k0 + (int64_t)SK * st) * hkv + kvh;
+    const unsigned dst = ring_lds + (st % NS) * SLOT + T8::region(k) + T8::ibytes(k) * (w1 + 2 * j - T8::first(k));
+    if constexpr (k == 0) dma16_sbase(kq + r0 * D, lo, dst);
+    if constexpr (k == 1) dma16_sbase(vq + r0 * D, lo, dst);
+    if constexpr (k >= 2) {
+      const unsigned char *const src = (const unsigned char *)(k == 2 ? ks : vs) + r0 * (D / 8);
+      if constexpr (T8::SX4)
+        dma16_sbase(src, lo, dst);
+      else
+        dma4_sbase(src, lo, dst);
     }
   };
-  // decode the registers' groups into the swizzled bf16 tiles of ring slot sl
-  auto store_stage = [&](int sl) {
-    unsigned char *kt = ring + sl * SLOT, *vt = ring + (2 + sl) * SLOT;
-#pragma unroll
-    for (int i = 0; i < GPT; ++i) {
-      const int gi = t + kThreads * i, key = gi / NG, grp = gi % NG;
-#pragma unroll
-      for (int tensor = 0; tensor < 2; ++tensor) {
-        const uint4 c = tensor ? vc[i] : kc[i];
-        const float s = (float)(tensor ? vsc[i] : ksc[i]);
-        const uint32_t w4[4] = {c.x, c.y, c.z, c.w};
-        f16x8 h[2];
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) {
-          const f32x2_t f = unpk_fp8(w4[j / 4], (j % 4) != 0);
-          h[j / 8][j % 8] = (f16_t)(f[0] * s);
-          h[j / 8][j % 8 + 1] = (f16_t)(f[1] * s);
-        }
-        unsigned char *tile = tensor ? vt : kt;
-        *(f16x8 *)(tile + swz<G::SW>(key, 2 * grp, RB)) = h[0];
-        *(f16x8 *)(tile + swz<G::SW>(key, 2 * grp + 1, RB)) = h[1];
-      }
-    }
-  };
-  if (nst > 0) load_stage(0);
 
-  // ---- query rows: norm, rotation, WHT, bf16 operands (16 lanes per row)
-  float2 *const tab = (float2 *)(arena + QBYTES);
-  rope_table(tab, p.positions, b, L, half, p.rope_step);
-  __syncthreads();
-  float wq[E], wk[E];
-  {
-    RawE<E> a, c;
-    a.load((const bf16_t *)p.wq + E * c16);
-    c.load((const bf16_t *)p.wk + E * c16);
-    a.to_float(wq);
-    c.to_float(wk);
-  }
-  const int hr = t / 16;                                // this lane group's row slot (0 .. 15)
+  // ---- prep waves: the new rows' loads (the second round trip: their
+  // addresses depend on n), before any copy of theirs
+  const int nr = 4 * (pw ^ 1) + g4;                     // new rows 8 k + nr go to the other prep wave
+  RawE<E> knraw[2], vnraw[2];
+  Turbo8Row<D> qk[2], qv[2];
+  if (!copier && tail) {
 #pragma unroll
-  for (int rt = 0; rt < RTM; ++rt) {
-    const int r = 16 * rt + hr, rc = min(r, R - 1);
-    const int l = rc / Gq, h = kvh * Gq + rc % Gq;
-    RawE<E> raw;
-    raw.load(q_gate + (((int64_t)b * L + l) * Hq + h) * 2 * D + E * c16);
-    float x[E];
-    raw.to_float(x);
-    norm_rope<D>(x, wq, r < R, p.eps, p.r, tab + l * half);
-    row_wht<D>(x);
-    put_row<D, f16_t>(arena, RB, r, E * c16, x);
-  }
-  // ---- the new rows (tail): quantized as the append does; stored when this
-  // call appends them, read back from the cache otherwise; kept decoded
-  float nk[E], nv[E];
-  Turbo8Row<D> qk, qv;
-  const int nl = hr;                                    // new row of this lane group
-  if (tail) {
-    const int lc = min(nl, L - 1);
-    const int64_t crow = (off + n + lc) * hkv + kvh;
-    if (fuse_new) {
-      RawE<E> a, c;
-      a.load((const bf16_t *)p.k_new + (((int64_t)b * L + lc) * hkv + kvh) * D + E * c16);
-      c.load((const bf16_t *)p.v_new + (((int64_t)b * L + lc) * hkv + kvh) * D + E * c16);
-      a.to_float(nk);
-      c.to_float(nv);
-      turbo8_new_row<D>(nk, true, wk, nl < L, p.eps, p.r, tab + lc * half, qk);
-      turbo8_new_row<D>(nv, false, wk, nl < L, p.eps, p.r, tab + lc * half, qv);
-    } else {
+    for (int k = 0; k < 2; ++k) {
+      const int l = min(8 * k + nr, L - 1);
+      if (fuse_new) {
+        const int64_t src = (((int64_t)b * L + l) * hkv + kvh) * D + E * c16;
+        knraw[k].load((const bf16_t *)p.k_new + src);
+        vnraw[k].load((const bf16_t *)p.v_new + src);
+      } else {
+        const int64_t crow = (off + n + l) * hkv + kvh;
 #pragma unroll
-      for (int c = 0; c < Turbo8Row<D>::CW; ++c) {
-        qk.codes[c] = *(const uint32_t *)(kq + crow * D + E * c16 + 4 * c);
-        qv.codes[c] = *(const uint32_t *)(vq + crow * D + E * c16 + 4 * c);
+        for (int c = 0; c < Turbo8Row<D>::CW; ++c) {
+          qk[k].codes[c] = *(const uint32_t *)(kq + crow * D + E * c16 + 4 * c);
+          qv[k].codes[c] = *(const uint32_t *)(vq + crow * D + E * c16 + 4 * c);
+        }
+        qk[k].scale = ks[crow * NG + E * c16 / 16];
+        qv[k].scale = vs[crow * NG + E * c16 / 16];
       }
-      qk.scale = ks[crow * NG + E * c16 / 16];
-      qv.scale = vs[crow * NG + E * c16 / 16];
-    }
-    qk.dequantize(nk);
-    qv.dequantize(nv);
-    if (nl >= L) {
-#pragma unroll
-      for (int j = 0; j < E; ++j) nk[j] = nv[j] = 0.f;
     }
   }
-  __syncthreads();
+  if (copier) {
+    for (int st = 0; st < min(NS, nst); ++st) static_for<2 * U>([&](auto jc) { issue(st, jc); });
+  }
+
+  float kx[2][E], vx[2][E];                             // decoded new rows 8 k + nr (prep waves, tail)
+  if (!copier) {
+    float2 *const tabw = (float2 *)(arena + QBYTES) + pw * TABN;
+    const double step = p.rope_step;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int e = lane + kWave * j;
+      if (kWave * j < L * half) {
+        float c, sn;
+        rope_angle_cs(tpos[j], rope_freq(step, tpair[j]), c, sn);
+        if (e < L * half) tabw[e] = make_float2(c, sn);
+      }
+    }
+    wave_lds_sync();
+    float wq[E], wk[E];
+    wqraw.to_float(wq);
+    wkraw.to_float(wk);
+#pragma unroll
+    for (int k = 0; k < NPASS; ++k) {
+      const int r = 8 * k + 4 * pw + g4;
+      float x[E];
+#pragma unroll
+      for (int j = 0; j < E; ++j) x[j] = 0.f;           // rows >= R are zero
+      if (8 * k + 4 * pw < R) {                         // the pass holds a row (wave-uniform)
+        qraw[k].to_float(x);
+        norm_rope<D>(x, wq, r < R, p.eps, p.r, tabw + (min(r, R - 1) / Gq) * half);
+        row_wht<D>(x);
+      }
+      put_row<D, f16_t>(arena, RB, r, E * c16, x);
+    }
+    if (tail) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int l = 8 * k + nr;
+        if (8 * k + 4 * (pw ^ 1) < L) {                 // the pass holds a new row (wave-uniform)
+          if (fuse_new) {
+            knraw[k].to_float(kx[k]);
+            vnraw[k].to_float(vx[k]);
+            turbo8_new_row<D>(kx[k], true, wk, l < L, p.eps, p.r, tabw + min(l, L - 1) * half, qk[k]);
+            turbo8_new_row<D>(vx[k], false, wk, l < L, p.eps, p.r, tabw + min(l, L - 1) * half, qv[k]);
+            if (l < L && cap_ok) {                      // the append: rows n + l
+              const int64_t crow = (off + n + l) * hkv + kvh;
+#pragma unroll
+              for (int c = 0; c < Turbo8Row<D>::CW; ++c) {
+                *(uint32_t *)(kq_w + crow * D + E * c16 + 4 * c) = qk[k].codes[c];
+                *(uint32_t *)(vq_w + crow * D + E * c16 + 4 * c) = qv[k].codes[c];
+              }
+              if (c16 % Turbo8Row<D>::LPG == 0) {
+                ks_w[crow * NG + E * c16 / 16] = qk[k].scale;
+                vs_w[crow * NG + E * c16 / 16] = qv[k].scale;
+              }
+            }
+          }
+          qk[k].dequantize(kx[k]);
+          qv[k].dequantize(vx[k]);
+        }
+        if (!(8 * k + 4 * (pw ^ 1) < L) || l >= L) {
+#pragma unroll
+          for (int j = 0; j < E; ++j) kx[k][j] = vx[k][j] = 0.f;
+        }
+      }
+    }
+  }
+  lds_barrier();                                        // query operands ready
+
   f16x8 qf[RTM][KST];
 #pragma unroll
   for (int rt = 0; rt < RTM; ++rt)
@@ -288,50 +417,108 @@ __global__ __launch_bounds__(kThreads) void turbo8_kernel(Params p, const uint8_
     for (int db = 0; db < DBW; ++db) O[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float sl2 = p.scale_log2;
-  __syncthreads();                                      // every wave holds its operands: the arena is the exchange now
+
+  // ---- the new rows first, from fp16 tiles in the V tile's place: V rows
+  // 0 .. 31 (zero from L on), K rows 0 .. 15 at rows 32 .. 47
+  if (tail) {
+    lds_barrier();                                      // every wave holds its query operands
+    if (!copier) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        put_row<D, f16_t>(vtile + 32 * RB, RB, 8 * k + nr, E * c16, kx[k]);
+        put_row<D, f16_t>(vtile, RB, 8 * k + nr, E * c16, vx[k]);
+      }
+    } else {
+      float z[E];
+#pragma unroll
+      for (int j = 0; j < E; ++j) z[j] = 0.f;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) put_row<D, f16_t>(vtile, RB, 16 + 8 * k + 4 * wave + g4, E * c16, z);
+    }
+    lds_barrier();
+    attend_stage<D, RTM, NoOp, f16_t>(vtile + 32 * RB, vtile, L, n, qf, O, mrun, lrun, lim, sl2, xch);
+  }
 
   // ---- cached stages
   for (int st = 0; st < nst; ++st) {
-    store_stage(st & 1);
-    if (st + 1 < nst) load_stage(st + 1);
-    __syncthreads();
+    // copies younger than stage st that this wave issued: of the ys later
+    // stages in flight, f are of the first fill (2 U per copy wave, none in a
+    // prep wave) and ys - f are refills (U per wave)
+    const int ys = min(NS - 1, nst - 1 - st);
+    const int f = max(0, min(NS, nst) - 1 - st);
+    WaitUnits<U, 2 * (NS - 1)>::run(copier ? ys + f : ys - f);
+    lds_barrier();
+    const unsigned char *const sl = ring + (st % NS) * SLOT;
+    // V codes -> fp16 V tile: thread t decodes groups t + 256 i (key, group);
+    // every read is issued before the first decode
+    constexpr int VG = SK * UPR / kThreads;
+    uint4 vcw[VG];
+    uint32_t vsb[VG];
+#pragma unroll
+    for (int i = 0; i < VG; ++i) {
+      const int gi = t + kThreads * i, key = gi / UPR, grp = gi % UPR;
+      vcw[i] = *(const uint4 *)(sl + T8::VC + key * D + 16 * grp);
+      vsb[i] = *(const uint16_t *)(sl + T8::VS + 2 * (key * UPR + grp));
+    }
+    const T8K<D> kop(sl);
+#pragma unroll
+    for (int i = 0; i < VG; ++i) {
+      const int gi = t + kThreads * i, key = gi / UPR, grp = gi % UPR;
+      const T8Scale sc(vsb[i]);
+      *(f16x8 *)(vtile + swz<G::SW>(key, 2 * grp, RB)) = t8_decode8(vcw[i].x, vcw[i].y, sc);
+      *(f16x8 *)(vtile + swz<G::SW>(key, 2 * grp + 1, RB)) = t8_decode8(vcw[i].z, vcw[i].w, sc);
+    }
     const int sk0 = (int)(k0 + (int64_t)SK * st);
     const int nk_ = (int)min<int64_t>(SK, cend - sk0);
-    attend_stage<D, RTM, NoOp, f16_t>(ring + (st & 1) * SLOT, ring + (2 + (st & 1)) * SLOT, nk_, sk0, qf, O, mrun,
-                                      lrun, lim, sl2, arena);
-  }
-  // ---- the new rows as a last stage: K and V rows 0 .. 15 (zero past L), V
-  // rows 16 .. 31 zero (read by the value product)
-  if (tail) {
-    const int sl = nst & 1;
-    unsigned char *kt = ring + sl * SLOT, *vt = ring + (2 + sl) * SLOT;
-    put_row<D, f16_t>(kt, RB, nl, E * c16, nk);
-    put_row<D, f16_t>(vt, RB, nl, E * c16, nv);
-    float z[E];
-#pragma unroll
-    for (int j = 0; j < E; ++j) z[j] = 0.f;
-    put_row<D, f16_t>(vt, RB, 16 + nl, E * c16, z);
-    __syncthreads();
-    attend_stage<D, RTM, NoOp, f16_t>(kt, vt, L, n, qf, O, mrun, lrun, lim, sl2, arena);
-  }
-
-  // ---- append (the fused call's new rows)
-  const int32_t *const capp = p.capacity;
-  const bool cap_ok = !capp || total <= (int64_t)capp[b];
-  if (tail && fuse_new && cap_ok && nl < L) {
-    const int64_t crow = (off + n + nl) * hkv + kvh;
-#pragma unroll
-    for (int c = 0; c < Turbo8Row<D>::CW; ++c) {
-      *(uint32_t *)(kq_w + crow * D + E * c16 + 4 * c) = qk.codes[c];
-      *(uint32_t *)(vq_w + crow * D + E * c16 + 4 * c) = qv.codes[c];
-    }
-    if (c16 % Turbo8Row<D>::LPG == 0) {
-      ks_w[crow * NG + E * c16 / 16] = qk.scale;
-      vs_w[crow * NG + E * c16 / 16] = qv.scale;
-    }
+    // The slot is consumed once every wave has its scores (its V codes were
+    // decoded and the K codes taken into registers before them): it is
+    // refilled then.  (Refilling at once, behind one more barrier, measured
+    // slower: the copies then wait in the memory pipeline ahead of the scores.)
+    auto refill = [&]() {
+      if (st + NS < nst) {
+        static_for<U>([&](auto jc) {
+          constexpr int j = 2 * decltype(jc)::value;
+          if (copier)
+            issue(st + NS, std::integral_constant<int, j>());
+          else
+            issue(st + NS, std::integral_constant<int, j + 1>());
+        });
+      }
+    };
+    attend_stage<D, RTM, decltype(refill), f16_t, T8K<D>>(nullptr, vtile, nk_, sk0, qf, O, mrun, lrun, lim, sl2,
+                                                           xch, refill, kop);
   }
 
-  // ---- rotate the rows back (iWHT) through LDS, then gate or store partials
+  const bool single = nch == 1;
+  const int64_t slot_rows = ((int64_t)slot * p.chunks + chunk) * p.rows;
+  if (!single) {
+    // ---- partials, still in the WHT basis (the merge rotates the merged
+    // rows): each wavefront stores its own dims of every row from registers
+    if (cap_ok) {
+#pragma unroll
+      for (int rt = 0; rt < RTM; ++rt) {
+        const int r = 16 * rt + m16;
+        if (r >= R) continue;
+#pragma unroll
+        for (int db = 0; db < DBW; ++db) {
+          const int d = 16 * (DBW * wave + db) + 4 * g4;
+          __builtin_nontemporal_store(O[rt][db], (f32x4 *)(p.part_o + (slot_rows + r) * D + d));
+        }
+        if (wave == 0 && g4 == 0) *(float2 *)(p.part_ml + (slot_rows + r) * 2) = make_float2(mrun[rt], lrun[rt]);
+      }
+    } else if (chunk == 0) {
+      for (int e = t; e < R * D; e += kThreads) {
+        const int r = e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
+        outp[(((int64_t)b * L + l) * Hq + h) * D + d] = (bf16_t)__builtin_nanf("");
+      }
+      if (t < R) *(float2 *)(p.part_ml + (slot_rows + t) * 2) = make_float2(__builtin_nanf(""), __builtin_nanf(""));
+      if (t == 0) flag_error(p);
+    }
+    return;
+  }
+
+  // ---- a chunk that is the whole sequence: rotate the rows back (iWHT)
+  // through LDS, 16 lanes per row, then the gate
   __syncthreads();                                      // every wave is done with the ring
   float *const otile = (float *)ring;                   // [16 RTM][D] fp32
   float *const linv = otile + 16 * RTM * D;             // [16 RTM] 1 / row sum
@@ -346,8 +533,7 @@ __global__ __launch_bounds__(kThreads) void turbo8_kernel(Params p, const uint8_
 #pragma unroll
     for (int rt = 0; rt < RTM; ++rt) linv[16 * rt + m16] = 1.f / lrun[rt];
   __syncthreads();
-  const bool single = nch == 1;
-  const int64_t slot_rows = ((int64_t)slot * p.chunks + chunk) * p.rows;
+  const int hr = t / 16;                                // this lane group's row slot (0 .. 15)
 #pragma unroll
   for (int rt = 0; rt < RTM; ++rt) {
     const int r = 16 * rt + hr;
@@ -358,45 +544,22 @@ __global__ __launch_bounds__(kThreads) void turbo8_kernel(Params p, const uint8_
     if (r >= R) continue;
     const int l = r / Gq, h = kvh * Gq + r % Gq;
     const int64_t orow = ((int64_t)b * L + l) * Hq + h;
-    if (single) {
-      RawE<E> zr;
-      zr.load(q_gate + orow * 2 * D + D + E * c16);
-      float z[E];
-      zr.to_float(z);
-      const float inv = linv[r];
-      float o[E];
+    RawE<E> zr;
+    zr.load(q_gate + orow * 2 * D + D + E * c16);
+    float z[E];
+    zr.to_float(z);
+    const float inv = linv[r];
+    bf16_t *dst = outp + orow * D + E * c16;
 #pragma unroll
-      for (int j = 0; j < E; ++j) o[j] = cap_ok ? x[j] * inv * sigmoid_f(z[j]) : __builtin_nanf("");
-      bf16_t *dst = outp + orow * D + E * c16;
-#pragma unroll
-      for (int j = 0; j < E; ++j) dst[j] = (bf16_t)o[j];
-    } else if (cap_ok) {
-      float *po = p.part_o + (slot_rows + r) * D + E * c16;
-#pragma unroll
-      for (int j = 0; j < E; j += 4) *(f32x4 *)(po + j) = f32x4{x[j], x[j + 1], x[j + 2], x[j + 3]};
-    }
+    for (int j = 0; j < E; ++j) dst[j] = (bf16_t)(cap_ok ? x[j] * inv * sigmoid_f(z[j]) : __builtin_nanf(""));
   }
-  if (!single && cap_ok && wave == 0 && g4 == 0) {
-#pragma unroll
-    for (int rt = 0; rt < RTM; ++rt)
-      if (16 * rt + m16 < R)
-        *(float2 *)(p.part_ml + (slot_rows + 16 * rt + m16) * 2) = make_float2(mrun[rt], lrun[rt]);
-  }
-  if (!cap_ok && chunk == 0) {
-    if (!single) {
-      for (int e = t; e < R * D; e += kThreads) {
-        const int r = e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
-        outp[(((int64_t)b * L + l) * Hq + h) * D + d] = (bf16_t)__builtin_nanf("");
-      }
-      if (t < R) *(float2 *)(p.part_ml + (slot_rows + t) * 2) = make_float2(__builtin_nanf(""), __builtin_nanf(""));
-    }
-    if (t == 0) flag_error(p);
-  }
+  if (!cap_ok && t == 0) flag_error(p);
 }
 
 template <int D>
 static hipError_t launch_turbo8_d(const Params &p, const Turbo8Cache &c, hipStream_t s, const Timing &tm) {
-  const int64_t blocks = (int64_t)p.B * p.Hkv * p.chunks;
+  const int64_t groups = ((int64_t)p.B * p.chunks + 7) / 8 * 8;   // (chunk, sequence) groups, rounded up to 8
+  const int64_t blocks = groups * p.Hkv;
   switch ((p.rows + 15) / 16) {
     case 1: launch_kernel(turbo8_kernel<D, 1>, blocks, s, tm, p, c.kq, c.ks, c.vq, c.vs, c.kq, c.ks, c.vq, c.vs); break;
     case 2: launch_kernel(turbo8_kernel<D, 2>, blocks, s, tm, p, c.kq, c.ks, c.vq, c.vs, c.kq, c.ks, c.vq, c.vs); break;
