@@ -243,3 +243,74 @@ def make_turbo8_inputs(w: Workload, variant: str = "graded", seed: int | None = 
                     torch.bfloat16)
         out[f"{t}_codes"], out[f"{t}_scales"] = codes, scales
     return out
+
+
+# ---------------------------------------------------------------- GatedDeltaNet decode
+@dataclass(frozen=True)
+class GdnWorkload:
+    """One decode step of the GatedDeltaNet (linear-attention) layer for a batch
+    of sequences.  Geometry of the 4B checkpoint (Atlas ``qwen3_5/mod.rs``,
+    ``Qwen35ForwardConfig::qwen3_5_4b_mlx_int8``: num_k_heads_lin 16,
+    num_v_heads_lin 32, k/v_head_dim_lin 128, conv_kernel_size 4, rms_eps 1e-6)."""
+    name: str
+    batch: int
+    num_k_heads: int = 16
+    num_v_heads: int = 32
+    k_head_dim: int = 128
+    v_head_dim: int = 128
+    conv_kernel: int = 4
+    seed: int = 0
+    rms_eps: float = 1e-6
+    description: str = ""
+
+    @property
+    def channels(self) -> int:        # QKV_TOTAL_LIN = 2 Hk Dk + Hv Dv
+        return 2 * self.num_k_heads * self.k_head_dim + self.num_v_heads * self.v_head_dim
+
+    def with_(self, **kw) -> "GdnWorkload":
+        return replace(self, **kw)
+
+
+GDN_WORKLOADS = {
+    "gdn_decode_4b": GdnWorkload("gdn_decode_4b", batch=64, seed=41,
+                                 description="4B GatedDeltaNet geometry, 64 sequences, one token each"),
+    "gdn_decode_4b_b1": GdnWorkload("gdn_decode_4b_b1", batch=1, seed=42,
+                                    description="4B GatedDeltaNet geometry, one sequence"),
+    "gdn_small": GdnWorkload("gdn_small", batch=3, num_k_heads=2, num_v_heads=4, seed=43,
+                             description="small parity case: 3 sequences, 2 key / 4 value heads"),
+}
+
+
+def make_gdn_inputs(w: GdnWorkload, seed: int | None = None, state_scale: float = 0.05) -> dict:
+    """Seeded inputs of one GatedDeltaNet decode step (one ``torch.Generator``
+    seeded with the workload's seed, drawn in this order, fp32 then cast):
+
+    1. ``qkv`` ``randn(B, C)`` bf16 (the q/k/v projection output, C = QKV_TOTAL_LIN);
+    2. ``z`` ``randn(B, Hv * Dv)`` bf16; ``a`` ``randn(B, Hv)`` bf16; ``b`` ``randn(B, Hv)`` bf16;
+    3. ``conv_w`` ``randn(C, K) / sqrt(K)`` bf16 ([C, K, 1] in the pages, the last axis dropped);
+    4. ``a_log`` ``log(uniform(1, 16))`` fp32 [Hv]; ``dt_bias`` ``1 + 0.1 randn(Hv)`` bf16;
+       ``norm_w`` ``1 + 0.1 randn(Dv)`` bf16;
+    5. ``conv_state`` ``randn(B, C, K)`` rounded to bf16 and held as fp32 (earlier inputs);
+    6. ``state`` ``state_scale * randn(B, Hv, Dk, Dv)`` fp32.
+
+    Shapes and dtypes follow the pages' layer structs (Atlas ``LinearAttentionLayer``:
+    a_log FP32, dt_bias BF16, conv1d_weight BF16, norm_weight BF16;
+    ``LinearAttentionState``: conv1d_state FP32 [C, K], gdn_state FP32 [Hv, Dk, Dv]
+    per sequence)."""
+    gen = torch.Generator("cpu").manual_seed(w.seed if seed is None else seed)
+    B, C, K = w.batch, w.channels, w.conv_kernel
+    Hv, Dk, Dv = w.num_v_heads, w.k_head_dim, w.v_head_dim
+    bf = torch.bfloat16
+    x = {
+        "qkv": torch.randn((B, C), generator=gen).to(bf),
+        "z": torch.randn((B, Hv * Dv), generator=gen).to(bf),
+        "a": torch.randn((B, Hv), generator=gen).to(bf),
+        "b": torch.randn((B, Hv), generator=gen).to(bf),
+        "conv_w": (torch.randn((C, K), generator=gen) / K ** 0.5).to(bf),
+        "a_log": torch.log(1.0 + 15.0 * torch.rand((Hv,), generator=gen)),
+        "dt_bias": (1.0 + 0.1 * torch.randn((Hv,), generator=gen)).to(bf),
+        "norm_w": (1.0 + 0.1 * torch.randn((Dv,), generator=gen)).to(bf),
+        "conv_state": torch.randn((B, C, K), generator=gen).to(bf).float(),
+        "state": state_scale * torch.randn((B, Hv, Dk, Dv), generator=gen),
+    }
+    return x
