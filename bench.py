@@ -397,6 +397,58 @@ def measure_proj(w, which, steps, warm, hidden=None):
             "call_achieved": round(gbs, 1), "call_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def measure_gdn(w, steps, warm):
+    """Time one GatedDeltaNet decode step (qsa_gdn_decode) of workload w in a HIP
+    graph, rotating over state sets of >= 1 GB in all so that every step streams
+    its recurrent state from HBM.  The state (read and written, fp32) dominates
+    the bytes; returns figures against the HBM roofline."""
+    from gated_gqa_attention_amd.workloads import make_gdn_inputs
+    dev = torch.device("cuda:0")
+    x = make_gdn_inputs(w)
+    B, C, K, Hv, D = w.batch, w.channels, w.conv_kernel, w.num_v_heads, w.v_head_dim
+    per_set = (x["state"].numel() + x["conv_state"].numel()) * 4
+    sets = max(1, min(64, -(-ROTATE_BYTES // per_set)))
+    fixed = {k: x[k].to(dev) for k in ("qkv", "z", "a", "b", "conv_w", "a_log", "dt_bias", "norm_w")}
+    states = [(x["conv_state"].to(dev), x["state"].to(dev)) for _ in range(sets)]
+    y = torch.empty((B, Hv, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.Stream()
+    cfg = binding.make_gdn_cfg(batch=B, num_k_heads=w.num_k_heads, num_v_heads=Hv, k_head_dim=w.k_head_dim,
+                               v_head_dim=D, conv_kernel=K, rms_eps=w.rms_eps, stream=stream.cuda_stream)
+
+    def call(i):
+        cs, st = states[i % sets]
+        binding.gdn_decode(cfg, fixed["qkv"], fixed["z"], fixed["a"], fixed["b"], fixed["conv_w"], fixed["a_log"],
+                           fixed["dt_bias"], fixed["norm_w"], cs, st, y)
+
+    with torch.cuda.stream(stream):
+        for i in range(warm):
+            call(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(steps):
+            call(warm + i)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    nbytes = (2 * per_set + (B * C + B * Hv * D + 2 * B * Hv + C * K + Hv + D) * 2 + Hv * 4 + B * Hv * D * 2)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    del states
+    torch.cuda.empty_cache()
+    return {"tokens_per_s": round(B / (ms / 1e3), 1), "us_per_call": round(ms * 1e3, 3), "steps": steps,
+            "warmup": warm, "batch": B, "state_sets": sets, "algorithmic_bytes": nbytes, "bound": "hbm",
+            "unit": "GB/s", "call_achieved": round(gbs, 1), "call_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "kernel": "gdn_decode_kernel (one launch per call)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -415,6 +467,8 @@ def main():
                     help="lay the cache out in shuffled blocks of this many rows (paged; 0: contiguous)")
     ap.add_argument("--proj", choices=["qkv", "o"], default=None,
                     help="time only the q/k/v (or o) projection at the decode shape and print its figures")
+    ap.add_argument("--gdn", choices=["gdn_decode_4b", "gdn_decode_4b_b1"], default=None,
+                    help="time only this GatedDeltaNet decode workload and print its figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 256 MiB device copy instead (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -432,6 +486,11 @@ def main():
         copy_calibration()
         return
     torch.cuda.set_device(torch.device("cuda:0"))
+    if args.gdn:
+        from gated_gqa_attention_amd.workloads import GDN_WORKLOADS
+        print(json.dumps({"gdn": args.gdn, **measure_gdn(GDN_WORKLOADS[args.gdn], args.steps or 200,
+                                                         args.warmup or 10)}), flush=True)
+        return
     if args.proj:
         print(json.dumps({"proj": args.proj, **measure_proj(WORKLOADS["decode_4b"], args.proj, args.steps or 1000,
                                                             args.warmup or 50)}), flush=True)
@@ -505,6 +564,10 @@ def main():
         # the projections either side of the core, at the decode shape (one row)
         extras["qkv_proj_4b"] = measure_proj(WORKLOADS["decode_4b"], "qkv", 1000, 50)
         extras["o_proj_4b"] = measure_proj(WORKLOADS["decode_4b"], "o", 1000, 50)
+        # the other layer type of the hybrid model: a GatedDeltaNet decode step
+        from gated_gqa_attention_amd.workloads import GDN_WORKLOADS
+        extras["gdn_decode_4b"] = measure_gdn(GDN_WORKLOADS["gdn_decode_4b"], 200, 10)
+        extras["gdn_decode_4b_b1"] = measure_gdn(GDN_WORKLOADS["gdn_decode_4b_b1"], 1000, 20)
         line["workloads"] = extras
     print(json.dumps(line), flush=True)
 

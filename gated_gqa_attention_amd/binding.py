@@ -20,7 +20,7 @@ QSA_KV_NATIVE, QSA_KV_TURBO8 = 0, 1
 _DT = {torch.bfloat16: QSA_BF16, torch.float32: QSA_F32}
 
 EXPORTS = ("qsa_workspace_size", "qsa_append_kv", "qsa_gated_attention", "qsa_gated_attention_noalloc",
-           "qsa_qkv_proj", "qsa_o_proj", "qsa_describe_plan", "qsa_last_error")
+           "qsa_qkv_proj", "qsa_o_proj", "qsa_gdn_decode", "qsa_describe_plan", "qsa_last_error")
 NOALLOC_SCRATCH_BYTES = 64 << 20     # QSA_NOALLOC_SCRATCH_BYTES
 
 
@@ -55,6 +55,14 @@ class KVCache(ctypes.Structure):
     ]
 
 
+class GdnCfg(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_k_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
+        ("k_head_dim", ctypes.c_int32), ("v_head_dim", ctypes.c_int32), ("conv_kernel", ctypes.c_int32),
+        ("rms_eps", ctypes.c_float), ("stream", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -84,6 +92,8 @@ def load():
         lib.qsa_qkv_proj.argtypes = [p, p, ctypes.c_int32, ctypes.POINTER(Cfg), p, p, p]
         lib.qsa_o_proj.restype = ctypes.c_int
         lib.qsa_o_proj.argtypes = [p, p, ctypes.c_int32, ctypes.POINTER(Cfg), p]
+        lib.qsa_gdn_decode.restype = ctypes.c_int
+        lib.qsa_gdn_decode.argtypes = [p] * 11 + [ctypes.POINTER(GdnCfg)]
         lib.qsa_describe_plan.restype = ctypes.c_int
         lib.qsa_describe_plan.argtypes = [ctypes.POINTER(Cfg), ctypes.c_char_p, ctypes.c_size_t]
         lib.qsa_last_error.restype = ctypes.c_char_p
@@ -178,3 +188,16 @@ def qkv_proj(cfg: Cfg, x, w_qkv, hidden: int, q_gate, k_new, v_new) -> None:
 def o_proj(cfg: Cfg, attn, w_o, hidden: int, y) -> None:
     """qsa_o_proj: y [rows, hidden] = attn [rows, Hq*D] times w_o^T."""
     _check(load().qsa_o_proj(_ptr(attn), _ptr(w_o), int(hidden), ctypes.byref(cfg), _ptr(y)))
+
+
+def make_gdn_cfg(*, batch, num_k_heads, num_v_heads, k_head_dim, v_head_dim, conv_kernel, rms_eps=1e-6,
+                 stream=None) -> GdnCfg:
+    return GdnCfg(batch, num_k_heads, num_v_heads, k_head_dim, v_head_dim, conv_kernel, rms_eps,
+                  stream if stream is not None else torch.cuda.current_stream().cuda_stream
+                  if torch.cuda.is_available() else None)
+
+
+def gdn_decode(cfg: GdnCfg, qkv, z, a, b, conv_w, a_log, dt_bias, norm_w, conv_state, state, y) -> None:
+    """qsa_gdn_decode: one GatedDeltaNet decode step; conv_state and state are updated in place."""
+    _check(load().qsa_gdn_decode(_ptr(qkv), _ptr(z), _ptr(a), _ptr(b), _ptr(conv_w), _ptr(a_log), _ptr(dt_bias),
+                                 _ptr(norm_w), _ptr(conv_state), _ptr(state), _ptr(y), ctypes.byref(cfg)))

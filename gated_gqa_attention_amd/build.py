@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqsa.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["qsa_api.hip", "qsa_rows.hip", "qsa_stream.hip", "qsa_prefill.hip", "qsa_merge.hip", "qsa_linear.hip",
-           "qsa_turbo.hip"]
+           "qsa_turbo.hip", "qsa_gdn.hip"]
 # per-source extra flags: the streaming, tile and merge kernels take their leading
 # argument dwords (metadata and query pointers, grid shape) preloaded into
 # SGPRs; their LDS copies set M0 from inline assembly, hence -Wno-inline-asm

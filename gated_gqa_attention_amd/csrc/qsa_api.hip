@@ -520,6 +520,69 @@ int qsa_o_proj(const void *attn, const void *w_o, int32_t hidden, const qsa_cfg 
   return QSA_OK;
 }
 
+int qsa_gdn_decode(const void *qkv, const void *z, const void *a, const void *b, const void *conv_w,
+                   const float *a_log, const void *dt_bias, const void *norm_w, float *conv_state, float *state,
+                   void *y, const qsa_gdn_cfg *cfg) {
+  if (!cfg) return fail(QSA_ERR_INVALID, "cfg is NULL");
+  const qsa_gdn_cfg &c = *cfg;
+  if (c.batch < 0 || c.num_k_heads < 1 || c.num_v_heads < 1 || c.num_v_heads % c.num_k_heads)
+    return fail(QSA_ERR_INVALID, "batch >= 0 and num_v_heads a multiple of num_k_heads >= 1 required");
+  const int R = c.num_v_heads / c.num_k_heads;
+  if (R != 1 && R != 2 && R != 4)
+    return fail(QSA_ERR_UNSUPPORTED, "num_v_heads / num_k_heads = %d not supported (1 | 2 | 4)", R);
+  if (c.k_head_dim != 128 || c.v_head_dim != 128)
+    return fail(QSA_ERR_UNSUPPORTED, "k_head_dim %d, v_head_dim %d not supported (128, 128)", c.k_head_dim,
+                c.v_head_dim);
+  if (c.conv_kernel < 1 || c.conv_kernel > 4)
+    return fail(QSA_ERR_UNSUPPORTED, "conv_kernel %d not supported (1 .. 4)", c.conv_kernel);
+  if (!(c.rms_eps >= 0.f)) return fail(QSA_ERR_INVALID, "rms_eps must be >= 0");
+  const void *ptrs[11] = {qkv, z, a, b, conv_w, a_log, dt_bias, norm_w, conv_state, state, y};
+  for (const void *q : ptrs) {
+    if (!q) return fail(QSA_ERR_INVALID, "every tensor argument is required");
+    if ((uintptr_t)q % 16) return fail(QSA_ERR_INVALID, "tensor arguments must be 16-byte aligned");
+  }
+  const int64_t B = c.batch, Hk = c.num_k_heads, Hv = c.num_v_heads, D = 128, K = c.conv_kernel;
+  const int64_t C = 2 * Hk * D + Hv * D;
+  if (B * Hk > 0x7fffffff) return fail(QSA_ERR_UNSUPPORTED, "batch * num_k_heads too large");
+  const size_t yb = (size_t)(B * Hv * D * 2);
+  const struct { const void *p; size_t n; } others[10] = {
+      {qkv, (size_t)(B * C * 2)}, {z, (size_t)(B * Hv * D * 2)}, {a, (size_t)(B * Hv * 2)},
+      {b, (size_t)(B * Hv * 2)}, {conv_w, (size_t)(C * K * 2)}, {a_log, (size_t)(Hv * 4)},
+      {dt_bias, (size_t)(Hv * 2)}, {norm_w, (size_t)(D * 2)}, {conv_state, (size_t)(B * C * K * 4)},
+      {state, (size_t)(B * Hv * D * D * 4)}};
+  for (const auto &o : others)
+    if (overlaps(y, yb, o.p, o.n)) return fail(QSA_ERR_INVALID, "y must not alias any other argument");
+  if (overlaps(conv_state, others[8].n, state, others[9].n))
+    return fail(QSA_ERR_INVALID, "conv_state and state overlap");
+  for (int i = 0; i < 8; ++i)
+    if (overlaps(others[i].p, others[i].n, conv_state, others[8].n) ||
+        overlaps(others[i].p, others[i].n, state, others[9].n))
+      return fail(QSA_ERR_INVALID, "the states must not alias the inputs");
+  int rc;
+  if ((rc = check_device()) != QSA_OK) return rc;
+  qsa::GdnParams p;
+  p.qkv = (const qsa::bf16_t *)qkv;
+  p.z = (const qsa::bf16_t *)z;
+  p.a = (const qsa::bf16_t *)a;
+  p.b = (const qsa::bf16_t *)b;
+  p.conv_w = (const qsa::bf16_t *)conv_w;
+  p.dt_bias = (const qsa::bf16_t *)dt_bias;
+  p.norm_w = (const qsa::bf16_t *)norm_w;
+  p.a_log = a_log;
+  p.conv_state = conv_state;
+  p.state = state;
+  p.y = (qsa::bf16_t *)y;
+  p.B = (int)B;
+  p.Hk = (int)Hk;
+  p.Hv = (int)Hv;
+  p.K = (int)K;
+  p.C = (int)C;
+  p.eps = c.rms_eps;
+  const hipError_t e = qsa::launch_gdn_decode(p, (hipStream_t)c.stream);
+  if (e != hipSuccess) return fail(QSA_ERR_DEVICE, "GatedDeltaNet launch failed: %s", hipGetErrorString(e));
+  return QSA_OK;
+}
+
 int qsa_gated_attention_noalloc(const void *q_gate, const void *k_new, const void *v_new, const qsa_kv_cache *kv,
                                 const int32_t *seq_lens, const int32_t *positions, const qsa_cfg *cfg,
                                 void *out) {

@@ -207,4 +207,18 @@ hipError_t launch_linear_bf16(const void *x, const void *w, int M, int N, int K,
                               void *y1, int n1_end, int ld1, void *y2, int ld2, hipStream_t s);
 constexpr int kMaxLinearRows = 64;    // rows (tokens) a projection call takes
 
+// One GatedDeltaNet decode step (qsa_gdn_decode): per sequence b, inputs qkv
+// [B][C] (C = 2 Hk D + Hv D), z [B][Hv D], a and b [B][Hv]; parameters conv_w
+// [C][K], a_log [Hv], dt_bias [Hv], norm_w [D]; states conv_state [B][C][K] and
+// state [B][Hv][D][D] (fp32, updated in place); output y [B][Hv][D].  D = 128.
+struct GdnParams {
+  const bf16_t *qkv, *z, *a, *b, *conv_w, *dt_bias, *norm_w;
+  const float *a_log;
+  float *conv_state, *state;
+  bf16_t *y;
+  int B, Hk, Hv, K, C;
+  float eps;
+};
+hipError_t launch_gdn_decode(const GdnParams &p, hipStream_t s);
+
 }  // namespace qsa

@@ -203,6 +203,51 @@ int qsa_qkv_proj(const void *x, const void *w_qkv, int32_t hidden, const qsa_cfg
  * output of qsa_gated_attention) and w_o [hidden][Hq D]. */
 int qsa_o_proj(const void *attn, const void *w_o, int32_t hidden, const qsa_cfg *cfg, void *y);
 
+/* One decode step of the GatedDeltaNet (linear-attention) layer that hybrid
+ * Qwen3.5 interleaves with the gated attention layers (Atlas docs,
+ * spark_model/forward/qwen3_5/mod.rs: LinearAttentionLayer, LinearAttentionState,
+ * LinearAttentionScratch, Qwen35ForwardConfig GDN sizes, Qwen35Kernels
+ * causal_conv1d_update_l2norm, gdn_compute_gate, sigmoid_bf16_to_f32,
+ * gated_delta_rule_decode), for a batch of sequences with one new token each.
+ * The pages give the tensors and kernel names; the rule is the published gated
+ * delta rule:
+ *   conv   : per channel c, the conv state row (the K latest inputs, oldest
+ *            first) takes the new input; u_c = silu(sum_j conv_w[c][j] row[j])
+ *   q, k   : per key head, x / sqrt(sum x^2 + 1e-6); q also / sqrt(Dk)
+ *   gate   : g = -exp(a_log) softplus(a + dt_bias); beta = sigmoid(b)
+ *   state  : per value head h (reading key head h / (Hv / Hk)),
+ *            S <- exp(g) S;  S <- S + beta k (v - S^T k)^T;  o = S^T q
+ *   output : y = o / sqrt(mean(o^2) + rms_eps) * norm_w * silu(z)
+ * u = [q channels Hk Dk | k channels Hk Dk | v channels Hv Dv] (C channels).
+ *
+ * Arguments (device pointers, 16-byte aligned, owned by the caller):
+ *   qkv        : [B][C] bf16, the in_proj_qkv output of each sequence's token
+ *   z          : [B][Hv Dv] bf16, the in_proj_z output (the output gate)
+ *   a, b       : [B][Hv] bf16, the in_proj_a / in_proj_b outputs
+ *   conv_w     : [C][K] bf16;  a_log : [Hv] fp32;  dt_bias : [Hv] bf16;
+ *   norm_w     : [Dv] bf16
+ *   conv_state : [B][C][K] fp32, read and updated in place
+ *   state      : [B][Hv][Dk][Dv] fp32, read and updated in place
+ *   y          : [B][Hv][Dv] bf16, written; must not alias any other argument
+ * Supported: Dk = Dv = 128, Hv / Hk in {1, 2, 4}, 1 <= K <= 4, batch >= 0.
+ * Arithmetic is fp32 (y rounded to bf16 once).  Asynchronous on cfg->stream;
+ * returns a qsa_status (invalid or unsupported arguments are refused before
+ * anything runs). */
+typedef struct qsa_gdn_cfg {
+  int32_t batch;        /* B: sequences */
+  int32_t num_k_heads;  /* Hk */
+  int32_t num_v_heads;  /* Hv (the state heads) */
+  int32_t k_head_dim;   /* Dk */
+  int32_t v_head_dim;   /* Dv */
+  int32_t conv_kernel;  /* K */
+  float rms_eps;        /* of the output norm */
+  void *stream;         /* hipStream_t, NULL for the default stream */
+} qsa_gdn_cfg;
+
+int qsa_gdn_decode(const void *qkv, const void *z, const void *a, const void *b, const void *conv_w,
+                   const float *a_log, const void *dt_bias, const void *norm_w, float *conv_state, float *state,
+                   void *y, const qsa_gdn_cfg *cfg);
+
 /* Bytes of device scratch that qsa_gated_attention_noalloc holds per GPU. */
 #define QSA_NOALLOC_SCRATCH_BYTES (64u << 20)
 

@@ -241,6 +241,31 @@ def test_paged_cache_descriptor_checked_before_launch():
     assert "128 blocks" in binding.last_error()
 
 
+def test_gdn_arguments_checked_before_launch():
+    lib = binding.load()
+    ptrs = [FAKE + (i << 30) for i in range(11)]
+
+    def call(cfg, p=ptrs):
+        return lib.qsa_gdn_decode(*p, ctypes.byref(cfg))
+
+    def cfg(**kw):
+        a = dict(batch=4, num_k_heads=16, num_v_heads=32, k_head_dim=128, v_head_dim=128, conv_kernel=4,
+                 stream=None)
+        a.update(kw)
+        return binding.make_gdn_cfg(**a)
+
+    assert call(cfg(num_v_heads=24)) == binding.QSA_ERR_INVALID                  # not a multiple of Hk
+    assert call(cfg(num_v_heads=48)) == binding.QSA_ERR_UNSUPPORTED              # Hv / Hk = 3
+    assert call(cfg(k_head_dim=64)) == binding.QSA_ERR_UNSUPPORTED
+    assert call(cfg(conv_kernel=5)) == binding.QSA_ERR_UNSUPPORTED
+    assert call(cfg(batch=-1)) == binding.QSA_ERR_INVALID
+    assert call(cfg(), ptrs[:10] + [None]) == binding.QSA_ERR_INVALID            # y missing
+    assert call(cfg(), ptrs[:10] + [ptrs[0] + 64]) == binding.QSA_ERR_INVALID    # y aliases qkv
+    assert call(cfg(), ptrs[:9] + [ptrs[8] + 16, ptrs[10]]) == binding.QSA_ERR_INVALID   # states overlap
+    assert call(cfg(), ptrs[:10] + [ptrs[10] + 8]) == binding.QSA_ERR_INVALID    # misaligned
+    assert "aligned" in binding.last_error()
+
+
 def test_workspace_scales_with_chunks():
     w = WORKLOADS["decode_4b"]
     one = binding.workspace_size(cfg_for(w, force_splits=1))
@@ -250,7 +275,7 @@ def test_workspace_scales_with_chunks():
 
 def test_ctypes_structs_match_the_header_layout(tmp_path):
     """Every field of the ctypes mirrors sits at the offset a C compiler gives it."""
-    structs = {"qsa_cfg": binding.Cfg, "qsa_kv_cache": binding.KVCache}
+    structs = {"qsa_cfg": binding.Cfg, "qsa_kv_cache": binding.KVCache, "qsa_gdn_cfg": binding.GdnCfg}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "qsa.h"', "int main(void) {"]
     for cname, py in structs.items():
         lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
