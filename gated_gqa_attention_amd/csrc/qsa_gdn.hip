@@ -163,11 +163,11 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_decode_kernel(GdnParams p) {
   const f32x4 delta = (v - eg * sk4) * bt;
   const f32x4 o = eg * sq4 + delta * kq;
 
-  // ---- the updated state
+  // ---- the updated state (written once, not read again here: non-temporal)
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const float kr = cbuf[D + rg * RPT + i];
-    *(f32x4 *)(srow + (int64_t)i * D) = eg * S[i] + kr * delta;
+    __builtin_nontemporal_store(eg * S[i] + kr * delta, (f32x4 *)(srow + (int64_t)i * D));
   }
 
   // ---- gated RMS norm over the value head's D outputs (lanes 0-31 of its first wavefront)
