@@ -314,3 +314,27 @@ def make_gdn_inputs(w: GdnWorkload, seed: int | None = None, state_scale: float 
         "state": state_scale * torch.randn((B, Hv, Dk, Dv), generator=gen),
     }
     return x
+
+
+def make_turbo4v_inputs(w: Workload, variant: str = "graded", seed: int | None = None) -> dict:
+    """Inputs of a call on a bf16-K / Turbo4-V cache: the bf16 inputs of
+    make_inputs (their K cache kept, their V cache replaced) plus V rows in
+    Turbo4 storage drawn directly: codes [rows, Hkv, D/2] as random bytes (two
+    uniform 4-bit indices each) and scales [rows, Hkv, D/16] as the E4M3 casts
+    of exp(0.25 N(0, 1)) (torch's float8_e4m3fn); rows past n_b are zero."""
+    x = make_inputs(w, variant=variant, seed=seed)
+    gen = torch.Generator("cpu").manual_seed((w.seed if seed is None else seed) + 3000)
+    rows = x["v_cache"].shape[0]
+    D, Hkv = w.head_dim, w.num_kv_heads
+    n, off = x["seq_lens"], x["seq_offset"]
+    out = {k: v for k, v in x.items() if k != "v_cache"}
+    codes = torch.zeros((rows, Hkv, D // 2), dtype=torch.uint8)
+    scales = torch.zeros((rows, Hkv, D // 16), dtype=torch.uint8)
+    for b in range(w.batch):
+        nb, o = int(n[b]), int(off[b])
+        if nb:
+            codes[o:o + nb] = torch.randint(0, 256, (nb, Hkv, D // 2), generator=gen, dtype=torch.uint8)
+            s = torch.exp(0.25 * torch.randn((nb, Hkv, D // 16), generator=gen))
+            scales[o:o + nb] = s.to(torch.float8_e4m3fn).view(torch.uint8)
+    out["v_codes"], out["v_scales"] = codes, scales
+    return out

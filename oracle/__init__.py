@@ -100,6 +100,16 @@ def _load():
         lib.qsa_oracle_turbo8_attention.restype = ctypes.c_int
         lib.qsa_oracle_turbo8_attention.argtypes = [ctypes.POINTER(_Cfg), p, p, p, p, p, p, p, p, p, p, p, p, p,
                                                     p, ctypes.c_int64, p]
+        lib.qsa_oracle_lloyd_max_normal.restype = ctypes.c_int
+        lib.qsa_oracle_lloyd_max_normal.argtypes = [ctypes.c_int, p]
+        lib.qsa_oracle_turbo4_quantize.restype = ctypes.c_int
+        lib.qsa_oracle_turbo4_quantize.argtypes = [p, ctypes.c_int, p, p, p]
+        lib.qsa_oracle_turbo4_dequantize.restype = ctypes.c_int
+        lib.qsa_oracle_turbo4_dequantize.argtypes = [p, p, ctypes.c_int, p, p]
+        lib.qsa_oracle_bf16k_turbo4v_new_kv.restype = ctypes.c_int
+        lib.qsa_oracle_bf16k_turbo4v_new_kv.argtypes = [ctypes.POINTER(_Cfg), p, p, p, p, p, p, p, p]
+        lib.qsa_oracle_bf16k_turbo4v_attention.restype = ctypes.c_int
+        lib.qsa_oracle_bf16k_turbo4v_attention.argtypes = [ctypes.POINTER(_Cfg)] + [p] * 13 + [ctypes.c_int64, p]
         lib.qsa_oracle_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -414,6 +424,109 @@ def turbo8_gated_attention(geo: Geometry, inputs: dict, rows=None, fused=True):
     out = turbo8_attention(geo, inputs["q_gate"], inputs["w_q"], inputs["k_codes"], inputs["k_scales"],
                            inputs["v_codes"], inputs["v_scales"], inputs["seq_offset"], inputs["seq_lens"],
                            inputs["positions"], new=new, rows=rows)
+    return out, new
+
+
+# ------------------------------------------------------------------ bf16 K + Turbo4 V
+# Atlas docs, spark_model/forward/qwen3_5/mod.rs, MetalKvDtype::Bf16KTurbo4V and
+# LayerKvCache::alloc: K stays a bf16 cache (not rotated); V is Turbo4 -- 4-bit
+# Lloyd-Max codebook indices and an FP8 scale per group of 16 (matched-norm L2)
+# in the WHT basis -- with the iWHT(out) bookend.  Readings (codebook, index
+# rule, scale rule, packing) are in qsa_oracle.h.
+
+def lloyd_max_normal(levels: int = 16) -> np.ndarray:
+    """The Lloyd-Max quantizer levels of N(0, 1), ascending."""
+    c = np.empty(levels)
+    if _load().qsa_oracle_lloyd_max_normal(levels, _ptr(c)) != 0:
+        raise ValueError("levels must be in 2 .. 256")
+    return c
+
+
+def turbo4_quantize(x, cb=None):
+    """Turbo4 codes (uint8, last axis / 2, two per byte) and E4M3 scales (uint8,
+    last axis / 16) of x."""
+    lib = _load()
+    cb = lloyd_max_normal() if cb is None else np.ascontiguousarray(cb, dtype=np.float64)
+    a = _f64(x)
+    flat = a.reshape(-1, a.shape[-1])
+    n = flat.shape[1]
+    codes = np.empty((flat.shape[0], n // 2), dtype=np.uint8)
+    scales = np.empty((flat.shape[0], n // 16), dtype=np.uint8)
+    for i in range(flat.shape[0]):
+        row = np.ascontiguousarray(flat[i])
+        cr, sr = np.empty(n // 2, dtype=np.uint8), np.empty(n // 16, dtype=np.uint8)
+        if lib.qsa_oracle_turbo4_quantize(_ptr(row), n, _ptr(cb), _ptr(cr), _ptr(sr)) != 0:
+            raise ValueError("Turbo4 rows need a multiple of 16 elements")
+        codes[i], scales[i] = cr, sr
+    return codes.reshape(a.shape[:-1] + (n // 2,)), scales.reshape(a.shape[:-1] + (n // 16,))
+
+
+def turbo4_dequantize(codes, scales, cb=None) -> np.ndarray:
+    """codebook level times group scale, in double."""
+    lib = _load()
+    cb = lloyd_max_normal() if cb is None else np.ascontiguousarray(cb, dtype=np.float64)
+    c, s = _u8(codes), _u8(scales)
+    n = c.shape[-1] * 2
+    cf, sf = c.reshape(-1, n // 2), s.reshape(-1, n // 16)
+    out = np.empty((cf.shape[0], n))
+    for i in range(cf.shape[0]):
+        row = np.empty(n)
+        lib.qsa_oracle_turbo4_dequantize(_ptr(np.ascontiguousarray(cf[i])), _ptr(np.ascontiguousarray(sf[i])), n,
+                                         _ptr(cb), _ptr(row))
+        out[i] = row
+    return out.reshape(c.shape[:-1] + (n,))
+
+
+def bf16k_turbo4v_new_kv(geo: Geometry, k_new, v_new, w_k, positions, cb=None):
+    """New rows: (K rows as bf16 values in double, V codes, V scales)."""
+    lib = _load()
+    cb = lloyd_max_normal() if cb is None else np.ascontiguousarray(cb, dtype=np.float64)
+    kn, vn, wk, pos = _f64(k_new), _f64(v_new), _f64(w_k), _i32(positions)
+    D = geo.head_dim
+    kr = np.empty(kn.shape)
+    vc = np.empty(kn.shape[:-1] + (D // 2,), dtype=np.uint8)
+    vs = np.empty(kn.shape[:-1] + (D // 16,), dtype=np.uint8)
+    if lib.qsa_oracle_bf16k_turbo4v_new_kv(ctypes.byref(geo._c()), _ptr(kn), _ptr(vn), _ptr(wk), _ptr(pos), _ptr(cb),
+                                           _ptr(kr), _ptr(vc), _ptr(vs)) != 0:
+        raise ValueError("oracle rejected the configuration")
+    return kr, vc, vs
+
+
+def bf16k_turbo4v_attention(geo: Geometry, q_gate, w_q, k_cache, v_codes, v_scales, seq_offset, seq_lens, positions,
+                            new=None, rows=None, cb=None):
+    """Gated attention with K from a bf16 cache and V from Turbo4 rows; `new` =
+    bf16k_turbo4v_new_kv(...) output for keys n_b .. n_b+L-1, or None when those
+    rows are in the cache."""
+    lib = _load()
+    cb = lloyd_max_normal() if cb is None else np.ascontiguousarray(cb, dtype=np.float64)
+    qg, wq = _f64(q_gate), _f64(w_q)
+    kc, vc, vs = _u16(k_cache), _u8(v_codes), _u8(v_scales)
+    off, sl, pos = _i64(seq_offset), _i32(seq_lens), _i32(positions)
+    nk = [None] * 3 if new is None else [np.ascontiguousarray(new[0], dtype=np.float64), _u8(new[1]), _u8(new[2])]
+    D = geo.head_dim
+    if rows is None:
+        out = np.empty((geo.batch, geo.q_len, geo.num_q_heads, D))
+        r, n = None, 0
+    else:
+        r = _i64(rows)
+        n = r.size
+        out = np.empty((n, D))
+    rc = lib.qsa_oracle_bf16k_turbo4v_attention(ctypes.byref(geo._c()), _ptr(qg), _ptr(wq), _ptr(kc), _ptr(vc),
+                                                _ptr(vs), _ptr(off), _ptr(sl), _ptr(pos), _ptr(cb), _ptr(nk[0]),
+                                                _ptr(nk[1]), _ptr(nk[2]), _ptr(r), n, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the configuration or a row index")
+    return out
+
+
+def bf16k_turbo4v_gated_attention(geo: Geometry, inputs: dict, rows=None, fused=True):
+    """Whole call on a bf16-K / Turbo4-V cache (inputs from make_turbo4v_inputs):
+    the new rows (when fused), then attention.  Returns (out, new rows)."""
+    new = (bf16k_turbo4v_new_kv(geo, inputs["k_new"], inputs["v_new"], inputs["w_k"], inputs["positions"])
+           if fused else None)
+    out = bf16k_turbo4v_attention(geo, inputs["q_gate"], inputs["w_q"], inputs["k_cache"], inputs["v_codes"],
+                                  inputs["v_scales"], inputs["seq_offset"], inputs["seq_lens"], inputs["positions"],
+                                  new=new, rows=rows)
     return out, new
 
 

@@ -406,6 +406,176 @@ int qsa_oracle_turbo8_attention(const qsa_oracle_cfg *c, const double *q_gate, c
   return err ? -1 : 0;
 }
 
+/* ---- bf16 K + Turbo4 V ------------------------------------------------- */
+
+static double npdf(double x) { return isinf(x) ? 0.0 : exp(-0.5 * x * x) / sqrt(2.0 * acos(-1.0)); }
+
+/* P(lo < X < hi) for X ~ N(0, 1), from whichever tail keeps the precision */
+static double nmass(double lo, double hi) {
+  const double r2 = sqrt(2.0);
+  if (hi <= 0.0) return 0.5 * (erfc(-hi / r2) - erfc(-lo / r2));
+  if (lo >= 0.0) return 0.5 * (erfc(lo / r2) - erfc(hi / r2));
+  return 1.0 - 0.5 * erfc(-lo / r2) - 0.5 * erfc(hi / r2);
+}
+
+int qsa_oracle_lloyd_max_normal(int levels, double *c) {
+  if (levels < 2 || levels > 256) return -1;
+  double nc[256];
+  for (int i = 0; i < levels; ++i) c[i] = -3.0 + 6.0 * (i + 0.5) / levels;
+  for (int it = 0; it < 200000; ++it) {
+    double change = 0.0;
+    for (int i = 0; i < levels; ++i) {
+      const double lo = i == 0 ? -INFINITY : 0.5 * (c[i - 1] + c[i]);
+      const double hi = i == levels - 1 ? INFINITY : 0.5 * (c[i] + c[i + 1]);
+      nc[i] = (npdf(lo) - npdf(hi)) / nmass(lo, hi);      /* the cell's conditional mean */
+      change = fmax(change, fabs(nc[i] - c[i]));
+    }
+    for (int i = 0; i < levels; ++i) c[i] = nc[i];
+    if (change < 1e-16) break;
+  }
+  for (int i = 0; i < levels / 2; ++i) {                  /* exact symmetry */
+    const double m = 0.5 * (c[levels - 1 - i] - c[i]);
+    c[i] = -m;
+    c[levels - 1 - i] = m;
+  }
+  return 0;
+}
+
+int qsa_oracle_turbo4_quantize(const double *x, int n, const double *cb, uint8_t *codes, uint8_t *scales) {
+  if (n < 16 || n % 16) return -1;
+  for (int g = 0; g < n / 16; ++g) {
+    const double *xg = x + 16 * g;
+    uint8_t *cg = codes + 8 * g;
+    double ss = 0.0;
+    for (int i = 0; i < 16; ++i) ss += xg[i] * xg[i];
+    for (int i = 0; i < 8; ++i) cg[i] = 0;
+    if (ss == 0.0) {
+      scales[g] = 0;
+      continue;
+    }
+    const double sigma = sqrt(ss / 16.0);
+    double cc = 0.0;
+    for (int i = 0; i < 16; ++i) {
+      const double u = xg[i] / sigma;
+      int idx = 0;                                         /* nearest level: thresholds below u */
+      for (int j = 0; j < 15; ++j)
+        if (0.5 * (cb[j] + cb[j + 1]) < u) idx = j + 1;
+      cc += cb[idx] * cb[idx];
+      cg[i / 2] |= (uint8_t)(idx << (4 * (i & 1)));
+    }
+    scales[g] = qsa_oracle_e4m3_code(sqrt(ss / cc));    /* matched L2 norm */
+  }
+  return 0;
+}
+
+int qsa_oracle_turbo4_dequantize(const uint8_t *codes, const uint8_t *scales, int n, const double *cb, double *x) {
+  if (n < 16 || n % 16) return -1;
+  for (int i = 0; i < n; ++i) x[i] = qsa_oracle_e4m3_value(scales[i / 16]) * cb[(codes[i / 2] >> (4 * (i & 1))) & 15];
+  return 0;
+}
+
+int qsa_oracle_bf16k_turbo4v_new_kv(const qsa_oracle_cfg *c, const double *k_new, const double *v_new,
+                                    const double *w_k, const int32_t *positions, const double *cb, double *k_rows,
+                                    uint8_t *v_codes, uint8_t *v_scales) {
+  if (!cfg_ok(c) || c->head_dim % 16 || (c->head_dim & (c->head_dim - 1))) return -1;
+  const int L = c->q_len, Hkv = c->num_kv_heads, D = c->head_dim;
+  const int64_t n = (int64_t)c->batch * L * Hkv;
+  int err = 0;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    double *r = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!r) {
+#pragma omp atomic write
+      err = 1;
+      continue;
+    }
+    double *ko = k_rows + i * D;                           /* K: the bf16 cache's row */
+    rms_norm(k_new + i * D, w_k, D, c->rms_eps, ko);
+    rope(ko, c->rotary_dim, c->rope_theta, (double)positions[i / Hkv]);
+    for (int d = 0; d < D; ++d) ko[d] = qsa_oracle_round(ko[d], 8);
+    qsa_oracle_wht(v_new + i * D, D, r);                   /* V: rotated, then Turbo4 */
+    qsa_oracle_turbo4_quantize(r, D, cb, v_codes + i * (D / 2), v_scales + i * (D / 16));
+    free(r);
+  }
+  return err ? -1 : 0;
+}
+
+int qsa_oracle_bf16k_turbo4v_attention(const qsa_oracle_cfg *c, const double *q_gate, const double *w_q,
+                                       const uint16_t *k_cache, const uint8_t *v_codes, const uint8_t *v_scales,
+                                       const int64_t *seq_offset, const int32_t *seq_lens, const int32_t *positions,
+                                       const double *cb, const double *nk_rows, const uint8_t *nv_codes,
+                                       const uint8_t *nv_scales, const int64_t *rows, int64_t n_rows, double *out) {
+  if (!cfg_ok(c) || c->head_dim % 16 || (c->head_dim & (c->head_dim - 1))) return -1;
+  const int given = (nk_rows != NULL) + (nv_codes != NULL) + (nv_scales != NULL);
+  if (given != 0 && given != 3) return -1;
+  const int B = c->batch, L = c->q_len, Hq = c->num_q_heads, Hkv = c->num_kv_heads;
+  const int D = c->head_dim, G = Hq / Hkv;
+  const double scale = scale_of(c);
+  const int64_t total = (int64_t)B * L * Hq;
+  const int64_t count = rows ? n_rows : total;
+  for (int64_t i = 0; i < count; ++i) {
+    const int64_t f = rows ? rows[i] : i;
+    if (f < 0 || f >= total) return -1;
+  }
+  int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < count; ++i) {
+    const int64_t f = rows ? rows[i] : i;
+    const int h = (int)(f % Hq);
+    const int64_t bl = f / Hq;
+    const int l = (int)(bl % L), b = (int)(bl / L), g = h / G;
+    const int64_t n = seq_lens[b], nkeys = n + l + 1;
+    double *q = (double *)malloc(sizeof(double) * (size_t)D);
+    double *vv = (double *)malloc(sizeof(double) * (size_t)D);
+    double *o = (double *)calloc((size_t)D, sizeof(double));
+    double *ob = (double *)malloc(sizeof(double) * (size_t)D);
+    double *s = (double *)malloc(sizeof(double) * (size_t)nkeys);
+    if (!q || !vv || !o || !ob || !s) {
+#pragma omp atomic write
+      err = 1;
+      free(q); free(vv); free(o); free(ob); free(s);
+      continue;
+    }
+    const double *qh = q_gate + f * 2 * D, *zh = qh + D;
+    rms_norm(qh, w_q, D, c->rms_eps, q);
+    rope(q, c->rotary_dim, c->rope_theta, (double)positions[bl]);   /* K is not rotated: no WHT(Q) */
+    for (int64_t j = 0; j < nkeys; ++j) {
+      double acc = 0.0;
+      if (j >= n && nk_rows) {
+        const double *kr = nk_rows + (((int64_t)b * L + (j - n)) * Hkv + g) * D;
+        for (int d = 0; d < D; ++d) acc += q[d] * kr[d];
+      } else {
+        const int64_t r = ((seq_offset[b] + j) * Hkv + g) * D;
+        for (int d = 0; d < D; ++d) acc += q[d] * load(k_cache, QSA_ORACLE_BF16, r + d);
+      }
+      s[j] = scale * acc;
+    }
+    double m = s[0];
+    for (int64_t j = 1; j < nkeys; ++j) m = s[j] > m ? s[j] : m;
+    double sum = 0.0;
+    for (int64_t j = 0; j < nkeys; ++j) {
+      s[j] = exp(s[j] - m);
+      sum += s[j];
+    }
+    for (int64_t j = 0; j < nkeys; ++j) {
+      if (j >= n && nv_codes) {
+        const int64_t r = ((int64_t)b * L + (j - n)) * Hkv + g;
+        qsa_oracle_turbo4_dequantize(nv_codes + r * (D / 2), nv_scales + r * (D / 16), D, cb, vv);
+      } else {
+        const int64_t r = (seq_offset[b] + j) * Hkv + g;
+        qsa_oracle_turbo4_dequantize(v_codes + r * (D / 2), v_scales + r * (D / 16), D, cb, vv);
+      }
+      const double p = s[j] / sum;
+      for (int d = 0; d < D; ++d) o[d] += p * vv[d];
+    }
+    qsa_oracle_wht(o, D, ob);                              /* iWHT(out): V is rotated */
+    double *dst = out + i * D;
+    for (int d = 0; d < D; ++d) dst[d] = qsa_oracle_round(ob[d] / (1.0 + exp(-zh[d])), c->store_bits);
+    free(q); free(vv); free(o); free(ob); free(s);
+  }
+  return err ? -1 : 0;
+}
+
 int qsa_oracle_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -150,6 +150,44 @@ int qsa_oracle_turbo8_attention(const qsa_oracle_cfg *cfg, const double *q_gate,
                                 const uint8_t *nv_codes, const uint16_t *nv_scales, const int64_t *rows,
                                 int64_t n_rows, double *out);
 
+/* ---- bf16 K + Turbo4 V (Atlas docs, spark_model/forward/qwen3_5/mod.rs:
+ * MetalKvDtype::Bf16KTurbo4V -- K raw bf16 (not rotated), V Turbo4: 4-bit
+ * Lloyd-Max codebook indices plus an FP8 scale per group of 16 elements,
+ * matched-norm L2, in the Walsh-Hadamard rotated basis; LayerKvCache::alloc --
+ * K two bytes per element, V half a byte per element and one scale byte per
+ * 16; the iWHT(out) bookend only, since only V is rotated).  Readings where
+ * the page is silent (parity against the page unpinned): the codebook is the
+ * 16-level Lloyd-Max quantizer of the standard normal (the WHT makes a row's
+ * coordinates near Gaussian), ascending, index 0 the most negative; a group's
+ * indices are the levels nearest to x / sigma (sigma its RMS, the lower index
+ * on a tie) and its scale is sqrt(sum x^2 / sum c^2) rounded to E4M3 (the
+ * reconstruction keeps the group's L2 norm), a zero group taking scale 0;
+ * codes pack two per byte, element 2i in the low nibble. */
+
+/* The Lloyd-Max quantizer of N(0, 1) with `levels` levels (Lloyd's iteration
+ * on the exact cell masses and conditional means), ascending, exactly
+ * symmetric.  Returns 0 or -1. */
+int qsa_oracle_lloyd_max_normal(int levels, double *centroids);
+/* Turbo4: codes[n/2] (two per byte) and E4M3 scales[n/16] of x[n] under the
+ * 16-level codebook cb.  Returns 0 or -1. */
+int qsa_oracle_turbo4_quantize(const double *x, int n, const double *cb, uint8_t *codes, uint8_t *scales);
+int qsa_oracle_turbo4_dequantize(const uint8_t *codes, const uint8_t *scales, int n, const double *cb, double *x);
+/* New rows: K = bf16(rope(rmsnorm(k_new) * w_k)) as double [B][L][Hkv][D];
+ * V = turbo4(WHT(v_new)): codes [B][L][Hkv][D/2], scales [B][L][Hkv][D/16]. */
+int qsa_oracle_bf16k_turbo4v_new_kv(const qsa_oracle_cfg *cfg, const double *k_new, const double *v_new,
+                                    const double *w_k, const int32_t *positions, const double *cb, double *k_rows,
+                                    uint8_t *v_codes, uint8_t *v_scales);
+/* Gated attention with K from a bf16 cache (bit patterns, [rows][Hkv][D]) and
+ * V decoded from Turbo4 rows ([rows][Hkv][D/2] codes, [rows][Hkv][D/16]
+ * scales), the attention output rotated back by WHT before the gate; new rows
+ * from qsa_oracle_bf16k_turbo4v_new_kv, or all three NULL when they are in the
+ * cache.  Returns 0 or -1. */
+int qsa_oracle_bf16k_turbo4v_attention(const qsa_oracle_cfg *cfg, const double *q_gate, const double *w_q,
+                                       const uint16_t *k_cache, const uint8_t *v_codes, const uint8_t *v_scales,
+                                       const int64_t *seq_offset, const int32_t *seq_lens, const int32_t *positions,
+                                       const double *cb, const double *nk_rows, const uint8_t *nv_codes,
+                                       const uint8_t *nv_scales, const int64_t *rows, int64_t n_rows, double *out);
+
 /* Number of OpenMP threads the oracle runs with. */
 int qsa_oracle_threads(void);
 
