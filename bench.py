@@ -26,7 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from gated_gqa_attention_amd import binding  # noqa: E402
-from gated_gqa_attention_amd.workloads import (DTYPES, WORKLOADS, make_inputs, make_turbo8_inputs,  # noqa: E402
+from gated_gqa_attention_amd.workloads import (DTYPES, WORKLOADS, make_inputs, make_turbo4v_inputs, make_turbo8_inputs,  # noqa: E402
                                                to_paged)
 
 METRIC = "gated-GQA attn tokens/s + effective HBM GB/s (% of peak), 4B geometry decode"
@@ -38,22 +38,24 @@ DEFAULT_STEPS = {"decode_4b": (2000, 200), "verify_24x2": (1000, 100), "ragged_4
                  "prefill_4b": (20, 3), "tiny_f32": (1000, 100)}
 
 
-def algorithmic_work(w, seq_lens, turbo8=False):
+def algorithmic_work(w, seq_lens, kv="native"):
     """Bytes the method must move and FLOPs it must do per call (QK^T and PV only).
 
     Returns (total bytes, output bytes, flops).  The output bytes are listed apart
     because a call that splits its keys writes the output from a second, small
     kernel; every other byte is moved by the kernel that streams the KV cache.
-    turbo8: a cached row of one KV head is D one-byte codes plus D/16 bf16
-    scales, for K and for V."""
+    Bytes of one cached row of one KV head: native D elements of the dtype;
+    turbo8 D one-byte codes plus D/16 bf16 scales, for K and for V; turbo4v K D
+    bf16, V D/2 index bytes plus D/16 E4M3 scale bytes."""
     es = 2 if w.dtype == "bf16" else 4
     B, L, Hq, Hkv, D = w.batch, w.q_len, w.num_q_heads, w.num_kv_heads, w.head_dim
     n = [int(x) for x in seq_lens]
-    row = D + D // 8 if turbo8 else D * es                # bytes of one cached row of one KV head
-    kv_read = sum(n) * Hkv * row * 2                    # cached K and V rows
+    krow, vrow = {"native": (D * es, D * es), "turbo8": (D + D // 8, D + D // 8),
+                  "turbo4v": (2 * D, D // 2 + D // 16)}[kv]
+    kv_read = sum(n) * Hkv * (krow + vrow)               # cached K and V rows
     reads = B * L * Hq * 2 * D * es + 2 * B * L * Hkv * D * es + 2 * D * es + 4 * B + 4 * B * L
     out = B * L * Hq * D * es
-    writes = out + 2 * B * L * Hkv * row
+    writes = out + B * L * Hkv * (krow + vrow)
     keys = sum(nb * L + L * (L + 1) // 2 for nb in n)    # sum over rows of the keys each row sees
     flops = keys * Hq * 4 * D
     return kv_read + reads + writes, out, flops
@@ -111,6 +113,9 @@ class Call:
         if "k_codes" in dev:
             self.kv = binding.make_kv(dev["k_codes"], dev["v_codes"], dev["seq_offset"], dev["capacity"],
                                       k_scales=dev["k_scales"], v_scales=dev["v_scales"])
+        elif "v_codes" in dev:                          # bf16 K + Turbo4 V
+            self.kv = binding.make_kv(dev["k_cache"], dev["v_codes"], dev["seq_offset"], dev["capacity"],
+                                      v_scales=dev["v_scales"])
         elif "block_table" in dev:
             self.kv = binding.make_kv(dev["k_cache"], dev["v_cache"], None, dev["capacity"], dev["block_table"],
                                       block_size)
@@ -223,14 +228,14 @@ def cpu_model():
     return "unknown"
 
 
-def measure(w, steps, warm, launch="graph", force_splits=0, sets=None, block_size=0, turbo8=False):
+def measure(w, steps, warm, launch="graph", force_splits=0, sets=None, block_size=0, kv="native"):
     """Time one workload: `warm` untimed eager calls, then `steps` calls captured in
     one HIP graph, replayed once untimed and once timed (HIP events on the launch
     stream), then the attention kernel on its own in an eager pass.  block_size >
     0: the cache is laid out in shuffled blocks of that many rows (paged).
     Returns the inputs and a dict of figures."""
     dev = torch.device("cuda:0")
-    inputs = make_turbo8_inputs(w) if turbo8 else make_inputs(w)
+    inputs = {"turbo8": make_turbo8_inputs, "turbo4v": make_turbo4v_inputs}.get(kv, make_inputs)(w)
     max_seq_len = int((inputs["seq_lens"].max() + w.q_len).item())
     base = {k: v.to(dev) for k, v in inputs.items()}
     if block_size:
@@ -298,7 +303,7 @@ def measure(w, steps, warm, launch="graph", force_splits=0, sets=None, block_siz
     kernel_ms = kernel_times(calls, stream, min(steps, 500))
 
     tokens_per_call = w.batch * w.q_len
-    bytes_call, out_bytes, flops_call = algorithmic_work(w, inputs["seq_lens"], turbo8)
+    bytes_call, out_bytes, flops_call = algorithmic_work(w, inputs["seq_lens"], kv)
     if block_size:                                      # the block table entries the call reads
         bytes_call += 4 * int(((inputs["seq_lens"] + w.q_len + block_size - 1) // block_size).sum())
     fields = dict(kv.split("=") for kv in plan.split())
@@ -316,8 +321,8 @@ def measure(w, steps, warm, launch="graph", force_splits=0, sets=None, block_siz
         call_ach, kern_ach = flops_call / step_s / 1e12, flops_call / (kernel_ms / 1e3) / 1e12
         peak, unit = MFMA_BF16_PEAK_TFS, "TFLOP/s"
     kname = {"fused_splitk": "stream_kernel", "prepared_tiles": "tile_kernel"}.get(route, "rows_f32_kernel")
-    if turbo8:
-        kname = "turbo8_kernel"
+    if kv != "native":
+        kname = "quant_kernel"
     res = {
         "steps": steps, "warmup": warm, "ms_per_step": ms / steps, "tokens_per_s": tokens_per_call / step_s,
         "effective_gbs": bytes_call / step_s / 1e9, "effective_tflops": flops_call / step_s / 1e12,
@@ -327,7 +332,7 @@ def measure(w, steps, warm, launch="graph", force_splits=0, sets=None, block_siz
         "kernel": kname, "kernel_us": kernel_ms * 1e3, "kernel_achieved": kern_ach,
         "kernel_frac": kern_ach / peak, "bytes_call": bytes_call, "bytes_kernel": bytes_kernel,
         "flops_call": flops_call, "tokens_per_call": tokens_per_call,
-        "cached_tokens": int(inputs["seq_lens"].sum()), "block_size": block_size, "kv": "turbo8" if turbo8 else w.dtype,
+        "cached_tokens": int(inputs["seq_lens"].sum()), "block_size": block_size, "kv": kv if kv != "native" else w.dtype,
     }
     del calls, base
     torch.cuda.synchronize()
@@ -461,8 +466,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="time only --workload (by default the other bf16 workloads follow as extra keys)")
     ap.add_argument("--sets", type=int, default=None, help="buffer sets to rotate over")
-    ap.add_argument("--kv", choices=["native", "turbo8"], default="native",
-                    help="cache storage: the activations' dtype, or Turbo8 (E4M3 codes + bf16 scales)")
+    ap.add_argument("--kv", choices=["native", "turbo8", "turbo4v"], default="native",
+                    help="cache storage: the activations' dtype, Turbo8 (E4M3 codes + bf16 scales) or bf16 K + "
+                         "Turbo4 V (4-bit Lloyd-Max indices + E4M3 scales)")
     ap.add_argument("--block-size", type=int, default=0,
                     help="lay the cache out in shuffled blocks of this many rows (paged; 0: contiguous)")
     ap.add_argument("--proj", choices=["qkv", "o"], default=None,
@@ -500,7 +506,7 @@ def main():
     steps = args.steps if args.steps is not None else steps
     warm = args.warmup if args.warmup is not None else warm
     inputs, r = measure(w, steps, warm, args.launch, args.force_splits, args.sets, args.block_size,
-                        args.kv == "turbo8")
+                        args.kv)
 
     traffic = traffic_from_profiles(w.name, r["route"]) if r["route"] in ROUTE_SOURCES else None
     roof = {"bound": r["bound"], "achieved": round(r["kernel_achieved"], 1), "peak": r["peak"],
@@ -551,16 +557,18 @@ def main():
             "unit": "GB/s", "call_achieved": round(x["call_achieved"], 1), "call_frac": round(x["call_frac"], 4),
             "kernel": x["kernel"], "kernel_us": round(x["kernel_us"], 3),
             "kernel_achieved": round(x["kernel_achieved"], 1), "kernel_frac": round(x["kernel_frac"], 4)}
-        # decode and the ragged batch on a Turbo8 cache (E4M3 codes, bf16 scale per 16)
-        for name in ("decode_4b", "ragged_4b"):
-            _, x = measure(WORKLOADS[name], *DEFAULT_STEPS[name], turbo8=True)
-            extras[f"{name}_turbo8"] = {
-                "tokens_per_s": round(x["tokens_per_s"], 1), "us_per_call": round(x["ms_per_step"] * 1e3, 3),
-                "steps": x["steps"], "warmup": x["warmup"], "plan": x["plan"], "kv": "turbo8", "bound": "hbm",
-                "unit": "GB/s", "algorithmic_bytes_per_call": x["bytes_call"],
-                "call_achieved": round(x["call_achieved"], 1), "call_frac": round(x["call_frac"], 4),
-                "kernel": x["kernel"], "kernel_us": round(x["kernel_us"], 3),
-                "kernel_achieved": round(x["kernel_achieved"], 1), "kernel_frac": round(x["kernel_frac"], 4)}
+        # decode and the ragged batch on the quantized caches: Turbo8 (E4M3 codes, bf16
+        # scale per 16) and bf16 K + Turbo4 V (4-bit indices, E4M3 scale per 16)
+        for kvq in ("turbo8", "turbo4v"):
+            for name in ("decode_4b", "ragged_4b"):
+                _, x = measure(WORKLOADS[name], *DEFAULT_STEPS[name], kv=kvq)
+                extras[f"{name}_{kvq}"] = {
+                    "tokens_per_s": round(x["tokens_per_s"], 1), "us_per_call": round(x["ms_per_step"] * 1e3, 3),
+                    "steps": x["steps"], "warmup": x["warmup"], "plan": x["plan"], "kv": kvq, "bound": "hbm",
+                    "unit": "GB/s", "algorithmic_bytes_per_call": x["bytes_call"],
+                    "call_achieved": round(x["call_achieved"], 1), "call_frac": round(x["call_frac"], 4),
+                    "kernel": x["kernel"], "kernel_us": round(x["kernel_us"], 3),
+                    "kernel_achieved": round(x["kernel_achieved"], 1), "kernel_frac": round(x["kernel_frac"], 4)}
         # the projections either side of the core, at the decode shape (one row)
         extras["qkv_proj_4b"] = measure_proj(WORKLOADS["decode_4b"], "qkv", 1000, 50)
         extras["o_proj_4b"] = measure_proj(WORKLOADS["decode_4b"], "o", 1000, 50)

@@ -16,7 +16,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsa.so"
 
 QSA_OK, QSA_ERR_INVALID, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE, QSA_ERR_DEVICE = 0, -1, -2, -3, -4
 QSA_BF16, QSA_F32 = 0, 1
-QSA_KV_NATIVE, QSA_KV_TURBO8 = 0, 1
+QSA_KV_NATIVE, QSA_KV_TURBO8, QSA_KV_BF16K_TURBO4V = 0, 1, 2
 _DT = {torch.bfloat16: QSA_BF16, torch.float32: QSA_F32}
 
 EXPORTS = ("qsa_workspace_size", "qsa_append_kv", "qsa_gated_attention", "qsa_gated_attention_noalloc",
@@ -137,13 +137,14 @@ def make_kv(k_cache, v_cache, seq_offset, capacity=None, block_table=None, block
             k_scales=None, v_scales=None) -> KVCache:
     """Describe a token-major cache: k/v ``[rows, Hkv, D]``; contiguous with
     seq_offset int64 ``[B]``, or paged with block_table int32 ``[B, max_blocks]``.
-    With k_scales / v_scales ``[rows, Hkv, D/16]`` (bf16) the cache is Turbo8:
-    k/v then hold E4M3 codes (uint8)."""
+    With k_scales and v_scales ``[rows, Hkv, D/16]`` (bf16) the cache is Turbo8
+    (k/v hold E4M3 codes); with v_scales only (E4M3 bytes) it is bf16 K + Turbo4
+    V (k bf16 rows, v ``[rows, Hkv, D/2]`` 4-bit indices)."""
     max_blocks = 0 if block_table is None else int(block_table.shape[1])
-    turbo8 = k_scales is not None
+    kind = QSA_KV_NATIVE if v_scales is None else QSA_KV_TURBO8 if k_scales is not None else QSA_KV_BF16K_TURBO4V
     return KVCache(_ptr(k_cache), _ptr(v_cache), _ptr(seq_offset), _ptr(capacity),
                    int(k_cache.shape[0]), _ptr(block_table), int(block_size), max_blocks,
-                   QSA_KV_TURBO8 if turbo8 else QSA_KV_NATIVE, _ptr(k_scales), _ptr(v_scales))
+                   kind, _ptr(k_scales), _ptr(v_scales))
 
 
 def workspace_size(cfg: Cfg) -> int:

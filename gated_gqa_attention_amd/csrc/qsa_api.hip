@@ -4,6 +4,7 @@
 // error, as the pages' engines do at admission (mlxd PR #99, Decision R1 and
 // the first reply: reject at load rather than approximate; Atlas
 // Qwen35Kernels::resolve: fail loudly).
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -206,13 +207,15 @@ int check_kv(const qsa_kv_cache *kv) {
   if (!kv->k || !kv->v) return fail(QSA_ERR_INVALID, "kv->k and kv->v are required");
   if (kv->num_rows < 1) return fail(QSA_ERR_INVALID, "kv->num_rows must be >= 1");
   if (kv->k == kv->v) return fail(QSA_ERR_INVALID, "kv->k and kv->v must be different buffers");
-  if (kv->kv_dtype != QSA_KV_NATIVE && kv->kv_dtype != QSA_KV_TURBO8)
-    return fail(QSA_ERR_UNSUPPORTED, "kv->kv_dtype %d not supported (QSA_KV_NATIVE | QSA_KV_TURBO8)", kv->kv_dtype);
-  if (kv->kv_dtype == QSA_KV_TURBO8) {
-    if (!kv->k_scales || !kv->v_scales)
-      return fail(QSA_ERR_INVALID, "a Turbo8 cache needs kv->k_scales and kv->v_scales");
-    if (kv->block_table) return fail(QSA_ERR_UNSUPPORTED, "Turbo8 caches are taken in the contiguous layout only");
-  }
+  if (kv->kv_dtype != QSA_KV_NATIVE && kv->kv_dtype != QSA_KV_TURBO8 && kv->kv_dtype != QSA_KV_BF16K_TURBO4V)
+    return fail(QSA_ERR_UNSUPPORTED,
+                "kv->kv_dtype %d not supported (QSA_KV_NATIVE | QSA_KV_TURBO8 | QSA_KV_BF16K_TURBO4V)", kv->kv_dtype);
+  if (kv->kv_dtype == QSA_KV_TURBO8 && (!kv->k_scales || !kv->v_scales))
+    return fail(QSA_ERR_INVALID, "a Turbo8 cache needs kv->k_scales and kv->v_scales");
+  if (kv->kv_dtype == QSA_KV_BF16K_TURBO4V && !kv->v_scales)
+    return fail(QSA_ERR_INVALID, "a bf16-K / Turbo4-V cache needs kv->v_scales");
+  if (kv->kv_dtype != QSA_KV_NATIVE && kv->block_table)
+    return fail(QSA_ERR_UNSUPPORTED, "quantized caches are taken in the contiguous layout only");
   if (!kv->block_table) {
     if (!kv->seq_offset) return fail(QSA_ERR_INVALID, "kv->seq_offset is required for a contiguous cache");
     return QSA_OK;
@@ -225,23 +228,70 @@ int check_kv(const qsa_kv_cache *kv) {
   return QSA_OK;
 }
 
-// Turbo8 caches: bf16 activations, and the short-query route's whole-lane
-// rotation (the quantizing append shares its key preparation).
-int check_turbo8(const qsa_cfg *c, const Plan &pl) {
-  if (c->dtype != QSA_BF16) return fail(QSA_ERR_UNSUPPORTED, "Turbo8 caches take bf16 activations only");
+// Quantized caches: bf16 activations, and the short-query route's whole-lane
+// rotation (the quantizing append shares its key preparation); bf16 K +
+// Turbo4 V at head_dim 256.
+int check_quant(const qsa_cfg *c, const Plan &pl, int32_t kv_dtype) {
+  const char *name = kv_dtype == QSA_KV_TURBO8 ? "Turbo8" : "bf16-K / Turbo4-V";
+  if (c->dtype != QSA_BF16) return fail(QSA_ERR_UNSUPPORTED, "%s caches take bf16 activations only", name);
+  if (kv_dtype == QSA_KV_BF16K_TURBO4V && c->head_dim != 256)
+    return fail(QSA_ERR_UNSUPPORTED, "bf16-K / Turbo4-V caches take head_dim 256 only (head_dim %d)", c->head_dim);
   if (pl.route != kRouteFused)
     return fail(QSA_ERR_UNSUPPORTED,
-                "Turbo8 caches are taken on the short-query route only (q_len <= 16, q_len * G <= 48, "
-                "rotary_dim / 2 a multiple of head_dim / 16); this call plans route %s", route_name(pl.route));
+                "%s caches are taken on the short-query route only (q_len <= 16, q_len * G <= 48, "
+                "rotary_dim / 2 a multiple of head_dim / 16); this call plans route %s", name, route_name(pl.route));
   return QSA_OK;
 }
 
-qsa::Turbo8Cache turbo8_of(const qsa_kv_cache *kv) {
-  qsa::Turbo8Cache c;
-  c.kq = (uint8_t *)kv->k;
-  c.vq = (uint8_t *)kv->v;
-  c.ks = (qsa::bf16_t *)kv->k_scales;
-  c.vs = (qsa::bf16_t *)kv->v_scales;
+// The 16-level Lloyd-Max quantizer of the standard normal distribution:
+// Lloyd's iteration from evenly spread levels, each level moved to the mean of
+// the normal over its cell (cells split at the midpoints between levels),
+// until no level moves.  Computed once, in double; the kernels get fp32
+// levels and fp32 midpoints.
+struct Turbo4Codebook {
+  float level[16], threshold[15];
+  Turbo4Codebook() {
+    const double inv_sqrt_2pi = 0.3989422804014327, r2 = 1.4142135623730951;
+    auto density = [&](double x) { return std::isinf(x) ? 0.0 : inv_sqrt_2pi * std::exp(-0.5 * x * x); };
+    auto upper_tail = [&](double x) { return 0.5 * std::erfc(x / r2); };   // P(X > x)
+    double c[16];
+    for (int i = 0; i < 16; ++i) c[i] = (i - 7.5) * 0.4;
+    for (int round = 0; round < 200000; ++round) {
+      double edges[17];
+      edges[0] = -INFINITY;
+      edges[16] = INFINITY;
+      for (int i = 1; i < 16; ++i) edges[i] = 0.5 * (c[i - 1] + c[i]);
+      double moved = 0.0;
+      for (int i = 0; i < 16; ++i) {
+        const double a = edges[i], b = edges[i + 1];
+        // mass of the cell from the tail on its own side (no cancellation of two values near 1)
+        const double mass = b <= 0.0 ? upper_tail(-b) - upper_tail(-a) : upper_tail(a) - upper_tail(b);
+        const double mean = (density(a) - density(b)) / mass;
+        moved = std::max(moved, std::fabs(mean - c[i]));
+        c[i] = mean;
+      }
+      if (moved < 1e-16) break;
+    }
+    for (int i = 0; i < 8; ++i) {                       // exactly symmetric
+      const double m = 0.5 * (c[15 - i] - c[i]);
+      c[i] = -m;
+      c[15 - i] = m;
+    }
+    for (int i = 0; i < 16; ++i) level[i] = (float)c[i];
+    for (int i = 0; i < 15; ++i) threshold[i] = (float)(0.5 * (c[i] + c[i + 1]));
+  }
+};
+
+qsa::QuantCache quant_of(const qsa_kv_cache *kv) {
+  static const Turbo4Codebook cb;
+  qsa::QuantCache c;
+  c.fmt = kv->kv_dtype == QSA_KV_TURBO8 ? 0 : 1;
+  c.k = kv->k;
+  c.ks = kv->k_scales;
+  c.v = kv->v;
+  c.vs = kv->v_scales;
+  for (int i = 0; i < 16; ++i) c.cb[i] = cb.level[i];
+  for (int i = 0; i < 15; ++i) c.thr[i] = cb.threshold[i];
   return c;
 }
 
@@ -308,9 +358,9 @@ int qsa_append_kv(const void *k_new, const void *v_new, const qsa_kv_cache *kv, 
   p.v_new = v_new;
   p.err = cfg->workspace ? (int32_t *)cfg->workspace : nullptr;
   hipError_t e;
-  if (kv->kv_dtype == QSA_KV_TURBO8) {
-    if ((rc = check_turbo8(cfg, pl)) != QSA_OK) return rc;
-    e = qsa::launch_turbo8_append(p, turbo8_of(kv), (hipStream_t)cfg->stream);
+  if (kv->kv_dtype != QSA_KV_NATIVE) {
+    if ((rc = check_quant(cfg, pl, kv->kv_dtype)) != QSA_OK) return rc;
+    e = qsa::launch_quant_append(p, quant_of(kv), (hipStream_t)cfg->stream);
     if (e != hipSuccess) return fail(QSA_ERR_DEVICE, "append launch failed: %s", hipGetErrorString(e));
     return QSA_OK;
   }
@@ -339,18 +389,23 @@ int gated_attention_in(const void *q_gate, const void *k_new, const void *v_new,
   const size_t es = cfg->dtype == QSA_BF16 ? 2 : 4;
   const size_t nrow = (size_t)cfg->batch * cfg->q_len;
   const size_t out_bytes = nrow * cfg->num_q_heads * cfg->head_dim * es;
-  const size_t kv_bytes = (size_t)kv->num_rows * cfg->num_kv_heads * cfg->head_dim *
-                          (kv->kv_dtype == QSA_KV_TURBO8 ? 1 : es);   // Turbo8: one byte per element
-  const size_t sc_bytes = kv->kv_dtype == QSA_KV_TURBO8 ? kv_bytes / 8 : 0;   // bf16 per 16 elements
+  // bytes of each cache tensor: elements times bytes per element (Turbo8 codes 1;
+  // Turbo4 indices 1/2), scales per 16 elements (Turbo8 bf16 2, Turbo4 E4M3 1)
+  const size_t elems = (size_t)kv->num_rows * cfg->num_kv_heads * cfg->head_dim;
+  const int32_t kd = kv->kv_dtype;
+  const size_t k_bytes = kd == QSA_KV_TURBO8 ? elems : elems * (kd == QSA_KV_BF16K_TURBO4V ? 2 : es);
+  const size_t v_bytes = kd == QSA_KV_TURBO8 ? elems : kd == QSA_KV_BF16K_TURBO4V ? elems / 2 : elems * es;
+  const size_t ks_bytes = kd == QSA_KV_TURBO8 ? elems / 8 : 0;
+  const size_t vs_bytes = kd == QSA_KV_TURBO8 ? elems / 8 : kd == QSA_KV_BF16K_TURBO4V ? elems / 16 : 0;
   const size_t new_bytes = nrow * cfg->num_kv_heads * cfg->head_dim * es;
   if (overlaps(out, out_bytes, q_gate, 2 * out_bytes) || overlaps(out, out_bytes, k_new, new_bytes) ||
-      overlaps(out, out_bytes, v_new, new_bytes) || overlaps(out, out_bytes, kv->k, kv_bytes) ||
-      overlaps(out, out_bytes, kv->v, kv_bytes) || overlaps(out, out_bytes, kv->k_scales, sc_bytes) ||
-      overlaps(out, out_bytes, kv->v_scales, sc_bytes))
+      overlaps(out, out_bytes, v_new, new_bytes) || overlaps(out, out_bytes, kv->k, k_bytes) ||
+      overlaps(out, out_bytes, kv->v, v_bytes) || overlaps(out, out_bytes, kv->k_scales, ks_bytes) ||
+      overlaps(out, out_bytes, kv->v_scales, vs_bytes))
     return fail(QSA_ERR_INVALID, "out must not alias q_gate, k_new, v_new or the cache");
   Plan pl;
   if ((rc = make_plan(cfg, &pl)) != QSA_OK) return rc;
-  if (kv->kv_dtype == QSA_KV_TURBO8 && (rc = check_turbo8(cfg, pl)) != QSA_OK) return rc;
+  if (kv->kv_dtype != QSA_KV_NATIVE && (rc = check_quant(cfg, pl, kv->kv_dtype)) != QSA_OK) return rc;
   if (kv->block_table) {
     // Paged caches on the short-query route only.  A workgroup holds the block
     // ids of its key chunk (at most 128): with fixed chunks the last one has
@@ -395,8 +450,8 @@ int gated_attention_in(const void *q_gate, const void *k_new, const void *v_new,
       if (e == hipSuccess) e = qsa::launch_rows_f32(p, s, tm);
       break;
     case kRouteFused:
-      if (kv->kv_dtype == QSA_KV_TURBO8) {
-        e = qsa::launch_turbo8_bf16(p, turbo8_of(kv), s, tm);
+      if (kv->kv_dtype != QSA_KV_NATIVE) {                // V in the WHT basis: the merge rotates back
+        e = qsa::launch_quant_bf16(p, quant_of(kv), s, tm);
         if (e == hipSuccess && pl.chunks > 1) e = qsa::launch_combine_wht_bf16(p, s);
       } else {
         e = qsa::launch_stream_bf16(p, s, tm);

@@ -392,6 +392,57 @@ struct Turbo8Row {
   }
 };
 
+// Turbo4 groups of 16 consecutive elements (the V side of Atlas
+// MetalKvDtype::Bf16KTurbo4V): 4-bit indices into a 16-level codebook and one
+// E4M3 scale per group.  A group's indices are the levels nearest to x / sigma
+// (sigma the group's RMS; the count of decision thresholds below it, so the
+// lower level on a tie) and its scale is sqrt(sum x^2 / sum level^2) in E4M3
+// (round to nearest even, after a clamp at 448), so that the decoded group
+// keeps the group's L2 norm; a zero group has scale 0 and index 0.  Indices
+// pack two per byte, element 2i in the low nibble.  cb: the 16 levels in LDS;
+// thr: the 15 thresholds.  fp32 throughout.  A group spans 16 / E lanes of a
+// 16-lane row.
+template <int D>
+struct Turbo4Row {
+  static constexpr int E = D / 16;
+  static constexpr int LPG = 16 / E < 1 ? 1 : 16 / E;   // lanes per group
+  static constexpr int CW = (E / 2 + 3) / 4;            // dwords of packed indices per lane
+  uint32_t codes[CW];
+  uint32_t scale;                                       // E4M3 bits (byte 0)
+  __device__ __forceinline__ void quantize(const float (&x)[E], const float *cb, const float (&thr)[15]) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < E; ++j) ss = fmaf(x[j], x[j], ss);
+#pragma unroll
+    for (int lh = 1; lh < LPG; lh <<= 1) ss += __shfl_xor(ss, lh, kWave);
+#pragma unroll
+    for (int w = 0; w < CW; ++w) codes[w] = 0;
+    scale = 0;
+    const float sigma = sqrtf(ss / 16.f);
+    float cc = 0.f;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const float u = ss > 0.f ? x[j] / sigma : 0.f;
+      int idx = 0;
+#pragma unroll
+      for (int t = 0; t < 15; ++t) idx += thr[t] < u ? 1 : 0;
+      if (ss == 0.f) idx = 0;
+      const float c = cb[idx];
+      cc = fmaf(c, c, cc);
+      codes[j / 8] |= (uint32_t)idx << (4 * (j % 8));
+    }
+#pragma unroll
+    for (int lh = 1; lh < LPG; lh <<= 1) cc += __shfl_xor(cc, lh, kWave);
+    if (ss > 0.f) scale = pk_fp8(fminf(sqrtf(ss / cc), 448.f), 0.f, 0u, false) & 0xffu;
+  }
+  // level x scale in fp32
+  __device__ __forceinline__ void dequantize(float (&x)[E], const float *cb) const {
+    const float s = unpk_fp8(scale, false)[0];
+#pragma unroll
+    for (int j = 0; j < E; ++j) x[j] = s * cb[(codes[j / 8] >> (4 * (j % 8))) & 15u];
+  }
+};
+
 // Turbo8 codes to fp16 MFMA operands, code x scale rounded once to nearest
 // even (exact in fp32: 4 x 8 significant bits).  gfx950's scaled conversion
 // takes only the exponent of its fp32 scale, so it gives code x 2^e exactly

@@ -196,13 +196,17 @@ hipError_t launch_tile_bf16(const Params &p, hipStream_t s, const Timing &tm);
 hipError_t launch_stream_bf16(const Params &p, hipStream_t s, const Timing &tm);
 hipError_t launch_combine_bf16(const Params &p, hipStream_t s, bool per_row);   // per_row: the tile route's merge
 hipError_t launch_combine_wht_bf16(const Params &p, hipStream_t s);              // partials in the WHT basis
-// A Turbo8 cache: codes [rows][Hkv][D] bytes and bf16 scales [rows][Hkv][D/16], for K and V.
-struct Turbo8Cache {
-  uint8_t *kq, *vq;
-  bf16_t *ks, *vs;
+// A quantized KV cache.  fmt 0, Turbo8: K and V codes [rows][Hkv][D] (E4M3)
+// with bf16 scales [rows][Hkv][D/16].  fmt 1, bf16 K + Turbo4 V: K bf16
+// [rows][Hkv][D] (no scales), V indices [rows][Hkv][D/2] (two per byte) with
+// E4M3 scales [rows][Hkv][D/16]; cb / thr the Turbo4 levels and thresholds.
+struct QuantCache {
+  int fmt;
+  void *k, *ks, *v, *vs;
+  float cb[16], thr[15];
 };
-hipError_t launch_turbo8_bf16(const Params &p, const Turbo8Cache &c, hipStream_t s, const Timing &tm);
-hipError_t launch_turbo8_append(const Params &p, const Turbo8Cache &c, hipStream_t s);
+hipError_t launch_quant_bf16(const Params &p, const QuantCache &c, hipStream_t s, const Timing &tm);
+hipError_t launch_quant_append(const Params &p, const QuantCache &c, hipStream_t s);
 hipError_t launch_linear_bf16(const void *x, const void *w, int M, int N, int K, void *y0, int n0_end, int ld0,
                               void *y1, int n1_end, int ld1, void *y2, int ld2, hipStream_t s);
 constexpr int kMaxLinearRows = 64;    // rows (tokens) a projection call takes

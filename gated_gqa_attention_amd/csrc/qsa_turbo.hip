@@ -49,14 +49,34 @@ __device__ __forceinline__ void turbo8_new_row(float (&x)[D / 16], bool is_k, co
 
 }  // namespace
 
+// Formats of a quantized cache, and what one launch reads of it.
+constexpr int kT8 = 0;                                   // Turbo8: K and V as E4M3 codes + bf16 scales
+constexpr int kB4 = 1;                                   // bf16 K + Turbo4 V (indices + E4M3 scales)
+
+// The tensors of a quantized cache (read; the fused append writes the new
+// rows through the same pointers) and the Turbo4 codebook.
+struct QArgs {
+  const void *k, *ks, *v, *vs;                           // K data and scales (none for bf16 K), V data and scales
+  float cb[16];                                          // Turbo4 levels, ascending
+  float thr[15];                                         // their decision thresholds (midpoints)
+};
+
 // ------------------------------------------------------------------ append
-template <int D>
-__global__ __launch_bounds__(kThreads) void turbo8_append_kernel(Params p, const bf16_t *__restrict__ k_new,
-                                                                 const bf16_t *__restrict__ v_new,
-                                                                 uint8_t *__restrict__ kq, bf16_t *__restrict__ ks,
-                                                                 uint8_t *__restrict__ vq, bf16_t *__restrict__ vs) {
-  constexpr int E = D / 16, ROWS = kThreads / 16;
+// One workgroup per new row (b, l); 16 lanes per head row.  Turbo8: K norm,
+// rotation, WHT, group quantizer; V WHT, quantizer.  bf16 K + Turbo4 V: K norm
+// and rotation rounded to bf16 (the bf16 cache's row); V WHT, Turbo4.  Stored
+// at row seq_lens[b] + l.
+template <int D, int FMT>
+__global__ __launch_bounds__(kThreads) void quant_append_kernel(Params p, QArgs a) {
+  constexpr int E = D / 16, ROWS = kThreads / 16, NG = D / 16;
   __shared__ __attribute__((aligned(16))) float2 cs[kMaxPairs];
+  __shared__ float cbs[16];
+  if constexpr (FMT == kB4) {
+    if (threadIdx.x < 16) cbs[threadIdx.x] = a.cb[threadIdx.x];
+  }
+  float thr[15];
+#pragma unroll
+  for (int i = 0; i < 15; ++i) thr[i] = a.thr[i];
   const int c16 = threadIdx.x & 15, hr = threadIdx.x / 16;
   const int64_t bl = blockIdx.x;
   const int b = (int)(bl / p.L), l = (int)(bl % p.L);
@@ -80,6 +100,7 @@ __global__ __launch_bounds__(kThreads) void turbo8_append_kernel(Params p, const
     wr.load((const bf16_t *)p.wk + E * c16);
     wr.to_float(w);
   }
+  const bf16_t *const k_new = (const bf16_t *)p.k_new, *const v_new = (const bf16_t *)p.v_new;
   const int njobs = 2 * p.Hkv;                          // K heads, then V heads
   for (int j0 = 0; j0 < njobs; j0 += ROWS) {
     const int job = j0 + hr;
@@ -91,24 +112,50 @@ __global__ __launch_bounds__(kThreads) void turbo8_append_kernel(Params p, const
     raw.load((is_k ? k_new : v_new) + (bl * p.Hkv + head) * D + E * c16);
     float x[E];
     raw.to_float(x);
-    Turbo8Row<D> q;
-    turbo8_new_row<D>(x, is_k, w, valid, p.eps, p.r, cs, q);
-    if (!valid || !ok) continue;
     const int64_t row = (off + n + l) * p.Hkv + head;
-    uint8_t *codes = (is_k ? kq : vq) + row * D + E * c16;
+    if constexpr (FMT == kT8) {
+      Turbo8Row<D> q;
+      turbo8_new_row<D>(x, is_k, w, valid, p.eps, p.r, cs, q);
+      if (!valid || !ok) continue;
+      uint8_t *codes = (uint8_t *)(is_k ? a.k : a.v) + row * D + E * c16;
 #pragma unroll
-    for (int c = 0; c < Turbo8Row<D>::CW; ++c) {
-      if constexpr (E >= 4) *(uint32_t *)(codes + 4 * c) = q.codes[c];
+      for (int c = 0; c < Turbo8Row<D>::CW; ++c) *(uint32_t *)(codes + 4 * c) = q.codes[c];
+      if (c16 % Turbo8Row<D>::LPG == 0) ((bf16_t *)(is_k ? a.ks : a.vs))[row * NG + E * c16 / 16] = q.scale;
+    } else {
+      Turbo4Row<D> q4;
+      if (is_k) {
+        norm_rope<D>(x, w, valid, p.eps, p.r, cs);
+      } else {
+        row_wht<D>(x);
+        q4.quantize(x, cbs, thr);
+      }
+      if (!valid || !ok) continue;
+      if (is_k) {
+#pragma unroll
+        for (int j = 0; j < E; ++j) ((bf16_t *)a.k)[row * D + E * c16 + j] = (bf16_t)x[j];
+      } else {
+        uint8_t *const cs4 = (uint8_t *)a.v + row * (D / 2) + E * c16 / 2;
+#pragma unroll
+        for (int c = 0; c < Turbo4Row<D>::CW; ++c) {
+          if constexpr (E >= 8)
+            *(uint32_t *)(cs4 + 4 * c) = q4.codes[c];
+          else
+            *(uint16_t *)cs4 = (uint16_t)q4.codes[0];
+        }
+        if (c16 % Turbo4Row<D>::LPG == 0) ((uint8_t *)a.vs)[row * NG + E * c16 / 16] = (uint8_t)q4.scale;
+      }
     }
-    if (c16 % Turbo8Row<D>::LPG == 0) (is_k ? ks : vs)[row * (D / 16) + E * c16 / 16] = q.scale;
   }
 }
 
 // ------------------------------------------------------------------ attention
-// Stage layout of the raw ring (one slot per 64-key stage): K codes [64][D]
-// with each row's 16-byte units XOR-swizzled by the key (conflict-free reads
-// of one column by 16 keys), K scales [64][D/16] bf16, V codes [64][D], V
-// scales [64][D/16], all copied straight from HBM by global_load_lds.
+// Stage layout of the raw ring (one slot per 64-key stage), copied straight
+// from HBM by global_load_lds.  Turbo8: K codes [64][D] with each row's
+// 16-byte units XOR-swizzled by the key (conflict-free reads of one column by
+// 16 keys), K scales [64][D/16] bf16, V codes [64][D], V scales [64][D/16].
+// Copy instruction q of a stage (64 lanes) has a kind: 0 K codes, 1 V codes,
+// 2 K scales, 3 V scales; kind k copies UPK(k) units of UB(k) bytes per key,
+// unit u of key r at LDS unit u ^ (r & SWZ(k)).
 template <int D>
 struct T8Geo {
   static constexpr int SK = Geo<D>::SK;
@@ -117,7 +164,7 @@ struct T8Geo {
   static constexpr int CODES = SK * D, SCL = SK * D / 8;
   static constexpr int KC = 0, KS = CODES, VC = CODES + SCL, VS = 2 * CODES + SCL;
   static constexpr int SLOT = 2 * (CODES + SCL);
-  static constexpr int NC = 2 * UPR;                    // 16-byte code copy instructions per stage (K, V), 64 lanes each
+  static constexpr int NC = 2 * UPR;                    // 16-byte code copy instructions per stage (K, V)
   // scale copies: 16-byte units when a key's scales fill whole units and the
   // counts stay even (head_dim 256: two units per key), dwords otherwise
   static constexpr bool SX4 = D == 256;
@@ -129,24 +176,56 @@ struct T8Geo {
   static constexpr int VT = SK * Geo<D>::RB;            // decoded fp16 V tile
   static_assert(NQ % 4 == 0 && 2 * (NS - 1) * U <= 63, "copy counts");
   static_assert(UPR % 2 == 0 && NSC % 2 == 0, "a copy wave's instructions q = w + 2 j have the kind of 2 j");
-  // instruction q copies: kind 0 K codes, 1 V codes, 2 K scales, 3 V scales
   static constexpr int kind(int q) { return q < UPR ? 0 : q < 2 * UPR ? 1 : q < 2 * UPR + NSC ? 2 : 3; }
   static constexpr int first(int k) { return k == 0 ? 0 : k == 1 ? UPR : k == 2 ? 2 * UPR : 2 * UPR + NSC; }
   static constexpr int region(int k) { return k == 0 ? KC : k == 1 ? VC : k == 2 ? KS : VS; }
-  static constexpr int ibytes(int k) { return k < 2 || SX4 ? 16 * kWave : 4 * kWave; }   // LDS bytes per instruction
-  // This lane's source offset for instruction q, in bytes from the stage's
-  // first key row (head kvh) of the tensor it copies; keys past `last` repeat it.
-  // rowc / rows_: bytes between consecutive keys of one head (codes / scales).
-  __device__ static __forceinline__ unsigned lane_off(int q, int lane, int last, unsigned rowc, unsigned rows_) {
-    const int k = kind(q), i = q - first(k), s = kWave * i + lane;
-    if (k < 2) {
-      const int key = s / UPR, pos = s % UPR, gu = k == 0 ? pos ^ (key & SWC) : pos;
-      return (unsigned)min(key, last) * rowc + 16u * (unsigned)gu;
-    }
-    const int key = s / SPK, unit = s % SPK;
-    return (unsigned)min(key, last) * rows_ + (SX4 ? 16u : 4u) * (unsigned)unit;
-  }
+  static constexpr int UPK(int k) { return k < 2 ? UPR : SPK; }
+  static constexpr int UB(int k) { return k < 2 || SX4 ? 16 : 4; }
+  static constexpr int SWZ(int k) { return k == 0 ? SWC : 0; }
+  static constexpr int ROWHEAD(int k) { return k < 2 ? D : D / 8; }   // bytes per (row, head) in HBM
+  __device__ static const void *tensor(const QArgs &a, int k) { return k == 0 ? a.k : k == 1 ? a.v : k == 2 ? a.ks : a.vs; }
 };
+
+// bf16 K + Turbo4 V (head_dim 256): K bf16 [64][D] swizzled like the bf16
+// kernel's K stages (the slot's K region is the stage's K tile), V indices
+// [64][D/2], V scales [64][D/16] (E4M3 bytes, copied as dwords).  Kinds: 0 K,
+// 1 V indices, 2 V scales.
+template <int D>
+struct B4Geo {
+  static_assert(D == 256, "the bf16-K / Turbo4-V copies split evenly over four wavefronts at head_dim 256 only");
+  static constexpr int SK = Geo<D>::SK;
+  static constexpr int KB = SK * 2 * D, CB = SK * D / 2, SB = SK * D / 16;
+  static constexpr int KC = 0, VC = KB, VS = KB + CB;
+  static constexpr int SLOT = KB + CB + SB;
+  static constexpr int NK = SK * (D / 8) / kWave, NV = SK * (D / 32) / kWave, NVS = SK * (D / 64) / kWave;
+  static constexpr int NQ = NK + NV + NVS;
+  static constexpr int U = NQ / 4;
+  static constexpr int NS = 2;
+  static constexpr int VT = SK * Geo<D>::RB;            // decoded bf16 V tile
+  static_assert(NQ % 4 == 0 && 2 * (NS - 1) * U <= 63, "copy counts");
+  static_assert(NK % 2 == 0 && NV % 2 == 0, "a copy wave's instructions q = w + 2 j have the kind of 2 j");
+  static constexpr int kind(int q) { return q < NK ? 0 : q < NK + NV ? 1 : 2; }
+  static constexpr int first(int k) { return k == 0 ? 0 : k == 1 ? NK : NK + NV; }
+  static constexpr int region(int k) { return k == 0 ? KC : k == 1 ? VC : VS; }
+  static constexpr int UPK(int k) { return k == 0 ? D / 8 : k == 1 ? D / 32 : D / 64; }
+  static constexpr int UB(int k) { return k < 2 ? 16 : 4; }
+  static constexpr int SWZ(int k) { return k == 0 ? Geo<D>::SW : 0; }
+  static constexpr int ROWHEAD(int k) { return k == 0 ? 2 * D : k == 1 ? D / 2 : D / 16; }
+  __device__ static const void *tensor(const QArgs &a, int k) { return k == 0 ? a.k : k == 1 ? a.v : a.vs; }
+};
+
+template <int D, int FMT>
+using QGeo = typename std::conditional<FMT == kT8, T8Geo<D>, B4Geo<D>>::type;
+
+// This lane's source offset for copy instruction q, in bytes from the stage's
+// first key row (head kvh) of the tensor it copies; keys past `last` repeat it.
+// rowb: bytes between consecutive keys of one head in that tensor.
+template <class QG>
+__device__ __forceinline__ unsigned copy_lane_off(int q, int lane, int last, unsigned rowb) {
+  const int k = QG::kind(q), i = q - QG::first(k), s = kWave * i + lane;
+  const int key = s / QG::UPK(k), pos = s % QG::UPK(k), gu = pos ^ (key & QG::SWZ(k));
+  return (unsigned)min(key, last) * rowb + (unsigned)QG::UB(k) * (unsigned)gu;
+}
 
 // The score product's K operand straight from a raw stage: this lane's key
 // row (16 wave + m16) and k-step ks hold 8 codes of scale group 2 ks + g4/2.
@@ -187,27 +266,38 @@ struct T8K {
 // At the end a chunk that is the whole sequence rotates its rows back
 // through LDS and gates them; other chunks store their partials as they are,
 // in the WHT basis, and the merge rotates the merged rows.
-template <int D, int RTM>
-__global__ __launch_bounds__(kThreads) void turbo8_kernel(Params p, const uint8_t *__restrict__ kq,
-                                                          const bf16_t *__restrict__ ks,
-                                                          const uint8_t *__restrict__ vq,
-                                                          const bf16_t *__restrict__ vs, uint8_t *kq_w, bf16_t *ks_w,
-                                                          uint8_t *vq_w, bf16_t *vs_w) {
+template <int D, int RTM, int FMT>
+__global__ __launch_bounds__(kThreads) void quant_kernel(Params p, QArgs a) {
   using G = Geo<D>;
-  using T8 = T8Geo<D>;
-  constexpr int E = G::E, KST = G::KST, RB = G::RB, DBW = D / 64, SK = G::SK, NS = T8::NS, U = T8::U;
-  constexpr int UPR = T8::UPR, NG = D / 16, SLOT = T8::SLOT;
+  using QG = QGeo<D, FMT>;
+  using OT = typename std::conditional<FMT == kT8, f16_t, bf16_t>::type;   // MFMA operand type
+  using OT8 = typename Op16<OT>::x8;
+  constexpr int E = G::E, KST = G::KST, RB = G::RB, DBW = D / 64, SK = G::SK, NS = QG::NS, U = QG::U;
+  constexpr int NG = D / 16, SLOT = QG::SLOT;
   constexpr int QBYTES = 16 * RTM * RB;
   constexpr int TABN = kMaxFusedTable;
   constexpr int PREP = QBYTES + 2 * TABN * 8;           // query rows, then one (cos, sin) table per prep wave
-  constexpr int WORK = T8::VT + Xch::BYTES;             // V tile, then the stage exchange
+  constexpr int WORK = QG::VT + Xch::BYTES;             // V tile, then the stage exchange
   constexpr int ARENA = PREP > WORK ? PREP : WORK;
   constexpr int NPASS = 2 * RTM;
   constexpr int TJ = TABN / kWave;
   static_assert(16 * RTM * D * 4 + 16 * RTM * 4 <= NS * SLOT, "the epilogue tile fits in the ring");
   __shared__ __attribute__((aligned(16))) unsigned char ring[NS * SLOT];
   __shared__ __attribute__((aligned(16))) unsigned char arena[ARENA];
-  unsigned char *const vtile = arena, *const xch = arena + T8::VT;
+  unsigned char *const vtile = arena, *const xch = arena + QG::VT;
+  // The Turbo4 levels, for per-lane lookups: copy 0 (written by wavefront 0)
+  // for the stages, which come after workgroup barriers; copies 1 and 2 each
+  // written and read by one prep wavefront alone, for the new rows it handles
+  // before the first barrier.
+  __shared__ float cbs_all[3][16];
+  if constexpr (FMT == kB4) {
+    const int wv = (int)threadIdx.x / kWave, ln = (int)threadIdx.x % kWave;
+    if ((wv == 0 || wv >= 2) && ln < 16) cbs_all[wv == 0 ? 0 : wv - 1][ln] = a.cb[ln];
+  }
+  const float *const cbs = cbs_all[0];
+  float thr[15];
+#pragma unroll
+  for (int i = 0; i < 15; ++i) thr[i] = a.thr[i];
 
   const int t = threadIdx.x, lane = t % kWave, g4 = lane >> 4, m16 = lane & 15, c16 = m16;
   const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
@@ -281,52 +371,58 @@ __global__ __launch_bounds__(kThreads) void turbo8_kernel(Params p, const uint8_
   // offsets are computed once; only a chunk's last, partial stage (keys past
   // the chunk repeat its last) computes them again.
   const unsigned ring_lds = (unsigned)(uintptr_t)(lds_void *)ring;
-  const unsigned rowc = (unsigned)(hkv * D), rows_ = (unsigned)(hkv * D / 8);
   const int w1 = wave & 1;
   unsigned offA[2 * U];
   static_for<2 * U>([&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    offA[j] = T8::lane_off(w1 + 2 * j, lane, SK - 1, rowc, rows_);
+    constexpr int j = decltype(jc)::value, k = QG::kind(2 * j);
+    offA[j] = copy_lane_off<QG>(w1 + 2 * j, lane, SK - 1, (unsigned)(hkv * QG::ROWHEAD(k)));
   });
   auto issue = [&](int st, auto jc) {
-    constexpr int j = decltype(jc)::value, k = T8::kind(2 * j);
+    constexpr int j = decltype(jc)::value, k = QG::kind(2 * j);
     const int last = (int)min<int64_t>(SK - 1, cend - 1 - (k0 + (int64_t)SK * st));
-    const unsigned lo = last == SK - 1 ? offA[j] : T8::lane_off(w1 + 2 * j, lane, last, rowc, rows_);
+    const unsigned lo =
+        last == SK - 1 ? offA[j] : copy_lane_off<QG>(w1 + 2 * j, lane, last, (unsigned)(hkv * QG::ROWHEAD(k)));
     const int64_t r0 = (off + k0 + (int64_t)SK * st) * hkv + kvh;
-    const unsigned dst = ring_lds + (st % NS) * SLOT + T8::region(k) + T8::ibytes(k) * (w1 + 2 * j - T8::first(k));
-    if constexpr (k == 0) dma16_sbase(kq + r0 * D, lo, dst);
-    if constexpr (k == 1) dma16_sbase(vq + r0 * D, lo, dst);
-    if constexpr (k >= 2) {
-      const unsigned char *const src = (const unsigned char *)(k == 2 ? ks : vs) + r0 * (D / 8);
-      if constexpr (T8::SX4)
-        dma16_sbase(src, lo, dst);
-      else
-        dma4_sbase(src, lo, dst);
-    }
+    const unsigned dst =
+        ring_lds + (st % NS) * SLOT + QG::region(k) + QG::UB(k) * kWave * (w1 + 2 * j - QG::first(k));
+    const unsigned char *const src = (const unsigned char *)QG::tensor(a, k) + r0 * QG::ROWHEAD(k);
+    if constexpr (QG::UB(k) == 16)
+      dma16_sbase(src, lo, dst);
+    else
+      dma4_sbase(src, lo, dst);
   };
 
   // ---- prep waves: the new rows' loads (the second round trip: their
   // addresses depend on n), before any copy of theirs
   const int nr = 4 * (pw ^ 1) + g4;                     // new rows 8 k + nr go to the other prep wave
+  // Turbo8: both rows as codes; bf16 K + Turbo4 V: K as a bf16 row (knraw), V as indices
   RawE<E> knraw[2], vnraw[2];
   Turbo8Row<D> qk[2], qv[2];
+  Turbo4Row<D> q4[2];
   if (!copier && tail) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int l = min(8 * k + nr, L - 1);
+      const int64_t crow = (off + n + l) * hkv + kvh;
       if (fuse_new) {
         const int64_t src = (((int64_t)b * L + l) * hkv + kvh) * D + E * c16;
         knraw[k].load((const bf16_t *)p.k_new + src);
         vnraw[k].load((const bf16_t *)p.v_new + src);
-      } else {
-        const int64_t crow = (off + n + l) * hkv + kvh;
+      } else if constexpr (FMT == kT8) {
 #pragma unroll
         for (int c = 0; c < Turbo8Row<D>::CW; ++c) {
-          qk[k].codes[c] = *(const uint32_t *)(kq + crow * D + E * c16 + 4 * c);
-          qv[k].codes[c] = *(const uint32_t *)(vq + crow * D + E * c16 + 4 * c);
+          qk[k].codes[c] = *(const uint32_t *)((const uint8_t *)a.k + crow * D + E * c16 + 4 * c);
+          qv[k].codes[c] = *(const uint32_t *)((const uint8_t *)a.v + crow * D + E * c16 + 4 * c);
         }
-        qk[k].scale = ks[crow * NG + E * c16 / 16];
-        qv[k].scale = vs[crow * NG + E * c16 / 16];
+        qk[k].scale = ((const bf16_t *)a.ks)[crow * NG + E * c16 / 16];
+        qv[k].scale = ((const bf16_t *)a.vs)[crow * NG + E * c16 / 16];
+      } else {
+        knraw[k].load((const bf16_t *)a.k + crow * D + E * c16);
+        const uint8_t *const cs4 = (const uint8_t *)a.v + crow * (D / 2) + E * c16 / 2;
+#pragma unroll
+        for (int c = 0; c < Turbo4Row<D>::CW; ++c)
+          q4[k].codes[c] = E >= 8 ? *(const uint32_t *)(cs4 + 4 * c) : (uint32_t)*(const uint16_t *)cs4;
+        q4[k].scale = ((const uint8_t *)a.vs)[crow * NG + E * c16 / 16];
       }
     }
   }
@@ -360,35 +456,67 @@ __global__ __launch_bounds__(kThreads) void turbo8_kernel(Params p, const uint8_
       if (8 * k + 4 * pw < R) {                         // the pass holds a row (wave-uniform)
         qraw[k].to_float(x);
         norm_rope<D>(x, wq, r < R, p.eps, p.r, tabw + (min(r, R - 1) / Gq) * half);
-        row_wht<D>(x);
+        if constexpr (FMT == kT8) row_wht<D>(x);        // the WHT(Q) bookend: K is rotated
       }
-      put_row<D, f16_t>(arena, RB, r, E * c16, x);
+      put_row<D, OT>(arena, RB, r, E * c16, x);
     }
     if (tail) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int l = 8 * k + nr;
         if (8 * k + 4 * (pw ^ 1) < L) {                 // the pass holds a new row (wave-uniform)
-          if (fuse_new) {
-            knraw[k].to_float(kx[k]);
-            vnraw[k].to_float(vx[k]);
-            turbo8_new_row<D>(kx[k], true, wk, l < L, p.eps, p.r, tabw + min(l, L - 1) * half, qk[k]);
-            turbo8_new_row<D>(vx[k], false, wk, l < L, p.eps, p.r, tabw + min(l, L - 1) * half, qv[k]);
-            if (l < L && cap_ok) {                      // the append: rows n + l
-              const int64_t crow = (off + n + l) * hkv + kvh;
+          const int64_t crow = (off + n + l) * hkv + kvh;
+          const bool store = fuse_new && l < L && cap_ok;   // the append: rows n + l
+          if constexpr (FMT == kT8) {
+            if (fuse_new) {
+              knraw[k].to_float(kx[k]);
+              vnraw[k].to_float(vx[k]);
+              turbo8_new_row<D>(kx[k], true, wk, l < L, p.eps, p.r, tabw + min(l, L - 1) * half, qk[k]);
+              turbo8_new_row<D>(vx[k], false, wk, l < L, p.eps, p.r, tabw + min(l, L - 1) * half, qv[k]);
+              if (store) {
 #pragma unroll
-              for (int c = 0; c < Turbo8Row<D>::CW; ++c) {
-                *(uint32_t *)(kq_w + crow * D + E * c16 + 4 * c) = qk[k].codes[c];
-                *(uint32_t *)(vq_w + crow * D + E * c16 + 4 * c) = qv[k].codes[c];
-              }
-              if (c16 % Turbo8Row<D>::LPG == 0) {
-                ks_w[crow * NG + E * c16 / 16] = qk[k].scale;
-                vs_w[crow * NG + E * c16 / 16] = qv[k].scale;
+                for (int c = 0; c < Turbo8Row<D>::CW; ++c) {
+                  *(uint32_t *)((uint8_t *)a.k + crow * D + E * c16 + 4 * c) = qk[k].codes[c];
+                  *(uint32_t *)((uint8_t *)a.v + crow * D + E * c16 + 4 * c) = qv[k].codes[c];
+                }
+                if (c16 % Turbo8Row<D>::LPG == 0) {
+                  ((bf16_t *)a.ks)[crow * NG + E * c16 / 16] = qk[k].scale;
+                  ((bf16_t *)a.vs)[crow * NG + E * c16 / 16] = qv[k].scale;
+                }
               }
             }
+            qk[k].dequantize(kx[k]);
+            qv[k].dequantize(vx[k]);
+          } else {
+            knraw[k].to_float(kx[k]);
+            if (fuse_new) {
+              // K: the bf16 cache's row (norm, rotation, rounded once); V: WHT, then Turbo4
+              norm_rope<D>(kx[k], wk, l < L, p.eps, p.r, tabw + min(l, L - 1) * half);
+              bf16_t kb[E];
+#pragma unroll
+              for (int j = 0; j < E; ++j) {
+                kb[j] = (bf16_t)kx[k][j];
+                kx[k][j] = (float)kb[j];
+              }
+              vnraw[k].to_float(vx[k]);
+              row_wht<D>(vx[k]);
+              q4[k].quantize(vx[k], cbs_all[1 + pw], thr);
+              if (store) {
+#pragma unroll
+                for (int j = 0; j < E; ++j) ((bf16_t *)a.k)[crow * D + E * c16 + j] = kb[j];
+                uint8_t *const cs4 = (uint8_t *)a.v + crow * (D / 2) + E * c16 / 2;
+#pragma unroll
+                for (int c = 0; c < Turbo4Row<D>::CW; ++c) {
+                  if constexpr (E >= 8)
+                    *(uint32_t *)(cs4 + 4 * c) = q4[k].codes[c];
+                  else
+                    *(uint16_t *)cs4 = (uint16_t)q4[k].codes[0];
+                }
+                if (c16 % Turbo4Row<D>::LPG == 0) ((uint8_t *)a.vs)[crow * NG + E * c16 / 16] = (uint8_t)q4[k].scale;
+              }
+            }
+            q4[k].dequantize(vx[k], cbs_all[1 + pw]);
           }
-          qk[k].dequantize(kx[k]);
-          qv[k].dequantize(vx[k]);
         }
         if (!(8 * k + 4 * (pw ^ 1) < L) || l >= L) {
 #pragma unroll
@@ -399,11 +527,11 @@ __global__ __launch_bounds__(kThreads) void turbo8_kernel(Params p, const uint8_
   }
   lds_barrier();                                        // query operands ready
 
-  f16x8 qf[RTM][KST];
+  OT8 qf[RTM][KST];
 #pragma unroll
   for (int rt = 0; rt < RTM; ++rt)
 #pragma unroll
-    for (int k = 0; k < KST; ++k) qf[rt][k] = *(const f16x8 *)(arena + swz<G::SW>(16 * rt + m16, 4 * k + g4, RB));
+    for (int k = 0; k < KST; ++k) qf[rt][k] = *(const OT8 *)(arena + swz<G::SW>(16 * rt + m16, 4 * k + g4, RB));
   int lim[RTM];
 #pragma unroll
   for (int rt = 0; rt < RTM; ++rt) lim[rt] = n + (16 * rt + m16) / Gq;
@@ -418,25 +546,25 @@ __global__ __launch_bounds__(kThreads) void turbo8_kernel(Params p, const uint8_
   }
   const float sl2 = p.scale_log2;
 
-  // ---- the new rows first, from fp16 tiles in the V tile's place: V rows
+  // ---- the new rows first, from operand tiles in the V tile's place: V rows
   // 0 .. 31 (zero from L on), K rows 0 .. 15 at rows 32 .. 47
   if (tail) {
     lds_barrier();                                      // every wave holds its query operands
     if (!copier) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        put_row<D, f16_t>(vtile + 32 * RB, RB, 8 * k + nr, E * c16, kx[k]);
-        put_row<D, f16_t>(vtile, RB, 8 * k + nr, E * c16, vx[k]);
+        put_row<D, OT>(vtile + 32 * RB, RB, 8 * k + nr, E * c16, kx[k]);
+        put_row<D, OT>(vtile, RB, 8 * k + nr, E * c16, vx[k]);
       }
     } else {
       float z[E];
 #pragma unroll
       for (int j = 0; j < E; ++j) z[j] = 0.f;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) put_row<D, f16_t>(vtile, RB, 16 + 8 * k + 4 * wave + g4, E * c16, z);
+      for (int k = 0; k < 2; ++k) put_row<D, OT>(vtile, RB, 16 + 8 * k + 4 * wave + g4, E * c16, z);
     }
     lds_barrier();
-    attend_stage<D, RTM, NoOp, f16_t>(vtile + 32 * RB, vtile, L, n, qf, O, mrun, lrun, lim, sl2, xch);
+    attend_stage<D, RTM, NoOp, OT>(vtile + 32 * RB, vtile, L, n, qf, O, mrun, lrun, lim, sl2, xch);
   }
 
   // ---- cached stages
@@ -449,24 +577,46 @@ __global__ __launch_bounds__(kThreads) void turbo8_kernel(Params p, const uint8_
     WaitUnits<U, 2 * (NS - 1)>::run(copier ? ys + f : ys - f);
     lds_barrier();
     const unsigned char *const sl = ring + (st % NS) * SLOT;
-    // V codes -> fp16 V tile: thread t decodes groups t + 256 i (key, group);
-    // every read is issued before the first decode
-    constexpr int VG = SK * UPR / kThreads;
-    uint4 vcw[VG];
-    uint32_t vsb[VG];
+    // V -> the operand V tile: thread t decodes groups t + 256 i (key, group
+    // of 16); every read is issued before the first decode
+    constexpr int VG = SK * NG / kThreads;
+    if constexpr (FMT == kT8) {
+      uint4 vcw[VG];
+      uint32_t vsb[VG];
 #pragma unroll
-    for (int i = 0; i < VG; ++i) {
-      const int gi = t + kThreads * i, key = gi / UPR, grp = gi % UPR;
-      vcw[i] = *(const uint4 *)(sl + T8::VC + key * D + 16 * grp);
-      vsb[i] = *(const uint16_t *)(sl + T8::VS + 2 * (key * UPR + grp));
-    }
-    const T8K<D> kop(sl);
+      for (int i = 0; i < VG; ++i) {
+        const int gi = t + kThreads * i, key = gi / NG, grp = gi % NG;
+        vcw[i] = *(const uint4 *)(sl + QG::VC + key * D + 16 * grp);
+        vsb[i] = *(const uint16_t *)(sl + QG::VS + 2 * (key * NG + grp));
+      }
 #pragma unroll
-    for (int i = 0; i < VG; ++i) {
-      const int gi = t + kThreads * i, key = gi / UPR, grp = gi % UPR;
-      const T8Scale sc(vsb[i]);
-      *(f16x8 *)(vtile + swz<G::SW>(key, 2 * grp, RB)) = t8_decode8(vcw[i].x, vcw[i].y, sc);
-      *(f16x8 *)(vtile + swz<G::SW>(key, 2 * grp + 1, RB)) = t8_decode8(vcw[i].z, vcw[i].w, sc);
+      for (int i = 0; i < VG; ++i) {
+        const int gi = t + kThreads * i, key = gi / NG, grp = gi % NG;
+        const T8Scale sc(vsb[i]);
+        *(f16x8 *)(vtile + swz<G::SW>(key, 2 * grp, RB)) = t8_decode8(vcw[i].x, vcw[i].y, sc);
+        *(f16x8 *)(vtile + swz<G::SW>(key, 2 * grp + 1, RB)) = t8_decode8(vcw[i].z, vcw[i].w, sc);
+      }
+    } else {
+      // Turbo4: level x scale in fp32, rounded once to bf16
+      uint2 vcw[VG];
+      uint32_t vsb[VG];
+#pragma unroll
+      for (int i = 0; i < VG; ++i) {
+        const int gi = t + kThreads * i, key = gi / NG, grp = gi % NG;
+        vcw[i] = *(const uint2 *)(sl + QG::VC + key * (D / 2) + 8 * grp);
+        vsb[i] = *(const uint8_t *)(sl + QG::VS + key * NG + grp);
+      }
+#pragma unroll
+      for (int i = 0; i < VG; ++i) {
+        const int gi = t + kThreads * i, key = gi / NG, grp = gi % NG;
+        const float sc = unpk_fp8(vsb[i], false)[0];
+        bf16x8 h[2];
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          h[e / 8][e % 8] = (bf16_t)(sc * cbs[((e < 8 ? vcw[i].x : vcw[i].y) >> (4 * (e % 8))) & 15u]);
+        *(bf16x8 *)(vtile + swz<G::SW>(key, 2 * grp, RB)) = h[0];
+        *(bf16x8 *)(vtile + swz<G::SW>(key, 2 * grp + 1, RB)) = h[1];
+      }
     }
     const int sk0 = (int)(k0 + (int64_t)SK * st);
     const int nk_ = (int)min<int64_t>(SK, cend - sk0);
@@ -485,8 +635,15 @@ __global__ __launch_bounds__(kThreads) void turbo8_kernel(Params p, const uint8_
         });
       }
     };
-    attend_stage<D, RTM, decltype(refill), f16_t, T8K<D>>(nullptr, vtile, nk_, sk0, qf, O, mrun, lrun, lim, sl2,
-                                                           xch, refill, kop);
+    if constexpr (FMT == kT8) {
+      const T8K<D> kop(sl);                             // this wave's K codes, into registers
+      attend_stage<D, RTM, decltype(refill), f16_t, T8K<D>>(nullptr, vtile, nk_, sk0, qf, O, mrun, lrun, lim, sl2,
+                                                             xch, refill, kop);
+    } else {
+      // the slot's K region is the stage's bf16 K tile
+      attend_stage<D, RTM, decltype(refill), bf16_t>(sl + QG::KC, vtile, nk_, sk0, qf, O, mrun, lrun, lim, sl2, xch,
+                                                     refill);
+    }
   }
 
   const bool single = nch == 1;
@@ -556,35 +713,53 @@ __global__ __launch_bounds__(kThreads) void turbo8_kernel(Params p, const uint8_
   if (!cap_ok && t == 0) flag_error(p);
 }
 
-template <int D>
-static hipError_t launch_turbo8_d(const Params &p, const Turbo8Cache &c, hipStream_t s, const Timing &tm) {
+static QArgs args_of(const QuantCache &c) {
+  QArgs a;
+  a.k = c.k;
+  a.ks = c.ks;
+  a.v = c.v;
+  a.vs = c.vs;
+  for (int i = 0; i < 16; ++i) a.cb[i] = c.cb[i];
+  for (int i = 0; i < 15; ++i) a.thr[i] = c.thr[i];
+  return a;
+}
+
+template <int D, int FMT>
+static hipError_t launch_quant_d(const Params &p, const QArgs &a, hipStream_t s, const Timing &tm) {
   const int64_t groups = ((int64_t)p.B * p.chunks + 7) / 8 * 8;   // (chunk, sequence) groups, rounded up to 8
   const int64_t blocks = groups * p.Hkv;
   switch ((p.rows + 15) / 16) {
-    case 1: launch_kernel(turbo8_kernel<D, 1>, blocks, s, tm, p, c.kq, c.ks, c.vq, c.vs, c.kq, c.ks, c.vq, c.vs); break;
-    case 2: launch_kernel(turbo8_kernel<D, 2>, blocks, s, tm, p, c.kq, c.ks, c.vq, c.vs, c.kq, c.ks, c.vq, c.vs); break;
-    case 3: launch_kernel(turbo8_kernel<D, 3>, blocks, s, tm, p, c.kq, c.ks, c.vq, c.vs, c.kq, c.ks, c.vq, c.vs); break;
+    case 1: launch_kernel(quant_kernel<D, 1, FMT>, blocks, s, tm, p, a); break;
+    case 2: launch_kernel(quant_kernel<D, 2, FMT>, blocks, s, tm, p, a); break;
+    case 3: launch_kernel(quant_kernel<D, 3, FMT>, blocks, s, tm, p, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_turbo8_bf16(const Params &p, const Turbo8Cache &c, hipStream_t s, const Timing &tm) {
+hipError_t launch_quant_bf16(const Params &p, const QuantCache &c, hipStream_t s, const Timing &tm) {
+  const QArgs a = args_of(c);
+  if (c.fmt == kB4) return p.D == 256 ? launch_quant_d<256, kB4>(p, a, s, tm) : hipErrorInvalidValue;
   switch (p.D) {
-    case 64: return launch_turbo8_d<64>(p, c, s, tm);
-    case 128: return launch_turbo8_d<128>(p, c, s, tm);
-    case 256: return launch_turbo8_d<256>(p, c, s, tm);
+    case 64: return launch_quant_d<64, kT8>(p, a, s, tm);
+    case 128: return launch_quant_d<128, kT8>(p, a, s, tm);
+    case 256: return launch_quant_d<256, kT8>(p, a, s, tm);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_turbo8_append(const Params &p, const Turbo8Cache &c, hipStream_t s) {
-  const int64_t blocks = (int64_t)p.B * p.L;
-  const bf16_t *kn = (const bf16_t *)p.k_new, *vn = (const bf16_t *)p.v_new;
+hipError_t launch_quant_append(const Params &p, const QuantCache &c, hipStream_t s) {
+  const QArgs a = args_of(c);
+  const dim3 grid((unsigned)((int64_t)p.B * p.L)), block(kThreads);
+  if (c.fmt == kB4) {
+    if (p.D != 256) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((quant_append_kernel<256, kB4>), grid, block, 0, s, p, a);
+    return hipGetLastError();
+  }
   switch (p.D) {
-    case 64: hipLaunchKernelGGL(turbo8_append_kernel<64>, dim3(blocks), dim3(kThreads), 0, s, p, kn, vn, c.kq, c.ks, c.vq, c.vs); break;
-    case 128: hipLaunchKernelGGL(turbo8_append_kernel<128>, dim3(blocks), dim3(kThreads), 0, s, p, kn, vn, c.kq, c.ks, c.vq, c.vs); break;
-    case 256: hipLaunchKernelGGL(turbo8_append_kernel<256>, dim3(blocks), dim3(kThreads), 0, s, p, kn, vn, c.kq, c.ks, c.vq, c.vs); break;
+    case 64: hipLaunchKernelGGL((quant_append_kernel<64, kT8>), grid, block, 0, s, p, a); break;
+    case 128: hipLaunchKernelGGL((quant_append_kernel<128, kT8>), grid, block, 0, s, p, a); break;
+    case 256: hipLaunchKernelGGL((quant_append_kernel<256, kT8>), grid, block, 0, s, p, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -34,6 +34,9 @@ class Session:
         if "k_codes" in d:                                 # Turbo8 cache
             self.kv = binding.make_kv(d["k_codes"], d["v_codes"], d["seq_offset"], d["capacity"],
                                       k_scales=d["k_scales"], v_scales=d["v_scales"])
+        elif "v_codes" in d:                               # bf16 K + Turbo4 V cache
+            self.kv = binding.make_kv(d["k_cache"], d["v_codes"], d["seq_offset"], d["capacity"],
+                                      v_scales=d["v_scales"])
         elif block_size:
             self.kv = binding.make_kv(d["k_cache"], d["v_cache"], None, d["capacity"], d["block_table"], block_size)
         else:

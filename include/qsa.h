@@ -82,7 +82,7 @@ typedef enum {
 /* Storage of the KV cache. */
 typedef enum {
   QSA_KV_NATIVE = 0,         /* rows in cfg->dtype */
-  QSA_KV_TURBO8 = 1          /* Turbo8 (Atlas qwen3_5/mod.rs, MetalKvDtype::Turbo8: FP8 E4M3 data and a
+  QSA_KV_TURBO8 = 1,         /* Turbo8 (Atlas qwen3_5/mod.rs, MetalKvDtype::Turbo8: FP8 E4M3 data and a
                                 bf16 scale per 16 elements, in the Walsh-Hadamard rotated basis): k / v
                                 hold one E4M3 code per element ([rows][Hkv][D] bytes) and k_scales /
                                 v_scales one bf16 scale per 16 consecutive elements of a row
@@ -93,6 +93,19 @@ typedef enum {
                                 norm and rotation), which the attention applies to the queries and
                                 undoes on its output.  bf16 activations only; contiguous caches on
                                 the short-query route. */
+  QSA_KV_BF16K_TURBO4V = 2   /* bf16 K + Turbo4 V (Atlas qwen3_5/mod.rs, MetalKvDtype::Bf16KTurbo4V: K raw
+                                bf16, not rotated; V as 4-bit Lloyd-Max codebook indices and an FP8 scale
+                                per 16 elements, matched-norm L2, in the Walsh-Hadamard rotated basis):
+                                k holds the bf16 cache's K rows ([rows][Hkv][D]); v holds two 4-bit
+                                indices per byte ([rows][Hkv][D/2], element 2i in the low nibble) into
+                                the 16-level Lloyd-Max quantizer of the standard normal (ascending),
+                                and v_scales one E4M3 scale byte per 16 elements ([rows][Hkv][D/16]);
+                                k_scales is not used.  A group's indices are the levels nearest to
+                                x / RMS(group) and its scale is sqrt(sum x^2 / sum level^2) rounded to
+                                E4M3, so the decoded group keeps the group's L2 norm; V rows are stored
+                                after the orthonormal Walsh-Hadamard transform, which the attention
+                                undoes on its output.  bf16 activations, head_dim 256; contiguous
+                                caches on the short-query route. */
 } qsa_kv_dtype;
 
 /* One call's shape, numerics and execution context. */
@@ -145,7 +158,8 @@ typedef struct {
   int32_t max_blocks;        /* paged: entries per sequence in block_table (row stride) */
   int32_t kv_dtype;          /* qsa_kv_dtype; 0 = rows in cfg->dtype */
   void *k_scales;            /* QSA_KV_TURBO8: device [rows][Hkv][D/16] bf16 group scales of k */
-  void *v_scales;            /* QSA_KV_TURBO8: the same for v */
+  void *v_scales;            /* QSA_KV_TURBO8: the same for v; QSA_KV_BF16K_TURBO4V: [rows][Hkv][D/16]
+                                E4M3 scale bytes of v */
 } qsa_kv_cache;
 
 /* Bytes of workspace a call with this cfg needs (split-K partials, the
