@@ -564,7 +564,29 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(Params p, QArgs a) {
       for (int k = 0; k < 2; ++k) put_row<D, OT>(vtile, RB, 16 + 8 * k + 4 * wave + g4, E * c16, z);
     }
     lds_barrier();
-    attend_stage<D, RTM, NoOp, OT>(vtile + 32 * RB, vtile, L, n, qf, O, mrun, lrun, lim, sl2, xch);
+    if (L == 1) {
+      // One new key, visible to every row: attending it leaves each row's
+      // reference max at its score, its sum at 1 (P = 2^0 exactly) and its
+      // output at the value row, as a stage would; each wavefront sets that
+      // state itself (the stage's score MFMAs, no exchange).
+      const unsigned char *const kt = vtile + 32 * RB;
+#pragma unroll
+      for (int rt = 0; rt < RTM; ++rt) {
+        f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < KST; ++k) S = mfma_qk(*(const OT8 *)(kt + swz<G::SW>(m16, 4 * k + g4, RB)), qf[rt][k], S);
+        mrun[rt] = rows4_max(g4 == 0 ? S[0] * sl2 : -INFINITY);   // key 0 sits in lane group 0
+        lrun[rt] = 1.f;
+#pragma unroll
+        for (int db = 0; db < DBW; ++db) {
+          const int d = 16 * (DBW * wave + db) + 4 * g4;
+          const typename Op16<OT>::x4 v4 = *(const typename Op16<OT>::x4 *)(vtile + swz<G::SW>(0, d / 8, RB) + 2 * (d % 8));
+          O[rt][db] = f32x4{(float)v4[0], (float)v4[1], (float)v4[2], (float)v4[3]};
+        }
+      }
+    } else {
+      attend_stage<D, RTM, NoOp, OT>(vtile + 32 * RB, vtile, L, n, qf, O, mrun, lrun, lim, sl2, xch);
+    }
   }
 
   // ---- cached stages
