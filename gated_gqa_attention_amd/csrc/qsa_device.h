@@ -531,12 +531,28 @@ __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsi
 #pragma unroll
   for (int rt = 0; rt < RTM; ++rt) S[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (nvalid > 0) {
+    // Every K operand is read before the first product, so the reads overlap
+    // one another instead of each product waiting out its own read's latency.
+    // One row tile accumulates in two chains (even and odd column blocks),
+    // which halves the chain of dependent products; they are summed at the end.
     const unsigned char *kb = kt + 16 * wave * RB;
+    V8 a[KST];
 #pragma unroll
-    for (int ks = 0; ks < KST; ++ks) {
-      const V8 a = kop(kb, ks);
+    for (int ks = 0; ks < KST; ++ks) a[ks] = kop(kb, ks);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (RTM == 1) {
+      f32x4 S1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int rt = 0; rt < RTM; ++rt) S[rt] = mfma_qk(a, qf[rt][ks], S[rt]);
+      for (int ks = 0; ks < KST; ks += 2) {
+        S[0] = mfma_qk(a[ks], qf[0][ks], S[0]);
+        S1 = mfma_qk(a[ks + 1], qf[0][ks + 1], S1);
+      }
+      S[0] += S1;
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KST; ++ks)
+#pragma unroll
+        for (int rt = 0; rt < RTM; ++rt) S[rt] = mfma_qk(a[ks], qf[rt][ks], S[rt]);
     }
   }
   float sc[RTM][4];
@@ -628,13 +644,17 @@ __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsi
   // V^T operand (dims dim0 + m16, keys kb + 8 g4 .. + 7) from two transposing
   // reads; lane (g4, i) addresses the 8-byte piece (key kb + 8 g4 + i/4 (+4),
   // dims dim0 + 4 (i%4) ..) of the swizzled V tile.
+  // Both 32-key halves' operands are read before the first product (the
+  // second half only when the stage has keys there).
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const bool two = nkeys > 32;
+  V8 bp[2][RTM], va[2][DBW];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    if (32 * ks >= nkeys) break;
-    V8 bp[RTM];
+    if (ks == 1 && !two) break;
 #pragma unroll
     for (int rt = 0; rt < RTM; ++rt)
-      bp[rt] = *(const V8 *)(xch + (16 * rt + m16) * Xch::PSTRIDE + 2 * (32 * ks + 8 * g4));
+      bp[ks][rt] = *(const V8 *)(xch + (16 * rt + m16) * Xch::PSTRIDE + 2 * (32 * ks + 8 * g4));
     const int vk = 32 * ks + 8 * g4 + (m16 >> 2), q4 = m16 & 3;
 #pragma unroll
     for (int db = 0; db < DBW; ++db) {
@@ -643,12 +663,18 @@ __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsi
       const unsigned char *p1 = vt + swz<G::SW>(vk + 4, unit, RB) + 8 * (q4 & 1);
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
-      typedef short s16x8 __attribute__((ext_vector_type(8)));
       const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      const V8 a = __builtin_bit_cast(V8, v8);
-#pragma unroll
-      for (int rt = 0; rt < RTM; ++rt) O[rt][db] = mfma_qk(a, bp[rt], O[rt][db]);
+      va[ks][db] = __builtin_bit_cast(V8, v8);
     }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    if (ks == 1 && !two) break;
+#pragma unroll
+    for (int db = 0; db < DBW; ++db)
+#pragma unroll
+      for (int rt = 0; rt < RTM; ++rt) O[rt][db] = mfma_qk(va[ks][db], bp[ks][rt], O[rt][db]);
   }
 }
 

@@ -299,6 +299,8 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     if (fuse_new) wkraw.load(wkp + E * m16);
   }
   lds_barrier();
+  // passes of prep wave w (rows 8 k + 4 w .. + 3 of pass k) that hold a query row
+  auto passes = [&](int w) { return min(NPASS, (R - 4 * w + 7) / 8); };
   if (copier) {
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
@@ -306,6 +308,15 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
         issue_first_half(st, true, wave);
         issue_first_half(st, false, wave);
       }
+    }
+    // The query rows of the passes that hold none (all >= R) are zero: the copy
+    // waves write them while their copies are in flight, so the prep waves only
+    // take the passes with rows to prepare.
+    const int z0 = 4 * (NPASS - passes(0)), zrows = z0 + 4 * (NPASS - passes(1));
+    for (int u = t; u < zrows * G::OCT; u += 2 * kWave) {
+      const int i = u / G::OCT, w = i < z0 ? 0 : 1, j = i < z0 ? i : i - z0;
+      const int row = 8 * (passes(w) + j / 4) + 4 * w + j % 4;
+      *(uint4 *)(arena + row * RB + 16 * (u % G::OCT)) = make_uint4(0u, 0u, 0u, 0u);
     }
   }
 
@@ -329,10 +340,13 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   // zero), into ring slot new_slot or into the arena.
   unsigned char *const nkb = early_new || !ARENA_NEW ? kring + new_slot : arena + NEWOFF + 16 * RB;
   unsigned char *const nvb = early_new || !ARENA_NEW ? vring + new_slot : arena + NEWOFF;
+  // A single new key is read only from row 0 (its score and its value row set
+  // the state directly); otherwise rows L .. 15 are zero for the products.
   auto put_new_rows = [&]() {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int l = 8 * k + nr;
+      if (L == 1 && early_new && l > 0) continue;
       float v[E];
       vnraw[k].to_float(v);
 #pragma unroll
@@ -365,21 +379,18 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     wqraw.to_float(wq);
     // The raw rows wait in their LDS slots and one loop (not unrolled: its code
     // stays in the instruction cache from the first pass on) prepares them in place.
+    const int npass = passes(pw);                       // later passes' rows are zero (the copy waves')
 #pragma unroll
-    for (int k = 0; k < NPASS; ++k) qraw[k].template store_lds<G::SW>(arena, RB, 8 * k + 4 * pw + g4, E * m16);
-    const int npass = min(NPASS, (R - 4 * pw + 7) / 8);   // passes with rows < R; later rows are zero
+    for (int k = 0; k < NPASS; ++k)
+      if (k < npass) qraw[k].template store_lds<G::SW>(arena, RB, 8 * k + 4 * pw + g4, E * m16);
 #pragma unroll 1
-    for (int k = 0; k < NPASS; ++k) {
+    for (int k = 0; k < npass; ++k) {
       const int r = 8 * k + 4 * pw + g4;
       float x[E];
-#pragma unroll
-      for (int j = 0; j < E; ++j) x[j] = 0.f;           // rows >= R are zero
-      if (k < npass) {
-        RawE<E> raw;
-        raw.template load_lds<G::SW>(arena, RB, r, E * m16);
-        raw.to_float(x);
-        norm_rope<D>(x, wq, r < R, eps, 2 * half, tabw + (min(r, R - 1) / Gq) * half);
-      }
+      RawE<E> raw;
+      raw.template load_lds<G::SW>(arena, RB, r, E * m16);
+      raw.to_float(x);
+      norm_rope<D>(x, wq, r < R, eps, 2 * half, tabw + (min(r, R - 1) / Gq) * half);   // rows >= R become zero
       put_row_bf16<D>(arena, RB, r, E * m16, x);
     }
     if (tail) {
