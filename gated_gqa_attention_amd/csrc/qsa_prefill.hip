@@ -268,9 +268,9 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
       }
     }
   };
-  static_assert(NS >= 2, "stage copies overlap the stage before");
+  static_assert(NS >= 3, "stage copies overlap the two stages before");
 #pragma unroll
-  for (int st = 0; st < NS - 1; ++st)
+  for (int st = 0; st < NS - 2; ++st)
     if (st < nst) issue_stage(st);
 
   f32x4 O[RT][NDB];
@@ -282,33 +282,46 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
 #pragma unroll
     for (int db = 0; db < NDB; ++db) O[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // One barrier per stage: stage st is in LDS, and every wavefront is done with
-  // stage st - 1, whose slot is refilled.  Each wavefront then scores, runs its
-  // softmax and accumulates the values of stage st; the two wavefronts of a SIMD
-  // overlap each other's waits.
-  for (int st = 0; st < nst; ++st) {
-    const int so = (st % NS) * G::STAGE;
-    wait_stages<2 * LPS, NS>(min(NS - 2, nst - 1 - st));
+  // Staggered wavefront pairs.  Every wavefront accumulates the values of
+  // stage st - 1 (its probabilities kept from the iteration before), then
+  // scores stage st and runs its softmax; the two wavefronts of a SIMD (w and
+  // w + 4) meet the stage's barrier at different points of that sequence: an
+  // early wavefront after the value product, a late one before it.  So between
+  // two barriers an early wavefront scores, runs its softmax and accumulates
+  // values, while its partner accumulates values, then scores and runs its
+  // softmax: while one runs its softmax on the vector ALUs, the other has
+  // products for the matrix cores.  One barrier per stage: stage st is in LDS,
+  // the early wavefronts are done with stage st - 1 and the late ones with
+  // stage st - 2, whose slot is refilled with stage st + NS - 2 (stages st + 1
+  // and st + 2 in flight while st - 1 and st are in use).
+  const bool late = wave >= kTileWaves / 2;
+  bf16x8 bq[RT];                                        // probabilities of the stage before
+  auto meet = [&](int st) {
+    wait_stages<2 * LPS, NS>(min(1, nst - 1 - st));
     lds_barrier();
-    if (st + NS - 1 < nst) issue_stage(st + NS - 1);    // refill the slot of stage st - 1
+    if (st + NS - 2 < nst) issue_stage(st + NS - 2);    // into the slot of stage st - 2
+  };
+  for (int st = 0; st < nst; ++st) {
+    if (late) meet(st);
+    if (st > 0) stage_values<D, RT>(vring + ((st - 1) % NS) * G::STAGE, bq, O);
+    if (!late) meet(st);
     const int64_t sk0 = k0 + (int64_t)SK * st;
     const int nk = (int)min<int64_t>(SK, k1 - sk0);
     f32x4 S[2][RT];
-    bf16x8 bp[RT];
     float alpha[RT];
     bool r = false;
-    stage_qk<D, RT>(kring + so, qf, S);
+    stage_qk<D, RT>(kring + (st % NS) * G::STAGE, qf, S);
     if (sk0 + SK <= kfull) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const f32x4 st2[2] = {S[0][rt], S[1][rt]};
-        r |= stage_softmax<false>(st2, nk, (int)(sk0 - n), mrun[rt], lrun[rt], lim[rt], sl2, bp[rt], alpha[rt]);
+        r |= stage_softmax<false>(st2, nk, (int)(sk0 - n), mrun[rt], lrun[rt], lim[rt], sl2, bq[rt], alpha[rt]);
       }
     } else {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const f32x4 st2[2] = {S[0][rt], S[1][rt]};
-        r |= stage_softmax<true>(st2, nk, (int)(sk0 - n), mrun[rt], lrun[rt], lim[rt], sl2, bp[rt], alpha[rt]);
+        r |= stage_softmax<true>(st2, nk, (int)(sk0 - n), mrun[rt], lrun[rt], lim[rt], sl2, bq[rt], alpha[rt]);
       }
     }
     if (__any(r)) {
@@ -317,8 +330,8 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
 #pragma unroll
         for (int db = 0; db < NDB; ++db) O[rt][db] *= alpha[rt];
     }
-    stage_values<D, RT>(vring + so, bp, O);
   }
+  if (nst > 0) stage_values<D, RT>(vring + ((nst - 1) % NS) * G::STAGE, bq, O);   // no refill after the loop
 
   // ------------------------------------------------------------ outputs
   // lane (g4, m16) holds dims 16 db + 4 g4 .. + 3 of row m16
