@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
       }
     }
   };
-  static_assert(NS >= 3, "stage copies overlap the two stages before");
+  static_assert(NS >= 4, "stage copies overlap the two stages before");
 #pragma unroll
   for (int st = 0; st < NS - 2; ++st)
     if (st < nst) issue_stage(st);
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
   const bool late = wave >= kTileWaves / 2;
   bf16x8 bq[RT];                                        // probabilities of the stage before
   auto meet = [&](int st) {
-    wait_stages<2 * LPS, NS>(min(1, nst - 1 - st));
+    wait_stages<2 * LPS, NS>(min(NS - 3, nst - 1 - st));
     lds_barrier();
     if (st + NS - 2 < nst) issue_stage(st + NS - 2);    // into the slot of stage st - 2
   };

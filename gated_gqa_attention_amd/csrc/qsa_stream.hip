@@ -552,7 +552,10 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
 #pragma unroll
       for (int db = 0; db < DBW; ++db) {
         const int d = 16 * (DBW * wave + db) + 4 * g4;
-        __builtin_nontemporal_store(O[rt][db], (f32x4 *)(p.part_o + (slot_rows + r) * D + d));
+        f32x4 *const dst = (f32x4 *)(p.part_o + (slot_rows + r) * D + d);
+        // one row tile's partials (4 KB per workgroup at head_dim 256) stay in the
+        // caches for the merge kernel; several tiles' are written past them (faster)
+        if constexpr (RTM == 1) *dst = O[rt][db]; else __builtin_nontemporal_store(O[rt][db], dst);
       }
       if (wave == 0 && g4 == 0) *(float2 *)(p.part_ml + (slot_rows + r) * 2) = make_float2(mrun[rt], lrun[rt]);
     }
