@@ -72,7 +72,9 @@ int validate_cfg(const qsa_cfg *c) {
   return QSA_OK;
 }
 
-int make_plan(const qsa_cfg *c, Plan *pl) {
+// row_tiles: the short-query route may cut a KV group's rows into row tiles (the bf16
+// cache's kernel; the quantized caches' kernel takes a group's rows whole).
+int make_plan(const qsa_cfg *c, Plan *pl, bool row_tiles = true) {
   const int64_t B = c->batch, L = c->q_len, Hq = c->num_q_heads, Hkv = c->num_kv_heads, D = c->head_dim;
   const int64_t G = Hq / Hkv;
   const int64_t rows_total = L * G;
@@ -95,9 +97,13 @@ int make_plan(const qsa_cfg *c, Plan *pl) {
                        c->num_q_heads <= 32767 && L * (c->rotary_dim / 2) <= qsa::kMaxFusedTable &&
                        (c->rotary_dim / 2) % (D / 16) == 0;
     p.route = fused ? kRouteFused : kRoutePrepared;
-    const int64_t tile_rows = fused ? qsa::kMaxFusedRows : qsa::kPrefillTileRows;
+    // Short-query route: a KV group's rows in tiles of at most kFusedTileRows,
+    // balanced (48 rows: two tiles of 24), so more workgroups share a group's
+    // keys and each takes a longer key chunk: fewer split-K partials, and fewer
+    // query rows to prepare per workgroup.
+    const int64_t tile_rows = fused ? (row_tiles ? qsa::kFusedTileRows : qsa::kMaxFusedRows) : qsa::kPrefillTileRows;
     p.tiles = (int)cdiv(rows_total, tile_rows);
-    p.rows = (int)std::min<int64_t>(rows_total, tile_rows);
+    p.rows = fused ? (int)cdiv(rows_total, p.tiles) : (int)std::min<int64_t>(rows_total, tile_rows);
     const int64_t base = B * Hkv * p.tiles;
     if (!fused) {
       // Tile route: a tile's keys are cut into chunks of equal length, just
@@ -130,7 +136,9 @@ int make_plan(const qsa_cfg *c, Plan *pl) {
       p.even_split = c->force_splits == 0 && p.chunk_keys >= 1024;
       p.chunks = (int)std::max<int64_t>(1, (S + (p.even_split ? p.chunk_keys / 2 : 0)) / p.chunk_keys);
     }
-    p.blocks = base * p.chunks;
+    // the short-query grid takes its work items in groups of 8 (one per XCD),
+    // times the row tiles; items past the count return at once
+    p.blocks = fused ? cdiv(B * Hkv * p.chunks, 8) * 8 * p.tiles : base * p.chunks;
   }
   if (p.blocks > 0x7fffffffLL) return fail(QSA_ERR_UNSUPPORTED, "launch grid too large (%lld workgroups)",
                                            (long long)p.blocks);
@@ -322,16 +330,18 @@ const char *qsa_last_error(void) { return g_err.c_str(); }
 
 size_t qsa_workspace_size(const qsa_cfg *cfg) {
   if (validate_cfg(cfg) != QSA_OK) return 0;
-  Plan pl;
-  if (make_plan(cfg, &pl) != QSA_OK) return 0;
-  return pl.total;
+  Plan pl, whole;                                       // the bf16 cache's plan, and the quantized caches'
+  if (make_plan(cfg, &pl) != QSA_OK || make_plan(cfg, &whole, false) != QSA_OK) return 0;
+  return std::max(pl.total, whole.total);
 }
 
 int qsa_describe_plan(const qsa_cfg *cfg, char *buf, size_t len) {
   int rc = validate_cfg(cfg);
   if (rc != QSA_OK) return rc;
-  Plan pl;
-  if ((rc = make_plan(cfg, &pl)) != QSA_OK) return rc;
+  Plan pl, whole;
+  if ((rc = make_plan(cfg, &pl)) != QSA_OK || (rc = make_plan(cfg, &whole, false)) != QSA_OK) return rc;
+  pl.total = std::max(pl.total, whole.total);           // what qsa_workspace_size asks for
+  // the plan of a bf16 cache (a quantized cache's takes a KV group's rows whole);
   // merge: how split-K partials are combined -- "kernel" (a second kernel, launched
   // only when the grid splits keys) or "none"
   return snprintf(buf, len,
@@ -404,7 +414,7 @@ int gated_attention_in(const void *q_gate, const void *k_new, const void *v_new,
       overlaps(out, out_bytes, kv->v_scales, vs_bytes))
     return fail(QSA_ERR_INVALID, "out must not alias q_gate, k_new, v_new or the cache");
   Plan pl;
-  if ((rc = make_plan(cfg, &pl)) != QSA_OK) return rc;
+  if ((rc = make_plan(cfg, &pl, kv->kv_dtype == QSA_KV_NATIVE)) != QSA_OK) return rc;
   if (kv->kv_dtype != QSA_KV_NATIVE && (rc = check_quant(cfg, pl, kv->kv_dtype)) != QSA_OK) return rc;
   if (kv->block_table) {
     // Paged caches on the short-query route only.  A workgroup holds the block
@@ -419,8 +429,12 @@ int gated_attention_in(const void *q_gate, const void *k_new, const void *v_new,
       return fail(QSA_ERR_UNSUPPORTED, "key chunks of %d keys span more than 128 blocks of %d rows",
                   pl.chunk_keys, kv->block_size);
   }
-  if (!ws_ptr || ws_bytes < pl.total)
-    return fail(QSA_ERR_WORKSPACE, "%s of %zu bytes needed, %zu %s", ws_name, pl.total,
+  // the contract is qsa_workspace_size(cfg), whichever cache format this call has
+  Plan whole;
+  if ((rc = make_plan(cfg, &whole, false)) != QSA_OK) return rc;
+  const size_t need = std::max(pl.total, whole.total);
+  if (!ws_ptr || ws_bytes < need)
+    return fail(QSA_ERR_WORKSPACE, "%s of %zu bytes needed, %zu %s", ws_name, need,
                 ws_ptr ? ws_bytes : (size_t)0, ws_ptr ? "available" : "given");
   if ((rc = check_device()) != QSA_OK) return rc;
 
@@ -643,8 +657,9 @@ int qsa_gated_attention_noalloc(const void *q_gate, const void *k_new, const voi
                                 void *out) {
   int rc = validate_cfg(cfg);
   if (rc != QSA_OK) return rc;
-  Plan pl;
-  if ((rc = make_plan(cfg, &pl)) != QSA_OK) return rc;
+  Plan pl, whole;
+  if ((rc = make_plan(cfg, &pl)) != QSA_OK || (rc = make_plan(cfg, &whole, false)) != QSA_OK) return rc;
+  pl.total = std::max(pl.total, whole.total);           // either cache format's plan fits
   if (pl.total > kScratchBytes)
     return fail(QSA_ERR_WORKSPACE,
                 "this call needs %zu bytes of scratch; the allocation-free entry point holds %zu "

@@ -30,6 +30,9 @@ constexpr int kMaxPairs = 128;        // rotary pairs (rotary_dim / 2) supported
 constexpr int kMaxChunks = 4096;      // key chunks per (sequence, KV head, tile)
 constexpr int kMaxFusedTable = 512;   // (cos, sin) pairs a short-query call tabulates: L * r/2
 constexpr int kMaxFusedRows = 48;     // query rows (group heads x new rows) of a short-query call
+constexpr int kFusedTileRows = 32;    // query rows per workgroup of the bf16 short-query kernel
+static_assert(2 * kFusedTileRows >= kMaxFusedRows && kFusedTileRows == 32,
+              "the short-query kernel takes one row tile of up to 32 rows, or two of 17 .. 24");
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Workspace layout (bytes, 256-aligned sections):

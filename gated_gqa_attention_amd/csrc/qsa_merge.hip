@@ -26,7 +26,8 @@ namespace qsa {
 // (taken for the grid's chunk count, before the sequence length is known) and
 // the length itself form one round trip.  A sequence out of range has NaN
 // statistics in chunk 0 (written by the attention kernel), so its merged rows
-// are NaN.  lg packs L (bits 0-15) and G (bits 16-31).
+// are NaN.  lg packs L (bits 0-7), the row tiles per KV head, one or two (bits
+// 8-15), and G (bits 16-31).
 //
 // ROT: the partials are in the Walsh-Hadamard basis (the Turbo8 cache's), so
 // the merged row is rotated back (the iWHT(out) bookend) before the gate; the
@@ -47,12 +48,13 @@ __global__ __launch_bounds__(ROT ? D : kWave) void combine_kernel(const int32_t 
   const int slice = ROT ? __builtin_amdgcn_readfirstlane(threadIdx.x / kWave) : blockIdx.x % NSL;
   const int rowid = ROT ? blockIdx.x : blockIdx.x / NSL;
   const int d = kWave * slice + 4 * c16;
-  const int L = lg & 0xffff, G = lg >> 16, Hq = G * hkv;
+  const int L = lg & 0xff, two = ((lg >> 8) & 0xff) == 2 ? 1 : 0, G = lg >> 16, Hq = G * hkv;
   const int rr = rowid % rows;
-  const int slot = rowid / rows;
-  const int kvh = slot % hkv, b = slot / hkv;
-  const int l = rr / G, h = kvh * G + rr % G;
-  if (rr >= L * G) return;
+  const int slot = rowid / rows;                        // (sequence, KV head, row tile)
+  const int kvh = (unsigned)(slot >> two) % (unsigned)hkv, b = (unsigned)(slot >> two) / (unsigned)hkv;
+  const int gr = (slot & two) * rows + rr;              // the row within the KV group
+  const int l = gr / G, h = kvh * G + gr % G;
+  if (gr >= L * G) return;
   const int64_t base = (int64_t)slot * chunks * rows + rr;   // + c * rows
   const int n = seq_lens[b];
   RawE<4> zr;
@@ -260,7 +262,7 @@ hipError_t launch_combine_bf16(const Params &p, hipStream_t s, bool per_row) {
     return hipGetLastError();
   }
   const int64_t blocks = (int64_t)p.B * p.Hkv * p.tiles * p.rows * (p.D / kWave);   // tiles == 1 on this route
-  const int lg = p.L | (p.G << 16);
+  const int lg = p.L | (p.tiles << 8) | (p.G << 16);
   const bf16_t *qg = (const bf16_t *)p.q_gate;
   switch (p.D) {
     case 64:
@@ -282,7 +284,7 @@ hipError_t launch_combine_bf16(const Params &p, hipStream_t s, bool per_row) {
 
 hipError_t launch_combine_wht_bf16(const Params &p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.B * p.Hkv * p.rows;
-  const int lg = p.L | (p.G << 16);
+  const int lg = p.L | (p.tiles << 8) | (p.G << 16);
   const bf16_t *qg = (const bf16_t *)p.q_gate;
   switch (p.D) {
     case 64:

@@ -61,7 +61,8 @@ namespace qsa {
 // keys, normalise and rotate those too.  Then all four wavefronts meet, take
 // their query operands and run the stages together; refills of the ring are
 // shared by all four.
-// lgh packs L (bits 0-7), G (bits 8-15) and r/2 (bits 16-31).  PAGED: the
+// lgh packs L (bits 0-7), G (bits 8-15), r/2 (bits 16-23) and the rows of a row
+// tile (bits 24-31).  nslot: sequences x KV heads.  PAGED: the
 // cache rows go through a block table.
 template <int D, int RTM, bool PAGED>
 __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restrict__ seq_lens,
@@ -95,11 +96,27 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   const int lane = t % kWave, g4 = lane >> 4, m16 = lane & 15;
   const bool copier = wave < 2;
   const int pw = wave - 2;                              // prep wave index (prep waves)
-  const int chunk = blockIdx.x / nslot, slot = blockIdx.x % nslot;
-  const int b = slot / hkv, kvh = slot % hkv;
-  const int L = lgh & 0xff, Gq = (lgh >> 8) & 0xff, half = lgh >> 16, Hq = Gq * hkv;
+  const int L = lgh & 0xff, Gq = (lgh >> 8) & 0xff, half = (lgh >> 16) & 0xff, Hq = Gq * hkv;
+  // Row tiles: a KV group's 33 .. 48 rows go in two tiles of 17 .. 24 rows (two
+  // row tiles of 16), fewer rows in one.  Work item (chunk, sequence, KV head)
+  // and row tile: the two tiles of one item run on one XCD (block i runs on XCD
+  // i mod 8), one after the other in its order, so the second reads the item's
+  // keys from that XCD's L2.  No division on the way to the first loads.
+  const int trows = (unsigned)lgh >> 24;
+  int tiles = 1, tile = 0, item = blockIdx.x;
+  if constexpr (RTM == 2) {
+    tiles = L * Gq > trows ? 2 : 1;
+    const int xj = blockIdx.x / 8;
+    tile = tiles == 2 ? xj & 1 : 0;
+    item = 8 * (tiles == 2 ? xj >> 1 : xj) + blockIdx.x % 8;
+  }
+  // items past the grid's (padding) have chunk >= the chunk count, and return
+  // with the chunks past a sequence's end
+  const int chunk = (unsigned)item / (unsigned)nslot, bk = (unsigned)item % (unsigned)nslot;
+  const int b = (unsigned)bk / (unsigned)hkv, kvh = (unsigned)bk % (unsigned)hkv, slot = bk * tiles + tile;
   constexpr bool paged = PAGED;                         // rows through a block table (seq_offset not read)
-  const int R = L * Gq;
+  // this workgroup's rows: row0 .. row0 + R - 1 of the KV group's L * G rows
+  const int row0 = tile * trows, R = min(trows, L * Gq - row0);
 
   // ------------------------------------------------------------ round trip 1
   const int n = seq_lens[b];
@@ -121,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   if (!copier) {
 #pragma unroll
     for (int k = 0; k < NPASS; ++k) {
-      const int r = min(8 * k + 4 * pw + g4, R - 1);
+      const int r = row0 + min(8 * k + 4 * pw + g4, R - 1);
       const int l = r / Gq, h = kvh * Gq + r % Gq;
       qraw[k].load(q_gate + (((int64_t)b * L + l) * Hq + h) * 2 * D + E * m16);
     }
@@ -154,11 +171,11 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     // writes NaN too; no append; error bit set
     if (chunk == 0) {
       for (int e = t; e < R * D; e += kThreads) {
-        const int r = e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
+        const int r = row0 + e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
         ((bf16_t *)p.out)[(((int64_t)b * L + l) * Hq + h) * D + d] = (bf16_t)__builtin_nanf("");
       }
       if (p.part_ml && t < R)
-        *(float2 *)(p.part_ml + ((int64_t)slot * pchunks * p.rows + t) * 2) =
+        *(float2 *)(p.part_ml + ((int64_t)slot * pchunks * trows + t) * 2) =
             make_float2(__builtin_nanf(""), __builtin_nanf(""));
       if (t == 0) flag_error(p);
     }
@@ -194,11 +211,11 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     if (__any(bad)) {
       if (nch == 1) {
         for (int e = t; e < R * D; e += kThreads) {
-          const int r = e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
+          const int r = row0 + e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
           ((bf16_t *)p.out)[(((int64_t)b * L + l) * Hq + h) * D + d] = (bf16_t)__builtin_nanf("");
         }
       } else if (t < R) {
-        *(float2 *)(p.part_ml + (((int64_t)slot * pchunks + chunk) * p.rows + t) * 2) =
+        *(float2 *)(p.part_ml + (((int64_t)slot * pchunks + chunk) * trows + t) * 2) =
             make_float2(__builtin_nanf(""), __builtin_nanf(""));
       }
       if (t == 0) flag_error(p);
@@ -390,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
       RawE<E> raw;
       raw.template load_lds<G::SW>(arena, RB, r, E * m16);
       raw.to_float(x);
-      norm_rope<D>(x, wq, r < R, eps, 2 * half, tabw + (min(r, R - 1) / Gq) * half);   // rows >= R become zero
+      norm_rope<D>(x, wq, r < R, eps, 2 * half, tabw + ((row0 + min(r, R - 1)) / Gq) * half);   // rows >= R become zero
       put_row_bf16<D>(arena, RB, r, E * m16, x);
     }
     if (tail) {
@@ -426,7 +443,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   // key positions and causal limits fit in 32 bits: n + L <= max_seq_len <= 2^30
   int lim[RTM];
 #pragma unroll
-  for (int rt = 0; rt < RTM; ++rt) lim[rt] = n + (16 * rt + m16) / Gq;
+  for (int rt = 0; rt < RTM; ++rt) lim[rt] = n + (row0 + 16 * rt + m16) / Gq;
 
   // ------------------------------------------------------------ key stages
   f32x4 O[RTM][DBW];
@@ -526,12 +543,12 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   asm volatile("" : "+v"(cap));                       // consumed only here, after every stage
   const bool cap_ok = total <= (int64_t)cap;
   const bool single = nch == 1;
-  const int64_t slot_rows = ((int64_t)slot * pchunks + chunk) * p.rows;
+  const int64_t slot_rows = ((int64_t)slot * pchunks + chunk) * trows;
 #pragma unroll
   for (int rt = 0; rt < RTM; ++rt) {
     const int r = 16 * rt + m16;
     if (r >= R) continue;
-    const int l = r / Gq, h = kvh * Gq + r % Gq;
+    const int l = (row0 + r) / Gq, h = kvh * Gq + (row0 + r) % Gq;
     const int64_t orow = ((int64_t)b * L + l) * Hq + h;
     if (single) {
       const float inv = 1.f / lrun[rt];
@@ -567,7 +584,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
     if (chunk == 0) {
       if (!single) {
         for (int e = t; e < R * D; e += kThreads) {
-          const int r = e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
+          const int r = row0 + e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
           ((bf16_t *)p.out)[(((int64_t)b * L + l) * Hq + h) * D + d] = (bf16_t)__builtin_nanf("");
         }
         if (t < R) *(float2 *)(p.part_ml + (slot_rows + t) * 2) = make_float2(__builtin_nanf(""), __builtin_nanf(""));
@@ -578,7 +595,9 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
   }
 
   // ------------------------------------------------------------ append the new rows to the cache
-  if (tail && fuse_new) {
+  // (the workgroup holding the new keys in every row tile prepares and
+  // attends them; the first tile's stores them)
+  if (tail && fuse_new && tile == 0) {
     for (int u = t; u < 16 * G::OCT; u += kThreads) {
       const int l = u / G::OCT, oct = u % G::OCT;
       const int64_t row = paged ? paged_row((int64_t)n + min(l, L - 1)) : off + n + l;
@@ -594,8 +613,9 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const int32_t *__restr
 template <int D, int RTM, bool PAGED>
 static void launch_stream_rt(const Params &p, hipStream_t s, const Timing &tm) {
   const int nslot = p.B * p.Hkv;
-  const int64_t blocks = (int64_t)nslot * p.chunks;
-  const int lgh = p.L | (p.G << 8) | ((p.r / 2) << 16);
+  const int64_t items = (int64_t)nslot * p.chunks;
+  const int64_t blocks = (items + 7) / 8 * 8 * p.tiles;   // items in groups of 8 (one per XCD), times the row tiles
+  const int lgh = p.L | (p.G << 8) | ((p.r / 2) << 16) | (p.rows << 24);
   launch_kernel(stream_kernel<D, RTM, PAGED>, blocks, s, tm, p.seq_lens, p.seq_offset, (const bf16_t *)p.q_gate,
                 (const bf16_t *)p.wq, p.positions, nslot, p.Hkv, lgh, p);
 }

@@ -81,6 +81,10 @@ SMALL = [
              rotary_dim=128, rope_theta=1e6, dtype="bf16", prior=191, seed=105),
     Workload("bf16_verify_small", batch=2, q_len=4, num_q_heads=24, num_kv_heads=2, head_dim=256,
              rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=130, seed=106),
+    # short-query route in two row tiles of unequal size: 3 new rows x 11 heads
+    # per KV group = 33 rows, tiles of 17 and 16
+    Workload("bf16_row_tiles_33", batch=3, q_len=3, num_q_heads=22, num_kv_heads=2, head_dim=128,
+             rotary_dim=32, rope_theta=1e6, dtype="bf16", prior=150, seed=117),
     Workload("bf16_fused_l16", batch=1, q_len=16, num_q_heads=4, num_kv_heads=1, head_dim=256,
              rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=77, seed=107),
     Workload("bf16_no_prior", batch=2, q_len=5, num_q_heads=16, num_kv_heads=4, head_dim=256,
