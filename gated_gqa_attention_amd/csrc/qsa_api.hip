@@ -38,7 +38,7 @@ struct Plan {
   int route = 0;
   int rows = 0, tiles = 0, chunks = 1, chunk_keys = 0, even_split = 0;
   int64_t blocks = 0;
-  size_t off_ml = 0, off_o = 0, off_qt = 0, total = 0;
+  size_t off_ml = 0, off_o = 0, off_tinfo = 0, off_qt = 0, total = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -142,13 +142,24 @@ int make_plan(const qsa_cfg *c, Plan *pl, bool row_tiles = true) {
   }
   if (p.blocks > 0x7fffffffLL) return fail(QSA_ERR_UNSUPPORTED, "launch grid too large (%lld workgroups)",
                                            (long long)p.blocks);
-  const int64_t slots = B * Hkv * p.tiles;
+  // split-K partial slots: chunks per (sequence, KV head, row tile); on the
+  // tile route 2 chunks + 1 per pair of row tiles (the middle tile of an odd
+  // count alone), for the pieces of the pair's equal key ranges
+  const int64_t parts = p.route == kRoutePrepared ? B * Hkv * (p.tiles - p.tiles / 2) * (2 * p.chunks + 1)
+                                                  : B * Hkv * p.tiles * p.chunks;
+  // (tile route: (max, sum, scale, 0) and fp16 outputs per row; otherwise
+  // (max, sum) and fp32 outputs)
+  const bool tile_route = p.route == kRoutePrepared;
   size_t off = 256;
   if (p.chunks > 1) {
     p.off_ml = off;
-    off = align256(off + (size_t)slots * p.chunks * p.rows * 2 * 4);
+    off = align256(off + (size_t)parts * p.rows * (tile_route ? 4 : 2) * 4);
     p.off_o = off;
-    off = align256(off + (size_t)slots * p.chunks * p.rows * D * 4);
+    off = align256(off + (size_t)parts * p.rows * D * (tile_route ? 2 : 4));
+    if (tile_route) {
+      p.off_tinfo = off;
+      off = align256(off + (size_t)(B * Hkv * p.tiles) * 4);
+    }
   }
   if (p.route != kRouteFused) {
     p.off_qt = off;
@@ -448,6 +459,7 @@ int gated_attention_in(const void *q_gate, const void *k_new, const void *v_new,
   p.err = (int32_t *)ws;
   p.part_ml = pl.off_ml ? (float *)(ws + pl.off_ml) : nullptr;
   p.part_o = pl.off_o ? (float *)(ws + pl.off_o) : nullptr;
+  p.tinfo = pl.off_tinfo ? (int32_t *)(ws + pl.off_tinfo) : nullptr;
   p.qt = pl.off_qt ? (void *)(ws + pl.off_qt) : nullptr;
   hipStream_t s = (hipStream_t)cfg->stream;
   const bool has_new = k_new != nullptr;

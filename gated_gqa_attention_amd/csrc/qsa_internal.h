@@ -40,7 +40,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 //   part_ml    float [slots][chunks][rows][2]   per-chunk running max (log2 units) and sum
 //   part_o     float [slots][chunks][rows][D]   per-chunk unnormalised outputs
 //   qt         prepared queries [B][L][Hq][D] (bf16 or fp32)
-// where slots = B * Hkv * tiles.
+//   tinfo      int32 [B][Hkv][tiles]            tile route: a split tile's partial slots
+// where slots = B * Hkv * tiles.  On the tile route the partials are instead
+// [B][Hkv][pairs][2 chunks + 1][rows] (pair_ranges), part_ml holding (max, sum,
+// scale, 0) per row and part_o the fp16 output divided by the sum and the scale;
+// tinfo holds the first and last slot of each tile's pieces within its pair
+// (first | last << 16).
 constexpr int32_t kErrRange = 1;
 
 struct Params {
@@ -74,6 +79,7 @@ struct Params {
   int32_t *err;       // may be null
   float *part_ml;
   float *part_o;
+  int32_t *tinfo;     // tile route with split tiles: each tile's piece slots
   void *qt;
   double rope_step;            // theta^(-2/r) (r > 0), computed on the host in double
 };
@@ -144,6 +150,38 @@ __device__ __forceinline__ int tile_chunk_count(int64_t kend, int even_split, in
 __device__ __forceinline__ int64_t chunk_begin(int64_t kend, int even_split, int nch, int chunk_keys, int c) {
   return even_split ? (int64_t)c * kend / nch : (int64_t)c * chunk_keys;
 }
+
+// Tile route (prepared queries, tiles of `rows` query rows).  Keys tile t of
+// sequence b can see: up to its last row's position, n_b + l_last.
+__device__ __forceinline__ int64_t tile_keys(int n, int t, int rows, int R, int G) {
+  return (int64_t)n + (min((t + 1) * rows, R) - 1) / G + 1;
+}
+// With more than one chunk per tile, tiles t and T - 1 - t of one (sequence,
+// KV head) form a pair (the middle tile of an odd count stands alone).  The
+// pair's keys, those of tile t followed by those of tile T - 1 - t (S in all),
+// are cut into nw ranges of equal length, range v = [v S / nw, (v + 1) S / nw),
+// with nw = min(most, max(1, round(S / chunk_keys))) and most = 2 chunks (one
+// tile alone: chunks).  A range that crosses the boundary between the two
+// tiles holds one piece of each.  The pieces' split-K partials take slot v of
+// the pair for the first tile's piece and v + 1 for the second's, 2 chunks + 1
+// slots per pair.
+//
+// floor(a / b) for integers 0 <= a < 2^53 and b >= 1, from the correctly
+// rounded double quotient: it is exact when the quotient is an integer, and
+// otherwise lies within a/b 2^-53 < 1/b of it, nearer than the next integer.
+// On the GPU this is a short fp64 sequence where a 64-bit integer division is
+// a long one.  Every numerator below is under 2^45.
+__device__ __forceinline__ int64_t floor_div(int64_t a, int64_t b) {
+  return (int64_t)__builtin_floor((double)a / (double)b);
+}
+__device__ __forceinline__ int pair_ranges(int64_t S, int most, int chunk_keys) {
+  const int64_t c = floor_div(S + chunk_keys / 2, chunk_keys);
+  return c < 1 ? 1 : (c > most ? most : (int)c);
+}
+// The first key of range v, and the range that holds key x of the pair's S
+// keys (0 <= x < S): the largest v with range_start(v) <= x.
+__device__ __forceinline__ int64_t range_start(int v, int64_t S, int nw) { return floor_div((int64_t)v * S, nw); }
+__device__ __forceinline__ int range_of(int64_t x, int64_t S, int nw) { return (int)floor_div((x + 1) * nw - 1, S); }
 
 // Sequence bounds check shared by the prologue and the fp32 kernel.  Returns
 // false when rows [0, n + L) of sequence b would leave the cache or pass its

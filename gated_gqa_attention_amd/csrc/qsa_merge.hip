@@ -159,20 +159,26 @@ __global__ __launch_bounds__(ROT ? D : kWave) void combine_kernel(const int32_t 
   }
 }
 
+// The tile route's merge: one wavefront per (slot, row), lane c holding dims
+// EPL c .. + EPL - 1.  The pieces of a tile are the key ranges of its pair
+// that hold its keys (pair_ranges): slots 0 .. of the pair for its first tile,
+// .. 2 chunks for its second, as the attention kernel recorded them in tinfo.
+// A piece's row holds (max, sum, scale) in fp32 and its output divided by the
+// sum and the scale in fp16.
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_rows_kernel(Params p) {
   constexpr int EPL = D / kWave;
   const int prows = p.rows, ptiles = p.tiles, hkv = p.Hkv, L = p.L, Gq = p.G, Hq = p.Hq, pch = p.chunks;
-  const int ck = p.chunk_keys, msl = p.max_seq_len, even = p.even_split;
+  const int msl = p.max_seq_len;
   const int64_t nrows = p.num_rows;
   const int32_t *const seq_lens = p.seq_lens, *const capp = p.capacity;
   const int64_t *const seq_offset = p.seq_offset;
   const bf16_t *const q_gate = (const bf16_t *)p.q_gate;
   const float *const part_ml = p.part_ml, *const part_o = p.part_o;
   bf16_t *const outp = (bf16_t *)p.out;
-  asm volatile("" ::"s"(prows), "s"(ptiles), "s"(hkv), "s"(L), "s"(Gq), "s"(Hq), "s"(pch), "s"(ck), "s"(msl),
-               "s"(even), "s"(nrows), "s"(seq_lens), "s"(capp), "s"(seq_offset), "s"(q_gate), "s"(part_ml),
-               "s"(part_o), "s"(outp));
+  asm volatile("" ::"s"(prows), "s"(ptiles), "s"(hkv), "s"(L), "s"(Gq), "s"(Hq), "s"(pch), "s"(msl),
+               "s"(nrows), "s"(seq_lens), "s"(capp), "s"(seq_offset), "s"(q_gate), "s"(part_ml), "s"(part_o),
+               "s"(outp));
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   const int64_t id = (int64_t)blockIdx.x * (kThreads / kWave) + wave;   // (slot, row) pair
   const int64_t nslots = (int64_t)p.B * hkv * ptiles;
@@ -180,34 +186,48 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(Params p) {
   const int rr = (int)(id % prows);
   const int64_t slot = id / prows;
   const int tile = (int)(slot % ptiles);
-  const int kvh = (int)((slot / ptiles) % hkv);
-  const int b = (int)(slot / ((int64_t)ptiles * hkv));
+  const int64_t bk = slot / ptiles;
+  const int kvh = (int)(bk % hkv);
+  const int b = (int)(bk / hkv);
   const int row0 = tile * prows;
-  const int R = min(prows, L * Gq - row0);
+  const int Rk = L * Gq, R = min(prows, Rk - row0);
   if (rr >= R) return;
+  // the tile's pair (this merge runs with more than one chunk per tile)
+  const int half = ptiles / 2, pair = min(tile, ptiles - 1 - tile);
+  const bool second = tile > ptiles - 1 - tile;
+  const int top = 2 * pch;                              // the pair's last slot
+  const int64_t base = ((bk * (ptiles - half) + pair) * (top + 1)) * prows + rr;   // + slot * rows
   // Every load whose address does not wait on the sequence length goes out
   // first, in the round trip of the length itself: the gate and the
-  // statistics and outputs of the first PF chunks of the grid (those past the
-  // sequence's own chunk count are read but not used).
+  // statistics and outputs of up to PF slots where the tile's pieces usually
+  // are (slots 0 .. chunks - 1 of a first tile or a tile alone, chunks .. 2
+  // chunks of a second; slots past those are clamped to the last, so no other
+  // tile's partials are fetched, and any outside the tile's actual pieces are
+  // read but not used).
   constexpr int PF = 4;
-  const int64_t base = slot * pch * prows + rr;         // + c * rows
+  const int g0 = second ? pch : 0, hi = second ? 2 * pch : pch - 1;
+  const int info = p.tinfo[slot];                       // this tile's piece slots in the pair
   const int rg = row0 + rr, l = rg / Gq, h = kvh * Gq + rg % Gq;
   const bf16_t *zp = q_gate + (((int64_t)b * L + l) * Hq + h) * 2 * D + D + lane * EPL;
   float z[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) z[j] = (float)zp[j];
-  // unconditional, at clamped (in-range) chunks, and held in place by an empty
+  // unconditional, at clamped (in-range) slots, and held in place by an empty
   // asm with a memory clobber, so that the compiler issues them all here
-  float pm[PF], pl[PF], pv[PF][EPL];
+  // a piece's row: (max, sum, scale, 0) in part_ml and its output divided by
+  // the sum and by the scale in fp16 in part_o, dim 16 db + 4 g + i at
+  // 32 (db / 2) + 8 g + 4 (db % 2) + i (the attention kernel's store order);
+  // this lane's EPL dims are contiguous there
+  typedef _Float16 hE __attribute__((ext_vector_type(EPL)));
+  const int d0 = lane * EPL, dpos = (d0 >> 5) * 32 + ((d0 >> 2) & 3) * 8 + ((d0 >> 4) & 1) * 4 + (d0 & 3);
+  const _Float16 *const po16 = (const _Float16 *)part_o + dpos;
+  f32x4 pml[PF];
+  hE pv[PF];
 #pragma unroll
   for (int c = 0; c < PF; ++c) {
-    const int cc = min(c, pch - 1);
-    const float *ml = part_ml + (base + (int64_t)cc * prows) * 2;
-    const float *po = part_o + (base + (int64_t)cc * prows) * D + lane * EPL;
-    pm[c] = ml[0];
-    pl[c] = ml[1];
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) pv[c][j] = po[j];
+    const int cc = min(g0 + c, hi);
+    pml[c] = *(const f32x4 *)(part_ml + (base + (int64_t)cc * prows) * 4);
+    pv[c] = *(const hE *)(po16 + (base + (int64_t)cc * prows) * D);
   }
   asm volatile("" ::: "memory");
   const int n = seq_lens[b];
@@ -216,32 +236,39 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(Params p) {
   const int64_t total = (int64_t)n + L;
   if (!(n >= 0 && off >= 0 && total <= msl && off + total <= nrows && total <= (int64_t)cap))
     return;                                             // the attention kernel wrote NaN
-  const int nch = tile_chunk_count((int64_t)n + (row0 + R - 1) / Gq + 1, even, pch, ck);
-  if (nch == 1) return;                                 // finished by the attention kernel
+  const int first = info & 0xffff, last = info >> 16;   // the tile's pieces: slots first .. last
+  if (first == last) return;                            // finished by the attention kernel
+  auto fetched = [&](int c) { return c >= g0 && c < g0 + PF && c <= hi; };   // slot c is in registers
+  auto held = [&](int j) { return g0 + j >= first && g0 + j <= last && fetched(g0 + j); };
   float M = -INFINITY;
 #pragma unroll
   for (int c = 0; c < PF; ++c)
-    if (c < nch) M = fmaxf(M, pm[c]);
-  for (int c = PF; c < nch; ++c) M = fmaxf(M, part_ml[(base + (int64_t)c * prows) * 2]);
+    if (held(c)) M = fmaxf(M, pml[c][0]);
+  for (int c = first; c <= last; ++c)
+    if (!fetched(c)) M = fmaxf(M, part_ml[(base + (int64_t)c * prows) * 4]);
+  // out = sum_c w_c l_c s_c x_c / sum_c w_c l_c, w_c = 2^(m_c - M)
   float lsum = 0.f, acc[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
 #pragma unroll
   for (int c = 0; c < PF; ++c) {
-    if (c < nch) {
-      const float wc = exp2f(pm[c] - M);                // a chunk whose rows saw no key has m = -inf: weight 0
-      lsum += wc * pl[c];
+    if (held(c)) {
+      const float wl = exp2f(pml[c][0] - M) * pml[c][1];   // a piece whose rows saw no key has m = -inf: weight 0
+      lsum += wl;
+      const float f = wl * pml[c][2];
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) acc[j] += wc * pv[c][j];
+      for (int j = 0; j < EPL; ++j) acc[j] += f * (float)pv[c][j];
     }
   }
-  for (int c = PF; c < nch; ++c) {
-    const float *ml = part_ml + (base + (int64_t)c * prows) * 2;
-    const float wc = exp2f(ml[0] - M);
-    lsum += wc * ml[1];
-    const float *po = part_o + (base + (int64_t)c * prows) * D + lane * EPL;
+  for (int c = first; c <= last; ++c) {
+    if (fetched(c)) continue;
+    const f32x4 ml = *(const f32x4 *)(part_ml + (base + (int64_t)c * prows) * 4);
+    const float wl = exp2f(ml[0] - M) * ml[1];
+    lsum += wl;
+    const float f = wl * ml[2];
+    const hE x = *(const hE *)(po16 + (base + (int64_t)c * prows) * D);
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) acc[j] += wc * po[j];
+    for (int j = 0; j < EPL; ++j) acc[j] += f * (float)x[j];
   }
   const float inv = 1.f / lsum;
   bf16_t *out = outp + (((int64_t)b * L + l) * Hq + h) * D + lane * EPL;

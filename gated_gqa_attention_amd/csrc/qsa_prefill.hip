@@ -158,9 +158,15 @@ __device__ __forceinline__ void stage_values(const unsigned char *vt, const bf16
 
 }  // namespace
 
-// Work items ((b, g, tile) slot, chunk) are numbered chunk-fastest; the
-// workgroup of block i runs on XCD i % 8, and each XCD takes a contiguous range
-// of items so that the tiles sharing a KV head share that XCD's L2.
+// Work items ((sequence, KV head) group, workgroup of the group) are numbered
+// so that the workgroup of block i runs on XCD i % 8 and each XCD takes a
+// contiguous range of items: the tiles that share a KV head share that XCD's
+// L2.  With C > 1 chunks per tile the group's tiles t and T - 1 - t form a pair
+// with 2 C workgroups (the middle tile of an odd count stands alone with C),
+// and the pair's keys are cut into equal ranges (pair_ranges): causal rows see
+// more keys the later their tile, and pairing the first tiles with the last
+// gives every workgroup about the same number of keys.  A range that crosses
+// the boundary between the pair's tiles runs as two segments, one per tile.
 // Preloaded arguments: sequence metadata, the prepared queries and the grid shape.
 template <int D>
 __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__restrict__ seq_lens,
@@ -179,204 +185,287 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
   const int per = nitems / 8, rem = nitems % 8, x = blockIdx.x % 8, j = blockIdx.x / 8;
   const int item = x * per + min(x, rem) + j;
   const int hkv = p.Hkv, pchunks = p.chunks;
-  const int chunk = item % pchunks, slot = item / pchunks;
-  const int tile = slot % tiles, bk = slot / tiles;
+  const int gw = tiles * pchunks;                       // workgroups per (sequence, KV head)
+  const int bk = item / gw, wi = item % gw;
   const int b = bk / hkv, kvh = bk % hkv;
-  const int R = L * Gq;                                 // rows of this KV head
-  const int row0 = tile * kPrefillRows;
-  int wrow[RT], wr[RT];                                 // this lane's row in each of its row tiles
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    wrow[rt] = row0 + 16 * (RT * wave + rt) + m16;
-    wr[rt] = min(wrow[rt], R - 1);
+  // this workgroup's pair of tiles (ta, tc; ta == tc for a tile alone) and its
+  // index v among the pair's wmax workgroups
+  const int half = pchunks > 1 ? tiles / 2 : 0;         // pairs of two tiles
+  int pair, v, wmax;
+  if (wi < 2 * pchunks * half) {
+    pair = wi / (2 * pchunks);
+    v = wi % (2 * pchunks);
+    wmax = 2 * pchunks;
+  } else {
+    pair = half + (wi - 2 * pchunks * half) / pchunks;
+    v = (wi - 2 * pchunks * half) % pchunks;
+    wmax = pchunks;
   }
+  const int ta = pair, tc = pair < half ? tiles - 1 - pair : pair;
+  const int R = L * Gq;                                 // rows of this KV head
+  int wrow[RT], wr[RT];                                 // this lane's row in each of its row tiles
+  bf16x8 qf[RT][KST];
+  auto load_queries = [&](int tile) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      wrow[rt] = tile * kPrefillRows + 16 * (RT * wave + rt) + m16;
+      wr[rt] = min(wrow[rt], R - 1);
+      const int l = wr[rt] / Gq, h = kvh * Gq + wr[rt] % Gq;
+      const bf16_t *src = qt + (((int64_t)b * L + l) * Hq + h) * D + 8 * g4;
+#pragma unroll
+      for (int ks = 0; ks < KST; ++ks) qf[rt][ks] = __builtin_bit_cast(bf16x8, gld<uint4>(src + 32 * ks));
+    }
+  };
+  auto queries_landed = [&]() {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ks = 0; ks < KST; ++ks) {
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        asm volatile("" ::"v"(__builtin_bit_cast(u32x4, qf[rt][ks])));
+      }
+  };
 
-  // ------------------------------------------------------------ round trip 1: metadata and queries
+  // ------------------------------------------------------------ round trip 1: metadata
   const int n = seq_lens[b];
   const int64_t off = seq_offset[b];
-  bf16x8 qf[RT][KST];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int l = wr[rt] / Gq, h = kvh * Gq + wr[rt] % Gq;
-    const bf16_t *src = qt + (((int64_t)b * L + l) * Hq + h) * D + 8 * g4;
-#pragma unroll
-    for (int ks = 0; ks < KST; ++ks) qf[rt][ks] = __builtin_bit_cast(bf16x8, gld<uint4>(src + 32 * ks));
-  }
-  const int ck = p.chunk_keys, msl = p.max_seq_len, even = p.even_split;
+  const int ck = p.chunk_keys, msl = p.max_seq_len;
   const int64_t nrows = p.num_rows;
   const bf16_t *const kc = (const bf16_t *)p.kc;
   const bf16_t *const vc = (const bf16_t *)p.vc;
   const int32_t *const capp = p.capacity;
   const float sl2 = p.scale_log2;
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::"s"(n), "s"(off), "s"(ck), "s"(msl), "s"(even), "s"(nrows), "s"(kc), "s"(vc), "s"(capp),
-               "s"(sl2));
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int ks = 0; ks < KST; ++ks) {
-      typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-      asm volatile("" ::"v"(__builtin_bit_cast(u32x4, qf[rt][ks])));
-    }
+  asm volatile("" ::"s"(n), "s"(off), "s"(ck), "s"(msl), "s"(nrows), "s"(kc), "s"(vc), "s"(capp), "s"(sl2));
 
   const int64_t total = (int64_t)n + L;
   const bool in_range = n >= 0 && off >= 0 && total <= msl && off + total <= nrows;
   const int cap = capp ? capp[b] : 0x7fffffff;
-  const int rlast = min(row0 + kPrefillRows, R) - 1;    // last row of the tile
-  const int64_t kend = (int64_t)n + rlast / Gq + 1;     // keys the tile's rows can see
-  const int nch = tile_chunk_count(kend, even, pchunks, ck);
-  if (chunk >= nch) return;
+  auto nan_rows = [&](int tile) {                       // every output of the tile's rows
+    const int r0 = tile * kPrefillRows, nr = min(r0 + kPrefillRows, R) - r0;
+    for (int e = t; e < nr * D; e += kTileThreads) {
+      const int r = r0 + e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
+      ((bf16_t *)p.out)[(((int64_t)b * L + l) * Hq + h) * D + d] = (bf16_t)__builtin_nanf("");
+    }
+  };
   if (!in_range) {
-    if (chunk == 0) {
-      for (int e = t; e < (rlast - row0 + 1) * D; e += kTileThreads) {
-        const int r = row0 + e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
-        ((bf16_t *)p.out)[(((int64_t)b * L + l) * Hq + h) * D + d] = (bf16_t)__builtin_nanf("");
-      }
+    if (v == 0) {
+      nan_rows(ta);
+      if (tc != ta) nan_rows(tc);
       if (t == 0) flag_error(p);
     }
     return;
   }
-  const int64_t k0 = chunk_begin(kend, even, nch, ck, chunk);
-  const int64_t k1 = chunk == nch - 1 ? kend : chunk_begin(kend, even, nch, ck, chunk + 1);
-  const int nst = (int)((k1 - k0 + SK - 1) / SK);
-  const int64_t kfull = min(k1, (int64_t)n + row0 / Gq + 1);   // keys below this are visible to every row
-  int lim[RT];                                          // causal limit of the lane's rows, relative to n_b
+  const int64_t Ka = tile_keys(n, ta, kPrefillRows, R, Gq);
+  const int64_t S = Ka + (tc != ta ? tile_keys(n, tc, kPrefillRows, R, Gq) : 0);
+  const int nw = pair_ranges(S, wmax, ck);
+  if (v >= nw) return;
+  const int64_t x0 = range_start(v, S, nw), x1 = range_start(v + 1, S, nw);   // this workgroup's keys of the pair
+  const int sg0 = x0 < Ka ? 0 : 1, sg1 = tc != ta && x1 > Ka ? 2 : 1;
+  // The segments' facts go through LDS, so that none of them holds a scalar
+  // register during the key stages: per segment (0: tile ta, 1: tile tc) the
+  // tile, its keys [k0, k1), flags (the tile's only piece, its first piece,
+  // within capacity) and this piece's partial slot.
+  __shared__ int seg_info[2][5];
+  if (t == 0) {
+    const int lasta = range_of(Ka - 1, S, nw);          // the last range with keys of tile ta
+    const int firstc = tc != ta ? range_of(Ka, S, nw) : nw;   // the first with keys of tile tc
+    const int pslot = (bk * (tiles - half) + pair) * (2 * pchunks + 1);   // partial slots of the pair
+    const int cap_ok = total <= (int64_t)cap;
+    // the merge finds each split tile's pieces here: the workgroup holding a
+    // tile's first piece writes them (pair-relative slots first | last << 16)
+    if (p.tinfo) {
+      if (v == 0) p.tinfo[bk * tiles + ta] = lasta << 16;
+      if (tc != ta && v == firstc) p.tinfo[bk * tiles + tc] = (firstc + 1) | nw << 16;
+    }
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) lim[rt] = wr[rt] / Gq;
-
-  // ------------------------------------------------------------ key stages
+    for (int sg = 0; sg < 2; ++sg) {
+      const int64_t kb0 = sg ? Ka : 0;
+      seg_info[sg][0] = sg ? tc : ta;
+      seg_info[sg][1] = (int)(max(x0, kb0) - kb0);
+      seg_info[sg][2] = (int)(min(x1, sg ? S : Ka) - kb0);
+      seg_info[sg][3] = (sg ? firstc == nw - 1 : lasta == 0) | (sg ? v == firstc : v == 0) << 1 | cap_ok << 2;
+      seg_info[sg][4] = pslot + v + sg;
+    }
+  }
+  lds_barrier();
   const unsigned kring_lds = (unsigned)(uintptr_t)(lds_void *)kring;
   const unsigned vring_lds = (unsigned)(uintptr_t)(lds_void *)vring;
-  // This thread's copies of a stage: key row u / OCT of the stage, and the
-  // 16-byte unit that the K (V) tile's swizzle puts at LDS position u % OCT of
-  // that row; the source is that key's row of KV head kvh, addressed from the
-  // stage's first key (wave-uniform) plus a lane offset.
   const unsigned rowb = (unsigned)(hkv * D * 2);       // bytes between consecutive keys of one KV head
-  auto issue_stage = [&](int st) {   // keys k0 + SK st .. into ring slot st % NS
-    const int64_t sk0 = k0 + (int64_t)SK * st;
-    const int last = (int)min<int64_t>(SK - 1, k1 - 1 - sk0);   // keys past the chunk repeat its last key
-    const int64_t row = ((off + sk0) * hkv + kvh) * D;
-    const bf16_t *kb = kc + row, *vb = vc + row;
-#pragma unroll
-    for (int i = 0; i < LPS; ++i) {
-      const int u = t + kTileThreads * i, key = u / G::OCT, pos = u % G::OCT;
-      const unsigned kr = (unsigned)min(key, last) * rowb;
-      const unsigned dst = (st % NS) * G::STAGE + kTileThreads * 16 * i + wave * 1024;
-      if (G::NCP % kTileThreads == 0 || kTileThreads * i + 64 * wave < G::NCP) {   // wave-uniform
-        dma16_sbase(kb, kr + 16u * (unsigned)(pos ^ (key & G::SW)), kring_lds + dst);
-        dma16_sbase(vb, kr + 16u * (unsigned)(pos ^ (2 * (key & G::SWV))), vring_lds + dst);
-      }
-    }
-  };
-  static_assert(NS >= 4, "stage copies overlap the two stages before");
-#pragma unroll
-  for (int st = 0; st < NS - 2; ++st)
-    if (st < nst) issue_stage(st);
 
-  f32x4 O[RT][NDB];
-  float mrun[RT], lrun[RT];                             // lrun: this lane's share of the row sum
+#pragma clang loop unroll(disable)
+  for (int sg = sg0; sg < sg1; ++sg) {
+    // ---------------------------------------------------------- one segment: tile `tile`, keys [k0, k1)
+    const int tile = __builtin_amdgcn_readfirstlane(seg_info[sg][0]);
+    const int k0 = __builtin_amdgcn_readfirstlane(seg_info[sg][1]);
+    const int k1 = __builtin_amdgcn_readfirstlane(seg_info[sg][2]);
+    const int row0 = tile * kPrefillRows;
+    // the segment's queries land before its first copies (no copy or store of
+    // the segment before is outstanding then)
+    load_queries(tile);
+    queries_landed();
+    if (sg != sg0) lds_barrier();                       // every wavefront is done with the ring
+    const int nst = (int)((k1 - k0 + SK - 1) / SK);
+    const int64_t kfull = min((int64_t)k1, (int64_t)n + row0 / Gq + 1);   // keys below this are visible to every row
+    int lim[RT];                                        // causal limit of the lane's rows, relative to n_b
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    mrun[rt] = -INFINITY;
-    lrun[rt] = 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) O[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  // Staggered wavefront pairs.  Every wavefront accumulates the values of
-  // stage st - 1 (its probabilities kept from the iteration before), then
-  // scores stage st and runs its softmax; the two wavefronts of a SIMD (w and
-  // w + 4) meet the stage's barrier at different points of that sequence: an
-  // early wavefront after the value product, a late one before it.  So between
-  // two barriers an early wavefront scores, runs its softmax and accumulates
-  // values, while its partner accumulates values, then scores and runs its
-  // softmax: while one runs its softmax on the vector ALUs, the other has
-  // products for the matrix cores.  One barrier per stage: stage st is in LDS,
-  // the early wavefronts are done with stage st - 1 and the late ones with
-  // stage st - 2, whose slot is refilled with stage st + NS - 2 (stages st + 1
-  // and st + 2 in flight while st - 1 and st are in use).
-  const bool late = wave >= kTileWaves / 2;
-  bf16x8 bq[RT];                                        // probabilities of the stage before
-  auto meet = [&](int st) {
-    wait_stages<2 * LPS, NS>(min(NS - 3, nst - 1 - st));
-    lds_barrier();
-    if (st + NS - 2 < nst) issue_stage(st + NS - 2);    // into the slot of stage st - 2
-  };
-  for (int st = 0; st < nst; ++st) {
-    if (late) meet(st);
-    if (st > 0) stage_values<D, RT>(vring + ((st - 1) % NS) * G::STAGE, bq, O);
-    if (!late) meet(st);
-    const int64_t sk0 = k0 + (int64_t)SK * st;
-    const int nk = (int)min<int64_t>(SK, k1 - sk0);
-    f32x4 S[2][RT];
-    float alpha[RT];
-    bool r = false;
-    stage_qk<D, RT>(kring + (st % NS) * G::STAGE, qf, S);
-    if (sk0 + SK <= kfull) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const f32x4 st2[2] = {S[0][rt], S[1][rt]};
-        r |= stage_softmax<false>(st2, nk, (int)(sk0 - n), mrun[rt], lrun[rt], lim[rt], sl2, bq[rt], alpha[rt]);
-      }
-    } else {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const f32x4 st2[2] = {S[0][rt], S[1][rt]};
-        r |= stage_softmax<true>(st2, nk, (int)(sk0 - n), mrun[rt], lrun[rt], lim[rt], sl2, bq[rt], alpha[rt]);
-      }
-    }
-    if (__any(r)) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) O[rt][db] *= alpha[rt];
-    }
-  }
-  if (nst > 0) stage_values<D, RT>(vring + ((nst - 1) % NS) * G::STAGE, bq, O);   // no refill after the loop
+    for (int rt = 0; rt < RT; ++rt) lim[rt] = wr[rt] / Gq;
 
-  // ------------------------------------------------------------ outputs
-  // lane (g4, m16) holds dims 16 db + 4 g4 .. + 3 of row m16
-  const bool cap_ok = total <= (int64_t)cap;
-  const bool single = nch == 1;
-  const int64_t slot_rows = ((int64_t)slot * pchunks + chunk) * p.rows;
+    // -------------------------------------------------------- key stages
+    // This thread's copies of a stage: key row u / OCT of the stage, and the
+    // 16-byte unit that the K (V) tile's swizzle puts at LDS position u % OCT
+    // of that row; the source is that key's row of KV head kvh, addressed from
+    // the stage's first key (wave-uniform) plus a lane offset.
+    auto issue_stage = [&](int st) {   // keys k0 + SK st .. into ring slot st % NS
+      const int64_t sk0 = k0 + (int64_t)SK * st;
+      const int last = (int)min<int64_t>(SK - 1, k1 - 1 - sk0);   // keys past the segment repeat its last key
+      const int64_t row = ((off + sk0) * hkv + kvh) * D;
+      const bf16_t *kb = kc + row, *vb = vc + row;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const float lsum = rows4_sum(lrun[rt]);
-    if (wrow[rt] >= R) continue;
-    const int l = wrow[rt] / Gq, h = kvh * Gq + wrow[rt] % Gq;
-    const int64_t orow = ((int64_t)b * L + l) * Hq + h;
+      for (int i = 0; i < LPS; ++i) {
+        const int u = t + kTileThreads * i, key = u / G::OCT, pos = u % G::OCT;
+        const unsigned kr = (unsigned)min(key, last) * rowb;
+        const unsigned dst = (st % NS) * G::STAGE + kTileThreads * 16 * i + wave * 1024;
+        if (G::NCP % kTileThreads == 0 || kTileThreads * i + 64 * wave < G::NCP) {   // wave-uniform
+          dma16_sbase(kb, kr + 16u * (unsigned)(pos ^ (key & G::SW)), kring_lds + dst);
+          dma16_sbase(vb, kr + 16u * (unsigned)(pos ^ (2 * (key & G::SWV))), vring_lds + dst);
+        }
+      }
+    };
+    static_assert(NS >= 4, "stage copies overlap the two stages before");
+#pragma unroll
+    for (int st = 0; st < NS - 2; ++st)
+      if (st < nst) issue_stage(st);
+
+    f32x4 O[RT][NDB];
+    float mrun[RT], lrun[RT];                           // lrun: this lane's share of the row sum
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      mrun[rt] = -INFINITY;
+      lrun[rt] = 0.f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) O[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // Staggered wavefront pairs.  Every wavefront accumulates the values of
+    // stage st - 1 (its probabilities kept from the iteration before), then
+    // scores stage st and runs its softmax; the two wavefronts of a SIMD (w
+    // and w + 4) meet the stage's barrier at different points of that
+    // sequence: an early wavefront after the value product, a late one before
+    // it.  So between two barriers an early wavefront scores, runs its softmax
+    // and accumulates values, while its partner accumulates values, then
+    // scores and runs its softmax: while one runs its softmax on the vector
+    // ALUs, the other has products for the matrix cores.  One barrier per
+    // stage: stage st is in LDS, the early wavefronts are done with stage
+    // st - 1 and the late ones with stage st - 2, whose slot is refilled with
+    // stage st + NS - 2 (stages st + 1 and st + 2 in flight while st - 1 and
+    // st are in use).
+    const bool late = wave >= kTileWaves / 2;
+    bf16x8 bq[RT];                                      // probabilities of the stage before
+    auto meet = [&](int st) {
+      wait_stages<2 * LPS, NS>(min(NS - 3, nst - 1 - st));
+      lds_barrier();
+      if (st + NS - 2 < nst) issue_stage(st + NS - 2);  // into the slot of stage st - 2
+    };
+    for (int st = 0; st < nst; ++st) {
+      if (late) meet(st);
+      if (st > 0) stage_values<D, RT>(vring + ((st - 1) % NS) * G::STAGE, bq, O);
+      if (!late) meet(st);
+      const int64_t sk0 = k0 + (int64_t)SK * st;
+      const int nk = (int)min<int64_t>(SK, k1 - sk0);
+      f32x4 Sc[2][RT];
+      float alpha[RT];
+      bool r = false;
+      stage_qk<D, RT>(kring + (st % NS) * G::STAGE, qf, Sc);
+      if (sk0 + SK <= kfull) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const f32x4 st2[2] = {Sc[0][rt], Sc[1][rt]};
+          r |= stage_softmax<false>(st2, nk, (int)(sk0 - n), mrun[rt], lrun[rt], lim[rt], sl2, bq[rt], alpha[rt]);
+        }
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const f32x4 st2[2] = {Sc[0][rt], Sc[1][rt]};
+          r |= stage_softmax<true>(st2, nk, (int)(sk0 - n), mrun[rt], lrun[rt], lim[rt], sl2, bq[rt], alpha[rt]);
+        }
+      }
+      if (__any(r)) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) O[rt][db] *= alpha[rt];
+      }
+    }
+    if (nst > 0) stage_values<D, RT>(vring + ((nst - 1) % NS) * G::STAGE, bq, O);   // no refill after the loop
+
+    // -------------------------------------------------------- outputs
+    // lane (g4, m16) holds dims 16 db + 4 g4 .. + 3 of row m16
+    float lsum[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) lsum[rt] = rows4_sum(lrun[rt]);
+    const int flags = __builtin_amdgcn_readfirstlane(seg_info[sg][3]);
+    const bool single = flags & 1, first_piece = flags & 2, cap_ok = flags & 4;
     if (single) {
-      const float inv = 1.f / lsum;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int d = 16 * db + 4 * g4;
-        RawE<4> zr;
-        zr.load((const bf16_t *)p.q_gate + orow * 2 * D + D + d);
-        float z[4];
-        zr.to_float(z);
-        bf16x4 o4;
+      for (int rt = 0; rt < RT; ++rt) {
+        if (wrow[rt] >= R) continue;
+        const int l = wrow[rt] / Gq, h = kvh * Gq + wrow[rt] % Gq;
+        const int64_t orow = ((int64_t)b * L + l) * Hq + h;
+        const float inv = 1.f / lsum[rt];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          o4[i] = (bf16_t)(cap_ok ? O[rt][db][i] * inv * sigmoid_f(z[i]) : __builtin_nanf(""));
-        *(bf16x4 *)((bf16_t *)p.out + orow * D + d) = o4;
+        for (int db = 0; db < NDB; ++db) {
+          const int d = 16 * db + 4 * g4;
+          RawE<4> zr;
+          zr.load((const bf16_t *)p.q_gate + orow * 2 * D + D + d);
+          float z[4];
+          zr.to_float(z);
+          bf16x4 o4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            o4[i] = (bf16_t)(cap_ok ? O[rt][db][i] * inv * sigmoid_f(z[i]) : __builtin_nanf(""));
+          *(bf16x4 *)((bf16_t *)p.out + orow * D + d) = o4;
+        }
       }
     } else if (cap_ok) {
-      const int rr = wrow[rt] - row0;
+      // The piece's partial: its running max and sum, and its output divided
+      // by the sum, in fp16 with the row scaled by a power of two s that puts
+      // its largest magnitude in [1/2, 1) (s kept in fp32 beside the sum).
+      // Each element keeps 11 significant bits, eight times finer than the
+      // bf16 result.  A row that saw no key of the piece has sum 0 and stores
+      // zeros (weight 0 in the merge).  Dim 16 db + 4 g4 + i of the row is
+      // stored at 32 (db / 2) + 8 g4 + 4 (db % 2) + i: each lane writes
+      // 16 bytes per store and the four lanes of a row 64 contiguous bytes.
+      const int64_t slot_rows = (int64_t)__builtin_amdgcn_readfirstlane(seg_info[sg][4]) * p.rows;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int d = 16 * db + 4 * g4;
-        __builtin_nontemporal_store(O[rt][db], (f32x4 *)(p.part_o + (slot_rows + rr) * D + d));
+      for (int rt = 0; rt < RT; ++rt) {
+        const float inv = lsum[rt] > 0.f ? 1.f / lsum[rt] : 0.f;
+        float mx = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, __builtin_fabsf(O[rt][db][i]));
+        mx = rows4_max(mx) * inv;                       // the four lane groups hold the row's dims
+        const int e = mx > 0.f ? min(__builtin_amdgcn_frexp_expf(mx), 127) : 0;   // mx = f 2^e, f in [1/2, 1)
+        if (wrow[rt] >= R) continue;
+        const int rr = wrow[rt] - row0;
+        typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        _Float16 *po = (_Float16 *)p.part_o + (slot_rows + rr) * D + 8 * g4;
+#pragma unroll
+        for (int db = 0; db < NDB; db += 2) {
+          h8 hv;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) hv[i] = (_Float16)__builtin_ldexpf(O[rt][db + i / 4][i % 4] * inv, -e);
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, hv), (u32x4 *)(po + 16 * db));
+        }
+        if (g4 == 0)
+          *(f32x4 *)(p.part_ml + (slot_rows + rr) * 4) = f32x4{mrun[rt], lsum[rt], __builtin_ldexpf(1.f, e), 0.f};
       }
-      if (g4 == 0) *(float2 *)(p.part_ml + (slot_rows + rr) * 2) = make_float2(mrun[rt], lsum);
     }
-  }
-  if (!cap_ok && chunk == 0) {
-    if (!single) {
-      for (int e = t; e < (rlast - row0 + 1) * D; e += kTileThreads) {
-        const int r = row0 + e / D, d = e % D, l = r / Gq, h = kvh * Gq + r % Gq;
-        ((bf16_t *)p.out)[(((int64_t)b * L + l) * Hq + h) * D + d] = (bf16_t)__builtin_nanf("");
-      }
+    if (!cap_ok && first_piece) {
+      if (!single) nan_rows(tile);
+      if (t == 0) flag_error(p);
     }
-    if (t == 0) flag_error(p);
   }
 }
 

@@ -96,7 +96,9 @@ int main(void) {
   CHECK(qsa_workspace_size(NULL) == 0, "NULL cfg");
   CHECK(qsa_gated_attention(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == QSA_ERR_INVALID, "all NULL");
   {
-    qsa_cfg c = good[4];                         /* prefill needs more than the no-alloc scratch */
+    qsa_cfg c = good[4];                         /* a 12288-row prefill chunk needs more than the no-alloc scratch */
+    c.q_len = 12288;
+    c.max_seq_len = 12288 + 30720;
     qsa_kv_cache kv = {(void *)0x10000, (void *)0x20000, (const int64_t *)0x30000, NULL, 1 << 20};
     CHECK(qsa_gated_attention_noalloc((const void *)0x50000, NULL, NULL, &kv, (const int32_t *)0x60000,
                                       (const int32_t *)0x70000, &c, (void *)0x7f0000000000ull) ==

@@ -175,12 +175,13 @@ def test_argument_errors_before_launch():
 
 def test_noalloc_entry_point_checks_before_any_launch():
     """The allocation-free entry point validates like qsa_gated_attention and
-    rejects a plan that needs more than its fixed scratch (prefill_4b needs
-    about 80 MiB) with QSA_ERR_WORKSPACE, before touching a device."""
+    rejects a plan that needs more than its fixed scratch (a 12288-row prefill
+    chunk of the 4B geometry needs 96 MiB of prepared queries) with
+    QSA_ERR_WORKSPACE, before touching a device."""
     lib = binding.load()
     kv = binding.KVCache(FAKE, FAKE + (1 << 30), FAKE, None, 1 << 20)
     out = FAKE + (2 << 30)
-    big = cfg_for(WORKLOADS["prefill_4b"])
+    big = cfg_for(WORKLOADS["prefill_4b"].with_(q_len=12288))
     assert binding.workspace_size(big) > binding.NOALLOC_SCRATCH_BYTES
     rc = lib.qsa_gated_attention_noalloc(FAKE, FAKE, FAKE, ctypes.byref(kv), FAKE, FAKE, ctypes.byref(big), out)
     assert rc == binding.QSA_ERR_WORKSPACE
@@ -188,7 +189,7 @@ def test_noalloc_entry_point_checks_before_any_launch():
     bad = cfg_for(WORKLOADS["decode_4b"], rotary_dim=63)
     rc = lib.qsa_gated_attention_noalloc(FAKE, FAKE, FAKE, ctypes.byref(kv), FAKE, FAKE, ctypes.byref(bad), out)
     assert rc == binding.QSA_ERR_INVALID
-    for name in ("decode_4b", "verify_24x2", "ragged_4b"):
+    for name in ("decode_4b", "verify_24x2", "ragged_4b", "prefill_4b"):
         assert binding.workspace_size(cfg_for(WORKLOADS[name])) <= binding.NOALLOC_SCRATCH_BYTES
 
 

@@ -97,12 +97,16 @@ SMALL = [
     Workload("bf16_new_rows_fold", batch=2, q_len=16, num_q_heads=4, num_kv_heads=1, head_dim=256,
              rotary_dim=64, rope_theta=1e7, dtype="bf16", prior=64, seed=112),
     # tile route at head_dim 64 (half of the workgroup issues no stage copies):
-    # 132 rows = one full and one ragged 128-row tile, 183 keys = 5 full 32-key stages + a ragged one
+    # 132 rows = one ragged 256-row tile, 183 keys = 5 full 32-key stages + a ragged one
     Workload("bf16_prefill_d64", batch=2, q_len=33, num_q_heads=8, num_kv_heads=2, head_dim=64,
              rotary_dim=32, rope_theta=1e4, dtype="bf16", prior=150, seed=113),
-    # tile route at head_dim 128: 280 rows = three tiles
+    # tile route at head_dim 128: 280 rows = a full 256-row tile and a ragged one (a pair when split)
     Workload("bf16_prefill_d128_tiles", batch=1, q_len=70, num_q_heads=8, num_kv_heads=2, head_dim=128,
              rotary_dim=64, rope_theta=1e6, dtype="bf16", prior=200, seed=114),
+    # tile route with an odd tile count: 600 rows = tiles 0 and 2 as a pair plus tile 1
+    # alone; with split key chunks one range per pair crosses from tile 0 into tile 2
+    Workload("bf16_prefill_tile_pairs", batch=2, q_len=150, num_q_heads=8, num_kv_heads=2, head_dim=128,
+             rotary_dim=32, rope_theta=1e6, dtype="bf16", prior=300, seed=135),
     # short-query route, smallest rotation by whole lanes: r/2 = D/16 at head_dim 64 and 128
     Workload("bf16_d64_r8", batch=2, q_len=3, num_q_heads=8, num_kv_heads=2, head_dim=64,
              rotary_dim=8, rope_theta=1e4, dtype="bf16", prior=90, seed=118),

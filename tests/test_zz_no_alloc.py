@@ -66,8 +66,8 @@ def test_noalloc_matches_workspace_call_twice_second_smaller():
 
 
 def test_noalloc_rejects_a_plan_larger_than_its_scratch():
-    w = WORKLOADS["prefill_4b"].with_(prior=4096)
-    inp = make_inputs(w.with_(prior=64))                 # small tensors; only the cfg matters here
+    w = WORKLOADS["prefill_4b"].with_(q_len=12288)     # 96 MiB of prepared queries
+    inp = make_inputs(w.with_(prior=64))                 # a short cache; only the plan's size matters here
     sess = Session(w.with_(prior=64), inp, max_seq_len=w.prior + w.q_len)
     need = binding.workspace_size(sess.cfg)
     say(f"case noalloc too large: needs {need} bytes")
