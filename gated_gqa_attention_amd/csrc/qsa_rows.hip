@@ -93,10 +93,21 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(Params p, int do_q, 
       if (!kv_ok) continue;
       const int64_t dst = (row * p.Hkv + head) * D + E * m16;
       const T *vsrc = (const T *)p.v_new + (bl * p.Hkv + head) * D + E * m16;
+      // the lane's E contiguous values in 16-byte pieces (8-byte when that is
+      // all of them), so that the K and V rows go out in whole vectors
+      using V = typename std::conditional<(E * sizeof(T) >= 16), uint4, uint2>::type;
+      constexpr int PER = (int)(sizeof(V) / sizeof(T)), NV = E / PER;
+      static_assert(NV * PER == E, "whole pieces");
+      V vv[NV];
 #pragma unroll
-      for (int j = 0; j < E; ++j) {
-        ((T *)p.kc)[dst + j] = from_f<T>(x[j]);
-        ((T *)p.vc)[dst + j] = vsrc[j];
+      for (int i = 0; i < NV; ++i) vv[i] = gld<V>(vsrc + PER * i);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        T k8[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) k8[j] = from_f<T>(x[PER * i + j]);
+        *(V *)((T *)p.kc + dst + PER * i) = __builtin_bit_cast(V, k8);
+        *(V *)((T *)p.vc + dst + PER * i) = vv[i];
       }
     } else {
       TQ *dst = (TQ *)p.qt + (bl * p.Hq + head) * D + E * m16;
