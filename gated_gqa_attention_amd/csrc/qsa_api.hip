@@ -142,6 +142,8 @@ int make_plan(const qsa_cfg *c, Plan *pl, bool row_tiles = true) {
   }
   if (p.blocks > 0x7fffffffLL) return fail(QSA_ERR_UNSUPPORTED, "launch grid too large (%lld workgroups)",
                                            (long long)p.blocks);
+  if (B * L * Hq > 0x7fffffffLL)                        // the merge kernels index query rows in 32 bits
+    return fail(QSA_ERR_UNSUPPORTED, "batch * q_len * num_q_heads too large (%lld)", (long long)(B * L * Hq));
   // split-K partial slots: chunks per (sequence, KV head, row tile); on the
   // tile route 2 chunks + 1 per pair of row tiles (the middle tile of an odd
   // count alone), for the pieces of the pair's equal key ranges

@@ -180,15 +180,17 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(Params p) {
                "s"(nrows), "s"(seq_lens), "s"(capp), "s"(seq_offset), "s"(q_gate), "s"(part_ml), "s"(part_o),
                "s"(outp));
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-  const int64_t id = (int64_t)blockIdx.x * (kThreads / kWave) + wave;   // (slot, row) pair
-  const int64_t nslots = (int64_t)p.B * hkv * ptiles;
-  if (id >= nslots * prows) return;
-  const int rr = (int)(id % prows);
-  const int64_t slot = id / prows;
-  const int tile = (int)(slot % ptiles);
-  const int64_t bk = slot / ptiles;
-  const int kvh = (int)(bk % hkv);
-  const int b = (int)(bk / hkv);
+  // (slot, row) pair; the planner keeps B L Hq below 2^31, so 32-bit unsigned
+  // divisions (a few instructions, where 64-bit ones are a long sequence)
+  const unsigned id = blockIdx.x * (unsigned)(kThreads / kWave) + (unsigned)wave;
+  const unsigned nslots = (unsigned)p.B * (unsigned)hkv * (unsigned)ptiles;
+  if (id >= nslots * (unsigned)prows) return;
+  const int rr = (int)(id % (unsigned)prows);
+  const unsigned slot = id / (unsigned)prows;
+  const int tile = (int)(slot % (unsigned)ptiles);
+  const int64_t bk = slot / (unsigned)ptiles;
+  const int kvh = (int)((unsigned)bk % (unsigned)hkv);
+  const int b = (int)((unsigned)bk / (unsigned)hkv);
   const int row0 = tile * prows;
   const int Rk = L * Gq, R = min(prows, Rk - row0);
   if (rr >= R) return;

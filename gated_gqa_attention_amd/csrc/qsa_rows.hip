@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(Params p, int do_q, 
   __shared__ __attribute__((aligned(16))) float2 cs[kMaxPairs];
   const int m16 = threadIdx.x & 15, hr = threadIdx.x / 16;   // head-row slot of these 16 lanes
   const int64_t bl = blockIdx.x;                        // new row (b, l)
-  const int b = (int)(bl / p.L), l = (int)(bl % p.L);
+  const int b = (int)(blockIdx.x / (unsigned)p.L), l = (int)(blockIdx.x % (unsigned)p.L);
   const int nk = do_kv ? p.Hkv : 0, nq = do_q ? p.Hq : 0, njobs = nk + nq;
   const int r = p.r, half = r / 2;
   const bool whole = half % E == 0;
