@@ -3,11 +3,13 @@
 // rotated the queries into the prepared buffer and appended the new keys and
 // values to the cache (Atlas qwen3_5/mod.rs module doc: append, then attend).
 //
-// tile_kernel: one workgroup = (sequence b, KV head g, tile of 256 query rows,
-// key chunk).  The rows are (new row l, head of group g) pairs in order
-// r = l * G + (h - g * G) (DS4Server issue #113, Reproduction: query heads
-// grouped within their KV group), so one K/V stream serves the whole group.
-// The chunk's keys stream through an HBM -> LDS ring of 32-key stages; eight
+// tile_kernel: one workgroup = (sequence b, KV head g, a range of keys of one
+// tile of 256 query rows, or of a pair of tiles: see pair_ranges).  The rows
+// are (new row l, head of group g) pairs in order r = l * G + (h - g * G)
+// (DS4Server issue #113, Reproduction: query heads grouped within their KV
+// group), so one K/V stream serves the whole group.  The keys of a segment
+// (one tile's part of the range) stream through an HBM -> LDS ring of 32-key
+// stages; eight
 // wavefronts (two per SIMD, so one can issue while the other waits) each own
 // two 16-row MFMA tiles (32 rows) and run their own online softmax over every
 // stage:
@@ -16,9 +18,9 @@
 // product takes its keys in a permuted order that matches the layout the score
 // product leaves the probabilities in, so P never goes through LDS; the
 // transposing LDS reads fetch V^T in that same order.  One workgroup barrier
-// per stage guards the ring slot.  A tile covered by one chunk applies the gate
-// attn * sigmoid(gate) (mlxd PR #99 Summary) and stores bf16; otherwise it
-// writes the chunk's (max, sum, unnormalised output) for the merge kernel.
+// per stage guards the ring slot.  A tile covered by one piece applies the gate
+// attn * sigmoid(gate) (mlxd PR #99 Summary) and stores bf16; otherwise each
+// piece writes its (max, sum, output / sum) for the merge kernel.
 #include "qsa_device.h"
 
 namespace qsa {
@@ -99,7 +101,7 @@ __device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2], int nkeys, in
   bm = rows4_max(bm) * scale_log2;
   // The reference max moves only when the block max passes it by more than
   // kLazyMax (log2 units), so the probabilities stay <= 2^kLazyMax and the
-  // output rarely needs rescaling; sums, outputs and the chunk's (max, sum)
+  // output rarely needs rescaling; sums, outputs and the piece's (max, sum)
   // all refer to the same reference, which keeps the result exact.
   const bool up = bm > m + kLazyMax;
   const float mn = up ? bm : m;
