@@ -107,6 +107,13 @@ SMALL = [
     # alone; with split key chunks one range per pair crosses from tile 0 into tile 2
     Workload("bf16_prefill_tile_pairs", batch=2, q_len=150, num_q_heads=8, num_kv_heads=2, head_dim=128,
              rotary_dim=32, rope_theta=1e6, dtype="bf16", prior=300, seed=135),
+    # tile route over sequences of unequal cached lengths: each (sequence, KV head)
+    # cuts its pair's keys by its own length; 400 rows = two tiles
+    Workload("bf16_prefill_ragged_pairs", batch=3, q_len=100, num_q_heads=8, num_kv_heads=2, head_dim=128,
+             rotary_dim=32, rope_theta=1e6, dtype="bf16", prior=0, seed=136, ragged=(0, 600)),
+    # tile route with no cached keys: the pair's first tile sees 64 keys, the second 100
+    Workload("bf16_prefill_no_prior_pairs", batch=1, q_len=100, num_q_heads=8, num_kv_heads=2, head_dim=128,
+             rotary_dim=32, rope_theta=1e6, dtype="bf16", prior=0, seed=137),
     # short-query route, smallest rotation by whole lanes: r/2 = D/16 at head_dim 64 and 128
     Workload("bf16_d64_r8", batch=2, q_len=3, num_q_heads=8, num_kv_heads=2, head_dim=64,
              rotary_dim=8, rope_theta=1e4, dtype="bf16", prior=90, seed=118),
