@@ -31,6 +31,7 @@ constexpr int kTileThreads = kPrefillThreads;        // eight wavefronts
 constexpr int kTileWaves = kTileThreads / kWave;
 constexpr int kRowTiles = kPrefillRowTiles;          // 16-row MFMA tiles per wavefront
 constexpr float kLazyMax = 8.f;                      // headroom of the running max, log2 units
+constexpr int kReadAhead = 2;                        // ring operand reads in flight ahead of the products
 constexpr int kPrefillRows = kPrefillTileRows;       // query rows per workgroup
 static_assert(kPrefillRows == kTileWaves * 16 * kRowTiles, "row tiles of the wavefronts");
 
@@ -49,29 +50,49 @@ struct PGeo {
 
 // Scores of one 32-key stage for this wavefront's RT row tiles:
 // S[kb][rt][i] = S^T[key 16 kb + 4 g4 + i][row m16 of tile rt], from the
-// swizzled K stage tile kt and the query fragments in registers.
+// swizzled K stage tile at LDS address kt and the query fragments in registers.
+// Unit 4 ks + g4 of key row 16 kb + m16 sits at unit (4 ks + g4) ^ (m16 & SW)
+// = 4 (ks ^ c) + (g4 ^ (m16 & 3)) with c = (m16 & SW) >> 2.  kl is the lane's
+// part of the address for ks = 0 (bits 6 and 7 hold c, and kt has none of
+// them), so every k-step's address is (kt + kl) ^ 64 (ks & 3) plus an
+// immediate: one register of lane offsets for every k-step.
 template <int D, int RT>
-__device__ __forceinline__ void stage_qk(const unsigned char *kt, const bf16x8 (&qf)[RT][D / 32], f32x4 (&S)[2][RT]) {
+__device__ __forceinline__ void stage_qk(unsigned kt, unsigned kl, const bf16x8 (&qf)[RT][D / 32], f32x4 (&S)[2][RT]) {
   using G = PGeo<D>;
   constexpr int KST = D / 32, RB = G::RB;
-  const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
+  typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) S[kb][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Unit 4 ks + g4 of key row 16 kb + m16 sits at unit (4 ks + g4) ^ (m16 & SW)
-  // = 4 ((ks & 3) ^ c) + 16 (ks >> 2) + (g4 ^ (m16 & 3)) with c = (m16 & SW) >> 2,
-  // so four lane offsets cover every k-step (the rest are immediates).
-  const int c = (m16 & G::SW) >> 2;
-  const unsigned char *kl = kt + m16 * RB + 16 * (g4 ^ (m16 & 3));
+  const unsigned a = kt + kl;
+  // the read of step i + kReadAhead (step j: k-step j / 2, key block j % 2)
+  // is issued before the products of step i
+  bf16x8 x[kReadAhead + 1];
+  auto fetch = [&](int i) {
+    const int ks = i / 2, kb = i % 2;
+    const unsigned ad = (a ^ (64u * (ks & 3))) + 256u * (ks >> 2) + 16u * RB * kb;
+    x[i % (kReadAhead + 1)] = *(const lds_bf16x8 *)(uintptr_t)ad;
+  };
 #pragma unroll
-  for (int ks = 0; ks < KST; ++ks)
+  for (int i = 0; i < kReadAhead; ++i) fetch(i);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 a = *(const bf16x8 *)(kl + 64 * ((ks & 3) ^ c) + 256 * (ks >> 2) + 16 * RB * kb);
+  for (int i = 0; i < 2 * KST; ++i) {
+    if (i + kReadAhead < 2 * KST) fetch(i + kReadAhead);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) S[kb][rt] = mfma_qk(a, qf[rt][ks], S[kb][rt]);
-    }
+    for (int rt = 0; rt < RT; ++rt) S[i % 2][rt] = mfma_qk(x[i % (kReadAhead + 1)], qf[rt][i / 2], S[i % 2][rt]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The lane's part of stage_qk's addresses: key row m16, unit g4 ^ (m16 & 3),
+// plus the k-step swizzle c in bits 6 and 7.
+template <int D>
+__device__ __forceinline__ unsigned qk_lane_offset() {
+  using G = PGeo<D>;
+  const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
+  return (unsigned)(m16 * G::RB + 16 * (g4 ^ (m16 & 3)) + 64 * ((m16 & G::SW) >> 2));
 }
 
 // Online softmax of one stage's scores.  Keys key0 .. key0 + nkeys - 1; this
@@ -97,8 +118,17 @@ __device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2], int nkeys, in
       }
       sc[4 * kb + i] = v;
     }
-  float bm = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-  bm = rows4_max(bm) * scale_log2;
+  // maxima as NaN-propagating maximum (v_maximum3_f32), which takes its
+  // operands as they are: fmaxf first quiets each operand with an instruction
+  // of its own.  The scores are finite or -inf (masked).
+  auto mx = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+  float bm = mx(mx(mx(mx(sc[0], sc[1]), sc[2]), mx(mx(sc[3], sc[4]), sc[5])), mx(sc[6], sc[7]));
+  {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+    bm = mx(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+    bm = mx(__uint_as_float(c[0]), __uint_as_float(c[1])) * scale_log2;
+  }
   // The reference max moves only when the block max passes it by more than
   // kLazyMax (log2 units), so the probabilities stay <= 2^kLazyMax and the
   // output rarely needs rescaling; sums, outputs and the piece's (max, sum)
@@ -113,6 +143,9 @@ __device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2], int nkeys, in
   m = mn;
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  // the stage's share of the row sum adds the rounded probabilities, two at a
+  // time, as a dot product with (1, 1) (v_dot2_f32_bf16)
+  const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
   float ps = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; j += 2) {
@@ -121,7 +154,7 @@ __device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2], int nkeys, in
     const bf16x2_t h = __builtin_convertvector(e, bf16x2_t);
     bp[j] = h[0];
     bp[j + 1] = h[1];
-    ps += (float)h[0] + (float)h[1];
+    ps = __builtin_amdgcn_fdot2_f32_bf16(h, ones, ps, false);
   }
   ls = ls * alpha + ps;
   return rescale;
@@ -131,31 +164,48 @@ __device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2], int nkeys, in
 // row tile, with the MFMA's k index j of lane group g4 standing for key
 // 4 g4 + j (j < 4) or 16 + 4 g4 + j - 4, the order the probabilities were left
 // in; the transposing reads fetch those two 4-key runs of the swizzled V tile
-// for dims 16 db + m16.
+// at LDS address vt for dims 16 db + m16.  Unit 2 db + h (h = bit 1 of m16) of
+// key row klo sits at unit 2 (db ^ s) + h, s = klo & SWV, = 2 ((db % E) ^ s) +
+// 2 E (db / E) + h with E = SWV + 1; row klo + 16 has the same s.  vl is the
+// lane's part of the address for db = 0 (bits 5 .. 4 + log2 E hold s, and vt
+// has none of them), so dim block db reads at (vt + vl) ^ 32 (db % E) plus an
+// immediate.  The swizzle leaves h alone, so the 32 lanes of rows klo = 0..7
+// (or 8..15) read 16 distinct units: no bank conflicts.
 template <int D, int RT>
-__device__ __forceinline__ void stage_values(const unsigned char *vt, const bf16x8 (&bp)[RT], f32x4 (&O)[RT][D / 16]) {
+__device__ __forceinline__ void stage_values(unsigned vt, unsigned vl, const bf16x8 (&bp)[RT], f32x4 (&O)[RT][D / 16]) {
   using G = PGeo<D>;
-  constexpr int NDB = D / 16, RB = G::RB;
-  const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
-  // Unit 2 db + h (h = bit 1 of m16) of key row klo sits at unit
-  // 2 (db ^ s) + h, s = klo & SWV, = 2 ((db % E) ^ s) + 2 E (db / E) + h with
-  // E = SWV + 1; row klo + 16 has the same s.  E lane offsets cover every dim
-  // block.  The swizzle leaves h alone, so the 32 lanes of rows klo = 0..7
-  // (or 8..15) read 16 distinct units: no bank conflicts.
-  constexpr int E = G::SWV + 1;
-  const int klo = 4 * g4 + (m16 >> 2), s = klo & G::SWV;
-  const unsigned char *vl = vt + klo * RB + 16 * ((m16 >> 1) & 1) + 8 * (m16 & 1);
+  constexpr int NDB = D / 16, RB = G::RB, E = G::SWV + 1;
   typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const unsigned a = vt + vl;
+  // the reads of dim block db + kReadAhead are issued before the products of
+  // db, so that each read's latency hides behind the products before it
+  s16x8 v8[kReadAhead + 1];
+  auto fetch = [&](int db) {
+    const unsigned p0 = (a ^ (32u * (db % E))) + 32u * E * (db / E), p1 = p0 + 16u * RB;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)p0);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)p1);
+    v8[db % (kReadAhead + 1)] = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+#pragma unroll
+  for (int db = 0; db < kReadAhead; ++db) fetch(db);
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
-    const unsigned char *p0 = vl + 32 * ((db % E) ^ s) + 32 * E * (db / E);
-    const unsigned char *p1 = p0 + 16 * RB;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
-    const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    if (db + kReadAhead < NDB) fetch(db + kReadAhead);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) O[rt][db] = mfma_qk(__builtin_bit_cast(bf16x8, v8), bp[rt], O[rt][db]);
+    for (int rt = 0; rt < RT; ++rt) O[rt][db] = mfma_qk(__builtin_bit_cast(bf16x8, v8[db % (kReadAhead + 1)]), bp[rt], O[rt][db]);
+    __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// The lane's part of stage_values's addresses: key row klo = 4 g4 + m16 / 4,
+// 8-byte half m16 & 1 of unit h, and the dim-block swizzle s in bits 5 and up.
+template <int D>
+__device__ __forceinline__ unsigned pv_lane_offset() {
+  using G = PGeo<D>;
+  const int lane = threadIdx.x % kWave, g4 = lane >> 4, m16 = lane & 15;
+  const int klo = 4 * g4 + (m16 >> 2);
+  return (unsigned)(klo * G::RB + 16 * ((m16 >> 1) & 1) + 8 * (m16 & 1) + 32 * (klo & G::SWV));
 }
 
 }  // namespace
@@ -177,7 +227,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
                                                         int tiles, int nitems, Params p) {
   using G = PGeo<D>;
   constexpr int KST = D / 32, NDB = D / 16, NS = G::NS, LPS = G::LPS, SK = G::SK, RT = kRowTiles;
-  __shared__ __attribute__((aligned(16))) unsigned char ring[2 * NS * G::STAGE];   // K ring | V ring
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[2 * NS * G::STAGE];   // K ring | V ring
   unsigned char *const kring = ring, *const vring = ring + NS * G::STAGE;
 
   const int t = threadIdx.x;
@@ -294,6 +344,14 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
   const unsigned kring_lds = (unsigned)(uintptr_t)(lds_void *)kring;
   const unsigned vring_lds = (unsigned)(uintptr_t)(lds_void *)vring;
   const unsigned rowb = (unsigned)(hkv * D * 2);       // bytes between consecutive keys of one KV head
+  // the lanes' parts of the ring read addresses; opaque() at each stage keeps
+  // the compiler from holding every k-step's or dim block's offset in a
+  // register of its own across the stage loop
+  const unsigned klane = qk_lane_offset<D>(), vlane = pv_lane_offset<D>();
+  auto opaque = [](unsigned x) {
+    asm volatile("" : "+v"(x));
+    return x;
+  };
 
 #pragma clang loop unroll(disable)
   for (int sg = sg0; sg < sg1; ++sg) {
@@ -370,14 +428,14 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
     };
     for (int st = 0; st < nst; ++st) {
       if (late) meet(st);
-      if (st > 0) stage_values<D, RT>(vring + ((st - 1) % NS) * G::STAGE, bq, O);
+      if (st > 0) stage_values<D, RT>(vring_lds + ((st - 1) % NS) * G::STAGE, opaque(vlane), bq, O);
       if (!late) meet(st);
       const int64_t sk0 = k0 + (int64_t)SK * st;
       const int nk = (int)min<int64_t>(SK, k1 - sk0);
       f32x4 Sc[2][RT];
       float alpha[RT];
       bool r = false;
-      stage_qk<D, RT>(kring + (st % NS) * G::STAGE, qf, Sc);
+      stage_qk<D, RT>(kring_lds + (st % NS) * G::STAGE, opaque(klane), qf, Sc);
       if (sk0 + SK <= kfull) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -398,7 +456,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
           for (int db = 0; db < NDB; ++db) O[rt][db] *= alpha[rt];
       }
     }
-    if (nst > 0) stage_values<D, RT>(vring + ((nst - 1) % NS) * G::STAGE, bq, O);   // no refill after the loop
+    if (nst > 0) stage_values<D, RT>(vring_lds + ((nst - 1) % NS) * G::STAGE, vlane, bq, O);   // no refill after the loop
 
     // -------------------------------------------------------- outputs
     // lane (g4, m16) holds dims 16 db + 4 g4 .. + 3 of row m16
