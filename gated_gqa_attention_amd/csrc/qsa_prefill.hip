@@ -48,46 +48,16 @@ struct PGeo {
   static constexpr int LPS = (NCP + kTileThreads - 1) / kTileThreads;   // per thread (some idle when D = 64)
 };
 
-// Scores of one 32-key stage for this wavefront's RT row tiles:
-// S[kb][rt][i] = S^T[key 16 kb + 4 g4 + i][row m16 of tile rt], from the
-// swizzled K stage tile at LDS address kt and the query fragments in registers.
-// Unit 4 ks + g4 of key row 16 kb + m16 sits at unit (4 ks + g4) ^ (m16 & SW)
-// = 4 (ks ^ c) + (g4 ^ (m16 & 3)) with c = (m16 & SW) >> 2.  kl is the lane's
-// part of the address for ks = 0 (bits 6 and 7 hold c, and kt has none of
-// them), so every k-step's address is (kt + kl) ^ 64 (ks & 3) plus an
-// immediate: one register of lane offsets for every k-step.
-template <int D, int RT>
-__device__ __forceinline__ void stage_qk(unsigned kt, unsigned kl, const bf16x8 (&qf)[RT][D / 32], f32x4 (&S)[2][RT]) {
-  using G = PGeo<D>;
-  constexpr int KST = D / 32, RB = G::RB;
-  typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) S[kb][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const unsigned a = kt + kl;
-  // the read of step i + kReadAhead (step j: k-step j / 2, key block j % 2)
-  // is issued before the products of step i
-  bf16x8 x[kReadAhead + 1];
-  auto fetch = [&](int i) {
-    const int ks = i / 2, kb = i % 2;
-    const unsigned ad = (a ^ (64u * (ks & 3))) + 256u * (ks >> 2) + 16u * RB * kb;
-    x[i % (kReadAhead + 1)] = *(const lds_bf16x8 *)(uintptr_t)ad;
-  };
-#pragma unroll
-  for (int i = 0; i < kReadAhead; ++i) fetch(i);
-#pragma unroll
-  for (int i = 0; i < 2 * KST; ++i) {
-    if (i + kReadAhead < 2 * KST) fetch(i + kReadAhead);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) S[i % 2][rt] = mfma_qk(x[i % (kReadAhead + 1)], qf[rt][i / 2], S[i % 2][rt]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// The lane's part of stage_qk's addresses: key row m16, unit g4 ^ (m16 & 3),
-// plus the k-step swizzle c in bits 6 and 7.
+// Scores of one 32-key stage for this wavefront's RT row tiles (score steps
+// of the tile kernel's stage loop): S[kb][rt][i] = S^T[key 16 kb + 4 g4 + i]
+// [row m16 of tile rt], from the swizzled K stage tile and the query fragments
+// in registers.  Unit 4 ks + g4 of key row 16 kb + m16 sits at unit
+// (4 ks + g4) ^ (m16 & SW) = 4 (ks ^ c) + (g4 ^ (m16 & 3)) with
+// c = (m16 & SW) >> 2.  The lane's part of the address for ks = 0 holds c in
+// bits 6 and 7 (and the stage's LDS address has none of them), so every
+// k-step's address is (stage + lane part) ^ 64 (ks & 3) plus an immediate:
+// one register of lane offsets for every k-step.  This is that lane part: key
+// row m16, unit g4 ^ (m16 & 3), plus c.
 template <int D>
 __device__ __forceinline__ unsigned qk_lane_offset() {
   using G = PGeo<D>;
@@ -161,45 +131,19 @@ __device__ __forceinline__ bool stage_softmax(const f32x4 (&S)[2], int nkeys, in
 }
 
 // O^T[dim][row] += V^T[dim][key] P^T[key][row] over one 32-key stage for each
-// row tile, with the MFMA's k index j of lane group g4 standing for key
-// 4 g4 + j (j < 4) or 16 + 4 g4 + j - 4, the order the probabilities were left
-// in; the transposing reads fetch those two 4-key runs of the swizzled V tile
-// at LDS address vt for dims 16 db + m16.  Unit 2 db + h (h = bit 1 of m16) of
-// key row klo sits at unit 2 (db ^ s) + h, s = klo & SWV, = 2 ((db % E) ^ s) +
-// 2 E (db / E) + h with E = SWV + 1; row klo + 16 has the same s.  vl is the
-// lane's part of the address for db = 0 (bits 5 .. 4 + log2 E hold s, and vt
-// has none of them), so dim block db reads at (vt + vl) ^ 32 (db % E) plus an
-// immediate.  The swizzle leaves h alone, so the 32 lanes of rows klo = 0..7
-// (or 8..15) read 16 distinct units: no bank conflicts.
-template <int D, int RT>
-__device__ __forceinline__ void stage_values(unsigned vt, unsigned vl, const bf16x8 (&bp)[RT], f32x4 (&O)[RT][D / 16]) {
-  using G = PGeo<D>;
-  constexpr int NDB = D / 16, RB = G::RB, E = G::SWV + 1;
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  const unsigned a = vt + vl;
-  // the reads of dim block db + kReadAhead are issued before the products of
-  // db, so that each read's latency hides behind the products before it
-  s16x8 v8[kReadAhead + 1];
-  auto fetch = [&](int db) {
-    const unsigned p0 = (a ^ (32u * (db % E))) + 32u * E * (db / E), p1 = p0 + 16u * RB;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)p0);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)p1);
-    v8[db % (kReadAhead + 1)] = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  };
-#pragma unroll
-  for (int db = 0; db < kReadAhead; ++db) fetch(db);
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    if (db + kReadAhead < NDB) fetch(db + kReadAhead);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) O[rt][db] = mfma_qk(__builtin_bit_cast(bf16x8, v8[db % (kReadAhead + 1)]), bp[rt], O[rt][db]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// The lane's part of stage_values's addresses: key row klo = 4 g4 + m16 / 4,
-// 8-byte half m16 & 1 of unit h, and the dim-block swizzle s in bits 5 and up.
+// row tile (value steps of the tile kernel's stage loop), with the MFMA's k
+// index j of lane group g4 standing for key 4 g4 + j (j < 4) or
+// 16 + 4 g4 + j - 4, the order the probabilities were left in; the
+// transposing reads fetch those two 4-key runs of the swizzled V tile for dims
+// 16 db + m16.  Unit 2 db + h (h = bit 1 of m16) of key row klo sits at unit
+// 2 (db ^ s) + h, s = klo & SWV, = 2 ((db % E) ^ s) + 2 E (db / E) + h with
+// E = SWV + 1; row klo + 16 has the same s.  The lane's part of the address
+// for db = 0 holds s in bits 5 .. 4 + log2 E (and the stage's LDS address has
+// none of them), so dim block db reads at (stage + lane part) ^ 32 (db % E)
+// plus an immediate.  The swizzle leaves h alone, so the 32 lanes of rows
+// klo = 0..7 (or 8..15) read 16 distinct units: no bank conflicts.  This is
+// that lane part: key row klo = 4 g4 + m16 / 4, 8-byte half m16 & 1 of unit h,
+// plus 32 s.
 template <int D>
 __device__ __forceinline__ unsigned pv_lane_offset() {
   using G = PGeo<D>;
@@ -341,6 +285,10 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
     }
   }
   lds_barrier();
+  auto opaque = [](unsigned x) {
+    asm volatile("" : "+v"(x));
+    return x;
+  };
   const unsigned kring_lds = (unsigned)(uintptr_t)(lds_void *)kring;
   const unsigned vring_lds = (unsigned)(uintptr_t)(lds_void *)vring;
   const unsigned rowb = (unsigned)(hkv * D * 2);       // bytes between consecutive keys of one KV head
@@ -348,10 +296,6 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
   // the compiler from holding every k-step's or dim block's offset in a
   // register of its own across the stage loop
   const unsigned klane = qk_lane_offset<D>(), vlane = pv_lane_offset<D>();
-  auto opaque = [](unsigned x) {
-    asm volatile("" : "+v"(x));
-    return x;
-  };
 
 #pragma clang loop unroll(disable)
   for (int sg = sg0; sg < sg1; ++sg) {
@@ -426,16 +370,71 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
       lds_barrier();
       if (st + NS - 2 < nst) issue_stage(st + NS - 2);  // into the slot of stage st - 2
     };
+    // Ring reads (addresses: qk_lane_offset, pv_lane_offset): each is issued
+    // kReadAhead steps before its products.  An iteration runs N = D / 16 value steps of stage st - 1
+    // (dim block db), then N score steps of stage st (k-step i / 2, key block
+    // i % 2); step j of those 2 N reads into x[j % NB].  A late wavefront has
+    // passed the barrier of stage st before its value steps, so its first
+    // score reads go out during its last value steps; an early one issues them
+    // after the barrier.
+    constexpr int N = D / 16, NB = kReadAhead + 1, RB = G::RB, E = G::SWV + 1;
+    typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    bf16x8 x[NB];
+    auto fetch_v = [&](unsigned va, int db) {
+      const unsigned p0 = (va ^ (32u * (db % E))) + 32u * E * (db / E), p1 = p0 + 16u * RB;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)p0);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)p1);
+      x[db % NB] = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    };
+    auto fetch_k = [&](unsigned ka, int i) {
+      const int ks = i / 2, kb = i % 2;
+      const unsigned ad = (ka ^ (64u * (ks & 3))) + 256u * (ks >> 2) + 16u * RB * kb;
+      x[(N + i) % NB] = *(const lds_bf16x8 *)(uintptr_t)ad;
+    };
+    // value steps of the stage at va; cross: the reads after them are the
+    // first score reads of the stage at ka
+    auto values = [&](unsigned va, unsigned ka, bool cross) {
+#pragma unroll
+      for (int db = 0; db < kReadAhead; ++db) fetch_v(va, db);
+#pragma unroll
+      for (int db = 0; db < N; ++db) {
+        if (db + kReadAhead < N)
+          fetch_v(va, db + kReadAhead);
+        else if (cross)
+          fetch_k(ka, db + kReadAhead - N);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) O[rt][db] = mfma_qk(x[db % NB], bq[rt], O[rt][db]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
     for (int st = 0; st < nst; ++st) {
+      const unsigned ka = kring_lds + (st % NS) * G::STAGE + opaque(klane);
       if (late) meet(st);
-      if (st > 0) stage_values<D, RT>(vring_lds + ((st - 1) % NS) * G::STAGE, opaque(vlane), bq, O);
+      if (st > 0) values(vring_lds + ((st - 1) % NS) * G::STAGE + opaque(vlane), ka, late);
       if (!late) meet(st);
+      if (!late || st == 0) {
+#pragma unroll
+        for (int i = 0; i < kReadAhead; ++i) fetch_k(ka, i);
+      }
+      f32x4 Sc[2][RT];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) Sc[kb][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        if (i + kReadAhead < N) fetch_k(ka, i + kReadAhead);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) Sc[i % 2][rt] = mfma_qk(x[(N + i) % NB], qf[rt][i / 2], Sc[i % 2][rt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const int64_t sk0 = k0 + (int64_t)SK * st;
       const int nk = (int)min<int64_t>(SK, k1 - sk0);
-      f32x4 Sc[2][RT];
       float alpha[RT];
       bool r = false;
-      stage_qk<D, RT>(kring_lds + (st % NS) * G::STAGE, opaque(klane), qf, Sc);
       if (sk0 + SK <= kfull) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -456,7 +455,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const int32_t *__res
           for (int db = 0; db < NDB; ++db) O[rt][db] *= alpha[rt];
       }
     }
-    if (nst > 0) stage_values<D, RT>(vring_lds + ((nst - 1) % NS) * G::STAGE, vlane, bq, O);   // no refill after the loop
+    if (nst > 0) values(vring_lds + ((nst - 1) % NS) * G::STAGE + vlane, 0u, false);   // no refill after the loop
 
     // -------------------------------------------------------- outputs
     // lane (g4, m16) holds dims 16 db + 4 g4 .. + 3 of row m16
