@@ -109,8 +109,11 @@ __global__ __launch_bounds__(WAVES * kWave) void linear_kernel(const bf16_t *__r
 // pieces are in flight at once; x's matching pieces (L2-resident) are loaded
 // alongside.  The fp32 products are summed over the lane's pieces, then over
 // the 64 lanes (a fixed tree of lane swaps), and lane 0 rounds and stores.
+// PMAX: the largest piece count the registers are sized for (K <= 512 PMAX);
+// sized to the call, so that short rows leave room for more wavefronts per
+// SIMD and so more loads in flight per CU.
 constexpr int kGemvMaxPieces = 16;                      // K <= 16 * 512
-template <int MR>
+template <int MR, int PMAX>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const bf16_t *__restrict__ x, const bf16_t *__restrict__ w,
                                                         int N, int K, bf16_t *__restrict__ y0, int n0_end, int ld0,
                                                         bf16_t *__restrict__ y1, int n1_end, int ld1,
@@ -120,9 +123,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const bf16_t *__restrict
   if (n >= N) return;
   const int pieces = K / 512;
   const bf16_t *wr = w + (int64_t)n * K + 8 * lane;
-  uint4 wv[kGemvMaxPieces], xv[MR][kGemvMaxPieces];
+  uint4 wv[PMAX], xv[MR][PMAX];
 #pragma unroll
-  for (int j = 0; j < kGemvMaxPieces; ++j)
+  for (int j = 0; j < PMAX; ++j)
     if (j < pieces) {
       wv[j] = gld<uint4>(wr + 512 * j);
 #pragma unroll
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const bf16_t *__restrict
 #pragma unroll
   for (int m = 0; m < MR; ++m) acc[m] = 0.f;
 #pragma unroll
-  for (int j = 0; j < kGemvMaxPieces; ++j)
+  for (int j = 0; j < PMAX; ++j)
     if (j < pieces) {
       const bf16x8 wb = __builtin_bit_cast(bf16x8, wv[j]);
 #pragma unroll
@@ -155,8 +158,16 @@ template <int MR>
 hipError_t launch_gemv_mr(const bf16_t *x, const bf16_t *w, int N, int K, bf16_t *y0, int n0_end, int ld0, bf16_t *y1,
                           int n1_end, int ld1, bf16_t *y2, int ld2, hipStream_t s) {
   const dim3 grid((N + kThreads / kWave - 1) / (kThreads / kWave));
-  hipLaunchKernelGGL((gemv_kernel<MR>), grid, dim3(kThreads), 0, s, x, w, N, K, y0, n0_end, ld0, y1, n1_end, ld1,
-                     y2, ld2);
+  const int pieces = K / 512;
+  if (pieces <= 4)
+    hipLaunchKernelGGL((gemv_kernel<MR, 4>), grid, dim3(kThreads), 0, s, x, w, N, K, y0, n0_end, ld0, y1, n1_end,
+                       ld1, y2, ld2);
+  else if (pieces <= 8)
+    hipLaunchKernelGGL((gemv_kernel<MR, 8>), grid, dim3(kThreads), 0, s, x, w, N, K, y0, n0_end, ld0, y1, n1_end,
+                       ld1, y2, ld2);
+  else
+    hipLaunchKernelGGL((gemv_kernel<MR, kGemvMaxPieces>), grid, dim3(kThreads), 0, s, x, w, N, K, y0, n0_end, ld0,
+                       y1, n1_end, ld1, y2, ld2);
   return hipGetLastError();
 }
 
