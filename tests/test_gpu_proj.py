@@ -65,6 +65,7 @@ CASES = [
     (WORKLOADS["decode_4b"], HIDDEN_4B),                 # 1 row, 4B geometry (one wavefront per feature)
     (WORKLOADS["decode_4b"].with_(batch=2), HIDDEN_4B),  # 2 rows
     (WORKLOADS["decode_4b"].with_(batch=4), 8192),       # 4 rows, 16 pieces of 512 per weight row
+    (WORKLOADS["decode_4b"].with_(batch=3), 1536),       # 3 rows, 3 pieces: registers sized for 4, one unused
     (WORKLOADS["decode_4b"].with_(batch=5), 512),        # 5 rows: the MFMA kernel
     (WORKLOADS["verify_24x2"], 2048),                    # 32 rows, 24 / 2 heads
     (WORKLOADS["decode_4b"].with_(batch=2, q_len=3), 1024),  # 6 rows
