@@ -45,6 +45,10 @@ template <> struct Op16<f16_t> { using x8 = f16x8; using x4 = f16x4; };
 
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + __expf(-z)); }
 
+// max of two floats as NaN-propagating maximum (v_maximum3_f32), which takes
+// its operands as they are: fmaxf has the compiler quiet each operand first
+// with an instruction of its own.  Scores and maxima here are finite or -inf.
+__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 // Cross-lane reductions without LDS traffic.  Each step combines a lane with
 // one partner symmetrically (a + b == b + a), so every lane of a group ends
 // with the bitwise same value.
@@ -62,10 +66,10 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 // max over the 16 lanes of a row
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp<0x128>(v));   // row_ror:8
-  v = fmaxf(v, dpp<0x124>(v));   // row_ror:4
-  v = fmaxf(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmax_nan(v, dpp<0x128>(v));   // row_ror:8
+  v = fmax_nan(v, dpp<0x124>(v));   // row_ror:4
+  v = fmax_nan(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmax_nan(v, dpp<0xB1>(v));    // quad_perm [1,0,3,2]
   return v;
 }
 // combine lanes i, i^16, i^32, i^48 (the four rows) with gfx950's lane swaps
@@ -77,9 +81,9 @@ __device__ __forceinline__ float rows4_sum(float v) {
 }
 __device__ __forceinline__ float rows4_max(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = fmax_nan(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+  return fmax_nan(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
 // Waits for this wave's LDS operations, then for every wave of the workgroup.
@@ -566,7 +570,7 @@ __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsi
     for (int i = 0; i < 4; ++i) {
       const int j = 4 * g4 + i;
       sc[rt][i] = j < vis ? S[rt][i] * scale_log2 : -INFINITY;
-      bm = fmaxf(bm, sc[rt][i]);
+      bm = fmax_nan(bm, sc[rt][i]);
     }
     bm = rows4_max(bm);
     if (g4 == 0) wmax[wave * 64 + 16 * rt + m16] = bm;
@@ -591,7 +595,7 @@ __device__ __forceinline__ void attend_stage(const unsigned char *kt, const unsi
       float mu = m[rt];
       alpha[rt] = 1.f;
       if (agreed) {
-        const float M = fmaxf(fmaxf(wmax[row], wmax[64 + row]), fmaxf(wmax[128 + row], wmax[192 + row]));
+        const float M = fmax_nan(fmax_nan(wmax[row], wmax[64 + row]), fmax_nan(wmax[128 + row], wmax[192 + row]));
         const bool grow = M > m[rt] + kMaxLead;         // also when m is -inf and M is finite
         const float mn = grow ? M : m[rt];
         mu = mn == -INFINITY ? 0.f : mn;
@@ -705,7 +709,7 @@ __device__ __forceinline__ void attend_new_rows(const unsigned char *kt, const u
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       sc[i] = 4 * g4 + i < vis ? S[i] * scale_log2 : -INFINITY;
-      bm = fmaxf(bm, sc[i]);
+      bm = fmax_nan(bm, sc[i]);
     }
     const float M = rows4_max(bm);                      // the reference: m was -inf
     const float mu = M == -INFINITY ? 0.f : M;
